@@ -1,0 +1,106 @@
+"""fp64 CPU oracle of the GSPN 2D line-scan propagation.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the product package
+(``linear_spatial_propagation_line_amd``) never does, and shares no code with
+it. The arithmetic lives in ``gspn_oracle.c`` (plain C, fp64); this module only
+builds it with gcc and marshals numpy arrays.
+
+What it computes, and the readings of open points, are documented at the top of
+``gspn_oracle.c`` (CSDN page on GSPN, sections 方法, 稳定性-上下文条件 and
+如何设计一个高效的传播层; aitntnews page, section 传播层的关键实现).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gspn_oracle.c")
+_LIB = os.path.join(_HERE, "libgspn_oracle.so")
+
+ORC_F64, ORC_F32, ORC_BF16 = 0, 1, 2
+T2B, B2T, L2R, R2L = 1, 2, 4, 8
+
+_lib = None
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math). Returns the .so path."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, src, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (building if needed) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        _lib = _bind(ctypes.CDLL(build()))
+    return _lib
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    f = lib.gspn_oracle_propagate
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    f.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                  ctypes.c_uint32, i64, vp, ctypes.c_int]
+    f.restype = ctypes.c_int
+    return lib
+
+
+def _as_input(a: np.ndarray, shape) -> tuple[np.ndarray, int]:
+    a = np.ascontiguousarray(a)
+    if a.shape != tuple(shape):
+        raise ValueError(f"shape {a.shape} != {tuple(shape)}")
+    if a.dtype == np.float64:
+        return a, ORC_F64
+    if a.dtype == np.float32:
+        return a, ORC_F32
+    if a.dtype == np.uint16:      # bf16 bit patterns
+        return a, ORC_BF16
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def propagate(x, l0, l1, l2, lam, u, dirs: int = 15, group_rows: int = 0,
+              nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """y = sum over directions in ``dirs`` of u * h_d, as float64 [B, C, H, W].
+
+    Inputs are numpy arrays of one dtype: float64, float32, or uint16 holding
+    bf16 bit patterns. ``l0, l1, l2`` are the logits of the neighbours at
+    orthogonal offsets -1, 0, +1.
+    """
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    shape = x.shape
+    arrs = []
+    dts = set()
+    for a in (x, l0, l1, l2, lam, u):
+        a2, dt = _as_input(np.asarray(a), shape)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    dt = dts.pop()
+    out = np.empty(shape, dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    L = lib if lib is not None else load()
+    B, C, H, W = shape
+    rc = L.gspn_oracle_propagate(*[a.ctypes.data for a in arrs], dt, B, C, H, W,
+                                 int(dirs), int(group_rows), out.ctypes.data,
+                                 int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out

@@ -1,0 +1,59 @@
+/*
+ * GSPN 2D line-scan propagation: fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link or
+ * call this library; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it. It shares no code, header or constant with the HIP
+ * library under linear_spatial_propagation_line_amd/.
+ *
+ * What it computes ("Parallel Sequence Modeling via Generalized Spatial
+ * Propagation Network", summarised on the CSDN page "GSPN——在convolution基础上
+ * 并行序列建模", section 方法 (method) and section 如何设计一个高效的传播层):
+ *
+ *   for each scan direction d in dir_mask, each plane (b, c):
+ *     h_s = w_s h_{s-1} + lambda_s (.) x_s          (recurrence, section 方法)
+ *     w_s tridiagonal: pixel o of line s links to o-1, o, o+1 of line s-1
+ *         (up-left, up, up-right; section 如何设计一个高效的传播层)
+ *     w_s[o][o+k-1] = sigmoid(l_k) / sum over in-range k' of sigmoid(l_k')
+ *         (row-wise normalisation, same section, the w_{tau,i,k} formula)
+ *   y = sum_d u (.) h_d                              (output gate y_i = u_i h_i,
+ *                                                     four-direction merge)
+ *
+ * Readings of points the pages leave open are listed in the source file.
+ */
+#ifndef GSPN_ORACLE_H
+#define GSPN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of the oracle's inputs */
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+
+/* direction bits: top->bottom, bottom->top, left->right, right->left */
+enum { ORC_T2B = 1, ORC_B2T = 2, ORC_L2R = 4, ORC_R2L = 8 };
+
+/*
+ * x, l0, l1, l2, lam, u: host arrays, contiguous [B, C, H, W], element type
+ * in_dtype (bf16 given as raw uint16 bit patterns). l0/l1/l2 hold the logit of
+ * the neighbour at orthogonal offset -1 / 0 / +1 (image coordinates).
+ * group_rows: 0 = global scan; G >= 1 = the scan restarts at every block of G
+ * positions [mG, (m+1)G) along the scan axis.
+ * out: host array of B*C*H*W doubles, overwritten with y.
+ * nthreads: worker threads over planes (<= 0 means 1).
+ * Returns 0, or -1 on a bad argument (nothing written).
+ */
+int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
+                          const void* l2, const void* lam, const void* u,
+                          int in_dtype, int64_t B, int64_t C, int64_t H,
+                          int64_t W, uint32_t dir_mask, int64_t group_rows,
+                          double* out, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
