@@ -1,0 +1,142 @@
+/*
+ * gspn.h -- C ABI of the MI355X (gfx950) GSPN 2D line-scan propagation.
+ *
+ * The operation (CSDN page "GSPN——在convolution基础上并行序列建模", sections
+ * 方法 and 如何设计一个高效的传播层; aitntnews page on GSPN, section
+ * 传播层的关键实现):
+ *
+ *   for every plane (b, c) and every scan direction d selected in dir_mask,
+ *     h_s = w_s h_{s-1} + lambda_s (.) x_s,   h before the first line = 0,
+ *   where line s is a row (vertical scans) or a column (horizontal scans) and
+ *   w_s is tridiagonal: pixel o of line s mixes pixels o-1, o, o+1 of line
+ *   s-1 (up-left, up, up-right for the top->bottom scan) with weights
+ *     w_k = sigmoid(l_k) / sum over in-range k' of sigmoid(l_k'),
+ *   l_k being the logit stored at pixel (line s, o) for orthogonal offset
+ *   k-1 in image coordinates. Every row of w_s sums to one (row-stochastic:
+ *   section 稳定性-上下文条件, Theorem 1). Neighbours outside the image do not
+ *   exist (edge pixels normalise over two, or one, neighbours).
+ *
+ *   out = sum over selected d of u (.) h_d       (output gate y = u (.) h,
+ *                                                 four-direction merge as a sum)
+ *
+ *   Local variant (section GSPN模块的设计): with group_rows = G >= 1 the scan
+ *   axis is cut into blocks of G consecutive positions [mG, (m+1)G) in image
+ *   coordinates (the last block may be shorter) and the state restarts at 0
+ *   whenever a scan enters a block, on both axes and in both scan orders.
+ *
+ * Layout: every tensor is a contiguous [B, C, H, W] array (W fastest) of one
+ * element type (dtype); all pointers are device memory owned by the caller.
+ * Arithmetic is fp32 for both storage types; bf16 outputs are rounded once
+ * (round-to-nearest-even) from the fp32 sum.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; on an error nothing is enqueued and out is untouched. Launch
+ * failures are reported as GSPN_E_HIP with the HIP error text available from
+ * gspn_last_error(). Work is asynchronous on `stream`; faults inside a kernel
+ * surface at the caller's next synchronisation. No call keeps a pointer after
+ * it returns. Calls are reentrant; gspn_last_error() is per thread.
+ */
+#ifndef GSPN_H
+#define GSPN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GSPN_F32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+
+/* scan directions: top->bottom, bottom->top, left->right, right->left */
+enum {
+  GSPN_T2B = 1u,
+  GSPN_B2T = 2u,
+  GSPN_L2R = 4u,
+  GSPN_R2L = 8u,
+  GSPN_ALL = 15u
+};
+
+typedef enum {
+  GSPN_OK = 0,
+  GSPN_E_NULL = 1,      /* a required pointer is NULL                      */
+  GSPN_E_SHAPE = 2,     /* B, C < 0, H, W < 1, or the size overflows       */
+  GSPN_E_DIRMASK = 3,   /* dir_mask is 0 or has bits above GSPN_ALL        */
+  GSPN_E_GROUP = 4,     /* group_rows < 0                                  */
+  GSPN_E_DTYPE = 5,     /* dtype is not a gspn_dtype                       */
+  GSPN_E_ALIGN = 6,     /* a pointer is not aligned to its element size    */
+  GSPN_E_ALIAS = 7,     /* out overlaps an input                           */
+  GSPN_E_NOMEM = 8,     /* the stream-ordered workspace allocation failed  */
+  GSPN_E_HIP = 9,       /* a HIP call or kernel launch failed              */
+  GSPN_E_WORKSPACE = 10 /* workspace is NULL or smaller than required      */
+} gspn_status;
+
+/*
+ * gspn_propagate -- out = sum_{d in dir_mask} u (.) h_d (see above).
+ *   x, lambda, u        inputs [B, C, H, W]
+ *   w_logits[0..2]      logits for orthogonal offsets -1, 0, +1
+ *   dir_mask            OR of GSPN_T2B/B2T/L2R/R2L
+ *   group_rows          0: global scan; G >= 1: local groups of G positions
+ *                       (G >= max(H, W) is the same as global)
+ *   dtype               element type of all seven tensors
+ *   out                 [B, C, H, W], write-only, fully overwritten; must not
+ *                       overlap any input
+ *   stream              HIP stream the work is enqueued on (0 = default)
+ * B*C == 0 is valid and enqueues nothing. When the chosen plan needs scratch
+ * memory (gspn_workspace_bytes > 0) it is taken with hipMallocAsync and given
+ * back with hipFreeAsync on `stream`.
+ */
+gspn_status gspn_propagate(const void* x, const void* const w_logits[3],
+                           const void* lambda, const void* u, int64_t B,
+                           int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                           int64_t group_rows, gspn_dtype dtype, void* out,
+                           hipStream_t stream);
+
+/*
+ * gspn_workspace_bytes -- scratch bytes gspn_propagate_ws needs for this
+ * problem (0 when the plan keeps everything on chip). Returns 0 for invalid
+ * arguments as well; gspn_propagate_ws reports those.
+ */
+size_t gspn_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                            uint32_t dir_mask, int64_t group_rows,
+                            gspn_dtype dtype);
+
+/*
+ * gspn_propagate_ws -- gspn_propagate with caller-owned scratch memory:
+ * `workspace` is device memory of at least ws_bytes >= gspn_workspace_bytes()
+ * bytes, 256-byte aligned, not overlapping any tensor, and not used by
+ * anything else until the enqueued work has finished. It may be NULL when the
+ * required size is 0.
+ */
+gspn_status gspn_propagate_ws(const void* x, const void* const w_logits[3],
+                              const void* lambda, const void* u, int64_t B,
+                              int64_t C, int64_t H, int64_t W,
+                              uint32_t dir_mask, int64_t group_rows,
+                              gspn_dtype dtype, void* out, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gspn_plan_name -- name of the kernel plan gspn_propagate would use for this
+ * problem ("plane16", "plane64", "stream", ...), or "invalid". Host-only.
+ */
+const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
+                           uint32_t dir_mask, int64_t group_rows,
+                           gspn_dtype dtype);
+
+/* gspn_status_str -- static text of a status code. */
+const char* gspn_status_str(gspn_status status);
+
+/* gspn_last_error -- detail of the calling thread's last failed call
+ * (e.g. the HIP error string); "" if none. Valid until the next call. */
+const char* gspn_last_error(void);
+
+/* gspn_abi_version -- version of this ABI (bumped on incompatible change). */
+int gspn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSPN_H */

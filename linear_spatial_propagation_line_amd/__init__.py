@@ -1,0 +1,148 @@
+"""GSPN 2D line-scan propagation on MI355X (gfx950).
+
+Thin ctypes binding over ``libgspn.so`` (built from ``csrc/`` by
+``python -m linear_spatial_propagation_line_amd.build``). It only marshals
+arguments: every step of the propagation runs in the library's HIP kernels,
+and there is no fallback -- a missing library raises.
+
+    out = propagate(x, (l0, l1, l2), lam, u, dirs=ALL, group_rows=0)
+
+computes, for every plane of the [B, C, H, W] tensors, the sum over the
+selected scan directions of u * h_d, where h_d is the line scan
+h_s = w_s h_{s-1} + lam * x with tridiagonal, row-normalised sigmoid weights
+(CSDN page on GSPN, sections 方法 and 如何设计一个高效的传播层). The C ABI and its
+argument rules are documented in include/gspn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+T2B, B2T, L2R, R2L, ALL = 1, 2, 4, 8, 15
+GSPN_F32, GSPN_BF16 = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgspn.so")
+
+_STATUS = ["GSPN_OK", "GSPN_E_NULL", "GSPN_E_SHAPE", "GSPN_E_DIRMASK", "GSPN_E_GROUP",
+           "GSPN_E_DTYPE", "GSPN_E_ALIGN", "GSPN_E_ALIAS", "GSPN_E_NOMEM", "GSPN_E_HIP",
+           "GSPN_E_WORKSPACE"]
+STATUS = {name: i for i, name in enumerate(_STATUS)}
+
+_lib = None
+
+
+class GspnError(RuntimeError):
+    """A gspn_* call returned a non-zero status."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = _STATUS[status] if 0 <= status < len(_STATUS) else str(status)
+        self.detail = detail
+        super().__init__(f"{self.name}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgspn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m linear_spatial_propagation_line_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
+        logits_t = ctypes.POINTER(ctypes.c_void_p)
+        common = [vp, logits_t, vp, vp, i64, i64, i64, i64, u32, i64, ctypes.c_int, vp]
+        L.gspn_propagate.argtypes = common + [vp]
+        L.gspn_propagate.restype = ctypes.c_int
+        L.gspn_propagate_ws.argtypes = common + [vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_ws.restype = ctypes.c_int
+        L.gspn_workspace_bytes.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_workspace_bytes.restype = ctypes.c_size_t
+        L.gspn_plan_name.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_plan_name.restype = ctypes.c_char_p
+        L.gspn_status_str.argtypes = [ctypes.c_int]
+        L.gspn_status_str.restype = ctypes.c_char_p
+        L.gspn_last_error.argtypes = []
+        L.gspn_last_error.restype = ctypes.c_char_p
+        L.gspn_abi_version.argtypes = []
+        L.gspn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return GSPN_F32
+    if t.dtype == torch.bfloat16:
+        return GSPN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GspnError(status, lib().gspn_last_error().decode())
+
+
+def workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
+    return int(lib().gspn_workspace_bytes(B, C, H, W, dirs, group_rows, dtype))
+
+
+def plan_name(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> str:
+    return lib().gspn_plan_name(B, C, H, W, dirs, group_rows, dtype).decode()
+
+
+def propagate(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
+              workspace=None, stream=None):
+    """out = sum_{d in dirs} u * h_d for contiguous [B, C, H, W] device tensors
+    of one dtype (float32 or bfloat16). ``logits`` = (l0, l1, l2) for the
+    neighbours at orthogonal offsets -1, 0, +1. Work is enqueued on ``stream``
+    (default: torch's current stream of x's device)."""
+    import torch
+    l0, l1, l2 = logits
+    ts = (x, l0, l1, l2, lam, u)
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("all inputs must be torch tensors on a GPU device")
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous tensors of one shape and dtype")
+    if x.dim() != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    L = lib()
+    need = int(L.gspn_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.gspn_propagate_ws(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H, W,
+                               dirs, group_rows, dt, out.data_ptr(), ws_ptr, ws_len, sptr))
+    return out
+
+
+def propagate_alloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
+                    stream=None):
+    """Same as propagate() but lets the library take its workspace with
+    hipMallocAsync on the stream (the plain gspn_propagate entry point)."""
+    import torch
+    l0, l1, l2 = logits
+    B, C, H, W = x.shape
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    _check(lib().gspn_propagate(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H, W,
+                                dirs, group_rows, dt, out.data_ptr(), sptr))
+    return out

@@ -1,0 +1,242 @@
+// C ABI of the GSPN propagation: host-side validation (no HIP call before an
+// argument is known to be good), plan choice, workspace handling and launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "gspn.h"
+#include "gspn_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gspn_status fail(gspn_status s, const std::string& detail) {
+  g_last_error = detail;
+  return s;
+}
+
+size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
+
+enum class Plan { kInvalid, kPlane16, kPlane64, kStream };
+
+struct Checked {
+  gspn_status status;
+  Plan plan;
+  size_t ws_bytes;
+};
+
+// Pure host logic: shape, mask, group, dtype limits and the plan they lead to.
+Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
+                    int64_t G, int dtype) {
+  Checked r{GSPN_OK, Plan::kInvalid, 0};
+  if (dtype != GSPN_F32 && dtype != GSPN_BF16) {
+    r.status = fail(GSPN_E_DTYPE, "dtype must be GSPN_F32 or GSPN_BF16");
+    return r;
+  }
+  if (B < 0 || C < 0 || H < 1 || W < 1) {
+    r.status = fail(GSPN_E_SHAPE, "need B >= 0, C >= 0, H >= 1, W >= 1");
+    return r;
+  }
+  const int64_t kMax = int64_t(1) << 31;
+  if (H >= kMax || W >= kMax || (B > 0 && C > INT64_MAX / B)) {
+    r.status = fail(GSPN_E_SHAPE, "dimension too large");
+    return r;
+  }
+  const int64_t planes = B * C;
+  if (H > INT64_MAX / W || (planes > 0 && H * W > INT64_MAX / 8 / planes)) {
+    r.status = fail(GSPN_E_SHAPE, "tensor size overflows");
+    return r;
+  }
+  if (planes >= kMax) {
+    r.status = fail(GSPN_E_SHAPE, "B * C must be below 2^31");
+    return r;
+  }
+  if (mask == 0 || mask > GSPN_ALL) {
+    r.status = fail(GSPN_E_DIRMASK, "dir_mask must be a non-empty subset of GSPN_ALL");
+    return r;
+  }
+  if (G < 0) {
+    r.status = fail(GSPN_E_GROUP, "group_rows must be >= 0");
+    return r;
+  }
+  if (gspn::plane_fits(H, W)) {
+    r.plan = gspn::plane_seg(H, W) == 16 ? Plan::kPlane16 : Plan::kPlane64;
+  } else {
+    if (H > gspn::stream_max_orth() || W > gspn::stream_max_orth()) {
+      r.status = fail(GSPN_E_SHAPE, "H and W must be <= 16384 for planes above 64x64");
+      return r;
+    }
+    r.plan = Plan::kStream;
+    const int nd = __builtin_popcount(mask);
+    if (nd > 1) r.ws_bytes = static_cast<size_t>(planes * H * W) * sizeof(float);
+  }
+  return r;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
+gspn_status check_all(const void* x, const void* const w_logits[3], const void* lambda,
+                      const void* u, int64_t B, int64_t C, int64_t H, int64_t W,
+                      uint32_t mask, int64_t G, gspn_dtype dtype, void* out,
+                      Checked* chk, gspn::Problem* pr) {
+  g_last_error.clear();
+  if (!x || !w_logits || !lambda || !u || !out)
+    return fail(GSPN_E_NULL, "x, w_logits, lambda, u and out must be non-null");
+  if (!w_logits[0] || !w_logits[1] || !w_logits[2])
+    return fail(GSPN_E_NULL, "w_logits[0..2] must be non-null");
+  *chk = check_shape(B, C, H, W, mask, G, static_cast<int>(dtype));
+  if (chk->status != GSPN_OK) return chk->status;
+  const size_t es = elem_size(dtype);
+  const void* ins[6] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u};
+  bool vec4 = true;
+  for (const void* p : ins) {
+    const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+    if (v % es) return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
+    if (v % (4 * es)) vec4 = false;
+  }
+  const uintptr_t vo = reinterpret_cast<uintptr_t>(out);
+  if (vo % es) return fail(GSPN_E_ALIGN, "out not aligned to its element size");
+  if (vo % (4 * es)) vec4 = false;
+  const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+  for (const void* p : ins)
+    if (overlaps(out, bytes, p, bytes)) return fail(GSPN_E_ALIAS, "out overlaps an input");
+  pr->x = x;
+  pr->l[0] = w_logits[0];
+  pr->l[1] = w_logits[1];
+  pr->l[2] = w_logits[2];
+  pr->lam = lambda;
+  pr->u = u;
+  pr->out = out;
+  pr->B = B; pr->C = C; pr->H = H; pr->W = W;
+  pr->mask = mask;
+  pr->G = G;
+  pr->dtype = dtype;
+  pr->aligned_vec4 = vec4;
+  return GSPN_OK;
+}
+
+gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  switch (plan) {
+    case Plan::kPlane16:
+    case Plan::kPlane64:
+      e = gspn::launch_plane(pr, stream);
+      break;
+    case Plan::kStream:
+      e = gspn::launch_stream(pr, static_cast<float*>(ws), stream);
+      break;
+    default:
+      return fail(GSPN_E_SHAPE, "no plan");
+  }
+  if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
+  return GSPN_OK;
+}
+
+const char* plan_str(Plan p) {
+  switch (p) {
+    case Plan::kPlane16: return "plane16";
+    case Plan::kPlane64: return "plane64";
+    case Plan::kStream: return "stream";
+    default: return "invalid";
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+gspn_status gspn_propagate(const void* x, const void* const w_logits[3], const void* lambda,
+                           const void* u, int64_t B, int64_t C, int64_t H, int64_t W,
+                           uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
+                           void* out, hipStream_t stream) {
+  Checked chk;
+  gspn::Problem pr;
+  gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
+                            dtype, out, &chk, &pr);
+  if (s != GSPN_OK) return s;
+  if (B * C == 0) return GSPN_OK;
+  void* ws = nullptr;
+  if (chk.ws_bytes > 0) {
+    hipError_t e = hipMallocAsync(&ws, chk.ws_bytes, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(GSPN_E_NOMEM, hipGetErrorString(e));
+    }
+  }
+  s = run(pr, chk.plan, ws, stream);
+  if (ws) {
+    hipError_t e = hipFreeAsync(ws, stream);
+    if (e != hipSuccess && s == GSPN_OK) s = fail(GSPN_E_HIP, hipGetErrorString(e));
+  }
+  return s;
+}
+
+size_t gspn_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                            int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  Checked chk = check_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  g_last_error = keep;
+  return chk.status == GSPN_OK ? chk.ws_bytes : 0;
+}
+
+gspn_status gspn_propagate_ws(const void* x, const void* const w_logits[3], const void* lambda,
+                              const void* u, int64_t B, int64_t C, int64_t H, int64_t W,
+                              uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
+                              void* out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  Checked chk;
+  gspn::Problem pr;
+  gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
+                            dtype, out, &chk, &pr);
+  if (s != GSPN_OK) return s;
+  if (chk.ws_bytes > 0) {
+    if (!workspace || ws_bytes < chk.ws_bytes)
+      return fail(GSPN_E_WORKSPACE, "workspace missing or smaller than gspn_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t bytes = static_cast<size_t>(B * C * H * W) * elem_size(dtype);
+    const void* all[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, out};
+    for (const void* p : all)
+      if (overlaps(workspace, chk.ws_bytes, p, bytes))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  if (B * C == 0) return GSPN_OK;
+  return run(pr, chk.plan, workspace, stream);
+}
+
+const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                           int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  Checked chk = check_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  g_last_error = keep;
+  return chk.status == GSPN_OK ? plan_str(chk.plan) : "invalid";
+}
+
+const char* gspn_status_str(gspn_status s) {
+  switch (s) {
+    case GSPN_OK: return "GSPN_OK";
+    case GSPN_E_NULL: return "GSPN_E_NULL: null pointer";
+    case GSPN_E_SHAPE: return "GSPN_E_SHAPE: bad or unsupported shape";
+    case GSPN_E_DIRMASK: return "GSPN_E_DIRMASK: bad direction mask";
+    case GSPN_E_GROUP: return "GSPN_E_GROUP: negative group_rows";
+    case GSPN_E_DTYPE: return "GSPN_E_DTYPE: bad dtype";
+    case GSPN_E_ALIGN: return "GSPN_E_ALIGN: misaligned pointer";
+    case GSPN_E_ALIAS: return "GSPN_E_ALIAS: output overlaps an input";
+    case GSPN_E_NOMEM: return "GSPN_E_NOMEM: workspace allocation failed";
+    case GSPN_E_HIP: return "GSPN_E_HIP: HIP error";
+    case GSPN_E_WORKSPACE: return "GSPN_E_WORKSPACE: workspace too small";
+  }
+  return "unknown gspn_status";
+}
+
+const char* gspn_last_error(void) { return g_last_error.c_str(); }
+
+int gspn_abi_version(void) { return 1; }
+
+}  // extern "C"

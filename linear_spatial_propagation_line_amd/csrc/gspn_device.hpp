@@ -1,0 +1,127 @@
+// Device helpers shared by the gfx950 GSPN kernels: storage decode/encode,
+// the fused sigmoid + row normalisation of the three neighbour logits, and
+// cross-lane neighbour exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gspn {
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v.bits) << 16);
+}
+// bf16 is the upper half of binary32: widening is exact
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// binary32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  __device__ static __forceinline__ void put(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Store<bf16_t> {
+  __device__ static __forceinline__ void put(bf16_t* p, int64_t i, float v) {
+    p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// weights of one pixel
+// ---------------------------------------------------------------------------
+// With a_k = 1 + exp(-l_k) (so sigmoid(l_k) = 1 / a_k), the normalised
+// weights are
+//     w_0 = a_1 a_2 / D,  w_1 = a_0 a_2 / D,  w_2 = a_0 a_1 / D,
+//     D   = a_1 a_2 + a_0 a_2 + a_0 a_1,
+// which needs three exponentials and one reciprocal per pixel instead of
+// three reciprocals more. Out-of-range neighbours get mask m = 0 (their
+// product term is dropped from both numerator and D). The centre neighbour
+// always exists. Logits are clamped below at -40 (sigmoid < 4.3e-18) so the
+// products stay finite in fp32; +inf gives a = 1 exactly.
+struct Weights {
+  float w0, w1, w2;
+};
+
+__device__ __forceinline__ float exp_neg(float l) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return __builtin_amdgcn_exp2f(-fmaxf(l, -40.0f) * kLog2e);
+}
+
+// Reciprocal: hardware estimate refined by one Newton-Raphson step
+// (r' = r + r (1 - d r)), which brings it to about half an ulp.
+__device__ __forceinline__ float recip(float d) {
+  float r = __builtin_amdgcn_rcpf(d);
+  float e = __builtin_fmaf(-d, r, 1.0f);
+  return __builtin_fmaf(r, e, r);
+}
+
+__device__ __forceinline__ Weights make_weights(float l0, float l1, float l2,
+                                                float m0, float m2) {
+  const float a0 = 1.0f + exp_neg(l0);
+  const float a1 = 1.0f + exp_neg(l1);
+  const float a2 = 1.0f + exp_neg(l2);
+  const float p12 = (m0 * a1) * a2;
+  const float p02 = a0 * a2;
+  const float p01 = (m2 * a0) * a1;
+  const float r = recip(p12 + p02 + p01);
+  return Weights{p12 * r, p02 * r, p01 * r};
+}
+
+// Renormalise already normalised interior weights for an edge pixel whose
+// side neighbours may be missing: w_k' = m_k w_k / sum_j m_j w_j.
+__device__ __forceinline__ Weights edge_weights(float w0, float w1, float w2,
+                                                float m0, float m2) {
+  const float v0 = m0 * w0, v2 = m2 * w2;
+  const float r = recip(v0 + w1 + v2);
+  return Weights{v0 * r, w1 * r, v2 * r};
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane neighbour values (DPP); lanes with no source read 0
+// ---------------------------------------------------------------------------
+// SEG = 64: the orthogonal axis spans the whole wave (wave_shr:1 / wave_shl:1).
+// SEG = 16: four independent 16-lane segments (row_shr:1 / row_shl:1).
+template <int SEG> __device__ __forceinline__ float from_left(float v);
+template <int SEG> __device__ __forceinline__ float from_right(float v);
+
+template <> __device__ __forceinline__ float from_left<64>(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true));
+}
+template <> __device__ __forceinline__ float from_right<64>(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
+}
+template <> __device__ __forceinline__ float from_left<16>(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+}
+template <> __device__ __forceinline__ float from_right<16>(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xf, 0xf, true));
+}
+
+// ---------------------------------------------------------------------------
+// small exact integer division for n < 2^24 (plane-local pixel indices)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int div_small(int n, int d, float inv_d, int* rem) {
+  int q = static_cast<int>(static_cast<float>(n) * inv_d);
+  int r = n - q * d;
+  if (r < 0) { q -= 1; r += d; }
+  if (r >= d) { q += 1; r -= d; }
+  *rem = r;
+  return q;
+}
+
+}  // namespace gspn

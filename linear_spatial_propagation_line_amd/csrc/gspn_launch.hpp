@@ -1,0 +1,36 @@
+// Internal interface between the C ABI (gspn_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gspn.h"
+
+namespace gspn {
+
+// A validated problem: every pointer non-null and aligned, shapes positive.
+struct Problem {
+  const void* x;
+  const void* l[3];
+  const void* lam;
+  const void* u;
+  void* out;
+  int64_t B, C, H, W;
+  uint32_t mask;
+  int64_t G;
+  gspn_dtype dtype;
+  bool aligned_vec4;   // every pointer aligned to 4 elements
+};
+
+// plane-resident path (gspn_plane.hip)
+bool plane_fits(int64_t H, int64_t W);
+int plane_seg(int64_t H, int64_t W);
+size_t plane_lds_bytes(int64_t H, int64_t W);
+hipError_t launch_plane(const Problem& pr, hipStream_t stream);
+
+// streaming per-direction path (gspn_stream.hip)
+int64_t stream_max_orth();
+hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream);
+
+}  // namespace gspn

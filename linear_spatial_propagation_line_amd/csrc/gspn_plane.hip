@@ -1,0 +1,263 @@
+// Plane-resident GSPN propagation for planes with H, W <= 64.
+//
+// One workgroup of four wavefronts owns PPB = 64 / SEG whole planes:
+//   1. all threads stream x, lambda and the three logits of the planes from
+//      HBM (coalesced, vectorised) and turn every pixel into a record
+//      (w0, w1, w2, lambda*x) in LDS -- sigmoid + normalisation computed once
+//      per pixel and shared by all four directions;
+//   2. records for the edge lanes (orthogonal index 0 and n_o - 1, whose
+//      missing neighbour changes the normalisation) go to small side arrays;
+//   3. wavefront d runs scan direction d: lane o of a SEG-lane segment is
+//      orthogonal index o, it walks the scan axis reading one record per step
+//      and takes its two neighbours' previous states by DPP (wave_shr/shl for
+//      SEG = 64, row_shr/shl inside 16-lane rows for SEG = 16, four planes
+//      per wavefront); its states stay in registers;
+//   4. the states are parked in LDS (over the now dead records), and all
+//      threads form out = u * (h_T2B + h_B2T + h_L2R + h_R2L) in that fixed
+//      order with one rounding to the storage type.
+// HBM traffic is the compulsory one: five inputs and u read once, out
+// written once.
+//
+// Line recurrence, output gate and unrolled form: CSDN page on GSPN, section
+// 方法; three-neighbour tridiagonal weights with sigmoid + row normalisation
+// and four scan directions: same page, section 如何设计一个高效的传播层;
+// local groups: section GSPN模块的设计.
+#include "gspn_device.hpp"
+#include "gspn_launch.hpp"
+
+namespace gspn {
+
+template <typename T>
+struct PlaneArgs {
+  const T* x;
+  const T* l0;
+  const T* l1;
+  const T* l2;
+  const T* lam;
+  const T* u;
+  T* out;
+  int64_t nplanes;
+  int H, W, G;
+  unsigned mask;
+  int pitch;        // records per LDS row (W rounded up to odd)
+  float inv_W, inv_HW;
+};
+
+// vector loads of four consecutive elements
+__device__ __forceinline__ void load4(const float* p, int64_t i, float v[4]) {
+  const float4 q = *reinterpret_cast<const float4*>(p + i);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float v[4]) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p + i);
+  v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+}
+__device__ __forceinline__ void store4(float* p, int64_t i, const float v[4]) {
+  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16_t* p, int64_t i, const float v[4]) {
+  uint2 q;
+  q.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+  q.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p + i) = q;
+}
+__device__ __forceinline__ void load1(const float* p, int64_t i, float v[4]) { v[0] = p[i]; }
+__device__ __forceinline__ void load1(const bf16_t* p, int64_t i, float v[4]) { v[0] = to_f32(p[i]); }
+__device__ __forceinline__ void store1(float* p, int64_t i, const float v[4]) { p[i] = v[0]; }
+__device__ __forceinline__ void store1(bf16_t* p, int64_t i, const float v[4]) {
+  p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v[0]));
+}
+
+template <typename T, int SEG, int VEC>
+__global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
+  constexpr int PPB = 64 / SEG;
+  extern __shared__ float4 smem[];
+  float* smem_f = reinterpret_cast<float*>(smem);
+
+  const int H = a.H, W = a.W, pitch = a.pitch;
+  const int HW = H * W;
+  const int64_t plane0 = static_cast<int64_t>(blockIdx.x) * PPB;
+  const int np = static_cast<int>(min<int64_t>(PPB, a.nplanes - plane0));
+  const int rec_sz = PPB * H * pitch;          // records (float4 units)
+  const int ev_off = rec_sz;                   // [PPB][2][H]
+  const int eh_off = ev_off + PPB * 2 * H;     // [PPB][2][W]
+  const int zero_off = eh_off + PPB * 2 * W;   // one zero record
+  const int64_t gbase = plane0 * HW;
+  const int npix = np * HW;
+  const int tid = threadIdx.x;
+
+  // ---- 1. records ----------------------------------------------------------
+  for (int i0 = tid * VEC; i0 < npix; i0 += 256 * VEC) {
+    float x[4], lm[4], g0[4], g1[4], g2[4];
+    if constexpr (VEC == 4) {
+      load4(a.x, gbase + i0, x); load4(a.lam, gbase + i0, lm);
+      load4(a.l0, gbase + i0, g0); load4(a.l1, gbase + i0, g1); load4(a.l2, gbase + i0, g2);
+    } else {
+      load1(a.x, gbase + i0, x); load1(a.lam, gbase + i0, lm);
+      load1(a.l0, gbase + i0, g0); load1(a.l1, gbase + i0, g1); load1(a.l2, gbase + i0, g2);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      int rem, c;
+      const int p = div_small(i0 + e, HW, a.inv_HW, &rem);
+      const int r = div_small(rem, W, a.inv_W, &c);
+      const Weights w = make_weights(g0[e], g1[e], g2[e], 1.0f, 1.0f);
+      smem[(p * H + r) * pitch + c] = make_float4(w.w0, w.w1, w.w2, lm[e] * x[e]);
+    }
+  }
+  if (tid == 0) smem[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+
+  // ---- 2. edge-lane records ------------------------------------------------
+  // vertical scans: lanes c = 0 (e = 0) and c = W-1 (e = 1), masks on c;
+  // horizontal scans: lanes r = 0 and r = H-1, masks on r.
+  const int n_ev = np * 2 * H, n_eh = np * 2 * W;
+  for (int k = tid; k < n_ev + n_eh; k += 256) {
+    int p, e, pos, r, c, idx, n_o, o;
+    if (k < n_ev) {
+      p = k / (2 * H); e = (k / H) & 1; pos = k % H;
+      r = pos; c = e ? W - 1 : 0; o = c; n_o = W; idx = ev_off + (p * 2 + e) * H + pos;
+    } else {
+      const int k2 = k - n_ev;
+      p = k2 / (2 * W); e = (k2 / W) & 1; pos = k2 % W;
+      c = pos; r = e ? H - 1 : 0; o = r; n_o = H; idx = eh_off + (p * 2 + e) * W + pos;
+    }
+    const float4 m = smem[(p * H + r) * pitch + c];
+    const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
+    smem[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
+  }
+  __syncthreads();
+
+  // ---- 3. one scan direction per wavefront ---------------------------------
+  const int d = tid >> 6;
+  const int lane = tid & 63;
+  const int p = lane / SEG, o = lane % SEG;
+  const bool on = (a.mask >> d) & 1u;
+  const bool vert = d < 2, fwd = (d == 0 || d == 2);
+  const int n_s = vert ? H : W, n_o = vert ? W : H;
+  const bool active = on && o < n_o && p < np;
+  // main-record position of step 0 and its per-step stride
+  int mbase, mstride;
+  if (vert) { mbase = (p * H + (fwd ? 0 : H - 1)) * pitch + o; mstride = fwd ? pitch : -pitch; }
+  else      { mbase = (p * H + o) * pitch + (fwd ? 0 : W - 1); mstride = fwd ? 1 : -1; }
+  int addr = mbase, stride = mstride;
+  if (!active) { addr = zero_off; stride = 0; }
+  else if (o == 0 || o == n_o - 1) {
+    const int e = (o == 0) ? 0 : 1;
+    if (vert) { addr = ev_off + (p * 2 + e) * H + (fwd ? 0 : H - 1); }
+    else      { addr = eh_off + (p * 2 + e) * W + (fwd ? 0 : W - 1); }
+    stride = fwd ? 1 : -1;
+  }
+  // steps at which the state restarts: 0, then every G from the first block edge
+  const int G = a.G;
+  int next_restart = n_s;
+  if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
+
+  float hist[SEG];
+  if (on) {
+    float h = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SEG; ++s) {
+      if (s < n_s) {
+        const float4 rc = smem[addr];
+        addr += stride;
+        const float hl = from_left<SEG>(h);
+        const float hr = from_right<SEG>(h);
+        const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+        bool restart = (s == 0);
+        if (s == next_restart) { restart = true; next_restart += G; }
+        h = restart ? rc.w : hn;
+        hist[s] = h;
+      }
+    }
+  }
+  __syncthreads();   // every wavefront is done with the records
+
+  // ---- 4. park states over the records, then merge --------------------------
+  if (active) {
+    int ya = d * rec_sz + mbase;
+#pragma unroll
+    for (int s = 0; s < SEG; ++s) {
+      if (s < n_s) { smem_f[ya] = hist[s]; ya += mstride; }
+    }
+  }
+  __syncthreads();
+
+  for (int i0 = tid * VEC; i0 < npix; i0 += 256 * VEC) {
+    float uu[4], y[4];
+    if constexpr (VEC == 4) load4(a.u, gbase + i0, uu); else load1(a.u, gbase + i0, uu);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      int rem, c;
+      const int pp = div_small(i0 + e, HW, a.inv_HW, &rem);
+      const int r = div_small(rem, W, a.inv_W, &c);
+      const int li = (pp * H + r) * pitch + c;
+      float sum = 0.0f;
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+        if ((a.mask >> dd) & 1u) sum += smem_f[dd * rec_sz + li];
+      y[e] = uu[e] * sum;
+    }
+    if constexpr (VEC == 4) store4(a.out, gbase + i0, y); else store1(a.out, gbase + i0, y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+bool plane_fits(int64_t H, int64_t W) { return H >= 1 && W >= 1 && H <= 64 && W <= 64; }
+
+int plane_seg(int64_t H, int64_t W) { return (H <= 16 && W <= 16) ? 16 : 64; }
+
+size_t plane_lds_bytes(int64_t H, int64_t W) {
+  const int seg = plane_seg(H, W);
+  const int ppb = 64 / seg;
+  const int pitch = static_cast<int>(W | 1);
+  const size_t recs = static_cast<size_t>(ppb) * (H * pitch + 2 * H + 2 * W) + 1;
+  return recs * sizeof(float4);
+}
+
+template <typename T, int SEG, int VEC>
+static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream) {
+  PlaneArgs<T> a;
+  a.x = static_cast<const T*>(pr.x);
+  a.l0 = static_cast<const T*>(pr.l[0]);
+  a.l1 = static_cast<const T*>(pr.l[1]);
+  a.l2 = static_cast<const T*>(pr.l[2]);
+  a.lam = static_cast<const T*>(pr.lam);
+  a.u = static_cast<const T*>(pr.u);
+  a.out = static_cast<T*>(pr.out);
+  a.nplanes = pr.B * pr.C;
+  a.H = static_cast<int>(pr.H);
+  a.W = static_cast<int>(pr.W);
+  a.G = static_cast<int>(pr.G >= pr.H && pr.G >= pr.W ? 0 : pr.G);
+  a.mask = pr.mask;
+  a.pitch = static_cast<int>(pr.W | 1);
+  a.inv_W = 1.0f / static_cast<float>(pr.W);
+  a.inv_HW = 1.0f / static_cast<float>(pr.H * pr.W);
+  constexpr int PPB = 64 / SEG;
+  const int64_t blocks = (a.nplanes + PPB - 1) / PPB;
+  const size_t lds = plane_lds_bytes(pr.H, pr.W);
+  auto kern = plane_kernel<T, SEG, VEC>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_plane_dt(const Problem& pr, hipStream_t stream) {
+  const bool vec = (pr.H * pr.W) % 4 == 0 && pr.aligned_vec4;
+  if (plane_seg(pr.H, pr.W) == 16)
+    return vec ? launch_plane_t<T, 16, 4>(pr, stream) : launch_plane_t<T, 16, 1>(pr, stream);
+  return vec ? launch_plane_t<T, 64, 4>(pr, stream) : launch_plane_t<T, 64, 1>(pr, stream);
+}
+
+hipError_t launch_plane(const Problem& pr, hipStream_t stream) {
+  if (pr.dtype == GSPN_F32) return launch_plane_dt<float>(pr, stream);
+  return launch_plane_dt<bf16_t>(pr, stream);
+}
+
+}  // namespace gspn

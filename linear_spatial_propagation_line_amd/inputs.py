@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module only draws random tensors; it holds none of the propagation's
+arithmetic. Both the HIP path and the CPU oracle consume the tensors it makes.
+
+Workloads (the pages' settings, with synthetic data in place of ImageNet,
+DiT latents and SD-XL text-to-image latents, which need datasets and trained
+weights):
+  tiny_16x16_t2b     B=1,  C=4,    16x16,     fp32, top->bottom only, global
+  cls_56x56          B=64, C=96,   56x56,     fp32, 4 directions, global
+                     (first stage of a Swin-like classifier; aitntnews page,
+                     section GSPN架构)
+  dit_16x16          B=32, C=1152, 16x16,     bf16, 4 directions, global
+                     (DiT-XL/2 latent of a 256x256 image: /8 VAE, patch 2)
+  local_128x128_g8   B=16, C=192,  128x128,   fp32, 4 directions, groups of 8
+  t2i_2048x1024      B=1,  C=320,  2048x1024, bf16, 4 directions, global
+                     (16Kx8K text-to-image latent, /8 VAE; aitntnews page,
+                     section 文本到图像生成)
+
+Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
+generator seeded with 1000 + k (k = 1..5 in the order above) and then cast
+(round-to-nearest-even) to the storage type.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # 1-based position in the table above (seed = 1000 + index)
+    B: int
+    C: int
+    H: int
+    W: int
+    dtype: str          # "f32" or "bf16"
+    dirs: int           # bit mask: 1 T->B, 2 B->T, 4 L->R, 8 R->L
+    group_rows: int     # 0 = global
+    logits: tuple       # distribution spec
+    x: tuple
+    lam: tuple
+    u: tuple
+
+    @property
+    def pixels(self) -> int:
+        return self.B * self.C * self.H * self.W
+
+    @property
+    def ndirs(self) -> int:
+        return bin(self.dirs).count("1")
+
+    @property
+    def elem_steps(self) -> int:
+        return self.pixels * self.ndirs
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == F32 else torch.bfloat16
+
+    def with_planes(self, B: int | None = None, C: int | None = None) -> "Workload":
+        return replace(self, B=self.B if B is None else B, C=self.C if C is None else C)
+
+
+NORMAL1 = ("normal", 1.0)
+SIG_NORMAL = ("sigmoid_normal", 1.0)
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_16x16_t2b", 1, 1, 4, 16, 16, F32, 1, 0,
+                 NORMAL1, ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0)),
+        Workload("cls_56x56", 2, 64, 96, 56, 56, F32, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
+        Workload("dit_16x16", 3, 32, 1152, 16, 16, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
+        Workload("local_128x128_g8", 4, 16, 192, 128, 128, F32, 15, 8,
+                 ("normal", 2.0), NORMAL1, ("uniform", 0.0, 1.0), ("uniform", 0.0, 1.0)),
+        Workload("t2i_2048x1024", 5, 1, 320, 2048, 1024, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
+    ]
+}
+
+
+def _draw(spec, shape, gen, device):
+    kind = spec[0]
+    if kind == "normal":
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * spec[1]
+    if kind == "sigmoid_normal":
+        return torch.sigmoid(torch.randn(shape, generator=gen, device=device,
+                                         dtype=torch.float32) * spec[1])
+    if kind == "uniform":
+        lo, hi = spec[1], spec[2]
+        return torch.rand(shape, generator=gen, device=device, dtype=torch.float32) * (hi - lo) + lo
+    raise ValueError(kind)
+
+
+def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
+                B: int | None = None, C: int | None = None, H: int | None = None,
+                W: int | None = None) -> dict:
+    """Tensors x, l0, l1, l2, lam, u of shape [B, C, H, W] in the workload's
+    storage dtype on ``device``. Shape overrides keep the distributions."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    shape = (B or w.B, C or w.C, H or w.H, W or w.W)
+    if seed is None:
+        seed = 1000 + w.index
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    for name, spec in (("x", w.x), ("lam", w.lam), ("u", w.u),
+                       ("l0", w.logits), ("l1", w.logits), ("l2", w.logits)):
+        out[name] = _draw(spec, shape, gen, device).to(w.torch_dtype)
+    return out

@@ -1,0 +1,111 @@
+"""Host-only checks of the C ABI (no GPU needed: no call here reaches a HIP
+API). The library must load, export every function include/gspn.h declares,
+and reject bad arguments with the documented status before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_spatial_propagation_line_amd as g
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gspn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g.LIB_PATH):
+        from linear_spatial_propagation_line_amd import build
+        build.build()
+    return g.lib()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gspn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gspn.h but not exported"
+
+
+def test_abi_version(L):
+    assert L.gspn_abi_version() == 1
+
+
+def test_status_strings(L):
+    for i in range(11):
+        s = L.gspn_status_str(i).decode()
+        assert s.startswith(g._STATUS[i])
+
+
+# fake, well-aligned device addresses: validation never dereferences them
+BASE = 1 << 40
+SZ = 1 << 32
+
+
+def call(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
+         u=BASE + 5 * SZ, B=1, C=1, H=8, W=8, mask=15, G=0, dt=0, out=BASE + 6 * SZ,
+         ws=None, ws_bytes=0, use_ws=False):
+    arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
+    if use_ws:
+        return L.gspn_propagate_ws(x, arr, lam, u, B, C, H, W, mask, G, dt, out, ws, ws_bytes, None)
+    return L.gspn_propagate(x, arr, lam, u, B, C, H, W, mask, G, dt, out, None)
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "GSPN_E_NULL"),
+    (dict(lg=None), "GSPN_E_NULL"),
+    (dict(lg=(BASE + SZ, None, BASE + 3 * SZ)), "GSPN_E_NULL"),
+    (dict(out=None), "GSPN_E_NULL"),
+    (dict(H=0), "GSPN_E_SHAPE"),
+    (dict(W=-3), "GSPN_E_SHAPE"),
+    (dict(B=-1), "GSPN_E_SHAPE"),
+    (dict(H=1 << 31), "GSPN_E_SHAPE"),
+    (dict(H=20000, W=100), "GSPN_E_SHAPE"),      # orthogonal length above the limit
+    (dict(mask=0), "GSPN_E_DIRMASK"),
+    (dict(mask=16), "GSPN_E_DIRMASK"),
+    (dict(G=-1), "GSPN_E_GROUP"),
+    (dict(dt=2), "GSPN_E_DTYPE"),
+    (dict(x=BASE + 2), "GSPN_E_ALIGN"),
+    (dict(dt=1, u=BASE + 5 * SZ + 1), "GSPN_E_ALIGN"),
+    (dict(out=BASE + 8), "GSPN_E_ALIAS"),          # overlaps x
+    (dict(out=BASE + 5 * SZ + 64), "GSPN_E_ALIAS"),  # overlaps u
+])
+def test_rejects_bad_arguments(L, kw, status, use_ws):
+    assert call(L, use_ws=use_ws, **kw) == g.STATUS[status]
+    assert L.gspn_last_error().decode() != ""
+
+
+def test_empty_batch_is_ok_without_gpu(L):
+    assert call(L, B=0) == 0
+    assert call(L, C=0, use_ws=True) == 0
+
+
+def test_workspace_checks(L):
+    need = L.gspn_workspace_bytes(2, 3, 300, 200, 15, 0, 0)
+    assert need == 2 * 3 * 300 * 200 * 4
+    assert call(L, B=2, C=3, H=300, W=200, use_ws=True) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert call(L, B=2, C=3, H=300, W=200, use_ws=True, ws=BASE + 7 * SZ,
+                ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert call(L, B=2, C=3, H=300, W=200, use_ws=True, ws=BASE + 7 * SZ + 16,
+                ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]
+    assert call(L, B=2, C=3, H=300, W=200, use_ws=True, ws=BASE + 6 * SZ,
+                ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]
+
+
+def test_workspace_and_plans(L):
+    assert g.workspace_bytes(64, 96, 56, 56) == 0
+    assert g.plan_name(64, 96, 56, 56) == "plane64"
+    assert g.plan_name(32, 1152, 16, 16, dtype=1) == "plane16"
+    assert g.plan_name(1, 1, 16, 17) == "plane64"
+    assert g.plan_name(1, 1, 65, 8) != "plane64"
+    assert g.workspace_bytes(1, 2, 100, 100, dirs=g.T2B) == 0
+    assert g.plan_name(1, 1, 0, 5) == "invalid"
+    assert g.workspace_bytes(1, 1, 0, 5) == 0

@@ -1,0 +1,152 @@
+"""HIP path vs the fp64 oracle, element by element, on the same seeded inputs
+(needs an MI355X). Every call goes through the C ABI via the binding."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import linear_spatial_propagation_line_amd as g
+from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs
+from parity import assert_parity, oracle_y
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(inp, dirs, G, **kw):
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    out = g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"],
+                      dirs=dirs, group_rows=G, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny_16x16_t2b", "cls_56x56", "dit_16x16",
+                                  "local_128x128_g8"])
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    print(f"[parity] {name} plan={g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, 0 if w.dtype == 'f32' else 1)}", flush=True)
+    inp = make_inputs(w)
+    out = run(inp, w.dirs, w.group_rows)
+    err = assert_parity(out, oracle_y(inp, w.dirs, w.group_rows), name)
+    print(f"[parity] {name} scaled error {err:.3e}", flush=True)
+
+
+def test_t2i_full_size_sampled_planes():
+    """The 2048x1024x320 bf16 workload at full size, in the launch
+    configuration the benchmark times; the oracle checks sampled planes."""
+    w = WORKLOADS["t2i_2048x1024"]
+    print("[parity] t2i full size, generating on device", flush=True)
+    d = make_inputs(w, device=DEV)
+    out = g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"],
+                      dirs=w.dirs, group_rows=w.group_rows)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for c in (0, 137, 319):
+        inp = {k: v[:, c:c + 1].cpu() for k, v in d.items()}
+        err = assert_parity(out[:, c:c + 1], oracle_y(inp, w.dirs, 0), f"t2i plane {c}")
+        print(f"[parity] t2i plane {c} scaled error {err:.3e}", flush=True)
+
+
+SHAPES = [
+    (1, 1, 1, 1), (1, 3, 1, 7), (2, 2, 7, 1), (1, 5, 16, 16), (3, 3, 13, 11),
+    (1, 2, 17, 16), (2, 3, 64, 64), (1, 3, 63, 61), (1, 2, 65, 64), (1, 2, 64, 65),
+    (1, 1, 100, 300), (1, 2, 300, 100), (1, 1, 1, 1000), (1, 1, 777, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(shape, dtype):
+    B, C, H, W = shape
+    base = WORKLOADS["cls_56x56"]
+    w = base if dtype == torch.float32 else WORKLOADS["dit_16x16"]
+    inp = make_inputs(w, seed=hash(shape) % 10000, B=B, C=C, H=H, W=W)
+    for G in (0, 3):
+        out = run(inp, 15, G)
+        assert_parity(out, oracle_y(inp, 15, G), f"{shape} G={G}")
+
+
+@pytest.mark.parametrize("shape", [(1, 6, 16, 16), (2, 2, 40, 24), (1, 2, 96, 80)],
+                         ids=["plane16", "plane64", "stream"])
+def test_every_direction_mask(shape):
+    B, C, H, W = shape
+    inp = make_inputs("cls_56x56", seed=21, B=B, C=C, H=H, W=W)
+    for mask in range(1, 16):
+        out = run(inp, mask, 0)
+        assert_parity(out, oracle_y(inp, mask, 0), f"{shape} mask={mask}")
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 16, 16), (1, 2, 48, 40), (1, 2, 130, 70)])
+@pytest.mark.parametrize("G", [1, 2, 5, 8, 16, 1000])
+def test_local_groups(shape, G):
+    B, C, H, W = shape
+    inp = make_inputs("local_128x128_g8", seed=31 + G, B=B, C=C, H=H, W=W)
+    out = run(inp, 15, G)
+    assert_parity(out, oracle_y(inp, 15, G), f"{shape} G={G}")
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 16, 16), (1, 2, 56, 56), (1, 2, 200, 150)])
+def test_row_stochastic_invariant(shape):
+    """lambda = x = u = 1: y = H + W + 2 everywhere (Theorem 1)."""
+    B, C, H, W = shape
+    inp = make_inputs("cls_56x56", seed=5, B=B, C=C, H=H, W=W)
+    for k in ("x", "lam", "u"):
+        inp[k] = torch.ones_like(inp[k])
+    out = run(inp, 15, 0)
+    assert torch.allclose(out.cpu(), torch.full(shape, float(H + W + 2)), rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (1, 2, 50, 60), (1, 1, 150, 90)])
+def test_one_hot_middle_weight(shape):
+    """l0 = l2 = -inf: w = I, so the scan is a per-line prefix sum."""
+    B, C, H, W = shape
+    inp = make_inputs("cls_56x56", seed=9, B=B, C=C, H=H, W=W)
+    inp["l0"] = torch.full(shape, -float("inf"))
+    inp["l2"] = torch.full(shape, -float("inf"))
+    for mask in (1, 2, 4, 8, 15):
+        out = run(inp, mask, 0)
+        assert_parity(out, oracle_y(inp, mask, 0), f"one-hot {shape} mask={mask}")
+
+
+@pytest.mark.parametrize("shape,dtype", [((4, 8, 56, 56), torch.float32),
+                                         ((2, 16, 16, 16), torch.bfloat16),
+                                         ((1, 3, 300, 200), torch.bfloat16)])
+def test_deterministic(shape, dtype):
+    B, C, H, W = shape
+    w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=2, B=B, C=C, H=H, W=W)
+    a = run(inp, 15, 0)
+    b = run(inp, 15, 0)
+    assert torch.equal(a, b)
+
+
+def test_alloc_entry_point_matches_workspace_entry_point():
+    inp = {k: v.to(DEV) for k, v in make_inputs("cls_56x56", seed=4, B=1, C=3, H=130, W=90).items()}
+    args = (inp["x"], (inp["l0"], inp["l1"], inp["l2"]), inp["lam"], inp["u"])
+    a = g.propagate(*args, dirs=15, group_rows=0)
+    b = g.propagate_alloc(*args, dirs=15, group_rows=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_side_stream():
+    inp = {k: v.to(DEV) for k, v in make_inputs("dit_16x16", seed=6, B=2, C=8).items()}
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = g.propagate(inp["x"], (inp["l0"], inp["l1"], inp["l2"]), inp["lam"], inp["u"])
+    s.synchronize()
+    ref = oracle_y({k: v.cpu() for k, v in inp.items()}, 15, 0)
+    assert_parity(out, ref, "side stream")
+
+
+def test_binding_rejects_mismatched_tensors():
+    x = torch.zeros(1, 1, 4, 4, device=DEV)
+    y = torch.zeros(1, 1, 4, 5, device=DEV)
+    with pytest.raises(ValueError):
+        g.propagate(x, (x, x, x), x, y)
+    with pytest.raises(g.GspnError) as ei:
+        g.propagate(x, (x, x, x), x, x, dirs=0)
+    assert ei.value.name == "GSPN_E_DIRMASK"
