@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the GSPN 2D line-scan propagation on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step = one full propagation (all selected scan directions, fused merge)
+over one batch of seeded synthetic inputs already resident in HBM. Prints ONE
+JSON line:
+  value     elem-steps/s = B*C*H*W*dirs*K / (time of K steps)
+  roofline  the dominant kernel: algorithmic bytes per launch / its average
+            launch time (HIP events recorded around each launch on the launch
+            stream, inside the timed region), against the 8 TB/s HBM peak;
+            traffic = HBM bytes per launch from the committed rocprofv3
+            counter summary when it was taken on the current kernel sources
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+            workload on this host's cores (rank 0, N = 1 only)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GSPN propagated elem-steps/s (B·C·H·W·dirs) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "t2i_2048x1024"
+CSRC = os.path.join(ROOT, "linear_spatial_propagation_line_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources; counter figures are only reported when
+    they were taken on exactly these sources."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """Just the HIP event calls the benchmark needs."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                               ctypes.c_void_p, ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.L.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        self.L.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.L.hipEventDestroy(e)
+
+
+def algorithmic_bytes(plan: str, launch: int, ndirs: int, w) -> tuple[str, float]:
+    """(kernel name, compulsory HBM bytes) of launch `launch` of one step.
+
+    Per pixel, with s = bytes per stored element:
+      plane16 / plane64  (one launch, all directions on chip):
+          x, lambda, l0, l1, l2, u read once, out written once -> 7 s
+      stream (one launch per direction, fp32 accumulator between them):
+          5 s inputs + {first: 4 (acc write), middle: 8 (acc read+write),
+                        last: 4 (acc read) + 2 s (u, out), only: 2 s}
+    """
+    s = 4 if w.dtype == "f32" else 2
+    px = w.pixels
+    if plan.startswith("plane"):
+        return f"plane_kernel<{plan}>", 7 * s * px
+    if plan == "stream":
+        if ndirs == 1:
+            per = 5 * s + 2 * s
+        elif launch == 0:
+            per = 5 * s + 4
+        elif launch == ndirs - 1:
+            per = 5 * s + 4 + 2 * s
+        else:
+            per = 5 * s + 8
+        return "stream_kernel", per * px
+    raise ValueError(plan)
+
+
+def counter_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from profiles/<kernel>__<workload>__pmc.txt, or
+    None when absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel.split('<')[0]}__{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp_dev, w, planes: int):
+    """The oracle as it stands on the first `planes` planes of the same
+    device-resident inputs, all host cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    planes = max(1, min(planes, w.B * w.C))
+    # planes are contiguous in [B, C, H, W]; take the first `planes` of them
+    arrs = []
+    for k in ("x", "l0", "l1", "l2", "lam", "u"):
+        t = inp_dev[k].reshape(-1, w.H, w.W)[:planes].cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            arrs.append(t.view(torch.int16).numpy().view(np.uint16).reshape(1, planes, w.H, w.W))
+        else:
+            arrs.append(t.numpy().reshape(1, planes, w.H, w.W))
+    threads = min(cores, planes)
+    t0 = time.perf_counter()
+    oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    steps = planes * w.H * w.W * w.ndirs
+    return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, {w.ndirs} dirs), "
+                      f"{steps} elem-steps in {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="rough wall time of the CPU oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the propagation shards by independent (b, c) "
+              f"planes with no collective, so --gpus {args.gpus} is not run here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_spatial_propagation_line_amd as g
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt_code = g.GSPN_F32 if w.dtype == "f32" else g.GSPN_BF16
+    plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+
+    # inputs resident in HBM; small problems rotate several input sets so the
+    # timed loop does not run out of the 256 MB last-level cache
+    s = 4 if w.dtype == "f32" else 2
+    set_bytes = 7 * s * w.pixels
+    nsets = max(1, min(8, -(-1024 ** 3 // set_bytes)))
+    sets = []
+    for i in range(nsets):
+        if set_bytes > 1 << 30:
+            sets.append(make_inputs(w, seed=1000 + w.index + 17 * i, device=dev))
+        else:
+            sets.append({k: v.to(dev) for k, v in
+                         make_inputs(w, seed=1000 + w.index + 17 * i).items()})
+    outs = [torch.empty_like(st["x"]) for st in sets]
+    ws_bytes = g.workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        st = sets[i % nsets]
+        g.propagate(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
+                    dirs=w.dirs, group_rows=w.group_rows, out=outs[i % nsets],
+                    workspace=ws if ws_bytes else None, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    L = g.lib()
+    max_launch = 8
+    evs = [hip.events(2 * max_launch) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    counts = []
+    for k in range(args.steps):
+        L.gspn_trace_events(evs[k], max_launch)
+        step(k)
+        counts.append(L.gspn_trace_count())
+    L.gspn_trace_events(None, 0)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    nl = min(counts[0], max_launch)
+    per_launch = [0.0] * nl
+    for k in range(args.steps):
+        for i in range(nl):
+            per_launch[i] += hip.elapsed_ms(evs[k][2 * i], evs[k][2 * i + 1])
+    per_launch = [t / args.steps for t in per_launch]
+    for e in evs:
+        hip.destroy(e)
+    dom = max(range(nl), key=lambda i: per_launch[i])
+    kname, kbytes = algorithmic_bytes(plan, dom, nl, w)
+    achieved = kbytes / (per_launch[dom] * 1e-3) / 1e9
+    traffic = counter_traffic(kname, w.name, source_digest())
+
+    value = w.elem_steps * args.steps / (ms_total * 1e-3)
+    q_min = 7 * s * w.pixels
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elem-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
+                   "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
+                   "plan": plan, "launches_per_step": counts[0],
+                   "launch_ms": [round(t, 4) for t in per_launch],
+                   "path_qmin_bytes": q_min,
+                   "path_qmin_gbs": q_min / (ms_per_step * 1e-3) / 1e9,
+                   "host_wall_s": round(wall, 3), "input_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
+                     "launch_ms": per_launch[dom]},
+    }
+    if not args.no_cpu_baseline:
+        cores = len(os.sched_getaffinity(0))
+        # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core
+        planes = int(args.cpu_seconds * 2.5e7 * cores / (w.H * w.W * w.ndirs)) + 1
+        result["cpu_baseline"] = cpu_baseline(sets[0], w, planes)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

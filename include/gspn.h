@@ -125,6 +125,18 @@ const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
                            uint32_t dir_mask, int64_t group_rows,
                            gspn_dtype dtype);
 
+/*
+ * gspn_trace_events -- optional launch tracing for benchmarks and profilers.
+ * While `events` is non-NULL, every following gspn_propagate* call made by
+ * the calling thread records events[2*i] right before and events[2*i + 1]
+ * right after its i-th kernel launch (for i < n_pairs) on the call's stream.
+ * The events are created and destroyed by the caller (hipEventCreate); the
+ * library only records them. gspn_trace_count() returns how many launches the
+ * last traced call made (which may exceed n_pairs). Pass NULL to stop.
+ */
+void gspn_trace_events(hipEvent_t* events, int n_pairs);
+int gspn_trace_count(void);
+
 /* gspn_status_str -- static text of a status code. */
 const char* gspn_status_str(gspn_status status);
 

@@ -12,6 +12,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t* g_trace_events = nullptr;
+thread_local int g_trace_pairs = 0;
+thread_local int g_trace_count = 0;
 
 gspn_status fail(gspn_status s, const std::string& detail) {
   g_last_error = detail;
@@ -123,17 +126,21 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
 
 gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  gspn::Tracer tr;
+  tr.events = g_trace_events;
+  tr.pairs = g_trace_pairs;
   switch (plan) {
     case Plan::kPlane16:
     case Plan::kPlane64:
-      e = gspn::launch_plane(pr, stream);
+      e = gspn::launch_plane(pr, stream, &tr);
       break;
     case Plan::kStream:
-      e = gspn::launch_stream(pr, static_cast<float*>(ws), stream);
+      e = gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
       break;
     default:
       return fail(GSPN_E_SHAPE, "no plan");
   }
+  if (g_trace_events) g_trace_count = tr.count;
   if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
   return GSPN_OK;
 }
@@ -217,6 +224,14 @@ const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t 
   g_last_error = keep;
   return chk.status == GSPN_OK ? plan_str(chk.plan) : "invalid";
 }
+
+void gspn_trace_events(hipEvent_t* events, int n_pairs) {
+  g_trace_events = n_pairs > 0 ? events : nullptr;
+  g_trace_pairs = n_pairs > 0 ? n_pairs : 0;
+  g_trace_count = 0;
+}
+
+int gspn_trace_count(void) { return g_trace_count; }
 
 const char* gspn_status_str(gspn_status s) {
   switch (s) {

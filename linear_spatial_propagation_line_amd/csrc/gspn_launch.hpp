@@ -23,14 +23,28 @@ struct Problem {
   bool aligned_vec4;   // every pointer aligned to 4 elements
 };
 
+// Records caller-owned events around kernel launches (gspn_trace_events).
+struct Tracer {
+  hipEvent_t* events = nullptr;
+  int pairs = 0;
+  int count = 0;
+  void before(hipStream_t s) {
+    if (events && count < pairs) (void)hipEventRecord(events[2 * count], s);
+  }
+  void after(hipStream_t s) {
+    if (events && count < pairs) (void)hipEventRecord(events[2 * count + 1], s);
+    ++count;
+  }
+};
+
 // plane-resident path (gspn_plane.hip)
 bool plane_fits(int64_t H, int64_t W);
 int plane_seg(int64_t H, int64_t W);
 size_t plane_lds_bytes(int64_t H, int64_t W);
-hipError_t launch_plane(const Problem& pr, hipStream_t stream);
+hipError_t launch_plane(const Problem& pr, hipStream_t stream, Tracer* tr);
 
 // streaming per-direction path (gspn_stream.hip)
 int64_t stream_max_orth();
-hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream);
+hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Tracer* tr);
 
 }  // namespace gspn

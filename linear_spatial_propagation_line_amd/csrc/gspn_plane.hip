@@ -216,7 +216,7 @@ size_t plane_lds_bytes(int64_t H, int64_t W) {
 }
 
 template <typename T, int SEG, int VEC>
-static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream) {
+static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* tr) {
   PlaneArgs<T> a;
   a.x = static_cast<const T*>(pr.x);
   a.l0 = static_cast<const T*>(pr.l[0]);
@@ -243,21 +243,23 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
+  tr->before(stream);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, a);
+  tr->after(stream);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_plane_dt(const Problem& pr, hipStream_t stream) {
+static hipError_t launch_plane_dt(const Problem& pr, hipStream_t stream, Tracer* tr) {
   const bool vec = (pr.H * pr.W) % 4 == 0 && pr.aligned_vec4;
   if (plane_seg(pr.H, pr.W) == 16)
-    return vec ? launch_plane_t<T, 16, 4>(pr, stream) : launch_plane_t<T, 16, 1>(pr, stream);
-  return vec ? launch_plane_t<T, 64, 4>(pr, stream) : launch_plane_t<T, 64, 1>(pr, stream);
+    return vec ? launch_plane_t<T, 16, 4>(pr, stream, tr) : launch_plane_t<T, 16, 1>(pr, stream, tr);
+  return vec ? launch_plane_t<T, 64, 4>(pr, stream, tr) : launch_plane_t<T, 64, 1>(pr, stream, tr);
 }
 
-hipError_t launch_plane(const Problem& pr, hipStream_t stream) {
-  if (pr.dtype == GSPN_F32) return launch_plane_dt<float>(pr, stream);
-  return launch_plane_dt<bf16_t>(pr, stream);
+hipError_t launch_plane(const Problem& pr, hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_plane_dt<float>(pr, stream, tr);
+  return launch_plane_dt<bf16_t>(pr, stream, tr);
 }
 
 }  // namespace gspn

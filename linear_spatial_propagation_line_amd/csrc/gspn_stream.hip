@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs<T> a) {
 int64_t stream_max_orth() { return 16384; }
 
 template <typename T>
-static hipError_t launch_stream_dt(const Problem& pr, float* acc, hipStream_t stream) {
+static hipError_t launch_stream_dt(const Problem& pr, float* acc, hipStream_t stream,
+                                   Tracer* tr) {
   const int64_t planes = pr.B * pr.C;
   int dirs[4], nd = 0;
   for (int d = 0; d < 4; ++d)
@@ -113,16 +114,18 @@ static hipError_t launch_stream_dt(const Problem& pr, float* acc, hipStream_t st
                                          static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
+    tr->before(stream);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(256), lds, stream, a);
+    tr->after(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream) {
-  if (pr.dtype == GSPN_F32) return launch_stream_dt<float>(pr, acc, stream);
-  return launch_stream_dt<bf16_t>(pr, acc, stream);
+hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_stream_dt<float>(pr, acc, stream, tr);
+  return launch_stream_dt<bf16_t>(pr, acc, stream, tr);
 }
 
 }  // namespace gspn
