@@ -77,31 +77,32 @@ class Hip:
             self.L.hipEventDestroy(e)
 
 
-def algorithmic_bytes(plan: str, launch: int, ndirs: int, w) -> tuple[str, float]:
-    """(kernel name, compulsory HBM bytes) of launch `launch` of one step.
+def algorithmic_bytes(kernel: str, planes: int, w) -> float:
+    """Compulsory HBM bytes of one launch of `kernel` over `planes` planes.
 
     Per pixel, with s = bytes per stored element:
-      plane16 / plane64  (one launch, all directions on chip):
-          x, lambda, l0, l1, l2, u read once, out written once -> 7 s
-      stream (one launch per direction, fp32 accumulator between them):
-          5 s inputs + {first: 4 (acc write), middle: 8 (acc read+write),
-                        last: 4 (acc read) + 2 s (u, out), only: 2 s}
+      plane_kernel16/64 (all directions on chip): x, lambda, l0, l1, l2, u
+          read once, out written once -> 7 s
+      stream_kernel (one launch per direction, fp32 accumulator between
+          them): 5 s inputs + 4 (accumulator read or write, counted once);
+          the u read / out write of the last direction are not included
+      tpipe (column-major copy = lambda*x in fp32 + 3 logits):
+          tp_vfwd  5 s inputs + (4 + 3 s) copy write + 4/8 checkpoints
+          tp_hpair 2 (4 + 3 s) copy reads + 2 * 4/4 checkpoints + 4 sum write
+          tp_vbwd  5 s inputs + 4/8 checkpoints + 4 sum read + s (u) + s (out)
     """
     s = 4 if w.dtype == "f32" else 2
-    px = w.pixels
-    if plan.startswith("plane"):
-        return f"plane_kernel<{plan}>", 7 * s * px
-    if plan == "stream":
-        if ndirs == 1:
-            per = 5 * s + 2 * s
-        elif launch == 0:
-            per = 5 * s + 4
-        elif launch == ndirs - 1:
-            per = 5 * s + 4 + 2 * s
-        else:
-            per = 5 * s + 8
-        return "stream_kernel", per * px
-    raise ValueError(plan)
+    px = planes * w.H * w.W
+    hz = bool(w.dirs & 12)
+    per = {
+        "plane_kernel16": 7 * s,
+        "plane_kernel64": 7 * s,
+        "stream_kernel": 5 * s + 4,
+        "tp_vfwd": 5 * s + (4 + 3 * s if hz else 0) + (0.5 if w.dirs & 1 else 0),
+        "tp_hpair": 2 * (4 + 3 * s) + 2.0 + 4,
+        "tp_vbwd": 5 * s + (0.5 if w.dirs & 1 else 0) + (4 if hz else 0) + 2 * s,
+    }[kernel]
+    return per * px
 
 
 def counter_traffic(kernel: str, workload: str, digest: str):
@@ -227,6 +228,11 @@ def main() -> int:
     ms_per_step = ms_total / args.steps
 
     nl = min(counts[0], max_launch)
+    launches = []
+    for i in range(nl):
+        np_ = ctypes.c_int64()
+        name = L.gspn_trace_kernel(i, ctypes.byref(np_))
+        launches.append((name.decode() if name else "?", int(np_.value)))
     per_launch = [0.0] * nl
     for k in range(args.steps):
         for i in range(nl):
@@ -234,10 +240,17 @@ def main() -> int:
     per_launch = [t / args.steps for t in per_launch]
     for e in evs:
         hip.destroy(e)
-    dom = max(range(nl), key=lambda i: per_launch[i])
-    kname, kbytes = algorithmic_bytes(plan, dom, nl, w)
-    achieved = kbytes / (per_launch[dom] * 1e-3) / 1e9
+    # per kernel: summed launch time and algorithmic bytes (launches of one
+    # kernel may run on two streams; each is timed on its own stream)
+    kt, kb = {}, {}
+    for (name, np_), t in zip(launches, per_launch):
+        kt[name] = kt.get(name, 0.0) + t
+        kb[name] = kb.get(name, 0.0) + algorithmic_bytes(name, np_, w)
+    kname = max(kt, key=kt.get)
+    kbytes = kb[kname]
+    achieved = kbytes / (kt[kname] * 1e-3) / 1e9
     traffic = counter_traffic(kname, w.name, source_digest())
+    path_bytes = sum(kb.values())
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
     q_min = 7 * s * w.pixels
@@ -257,14 +270,18 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
                    "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
                    "plan": plan, "launches_per_step": counts[0],
+                   "launches": [f"{n}[{p}]" for n, p in launches],
                    "launch_ms": [round(t, 4) for t in per_launch],
+                   "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
+                   "path_design_bytes": path_bytes,
+                   "path_design_gbs": path_bytes / (ms_per_step * 1e-3) / 1e9,
                    "path_qmin_bytes": q_min,
                    "path_qmin_gbs": q_min / (ms_per_step * 1e-3) / 1e9,
                    "host_wall_s": round(wall, 3), "input_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
-                     "launch_ms": per_launch[dom]},
+                     "traffic": traffic, "algorithmic_bytes_per_step": kbytes,
+                     "kernel_ms_per_step": kt[kname]},
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))

@@ -137,6 +137,15 @@ const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
 void gspn_trace_events(hipEvent_t* events, int n_pairs);
 int gspn_trace_count(void);
 
+/*
+ * gspn_trace_kernel -- name of the kernel of launch i of the last traced call
+ * (static string), storing the number of planes it processed in *planes;
+ * NULL when i is out of range. Launches may run on a library-owned helper
+ * stream that is forked from and joined back to the caller's stream; each
+ * launch's events are recorded on the stream that launch runs on.
+ */
+const char* gspn_trace_kernel(int i, int64_t* planes);
+
 /* gspn_status_str -- static text of a status code. */
 const char* gspn_status_str(gspn_status status);
 

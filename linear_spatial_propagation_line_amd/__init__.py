@@ -66,6 +66,12 @@ def lib() -> ctypes.CDLL:
         L.gspn_status_str.restype = ctypes.c_char_p
         L.gspn_last_error.argtypes = []
         L.gspn_last_error.restype = ctypes.c_char_p
+        L.gspn_trace_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.gspn_trace_events.restype = None
+        L.gspn_trace_count.argtypes = []
+        L.gspn_trace_count.restype = ctypes.c_int
+        L.gspn_trace_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+        L.gspn_trace_kernel.restype = ctypes.c_char_p
         L.gspn_abi_version.argtypes = []
         L.gspn_abi_version.restype = ctypes.c_int
         _lib = L

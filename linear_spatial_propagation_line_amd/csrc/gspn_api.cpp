@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -15,6 +16,8 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t* g_trace_events = nullptr;
 thread_local int g_trace_pairs = 0;
 thread_local int g_trace_count = 0;
+thread_local const char* g_trace_names[gspn::kTraceMax] = {};
+thread_local int64_t g_trace_planes[gspn::kTraceMax] = {};
 
 gspn_status fail(gspn_status s, const std::string& detail) {
   g_last_error = detail;
@@ -23,7 +26,7 @@ gspn_status fail(gspn_status s, const std::string& detail) {
 
 size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
 
-enum class Plan { kInvalid, kPlane16, kPlane64, kStream };
+enum class Plan { kInvalid, kPlane16, kPlane64, kTpipe, kStream };
 
 struct Checked {
   gspn_status status;
@@ -65,16 +68,28 @@ Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
     r.status = fail(GSPN_E_GROUP, "group_rows must be >= 0");
     return r;
   }
-  if (gspn::plane_fits(H, W)) {
+  // GSPN_FORCE_PLAN=plane|tpipe|stream picks a path for testing when the
+  // shape allows it; otherwise the first path that fits, in that order.
+  const char* force = std::getenv("GSPN_FORCE_PLAN");
+  const bool f_plane = force && !std::strcmp(force, "plane");
+  const bool f_tpipe = force && !std::strcmp(force, "tpipe");
+  const bool f_stream = force && !std::strcmp(force, "stream");
+  const bool any = !f_plane && !f_tpipe && !f_stream;
+  const bool stream_ok = H <= gspn::stream_max_orth() && W <= gspn::stream_max_orth();
+  if ((any || f_plane) && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? Plan::kPlane16 : Plan::kPlane64;
-  } else {
-    if (H > gspn::stream_max_orth() || W > gspn::stream_max_orth()) {
-      r.status = fail(GSPN_E_SHAPE, "H and W must be <= 16384 for planes above 64x64");
-      return r;
-    }
+  } else if ((any || f_tpipe) && gspn::tpipe_fits(H, W)) {
+    r.plan = Plan::kTpipe;
+    r.ws_bytes = gspn::tpipe_workspace_bytes(planes, H, W, static_cast<gspn_dtype>(dtype));
+  } else if (stream_ok && (any || f_stream || !gspn::plane_fits(H, W))) {
     r.plan = Plan::kStream;
     const int nd = __builtin_popcount(mask);
     if (nd > 1) r.ws_bytes = static_cast<size_t>(planes * H * W) * sizeof(float);
+  } else if (gspn::plane_fits(H, W)) {
+    r.plan = gspn::plane_seg(H, W) == 16 ? Plan::kPlane16 : Plan::kPlane64;
+  } else {
+    r.status = fail(GSPN_E_SHAPE, "H and W must be <= 16384 for planes above 64x64");
+    return r;
   }
   return r;
 }
@@ -134,13 +149,22 @@ gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream
     case Plan::kPlane64:
       e = gspn::launch_plane(pr, stream, &tr);
       break;
+    case Plan::kTpipe:
+      e = gspn::launch_tpipe(pr, ws, stream, &tr);
+      break;
     case Plan::kStream:
       e = gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
       break;
     default:
       return fail(GSPN_E_SHAPE, "no plan");
   }
-  if (g_trace_events) g_trace_count = tr.count;
+  if (g_trace_events) {
+    g_trace_count = tr.count;
+    for (int i = 0; i < gspn::kTraceMax; ++i) {
+      g_trace_names[i] = tr.names[i];
+      g_trace_planes[i] = tr.planes[i];
+    }
+  }
   if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
   return GSPN_OK;
 }
@@ -149,6 +173,7 @@ const char* plan_str(Plan p) {
   switch (p) {
     case Plan::kPlane16: return "plane16";
     case Plan::kPlane64: return "plane64";
+    case Plan::kTpipe: return "tpipe";
     case Plan::kStream: return "stream";
     default: return "invalid";
   }
@@ -226,12 +251,18 @@ const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t 
 }
 
 void gspn_trace_events(hipEvent_t* events, int n_pairs) {
+  // the record of the last traced call stays readable after tracing stops
   g_trace_events = n_pairs > 0 ? events : nullptr;
   g_trace_pairs = n_pairs > 0 ? n_pairs : 0;
-  g_trace_count = 0;
 }
 
 int gspn_trace_count(void) { return g_trace_count; }
+
+const char* gspn_trace_kernel(int i, int64_t* planes) {
+  if (i < 0 || i >= g_trace_count || i >= gspn::kTraceMax || !g_trace_names[i]) return nullptr;
+  if (planes) *planes = g_trace_planes[i];
+  return g_trace_names[i];
+}
 
 const char* gspn_status_str(gspn_status s) {
   switch (s) {

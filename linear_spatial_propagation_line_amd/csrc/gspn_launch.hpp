@@ -23,12 +23,17 @@ struct Problem {
   bool aligned_vec4;   // every pointer aligned to 4 elements
 };
 
-// Records caller-owned events around kernel launches (gspn_trace_events).
+// Records caller-owned events around kernel launches (gspn_trace_events),
+// and the kernel name and plane count of each launch.
+constexpr int kTraceMax = 16;
 struct Tracer {
   hipEvent_t* events = nullptr;
   int pairs = 0;
   int count = 0;
-  void before(hipStream_t s) {
+  const char* names[kTraceMax] = {};
+  int64_t planes[kTraceMax] = {};
+  void before(hipStream_t s, const char* name, int64_t np) {
+    if (count < kTraceMax) { names[count] = name; planes[count] = np; }
     if (events && count < pairs) (void)hipEventRecord(events[2 * count], s);
   }
   void after(hipStream_t s) {
@@ -42,6 +47,11 @@ bool plane_fits(int64_t H, int64_t W);
 int plane_seg(int64_t H, int64_t W);
 size_t plane_lds_bytes(int64_t H, int64_t W);
 hipError_t launch_plane(const Problem& pr, hipStream_t stream, Tracer* tr);
+
+// large-plane transpose pipeline (gspn_tpipe.hip)
+bool tpipe_fits(int64_t H, int64_t W);
+size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt);
+hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
 // streaming per-direction path (gspn_stream.hip)
 int64_t stream_max_orth();

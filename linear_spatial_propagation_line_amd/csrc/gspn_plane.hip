@@ -243,7 +243,7 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  tr->before(stream);
+  tr->before(stream, SEG == 16 ? "plane_kernel16" : "plane_kernel64", a.nplanes);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, a);
   tr->after(stream);
   return hipGetLastError();

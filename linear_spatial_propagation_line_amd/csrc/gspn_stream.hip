@@ -114,7 +114,7 @@ static hipError_t launch_stream_dt(const Problem& pr, float* acc, hipStream_t st
                                          static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    tr->before(stream);
+    tr->before(stream, "stream_kernel", planes);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(256), lds, stream, a);
     tr->after(stream);
     hipError_t e = hipGetLastError();

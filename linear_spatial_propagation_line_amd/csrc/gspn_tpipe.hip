@@ -1,0 +1,768 @@
+// Large-plane GSPN propagation ("transpose pipeline"), for planes above 64x64
+// with W <= 1024 and H <= 2048, both even.
+//
+// A plane is too large for on-chip memory, and every scan step couples a whole
+// line (each pixel mixes its three predecessors), so one workgroup must own a
+// whole line of a plane. Three launches, one workgroup per plane each:
+//
+//   K1 vfwd  -- top->bottom sweep over the row-major inputs (lane pair = two
+//               adjacent columns, coalesced 4-byte loads prefetched 8 rows
+//               ahead). Saves the state every 8 rows (checkpoints) and writes a
+//               column-major copy of lambda*x (fp32) and the three logits
+//               through per-thread register buffers, so every store is a
+//               contiguous >= 64-byte column segment.
+//   K2 hpair -- left->right and right->left on the column-major copy, where a
+//               horizontal scan reads whole contiguous lines. The right->left
+//               pass walks 4-column chunks from the right; for each chunk it
+//               recomputes left->right from the checkpoint before it, so one
+//               pass over the copy serves both directions. Writes
+//               h_L2R + h_R2L column-major (fp32).
+//   K3 vbwd  -- bottom->top over the row-major inputs in 8-row chunks, with
+//               top->bottom recomputed per chunk from K1's checkpoints; reads
+//               the horizontal sum of the chunk as one 32-byte column segment
+//               per column and writes out = u * (h_T2B + h_B2T + h_H) once,
+//               row-major.
+//
+// The normalised weights of a pixel are the same for both scans of one axis
+// (same logits, same in-range neighbours), so each chunk computes them once
+// for its recompute and its reverse pass.
+//
+// Line recurrence, output gate: CSDN page on GSPN, section 方法; tridiagonal
+// row-normalised sigmoid weights and four scan directions: section
+// 如何设计一个高效的传播层; local groups: section GSPN模块的设计.
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <type_traits>
+
+#include "gspn_device.hpp"
+#include "gspn_launch.hpp"
+
+namespace gspn {
+
+namespace {
+
+constexpr int kCkV = 8;    // rows per vertical chunk / checkpoint interval
+constexpr int kCkH = 4;    // columns per horizontal chunk / checkpoint interval
+constexpr int kPf = 8;     // prefetch distance (steps) of the forward sweeps
+// K1 holds copy buffers as well: fp32 elements get a shorter prefetch ring
+template <typename T> constexpr int pf_rows() { return sizeof(T) == 2 ? 8 : 4; }
+
+// ---- storage access: pairs of adjacent elements --------------------------
+template <typename T> struct Pair;
+template <> struct Pair<float> {
+  using raw = float2;
+  __device__ static raw load(const float* p, int64_t i) {
+    return *reinterpret_cast<const float2*>(p + i);
+  }
+  __device__ static float lo(raw v) { return v.x; }
+  __device__ static float hi(raw v) { return v.y; }
+};
+template <> struct Pair<bf16_t> {
+  using raw = uint32_t;
+  __device__ static raw load(const bf16_t* p, int64_t i) {
+    return *reinterpret_cast<const uint32_t*>(p + i);
+  }
+  __device__ static float lo(raw v) { return bf16_lo(v); }
+  __device__ static float hi(raw v) { return bf16_hi(v); }
+};
+
+__device__ __forceinline__ void store_pair(float* p, int64_t i, float a, float b) {
+  *reinterpret_cast<float2*>(p + i) = make_float2(a, b);
+}
+__device__ __forceinline__ void store_pair(bf16_t* p, int64_t i, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p + i) = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// raw inputs of two adjacent pixels
+template <typename T>
+struct Raw2 {
+  typename Pair<T>::raw x, lam, l0, l1, l2;
+};
+
+template <typename T>
+__device__ __forceinline__ Raw2<T> load_raw2(const T* x, const T* lam, const T* l0, const T* l1,
+                                             const T* l2, int64_t i) {
+  Raw2<T> r;
+  r.x = Pair<T>::load(x, i);
+  r.lam = Pair<T>::load(lam, i);
+  r.l0 = Pair<T>::load(l0, i);
+  r.l1 = Pair<T>::load(l1, i);
+  r.l2 = Pair<T>::load(l2, i);
+  return r;
+}
+
+// record of one pixel: normalised weights and lambda*x
+struct Rec {
+  float w0, w1, w2, lx;
+};
+
+__device__ __forceinline__ Rec make_rec(float l0, float l1, float l2, float lx, float m0,
+                                        float m2) {
+  const Weights w = make_weights(l0, l1, l2, m0, m2);
+  return Rec{w.w0, w.w1, w.w2, lx};
+}
+
+__device__ __forceinline__ float mix(const Rec& r, float hl, float hc, float hr) {
+  return __builtin_fmaf(r.w0, hl, __builtin_fmaf(r.w1, hc, __builtin_fmaf(r.w2, hr, r.lx)));
+}
+
+// Restart bookkeeping without a division per step. A forward scan restarts
+// at position 0 and at every multiple of G (G > 0); a reverse scan (positions
+// decreasing) at n - 1 and at every mG - 1. These give the first restart
+// position met from p on; later ones follow by adding / subtracting G.
+constexpr int kNone = 1 << 30;
+__device__ __forceinline__ int fwd_restart_from(int p, int G) {
+  if (p <= 0) return 0;
+  if (G <= 0) return kNone;
+  return (p + G - 1) / G * G;
+}
+__device__ __forceinline__ int rev_restart_from(int p, int n, int G) {
+  if (p >= n - 1) return n - 1;
+  if (G <= 0) return -kNone;
+  return (p + 1) / G * G - 1;
+}
+// state of a forward restart counter: next restart position
+struct FwdRestart {
+  int next, G;
+  __device__ bool at(int p) {
+    const bool r = (p == next);
+    next = r ? (G > 0 ? p + G : kNone) : next;
+    return r;
+  }
+};
+// reverse counter: after position n - 1 the next one is not n - 1 - G in
+// general, so it is precomputed
+struct RevRestart {
+  int next, after_last, G, last;
+  __device__ bool at(int p) {
+    const bool r = (p == next);
+    next = r ? (p == last ? after_last : p - G) : next;
+    return r;
+  }
+};
+__device__ __forceinline__ RevRestart rev_counter(int p, int n, int G) {
+  return RevRestart{rev_restart_from(p, n, G), rev_restart_from(n - 2, n, G), G, n - 1};
+}
+
+// Line exchange: the states of one line, two per thread, in LDS with two
+// zero pads on each side (index = position + 2); double-buffered so that one
+// barrier per step suffices. Only threads that own positions of the line
+// write it; the pads stay zero from the initial clear.
+struct LineX {
+  float* buf;     // [2][n + 4]
+  int n4;         // n + 4
+  int par;
+  __device__ float* cur() { return buf + par * n4; }
+  __device__ float* nxt() { return buf + (par ^ 1) * n4; }
+};
+
+}  // namespace
+
+template <typename T>
+struct TpArgs {
+  const T* x;
+  const T* lam;
+  const T* l0;
+  const T* l1;
+  const T* l2;
+  const T* u;
+  T* out;
+  float* lxt;     // [planes][W][Hp]   lambda*x, column-major
+  T* lgt;         // [3][planes][W][Hp] logits, column-major
+  float* yht;     // [planes][W][Hp]   h_L2R + h_R2L, column-major
+  float* ckv;     // [planes][nckv][W] top->bottom states after rows 8k+7
+  float* ckh;     // [planes][nckh][H] left->right states after columns 4k+3
+  int H, W, G, Hp, nckv, nckh;
+  unsigned mask;
+  int64_t lg_stride;   // elements between the three logit copies
+  int64_t plane0;      // first plane of this launch (blockIdx.x is relative)
+};
+
+// ===========================================================================
+// K1: top->bottom forward sweep, checkpoints, column-major copy
+// ===========================================================================
+// SCAN: run top->bottom and save checkpoints; COPY: write the column-major copy.
+// The main loop covers full 32-row blocks with straight-line code and
+// unconditional (row-clamped) loads so that the prefetch ring stays in flight;
+// a partial last block runs the same body with per-row guards.
+template <typename T, bool SCAN, bool COPY>
+__global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
+  __shared__ float lbuf[2 * (1024 + 4)];
+  constexpr int LGP = sizeof(T) == 2 ? 32 : 16;   // logit flush period (rows): 64 B
+  constexpr int LXP = 16;                         // lambda*x flush period: 64 B
+  constexpr int U = 32;                           // unroll (multiple of both periods)
+  constexpr int PF = sizeof(T) == 2 ? 8 : 4;      // prefetch distance (rows)
+  using P = Pair<T>;
+  const int H = a.H, W = a.W, G = a.G;
+  const int t = threadIdx.x;
+  const int c0 = 2 * t;
+  const bool act = c0 < W;
+  const int cl = act ? c0 : 0;                    // in-bounds column for idle threads
+  const int64_t plane = a.plane0 + blockIdx.x;
+  const int64_t base = plane * H * W;
+  const int n4 = W + 4;
+  for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
+  __syncthreads();
+  LineX lx{lbuf, n4, 0};
+  const float mA0 = c0 > 0 ? 1.f : 0.f;              // column c0 has a left neighbour
+  const float mB2 = c0 + 1 < W - 1 ? 1.f : 0.f;      // column c0+1 has a right neighbour
+  auto load_row = [&](int r) {
+    return load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, base + (int64_t)min(r, H - 1) * W + cl);
+  };
+
+  Raw2<T> ring[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) ring[j] = load_row(j);
+
+  float hA = 0.f, hB = 0.f;
+  FwdRestart rst{0, G};
+  float lxA[LXP], lxB[LXP];
+  uint32_t lgA[3][16], lgB[3][16];   // bf16: rows 2k (low half) and 2k+1 (high half)
+  float lgAf[3][16], lgBf[3][16];    // fp32
+  const int64_t cbase = (plane * W + c0) * a.Hp;   // column c0 of this plane in the copy
+
+  auto block = [&](int r0, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int r = r0 + j;
+      if (!TAIL || r < H) {
+        const Raw2<T> v = ring[j % PF];
+        ring[j % PF] = load_row(r + PF);
+        const float lxa = P::lo(v.lam) * P::lo(v.x);
+        const float lxb = P::hi(v.lam) * P::hi(v.x);
+        if constexpr (SCAN) {
+          const bool restart = rst.at(r);
+          const float* pv = lx.cur();
+          const Rec ra = make_rec(P::lo(v.l0), P::lo(v.l1), P::lo(v.l2), lxa, mA0, 1.f);
+          const Rec rb = make_rec(P::hi(v.l0), P::hi(v.l1), P::hi(v.l2), lxb, 1.f, mB2);
+          const float na = mix(ra, pv[c0 + 1], hA, hB);
+          const float nb = mix(rb, hA, hB, pv[c0 + 4]);
+          hA = restart ? lxa : na;
+          hB = restart ? lxb : nb;
+          if (act) *reinterpret_cast<float2*>(lx.nxt() + c0 + 2) = make_float2(hA, hB);
+          lx.par ^= 1;
+          if ((j + 1) % kCkV == 0 && act)
+            store_pair(a.ckv, (plane * a.nckv + r / kCkV) * W + c0, hA, hB);
+          __syncthreads();
+        }
+        if constexpr (COPY) {
+          lxA[j % LXP] = lxa;
+          lxB[j % LXP] = lxb;
+          if constexpr (sizeof(T) == 2) {
+            const int q = (j % LGP) / 2;
+            const uint32_t g[3] = {v.l0, v.l1, v.l2};
+#pragma unroll
+            for (int z = 0; z < 3; ++z) {
+              // column c0 holds the low halves, column c0+1 the high halves
+              if (j % 2 == 0) {
+                lgA[z][q] = g[z] & 0xffffu;
+                lgB[z][q] = g[z] >> 16;
+              } else {
+                lgA[z][q] |= g[z] << 16;
+                lgB[z][q] |= g[z] & 0xffff0000u;
+              }
+            }
+          } else {
+            lgAf[0][j % 16] = P::lo(v.l0); lgAf[1][j % 16] = P::lo(v.l1); lgAf[2][j % 16] = P::lo(v.l2);
+            lgBf[0][j % 16] = P::hi(v.l0); lgBf[1][j % 16] = P::hi(v.l1); lgBf[2][j % 16] = P::hi(v.l2);
+          }
+        }
+      }
+      if constexpr (COPY) {
+        // flush full segments; the column pitch Hp is a multiple of 32, so a
+        // segment that runs past H lands in padding
+        if ((j % LXP) == LXP - 1 && act && (!TAIL || r0 + j - (LXP - 1) < H)) {
+          const int rs = r0 + j - (LXP - 1);
+          float4* dA = reinterpret_cast<float4*>(a.lxt + cbase + rs);
+          float4* dB = reinterpret_cast<float4*>(a.lxt + cbase + a.Hp + rs);
+#pragma unroll
+          for (int q = 0; q < LXP / 4; ++q) {
+            dA[q] = make_float4(lxA[4 * q], lxA[4 * q + 1], lxA[4 * q + 2], lxA[4 * q + 3]);
+            dB[q] = make_float4(lxB[4 * q], lxB[4 * q + 1], lxB[4 * q + 2], lxB[4 * q + 3]);
+          }
+        }
+        if ((j % LGP) == LGP - 1 && act && (!TAIL || r0 + j - (LGP - 1) < H)) {
+          const int rs = r0 + j - (LGP - 1);
+#pragma unroll
+          for (int z = 0; z < 3; ++z) {
+            T* g = a.lgt + z * a.lg_stride;
+            if constexpr (sizeof(T) == 2) {
+              uint4* dA = reinterpret_cast<uint4*>(g + cbase + rs);
+              uint4* dB = reinterpret_cast<uint4*>(g + cbase + a.Hp + rs);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                dA[q] = make_uint4(lgA[z][4 * q], lgA[z][4 * q + 1], lgA[z][4 * q + 2], lgA[z][4 * q + 3]);
+                dB[q] = make_uint4(lgB[z][4 * q], lgB[z][4 * q + 1], lgB[z][4 * q + 2], lgB[z][4 * q + 3]);
+              }
+            } else {
+              float4* dA = reinterpret_cast<float4*>(reinterpret_cast<float*>(g) + cbase + rs);
+              float4* dB = reinterpret_cast<float4*>(reinterpret_cast<float*>(g) + cbase + a.Hp + rs);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                dA[q] = make_float4(lgAf[z][4 * q], lgAf[z][4 * q + 1], lgAf[z][4 * q + 2], lgAf[z][4 * q + 3]);
+                dB[q] = make_float4(lgBf[z][4 * q], lgBf[z][4 * q + 1], lgBf[z][4 * q + 2], lgBf[z][4 * q + 3]);
+              }
+            }
+          }
+        }
+      }
+    }
+  };
+  int r0 = 0;
+  for (; r0 + U <= H; r0 += U) block(r0, std::false_type{});
+  if (r0 < H) block(r0, std::true_type{});
+}
+
+// ===========================================================================
+// K2: left->right and right->left on the column-major copy
+// ===========================================================================
+template <typename T, bool LR, bool RL>
+__global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
+  __shared__ float lbuf[2 * (2048 + 4)];
+  constexpr int PF = 8;
+  using P = Pair<T>;
+  const int H = a.H, W = a.W, G = a.G, Hp = a.Hp;
+  const int t = threadIdx.x;
+  const int o0 = 2 * t;                 // image rows o0, o0 + 1
+  const bool act = o0 < H;
+  const int ol = act ? o0 : 0;
+  const int64_t plane = a.plane0 + blockIdx.x;
+  const int64_t pb = plane * W * Hp;    // this plane in the copy
+  const int n4 = H + 4;
+  for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
+  __syncthreads();
+  LineX lx{lbuf, n4, 0};
+  const float mA0 = o0 > 0 ? 1.f : 0.f;
+  const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
+
+  struct In {
+    float2 lx;
+    typename P::raw g0, g1, g2;
+  };
+  auto load_in = [&](int c) {
+    In v;
+    const int64_t i = pb + (int64_t)min(max(c, 0), W - 1) * Hp + ol;
+    v.lx = *reinterpret_cast<const float2*>(a.lxt + i);
+    v.g0 = P::load(a.lgt, i);
+    v.g1 = P::load(a.lgt + a.lg_stride, i);
+    v.g2 = P::load(a.lgt + 2 * a.lg_stride, i);
+    return v;
+  };
+  auto recs = [&](const In& v, Rec& ra, Rec& rb) {
+    ra = make_rec(P::lo(v.g0), P::lo(v.g1), P::lo(v.g2), v.lx.x, mA0, 1.f);
+    rb = make_rec(P::hi(v.g0), P::hi(v.g1), P::hi(v.g2), v.lx.y, 1.f, mB2);
+  };
+  // one scan step on the line: the new pair is the mix of the previous line
+  // (or the restart value); publishes it and waits for the whole line
+  auto step = [&](const Rec& ra, const Rec& rb, bool restart, float& hA, float& hB) {
+    const float* pv = lx.cur();
+    const float na = mix(ra, pv[o0 + 1], hA, hB);
+    const float nb = mix(rb, hA, hB, pv[o0 + 4]);
+    hA = restart ? ra.lx : na;
+    hB = restart ? rb.lx : nb;
+    if (act) *reinterpret_cast<float2*>(lx.nxt() + o0 + 2) = make_float2(hA, hB);
+    lx.par ^= 1;
+    __syncthreads();
+  };
+  auto seed = [&](float hA, float hB) {
+    if (act) *reinterpret_cast<float2*>(lx.nxt() + o0 + 2) = make_float2(hA, hB);
+    lx.par ^= 1;
+    __syncthreads();
+  };
+
+  // ---- left->right: checkpoints, or the final sum when there is no reverse
+  if constexpr (LR) {
+    In ring[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) ring[j] = load_in(j);
+    float hA = 0.f, hB = 0.f;
+    FwdRestart rst{0, G};
+    auto block = [&](int cb, auto tail) {
+      constexpr bool TAIL = decltype(tail)::value;
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int c = cb + j;
+        if (!TAIL || c < W) {
+          const In v = ring[j];
+          ring[j] = load_in(c + PF);
+          Rec ra, rb;
+          recs(v, ra, rb);
+          step(ra, rb, rst.at(c), hA, hB);
+          if (act) {
+            if constexpr (RL) {
+              if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
+            } else {
+              store_pair(a.yht, pb + (int64_t)c * Hp + o0, hA, hB);
+            }
+          }
+        }
+      }
+    };
+    int cb = 0;
+    for (; cb + PF <= W; cb += PF) block(cb, std::false_type{});
+    if (cb < W) block(cb, std::true_type{});
+  }
+
+  // ---- right->left in chunks of kCkH columns, recomputing left->right -----
+  if constexpr (RL) {
+    struct Chunk {
+      In in[kCkH];
+      float2 ck;
+    };
+    auto load_chunk = [&](int k) {
+      Chunk ch;
+#pragma unroll
+      for (int i = 0; i < kCkH; ++i) ch.in[i] = load_in(k * kCkH + i);
+      ch.ck = make_float2(0.f, 0.f);
+      if constexpr (LR)
+        ch.ck = *reinterpret_cast<const float2*>(a.ckh + (plane * a.nckh + max(k - 1, 0)) * H + ol);
+      return ch;
+    };
+    float hrA = 0.f, hrB = 0.f;   // right->left state, carried across chunks
+    auto chunk = [&](const Chunk& ch, int k, auto tail) {
+      constexpr bool TAIL = decltype(tail)::value;
+      const int cs = k * kCkH;
+      Rec ra[kCkH], rb[kCkH];
+#pragma unroll
+      for (int i = 0; i < kCkH; ++i) recs(ch.in[i], ra[i], rb[i]);
+      float hlA[kCkH], hlB[kCkH];
+#pragma unroll
+      for (int i = 0; i < kCkH; ++i) { hlA[i] = 0.f; hlB[i] = 0.f; }
+      if constexpr (LR) {
+        float hA = k > 0 ? ch.ck.x : 0.f, hB = k > 0 ? ch.ck.y : 0.f;
+        seed(hA, hB);
+        FwdRestart rst{fwd_restart_from(cs, G), G};
+#pragma unroll
+        for (int i = 0; i < kCkH; ++i) {
+          if (!TAIL || cs + i < W) step(ra[i], rb[i], rst.at(cs + i), hA, hB);
+          hlA[i] = hA;
+          hlB[i] = hB;
+        }
+      }
+      seed(hrA, hrB);
+      RevRestart rst = rev_counter(min(cs + kCkH - 1, W - 1), W, G);
+#pragma unroll
+      for (int i = kCkH - 1; i >= 0; --i) {
+        const int c = cs + i;
+        if (!TAIL || c < W) {
+          step(ra[i], rb[i], rst.at(c), hrA, hrB);
+          if (act) store_pair(a.yht, pb + (int64_t)c * Hp + o0, hlA[i] + hrA, hlB[i] + hrB);
+        }
+      }
+    };
+    int k = (W + kCkH - 1) / kCkH - 1;
+    Chunk nxt = load_chunk(k);
+    if (W % kCkH) {
+      const Chunk cur = nxt;
+      nxt = load_chunk(max(k - 1, 0));
+      chunk(cur, k, std::true_type{});
+      --k;
+    }
+    for (; k >= 0; --k) {
+      const Chunk cur = nxt;
+      nxt = load_chunk(max(k - 1, 0));
+      chunk(cur, k, std::false_type{});
+    }
+  }
+}
+
+// ===========================================================================
+// K3: bottom->top with top->bottom recomputed per chunk, merge, output
+// ===========================================================================
+template <typename T, bool TB, bool BT, bool HZ>
+__global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
+  __shared__ float lbuf[2 * (1024 + 4)];
+  using P = Pair<T>;
+  const int H = a.H, W = a.W, G = a.G, Hp = a.Hp;
+  const int t = threadIdx.x;
+  const int c0 = 2 * t;
+  const bool act = c0 < W;
+  const int cl = act ? c0 : 0;
+  const int64_t plane = a.plane0 + blockIdx.x;
+  const int64_t base = plane * H * W;
+  const int n4 = W + 4;
+  for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
+  __syncthreads();
+  LineX lx{lbuf, n4, 0};
+  const float mA0 = c0 > 0 ? 1.f : 0.f;
+  const float mB2 = c0 + 1 < W - 1 ? 1.f : 0.f;
+  const int64_t cb = (plane * W + cl) * Hp;   // column c0 in the horizontal sum
+
+  struct Chunk {
+    Raw2<T> in[kCkV];
+    typename P::raw u[kCkV];
+    float4 yA[2], yB[2];
+    float2 ck;
+  };
+  auto load_chunk = [&](int k) {
+    Chunk ch;
+    const int rs = k * kCkV;
+#pragma unroll
+    for (int i = 0; i < kCkV; ++i) {
+      const int64_t idx = base + (int64_t)min(rs + i, H - 1) * W + cl;
+      ch.in[i] = load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, idx);
+      ch.u[i] = P::load(a.u, idx);
+    }
+    if constexpr (HZ) {
+      ch.yA[0] = *reinterpret_cast<const float4*>(a.yht + cb + rs);
+      ch.yA[1] = *reinterpret_cast<const float4*>(a.yht + cb + rs + 4);
+      ch.yB[0] = *reinterpret_cast<const float4*>(a.yht + cb + Hp + rs);
+      ch.yB[1] = *reinterpret_cast<const float4*>(a.yht + cb + Hp + rs + 4);
+    } else {
+      ch.yA[0] = ch.yA[1] = ch.yB[0] = ch.yB[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ch.ck = make_float2(0.f, 0.f);
+    if constexpr (TB)
+      ch.ck = *reinterpret_cast<const float2*>(a.ckv + (plane * a.nckv + max(k - 1, 0)) * W + cl);
+    return ch;
+  };
+  auto step = [&](const Rec& ra, const Rec& rb, bool restart, float& hA, float& hB) {
+    const float* pv = lx.cur();
+    const float na = mix(ra, pv[c0 + 1], hA, hB);
+    const float nb = mix(rb, hA, hB, pv[c0 + 4]);
+    hA = restart ? ra.lx : na;
+    hB = restart ? rb.lx : nb;
+    if (act) *reinterpret_cast<float2*>(lx.nxt() + c0 + 2) = make_float2(hA, hB);
+    lx.par ^= 1;
+    __syncthreads();
+  };
+  auto seed = [&](float hA, float hB) {
+    if (act) *reinterpret_cast<float2*>(lx.nxt() + c0 + 2) = make_float2(hA, hB);
+    lx.par ^= 1;
+    __syncthreads();
+  };
+  auto pick = [](const float4* y, int i) {
+    const float4 q = y[i / 4];
+    const int m = i % 4;
+    return m == 0 ? q.x : (m == 1 ? q.y : (m == 2 ? q.z : q.w));
+  };
+
+  float hbA = 0.f, hbB = 0.f;   // bottom->top state, carried across chunks
+  auto chunk = [&](const Chunk& ch, int k, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const int rs = k * kCkV;
+    Rec ra[kCkV], rb[kCkV];
+#pragma unroll
+    for (int i = 0; i < kCkV; ++i) {
+      const Raw2<T>& v = ch.in[i];
+      ra[i] = make_rec(P::lo(v.l0), P::lo(v.l1), P::lo(v.l2), P::lo(v.lam) * P::lo(v.x), mA0, 1.f);
+      rb[i] = make_rec(P::hi(v.l0), P::hi(v.l1), P::hi(v.l2), P::hi(v.lam) * P::hi(v.x), 1.f, mB2);
+    }
+    float htA[kCkV], htB[kCkV];
+#pragma unroll
+    for (int i = 0; i < kCkV; ++i) { htA[i] = 0.f; htB[i] = 0.f; }
+    if constexpr (TB) {
+      float hA = k > 0 ? ch.ck.x : 0.f, hB = k > 0 ? ch.ck.y : 0.f;
+      seed(hA, hB);
+      FwdRestart rst{fwd_restart_from(rs, G), G};
+#pragma unroll
+      for (int i = 0; i < kCkV; ++i) {
+        if (!TAIL || rs + i < H) step(ra[i], rb[i], rst.at(rs + i), hA, hB);
+        htA[i] = hA;
+        htB[i] = hB;
+      }
+    }
+    if constexpr (BT) seed(hbA, hbB);
+    RevRestart rst = rev_counter(min(rs + kCkV - 1, H - 1), H, G);
+#pragma unroll
+    for (int i = kCkV - 1; i >= 0; --i) {
+      const int r = rs + i;
+      if (!TAIL || r < H) {
+        float sA = htA[i] + pick(ch.yA, i), sB = htB[i] + pick(ch.yB, i);
+        if constexpr (BT) {
+          step(ra[i], rb[i], rst.at(r), hbA, hbB);
+          sA += hbA;
+          sB += hbB;
+        }
+        if (act)
+          store_pair(a.out, base + (int64_t)r * W + c0, P::lo(ch.u[i]) * sA, P::hi(ch.u[i]) * sB);
+      }
+    }
+  };
+  int k = (H + kCkV - 1) / kCkV - 1;
+  Chunk nxt = load_chunk(k);
+  if (H % kCkV) {
+    const Chunk cur = nxt;
+    nxt = load_chunk(max(k - 1, 0));
+    chunk(cur, k, std::true_type{});
+    --k;
+  }
+  for (; k >= 0; --k) {
+    const Chunk cur = nxt;
+    nxt = load_chunk(max(k - 1, 0));
+    chunk(cur, k, std::false_type{});
+  }
+}
+
+// ---------------------------------------------------------------------------
+bool tpipe_fits(int64_t H, int64_t W) {
+  return H >= 2 && W >= 2 && H % 2 == 0 && W % 2 == 0 && W <= 1024 && H <= 2048;
+}
+
+namespace {
+struct TpLayout {
+  int64_t Hp, nckv, nckh;
+  size_t off_lxt, off_lgt, off_yht, off_ckv, off_ckh, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+TpLayout tp_layout(int64_t planes, int64_t H, int64_t W, size_t es) {
+  TpLayout L;
+  L.Hp = (H + 31) / 32 * 32;
+  L.nckv = (H + kCkV - 1) / kCkV;
+  L.nckh = (W + kCkH - 1) / kCkH;
+  const size_t cp = static_cast<size_t>(planes * W * L.Hp);
+  size_t o = 0;
+  L.off_lxt = o; o = align256(o + cp * 4);
+  L.off_lgt = o; o = align256(o + 3 * cp * es);
+  L.off_yht = o; o = align256(o + cp * 4);
+  L.off_ckv = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * 4);
+  L.off_ckh = o; o = align256(o + static_cast<size_t>(planes * L.nckh * H) * 4);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+namespace {
+// compute units of the current device (cached per device)
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// one non-blocking, default-priority helper stream per device, created on
+// first use and kept for the life of the process
+hipStream_t aux_stream() {
+  static std::mutex mu;
+  static hipStream_t cache[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev] && hipStreamCreateWithFlags(&cache[dev], hipStreamNonBlocking) != hipSuccess)
+    cache[dev] = nullptr;
+  return cache[dev];
+}
+
+// 1 or 2 plane groups (GSPN_TPIPE_GROUPS=1|2 overrides, for measurements)
+int tpipe_groups(int64_t planes) {
+  if (const char* v = std::getenv("GSPN_TPIPE_GROUPS")) {
+    if (!std::strcmp(v, "1")) return 1;
+    if (!std::strcmp(v, "2")) return planes >= 2 ? 2 : 1;
+  }
+  const int cus = cu_count();
+  return (planes > cus && planes < 2 * cus) ? 2 : 1;
+}
+}  // namespace
+
+size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt) {
+  return tp_layout(planes, H, W, dt == GSPN_F32 ? 4 : 2).total;
+}
+
+template <typename T>
+static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+  const int64_t planes = pr.B * pr.C;
+  const TpLayout L = tp_layout(planes, pr.H, pr.W, sizeof(T));
+  char* w = static_cast<char*>(ws);
+  TpArgs<T> a;
+  a.x = static_cast<const T*>(pr.x);
+  a.lam = static_cast<const T*>(pr.lam);
+  a.l0 = static_cast<const T*>(pr.l[0]);
+  a.l1 = static_cast<const T*>(pr.l[1]);
+  a.l2 = static_cast<const T*>(pr.l[2]);
+  a.u = static_cast<const T*>(pr.u);
+  a.out = static_cast<T*>(pr.out);
+  a.lxt = reinterpret_cast<float*>(w + L.off_lxt);
+  a.lgt = reinterpret_cast<T*>(w + L.off_lgt);
+  a.yht = reinterpret_cast<float*>(w + L.off_yht);
+  a.ckv = reinterpret_cast<float*>(w + L.off_ckv);
+  a.ckh = reinterpret_cast<float*>(w + L.off_ckh);
+  a.H = static_cast<int>(pr.H);
+  a.W = static_cast<int>(pr.W);
+  a.G = static_cast<int>(pr.G >= pr.H && pr.G >= pr.W ? 0 : pr.G);
+  a.Hp = static_cast<int>(L.Hp);
+  a.nckv = static_cast<int>(L.nckv);
+  a.nckh = static_cast<int>(L.nckh);
+  a.mask = pr.mask;
+  a.lg_stride = planes * pr.W * L.Hp;
+  a.plane0 = 0;
+  const unsigned tv = static_cast<unsigned>((pr.W / 2 + 63) / 64 * 64);
+  const unsigned th = static_cast<unsigned>((pr.H / 2 + 63) / 64 * 64);
+  const unsigned m = pr.mask;
+  const bool tb = m & 1u, bt = m & 2u, lr = m & 4u, rl = m & 8u, hz = lr || rl;
+  using K = void (*)(TpArgs<T>);
+  const K k1 = tb ? (hz ? tp_vfwd<T, true, true> : tp_vfwd<T, true, false>) : tp_vfwd<T, false, true>;
+  const K k2 = lr ? (rl ? tp_hpair<T, true, true> : tp_hpair<T, true, false>) : tp_hpair<T, false, true>;
+  static const K k3s[8] = {tp_vbwd<T, false, false, false>, tp_vbwd<T, true, false, false>,
+                           tp_vbwd<T, false, true, false>, tp_vbwd<T, true, true, false>,
+                           tp_vbwd<T, false, false, true>, tp_vbwd<T, true, false, true>,
+                           tp_vbwd<T, false, true, true>, tp_vbwd<T, true, true, true>};
+  const K k3 = k3s[(tb ? 1 : 0) | (bt ? 2 : 0) | (hz ? 4 : 0)];
+
+  // Every kernel needs one whole compute unit per plane, so a plane count a
+  // little above the CU count leaves a latency-bound second round. Two plane
+  // groups on two streams let one group's K2/K3 overlap the other's tail.
+  const int ngroups = tpipe_groups(planes);
+  hipStream_t streams[2] = {stream, stream};
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t e;
+  if (ngroups == 2) {
+    streams[1] = aux_stream();
+    if (!streams[1]) return hipErrorOutOfMemory;
+    if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess) {
+      (void)hipEventDestroy(fork);
+      return e;
+    }
+    if ((e = hipEventRecord(fork, stream)) == hipSuccess) e = hipStreamWaitEvent(streams[1], fork, 0);
+    if (e != hipSuccess) {
+      (void)hipEventDestroy(fork);
+      (void)hipEventDestroy(join);
+      return e;
+    }
+  }
+  const int64_t split = ngroups == 2 ? planes / 2 : planes;
+  const int64_t g0[2] = {0, split}, gn[2] = {split, planes - split};
+  auto launch = [&](K k, unsigned threads, const char* name, int g) -> hipError_t {
+    if (gn[g] == 0) return hipSuccess;
+    TpArgs<T> ag = a;
+    ag.plane0 = g0[g];
+    tr->before(streams[g], name, gn[g]);
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(gn[g])), dim3(threads), 0, streams[g], ag);
+    tr->after(streams[g]);
+    return hipGetLastError();
+  };
+  e = hipSuccess;
+  for (int g = 0; g < ngroups && e == hipSuccess; ++g)
+    if (tb || hz) e = launch(k1, tv, "tp_vfwd", g);
+  for (int g = 0; g < ngroups && e == hipSuccess; ++g)
+    if (hz) e = launch(k2, th, "tp_hpair", g);
+  for (int g = 0; g < ngroups && e == hipSuccess; ++g) e = launch(k3, tv, "tp_vbwd", g);
+  if (ngroups == 2) {
+    hipError_t e2 = hipEventRecord(join, streams[1]);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, join, 0);
+    (void)hipEventDestroy(fork);
+    (void)hipEventDestroy(join);
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
+}
+
+hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_tpipe_dt<float>(pr, ws, stream, tr);
+  return launch_tpipe_dt<bf16_t>(pr, ws, stream, tr);
+}
+
+}  // namespace gspn

@@ -88,7 +88,8 @@ def test_empty_batch_is_ok_without_gpu(L):
     assert call(L, C=0, use_ws=True) == 0
 
 
-def test_workspace_checks(L):
+def test_workspace_checks(L, monkeypatch):
+    monkeypatch.setenv("GSPN_FORCE_PLAN", "stream")
     need = L.gspn_workspace_bytes(2, 3, 300, 200, 15, 0, 0)
     assert need == 2 * 3 * 300 * 200 * 4
     assert call(L, B=2, C=3, H=300, W=200, use_ws=True) == g.STATUS["GSPN_E_WORKSPACE"]
@@ -100,12 +101,21 @@ def test_workspace_checks(L):
                 ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]
 
 
-def test_workspace_and_plans(L):
+def test_workspace_and_plans(L, monkeypatch):
     assert g.workspace_bytes(64, 96, 56, 56) == 0
     assert g.plan_name(64, 96, 56, 56) == "plane64"
     assert g.plan_name(32, 1152, 16, 16, dtype=1) == "plane16"
     assert g.plan_name(1, 1, 16, 17) == "plane64"
-    assert g.plan_name(1, 1, 65, 8) != "plane64"
-    assert g.workspace_bytes(1, 2, 100, 100, dirs=g.T2B) == 0
+    assert g.plan_name(1, 1, 65, 8) == "stream"          # odd H: no pair kernels
+    assert g.plan_name(1, 320, 2048, 1024, dtype=1) == "tpipe"
+    assert g.plan_name(16, 192, 128, 128, group_rows=8) == "tpipe"
+    assert g.plan_name(1, 1, 100, 2048) == "stream"       # W above the pair-kernel limit
+    assert g.workspace_bytes(1, 2, 100, 100) > 0
     assert g.plan_name(1, 1, 0, 5) == "invalid"
     assert g.workspace_bytes(1, 1, 0, 5) == 0
+    monkeypatch.setenv("GSPN_FORCE_PLAN", "stream")
+    assert g.plan_name(1, 2, 8, 8) == "stream"
+    assert g.workspace_bytes(1, 2, 100, 100, dirs=g.T2B) == 0
+    monkeypatch.setenv("GSPN_FORCE_PLAN", "tpipe")
+    assert g.plan_name(1, 2, 8, 8) == "tpipe"
+    assert g.plan_name(1, 2, 7, 8) == "plane16"           # tpipe needs even sizes

@@ -113,14 +113,21 @@ def test_one_hot_middle_weight(shape):
 
 @pytest.mark.parametrize("shape,dtype", [((4, 8, 56, 56), torch.float32),
                                          ((2, 16, 16, 16), torch.bfloat16),
-                                         ((1, 3, 300, 200), torch.bfloat16)])
+                                         ((1, 3, 300, 200), torch.bfloat16),
+                                         ((1, 4, 96, 300), torch.float32),
+                                         ((1, 4, 128, 300), torch.bfloat16)])
 def test_deterministic(shape, dtype):
+    """Bitwise-identical repeats (no atomics; catches LDS races between
+    steps, e.g. with idle threads in a partly filled workgroup)."""
     B, C, H, W = shape
     w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
     inp = make_inputs(w, seed=2, B=B, C=C, H=H, W=W)
     a = run(inp, 15, 0)
-    b = run(inp, 15, 0)
-    assert torch.equal(a, b)
+    for mask in (15, 1, 8):
+        ref = run(inp, mask, 0)
+        for _ in range(3):
+            assert torch.equal(run(inp, mask, 0), ref)
+    assert torch.equal(run(inp, 15, 0), a)
 
 
 def test_alloc_entry_point_matches_workspace_entry_point():
@@ -150,3 +157,31 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(g.GspnError) as ei:
         g.propagate(x, (x, x, x), x, x, dirs=0)
     assert ei.value.name == "GSPN_E_DIRMASK"
+
+
+FORCED_SHAPES = [(1, 2, 2, 2), (1, 2, 8, 8), (2, 3, 16, 32), (1, 2, 66, 40), (1, 1, 130, 96),
+                 (1, 2, 40, 130), (2, 1, 48, 1024), (1, 1, 2048, 64)]
+
+
+@pytest.fixture
+def force_plan(monkeypatch):
+    def _set(name):
+        monkeypatch.setenv("GSPN_FORCE_PLAN", name)
+    return _set
+
+
+@pytest.mark.parametrize("plan", ["tpipe", "stream"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", FORCED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forced_plan(force_plan, plan, shape, dtype):
+    """Each large-plane path on small and odd-sized planes, every direction
+    subset family, global and local."""
+    force_plan(plan)
+    B, C, H, W = shape
+    assert g.plan_name(B, C, H, W, 15, 0, 0 if dtype == torch.float32 else 1) == plan
+    w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=(H * 31 + W) % 997, B=B, C=C, H=H, W=W)
+    for mask in (15, 1, 2, 3, 4, 8, 12, 5, 10):
+        for G in ((0, 3, 8) if mask == 15 else (0,)):
+            out = run(inp, mask, G)
+            assert_parity(out, oracle_y(inp, mask, G), f"{plan} {shape} mask={mask} G={G}")
