@@ -152,6 +152,30 @@ def cpu_baseline(inp_dev, w, planes: int):
                       f"{steps} elem-steps in {dt:.2f} s"}
 
 
+def calibrate(torch, reps: int) -> int:
+    """Plain copy of a 4 GiB buffer (4 GiB read + 4 GiB written per call) and
+    a sum over it (4 GiB read), timed with events; one JSON line."""
+    n = 1 << 30                      # float32 elements = 4 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    res = {"copy_bytes_per_call": 2 * 4 * n, "read_bytes_per_call": 4 * n}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 8 * n),
+                             ("read", lambda: src.sum(), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"{name}_ms"] = ms
+        res[f"{name}_gbs"] = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +185,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough wall time of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time a plain device copy and a read-only reduction of known size "
+                         "(the reference points for HBM bandwidth and for counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -170,6 +197,9 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.calibrate:
+        return calibrate(torch, args.steps)
 
     import linear_spatial_propagation_line_amd as g
     from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs

@@ -30,6 +30,7 @@
 // Line recurrence, output gate: CSDN page on GSPN, section 方法; tridiagonal
 // row-normalised sigmoid weights and four scan directions: section
 // 如何设计一个高效的传播层; local groups: section GSPN模块的设计.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -65,6 +66,30 @@ template <> struct Pair<bf16_t> {
   }
   __device__ static float lo(raw v) { return bf16_lo(v); }
   __device__ static float hi(raw v) { return bf16_hi(v); }
+};
+
+// four elements (rows o, o+1 of a column pair) of the copy
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+  using raw = float4;
+  __device__ static raw load(const float* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
+  // values of column `odd` of the pair for the two rows
+  __device__ static void split(raw v, int odd, float out[2]) {
+    out[0] = odd ? v.y : v.x;
+    out[1] = odd ? v.w : v.z;
+  }
+};
+template <> struct Quad<bf16_t> {
+  using raw = uint2;
+  __device__ static raw load(const bf16_t* p, int64_t i) {
+    return *reinterpret_cast<const uint2*>(p + i);
+  }
+  __device__ static void split(raw v, int odd, float out[2]) {
+    out[0] = odd ? bf16_hi(v.x) : bf16_lo(v.x);
+    out[1] = odd ? bf16_hi(v.y) : bf16_lo(v.y);
+  }
 };
 
 __device__ __forceinline__ void store_pair(float* p, int64_t i, float a, float b) {
@@ -168,9 +193,9 @@ struct TpArgs {
   const T* l2;
   const T* u;
   T* out;
-  float* lxt;     // [planes][W][Hp]   lambda*x, column-major
-  T* lgt;         // [3][planes][W][Hp] logits, column-major
-  float* yht;     // [planes][W][Hp]   h_L2R + h_R2L, column-major
+  float* lxt;     // [planes][W/2][Hp][2] lambda*x, column-major by column pairs
+  T* lgt;         // [3][planes][W/2][Hp][2] logits, same layout
+  float* yht;     // [planes][nckv][W][8] h_L2R + h_R2L, in 8-row chunks
   float* ckv;     // [planes][nckv][W] top->bottom states after rows 8k+7
   float* ckh;     // [planes][nckh][H] left->right states after columns 4k+3
   int H, W, G, Hp, nckv, nckh;
@@ -217,10 +242,12 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
 
   float hA = 0.f, hB = 0.f;
   FwdRestart rst{0, G};
-  float lxA[LXP], lxB[LXP];
-  uint32_t lgA[3][16], lgB[3][16];   // bf16: rows 2k (low half) and 2k+1 (high half)
-  float lgAf[3][16], lgBf[3][16];    // fp32
-  const int64_t cbase = (plane * W + c0) * a.Hp;   // column c0 of this plane in the copy
+  // copy buffers, kept in the copy's pair-interleaved layout: per row, the
+  // values of columns c0 and c0+1 side by side
+  float2 lxP[LXP];
+  typename P::raw lgP[3][LGP];
+  // this thread's column pair in the copy ([plane][W/2][Hp][2])
+  const int64_t pbase = ((plane * (W / 2) + t) * a.Hp) * 2;
 
   auto block = [&](int r0, auto tail) {
     constexpr bool TAIL = decltype(tail)::value;
@@ -248,62 +275,38 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
           __syncthreads();
         }
         if constexpr (COPY) {
-          lxA[j % LXP] = lxa;
-          lxB[j % LXP] = lxb;
-          if constexpr (sizeof(T) == 2) {
-            const int q = (j % LGP) / 2;
-            const uint32_t g[3] = {v.l0, v.l1, v.l2};
-#pragma unroll
-            for (int z = 0; z < 3; ++z) {
-              // column c0 holds the low halves, column c0+1 the high halves
-              if (j % 2 == 0) {
-                lgA[z][q] = g[z] & 0xffffu;
-                lgB[z][q] = g[z] >> 16;
-              } else {
-                lgA[z][q] |= g[z] << 16;
-                lgB[z][q] |= g[z] & 0xffff0000u;
-              }
-            }
-          } else {
-            lgAf[0][j % 16] = P::lo(v.l0); lgAf[1][j % 16] = P::lo(v.l1); lgAf[2][j % 16] = P::lo(v.l2);
-            lgBf[0][j % 16] = P::hi(v.l0); lgBf[1][j % 16] = P::hi(v.l1); lgBf[2][j % 16] = P::hi(v.l2);
-          }
+          lxP[j % LXP] = make_float2(lxa, lxb);
+          lgP[0][j % LGP] = v.l0;
+          lgP[1][j % LGP] = v.l1;
+          lgP[2][j % LGP] = v.l2;
         }
       }
       if constexpr (COPY) {
-        // flush full segments; the column pitch Hp is a multiple of 32, so a
-        // segment that runs past H lands in padding
+        // flush whole 128-byte runs (16 rows of lambda*x pairs, 32 rows of
+        // bf16 logit pairs or 16 of fp32); the row pitch Hp is a multiple of
+        // 32, so a run that passes H lands in padding
         if ((j % LXP) == LXP - 1 && act && (!TAIL || r0 + j - (LXP - 1) < H)) {
           const int rs = r0 + j - (LXP - 1);
-          float4* dA = reinterpret_cast<float4*>(a.lxt + cbase + rs);
-          float4* dB = reinterpret_cast<float4*>(a.lxt + cbase + a.Hp + rs);
+          float4* d = reinterpret_cast<float4*>(a.lxt + pbase + 2 * rs);
 #pragma unroll
-          for (int q = 0; q < LXP / 4; ++q) {
-            dA[q] = make_float4(lxA[4 * q], lxA[4 * q + 1], lxA[4 * q + 2], lxA[4 * q + 3]);
-            dB[q] = make_float4(lxB[4 * q], lxB[4 * q + 1], lxB[4 * q + 2], lxB[4 * q + 3]);
-          }
+          for (int q = 0; q < LXP / 2; ++q)
+            d[q] = make_float4(lxP[2 * q].x, lxP[2 * q].y, lxP[2 * q + 1].x, lxP[2 * q + 1].y);
         }
         if ((j % LGP) == LGP - 1 && act && (!TAIL || r0 + j - (LGP - 1) < H)) {
           const int rs = r0 + j - (LGP - 1);
 #pragma unroll
           for (int z = 0; z < 3; ++z) {
-            T* g = a.lgt + z * a.lg_stride;
+            T* g = a.lgt + z * a.lg_stride + pbase + 2 * rs;
             if constexpr (sizeof(T) == 2) {
-              uint4* dA = reinterpret_cast<uint4*>(g + cbase + rs);
-              uint4* dB = reinterpret_cast<uint4*>(g + cbase + a.Hp + rs);
+              uint4* d = reinterpret_cast<uint4*>(g);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                dA[q] = make_uint4(lgA[z][4 * q], lgA[z][4 * q + 1], lgA[z][4 * q + 2], lgA[z][4 * q + 3]);
-                dB[q] = make_uint4(lgB[z][4 * q], lgB[z][4 * q + 1], lgB[z][4 * q + 2], lgB[z][4 * q + 3]);
-              }
+              for (int q = 0; q < LGP / 4; ++q)
+                d[q] = make_uint4(lgP[z][4 * q], lgP[z][4 * q + 1], lgP[z][4 * q + 2], lgP[z][4 * q + 3]);
             } else {
-              float4* dA = reinterpret_cast<float4*>(reinterpret_cast<float*>(g) + cbase + rs);
-              float4* dB = reinterpret_cast<float4*>(reinterpret_cast<float*>(g) + cbase + a.Hp + rs);
+              float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                dA[q] = make_float4(lgAf[z][4 * q], lgAf[z][4 * q + 1], lgAf[z][4 * q + 2], lgAf[z][4 * q + 3]);
-                dB[q] = make_float4(lgBf[z][4 * q], lgBf[z][4 * q + 1], lgBf[z][4 * q + 2], lgBf[z][4 * q + 3]);
-              }
+              for (int q = 0; q < LGP / 2; ++q)
+                d[q] = make_float4(lgP[z][2 * q].x, lgP[z][2 * q].y, lgP[z][2 * q + 1].x, lgP[z][2 * q + 1].y);
             }
           }
         }
@@ -337,22 +340,43 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
   const float mA0 = o0 > 0 ? 1.f : 0.f;
   const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
 
-  struct In {
-    float2 lx;
-    typename P::raw g0, g1, g2;
+  // One load covers rows o0, o0+1 of the column pair (2 cp, 2 cp + 1): the
+  // copy stores, per row, both columns of a pair side by side.
+  using Q = Quad<T>;
+  struct In2 {
+    float4 lx;                          // (o0: even, odd), (o0+1: even, odd)
+    typename Q::raw g0, g1, g2;
   };
-  auto load_in = [&](int c) {
-    In v;
-    const int64_t i = pb + (int64_t)min(max(c, 0), W - 1) * Hp + ol;
-    v.lx = *reinterpret_cast<const float2*>(a.lxt + i);
-    v.g0 = P::load(a.lgt, i);
-    v.g1 = P::load(a.lgt + a.lg_stride, i);
-    v.g2 = P::load(a.lgt + 2 * a.lg_stride, i);
+  auto load_pair = [&](int cp) {
+    In2 v;
+    const int64_t i = ((plane * (W / 2) + min(max(cp, 0), W / 2 - 1)) * Hp + ol) * 2;
+    v.lx = *reinterpret_cast<const float4*>(a.lxt + i);
+    v.g0 = Q::load(a.lgt, i);
+    v.g1 = Q::load(a.lgt + a.lg_stride, i);
+    v.g2 = Q::load(a.lgt + 2 * a.lg_stride, i);
     return v;
   };
+  // the column (odd = 0: even column of the pair, 1: odd) as a per-row view
+  struct In {
+    float2 lx;
+    float g0[2], g1[2], g2[2];
+  };
+  auto column = [&](const In2& v, int odd) {
+    In c;
+    c.lx = odd ? make_float2(v.lx.y, v.lx.w) : make_float2(v.lx.x, v.lx.z);
+    Q::split(v.g0, odd, c.g0);
+    Q::split(v.g1, odd, c.g1);
+    Q::split(v.g2, odd, c.g2);
+    return c;
+  };
+  // the horizontal sum is stored in 8-row chunks, [plane][row / 8][column][8],
+  // so that the bottom->top kernel reads whole chunks contiguously
+  auto yidx = [&](int c) {
+    return ((plane * a.nckv + o0 / 8) * W + c) * 8 + (o0 % 8);
+  };
   auto recs = [&](const In& v, Rec& ra, Rec& rb) {
-    ra = make_rec(P::lo(v.g0), P::lo(v.g1), P::lo(v.g2), v.lx.x, mA0, 1.f);
-    rb = make_rec(P::hi(v.g0), P::hi(v.g1), P::hi(v.g2), v.lx.y, 1.f, mB2);
+    ra = make_rec(v.g0[0], v.g1[0], v.g2[0], v.lx.x, mA0, 1.f);
+    rb = make_rec(v.g0[1], v.g1[1], v.g2[1], v.lx.y, 1.f, mB2);
   };
   // one scan step on the line: the new pair is the mix of the previous line
   // (or the restart value); publishes it and waits for the whole line
@@ -374,27 +398,32 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
 
   // ---- left->right: checkpoints, or the final sum when there is no reverse
   if constexpr (LR) {
-    In ring[PF];
+    constexpr int PP = PF / 2;            // column pairs in flight
+    In2 ring[PP];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) ring[j] = load_in(j);
+    for (int j = 0; j < PP; ++j) ring[j] = load_pair(j);
     float hA = 0.f, hB = 0.f;
     FwdRestart rst{0, G};
     auto block = [&](int cb, auto tail) {
       constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int c = cb + j;
-        if (!TAIL || c < W) {
-          const In v = ring[j];
-          ring[j] = load_in(c + PF);
-          Rec ra, rb;
-          recs(v, ra, rb);
-          step(ra, rb, rst.at(c), hA, hB);
-          if (act) {
-            if constexpr (RL) {
-              if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
-            } else {
-              store_pair(a.yht, pb + (int64_t)c * Hp + o0, hA, hB);
+      for (int j = 0; j < PP; ++j) {
+        const int cp = cb / 2 + j;
+        if (!TAIL || 2 * cp < W) {
+          const In2 v2 = ring[j];
+          ring[j] = load_pair(cp + PP);
+#pragma unroll
+          for (int odd = 0; odd < 2; ++odd) {
+            const int c = 2 * cp + odd;
+            Rec ra, rb;
+            recs(column(v2, odd), ra, rb);
+            step(ra, rb, rst.at(c), hA, hB);
+            if (act) {
+              if constexpr (RL) {
+                if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
+              } else {
+                store_pair(a.yht, yidx(c), hA, hB);
+              }
             }
           }
         }
@@ -408,13 +437,13 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
   // ---- right->left in chunks of kCkH columns, recomputing left->right -----
   if constexpr (RL) {
     struct Chunk {
-      In in[kCkH];
+      In2 in[kCkH / 2];
       float2 ck;
     };
     auto load_chunk = [&](int k) {
       Chunk ch;
 #pragma unroll
-      for (int i = 0; i < kCkH; ++i) ch.in[i] = load_in(k * kCkH + i);
+      for (int i = 0; i < kCkH / 2; ++i) ch.in[i] = load_pair(k * (kCkH / 2) + i);
       ch.ck = make_float2(0.f, 0.f);
       if constexpr (LR)
         ch.ck = *reinterpret_cast<const float2*>(a.ckh + (plane * a.nckh + max(k - 1, 0)) * H + ol);
@@ -426,7 +455,7 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
       const int cs = k * kCkH;
       Rec ra[kCkH], rb[kCkH];
 #pragma unroll
-      for (int i = 0; i < kCkH; ++i) recs(ch.in[i], ra[i], rb[i]);
+      for (int i = 0; i < kCkH; ++i) recs(column(ch.in[i / 2], i % 2), ra[i], rb[i]);
       float hlA[kCkH], hlB[kCkH];
 #pragma unroll
       for (int i = 0; i < kCkH; ++i) { hlA[i] = 0.f; hlB[i] = 0.f; }
@@ -448,7 +477,7 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
         const int c = cs + i;
         if (!TAIL || c < W) {
           step(ra[i], rb[i], rst.at(c), hrA, hrB);
-          if (act) store_pair(a.yht, pb + (int64_t)c * Hp + o0, hlA[i] + hrA, hlB[i] + hrB);
+          if (act) store_pair(a.yht, yidx(c), hlA[i] + hrA, hlB[i] + hrB);
         }
       }
     };
@@ -488,7 +517,6 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
   LineX lx{lbuf, n4, 0};
   const float mA0 = c0 > 0 ? 1.f : 0.f;
   const float mB2 = c0 + 1 < W - 1 ? 1.f : 0.f;
-  const int64_t cb = (plane * W + cl) * Hp;   // column c0 in the horizontal sum
 
   struct Chunk {
     Raw2<T> in[kCkV];
@@ -506,10 +534,12 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
       ch.u[i] = P::load(a.u, idx);
     }
     if constexpr (HZ) {
-      ch.yA[0] = *reinterpret_cast<const float4*>(a.yht + cb + rs);
-      ch.yA[1] = *reinterpret_cast<const float4*>(a.yht + cb + rs + 4);
-      ch.yB[0] = *reinterpret_cast<const float4*>(a.yht + cb + Hp + rs);
-      ch.yB[1] = *reinterpret_cast<const float4*>(a.yht + cb + Hp + rs + 4);
+      // rows rs..rs+7 of columns c0, c0+1: 64 contiguous bytes
+      const float4* y = reinterpret_cast<const float4*>(a.yht + ((plane * a.nckv + k) * W + cl) * 8);
+      ch.yA[0] = y[0];
+      ch.yA[1] = y[1];
+      ch.yB[0] = y[2];
+      ch.yB[1] = y[3];
     } else {
       ch.yA[0] = ch.yA[1] = ch.yB[0] = ch.yB[1] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -618,7 +648,7 @@ TpLayout tp_layout(int64_t planes, int64_t H, int64_t W, size_t es) {
   size_t o = 0;
   L.off_lxt = o; o = align256(o + cp * 4);
   L.off_lgt = o; o = align256(o + 3 * cp * es);
-  L.off_yht = o; o = align256(o + cp * 4);
+  L.off_yht = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * 8 * 4);
   L.off_ckv = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * 4);
   L.off_ckh = o; o = align256(o + static_cast<size_t>(planes * L.nckh * H) * 4);
   L.total = o;
@@ -643,24 +673,26 @@ int cu_count() {
   return cache[dev];
 }
 
-// one non-blocking, default-priority helper stream per device, created on
-// first use and kept for the life of the process
-hipStream_t aux_stream() {
+// up to three non-blocking, default-priority helper streams per device,
+// created on first use and kept for the life of the process
+constexpr int kMaxGroups = 4;
+hipStream_t aux_stream(int i) {
   static std::mutex mu;
-  static hipStream_t cache[64] = {nullptr};
+  static hipStream_t cache[64][kMaxGroups - 1] = {};
   int dev = 0;
+  if (i < 0 || i >= kMaxGroups - 1) return nullptr;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   std::lock_guard<std::mutex> lk(mu);
-  if (!cache[dev] && hipStreamCreateWithFlags(&cache[dev], hipStreamNonBlocking) != hipSuccess)
-    cache[dev] = nullptr;
-  return cache[dev];
+  if (!cache[dev][i] && hipStreamCreateWithFlags(&cache[dev][i], hipStreamNonBlocking) != hipSuccess)
+    cache[dev][i] = nullptr;
+  return cache[dev][i];
 }
 
-// 1 or 2 plane groups (GSPN_TPIPE_GROUPS=1|2 overrides, for measurements)
+// number of plane groups (GSPN_TPIPE_GROUPS=1..4 overrides, for measurements)
 int tpipe_groups(int64_t planes) {
   if (const char* v = std::getenv("GSPN_TPIPE_GROUPS")) {
-    if (!std::strcmp(v, "1")) return 1;
-    if (!std::strcmp(v, "2")) return planes >= 2 ? 2 : 1;
+    const int n = std::atoi(v);
+    if (n >= 1 && n <= kMaxGroups) return static_cast<int>(std::min<int64_t>(n, planes));
   }
   const int cus = cu_count();
   return (planes > cus && planes < 2 * cus) ? 2 : 1;
@@ -715,26 +747,33 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   // little above the CU count leaves a latency-bound second round. Two plane
   // groups on two streams let one group's K2/K3 overlap the other's tail.
   const int ngroups = tpipe_groups(planes);
-  hipStream_t streams[2] = {stream, stream};
-  hipEvent_t fork = nullptr, join = nullptr;
-  hipError_t e;
-  if (ngroups == 2) {
-    streams[1] = aux_stream();
-    if (!streams[1]) return hipErrorOutOfMemory;
+  hipStream_t streams[kMaxGroups] = {stream, stream, stream, stream};
+  hipEvent_t fork = nullptr, join[kMaxGroups] = {};
+  hipError_t e = hipSuccess;
+  auto release = [&]() {
+    if (fork) (void)hipEventDestroy(fork);
+    for (int g = 1; g < ngroups; ++g)
+      if (join[g]) (void)hipEventDestroy(join[g]);
+  };
+  if (ngroups > 1) {
     if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess) {
-      (void)hipEventDestroy(fork);
-      return e;
+    for (int g = 1; g < ngroups && e == hipSuccess; ++g) {
+      streams[g] = aux_stream(g - 1);
+      if (!streams[g]) e = hipErrorOutOfMemory;
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&join[g], hipEventDisableTiming);
     }
-    if ((e = hipEventRecord(fork, stream)) == hipSuccess) e = hipStreamWaitEvent(streams[1], fork, 0);
+    if (e == hipSuccess) e = hipEventRecord(fork, stream);
+    for (int g = 1; g < ngroups && e == hipSuccess; ++g) e = hipStreamWaitEvent(streams[g], fork, 0);
     if (e != hipSuccess) {
-      (void)hipEventDestroy(fork);
-      (void)hipEventDestroy(join);
+      release();
       return e;
     }
   }
-  const int64_t split = ngroups == 2 ? planes / 2 : planes;
-  const int64_t g0[2] = {0, split}, gn[2] = {split, planes - split};
+  int64_t g0[kMaxGroups], gn[kMaxGroups];
+  for (int g = 0; g < ngroups; ++g) {
+    g0[g] = planes * g / ngroups;
+    gn[g] = planes * (g + 1) / ngroups - g0[g];
+  }
   auto launch = [&](K k, unsigned threads, const char* name, int g) -> hipError_t {
     if (gn[g] == 0) return hipSuccess;
     TpArgs<T> ag = a;
@@ -744,19 +783,17 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
     tr->after(streams[g]);
     return hipGetLastError();
   };
-  e = hipSuccess;
   for (int g = 0; g < ngroups && e == hipSuccess; ++g)
     if (tb || hz) e = launch(k1, tv, "tp_vfwd", g);
   for (int g = 0; g < ngroups && e == hipSuccess; ++g)
     if (hz) e = launch(k2, th, "tp_hpair", g);
   for (int g = 0; g < ngroups && e == hipSuccess; ++g) e = launch(k3, tv, "tp_vbwd", g);
-  if (ngroups == 2) {
-    hipError_t e2 = hipEventRecord(join, streams[1]);
-    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, join, 0);
-    (void)hipEventDestroy(fork);
-    (void)hipEventDestroy(join);
+  for (int g = 1; g < ngroups; ++g) {
+    hipError_t e2 = hipEventRecord(join[g], streams[g]);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, join[g], 0);
     if (e == hipSuccess) e = e2;
   }
+  release();
   return e;
 }
 
