@@ -1,10 +1,13 @@
 // Plane-resident GSPN propagation for planes with H, W <= 64.
 //
-// One workgroup of four wavefronts owns PPB = 64 / SEG whole planes:
-//   1. all threads stream x, lambda and the three logits of the planes from
-//      HBM (coalesced, vectorised) and turn every pixel into a record
-//      (w0, w1, w2, lambda*x) in LDS -- sigmoid + normalisation computed once
-//      per pixel and shared by all four directions;
+// A workgroup of four wavefronts owns PPB = 64 / SEG whole planes at a time
+// and loops over plane groups (a persistent grid sized to what fits on the
+// GPU at once):
+//   1. records: every pixel becomes (w0, w1, w2, lambda*x) in LDS -- sigmoid
+//      and normalisation computed once per pixel and shared by all four
+//      directions. The inputs come from registers filled by the previous
+//      iteration, and right after the records are built the loads of the next
+//      plane group are issued, so HBM transfers overlap steps 2-4;
 //   2. records for the edge lanes (orthogonal index 0 and n_o - 1, whose
 //      missing neighbour changes the normalisation) go to small side arrays;
 //   3. wavefront d runs scan direction d: lane o of a SEG-lane segment is
@@ -37,168 +40,242 @@ struct PlaneArgs {
   const T* u;
   T* out;
   int64_t nplanes;
+  int64_t ngroups;  // plane groups of PPB planes
   int H, W, G;
   unsigned mask;
   int pitch;        // records per LDS row (W rounded up to odd)
   float inv_W, inv_HW;
 };
 
-// vector loads of four consecutive elements
-__device__ __forceinline__ void load4(const float* p, int64_t i, float v[4]) {
-  const float4 q = *reinterpret_cast<const float4*>(p + i);
-  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-}
-__device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float v[4]) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p + i);
-  v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-}
-__device__ __forceinline__ void store4(float* p, int64_t i, const float v[4]) {
-  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void store4(bf16_t* p, int64_t i, const float v[4]) {
-  uint2 q;
-  q.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-  q.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-  *reinterpret_cast<uint2*>(p + i) = q;
-}
-__device__ __forceinline__ void load1(const float* p, int64_t i, float v[4]) { v[0] = p[i]; }
-__device__ __forceinline__ void load1(const bf16_t* p, int64_t i, float v[4]) { v[0] = to_f32(p[i]); }
-__device__ __forceinline__ void store1(float* p, int64_t i, const float v[4]) { p[i] = v[0]; }
-__device__ __forceinline__ void store1(bf16_t* p, int64_t i, const float v[4]) {
-  p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v[0]));
+// four consecutive elements, kept in their storage form until used
+template <typename T> struct V4;
+template <> struct V4<float> {
+  using raw = float4;
+  __device__ static raw load(const float* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
+  __device__ static float get(const raw& v, int e) {
+    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+  }
+  __device__ static void store(float* p, int64_t i, const float v[4]) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct V4<bf16_t> {
+  using raw = uint2;
+  __device__ static raw load(const bf16_t* p, int64_t i) {
+    return *reinterpret_cast<const uint2*>(p + i);
+  }
+  __device__ static float get(const raw& v, int e) {
+    const uint32_t w = e < 2 ? v.x : v.y;
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  __device__ static void store(bf16_t* p, int64_t i, const float v[4]) {
+    uint2 q;
+    q.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    q.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p + i) = q;
+  }
+};
+
+__device__ __forceinline__ float ld1(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld1(const bf16_t* p, int64_t i) { return to_f32(p[i]); }
+__device__ __forceinline__ void st1(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st1(bf16_t* p, int64_t i, float v) {
+  p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
 
 template <typename T, int SEG, int VEC>
 __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
   constexpr int PPB = 64 / SEG;
+  // pixels per thread handled in 4-wide vectors: up to 4096 (SEG 64) or 1024
+  // (SEG 16) pixels per plane group over 256 threads
+  constexpr int NIT = VEC == 4 ? (SEG == 64 ? 4 : 1) : 1;
+  using V = V4<T>;
   extern __shared__ float4 smem[];
   float* smem_f = reinterpret_cast<float*>(smem);
 
   const int H = a.H, W = a.W, pitch = a.pitch;
   const int HW = H * W;
-  const int64_t plane0 = static_cast<int64_t>(blockIdx.x) * PPB;
-  const int np = static_cast<int>(min<int64_t>(PPB, a.nplanes - plane0));
   const int rec_sz = PPB * H * pitch;          // records (float4 units)
   const int ev_off = rec_sz;                   // [PPB][2][H]
   const int eh_off = ev_off + PPB * 2 * H;     // [PPB][2][W]
   const int zero_off = eh_off + PPB * 2 * W;   // one zero record
-  const int64_t gbase = plane0 * HW;
-  const int npix = np * HW;
   const int tid = threadIdx.x;
 
-  // ---- 1. records ----------------------------------------------------------
-  for (int i0 = tid * VEC; i0 < npix; i0 += 256 * VEC) {
-    float x[4], lm[4], g0[4], g1[4], g2[4];
+  // registers filled one iteration ahead (VEC == 4 only)
+  typename V::raw rx[NIT], rl[NIT], r0[NIT], r1[NIT], r2[NIT], ru[NIT];
+  auto issue = [&](int64_t grp) {
+    const int64_t gb = grp * PPB * HW;
+    const int npx = static_cast<int>(min<int64_t>(PPB, a.nplanes - grp * PPB)) * HW;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i0 = tid * 4 + it * 1024;
+      const int64_t gi = gb + (i0 < npx ? i0 : 0);   // always in bounds
+      rx[it] = V::load(a.x, gi);
+      rl[it] = V::load(a.lam, gi);
+      r0[it] = V::load(a.l0, gi);
+      r1[it] = V::load(a.l1, gi);
+      r2[it] = V::load(a.l2, gi);
+      ru[it] = V::load(a.u, gi);
+    }
+  };
+  if constexpr (VEC == 4)
+    if (static_cast<int64_t>(blockIdx.x) < a.ngroups) issue(blockIdx.x);
+
+  for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+    const int64_t plane0 = grp * PPB;
+    const int np = static_cast<int>(min<int64_t>(PPB, a.nplanes - plane0));
+    const int64_t gbase = plane0 * HW;
+    const int npix = np * HW;
+
+    // ---- 1. records --------------------------------------------------------
+    typename V::raw uu[NIT];
     if constexpr (VEC == 4) {
-      load4(a.x, gbase + i0, x); load4(a.lam, gbase + i0, lm);
-      load4(a.l0, gbase + i0, g0); load4(a.l1, gbase + i0, g1); load4(a.l2, gbase + i0, g2);
-    } else {
-      load1(a.x, gbase + i0, x); load1(a.lam, gbase + i0, lm);
-      load1(a.l0, gbase + i0, g0); load1(a.l1, gbase + i0, g1); load1(a.l2, gbase + i0, g2);
-    }
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      int rem, c;
-      const int p = div_small(i0 + e, HW, a.inv_HW, &rem);
-      const int r = div_small(rem, W, a.inv_W, &c);
-      const Weights w = make_weights(g0[e], g1[e], g2[e], 1.0f, 1.0f);
-      smem[(p * H + r) * pitch + c] = make_float4(w.w0, w.w1, w.w2, lm[e] * x[e]);
-    }
-  }
-  if (tid == 0) smem[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();
-
-  // ---- 2. edge-lane records ------------------------------------------------
-  // vertical scans: lanes c = 0 (e = 0) and c = W-1 (e = 1), masks on c;
-  // horizontal scans: lanes r = 0 and r = H-1, masks on r.
-  const int n_ev = np * 2 * H, n_eh = np * 2 * W;
-  for (int k = tid; k < n_ev + n_eh; k += 256) {
-    int p, e, pos, r, c, idx, n_o, o;
-    if (k < n_ev) {
-      p = k / (2 * H); e = (k / H) & 1; pos = k % H;
-      r = pos; c = e ? W - 1 : 0; o = c; n_o = W; idx = ev_off + (p * 2 + e) * H + pos;
-    } else {
-      const int k2 = k - n_ev;
-      p = k2 / (2 * W); e = (k2 / W) & 1; pos = k2 % W;
-      c = pos; r = e ? H - 1 : 0; o = r; n_o = H; idx = eh_off + (p * 2 + e) * W + pos;
-    }
-    const float4 m = smem[(p * H + r) * pitch + c];
-    const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
-    smem[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
-  }
-  __syncthreads();
-
-  // ---- 3. one scan direction per wavefront ---------------------------------
-  const int d = tid >> 6;
-  const int lane = tid & 63;
-  const int p = lane / SEG, o = lane % SEG;
-  const bool on = (a.mask >> d) & 1u;
-  const bool vert = d < 2, fwd = (d == 0 || d == 2);
-  const int n_s = vert ? H : W, n_o = vert ? W : H;
-  const bool active = on && o < n_o && p < np;
-  // main-record position of step 0 and its per-step stride
-  int mbase, mstride;
-  if (vert) { mbase = (p * H + (fwd ? 0 : H - 1)) * pitch + o; mstride = fwd ? pitch : -pitch; }
-  else      { mbase = (p * H + o) * pitch + (fwd ? 0 : W - 1); mstride = fwd ? 1 : -1; }
-  int addr = mbase, stride = mstride;
-  if (!active) { addr = zero_off; stride = 0; }
-  else if (o == 0 || o == n_o - 1) {
-    const int e = (o == 0) ? 0 : 1;
-    if (vert) { addr = ev_off + (p * 2 + e) * H + (fwd ? 0 : H - 1); }
-    else      { addr = eh_off + (p * 2 + e) * W + (fwd ? 0 : W - 1); }
-    stride = fwd ? 1 : -1;
-  }
-  // steps at which the state restarts: 0, then every G from the first block edge
-  const int G = a.G;
-  int next_restart = n_s;
-  if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
-
-  float hist[SEG];
-  if (on) {
-    float h = 0.0f;
+      for (int it = 0; it < NIT; ++it) {
+        uu[it] = ru[it];
+        const int i0 = tid * 4 + it * 1024;
+        if (i0 < npix) {
+          int rem, c;
+          const int p = div_small(i0, HW, a.inv_HW, &rem);
+          const int r = div_small(rem, W, a.inv_W, &c);
+          // W % 4 == 0 on this path, so the four pixels share row r
 #pragma unroll
-    for (int s = 0; s < SEG; ++s) {
-      if (s < n_s) {
-        const float4 rc = smem[addr];
-        addr += stride;
-        const float hl = from_left<SEG>(h);
-        const float hr = from_right<SEG>(h);
-        const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
-        bool restart = (s == 0);
-        if (s == next_restart) { restart = true; next_restart += G; }
-        h = restart ? rc.w : hn;
-        hist[s] = h;
+          for (int e = 0; e < 4; ++e) {
+            const Weights w = make_weights(V::get(r0[it], e), V::get(r1[it], e),
+                                           V::get(r2[it], e), 1.0f, 1.0f);
+            smem[(p * H + r) * pitch + c + e] =
+                make_float4(w.w0, w.w1, w.w2, V::get(rl[it], e) * V::get(rx[it], e));
+          }
+        }
+      }
+      // the next plane group's loads fly during steps 2-4
+      if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x);
+    } else {
+      for (int i0 = tid; i0 < npix; i0 += 256) {
+        int rem, c;
+        const int p = div_small(i0, HW, a.inv_HW, &rem);
+        const int r = div_small(rem, W, a.inv_W, &c);
+        const int64_t gi = gbase + i0;
+        const Weights w = make_weights(ld1(a.l0, gi), ld1(a.l1, gi), ld1(a.l2, gi), 1.0f, 1.0f);
+        smem[(p * H + r) * pitch + c] = make_float4(w.w0, w.w1, w.w2, ld1(a.lam, gi) * ld1(a.x, gi));
       }
     }
-  }
-  __syncthreads();   // every wavefront is done with the records
+    if (tid == 0) smem[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
 
-  // ---- 4. park states over the records, then merge --------------------------
-  if (active) {
-    int ya = d * rec_sz + mbase;
-#pragma unroll
-    for (int s = 0; s < SEG; ++s) {
-      if (s < n_s) { smem_f[ya] = hist[s]; ya += mstride; }
+    // ---- 2. edge-lane records ----------------------------------------------
+    // vertical scans: lanes c = 0 (e = 0) and c = W-1 (e = 1), masks on c;
+    // horizontal scans: lanes r = 0 and r = H-1, masks on r.
+    const int n_ev = np * 2 * H, n_eh = np * 2 * W;
+    for (int k = tid; k < n_ev + n_eh; k += 256) {
+      int p, e, pos, r, c, idx, n_o, o;
+      if (k < n_ev) {
+        p = k / (2 * H); e = (k / H) & 1; pos = k % H;
+        r = pos; c = e ? W - 1 : 0; o = c; n_o = W; idx = ev_off + (p * 2 + e) * H + pos;
+      } else {
+        const int k2 = k - n_ev;
+        p = k2 / (2 * W); e = (k2 / W) & 1; pos = k2 % W;
+        c = pos; r = e ? H - 1 : 0; o = r; n_o = H; idx = eh_off + (p * 2 + e) * W + pos;
+      }
+      const float4 m = smem[(p * H + r) * pitch + c];
+      const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
+      smem[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  for (int i0 = tid * VEC; i0 < npix; i0 += 256 * VEC) {
-    float uu[4], y[4];
-    if constexpr (VEC == 4) load4(a.u, gbase + i0, uu); else load1(a.u, gbase + i0, uu);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      int rem, c;
-      const int pp = div_small(i0 + e, HW, a.inv_HW, &rem);
-      const int r = div_small(rem, W, a.inv_W, &c);
-      const int li = (pp * H + r) * pitch + c;
-      float sum = 0.0f;
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
-        if ((a.mask >> dd) & 1u) sum += smem_f[dd * rec_sz + li];
-      y[e] = uu[e] * sum;
+    // ---- 3. one scan direction per wavefront -------------------------------
+    const int d = tid >> 6;
+    const int lane = tid & 63;
+    const int p = lane / SEG, o = lane % SEG;
+    const bool on = (a.mask >> d) & 1u;
+    const bool vert = d < 2, fwd = (d == 0 || d == 2);
+    const int n_s = vert ? H : W, n_o = vert ? W : H;
+    const bool active = on && o < n_o && p < np;
+    // main-record position of step 0 and its per-step stride
+    int mbase, mstride;
+    if (vert) { mbase = (p * H + (fwd ? 0 : H - 1)) * pitch + o; mstride = fwd ? pitch : -pitch; }
+    else      { mbase = (p * H + o) * pitch + (fwd ? 0 : W - 1); mstride = fwd ? 1 : -1; }
+    int addr = mbase, stride = mstride;
+    if (!active) { addr = zero_off; stride = 0; }
+    else if (o == 0 || o == n_o - 1) {
+      const int e = (o == 0) ? 0 : 1;
+      if (vert) { addr = ev_off + (p * 2 + e) * H + (fwd ? 0 : H - 1); }
+      else      { addr = eh_off + (p * 2 + e) * W + (fwd ? 0 : W - 1); }
+      stride = fwd ? 1 : -1;
     }
-    if constexpr (VEC == 4) store4(a.out, gbase + i0, y); else store1(a.out, gbase + i0, y);
+    // steps at which the state restarts: 0, then every G from the first
+    // block edge met
+    const int G = a.G;
+    int next_restart = n_s;
+    if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
+
+    float hist[SEG];
+    if (on) {
+      float h = 0.0f;
+#pragma unroll
+      for (int s = 0; s < SEG; ++s) {
+        if (s < n_s) {
+          const float4 rc = smem[addr];
+          addr += stride;
+          const float hl = from_left<SEG>(h);
+          const float hr = from_right<SEG>(h);
+          const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+          bool restart = (s == 0);
+          if (s == next_restart) { restart = true; next_restart += G; }
+          h = restart ? rc.w : hn;
+          hist[s] = h;
+        }
+      }
+    }
+    __syncthreads();   // every wavefront is done with the records
+
+    // ---- 4. park states over the records, then merge ------------------------
+    if (active) {
+      int ya = d * rec_sz + mbase;
+#pragma unroll
+      for (int s = 0; s < SEG; ++s) {
+        if (s < n_s) { smem_f[ya] = hist[s]; ya += mstride; }
+      }
+    }
+    __syncthreads();
+
+    if constexpr (VEC == 4) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i0 = tid * 4 + it * 1024;
+        if (i0 < npix) {
+          int rem, c;
+          const int pp = div_small(i0, HW, a.inv_HW, &rem);
+          const int r = div_small(rem, W, a.inv_W, &c);
+          const int li = (pp * H + r) * pitch + c;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd)
+              if ((a.mask >> dd) & 1u) sum += smem_f[dd * rec_sz + li + e];
+            y[e] = V::get(uu[it], e) * sum;
+          }
+          V::store(a.out, gbase + i0, y);
+        }
+      }
+    } else {
+      for (int i0 = tid; i0 < npix; i0 += 256) {
+        int rem, c;
+        const int pp = div_small(i0, HW, a.inv_HW, &rem);
+        const int r = div_small(rem, W, a.inv_W, &c);
+        const int li = (pp * H + r) * pitch + c;
+        float sum = 0.0f;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+          if ((a.mask >> dd) & 1u) sum += smem_f[dd * rec_sz + li];
+        st1(a.out, gbase + i0, ld1(a.u, gbase + i0) * sum);
+      }
+    }
+    __syncthreads();   // LDS is rewritten by the next plane group
   }
 }
 
@@ -226,6 +303,8 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   a.u = static_cast<const T*>(pr.u);
   a.out = static_cast<T*>(pr.out);
   a.nplanes = pr.B * pr.C;
+  constexpr int PPB = 64 / SEG;
+  a.ngroups = (a.nplanes + PPB - 1) / PPB;
   a.H = static_cast<int>(pr.H);
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G >= pr.H && pr.G >= pr.W ? 0 : pr.G);
@@ -233,25 +312,36 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   a.pitch = static_cast<int>(pr.W | 1);
   a.inv_W = 1.0f / static_cast<float>(pr.W);
   a.inv_HW = 1.0f / static_cast<float>(pr.H * pr.W);
-  constexpr int PPB = 64 / SEG;
-  const int64_t blocks = (a.nplanes + PPB - 1) / PPB;
   const size_t lds = plane_lds_bytes(pr.H, pr.W);
   auto kern = plane_kernel<T, SEG, VEC>;
+  hipError_t e;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
+  // SEG 64 (one large plane per workgroup): persistent grid of as many
+  // workgroups as are resident at once, each prefetching its next plane.
+  // SEG 16 (four tiny planes per workgroup): one plane group per workgroup.
+  int per_cu = 0, dev = 0, cus = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                        256, lds)) != hipSuccess)
+    return e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  const int64_t resident = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  const int64_t grid = (SEG == 16 || a.ngroups < resident) ? a.ngroups : resident;
   tr->before(stream, SEG == 16 ? "plane_kernel16" : "plane_kernel64", a.nplanes);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), lds, stream, a);
   tr->after(stream);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_plane_dt(const Problem& pr, hipStream_t stream, Tracer* tr) {
-  const bool vec = (pr.H * pr.W) % 4 == 0 && pr.aligned_vec4;
+  // 4-wide vectors need whole rows of 4 (W % 4 == 0) and aligned pointers
+  const bool vec = pr.W % 4 == 0 && pr.aligned_vec4;
   if (plane_seg(pr.H, pr.W) == 16)
     return vec ? launch_plane_t<T, 16, 4>(pr, stream, tr) : launch_plane_t<T, 16, 1>(pr, stream, tr);
   return vec ? launch_plane_t<T, 64, 4>(pr, stream, tr) : launch_plane_t<T, 64, 1>(pr, stream, tr);
