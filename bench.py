@@ -7,10 +7,12 @@ One step = one full propagation (all selected scan directions, fused merge)
 over one batch of seeded synthetic inputs already resident in HBM. Prints ONE
 JSON line:
   value     elem-steps/s = B*C*H*W*dirs*K / (time of K steps)
-  roofline  the dominant kernel: algorithmic bytes per launch / its average
-            launch time (HIP events recorded around each launch on the launch
-            stream, inside the timed region), against the 8 TB/s HBM peak;
-            traffic = HBM bytes per launch from the committed rocprofv3
+  roofline  the launches of one step (one kernel, or the three-kernel
+            pipeline of large planes): compulsory bytes Q_min = 7 s per pixel
+            / their time (HIP events recorded around each launch on its
+            stream inside the timed region; the step time for a pipeline
+            whose launches overlap on two streams), against the 8 TB/s HBM
+            peak; traffic = HBM bytes per step from the committed rocprofv3
             counter summary when it was taken on the current kernel sources
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
             workload on this host's cores (rank 0, N = 1 only)
@@ -77,8 +79,9 @@ class Hip:
             self.L.hipEventDestroy(e)
 
 
-def algorithmic_bytes(kernel: str, planes: int, w) -> float:
-    """Compulsory HBM bytes of one launch of `kernel` over `planes` planes.
+def design_bytes(kernel: str, planes: int, w) -> float:
+    """HBM bytes one launch of `kernel` over `planes` planes moves by design
+    (every tensor it touches read or written once).
 
     Per pixel, with s = bytes per stored element:
       plane_kernel16/64 (all directions on chip): x, lambda, l0, l1, l2, u
@@ -105,10 +108,11 @@ def algorithmic_bytes(kernel: str, planes: int, w) -> float:
     return per * px
 
 
-def counter_traffic(kernel: str, workload: str, digest: str):
-    """HBM bytes per launch from profiles/<kernel>__<workload>__pmc.txt, or
-    None when absent or taken on other kernel sources."""
-    path = os.path.join(PROFILES, f"{kernel.split('<')[0]}__{workload}__pmc.txt")
+def counter_traffic(plan: str, workload: str, digest: str):
+    """HBM bytes per step (the launches of one step) from
+    profiles/<plan>__<workload>__pmc.txt, or None when absent or taken on
+    other kernel sources."""
+    path = os.path.join(PROFILES, f"{plan}__{workload}__pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -120,7 +124,7 @@ def counter_traffic(kernel: str, workload: str, digest: str):
     if vals.get("source_digest") != digest:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 
@@ -270,20 +274,28 @@ def main() -> int:
     per_launch = [t / args.steps for t in per_launch]
     for e in evs:
         hip.destroy(e)
-    # per kernel: summed launch time and algorithmic bytes (launches of one
-    # kernel may run on two streams; each is timed on its own stream)
+    # per kernel: summed launch time and design bytes (launches of one kernel
+    # may run on two streams; each is timed on its own stream)
     kt, kb = {}, {}
     for (name, np_), t in zip(launches, per_launch):
         kt[name] = kt.get(name, 0.0) + t
-        kb[name] = kb.get(name, 0.0) + algorithmic_bytes(name, np_, w)
-    kname = max(kt, key=kt.get)
-    kbytes = kb[kname]
-    achieved = kbytes / (kt[kname] * 1e-3) / 1e9
-    traffic = counter_traffic(kname, w.name, source_digest())
+        kb[name] = kb.get(name, 0.0) + design_bytes(name, np_, w)
     path_bytes = sum(kb.values())
+    # Roofline unit: the launches of one step. A single launch is timed by its
+    # own events; a pipeline of several launches (overlapping on two streams)
+    # by the step time. Algorithmic bytes: the compulsory Q_min = 7 s per
+    # pixel (five inputs and u read once, out written once).
+    s = 4 if w.dtype == "f32" else 2
+    q_min = 7 * s * w.pixels
+    if nl == 1:
+        unit_name, unit_ms = launches[0][0], per_launch[0]
+    else:
+        unit_name = "+".join(dict.fromkeys(n for n, _ in launches))
+        unit_ms = ms_per_step
+    achieved = q_min / (unit_ms * 1e-3) / 1e9
+    traffic = counter_traffic(plan, w.name, source_digest())
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
-    q_min = 7 * s * w.pixels
     result = {
         "metric": METRIC,
         "value": value,
@@ -306,12 +318,11 @@ def main() -> int:
                    "path_design_bytes": path_bytes,
                    "path_design_gbs": path_bytes / (ms_per_step * 1e-3) / 1e9,
                    "path_qmin_bytes": q_min,
-                   "path_qmin_gbs": q_min / (ms_per_step * 1e-3) / 1e9,
                    "host_wall_s": round(wall, 3), "input_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": unit_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_step": kbytes,
-                     "kernel_ms_per_step": kt[kname]},
+                     "traffic": traffic, "algorithmic_bytes_per_step": q_min,
+                     "unit_ms": unit_ms},
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
