@@ -89,6 +89,8 @@ def design_bytes(kernel: str, planes: int, w) -> float:
       stream_kernel (one launch per direction, fp32 accumulator between
           them): 5 s inputs + 4 (accumulator read or write, counted once);
           the u read / out write of the last direction are not included
+      band_kernel (local groups; vertical phase, then horizontal phase that
+          reads the plane again): 2 * 5 s inputs + s (u) + s (out)
       tpipe (column-major copy = lambda*x in fp32 + 3 logits):
           tp_vfwd  5 s inputs + (4 + 3 s) copy write + 4/8 checkpoints
           tp_hpair 2 (4 + 3 s) copy reads + 2 * 4/4 checkpoints + 4 sum write
@@ -101,6 +103,7 @@ def design_bytes(kernel: str, planes: int, w) -> float:
         "plane_kernel16": 7 * s,
         "plane_kernel64": 7 * s,
         "stream_kernel": 5 * s + 4,
+        "band_kernel": 12 * s,
         "tp_vfwd": 5 * s + (4 + 3 * s if hz else 0) + (0.5 if w.dirs & 1 else 0),
         "tp_hpair": 2 * (4 + 3 * s) + 2.0 + 4,
         "tp_vbwd": 5 * s + (0.5 if w.dirs & 1 else 0) + (4 if hz else 0) + 2 * s,

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgspn.so")
 
-SOURCES = ["gspn_api.cpp", "gspn_plane.hip", "gspn_stream.hip", "gspn_tpipe.hip"]
+SOURCES = ["gspn_api.cpp", "gspn_plane.hip", "gspn_stream.hip", "gspn_tpipe.hip",
+           "gspn_band.hip"]
 ARCH = os.environ.get("GSPN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -26,7 +26,7 @@ gspn_status fail(gspn_status s, const std::string& detail) {
 
 size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
 
-enum class Plan { kInvalid, kPlane16, kPlane64, kTpipe, kStream };
+enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream };
 
 struct Checked {
   gspn_status status;
@@ -68,16 +68,19 @@ Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
     r.status = fail(GSPN_E_GROUP, "group_rows must be >= 0");
     return r;
   }
-  // GSPN_FORCE_PLAN=plane|tpipe|stream picks a path for testing when the
-  // shape allows it; otherwise the first path that fits, in that order.
+  // GSPN_FORCE_PLAN=plane|band|tpipe|stream picks a path for testing when
+  // the shape allows it; otherwise the first path that fits, in that order.
   const char* force = std::getenv("GSPN_FORCE_PLAN");
   const bool f_plane = force && !std::strcmp(force, "plane");
+  const bool f_band = force && !std::strcmp(force, "band");
   const bool f_tpipe = force && !std::strcmp(force, "tpipe");
   const bool f_stream = force && !std::strcmp(force, "stream");
-  const bool any = !f_plane && !f_tpipe && !f_stream;
+  const bool any = !f_plane && !f_band && !f_tpipe && !f_stream;
   const bool stream_ok = H <= gspn::stream_max_orth() && W <= gspn::stream_max_orth();
   if ((any || f_plane) && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? Plan::kPlane16 : Plan::kPlane64;
+  } else if ((any || f_band) && gspn::band_fits(H, W, G)) {
+    r.plan = Plan::kBand;
   } else if ((any || f_tpipe) && gspn::tpipe_fits(H, W)) {
     r.plan = Plan::kTpipe;
     r.ws_bytes = gspn::tpipe_workspace_bytes(planes, H, W, static_cast<gspn_dtype>(dtype));
@@ -149,6 +152,9 @@ gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream
     case Plan::kPlane64:
       e = gspn::launch_plane(pr, stream, &tr);
       break;
+    case Plan::kBand:
+      e = gspn::launch_band(pr, stream, &tr);
+      break;
     case Plan::kTpipe:
       e = gspn::launch_tpipe(pr, ws, stream, &tr);
       break;
@@ -173,6 +179,7 @@ const char* plan_str(Plan p) {
   switch (p) {
     case Plan::kPlane16: return "plane16";
     case Plan::kPlane64: return "plane64";
+    case Plan::kBand: return "band";
     case Plan::kTpipe: return "tpipe";
     case Plan::kStream: return "stream";
     default: return "invalid";

@@ -48,6 +48,10 @@ int plane_seg(int64_t H, int64_t W);
 size_t plane_lds_bytes(int64_t H, int64_t W);
 hipError_t launch_plane(const Problem& pr, hipStream_t stream, Tracer* tr);
 
+// band-resident path for small local groups (gspn_band.hip)
+bool band_fits(int64_t H, int64_t W, int64_t G);
+hipError_t launch_band(const Problem& pr, hipStream_t stream, Tracer* tr);
+
 // large-plane transpose pipeline (gspn_tpipe.hip)
 bool tpipe_fits(int64_t H, int64_t W);
 size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt);

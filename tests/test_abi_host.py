@@ -108,7 +108,10 @@ def test_workspace_and_plans(L, monkeypatch):
     assert g.plan_name(1, 1, 16, 17) == "plane64"
     assert g.plan_name(1, 1, 65, 8) == "stream"          # odd H: no pair kernels
     assert g.plan_name(1, 320, 2048, 1024, dtype=1) == "tpipe"
-    assert g.plan_name(16, 192, 128, 128, group_rows=8) == "tpipe"
+    assert g.plan_name(16, 192, 128, 128, group_rows=8) == "band"
+    assert g.plan_name(16, 192, 128, 128, group_rows=0) == "tpipe"
+    assert g.plan_name(16, 192, 128, 128, group_rows=17) == "tpipe"   # groups above 16
+    assert g.plan_name(1, 1, 512, 512, group_rows=8) == "tpipe"       # y_V too big for LDS
     assert g.plan_name(1, 1, 100, 2048) == "stream"       # W above the pair-kernel limit
     assert g.workspace_bytes(1, 2, 100, 100) > 0
     assert g.plan_name(1, 1, 0, 5) == "invalid"

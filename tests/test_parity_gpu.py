@@ -185,3 +185,24 @@ def test_forced_plan(force_plan, plan, shape, dtype):
         for G in ((0, 3, 8) if mask == 15 else (0,)):
             out = run(inp, mask, G)
             assert_parity(out, oracle_y(inp, mask, G), f"{plan} {shape} mask={mask} G={G}")
+
+
+BAND_SHAPES = [(1, 2, 72, 40), (2, 1, 128, 128), (1, 1, 100, 70), (1, 2, 66, 130),
+               (1, 1, 160, 96), (1, 1, 8, 300)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", BAND_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_band_plan(force_plan, shape, dtype):
+    """Band-resident local plan: group sizes 1..16 (ragged last bands included),
+    every direction-mask family."""
+    force_plan("band")
+    B, C, H, W = shape
+    w = "local_128x128_g8" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=(H * 7 + W) % 991, B=B, C=C, H=H, W=W)
+    for G in (1, 2, 3, 5, 8, 13, 16):
+        assert g.plan_name(B, C, H, W, 15, G, 0 if dtype == torch.float32 else 1) == "band"
+        masks = (15, 1, 2, 4, 8, 3, 12, 5, 10) if G in (3, 8) else (15,)
+        for mask in masks:
+            out = run(inp, mask, G)
+            assert_parity(out, oracle_y(inp, mask, G), f"band {shape} mask={mask} G={G}")
