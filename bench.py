@@ -37,11 +37,22 @@ CSRC = os.path.join(ROOT, "linear_spatial_propagation_line_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources; counter figures are only reported when
-    they were taken on exactly these sources."""
+# kernel source of each plan; the counter figures of a plan stay valid while
+# these files are unchanged
+PLAN_SOURCES = {
+    "plane16": ("gspn_plane.hip", "gspn_device.hpp"),
+    "plane64": ("gspn_plane.hip", "gspn_device.hpp"),
+    "band": ("gspn_band.hip", "gspn_device.hpp"),
+    "tpipe": ("gspn_tpipe.hip", "gspn_device.hpp"),
+    "stream": ("gspn_stream.hip", "gspn_device.hpp"),
+}
+
+
+def source_digest(plan: str) -> str:
+    """sha256 over the kernel sources of `plan`; counter figures are only
+    reported when they were taken on exactly these sources."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in PLAN_SOURCES[plan]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -296,7 +307,7 @@ def main() -> int:
         unit_name = "+".join(dict.fromkeys(n for n, _ in launches))
         unit_ms = ms_per_step
     achieved = q_min / (unit_ms * 1e-3) / 1e9
-    traffic = counter_traffic(plan, w.name, source_digest())
+    traffic = counter_traffic(plan, w.name, source_digest(plan))
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
     result = {

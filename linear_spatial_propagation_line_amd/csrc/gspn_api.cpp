@@ -115,15 +115,17 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   if (chk->status != GSPN_OK) return chk->status;
   const size_t es = elem_size(dtype);
   const void* ins[6] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u};
-  bool vec4 = true;
+  bool vec4 = true, pair = true;
   for (const void* p : ins) {
     const uintptr_t v = reinterpret_cast<uintptr_t>(p);
     if (v % es) return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
     if (v % (4 * es)) vec4 = false;
+    if (v % (2 * es)) pair = false;
   }
   const uintptr_t vo = reinterpret_cast<uintptr_t>(out);
   if (vo % es) return fail(GSPN_E_ALIGN, "out not aligned to its element size");
   if (vo % (4 * es)) vec4 = false;
+  if (vo % (2 * es)) pair = false;
   const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
   for (const void* p : ins)
     if (overlaps(out, bytes, p, bytes)) return fail(GSPN_E_ALIAS, "out overlaps an input");
@@ -139,6 +141,7 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   pr->G = G;
   pr->dtype = dtype;
   pr->aligned_vec4 = vec4;
+  pr->aligned_pair = pair;
   return GSPN_OK;
 }
 
@@ -156,7 +159,11 @@ gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream
       e = gspn::launch_band(pr, stream, &tr);
       break;
     case Plan::kTpipe:
-      e = gspn::launch_tpipe(pr, ws, stream, &tr);
+      // the pipeline moves adjacent column pairs as one access; tensors that
+      // start at an odd element take the streaming path, whose fp32
+      // accumulator fits in the front of the pipeline's larger workspace
+      e = pr.aligned_pair ? gspn::launch_tpipe(pr, ws, stream, &tr)
+                          : gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
       break;
     case Plan::kStream:
       e = gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);

@@ -38,6 +38,42 @@ __device__ __forceinline__ void bst(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void bst(bf16_t* p, int64_t i, float v) {
   p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
+// N contiguous elements at a 16-byte aligned index, widened to fp32 ...
+template <int N> __device__ __forceinline__ void run_ld(const float* p, int64_t i, float* d) {
+  const float4* q = reinterpret_cast<const float4*>(p + i);
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    const float4 v = q[k];
+    d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
+  }
+}
+template <int N> __device__ __forceinline__ void run_ld(const bf16_t* p, int64_t i, float* d) {
+  const uint4* q = reinterpret_cast<const uint4*>(p + i);
+#pragma unroll
+  for (int k = 0; k < N / 8; ++k) {
+    const uint4 v = q[k];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { d[8 * k + 2 * j] = bf16_lo(w[j]); d[8 * k + 2 * j + 1] = bf16_hi(w[j]); }
+  }
+}
+// ... and stored back the same way (bf16 rounded to nearest even)
+template <int N> __device__ __forceinline__ void run_st(float* p, int64_t i, const float* d) {
+  float4* q = reinterpret_cast<float4*>(p + i);
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) q[k] = make_float4(d[4 * k], d[4 * k + 1], d[4 * k + 2], d[4 * k + 3]);
+}
+template <int N> __device__ __forceinline__ void run_st(bf16_t* p, int64_t i, const float* d) {
+  uint4* q = reinterpret_cast<uint4*>(p + i);
+#pragma unroll
+  for (int k = 0; k < N / 8; ++k) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = f32_to_bf16_bits(d[8 * k + 2 * j]) | (f32_to_bf16_bits(d[8 * k + 2 * j + 1]) << 16);
+    q[k] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
 }  // namespace
 
 template <typename T>
@@ -55,12 +91,15 @@ struct BandArgs {
 };
 
 // GM = compile-time bound on G (8 or 16); chains have min(G, rest) steps.
+// VH: G == GM, W a multiple of GM and every tensor 16-byte aligned, so a
+// horizontal chain's G columns are read and written as whole 16-byte vectors.
 // The grid is persistent: a workgroup walks a list of rounds -- for each of
 // its planes, the vertical rounds then the horizontal rounds -- and issues
-// the loads of the next round before computing the current one, so HBM (or
-// last-level cache) transfers overlap the scans.
-template <typename T, int GM>
-__global__ __launch_bounds__(kBandThreads) void band_kernel(BandArgs<T> a) {
+// the loads of the next round as soon as the current one is done. With
+// G <= 8 the register budget allows two workgroups per CU, whose rounds
+// interleave and hide each other's load latency.
+template <typename T, int GM, bool VH>
+__global__ __launch_bounds__(kBandThreads, GM <= 8 ? 4 : 2) void band_kernel(BandArgs<T> a) {
   extern __shared__ float sm[];
   const int H = a.H, W = a.W, G = a.G;
   const int t = threadIdx.x;
@@ -109,11 +148,17 @@ __global__ __launch_bounds__(kBandThreads) void band_kernel(BandArgs<T> a) {
       const int cb = (rd - nrv) * ph + hbl;
       const int c0 = min(cb, nbh - 1) * G;
       const int r = min(hr, H - 1);
+      if constexpr (VH) {
+        const int64_t i = base + static_cast<int64_t>(r) * W + c0;
+        run_ld<GM>(a.l0, i, L.g0); run_ld<GM>(a.l1, i, L.g1); run_ld<GM>(a.l2, i, L.g2);
+        run_ld<GM>(a.x, i, L.x); run_ld<GM>(a.lam, i, L.l);
+      } else {
 #pragma unroll
-      for (int s = 0; s < GM; ++s) {
-        const int64_t i = base + static_cast<int64_t>(r) * W + min(c0 + s, W - 1);
-        L.g0[s] = bld(a.l0, i); L.g1[s] = bld(a.l1, i); L.g2[s] = bld(a.l2, i);
-        L.x[s] = bld(a.x, i); L.l[s] = bld(a.lam, i);
+        for (int s = 0; s < GM; ++s) {
+          const int64_t i = base + static_cast<int64_t>(r) * W + min(c0 + s, W - 1);
+          L.g0[s] = bld(a.l0, i); L.g1[s] = bld(a.l1, i); L.g2[s] = bld(a.l2, i);
+          L.x[s] = bld(a.x, i); L.l[s] = bld(a.lam, i);
+        }
       }
     }
   };
@@ -173,9 +218,6 @@ __global__ __launch_bounds__(kBandThreads) void band_kernel(BandArgs<T> a) {
     }
   };
 
-  // with G <= 8 the next round's loads are issued right after the current
-  // records are built; 16-wide chains would not fit both in registers
-  constexpr bool PIPE = GM <= 8;
   const int64_t planes = a.planes;
   const int nrounds = nrv + nrh;
   int64_t p = blockIdx.x;
@@ -196,7 +238,6 @@ __global__ __launch_bounds__(kBandThreads) void band_kernel(BandArgs<T> a) {
       const int r0 = min(b, nbv - 1) * G;
       const int len = act ? min(G, H - r0) : 0;
       build(L, vc > 0 ? 1.f : 0.f, vc < W - 1 ? 1.f : 0.f, len, R);
-      if (PIPE && p2 < planes) issue(p2, rd2, L);   // in flight during this round
       pair_scan(R, len, act, lw, pv, vbl * lw + vc + 1, tb, bt, hs);
 #pragma unroll
       for (int s = 0; s < GM; ++s)
@@ -209,23 +250,34 @@ __global__ __launch_bounds__(kBandThreads) void band_kernel(BandArgs<T> a) {
       const int len = act ? min(G, W - c0) : 0;
       const int r = min(hr, H - 1);
       build(L, r > 0 ? 1.f : 0.f, r < H - 1 ? 1.f : 0.f, len, R);
-      if (PIPE && p2 < planes) issue(p2, rd2, L);
       // u is needed only after the scans: its loads fly during them
+      const int64_t row = base + static_cast<int64_t>(r) * W;
       float uu[GM];
+      if constexpr (VH) {
+        run_ld<GM>(a.u, row + c0, uu);
+      } else {
 #pragma unroll
-      for (int s = 0; s < GM; ++s)
-        uu[s] = bld(a.u, base + static_cast<int64_t>(r) * W + min(c0 + s, W - 1));
+        for (int s = 0; s < GM; ++s) uu[s] = bld(a.u, row + min(c0 + s, W - 1));
+      }
       pair_scan(R, len, act, lh, ph, hbl * lh + r + 1, lr, rl, hs);
+      if constexpr (VH) {
+        if (act) {
 #pragma unroll
-      for (int s = 0; s < GM; ++s) {
-        if (act && s < len) {
-          const int c = c0 + s;
-          const float yvv = vert ? yv[r * yp + c] : 0.f;
-          bst(a.out, base + static_cast<int64_t>(r) * W + c, uu[s] * (yvv + hs[s]));
+          for (int s = 0; s < GM; ++s) hs[s] = uu[s] * ((vert ? yv[r * yp + c0 + s] : 0.f) + hs[s]);
+          run_st<GM>(a.out, row + c0, hs);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < GM; ++s) {
+          if (act && s < len) {
+            const int c = c0 + s;
+            const float yvv = vert ? yv[r * yp + c] : 0.f;
+            bst(a.out, row + c, uu[s] * (yvv + hs[s]));
+          }
         }
       }
     }
-    if (!PIPE && p2 < planes) issue(p2, rd2, L);
+    if (p2 < planes) issue(p2, rd2, L);
     __syncthreads();   // line and y_V are rewritten by the next round
     p = p2;
     rd = rd2;
@@ -250,7 +302,7 @@ bool band_fits(int64_t H, int64_t W, int64_t G) {
          band_lds_bytes(H, W, G) <= 160 * 1024;
 }
 
-template <typename T, int GM>
+template <typename T, int GM, bool VH>
 static hipError_t launch_band_t(const Problem& pr, hipStream_t stream, Tracer* tr) {
   BandArgs<T> a;
   a.x = static_cast<const T*>(pr.x);
@@ -265,7 +317,7 @@ static hipError_t launch_band_t(const Problem& pr, hipStream_t stream, Tracer* t
   a.G = static_cast<int>(pr.G);
   a.mask = pr.mask;
   const size_t lds = band_lds_bytes(pr.H, pr.W, pr.G);
-  auto kern = band_kernel<T, GM>;
+  auto kern = band_kernel<T, GM, VH>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -291,10 +343,22 @@ static hipError_t launch_band_t(const Problem& pr, hipStream_t stream, Tracer* t
   return hipGetLastError();
 }
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename T>
+static hipError_t launch_band_dt(const Problem& pr, hipStream_t stream, Tracer* tr) {
+  const int gm = pr.G <= 8 ? 8 : 16;
+  const bool vh = pr.G == gm && pr.W % gm == 0 && aligned16(pr.x) && aligned16(pr.lam) &&
+                  aligned16(pr.l[0]) && aligned16(pr.l[1]) && aligned16(pr.l[2]) &&
+                  aligned16(pr.u) && aligned16(pr.out);
+  if (gm == 8)
+    return vh ? launch_band_t<T, 8, true>(pr, stream, tr) : launch_band_t<T, 8, false>(pr, stream, tr);
+  return vh ? launch_band_t<T, 16, true>(pr, stream, tr) : launch_band_t<T, 16, false>(pr, stream, tr);
+}
+
 hipError_t launch_band(const Problem& pr, hipStream_t stream, Tracer* tr) {
-  if (pr.dtype == GSPN_F32)
-    return pr.G <= 8 ? launch_band_t<float, 8>(pr, stream, tr) : launch_band_t<float, 16>(pr, stream, tr);
-  return pr.G <= 8 ? launch_band_t<bf16_t, 8>(pr, stream, tr) : launch_band_t<bf16_t, 16>(pr, stream, tr);
+  return pr.dtype == GSPN_F32 ? launch_band_dt<float>(pr, stream, tr)
+                              : launch_band_dt<bf16_t>(pr, stream, tr);
 }
 
 }  // namespace gspn

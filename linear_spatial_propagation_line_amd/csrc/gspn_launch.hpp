@@ -21,6 +21,7 @@ struct Problem {
   int64_t G;
   gspn_dtype dtype;
   bool aligned_vec4;   // every pointer aligned to 4 elements
+  bool aligned_pair;   // every pointer aligned to 2 elements
 };
 
 // Records caller-owned events around kernel launches (gspn_trace_events),

@@ -206,3 +206,35 @@ def test_band_plan(force_plan, shape, dtype):
         for mask in masks:
             out = run(inp, mask, G)
             assert_parity(out, oracle_y(inp, mask, G), f"band {shape} mask={mask} G={G}")
+
+
+def _offset_view(t, off):
+    """A contiguous copy of t that starts `off` elements into its allocation."""
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=DEV)
+    v = buf[off:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape,G,plan", [
+    ((1, 3, 16, 16), 0, "plane16"), ((1, 2, 56, 56), 0, "plane64"),
+    ((1, 2, 128, 128), 8, "band"), ((1, 1, 96, 64), 16, "band"),
+    ((1, 2, 130, 96), 0, "tpipe"), ((1, 1, 65, 80), 0, "stream")],
+    ids=["plane16", "plane64", "band8", "band16", "tpipe", "stream"])
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_element_offset_views(shape, G, plan, dtype, off):
+    """Tensors that start 1-3 elements into their allocation (naturally
+    aligned, but not to the 8- or 16-byte vectors the fast paths use) take
+    the element-wise code and still match the oracle."""
+    B, C, H, W = shape
+    dt = 0 if dtype == torch.float32 else 1
+    assert g.plan_name(B, C, H, W, 15, G, dt) == plan
+    w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=17 + off, B=B, C=C, H=H, W=W)
+    d = {k: _offset_view(v.to(DEV), off) for k, v in inp.items()}
+    out = _offset_view(torch.zeros(shape, dtype=dtype, device=DEV), off)
+    g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], dirs=15, group_rows=G,
+                out=out)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_y(inp, 15, G), f"{plan} offset {off}")
