@@ -56,6 +56,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     f.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
                   ctypes.c_uint32, i64, vp, ctypes.c_int]
     f.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_backward"):
+        b = lib.gspn_oracle_backward
+        b.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                      ctypes.c_uint32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        b.restype = ctypes.c_int
     return lib
 
 
@@ -104,3 +109,39 @@ def propagate(x, l0, l1, l2, lam, u, dirs: int = 15, group_rows: int = 0,
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
+
+
+GRAD_NAMES = ("x", "l0", "l1", "l2", "lam", "u")
+
+
+def backward(x, l0, l1, l2, lam, u, gy, dirs: int = 15, group_rows: int = 0,
+             nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> dict:
+    """Gradients of a loss L with respect to every input of ``propagate``,
+    given ``gy`` = dL/dy (same shape and dtype as the inputs). Returns a dict
+    ``{"x", "l0", "l1", "l2", "lam", "u"}`` of float64 [B, C, H, W] arrays
+    (CSDN page on GSPN, section 反向传播; the logit gradients are taken through
+    the sigmoid and the normalisation)."""
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    shape = x.shape
+    arrs = []
+    dts = set()
+    for a in (x, l0, l1, l2, lam, u, gy):
+        a2, dt = _as_input(np.asarray(a), shape)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    dt = dts.pop()
+    outs = {k: np.empty(shape, dtype=np.float64) for k in GRAD_NAMES}
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    L = lib if lib is not None else load()
+    B, C, H, W = shape
+    rc = L.gspn_oracle_backward(*[a.ctypes.data for a in arrs], dt, B, C, H, W,
+                                int(dirs), int(group_rows),
+                                *[outs[k].ctypes.data for k in GRAD_NAMES], int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return outs

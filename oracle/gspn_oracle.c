@@ -42,6 +42,13 @@
  *     block, in either scan order, on both axes.
  *  R7 sigmoid(+inf) = 1, sigmoid(-inf) = 0. A pixel whose in-range logits
  *     all give sigmoid 0 has no defined weights (0/0) and yields NaN.
+ *  R8 Backward pass (CSDN page, section 反向传播): the gradients are taken
+ *     with respect to this layer's own inputs -- x, lambda, the three logits
+ *     before the sigmoid and the normalisation, and u -- for a scalar loss
+ *     whose gradient dL/dy is given. The page's version stops at the gates
+ *     G1..G3; here the chain rule continues through the normalisation and
+ *     the sigmoid, since the gates are built from the logits inside the
+ *     layer.
  */
 #include "gspn_oracle.h"
 
@@ -193,6 +200,207 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
       void* ret = NULL;
       pthread_join(th[t], &ret);
       if (ret != NULL) rc = -1;
+    }
+    free(th);
+  }
+  pthread_mutex_destroy(&j.lock);
+  return rc;
+}
+
+/* ========================================================================
+ * Backward pass (CSDN page, section 反向传播 (backward pass): every input
+ * gets a gradient; the gradient of a hidden state collects what the later
+ * steps of the scan send back; the input gradient goes through the lambda
+ * (there: B) factor; the gate gradients combine the error term with the
+ * previous hidden state). Reading R8 for the logits.
+ *
+ * For one direction, with e_s = dL/dh_s (the "error term"):
+ *   e_s[o] = u gy at pixel (s, o)
+ *            + sum over the pixels o' of line s+1 that link to o (link k of
+ *              o' points at o = o' + k - 1) of w_{s+1,k}[o'] e_{s+1}[o'],
+ *              unless line s+1 restarts (then it reads nothing from line s);
+ *   d(lambda x) at (s, o) += e_s[o];
+ *   d w_{s,k}[o] = e_s[o] h_{s-1}[o+k-1] for the in-range links of a line that
+ *              does not restart;
+ *   w_k = sig_k / S, S = sum_j sig_j  =>  d sig_j = d w_j / S
+ *              - (sum_k d w_k sig_k) / S^2;
+ *   d l_j = d sig_j sig_j (1 - sig_j);
+ *   du += gy h_s (summed over directions), and finally
+ *   dx = lambda d(lambda x), dlambda = x d(lambda x).
+ * ====================================================================== */
+
+typedef struct {
+  const void *x, *l[3], *lam, *u, *gy;
+  int dt;
+  int64_t B, C, H, W, G;
+  uint32_t mask;
+  double *dx, *dl[3], *dlam, *du;
+  int64_t next_plane;
+  pthread_mutex_t lock;
+} bjob_t;
+
+/* sigmoids of the in-range links of the pixel at plane offset idx, which sits
+ * at orthogonal index o of a line of n_o pixels; returns their sum S */
+static double link_sigmoids(const bjob_t* j, int64_t idx, int64_t o, int64_t n_o,
+                            double sig[3], int in_range[3]) {
+  double S = 0.0;
+  for (int k = 0; k < 3; ++k) {
+    const int64_t q = o + k - 1;
+    in_range[k] = q >= 0 && q < n_o;
+    sig[k] = in_range[k] ? sigmoid(load_value(j->l[k], j->dt, idx)) : 0.0;
+    S += sig[k];
+  }
+  return S;
+}
+
+/* plane offset of the pixel at step s, orthogonal index o of direction d */
+static int64_t pixel_offset(const bjob_t* j, int d, int64_t s, int64_t o) {
+  const int64_t n_s = scan_len(d, j->H, j->W);
+  int64_t r, c;
+  pixel_of(d, scan_pos(d, n_s, s), o, &r, &c);
+  return r * j->W + c;
+}
+
+/* one direction over one plane: adds this direction's share of
+ * d(lambda x) into dphi, of du / gy into hsum and of the logit gradients
+ * into the output arrays */
+static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
+                           double* e_cur, double* e_next, double* dphi, double* hsum) {
+  const int64_t H = j->H, W = j->W;
+  const int64_t n_s = scan_len(d, H, W), n_o = orth_len(d, H, W);
+  const int64_t base = plane * H * W;
+
+  /* forward: every hidden state of the scan, h[s * n_o + o] */
+  for (int64_t s = 0; s < n_s; ++s) {
+    const int first = restarts(d, n_s, s, j->G);
+    for (int64_t o = 0; o < n_o; ++o) {
+      const int64_t pix = pixel_offset(j, d, s, o);
+      const int64_t idx = base + pix;
+      double acc = 0.0;
+      if (!first) {
+        double sig[3];
+        int in_range[3];
+        const double S = link_sigmoids(j, idx, o, n_o, sig, in_range);
+        for (int k = 0; k < 3; ++k)
+          if (in_range[k]) acc += (sig[k] / S) * h[(s - 1) * n_o + o + k - 1];
+      }
+      h[s * n_o + o] = acc + load_value(j->lam, j->dt, idx) * load_value(j->x, j->dt, idx);
+      hsum[pix] += h[s * n_o + o];
+    }
+  }
+
+  /* adjoint, last step first */
+  for (int64_t o = 0; o < n_o; ++o) e_next[o] = 0.0;
+  for (int64_t s = n_s - 1; s >= 0; --s) {
+    const int next_reads = s + 1 < n_s && !restarts(d, n_s, s + 1, j->G);
+    for (int64_t o = 0; o < n_o; ++o) {
+      const int64_t pix = pixel_offset(j, d, s, o);
+      const int64_t idx = base + pix;
+      double e = load_value(j->u, j->dt, idx) * load_value(j->gy, j->dt, idx);
+      if (next_reads) {
+        for (int k = 0; k < 3; ++k) {
+          const int64_t op = o - k + 1;   /* o' with o' + k - 1 == o */
+          if (op < 0 || op >= n_o) continue;
+          double sig[3];
+          int in_range[3];
+          const double S = link_sigmoids(j, base + pixel_offset(j, d, s + 1, op), op, n_o,
+                                         sig, in_range);
+          e += (sig[k] / S) * e_next[op];
+        }
+      }
+      e_cur[o] = e;
+      dphi[pix] += e;
+      if (!restarts(d, n_s, s, j->G)) {
+        double sig[3], dw[3] = {0.0, 0.0, 0.0};
+        int in_range[3];
+        const double S = link_sigmoids(j, idx, o, n_o, sig, in_range);
+        double t = 0.0;   /* sum_k dw_k sig_k */
+        for (int k = 0; k < 3; ++k) {
+          if (!in_range[k]) continue;
+          dw[k] = e * h[(s - 1) * n_o + o + k - 1];
+          t += dw[k] * sig[k];
+        }
+        for (int k = 0; k < 3; ++k) {
+          if (!in_range[k]) continue;
+          const double dsig = dw[k] / S - t / (S * S);
+          j->dl[k][idx] += dsig * sig[k] * (1.0 - sig[k]);
+        }
+      }
+    }
+    double* tmp = e_next; e_next = e_cur; e_cur = tmp;
+  }
+}
+
+static void* bworker(void* arg) {
+  bjob_t* j = (bjob_t*)arg;
+  const int64_t H = j->H, W = j->W;
+  const int64_t n_max = H > W ? H : W;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(H * W));
+  double* dphi = (double*)malloc(sizeof(double) * (size_t)(H * W));
+  double* hsum = (double*)malloc(sizeof(double) * (size_t)(H * W));
+  double* e_cur = (double*)malloc(sizeof(double) * (size_t)n_max);
+  double* e_next = (double*)malloc(sizeof(double) * (size_t)n_max);
+  void* ret = NULL;
+  if (!h || !dphi || !hsum || !e_cur || !e_next) { ret = (void*)1; goto done; }
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t plane = j->next_plane++;
+    pthread_mutex_unlock(&j->lock);
+    if (plane >= j->B * j->C) break;
+    const int64_t base = plane * H * W;
+    for (int64_t i = 0; i < H * W; ++i) {
+      dphi[i] = 0.0;
+      hsum[i] = 0.0;
+      for (int k = 0; k < 3; ++k) j->dl[k][base + i] = 0.0;
+    }
+    for (int d = 0; d < 4; ++d)
+      if (j->mask & (1u << d)) backward_plane(j, d, plane, h, e_cur, e_next, dphi, hsum);
+    for (int64_t i = 0; i < H * W; ++i) {
+      j->dx[base + i] = load_value(j->lam, j->dt, base + i) * dphi[i];
+      j->dlam[base + i] = load_value(j->x, j->dt, base + i) * dphi[i];
+      j->du[base + i] = load_value(j->gy, j->dt, base + i) * hsum[i];
+    }
+  }
+done:
+  free(h); free(dphi); free(hsum); free(e_cur); free(e_next);
+  return ret;
+}
+
+int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const void* l2,
+                         const void* lam, const void* u, const void* gy, int in_dtype,
+                         int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                         int64_t group_rows, double* dx, double* dl0, double* dl1,
+                         double* dl2, double* dlam, double* du, int nthreads) {
+  if (!x || !l0 || !l1 || !l2 || !lam || !u || !gy) return -1;
+  if (!dx || !dl0 || !dl1 || !dl2 || !dlam || !du) return -1;
+  if (B < 0 || C < 0 || H <= 0 || W <= 0) return -1;
+  if (dir_mask == 0 || dir_mask > 15) return -1;
+  if (group_rows < 0) return -1;
+  if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16)
+    return -1;
+  if (B * C == 0) return 0;
+
+  bjob_t j;
+  j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u; j.gy = gy;
+  j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
+  j.mask = dir_mask;
+  j.dx = dx; j.dl[0] = dl0; j.dl[1] = dl1; j.dl[2] = dl2; j.dlam = dlam; j.du = du;
+  j.next_plane = 0;
+  pthread_mutex_init(&j.lock, NULL);
+
+  int nt = nthreads <= 0 ? 1 : nthreads;
+  if ((int64_t)nt > B * C) nt = (int)(B * C);
+  int rc = 0;
+  if (nt == 1) {
+    if (bworker(&j) != NULL) rc = -1;
+  } else {
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    if (!th) { pthread_mutex_destroy(&j.lock); return -1; }
+    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, bworker, &j);
+    for (int t = 0; t < nt; ++t) {
+      void* r = NULL;
+      pthread_join(th[t], &r);
+      if (r != NULL) rc = -1;
     }
     free(th);
   }

@@ -52,6 +52,19 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
                           int64_t W, uint32_t dir_mask, int64_t group_rows,
                           double* out, int nthreads);
 
+/*
+ * Backward pass (CSDN page, section 反向传播): given gy = dL/dy (same layout
+ * and element type as the inputs), writes dL/dx, dL/dl0, dL/dl1, dL/dl2,
+ * dL/dlambda and dL/du as B*C*H*W doubles each (the logit gradients go
+ * through the sigmoid and the normalisation). Same arguments and return
+ * value as gspn_oracle_propagate otherwise.
+ */
+int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const void* l2,
+                         const void* lam, const void* u, const void* gy, int in_dtype,
+                         int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                         int64_t group_rows, double* dx, double* dl0, double* dl1,
+                         double* dl2, double* dlam, double* du, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -73,6 +73,21 @@ def _step_matrix(d, H, W, s, lg):
 def gmatrix_plane(x, lg, lam, d, G):
     """h for one plane and direction via the unrolled form H = G X."""
     H, W = x.shape
+    Gm, lines = gmatrix_of(H, W, lg, lam, d, G)
+    n_o = len(lines[0])
+    X = np.array([x[p] for line in lines for p in line])
+    Hv = Gm @ X
+    h = np.zeros((H, W))
+    for i, line in enumerate(lines):
+        for o, p in enumerate(line):
+            h[p] = Hv[i * n_o + o]
+    return h
+
+
+def gmatrix_of(H, W, lg, lam, d, G):
+    """The explicit block lower-triangular G of one plane and direction (rows
+    and columns in scan order: line by line, orthogonal index fastest) and
+    the (row, col) pixels of each line."""
     n_s = H if d < 2 else W
     n_o = W if d < 2 else H
     ws = [_step_matrix(d, H, W, s, lg) for s in range(n_s)]
@@ -88,13 +103,7 @@ def gmatrix_plane(x, lg, lam, d, G):
                 prod = ws[r] @ prod
             lam_j = np.diag([lam[p] for p in lines[j]])
             Gm[i * n_o:(i + 1) * n_o, j * n_o:(j + 1) * n_o] = prod @ lam_j
-    X = np.array([x[p] for line in lines for p in line])
-    Hv = Gm @ X
-    h = np.zeros((H, W))
-    for i, line in enumerate(lines):
-        for o, p in enumerate(line):
-            h[p] = Hv[i * n_o + o]
-    return h
+    return Gm, lines
 
 
 def gmatrix_reference(x, l0, l1, l2, lam, u, dirs, G):
@@ -305,6 +314,11 @@ def load_golden(path):
             assert a.shape == (H, W), (c["name"], a.shape)
             return a.reshape(1, 1, H, W)
         inputs = tuple(grid(c[k]) for k in ("x", "l0", "l1", "l2", "lam", "u"))
-        out.append({"name": c["name"], "dirs": int(c["dirs"]), "G": int(c["G"]),
-                    "inputs": inputs, "y": grid(c["y"])})
+        case = {"name": c["name"], "dirs": int(c["dirs"]), "G": int(c["G"]),
+                "inputs": inputs, "y": grid(c["y"])}
+        # backward examples also give gy and the six gradients
+        for k in ("gy", "dx", "dl0", "dl1", "dl2", "dlam", "du"):
+            if k in c:
+                case[k] = grid(c[k])
+        out.append(case)
     return out
