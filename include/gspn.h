@@ -67,7 +67,7 @@ typedef enum {
   GSPN_E_GROUP = 4,     /* group_rows < 0                                  */
   GSPN_E_DTYPE = 5,     /* dtype is not a gspn_dtype                       */
   GSPN_E_ALIGN = 6,     /* a pointer is not aligned to its element size    */
-  GSPN_E_ALIAS = 7,     /* out overlaps an input                           */
+  GSPN_E_ALIAS = 7,     /* an output overlaps an input or another output   */
   GSPN_E_NOMEM = 8,     /* the stream-ordered workspace allocation failed  */
   GSPN_E_HIP = 9,       /* a HIP call or kernel launch failed              */
   GSPN_E_WORKSPACE = 10 /* workspace is NULL or smaller than required      */
@@ -155,6 +155,64 @@ const char* gspn_last_error(void);
 
 /* gspn_abi_version -- version of this ABI (bumped on incompatible change). */
 int gspn_abi_version(void);
+
+/*
+ * gspn_propagate_backward -- gradients of every input of gspn_propagate
+ * (CSDN page, section 反向传播: the gradient of a line's hidden state collects
+ * what the later lines send back, the input gradient goes through the lambda
+ * factor, and the gate gradients pair the error term with the previous hidden
+ * state). For a scalar loss L and grad_out = dL/dout:
+ *   e_{d,s} = u (.) grad_out + w_{d,s+1}^T e_{d,s+1}
+ *       (reverse scan with the transposed tridiagonal; a line that restarts
+ *        sends nothing back to the line before it)
+ *   grad_x      = lambda (.) sum_d e_d
+ *   grad_lambda = x (.) sum_d e_d
+ *   grad_u      = grad_out (.) sum_d h_d
+ *   grad_logits[k] at pixel (s, o) = sum_d e_{d,s}[o] w_k (1 - sigmoid(l_k))
+ *       (h_{d,s-1}[o+k-1] - sum_j w_j h_{d,s-1}[o+j-1])
+ *       -- the chain rule through the row normalisation and the sigmoid;
+ *       0 on restart lines and for links that would leave the image.
+ * Problem arguments (x, w_logits, lambda, u, B, C, H, W, dir_mask,
+ * group_rows, dtype, stream) as for gspn_propagate. grad_out has the same
+ * layout and dtype. grad_x, grad_logits[0..2], grad_lambda and grad_u are
+ * [B, C, H, W] in dtype (bf16 rounded once from the fp32 result),
+ * write-only, fully overwritten, and may not overlap an input or each other
+ * (GSPN_E_ALIAS). Scratch memory (gspn_backward_workspace_bytes) is taken
+ * with hipMallocAsync and given back with hipFreeAsync on `stream`.
+ * Errors as for gspn_propagate.
+ */
+gspn_status gspn_propagate_backward(const void* x, const void* const w_logits[3],
+                                    const void* lambda, const void* u,
+                                    const void* grad_out, int64_t B, int64_t C,
+                                    int64_t H, int64_t W, uint32_t dir_mask,
+                                    int64_t group_rows, gspn_dtype dtype,
+                                    void* grad_x, void* const grad_logits[3],
+                                    void* grad_lambda, void* grad_u,
+                                    hipStream_t stream);
+
+/* gspn_backward_workspace_bytes -- scratch bytes gspn_propagate_backward_ws
+ * needs (0 for invalid arguments, which the call itself reports). */
+size_t gspn_backward_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                                     uint32_t dir_mask, int64_t group_rows,
+                                     gspn_dtype dtype);
+
+/* gspn_propagate_backward_ws -- gspn_propagate_backward with caller-owned
+ * scratch memory, under the same rules as gspn_propagate_ws. */
+gspn_status gspn_propagate_backward_ws(const void* x, const void* const w_logits[3],
+                                       const void* lambda, const void* u,
+                                       const void* grad_out, int64_t B, int64_t C,
+                                       int64_t H, int64_t W, uint32_t dir_mask,
+                                       int64_t group_rows, gspn_dtype dtype,
+                                       void* grad_x, void* const grad_logits[3],
+                                       void* grad_lambda, void* grad_u,
+                                       void* workspace, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* gspn_backward_plan_name -- kernel plan gspn_propagate_backward would use,
+ * or "invalid". Host-only. */
+const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
+                                    uint32_t dir_mask, int64_t group_rows,
+                                    gspn_dtype dtype);
 
 #ifdef __cplusplus
 }

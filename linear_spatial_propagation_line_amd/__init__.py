@@ -74,6 +74,16 @@ def lib() -> ctypes.CDLL:
         L.gspn_trace_kernel.restype = ctypes.c_char_p
         L.gspn_abi_version.argtypes = []
         L.gspn_abi_version.restype = ctypes.c_int
+        bcommon = [vp, logits_t, vp, vp, vp, i64, i64, i64, i64, u32, i64, ctypes.c_int,
+                   vp, logits_t, vp, vp]
+        L.gspn_propagate_backward.argtypes = bcommon + [vp]
+        L.gspn_propagate_backward.restype = ctypes.c_int
+        L.gspn_propagate_backward_ws.argtypes = bcommon + [vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_backward_ws.restype = ctypes.c_int
+        L.gspn_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.gspn_backward_plan_name.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_backward_plan_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -152,3 +162,61 @@ def propagate_alloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out
     _check(lib().gspn_propagate(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H, W,
                                 dirs, group_rows, dt, out.data_ptr(), sptr))
     return out
+
+
+def backward_workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
+    return int(lib().gspn_backward_workspace_bytes(B, C, H, W, dirs, group_rows, dtype))
+
+
+def backward_plan_name(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> str:
+    return lib().gspn_backward_plan_name(B, C, H, W, dirs, group_rows, dtype).decode()
+
+
+GRAD_NAMES = ("x", "l0", "l1", "l2", "lam", "u")
+
+
+def propagate_backward(x, logits, lam, u, grad_out, dirs: int = ALL, group_rows: int = 0,
+                       grads=None, workspace=None, stream=None, alloc: bool = False) -> dict:
+    """Gradients of a loss with respect to every input of propagate(), given
+    ``grad_out`` = dL/dout: a dict ``{"x", "l0", "l1", "l2", "lam", "u"}`` of
+    tensors shaped and typed like the inputs (``grads`` may supply them).
+    ``alloc=True`` lets the library take its own workspace (the plain
+    gspn_propagate_backward entry point)."""
+    import torch
+    l0, l1, l2 = logits
+    ts = (x, l0, l1, l2, lam, u, grad_out)
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("all inputs must be torch tensors on a GPU device")
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous tensors of one shape and dtype")
+    if x.dim() != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    dt = _dtype_code(x)
+    if grads is None:
+        grads = {k: torch.empty_like(x) for k in GRAD_NAMES}
+    for k in GRAD_NAMES:
+        t = grads[k]
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("gradient tensors must match the inputs")
+    L = lib()
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    dlg = (ctypes.c_void_p * 3)(grads["l0"].data_ptr(), grads["l1"].data_ptr(),
+                                grads["l2"].data_ptr())
+    args = (x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), grad_out.data_ptr(), B, C, H, W,
+            dirs, group_rows, dt, grads["x"].data_ptr(), dlg, grads["lam"].data_ptr(),
+            grads["u"].data_ptr())
+    if alloc:
+        _check(L.gspn_propagate_backward(*args, sptr))
+        return grads
+    need = int(L.gspn_backward_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.gspn_propagate_backward_ws(*args, ws_ptr, ws_len, sptr))
+    return grads

@@ -193,6 +193,104 @@ const char* plan_str(Plan p) {
   }
 }
 
+// ---- backward pass ---------------------------------------------------------
+enum class BPlan { kInvalid, kStream };
+
+struct BChecked {
+  gspn_status status;
+  BPlan plan;
+  size_t ws_bytes;
+};
+
+BChecked check_bwd_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
+                         int dtype) {
+  BChecked r{GSPN_OK, BPlan::kInvalid, 0};
+  const Checked f = check_shape(B, C, H, W, mask, G, dtype);
+  if (f.status != GSPN_OK) {
+    r.status = f.status;
+    return r;
+  }
+  r.plan = BPlan::kStream;
+  r.ws_bytes = gspn::bwd_stream_workspace_bytes(B * C, H, W, mask);
+  return r;
+}
+
+const char* bplan_str(BPlan p) {
+  switch (p) {
+    case BPlan::kStream: return "bwd_stream";
+    default: return "invalid";
+  }
+}
+
+gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const void* lambda,
+                          const void* u, const void* gy, int64_t B, int64_t C, int64_t H,
+                          int64_t W, uint32_t mask, int64_t G, gspn_dtype dtype, void* dx,
+                          void* const dlogits[3], void* dlam, void* du, BChecked* chk,
+                          gspn::BwdProblem* pr) {
+  if (!x || !w_logits || !lambda || !u || !gy || !dx || !dlogits || !dlam || !du)
+    return fail(GSPN_E_NULL, "inputs, grad_out and the gradient outputs must be non-null");
+  if (!w_logits[0] || !w_logits[1] || !w_logits[2] || !dlogits[0] || !dlogits[1] || !dlogits[2])
+    return fail(GSPN_E_NULL, "w_logits[0..2] and grad_logits[0..2] must be non-null");
+  *chk = check_bwd_shape(B, C, H, W, mask, G, static_cast<int>(dtype));
+  if (chk->status != GSPN_OK) return chk->status;
+  const size_t es = elem_size(dtype);
+  const void* ins[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, gy};
+  const void* outs[6] = {dx, dlogits[0], dlogits[1], dlogits[2], dlam, du};
+  for (const void* p : ins)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
+  for (const void* p : outs)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "gradient pointer not aligned to its element size");
+  const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+  for (int i = 0; i < 6; ++i) {
+    for (const void* p : ins)
+      if (overlaps(outs[i], bytes, p, bytes)) return fail(GSPN_E_ALIAS, "a gradient overlaps an input");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], bytes, outs[j], bytes))
+        return fail(GSPN_E_ALIAS, "two gradient outputs overlap");
+  }
+  pr->x = x;
+  for (int k = 0; k < 3; ++k) {
+    pr->l[k] = w_logits[k];
+    pr->dl[k] = dlogits[k];
+  }
+  pr->lam = lambda;
+  pr->u = u;
+  pr->gy = gy;
+  pr->dx = dx;
+  pr->dlam = dlam;
+  pr->du = du;
+  pr->B = B; pr->C = C; pr->H = H; pr->W = W;
+  pr->mask = mask;
+  pr->G = G;
+  pr->dtype = dtype;
+  return GSPN_OK;
+}
+
+gspn_status run_bwd(const gspn::BwdProblem& pr, BPlan plan, void* ws, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  gspn::Tracer tr;
+  tr.events = g_trace_events;
+  tr.pairs = g_trace_pairs;
+  switch (plan) {
+    case BPlan::kStream:
+      e = gspn::launch_bwd_stream(pr, ws, stream, &tr);
+      break;
+    default:
+      return fail(GSPN_E_SHAPE, "no backward plan");
+  }
+  if (g_trace_events) {
+    g_trace_count = tr.count;
+    for (int i = 0; i < gspn::kTraceMax; ++i) {
+      g_trace_names[i] = tr.names[i];
+      g_trace_planes[i] = tr.planes[i];
+    }
+  }
+  if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
+  return GSPN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,5 +396,81 @@ const char* gspn_status_str(gspn_status s) {
 const char* gspn_last_error(void) { return g_last_error.c_str(); }
 
 int gspn_abi_version(void) { return 1; }
+
+gspn_status gspn_propagate_backward(const void* x, const void* const w_logits[3],
+                                    const void* lambda, const void* u, const void* grad_out,
+                                    int64_t B, int64_t C, int64_t H, int64_t W,
+                                    uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
+                                    void* grad_x, void* const grad_logits[3], void* grad_lambda,
+                                    void* grad_u, hipStream_t stream) {
+  BChecked chk;
+  gspn::BwdProblem pr;
+  gspn_status s = check_all_bwd(x, w_logits, lambda, u, grad_out, B, C, H, W, dir_mask,
+                                group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u,
+                                &chk, &pr);
+  if (s != GSPN_OK) return s;
+  if (B * C == 0) return GSPN_OK;
+  void* ws = nullptr;
+  if (chk.ws_bytes > 0) {
+    hipError_t e = hipMallocAsync(&ws, chk.ws_bytes, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(GSPN_E_NOMEM, hipGetErrorString(e));
+    }
+  }
+  s = run_bwd(pr, chk.plan, ws, stream);
+  if (ws) {
+    hipError_t e = hipFreeAsync(ws, stream);
+    if (e != hipSuccess && s == GSPN_OK) s = fail(GSPN_E_HIP, hipGetErrorString(e));
+  }
+  return s;
+}
+
+size_t gspn_backward_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                                     uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  g_last_error = keep;
+  return chk.status == GSPN_OK ? chk.ws_bytes : 0;
+}
+
+gspn_status gspn_propagate_backward_ws(const void* x, const void* const w_logits[3],
+                                       const void* lambda, const void* u, const void* grad_out,
+                                       int64_t B, int64_t C, int64_t H, int64_t W,
+                                       uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
+                                       void* grad_x, void* const grad_logits[3],
+                                       void* grad_lambda, void* grad_u, void* workspace,
+                                       size_t ws_bytes, hipStream_t stream) {
+  BChecked chk;
+  gspn::BwdProblem pr;
+  gspn_status s = check_all_bwd(x, w_logits, lambda, u, grad_out, B, C, H, W, dir_mask,
+                                group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u,
+                                &chk, &pr);
+  if (s != GSPN_OK) return s;
+  if (chk.ws_bytes > 0) {
+    if (!workspace || ws_bytes < chk.ws_bytes)
+      return fail(GSPN_E_WORKSPACE,
+                  "workspace missing or smaller than gspn_backward_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t bytes = static_cast<size_t>(B * C * H * W) * elem_size(dtype);
+    const void* all[13] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, grad_out,
+                           grad_x, grad_logits[0], grad_logits[1], grad_logits[2],
+                           grad_lambda, grad_u};
+    for (const void* p : all)
+      if (overlaps(workspace, chk.ws_bytes, p, bytes))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  if (B * C == 0) return GSPN_OK;
+  return run_bwd(pr, chk.plan, workspace, stream);
+}
+
+const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
+                                    uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  g_last_error = keep;
+  return chk.status == GSPN_OK ? bplan_str(chk.plan) : "invalid";
+}
 
 }  // extern "C"

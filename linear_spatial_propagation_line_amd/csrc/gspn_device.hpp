@@ -82,6 +82,32 @@ __device__ __forceinline__ Weights make_weights(float l0, float l1, float l2,
   return Weights{p12 * r, p02 * r, p01 * r};
 }
 
+// Weights and their sigmoid slopes for the backward pass: q_k = w_k (1 -
+// sigmoid(l_k)), with 1 - sigmoid(l) = exp(-l) / (1 + exp(-l)) taken from the
+// same exponentials (no cancellation as sigmoid -> 1). Out-of-range links
+// have w_k = q_k = 0.
+struct WeightSlopes {
+  float w0, w1, w2, q0, q1, q2;
+};
+
+__device__ __forceinline__ WeightSlopes make_weight_slopes(float l0, float l1, float l2,
+                                                           float m0, float m2) {
+  const float e0 = exp_neg(l0), e1 = exp_neg(l1), e2 = exp_neg(l2);
+  const float a0 = 1.0f + e0, a1 = 1.0f + e1, a2 = 1.0f + e2;
+  const float p12 = (m0 * a1) * a2;
+  const float p02 = a0 * a2;
+  const float p01 = (m2 * a0) * a1;
+  const float r = recip(p12 + p02 + p01);
+  WeightSlopes q;
+  q.w0 = p12 * r;
+  q.w1 = p02 * r;
+  q.w2 = p01 * r;
+  q.q0 = q.w0 * (e0 * recip(a0));
+  q.q1 = q.w1 * (e1 * recip(a1));
+  q.q2 = q.w2 * (e2 * recip(a2));
+  return q;
+}
+
 // Renormalise already normalised interior weights for an edge pixel whose
 // side neighbours may be missing: w_k' = m_k w_k / sum_j m_j w_j.
 __device__ __forceinline__ Weights edge_weights(float w0, float w1, float w2,

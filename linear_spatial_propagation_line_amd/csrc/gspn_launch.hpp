@@ -24,6 +24,24 @@ struct Problem {
   bool aligned_pair;   // every pointer aligned to 2 elements
 };
 
+// A validated backward problem: the forward inputs, grad_out (gy) and the six
+// gradient outputs, all of one dtype and layout.
+struct BwdProblem {
+  const void* x;
+  const void* l[3];
+  const void* lam;
+  const void* u;
+  const void* gy;
+  void* dx;
+  void* dl[3];
+  void* dlam;
+  void* du;
+  int64_t B, C, H, W;
+  uint32_t mask;
+  int64_t G;
+  gspn_dtype dtype;
+};
+
 // Records caller-owned events around kernel launches (gspn_trace_events),
 // and the kernel name and plane count of each launch.
 constexpr int kTraceMax = 16;
@@ -61,5 +79,9 @@ hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer*
 // streaming per-direction path (gspn_stream.hip)
 int64_t stream_max_orth();
 hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Tracer* tr);
+
+// backward pass, streaming path for any plane (gspn_bwd_stream.hip)
+size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask);
+hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
 }  // namespace gspn

@@ -19,7 +19,9 @@ weights):
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
 generator seeded with 1000 + k (k = 1..5 in the order above) and then cast
-(round-to-nearest-even) to the storage type.
+(round-to-nearest-even) to the storage type. The output gradient of the
+backward pass (make_grad_out) is N(0, 1) from a generator seeded with
+2000 + k, cast the same way.
 """
 from __future__ import annotations
 
@@ -117,3 +119,17 @@ def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
                        ("l0", w.logits), ("l1", w.logits), ("l2", w.logits)):
         out[name] = _draw(spec, shape, gen, device).to(w.torch_dtype)
     return out
+
+
+def make_grad_out(w: Workload | str, seed: int | None = None, device="cpu",
+                  B: int | None = None, C: int | None = None, H: int | None = None,
+                  W: int | None = None) -> torch.Tensor:
+    """dL/dout for the backward pass: N(0, 1) in the workload's storage dtype."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    shape = (B or w.B, C or w.C, H or w.H, W or w.W)
+    if seed is None:
+        seed = 2000 + w.index
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(w.torch_dtype)

@@ -5,6 +5,12 @@ the oracle output, rms is taken over the whole compared tensor (outputs are
 roughly zero-mean, so a purely relative bound is meaningless near zero), and
 rtol = 1e-5 for float32 storage, 1e-2 for bfloat16 storage with fp32
 accumulation.
+
+Gradients (backward pass) use the same bound per tensor, with one more term
+in the scale: 1e-3 of the largest rms among the six gradient tensors of the
+call. It only matters for a tensor that is (nearly) zero everywhere -- the
+logit gradients of a one-pixel-wide line, or under Theorem 1 -- where the
+oracle's own fp64 rounding (~1e-16) would otherwise set the scale.
 """
 from __future__ import annotations
 
@@ -46,3 +52,31 @@ def assert_parity(got: torch.Tensor, ref: np.ndarray, what: str = "") -> float:
     err = scaled_error(got, ref)
     assert err <= rtol, f"{what}: scaled error {err:.3e} > {rtol:.0e}"
     return err
+
+
+GRAD_NAMES = ("x", "l0", "l1", "l2", "lam", "u")
+
+
+def oracle_grads(inp: dict, gy: torch.Tensor, dirs: int, G: int, nthreads=None) -> dict:
+    arrs = [to_oracle_array(inp[k]) for k in ("x", "l0", "l1", "l2", "lam", "u")]
+    return oracle.backward(*arrs, to_oracle_array(gy), dirs=dirs, group_rows=G,
+                           nthreads=nthreads)
+
+
+def assert_grad_parity(got: dict, ref: dict, what: str = "", names=GRAD_NAMES) -> float:
+    """Every gradient tensor in ``names`` within the dtype's bound; returns the
+    worst scaled error."""
+    floor = 1e-3 * max(float(np.sqrt(np.mean(ref[k] * ref[k]))) for k in GRAD_NAMES)
+    worst = 0.0
+    for k in names:
+        g_t = got[k]
+        rtol = RTOL[g_t.dtype]
+        assert tuple(g_t.shape) == ref[k].shape, (k, g_t.shape, ref[k].shape)
+        g = g_t.detach().float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(g)), f"{what} d{k}: non-finite gradient"
+        o = ref[k]
+        rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
+        err = float(np.max(np.abs(g - o) / (np.abs(o) + rms + floor + 1e-300))) if o.size else 0.0
+        assert err <= rtol, f"{what} d{k}: scaled error {err:.3e} > {rtol:.0e}"
+        worst = max(worst, err)
+    return worst

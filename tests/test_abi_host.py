@@ -122,3 +122,69 @@ def test_workspace_and_plans(L, monkeypatch):
     monkeypatch.setenv("GSPN_FORCE_PLAN", "tpipe")
     assert g.plan_name(1, 2, 8, 8) == "tpipe"
     assert g.plan_name(1, 2, 7, 8) == "plane16"           # tpipe needs even sizes
+
+
+def bcall(L, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), gy=BASE + 6 * SZ,
+          outs=(BASE + 7 * SZ, BASE + 8 * SZ, BASE + 9 * SZ, BASE + 10 * SZ, BASE + 11 * SZ,
+                BASE + 12 * SZ), B=1, C=1, H=8, W=8, mask=15, G=0, dt=0, ws=None, ws_bytes=0,
+          use_ws=False):
+    arr = (ctypes.c_void_p * 3)(*lg)
+    dlg = None if outs[1] is None and outs[2] is None and outs[3] is None else \
+        (ctypes.c_void_p * 3)(*outs[1:4])
+    args = (BASE, arr, BASE + 4 * SZ, BASE + 5 * SZ, gy, B, C, H, W, mask, G, dt, outs[0], dlg,
+            outs[4], outs[5])
+    if use_ws:
+        return L.gspn_propagate_backward_ws(*args, ws, ws_bytes, None)
+    return L.gspn_propagate_backward(*args, None)
+
+
+@pytest.fixture(scope="module")
+def LB(L):
+    g.lib()   # sets the backward argtypes
+    return L
+
+
+O = BASE + 7 * SZ
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(gy=None), "GSPN_E_NULL"),
+    (dict(outs=(None, O + SZ, O + 2 * SZ, O + 3 * SZ, O + 4 * SZ, O + 5 * SZ)), "GSPN_E_NULL"),
+    (dict(outs=(O, None, None, None, O + 4 * SZ, O + 5 * SZ)), "GSPN_E_NULL"),
+    (dict(outs=(O, O + SZ, None, O + 3 * SZ, O + 4 * SZ, O + 5 * SZ)), "GSPN_E_NULL"),
+    (dict(H=0), "GSPN_E_SHAPE"),
+    (dict(mask=0), "GSPN_E_DIRMASK"),
+    (dict(G=-2), "GSPN_E_GROUP"),
+    (dict(dt=7), "GSPN_E_DTYPE"),
+    (dict(gy=BASE + 6 * SZ + 2), "GSPN_E_ALIGN"),
+    (dict(outs=(O + 1, O + SZ, O + 2 * SZ, O + 3 * SZ, O + 4 * SZ, O + 5 * SZ), dt=1), "GSPN_E_ALIGN"),
+    (dict(outs=(BASE + 8, O + SZ, O + 2 * SZ, O + 3 * SZ, O + 4 * SZ, O + 5 * SZ)), "GSPN_E_ALIAS"),
+    (dict(outs=(O, O + SZ, O + 2 * SZ, O + 3 * SZ, O + 4 * SZ, BASE + 6 * SZ)), "GSPN_E_ALIAS"),
+    (dict(outs=(O, O + SZ, O + 2 * SZ, O + 3 * SZ, O + 4 * SZ, O + 16)), "GSPN_E_ALIAS"),
+])
+def test_backward_rejects_bad_arguments(LB, kw, status, use_ws):
+    assert bcall(LB, use_ws=use_ws, **kw) == g.STATUS[status]
+    assert LB.gspn_last_error().decode() != ""
+
+
+def test_backward_workspace_checks(LB):
+    need = g.backward_workspace_bytes(2, 3, 30, 20)
+    assert need == 6 * 2 * 3 * 30 * 20 * 4
+    assert g.backward_workspace_bytes(2, 3, 30, 20, dirs=g.L2R) == 2 * 3 * 30 * 20 * 4
+    assert g.backward_workspace_bytes(1, 1, 0, 20) == 0
+    assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True, ws=BASE + 13 * SZ,
+                 ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True, ws=BASE + 13 * SZ + 16,
+                 ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]
+    assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True, ws=BASE + 12 * SZ,
+                 ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]
+    assert bcall(LB, B=0, use_ws=True) == 0
+    assert bcall(LB, C=0) == 0
+
+
+def test_backward_plans(LB):
+    assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"
+    assert g.backward_plan_name(1, 320, 2048, 1024, dtype=1) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 0, 4) == "invalid"

@@ -1,0 +1,123 @@
+"""Backward pass on the GPU vs the fp64 oracle's backward, gradient by
+gradient, on the same seeded inputs (needs an MI355X). Every call goes
+through the C ABI via the binding."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import linear_spatial_propagation_line_amd as g
+from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_grad_out, make_inputs
+from parity import GRAD_NAMES, assert_grad_parity, oracle_grads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run_bwd(inp, gy, dirs, G, **kw):
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    grads = g.propagate_backward(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"],
+                                 gy.to(DEV), dirs=dirs, group_rows=G, **kw)
+    torch.cuda.synchronize()
+    return grads
+
+
+def case(name, seed, **shape):
+    return make_inputs(name, seed=seed, **shape), make_grad_out(name, seed=seed + 7, **shape)
+
+
+@pytest.mark.parametrize("name,planes", [("tiny_16x16_t2b", None), ("cls_56x56", (8, 96)),
+                                         ("dit_16x16", (4, 1152)),
+                                         ("local_128x128_g8", (2, 192))])
+def test_workload_shapes(name, planes):
+    """The workloads' plane shapes, dtypes, direction sets and groups (fewer
+    planes than the benchmark: the fp64 oracle backward is slow)."""
+    w = WORKLOADS[name]
+    B, C = planes if planes else (w.B, w.C)
+    print(f"[bwd] {name} B={B} C={C} plan={g.backward_plan_name(B, C, w.H, w.W, w.dirs, w.group_rows, 0 if w.dtype == 'f32' else 1)}", flush=True)
+    inp, gy = case(name, 5, B=B, C=C)
+    got = run_bwd(inp, gy, w.dirs, w.group_rows)
+    err = assert_grad_parity(got, oracle_grads(inp, gy, w.dirs, w.group_rows), name)
+    print(f"[bwd] {name} worst scaled error {err:.3e}", flush=True)
+
+
+SHAPES = [(1, 1, 1, 1), (1, 2, 1, 7), (1, 2, 7, 1), (1, 3, 16, 16), (2, 2, 13, 11),
+          (1, 2, 17, 16), (1, 2, 64, 64), (1, 2, 65, 64), (1, 1, 100, 300), (1, 1, 300, 100),
+          (1, 1, 1, 1000), (1, 1, 777, 1), (1, 1, 1030, 40)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(shape, dtype):
+    B, C, H, W = shape
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, hash(shape) % 10000, B=B, C=C, H=H, W=W)
+    for G in (0, 3):
+        got = run_bwd(inp, gy, 15, G)
+        assert_grad_parity(got, oracle_grads(inp, gy, 15, G), f"{shape} G={G}")
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (1, 2, 40, 24), (1, 2, 96, 80)])
+def test_every_direction_mask(shape):
+    B, C, H, W = shape
+    inp, gy = case("cls_56x56", 21, B=B, C=C, H=H, W=W)
+    for mask in range(1, 16):
+        got = run_bwd(inp, gy, mask, 0)
+        assert_grad_parity(got, oracle_grads(inp, gy, mask, 0), f"{shape} mask={mask}")
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 16, 16), (1, 2, 48, 40), (1, 2, 130, 70)])
+@pytest.mark.parametrize("G", [1, 2, 5, 8, 16, 1000])
+def test_local_groups(shape, G):
+    B, C, H, W = shape
+    inp, gy = case("local_128x128_g8", 33 + G, B=B, C=C, H=H, W=W)
+    got = run_bwd(inp, gy, 15, G)
+    assert_grad_parity(got, oracle_grads(inp, gy, 15, G), f"{shape} G={G}")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 16, 16), (1, 2, 56, 56), (1, 1, 150, 90)])
+def test_invariant_zero_logit_gradients(shape):
+    """Theorem 1: with lambda x = 1 every predecessor of a pixel holds the same
+    state, so the logit gradients vanish. In fp32 the neighbouring states still
+    differ by rounding (sum_k w_k is 1 only to ~1 ulp), so the logit gradients
+    are bounded by a few ulps of e * h instead of compared with the oracle's
+    zeros; the other gradients are compared as usual."""
+    B, C, H, W = shape
+    inp, gy = case("cls_56x56", 8, B=B, C=C, H=H, W=W)
+    inp["x"] = torch.ones_like(inp["x"])
+    inp["lam"] = torch.ones_like(inp["lam"])
+    got = run_bwd(inp, gy, 15, 0)
+    assert_grad_parity(got, oracle_grads(inp, gy, 15, 0), f"invariant {shape}",
+                       names=("x", "lam", "u"))
+    e_max = got["x"].abs().max().item()          # lambda = 1: dx = sum_d e_d
+    h_max = float(H + W + 2)                     # sum_d h_d under Theorem 1
+    for k in ("l0", "l1", "l2"):
+        assert got[k].abs().max().item() <= 1e-5 * e_max * h_max, k
+
+
+def test_alloc_entry_point_matches_workspace_entry_point():
+    inp, gy = case("cls_56x56", 4, B=1, C=3, H=70, W=90)
+    a = run_bwd(inp, gy, 15, 0)
+    b = run_bwd(inp, gy, 15, 0, alloc=True)
+    for k in GRAD_NAMES:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_deterministic():
+    inp, gy = case("cls_56x56", 9, B=2, C=4, H=56, W=56)
+    a = run_bwd(inp, gy, 15, 0)
+    for _ in range(2):
+        b = run_bwd(inp, gy, 15, 0)
+        for k in GRAD_NAMES:
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_binding_rejects_aliased_gradients():
+    x = torch.zeros(1, 1, 4, 4, device=DEV)
+    t = [torch.zeros_like(x) for _ in range(6)]
+    grads = dict(zip(GRAD_NAMES, t))
+    grads["u"] = grads["x"]
+    with pytest.raises(g.GspnError) as ei:
+        g.propagate_backward(x, (t[0], t[1], t[2]), t[3], t[4], t[5], grads=grads)
+    assert ei.value.name == "GSPN_E_ALIAS"
