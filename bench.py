@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the GSPN 2D line-scan propagation on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--backward]
 
 One step = one full propagation (all selected scan directions, fused merge)
 over one batch of seeded synthetic inputs already resident in HBM. Prints ONE
@@ -16,6 +16,9 @@ JSON line:
             counter summary when it was taken on the current kernel sources
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
             workload on this host's cores (rank 0, N = 1 only)
+With --backward a step is one backward pass instead (gradients of x, lambda,
+the three logits and u for a seeded dL/dout), with Q_min = 13 s per pixel
+(seven tensors read, six written).
 """
 from __future__ import annotations
 
@@ -31,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GSPN propagated elem-steps/s (B·C·H·W·dirs) + achieved HBM GB/s vs peak"
+METRIC_BWD = "GSPN backward elem-steps/s (B·C·H·W·dirs) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "t2i_2048x1024"
 CSRC = os.path.join(ROOT, "linear_spatial_propagation_line_amd", "csrc")
@@ -45,6 +49,9 @@ PLAN_SOURCES = {
     "band": ("gspn_band.hip", "gspn_device.hpp"),
     "tpipe": ("gspn_tpipe.hip", "gspn_device.hpp"),
     "stream": ("gspn_stream.hip", "gspn_device.hpp"),
+    "bwd_plane16": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
+    "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
+    "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
 }
 
 
@@ -106,6 +113,16 @@ def design_bytes(kernel: str, planes: int, w) -> float:
           tp_vfwd  5 s inputs + (4 + 3 s) copy write + 4/8 checkpoints
           tp_hpair 2 (4 + 3 s) copy reads + 2 * 4/4 checkpoints + 4 sum write
           tp_vbwd  5 s inputs + 4/8 checkpoints + 4 sum read + s (u) + s (out)
+    Backward pass:
+      bplane_kernel16/64: x, lambda, l0, l1, l2, u, grad_out read once, six
+          gradients written -> 13 s (the second read of five inputs in the
+          gradient phase comes from L2)
+      bwd_fwd  5 s inputs + 4 state write + 4 running sum of h
+      bwd_adj  5 s (u, grad_out, logits) + 4 state read + 16 accumulator
+          write + 16 accumulator read (a middle direction; approximate)
+      bwd_transpose  seven inputs read and written (2 * 7 s), or, over 5x the
+          planes, the fp32 accumulators (2 * 4)
+      bwd_finish  5 * 4 accumulators + 3 s (x, lambda, grad_out) + 6 s out
     """
     s = 4 if w.dtype == "f32" else 2
     px = planes * w.H * w.W
@@ -118,6 +135,12 @@ def design_bytes(kernel: str, planes: int, w) -> float:
         "tp_vfwd": 5 * s + (4 + 3 * s if hz else 0) + (0.5 if w.dirs & 1 else 0),
         "tp_hpair": 2 * (4 + 3 * s) + 2.0 + 4,
         "tp_vbwd": 5 * s + (0.5 if w.dirs & 1 else 0) + (4 if hz else 0) + 2 * s,
+        "bplane_kernel16": 13 * s,
+        "bplane_kernel64": 13 * s,
+        "bwd_fwd": 5 * s + 8,
+        "bwd_adj": 5 * s + 4 + 32,
+        "bwd_transpose": 2 * 7 * s if planes == w.B * w.C else 2 * 4,
+        "bwd_finish": 20 + 9 * s,
     }[kernel]
     return per * px
 
@@ -143,30 +166,37 @@ def counter_traffic(plan: str, workload: str, digest: str):
         return None
 
 
-def cpu_baseline(inp_dev, w, planes: int):
+def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
     """The oracle as it stands on the first `planes` planes of the same
-    device-resident inputs, all host cores."""
+    device-resident inputs, all host cores (its backward pass when grad_out
+    is given)."""
     import numpy as np
     import torch
 
     import oracle
     cores = len(os.sched_getaffinity(0))
     planes = max(1, min(planes, w.B * w.C))
-    # planes are contiguous in [B, C, H, W]; take the first `planes` of them
-    arrs = []
-    for k in ("x", "l0", "l1", "l2", "lam", "u"):
-        t = inp_dev[k].reshape(-1, w.H, w.W)[:planes].cpu().contiguous()
+
+    def host(t):
+        # planes are contiguous in [B, C, H, W]; take the first `planes` of them
+        t = t.reshape(-1, w.H, w.W)[:planes].cpu().contiguous()
         if t.dtype == torch.bfloat16:
-            arrs.append(t.view(torch.int16).numpy().view(np.uint16).reshape(1, planes, w.H, w.W))
-        else:
-            arrs.append(t.numpy().reshape(1, planes, w.H, w.W))
+            return t.view(torch.int16).numpy().view(np.uint16).reshape(1, planes, w.H, w.W)
+        return t.numpy().reshape(1, planes, w.H, w.W)
+
+    arrs = [host(inp_dev[k]) for k in ("x", "l0", "l1", "l2", "lam", "u")]
     threads = min(cores, planes)
     t0 = time.perf_counter()
-    oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
+    if grad_out is None:
+        oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
+    else:
+        oracle.backward(*arrs, host(grad_out), dirs=w.dirs, group_rows=w.group_rows,
+                        nthreads=threads)
     dt = time.perf_counter() - t0
     steps = planes * w.H * w.W * w.ndirs
+    what = "backward " if grad_out is not None else ""
     return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, {w.ndirs} dirs), "
+            "sample": f"{what}first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, {w.ndirs} dirs), "
                       f"{steps} elem-steps in {dt:.2f} s"}
 
 
@@ -203,6 +233,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough wall time of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (all six gradients) instead of the forward")
     ap.add_argument("--calibrate", action="store_true",
                     help="time a plain device copy and a read-only reduction of known size "
                          "(the reference points for HBM bandwidth and for counter scaling)")
@@ -220,35 +252,55 @@ def main() -> int:
         return calibrate(torch, args.steps)
 
     import linear_spatial_propagation_line_amd as g
-    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_grad_out, make_inputs
 
     w = WORKLOADS[args.workload]
+    bwd = args.backward
     dev = torch.device("cuda:0")
     dt_code = g.GSPN_F32 if w.dtype == "f32" else g.GSPN_BF16
-    plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+    if bwd:
+        plan = g.backward_plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+    else:
+        plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
 
     # inputs resident in HBM; small problems rotate several input sets so the
     # timed loop does not run out of the 256 MB last-level cache
     s = 4 if w.dtype == "f32" else 2
-    set_bytes = 7 * s * w.pixels
+    per_px = 13 * s if bwd else 7 * s     # compulsory bytes per pixel
+    set_bytes = per_px * w.pixels
     nsets = max(1, min(8, -(-1024 ** 3 // set_bytes)))
     sets = []
     for i in range(nsets):
+        seed = 1000 + w.index + 17 * i
         if set_bytes > 1 << 30:
-            sets.append(make_inputs(w, seed=1000 + w.index + 17 * i, device=dev))
+            st = make_inputs(w, seed=seed, device=dev)
+            if bwd:
+                st["gy"] = make_grad_out(w, seed=seed + 1000, device=dev)
         else:
-            sets.append({k: v.to(dev) for k, v in
-                         make_inputs(w, seed=1000 + w.index + 17 * i).items()})
-    outs = [torch.empty_like(st["x"]) for st in sets]
-    ws_bytes = g.workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+            st = {k: v.to(dev) for k, v in make_inputs(w, seed=seed).items()}
+            if bwd:
+                st["gy"] = make_grad_out(w, seed=seed + 1000).to(dev)
+        sets.append(st)
+    if bwd:
+        outs = [{k: torch.empty_like(st["x"]) for k in g.GRAD_NAMES} for st in sets]
+        ws_bytes = g.backward_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+    else:
+        outs = [torch.empty_like(st["x"]) for st in sets]
+        ws_bytes = g.workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         st = sets[i % nsets]
-        g.propagate(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
-                    dirs=w.dirs, group_rows=w.group_rows, out=outs[i % nsets],
-                    workspace=ws if ws_bytes else None, stream=stream)
+        if bwd:
+            g.propagate_backward(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
+                                 st["gy"], dirs=w.dirs, group_rows=w.group_rows,
+                                 grads=outs[i % nsets], workspace=ws if ws_bytes else None,
+                                 stream=stream)
+        else:
+            g.propagate(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
+                        dirs=w.dirs, group_rows=w.group_rows, out=outs[i % nsets],
+                        workspace=ws if ws_bytes else None, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -256,7 +308,7 @@ def main() -> int:
 
     hip = Hip()
     L = g.lib()
-    max_launch = 8
+    max_launch = 16
     evs = [hip.events(2 * max_launch) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -298,9 +350,9 @@ def main() -> int:
     # Roofline unit: the launches of one step. A single launch is timed by its
     # own events; a pipeline of several launches (overlapping on two streams)
     # by the step time. Algorithmic bytes: the compulsory Q_min = 7 s per
-    # pixel (five inputs and u read once, out written once).
-    s = 4 if w.dtype == "f32" else 2
-    q_min = 7 * s * w.pixels
+    # pixel (five inputs and u read once, out written once), 13 s for the
+    # backward pass (seven tensors read, six gradients written).
+    q_min = per_px * w.pixels
     if nl == 1:
         unit_name, unit_ms = launches[0][0], per_launch[0]
     else:
@@ -311,7 +363,7 @@ def main() -> int:
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
         "unit": "elem-steps/s",
         "n_gpus": 1,
@@ -340,9 +392,12 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
-        # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core
-        planes = int(args.cpu_seconds * 2.5e7 * cores / (w.H * w.W * w.ndirs)) + 1
-        result["cpu_baseline"] = cpu_baseline(sets[0], w, planes)
+        # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core forward
+        # and about a tenth of that backward
+        rate = 2.5e6 if bwd else 2.5e7
+        planes = int(args.cpu_seconds * rate * cores / (w.H * w.W * w.ndirs)) + 1
+        result["cpu_baseline"] = cpu_baseline(sets[0], w, planes,
+                                              grad_out=sets[0]["gy"] if bwd else None)
     print(json.dumps(result), flush=True)
     return 0
 

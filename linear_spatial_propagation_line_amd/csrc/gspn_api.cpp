@@ -194,7 +194,7 @@ const char* plan_str(Plan p) {
 }
 
 // ---- backward pass ---------------------------------------------------------
-enum class BPlan { kInvalid, kStream };
+enum class BPlan { kInvalid, kPlane16, kPlane64, kStream };
 
 struct BChecked {
   gspn_status status;
@@ -210,13 +210,23 @@ BChecked check_bwd_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t ma
     r.status = f.status;
     return r;
   }
+  // GSPN_FORCE_BWD_PLAN=plane|stream picks a path for testing when the shape
+  // allows it
+  const char* force = std::getenv("GSPN_FORCE_BWD_PLAN");
+  const bool f_stream = force && !std::strcmp(force, "stream");
+  if (!f_stream && gspn::plane_fits(H, W)) {
+    r.plan = gspn::plane_seg(H, W) == 16 ? BPlan::kPlane16 : BPlan::kPlane64;
+    return r;
+  }
   r.plan = BPlan::kStream;
-  r.ws_bytes = gspn::bwd_stream_workspace_bytes(B * C, H, W, mask);
+  r.ws_bytes = gspn::bwd_stream_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
   return r;
 }
 
 const char* bplan_str(BPlan p) {
   switch (p) {
+    case BPlan::kPlane16: return "bwd_plane16";
+    case BPlan::kPlane64: return "bwd_plane64";
     case BPlan::kStream: return "bwd_stream";
     default: return "invalid";
   }
@@ -236,12 +246,17 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
   const size_t es = elem_size(dtype);
   const void* ins[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, gy};
   const void* outs[6] = {dx, dlogits[0], dlogits[1], dlogits[2], dlam, du};
-  for (const void* p : ins)
+  bool vec4 = true;
+  for (const void* p : ins) {
     if (reinterpret_cast<uintptr_t>(p) % es)
       return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
-  for (const void* p : outs)
+    if (reinterpret_cast<uintptr_t>(p) % (4 * es)) vec4 = false;
+  }
+  for (const void* p : outs) {
     if (reinterpret_cast<uintptr_t>(p) % es)
       return fail(GSPN_E_ALIGN, "gradient pointer not aligned to its element size");
+    if (reinterpret_cast<uintptr_t>(p) % (4 * es)) vec4 = false;
+  }
   const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
   for (int i = 0; i < 6; ++i) {
     for (const void* p : ins)
@@ -265,6 +280,7 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
   pr->mask = mask;
   pr->G = G;
   pr->dtype = dtype;
+  pr->aligned_vec4 = vec4;
   return GSPN_OK;
 }
 
@@ -274,6 +290,10 @@ gspn_status run_bwd(const gspn::BwdProblem& pr, BPlan plan, void* ws, hipStream_
   tr.events = g_trace_events;
   tr.pairs = g_trace_pairs;
   switch (plan) {
+    case BPlan::kPlane16:
+    case BPlan::kPlane64:
+      e = gspn::launch_bplane(pr, stream, &tr);
+      break;
     case BPlan::kStream:
       e = gspn::launch_bwd_stream(pr, ws, stream, &tr);
       break;

@@ -25,15 +25,19 @@
 // three logit gradients, sum of h): the first direction writes them, later
 // ones add, the last one writes the six gradients in the storage type.
 //
-// Horizontal scans read the row-major tensors with a stride of W; this path
-// is the general one, not the fast one.
+// Horizontal directions run in a transposed copy of the plane, where they are
+// vertical scans and every access is coalesced: the seven inputs are
+// transposed once (64 x 64 LDS tiles), left->right and right->left run as
+// top->bottom and bottom->top there into transposed accumulators, and those
+// are transposed back before the vertical directions add to them (or, with
+// no vertical direction, a pointwise pass writes the gradients).
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 
 namespace gspn {
 
 namespace {
-constexpr int kBwThreads = 1024;
+constexpr int kBwThreads = 1024;   // upper bound; a launch uses n_o rounded up to 64
 enum : int { kBwFirst = 1, kBwLast = 2 };
 
 __device__ __forceinline__ float bl(const float* p, int64_t i) { return p[i]; }
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
     const int pos = fwd ? s : n_s - 1 - s;
     float* cur = line + (s & 1) * n_o;
     const float* prev = line + ((s & 1) ^ 1) * n_o;
-    for (int o = threadIdx.x; o < n_o; o += kBwThreads) {
+    for (int o = threadIdx.x; o < n_o; o += blockDim.x) {
       const int r = vert ? pos : o, c = vert ? o : pos;
       const int64_t idx = base + static_cast<int64_t>(r) * W + c;
       float h = bl(a.lam, idx) * bl(a.x, idx);
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
 }
 
 // reverse scan of the error term and the gradients of one direction.
-// MAXP = bound on orthogonal positions per thread (n_o <= MAXP * 1024).
+// MAXP = bound on orthogonal positions per thread (n_o <= MAXP * blockDim.x).
 template <typename T, int MAXP>
 __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   extern __shared__ float sm[];   // [2][n_o]: w_0 e and w_2 e of the line below
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   float a1[MAXP], b0[MAXP], b2[MAXP];
 #pragma unroll
   for (int i = 0; i < MAXP; ++i) a1[i] = 0.f;
-  for (int o = threadIdx.x; o < n_o; o += kBwThreads) { A0[o] = 0.f; A2[o] = 0.f; }
+  for (int o = threadIdx.x; o < n_o; o += blockDim.x) { A0[o] = 0.f; A2[o] = 0.f; }
   __syncthreads();
 
   for (int s = n_s - 1; s >= 0; --s) {
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
     const int pos = fwd ? s : n_s - 1 - s;
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
-      const int o = threadIdx.x + i * kBwThreads;
+      const int o = threadIdx.x + i * blockDim.x;
       b0[i] = 0.f;
       b2[i] = 0.f;
       if (o < n_o) {
@@ -193,16 +197,100 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
     __syncthreads();   // every thread has read the line below
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
-      const int o = threadIdx.x + i * kBwThreads;
+      const int o = threadIdx.x + i * blockDim.x;
       if (o < n_o) { A0[o] = b0[i]; A2[o] = b2[i]; }
     }
     __syncthreads();
   }
 }
 
-size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask) {
+// [n][R][C] -> [n][C][R] for up to seven tensors at once (blockIdx.y picks
+// the tensor), through 64 x 64 LDS tiles; grid-stride over tiles
+template <typename E>
+struct TrArgs {
+  const E* src[7];
+  E* dst[7];
+  int64_t n;
+  int R, C;
+};
+
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_transpose(TrArgs<E> a) {
+  __shared__ E tile[64][65];
+  const E* src = a.src[blockIdx.y];
+  E* dst = a.dst[blockIdx.y];
+  const int R = a.R, C = a.C;
+  const int tr = (R + 63) / 64, tc = (C + 63) / 64;
+  const int64_t ntiles = a.n * tr * tc;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t p = t / (tr * tc);
+    const int rem = static_cast<int>(t - p * tr * tc);
+    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
+    const int64_t base = p * R * C;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = r0 + ty + 4 * k, c = c0 + tx;
+      if (r < R && c < C) tile[ty + 4 * k][tx] = src[base + static_cast<int64_t>(r) * C + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = c0 + ty + 4 * k, r = r0 + tx;
+      if (c < C && r < R) dst[base + static_cast<int64_t>(c) * R + r] = tile[tx][ty + 4 * k];
+    }
+    __syncthreads();
+  }
+}
+
+// gradients from complete accumulators (no direction left to run)
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_finish(BwArgs<T> a) {
+  const int64_t ps = a.pstride;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < ps;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float dphi = a.acc[i];
+    Store<T>::put(a.dx, i, bl(a.lam, i) * dphi);
+    Store<T>::put(a.dlam, i, bl(a.x, i) * dphi);
+    Store<T>::put(a.dl0, i, a.acc[ps + i]);
+    Store<T>::put(a.dl1, i, a.acc[2 * ps + i]);
+    Store<T>::put(a.dl2, i, a.acc[3 * ps + i]);
+    Store<T>::put(a.du, i, bl(a.gy, i) * a.acc[4 * ps + i]);
+  }
+}
+
+namespace {
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// workspace regions (bytes from the start): forward states, accumulators,
+// and for horizontal directions the transposed inputs and accumulators
+struct BwLayout {
+  size_t hbuf, acc, in_t, acc_t, total;
+};
+
+BwLayout bw_layout(int64_t planes, int64_t H, int64_t W, uint32_t mask, size_t es) {
   const size_t px = static_cast<size_t>(planes * H * W);
-  return (__builtin_popcount(mask) > 1 ? 6 : 1) * px * sizeof(float);
+  const bool hz = mask & 12u;
+  const bool accs = hz || __builtin_popcount(mask) > 1;
+  BwLayout L;
+  size_t o = 0;
+  L.hbuf = o; o = al256(o + px * 4);
+  L.acc = o; o = al256(o + (accs ? 5 * px * 4 : 0));
+  L.in_t = o; o = al256(o + (hz ? 7 * px * es : 0));
+  L.acc_t = o; o = al256(o + (hz ? 5 * px * 4 : 0));
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                  gspn_dtype dt) {
+  return bw_layout(planes, H, W, mask, dt == GSPN_F32 ? 4 : 2).total;
+}
+
+static int bw_block(int64_t n_o) {
+  const int64_t r = (n_o + 63) / 64 * 64;
+  return static_cast<int>(r < kBwThreads ? r : kBwThreads);
 }
 
 template <typename T, int MAXP>
@@ -217,7 +305,56 @@ static hipError_t launch_adj(const BwArgs<T>& a, int64_t planes, int64_t n_o, hi
     if (e != hipSuccess) return e;
   }
   tr->before(stream, "bwd_adj", planes);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(kBwThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(bw_block(n_o)), lds, stream,
+                     a);
+  tr->after(stream);
+  return hipGetLastError();
+}
+
+// forward scan + reverse scan of scan direction d (0 top->bottom, 1
+// bottom->top) over planes of a.H x a.W
+template <typename T>
+static hipError_t run_direction(BwArgs<T> a, int d, int mode, int64_t planes, hipStream_t stream,
+                                Tracer* tr) {
+  a.dir = d;
+  a.mode = mode;
+  const int64_t n_o = d < 2 ? a.W : a.H;
+  {
+    auto kern = bwd_fwd<T>;
+    const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    tr->before(stream, "bwd_fwd", planes);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(bw_block(n_o)), lds,
+                       stream, a);
+    tr->after(stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nb = bw_block(n_o);
+  if (n_o <= nb) return launch_adj<T, 1>(a, planes, n_o, stream, tr);
+  if (n_o <= 4 * nb) return launch_adj<T, 4>(a, planes, n_o, stream, tr);
+  return launch_adj<T, 16>(a, planes, n_o, stream, tr);
+}
+
+template <typename E>
+static hipError_t transpose(const E* const* src, E* const* dst, int count, int64_t n, int R, int C,
+                            hipStream_t stream, Tracer* tr) {
+  TrArgs<E> t;
+  for (int i = 0; i < count; ++i) { t.src[i] = src[i]; t.dst[i] = dst[i]; }
+  for (int i = count; i < 7; ++i) { t.src[i] = nullptr; t.dst[i] = nullptr; }
+  t.n = n;
+  t.R = R;
+  t.C = C;
+  const int64_t tiles = n * ((R + 63) / 64) * ((C + 63) / 64);
+  const int64_t grid = tiles < (int64_t(1) << 20) ? tiles : (int64_t(1) << 20);
+  tr->before(stream, "bwd_transpose", n);
+  hipLaunchKernelGGL(bwd_transpose<E>, dim3(static_cast<unsigned>(grid), count), dim3(256), 0,
+                     stream, t);
   tr->after(stream);
   return hipGetLastError();
 }
@@ -226,9 +363,8 @@ template <typename T>
 static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream_t stream,
                                        Tracer* tr) {
   const int64_t planes = pr.B * pr.C;
-  int dirs[4], nd = 0;
-  for (int d = 0; d < 4; ++d)
-    if ((pr.mask >> d) & 1u) dirs[nd++] = d;
+  const BwLayout lay = bw_layout(planes, pr.H, pr.W, pr.mask, sizeof(T));
+  char* wsb = static_cast<char*>(ws);
   BwArgs<T> a;
   a.x = static_cast<const T*>(pr.x);
   a.l0 = static_cast<const T*>(pr.l[0]);
@@ -244,39 +380,53 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
   a.dlam = static_cast<T*>(pr.dlam);
   a.du = static_cast<T*>(pr.du);
   a.pstride = planes * pr.H * pr.W;
-  a.hbuf = static_cast<float*>(ws);
-  a.acc = a.hbuf + a.pstride;
+  a.hbuf = reinterpret_cast<float*>(wsb + lay.hbuf);
+  a.acc = reinterpret_cast<float*>(wsb + lay.acc);
   a.H = static_cast<int>(pr.H);
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G);
-  for (int i = 0; i < nd; ++i) {
-    a.dir = dirs[i];
-    a.mode = (i == 0 ? kBwFirst : 0) | (i == nd - 1 ? kBwLast : 0);
-    const int64_t n_o = dirs[i] < 2 ? pr.W : pr.H;
-    {
-      auto kern = bwd_fwd<T>;
-      const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);
-      if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-      }
-      tr->before(stream, "bwd_fwd", planes);
-      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(kBwThreads), lds,
-                         stream, a);
+  const bool t2b = pr.mask & 1u, b2t = pr.mask & 2u, l2r = pr.mask & 4u, r2l = pr.mask & 8u;
+  hipError_t e;
+  bool acc_written = false;
+  if (l2r || r2l) {
+    // transposed copies: left->right is top->bottom there, right->left is
+    // bottom->top, and "up-left, up, up-right" keeps meaning rows r-1, r, r+1
+    const T* src[7] = {a.x, a.l0, a.l1, a.l2, a.lam, a.u, a.gy};
+    T* dst[7];
+    T* in_t = reinterpret_cast<T*>(wsb + lay.in_t);
+    for (int i = 0; i < 7; ++i) dst[i] = in_t + i * a.pstride;
+    if ((e = transpose<T>(src, dst, 7, planes, a.H, a.W, stream, tr)) != hipSuccess) return e;
+    BwArgs<T> t = a;
+    t.x = dst[0]; t.l0 = dst[1]; t.l1 = dst[2]; t.l2 = dst[3]; t.lam = dst[4]; t.u = dst[5];
+    t.gy = dst[6];
+    t.acc = reinterpret_cast<float*>(wsb + lay.acc_t);
+    t.H = a.W;
+    t.W = a.H;
+    if (l2r && (e = run_direction(t, 0, kBwFirst, planes, stream, tr)) != hipSuccess) return e;
+    if (r2l && (e = run_direction(t, 1, l2r ? 0 : kBwFirst, planes, stream, tr)) != hipSuccess)
+      return e;
+    // the five accumulators back to row-major ([5 planes][W][H] -> [H][W])
+    const float* fs[1] = {t.acc};
+    float* fd[1] = {a.acc};
+    if ((e = transpose<float>(fs, fd, 1, 5 * planes, a.W, a.H, stream, tr)) != hipSuccess)
+      return e;
+    acc_written = true;
+    if (!t2b && !b2t) {
+      tr->before(stream, "bwd_finish", planes);
+      const int64_t blocks = (a.pstride + 255) / 256;
+      hipLaunchKernelGGL(bwd_finish<T>, dim3(static_cast<unsigned>(blocks < 65536 * 16 ? blocks : 65536 * 16)),
+                         dim3(256), 0, stream, a);
       tr->after(stream);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      return hipGetLastError();
     }
-    hipError_t e;
-    if (n_o <= kBwThreads)
-      e = launch_adj<T, 1>(a, planes, n_o, stream, tr);
-    else if (n_o <= 4 * kBwThreads)
-      e = launch_adj<T, 4>(a, planes, n_o, stream, tr);
-    else
-      e = launch_adj<T, 16>(a, planes, n_o, stream, tr);
-    if (e != hipSuccess) return e;
+  }
+  if (t2b) {
+    const int mode = (acc_written ? 0 : kBwFirst) | (b2t ? 0 : kBwLast);
+    if ((e = run_direction(a, 0, mode, planes, stream, tr)) != hipSuccess) return e;
+  }
+  if (b2t) {
+    const int mode = (acc_written || t2b ? 0 : kBwFirst) | kBwLast;
+    if ((e = run_direction(a, 1, mode, planes, stream, tr)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -40,6 +40,7 @@ struct BwdProblem {
   uint32_t mask;
   int64_t G;
   gspn_dtype dtype;
+  bool aligned_vec4;   // every pointer aligned to 4 elements
 };
 
 // Records caller-owned events around kernel launches (gspn_trace_events),
@@ -80,8 +81,13 @@ hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer*
 int64_t stream_max_orth();
 hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Tracer* tr);
 
+// backward pass, plane-resident path for H, W <= 64 (gspn_bwd_plane.hip)
+size_t bplane_lds_bytes(int64_t H, int64_t W);
+hipError_t launch_bplane(const BwdProblem& pr, hipStream_t stream, Tracer* tr);
+
 // backward pass, streaming path for any plane (gspn_bwd_stream.hip)
-size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask);
+size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                  gspn_dtype dt);
 hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
 }  // namespace gspn

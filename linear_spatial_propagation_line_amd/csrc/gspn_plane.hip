@@ -47,37 +47,6 @@ struct PlaneArgs {
   float inv_W, inv_HW;
 };
 
-// four consecutive elements, kept in their storage form until used
-template <typename T> struct V4;
-template <> struct V4<float> {
-  using raw = float4;
-  __device__ static raw load(const float* p, int64_t i) {
-    return *reinterpret_cast<const float4*>(p + i);
-  }
-  __device__ static float get(const raw& v, int e) {
-    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-  }
-  __device__ static void store(float* p, int64_t i, const float v[4]) {
-    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-};
-template <> struct V4<bf16_t> {
-  using raw = uint2;
-  __device__ static raw load(const bf16_t* p, int64_t i) {
-    return *reinterpret_cast<const uint2*>(p + i);
-  }
-  __device__ static float get(const raw& v, int e) {
-    const uint32_t w = e < 2 ? v.x : v.y;
-    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-  }
-  __device__ static void store(bf16_t* p, int64_t i, const float v[4]) {
-    uint2 q;
-    q.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    q.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p + i) = q;
-  }
-};
-
 __device__ __forceinline__ float ld1(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld1(const bf16_t* p, int64_t i) { return to_f32(p[i]); }
 __device__ __forceinline__ void st1(float* p, int64_t i, float v) { p[i] = v; }

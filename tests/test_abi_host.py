@@ -168,10 +168,19 @@ def test_backward_rejects_bad_arguments(LB, kw, status, use_ws):
     assert LB.gspn_last_error().decode() != ""
 
 
-def test_backward_workspace_checks(LB):
+def test_backward_workspace_checks(LB, monkeypatch):
+    monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
     need = g.backward_workspace_bytes(2, 3, 30, 20)
-    assert need == 6 * 2 * 3 * 30 * 20 * 4
-    assert g.backward_workspace_bytes(2, 3, 30, 20, dirs=g.L2R) == 2 * 3 * 30 * 20 * 4
+    px = 2 * 3 * 30 * 20
+    r256 = lambda v: (v + 255) // 256 * 256
+    # states, 5 accumulators, and for horizontal directions 7 transposed
+    # inputs and 5 transposed accumulators (regions 256-byte aligned)
+    assert need == r256(r256(r256(r256(px * 4) + 5 * px * 4) + 7 * px * 4) + 5 * px * 4)
+    assert g.backward_workspace_bytes(2, 3, 30, 20, dirs=g.T2B) == r256(px * 4)
+    assert g.backward_workspace_bytes(2, 3, 30, 20, dirs=g.T2B | g.B2T) == \
+        r256(r256(px * 4) + 5 * px * 4)
+    assert g.backward_workspace_bytes(2, 3, 30, 20, dirs=g.L2R, dtype=g.GSPN_BF16) == \
+        r256(r256(r256(r256(px * 4) + 5 * px * 4) + 7 * px * 2) + 5 * px * 4)
     assert g.backward_workspace_bytes(1, 1, 0, 20) == 0
     assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True) == g.STATUS["GSPN_E_WORKSPACE"]
     assert bcall(LB, B=2, C=3, H=30, W=20, use_ws=True, ws=BASE + 13 * SZ,
@@ -184,7 +193,13 @@ def test_backward_workspace_checks(LB):
     assert bcall(LB, C=0) == 0
 
 
-def test_backward_plans(LB):
-    assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"
+def test_backward_plans(LB, monkeypatch):
+    assert g.backward_plan_name(64, 96, 56, 56) == "bwd_plane64"
+    assert g.backward_plan_name(32, 1152, 16, 16, dtype=1) == "bwd_plane16"
+    assert g.backward_plan_name(1, 1, 65, 8) == "bwd_stream"
     assert g.backward_plan_name(1, 320, 2048, 1024, dtype=1) == "bwd_stream"
     assert g.backward_plan_name(1, 1, 0, 4) == "invalid"
+    assert g.backward_workspace_bytes(64, 96, 56, 56) == 0
+    monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
+    assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"
+    assert g.backward_workspace_bytes(1, 2, 8, 8, dirs=g.T2B | g.B2T) == 6 * 2 * 64 * 4

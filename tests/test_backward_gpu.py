@@ -121,3 +121,91 @@ def test_binding_rejects_aliased_gradients():
     with pytest.raises(g.GspnError) as ei:
         g.propagate_backward(x, (t[0], t[1], t[2]), t[3], t[4], t[5], grads=grads)
     assert ei.value.name == "GSPN_E_ALIAS"
+
+
+@pytest.fixture
+def force_bwd_plan(monkeypatch):
+    def _set(name):
+        monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", name)
+    return _set
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (2, 2, 13, 11), (1, 2, 40, 24),
+                                   (1, 1, 64, 64), (1, 2, 1, 9)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_streaming_path_on_small_planes(force_bwd_plan, shape, dtype):
+    """The general backward path forced onto shapes the plane-resident path
+    normally takes, every direction subset family, global and local."""
+    force_bwd_plan("stream")
+    B, C, H, W = shape
+    assert g.backward_plan_name(B, C, H, W) == "bwd_stream"
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, 50 + H, B=B, C=C, H=H, W=W)
+    for mask in (15, 1, 2, 4, 8, 5, 10):
+        for G in ((0, 3) if mask == 15 else (0,)):
+            got = run_bwd(inp, gy, mask, G)
+            assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
+                               f"stream {shape} mask={mask} G={G}")
+
+
+def _offset_view(t, off):
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=DEV)
+    v = buf[off:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (1, 2, 56, 56), (1, 1, 70, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_element_offset_views(shape, dtype):
+    """Tensors starting 1 element into their allocation take the element-wise
+    loads and stores and still match the oracle."""
+    B, C, H, W = shape
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, 61, B=B, C=C, H=H, W=W)
+    d = {k: _offset_view(v.to(DEV), 1) for k, v in inp.items()}
+    gyd = _offset_view(gy.to(DEV), 1)
+    grads = {k: _offset_view(torch.zeros(shape, dtype=dtype, device=DEV), 1) for k in GRAD_NAMES}
+    g.propagate_backward(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], gyd,
+                         grads=grads)
+    torch.cuda.synchronize()
+    assert_grad_parity(grads, oracle_grads(inp, gy, 15, 0), f"offset {shape}")
+
+
+def test_plane_path_matches_streaming_path(force_bwd_plan):
+    """Both backward paths on the same classification-stage planes agree to
+    the fp32 bound (they round differently, so not bitwise)."""
+    inp, gy = case("cls_56x56", 71, B=2, C=8)
+    a = run_bwd(inp, gy, 15, 0)
+    force_bwd_plan("stream")
+    b = run_bwd(inp, gy, 15, 0)
+    ref = {k: a[k].double().cpu().numpy() for k in GRAD_NAMES}
+    assert_grad_parity(b, ref, "plane vs stream")
+
+
+def test_t2i_full_size_sampled_planes():
+    """The 2048x1024x320 bf16 workload at full size, as the benchmark runs it;
+    the fp64 oracle checks sampled planes."""
+    w = WORKLOADS["t2i_2048x1024"]
+    print("[bwd] t2i full size, generating on device", flush=True)
+    d = make_inputs(w, device=DEV)
+    gy = make_grad_out(w, device=DEV)
+    grads = g.propagate_backward(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], gy,
+                                 dirs=w.dirs, group_rows=w.group_rows)
+    torch.cuda.synchronize()
+    for c in (0, 211):
+        inp = {k: v[:, c:c + 1].cpu() for k, v in d.items()}
+        got = {k: v[:, c:c + 1] for k, v in grads.items()}
+        err = assert_grad_parity(got, oracle_grads(inp, gy[:, c:c + 1].cpu(), w.dirs, 0),
+                                 f"t2i plane {c}")
+        print(f"[bwd] t2i plane {c} worst scaled error {err:.3e}", flush=True)
+
+
+def test_local_full_size():
+    w = WORKLOADS["local_128x128_g8"]
+    inp, gy = make_inputs(w), make_grad_out(w)
+    got = run_bwd(inp, gy, w.dirs, w.group_rows)
+    err = assert_grad_parity(got, oracle_grads(inp, gy, w.dirs, w.group_rows), w.name)
+    print(f"[bwd] {w.name} full size worst scaled error {err:.3e}", flush=True)
