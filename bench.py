@@ -52,6 +52,7 @@ PLAN_SOURCES = {
     "bwd_plane16": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
+    "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
 }
 
 
@@ -123,6 +124,9 @@ def design_bytes(kernel: str, planes: int, w) -> float:
       bwd_transpose  seven inputs read and written (2 * 7 s), or, over 5x the
           planes, the fp32 accumulators (2 * 4)
       bwd_finish  5 * 4 accumulators + 3 s (x, lambda, grad_out) + 6 s out
+      bband_kernel (local groups): seven inputs read in the vertical and again
+          in the horizontal rounds, five fp32 partial sums written and read
+          back, six gradients written -> 20 s + 40
     """
     s = 4 if w.dtype == "f32" else 2
     px = planes * w.H * w.W
@@ -141,6 +145,7 @@ def design_bytes(kernel: str, planes: int, w) -> float:
         "bwd_adj": 5 * s + 4 + 32,
         "bwd_transpose": 2 * 7 * s if planes == w.B * w.C else 2 * 4,
         "bwd_finish": 20 + 9 * s,
+        "bband_kernel": 20 * s + 40,
     }[kernel]
     return per * px
 

@@ -194,7 +194,7 @@ const char* plan_str(Plan p) {
 }
 
 // ---- backward pass ---------------------------------------------------------
-enum class BPlan { kInvalid, kPlane16, kPlane64, kStream };
+enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kStream };
 
 struct BChecked {
   gspn_status status;
@@ -210,11 +210,23 @@ BChecked check_bwd_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t ma
     r.status = f.status;
     return r;
   }
-  // GSPN_FORCE_BWD_PLAN=plane|stream picks a path for testing when the shape
-  // allows it
+  // GSPN_FORCE_BWD_PLAN=plane|band|stream picks a path for testing when the
+  // shape allows it; otherwise the first path that fits, in that order
   const char* force = std::getenv("GSPN_FORCE_BWD_PLAN");
+  const bool f_plane = force && !std::strcmp(force, "plane");
+  const bool f_band = force && !std::strcmp(force, "band");
   const bool f_stream = force && !std::strcmp(force, "stream");
-  if (!f_stream && gspn::plane_fits(H, W)) {
+  const bool any = !f_plane && !f_band && !f_stream;
+  if ((any || f_plane) && gspn::plane_fits(H, W)) {
+    r.plan = gspn::plane_seg(H, W) == 16 ? BPlan::kPlane16 : BPlan::kPlane64;
+    return r;
+  }
+  if ((any || f_band) && gspn::bband_fits(H, W, G)) {
+    r.plan = BPlan::kBand;
+    r.ws_bytes = gspn::bband_workspace_bytes(B * C, H, W, mask);
+    return r;
+  }
+  if (f_plane && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? BPlan::kPlane16 : BPlan::kPlane64;
     return r;
   }
@@ -227,6 +239,7 @@ const char* bplan_str(BPlan p) {
   switch (p) {
     case BPlan::kPlane16: return "bwd_plane16";
     case BPlan::kPlane64: return "bwd_plane64";
+    case BPlan::kBand: return "bwd_band";
     case BPlan::kStream: return "bwd_stream";
     default: return "invalid";
   }
@@ -293,6 +306,9 @@ gspn_status run_bwd(const gspn::BwdProblem& pr, BPlan plan, void* ws, hipStream_
     case BPlan::kPlane16:
     case BPlan::kPlane64:
       e = gspn::launch_bplane(pr, stream, &tr);
+      break;
+    case BPlan::kBand:
+      e = gspn::launch_bband(pr, ws, stream, &tr);
       break;
     case BPlan::kStream:
       e = gspn::launch_bwd_stream(pr, ws, stream, &tr);

@@ -238,7 +238,8 @@ __global__ __launch_bounds__(kBandThreads, GM <= 8 ? 4 : 2) void band_kernel(Ban
       const int r0 = min(b, nbv - 1) * G;
       const int len = act ? min(G, H - r0) : 0;
       build(L, vc > 0 ? 1.f : 0.f, vc < W - 1 ? 1.f : 0.f, len, R);
-      pair_scan(R, len, act, lw, pv, vbl * lw + vc + 1, tb, bt, hs);
+      // idle threads read a pad slot of band 0 and write nothing
+      pair_scan(R, len, act, lw, pv, act ? vbl * lw + vc + 1 : 1, tb, bt, hs);
 #pragma unroll
       for (int s = 0; s < GM; ++s)
         if (act && s < len) yv[(r0 + s) * yp + vc] = hs[s];
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kBandThreads, GM <= 8 ? 4 : 2) void band_kernel(Ban
 #pragma unroll
         for (int s = 0; s < GM; ++s) uu[s] = bld(a.u, row + min(c0 + s, W - 1));
       }
-      pair_scan(R, len, act, lh, ph, hbl * lh + r + 1, lr, rl, hs);
+      pair_scan(R, len, act, lh, ph, act ? hbl * lh + r + 1 : 1, lr, rl, hs);
       if constexpr (VH) {
         if (act) {
 #pragma unroll

@@ -85,6 +85,11 @@ hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Trac
 size_t bplane_lds_bytes(int64_t H, int64_t W);
 hipError_t launch_bplane(const BwdProblem& pr, hipStream_t stream, Tracer* tr);
 
+// backward pass, band path for local groups G <= 8 (gspn_bwd_band.hip)
+bool bband_fits(int64_t H, int64_t W, int64_t G);
+size_t bband_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask);
+hipError_t launch_bband(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
+
 // backward pass, streaming path for any plane (gspn_bwd_stream.hip)
 size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
                                   gspn_dtype dt);

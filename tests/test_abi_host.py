@@ -199,6 +199,11 @@ def test_backward_plans(LB, monkeypatch):
     assert g.backward_plan_name(1, 1, 65, 8) == "bwd_stream"
     assert g.backward_plan_name(1, 320, 2048, 1024, dtype=1) == "bwd_stream"
     assert g.backward_plan_name(1, 1, 0, 4) == "invalid"
+    assert g.backward_plan_name(16, 192, 128, 128, group_rows=8) == "bwd_band"
+    assert g.backward_plan_name(16, 192, 128, 128, group_rows=9) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 600, 100, group_rows=4) == "bwd_stream"   # H > 512
+    assert g.backward_workspace_bytes(2, 3, 128, 128, group_rows=8) == 5 * 6 * 128 * 128 * 4
+    assert g.backward_workspace_bytes(2, 3, 128, 128, dirs=g.T2B, group_rows=8) == 0
     assert g.backward_workspace_bytes(64, 96, 56, 56) == 0
     monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
     assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"

@@ -209,3 +209,25 @@ def test_local_full_size():
     got = run_bwd(inp, gy, w.dirs, w.group_rows)
     err = assert_grad_parity(got, oracle_grads(inp, gy, w.dirs, w.group_rows), w.name)
     print(f"[bwd] {w.name} full size worst scaled error {err:.3e}", flush=True)
+
+
+BAND_SHAPES = [(1, 2, 72, 40), (2, 1, 128, 128), (1, 1, 100, 70), (1, 2, 66, 130),
+               (1, 1, 8, 200), (1, 1, 256, 24), (1, 1, 24, 300), (1, 1, 512, 16)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", BAND_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_band_path(force_bwd_plan, shape, dtype):
+    """Band-resident backward for local groups 1..8 (ragged last bands
+    included) and every direction-mask family."""
+    force_bwd_plan("band")
+    B, C, H, W = shape
+    name = "local_128x128_g8" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, (H * 7 + W) % 991, B=B, C=C, H=H, W=W)
+    for G in (1, 2, 3, 5, 8):
+        assert g.backward_plan_name(B, C, H, W, 15, G, 0 if dtype == torch.float32 else 1) == "bwd_band"
+        masks = (15, 1, 2, 4, 8, 3, 12, 5, 10) if G in (3, 8) else (15,)
+        for mask in masks:
+            got = run_bwd(inp, gy, mask, G)
+            assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
+                               f"band {shape} mask={mask} G={G}")
