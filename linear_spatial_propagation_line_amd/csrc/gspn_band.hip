@@ -38,42 +38,6 @@ __device__ __forceinline__ void bst(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void bst(bf16_t* p, int64_t i, float v) {
   p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
-// N contiguous elements at a 16-byte aligned index, widened to fp32 ...
-template <int N> __device__ __forceinline__ void run_ld(const float* p, int64_t i, float* d) {
-  const float4* q = reinterpret_cast<const float4*>(p + i);
-#pragma unroll
-  for (int k = 0; k < N / 4; ++k) {
-    const float4 v = q[k];
-    d[4 * k] = v.x; d[4 * k + 1] = v.y; d[4 * k + 2] = v.z; d[4 * k + 3] = v.w;
-  }
-}
-template <int N> __device__ __forceinline__ void run_ld(const bf16_t* p, int64_t i, float* d) {
-  const uint4* q = reinterpret_cast<const uint4*>(p + i);
-#pragma unroll
-  for (int k = 0; k < N / 8; ++k) {
-    const uint4 v = q[k];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { d[8 * k + 2 * j] = bf16_lo(w[j]); d[8 * k + 2 * j + 1] = bf16_hi(w[j]); }
-  }
-}
-// ... and stored back the same way (bf16 rounded to nearest even)
-template <int N> __device__ __forceinline__ void run_st(float* p, int64_t i, const float* d) {
-  float4* q = reinterpret_cast<float4*>(p + i);
-#pragma unroll
-  for (int k = 0; k < N / 4; ++k) q[k] = make_float4(d[4 * k], d[4 * k + 1], d[4 * k + 2], d[4 * k + 3]);
-}
-template <int N> __device__ __forceinline__ void run_st(bf16_t* p, int64_t i, const float* d) {
-  uint4* q = reinterpret_cast<uint4*>(p + i);
-#pragma unroll
-  for (int k = 0; k < N / 8; ++k) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = f32_to_bf16_bits(d[8 * k + 2 * j]) | (f32_to_bf16_bits(d[8 * k + 2 * j + 1]) << 16);
-    q[k] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
 }  // namespace
 
 template <typename T>

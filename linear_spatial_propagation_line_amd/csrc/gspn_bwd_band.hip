@@ -62,7 +62,11 @@ struct BBandArgs {
   unsigned mask;
 };
 
-template <typename T>
+// VH: G == 8, W a multiple of 8 and every tensor 16-byte aligned, so a
+// horizontal chain's eight columns move as whole 16-byte vectors (one
+// instruction covers a row's cache line; scalar column accesses spread over
+// eight instructions lose their lines from L2 in between).
+template <typename T, bool VH>
 __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
   constexpr int GM = kBbG;
   extern __shared__ float line[];
@@ -117,19 +121,30 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
       // queue at each guard); positions past the chain are masked afterwards
       float w0[GM], w1[GM], w2[GM], q0[GM], q1[GM], q2[GM], lx[GM], ug[GM];
       const float m0 = o > 0 ? 1.f : 0.f, m2 = o < n_o - 1 ? 1.f : 0.f;
+      {
+        float vl0[GM], vl1[GM], vl2[GM], vlam[GM], vx[GM], vu[GM], vgy[GM];
+        if (VH && !vround) {
+          run_ld<GM>(a.l0, gi0, vl0); run_ld<GM>(a.l1, gi0, vl1); run_ld<GM>(a.l2, gi0, vl2);
+          run_ld<GM>(a.lam, gi0, vlam); run_ld<GM>(a.x, gi0, vx);
+          run_ld<GM>(a.u, gi0, vu); run_ld<GM>(a.gy, gi0, vgy);
+        } else {
 #pragma unroll
-      for (int s = 0; s < GM; ++s) {
-        const int sc = min(s, max(len - 1, 0));
-        const int64_t i = gi0 + sc * gstride;
-        const float vl0 = bb_ld(a.l0, i), vl1 = bb_ld(a.l1, i), vl2 = bb_ld(a.l2, i);
-        const float vlam = bb_ld(a.lam, i), vx = bb_ld(a.x, i);
-        const float vu = bb_ld(a.u, i), vgy = bb_ld(a.gy, i);
-        const WeightSlopes q = make_weight_slopes(vl0, vl1, vl2, m0, m2);
-        const bool in = s < len;
-        w0[s] = in ? q.w0 : 0.f; w1[s] = in ? q.w1 : 0.f; w2[s] = in ? q.w2 : 0.f;
-        q0[s] = q.q0; q1[s] = q.q1; q2[s] = q.q2;
-        lx[s] = in ? vlam * vx : 0.f;
-        ug[s] = in ? vu * vgy : 0.f;
+          for (int s = 0; s < GM; ++s) {
+            const int64_t i = gi0 + min(s, max(len - 1, 0)) * gstride;
+            vl0[s] = bb_ld(a.l0, i); vl1[s] = bb_ld(a.l1, i); vl2[s] = bb_ld(a.l2, i);
+            vlam[s] = bb_ld(a.lam, i); vx[s] = bb_ld(a.x, i);
+            vu[s] = bb_ld(a.u, i); vgy[s] = bb_ld(a.gy, i);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < GM; ++s) {
+          const WeightSlopes q = make_weight_slopes(vl0[s], vl1[s], vl2[s], m0, m2);
+          const bool in = s < len;
+          w0[s] = in ? q.w0 : 0.f; w1[s] = in ? q.w1 : 0.f; w2[s] = in ? q.w2 : 0.f;
+          q0[s] = q.q0; q1[s] = q.q1; q2[s] = q.q2;
+          lx[s] = in ? vlam[s] * vx[s] : 0.f;
+          ug[s] = in ? vu[s] * vgy[s] : 0.f;
+        }
       }
       // sums over this round's two directions
       float se[GM], sh[GM], g0[GM], g1[GM], g2[GM];
@@ -220,23 +235,56 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
       float xs[GM], lams[GM], gys[GM];
       float pe[GM], p0[GM], p1_[GM], p2[GM], psum[GM];
       const bool take_part = !vround && vert;   // uniform
-#pragma unroll
-      for (int s = 0; s < GM; ++s) {
-        const int64_t i = gi0 + min(s, max(len - 1, 0)) * gstride;
-        if (final_round) {
-          xs[s] = bb_ld(a.x, i);
-          lams[s] = bb_ld(a.lam, i);
-          gys[s] = bb_ld(a.gy, i);
-        }
+      if (VH && !vround) {
+        // horizontal round: final, and every chain has G = 8 positions
+        run_ld<GM>(a.x, gi0, xs); run_ld<GM>(a.lam, gi0, lams); run_ld<GM>(a.gy, gi0, gys);
         if (take_part) {
-          pe[s] = a.part[i];
-          p0[s] = a.part[ps + i];
-          p1_[s] = a.part[2 * ps + i];
-          p2[s] = a.part[3 * ps + i];
-          psum[s] = a.part[4 * ps + i];
+          run_ld<GM>(a.part, gi0, pe); run_ld<GM>(a.part + ps, gi0, p0);
+          run_ld<GM>(a.part + 2 * ps, gi0, p1_); run_ld<GM>(a.part + 3 * ps, gi0, p2);
+          run_ld<GM>(a.part + 4 * ps, gi0, psum);
         } else {
-          pe[s] = 0.f; p0[s] = 0.f; p1_[s] = 0.f; p2[s] = 0.f; psum[s] = 0.f;
+#pragma unroll
+          for (int s = 0; s < GM; ++s) { pe[s] = 0.f; p0[s] = 0.f; p1_[s] = 0.f; p2[s] = 0.f; psum[s] = 0.f; }
         }
+      } else {
+#pragma unroll
+        for (int s = 0; s < GM; ++s) {
+          const int64_t i = gi0 + min(s, max(len - 1, 0)) * gstride;
+          if (final_round) {
+            xs[s] = bb_ld(a.x, i);
+            lams[s] = bb_ld(a.lam, i);
+            gys[s] = bb_ld(a.gy, i);
+          }
+          if (take_part) {
+            pe[s] = a.part[i];
+            p0[s] = a.part[ps + i];
+            p1_[s] = a.part[2 * ps + i];
+            p2[s] = a.part[3 * ps + i];
+            psum[s] = a.part[4 * ps + i];
+          } else {
+            pe[s] = 0.f; p0[s] = 0.f; p1_[s] = 0.f; p2[s] = 0.f; psum[s] = 0.f;
+          }
+        }
+      }
+      if (VH && !vround) {
+        if (act) {
+          float o6[6][GM];
+#pragma unroll
+          for (int s = 0; s < GM; ++s) {
+            const float te = se[s] + pe[s], th = sh[s] + psum[s];
+            o6[0][s] = lams[s] * te;
+            o6[1][s] = g0[s] + p0[s];
+            o6[2][s] = g1[s] + p1_[s];
+            o6[3][s] = g2[s] + p2[s];
+            o6[4][s] = xs[s] * te;
+            o6[5][s] = gys[s] * th;
+          }
+          run_st<GM>(a.dx, gi0, o6[0]); run_st<GM>(a.dl0, gi0, o6[1]);
+          run_st<GM>(a.dl1, gi0, o6[2]); run_st<GM>(a.dl2, gi0, o6[3]);
+          run_st<GM>(a.dlam, gi0, o6[4]); run_st<GM>(a.du, gi0, o6[5]);
+        }
+        __syncthreads();   // the line is cleared by the next round
+        continue;
       }
 #pragma unroll
       for (int s = 0; s < GM; ++s) {
@@ -274,7 +322,7 @@ size_t bband_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask
   return both ? static_cast<size_t>(5 * planes * H * W) * sizeof(float) : 0;
 }
 
-template <typename T>
+template <typename T, bool VH>
 static hipError_t launch_bband_t(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr) {
   BBandArgs<T> a;
   a.x = static_cast<const T*>(pr.x);
@@ -303,7 +351,7 @@ static hipError_t launch_bband_t(const BwdProblem& pr, void* ws, hipStream_t str
   const int64_t ph = kBbThreads / pr.H < nbh ? kBbThreads / pr.H : nbh;
   const int64_t lv = pv * (pr.W + 2), lhz = ph * bband_row(pr.H);
   const size_t lds = static_cast<size_t>(4 * (lv > lhz ? lv : lhz)) * sizeof(float);
-  auto kern = bband_kernel<T>;
+  auto kern = bband_kernel<T, VH>;
   int per_cu = 0, dev = 0, cus = 0;
   hipError_t e;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
@@ -320,9 +368,20 @@ static hipError_t launch_bband_t(const BwdProblem& pr, void* ws, hipStream_t str
   return hipGetLastError();
 }
 
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename T>
+static hipError_t launch_bband_dt(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+  const bool vh = pr.G == kBbG && pr.W % kBbG == 0 && al16(pr.x) && al16(pr.lam) &&
+                  al16(pr.l[0]) && al16(pr.l[1]) && al16(pr.l[2]) && al16(pr.u) &&
+                  al16(pr.gy) && al16(pr.dx) && al16(pr.dl[0]) && al16(pr.dl[1]) &&
+                  al16(pr.dl[2]) && al16(pr.dlam) && al16(pr.du) && al16(ws);
+  return vh ? launch_bband_t<T, true>(pr, ws, stream, tr) : launch_bband_t<T, false>(pr, ws, stream, tr);
+}
+
 hipError_t launch_bband(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr) {
-  if (pr.dtype == GSPN_F32) return launch_bband_t<float>(pr, ws, stream, tr);
-  return launch_bband_t<bf16_t>(pr, ws, stream, tr);
+  if (pr.dtype == GSPN_F32) return launch_bband_dt<float>(pr, ws, stream, tr);
+  return launch_bband_dt<bf16_t>(pr, ws, stream, tr);
 }
 
 }  // namespace gspn
