@@ -73,134 +73,214 @@ struct BwArgs {
   int H, W, G, dir, mode;
 };
 
+// Both scans keep every position's loads for D consecutive steps in flight
+// together: all loads of a batch are issued first, unconditionally, at
+// clamped in-bounds addresses, then the D steps are computed with one
+// barrier each. (One workgroup per plane leaves few wavefronts per CU, so
+// loads issued step by step would expose the full memory latency at every
+// step.) MAXP bounds the orthogonal positions per thread
+// (n_o <= MAXP * blockDim.x); MAXP * D stays small to fit the registers.
+
 // forward scan of one direction: h into hbuf, and into the running sum of h
-template <typename T>
+template <typename T, int MAXP, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
   extern __shared__ float line[];   // [2][n_o]
   const int H = a.H, W = a.W, G = a.G, d = a.dir;
   const bool vert = d < 2, fwd = (d == 0 || d == 2);
   const int n_s = vert ? H : W, n_o = vert ? W : H;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * H * W;
+  const bool first = a.mode & kBwFirst, last = a.mode & kBwLast;
+  const bool keep_sum = !(first && last);   // a single direction needs no running sum
   float* hsum = a.acc + 4 * a.pstride;
-  for (int s = 0; s < n_s; ++s) {
-    const bool restart = restarts(s, n_s, G, fwd);
-    const int pos = fwd ? s : n_s - 1 - s;
-    float* cur = line + (s & 1) * n_o;
-    const float* prev = line + ((s & 1) ^ 1) * n_o;
-    for (int o = threadIdx.x; o < n_o; o += blockDim.x) {
-      const int r = vert ? pos : o, c = vert ? o : pos;
-      const int64_t idx = base + static_cast<int64_t>(r) * W + c;
-      float h = bl(a.lam, idx) * bl(a.x, idx);
-      if (!restart) {
-        const Weights w = make_weights(bl(a.l0, idx), bl(a.l1, idx), bl(a.l2, idx),
-                                       o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
-        const float hl = prev[o > 0 ? o - 1 : 0];
-        const float hr = prev[o < n_o - 1 ? o + 1 : o];
-        h = __builtin_fmaf(w.w0, hl, __builtin_fmaf(w.w1, prev[o], __builtin_fmaf(w.w2, hr, h)));
-      }
-      cur[o] = h;
-      a.hbuf[idx] = h;
-      if (a.mode & kBwFirst) {
-        if (!(a.mode & kBwLast)) hsum[idx] = h;
-      } else {
-        hsum[idx] += h;
+  for (int s0 = 0; s0 < n_s; s0 += D) {
+    float lx[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP], hs[D][MAXP];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int s = min(s0 + j, n_s - 1);
+      const int pos = fwd ? s : n_s - 1 - s;
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int o = min(static_cast<int>(threadIdx.x + i * blockDim.x), n_o - 1);
+        const int r = vert ? pos : o, c = vert ? o : pos;
+        const int64_t idx = base + static_cast<int64_t>(r) * W + c;
+        lx[j][i] = bl(a.lam, idx) * bl(a.x, idx);
+        g0[j][i] = bl(a.l0, idx);
+        g1[j][i] = bl(a.l1, idx);
+        g2[j][i] = bl(a.l2, idx);
+        hs[j][i] = (keep_sum && !first) ? hsum[idx] : 0.f;
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int s = s0 + j;
+      if (s >= n_s) break;   // uniform
+      const bool restart = restarts(s, n_s, G, fwd);
+      const int pos = fwd ? s : n_s - 1 - s;
+      float* cur = line + (s & 1) * n_o;
+      const float* prev = line + ((s & 1) ^ 1) * n_o;
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int o = threadIdx.x + i * blockDim.x;
+        if (o < n_o) {
+          const int r = vert ? pos : o, c = vert ? o : pos;
+          const int64_t idx = base + static_cast<int64_t>(r) * W + c;
+          float h = lx[j][i];
+          if (!restart) {
+            const Weights w = make_weights(g0[j][i], g1[j][i], g2[j][i], o > 0 ? 1.f : 0.f,
+                                           o < n_o - 1 ? 1.f : 0.f);
+            const float hl = prev[o > 0 ? o - 1 : 0];
+            const float hr = prev[o < n_o - 1 ? o + 1 : o];
+            h = __builtin_fmaf(w.w0, hl, __builtin_fmaf(w.w1, prev[o], __builtin_fmaf(w.w2, hr, h)));
+          }
+          cur[o] = h;
+          a.hbuf[idx] = h;
+          if (keep_sum) hsum[idx] = hs[j][i] + h;
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
 // reverse scan of the error term and the gradients of one direction.
-// MAXP = bound on orthogonal positions per thread (n_o <= MAXP * blockDim.x).
-template <typename T, int MAXP>
+// DB: the w_0 e / w_2 e line is double-buffered (one barrier per step);
+// lines above 8192 positions use one buffer and two barriers per step.
+template <typename T, int MAXP, int D, bool DB>
 __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
-  extern __shared__ float sm[];   // [2][n_o]: w_0 e and w_2 e of the line below
+  // w_0 e and w_2 e of the line after this one in scan order,
+  // [parity (DB only)][2][n_o]
+  extern __shared__ float sm[];
   const int H = a.H, W = a.W, G = a.G, d = a.dir;
   const bool vert = d < 2, fwd = (d == 0 || d == 2);
   const int n_s = vert ? H : W, n_o = vert ? W : H;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * H * W;
   const int64_t ps = a.pstride;
   const bool first = a.mode & kBwFirst, last = a.mode & kBwLast;
-  float* A0 = sm;
-  float* A2 = sm + n_o;
   // previous line in scan order sits one position back along the scan axis
   const int back = fwd ? -1 : 1;
   const int64_t back_off = vert ? static_cast<int64_t>(back) * W : back;
+  const int64_t oo = vert ? 1 : W;   // orthogonal stride
 
-  float a1[MAXP], b0[MAXP], b2[MAXP];
+  float a1[MAXP];
 #pragma unroll
   for (int i = 0; i < MAXP; ++i) a1[i] = 0.f;
-  for (int o = threadIdx.x; o < n_o; o += blockDim.x) { A0[o] = 0.f; A2[o] = 0.f; }
+  for (int o = threadIdx.x; o < (DB ? 4 : 2) * n_o; o += blockDim.x) sm[o] = 0.f;
   __syncthreads();
 
-  for (int s = n_s - 1; s >= 0; --s) {
-    const bool restart = restarts(s, n_s, G, fwd);
-    const int pos = fwd ? s : n_s - 1 - s;
+  int par = 0;
+  for (int s0 = n_s - 1; s0 >= 0; s0 -= D) {
+    // ---- loads of D steps
+    float gy[D][MAXP], ug[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP];
+    float hc[D][MAXP], hl[D][MAXP], hr[D][MAXP];
+    float c0[D][MAXP], c1[D][MAXP], c2[D][MAXP], c3[D][MAXP];
+    float xs[D][MAXP], ls[D][MAXP], hs[D][MAXP];
 #pragma unroll
-    for (int i = 0; i < MAXP; ++i) {
-      const int o = threadIdx.x + i * blockDim.x;
-      b0[i] = 0.f;
-      b2[i] = 0.f;
-      if (o < n_o) {
+    for (int j = 0; j < D; ++j) {
+      const int s = max(s0 - j, 0);
+      const bool restart = restarts(s, n_s, G, fwd);
+      const int pos = fwd ? s : n_s - 1 - s;
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int ot = static_cast<int>(threadIdx.x + i * blockDim.x);
+        const int o = min(ot, n_o - 1);
         const int r = vert ? pos : o, c = vert ? o : pos;
         const int64_t idx = base + static_cast<int64_t>(r) * W + c;
-        const float gyv = bl(a.gy, idx);
-        float e = bl(a.u, idx) * gyv + a1[i];
-        if (o + 1 < n_o) e += A0[o + 1];
-        if (o > 0) e += A2[o - 1];
-        float dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
-        float w1e = 0.f;
-        if (!restart) {
-          const float m0 = o > 0 ? 1.f : 0.f, m2 = o < n_o - 1 ? 1.f : 0.f;
-          const WeightSlopes q = make_weight_slopes(bl(a.l0, idx), bl(a.l1, idx), bl(a.l2, idx), m0, m2);
-          const int64_t pidx = idx + back_off;
-          const int64_t oo = vert ? 1 : W;   // orthogonal stride
-          const float hc = a.hbuf[pidx];
-          const float hl = o > 0 ? a.hbuf[pidx - oo] : hc;
-          const float hr = o < n_o - 1 ? a.hbuf[pidx + oo] : hc;
-          // h_k - p = sum_j w_j (h_k - h_j)
-          const float d01 = hl - hc, d12 = hc - hr, d02 = hl - hr;
-          const float dev0 = q.w1 * d01 + q.w2 * d02;
-          const float dev1 = q.w2 * d12 - q.w0 * d01;
-          const float dev2 = -(q.w0 * d02 + q.w1 * d12);
-          dl0 = e * q.q0 * dev0;
-          dl1 = e * q.q1 * dev1;
-          dl2 = e * q.q2 * dev2;
-          b0[i] = q.w0 * e;
-          b2[i] = q.w2 * e;
-          w1e = q.w1 * e;
-        }
-        a1[i] = w1e;
-        float dphi = e;
+        // a restart line has no previous line: its own position stands in
+        const int64_t pidx = restart ? idx : idx + back_off;
+        gy[j][i] = bl(a.gy, idx);
+        ug[j][i] = bl(a.u, idx) * gy[j][i];
+        g0[j][i] = bl(a.l0, idx);
+        g1[j][i] = bl(a.l1, idx);
+        g2[j][i] = bl(a.l2, idx);
+        hc[j][i] = a.hbuf[pidx];
+        hl[j][i] = a.hbuf[o > 0 ? pidx - oo : pidx];
+        hr[j][i] = a.hbuf[o < n_o - 1 ? pidx + oo : pidx];
         if (!first) {
-          dphi += a.acc[idx];
-          dl0 += a.acc[ps + idx];
-          dl1 += a.acc[2 * ps + idx];
-          dl2 += a.acc[3 * ps + idx];
+          c0[j][i] = a.acc[idx];
+          c1[j][i] = a.acc[ps + idx];
+          c2[j][i] = a.acc[2 * ps + idx];
+          c3[j][i] = a.acc[3 * ps + idx];
+        } else {
+          c0[j][i] = 0.f; c1[j][i] = 0.f; c2[j][i] = 0.f; c3[j][i] = 0.f;
         }
         if (last) {
-          Store<T>::put(a.dx, idx, bl(a.lam, idx) * dphi);
-          Store<T>::put(a.dlam, idx, bl(a.x, idx) * dphi);
-          Store<T>::put(a.dl0, idx, dl0);
-          Store<T>::put(a.dl1, idx, dl1);
-          Store<T>::put(a.dl2, idx, dl2);
-          const float hs = first ? a.hbuf[idx] : a.acc[4 * ps + idx];
-          Store<T>::put(a.du, idx, gyv * hs);
+          xs[j][i] = bl(a.x, idx);
+          ls[j][i] = bl(a.lam, idx);
+          hs[j][i] = first ? a.hbuf[idx] : a.acc[4 * ps + idx];
         } else {
-          a.acc[idx] = dphi;
-          a.acc[ps + idx] = dl0;
-          a.acc[2 * ps + idx] = dl1;
-          a.acc[3 * ps + idx] = dl2;
+          xs[j][i] = 0.f; ls[j][i] = 0.f; hs[j][i] = 0.f;
         }
       }
     }
-    __syncthreads();   // every thread has read the line below
+    // ---- D steps
 #pragma unroll
-    for (int i = 0; i < MAXP; ++i) {
-      const int o = threadIdx.x + i * blockDim.x;
-      if (o < n_o) { A0[o] = b0[i]; A2[o] = b2[i]; }
+    for (int j = 0; j < D; ++j) {
+      const int s = s0 - j;
+      if (s < 0) break;   // uniform
+      const bool restart = restarts(s, n_s, G, fwd);
+      const int pos = fwd ? s : n_s - 1 - s;
+      const float* A0 = sm + (DB ? par * 2 * n_o : 0);
+      const float* A2 = A0 + n_o;
+      float* B0 = sm + (DB ? (par ^ 1) * 2 * n_o : 0);
+      float* B2 = B0 + n_o;
+      float st0[MAXP], st2[MAXP];
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int o = threadIdx.x + i * blockDim.x;
+        if (o < n_o) {
+          const int r = vert ? pos : o, c = vert ? o : pos;
+          const int64_t idx = base + static_cast<int64_t>(r) * W + c;
+          float e = ug[j][i] + a1[i];
+          if (o + 1 < n_o) e += A0[o + 1];
+          if (o > 0) e += A2[o - 1];
+          float dl0 = 0.f, dl1 = 0.f, dl2 = 0.f, s0v = 0.f, s2v = 0.f, w1e = 0.f;
+          if (!restart) {
+            const float m0 = o > 0 ? 1.f : 0.f, m2 = o < n_o - 1 ? 1.f : 0.f;
+            const WeightSlopes q = make_weight_slopes(g0[j][i], g1[j][i], g2[j][i], m0, m2);
+            // h_k - p = sum_j w_j (h_k - h_j)
+            const float d01 = hl[j][i] - hc[j][i], d12 = hc[j][i] - hr[j][i];
+            const float d02 = hl[j][i] - hr[j][i];
+            const float dev0 = q.w1 * d01 + q.w2 * d02;
+            const float dev1 = q.w2 * d12 - q.w0 * d01;
+            const float dev2 = -(q.w0 * d02 + q.w1 * d12);
+            dl0 = e * q.q0 * dev0;
+            dl1 = e * q.q1 * dev1;
+            dl2 = e * q.q2 * dev2;
+            s0v = q.w0 * e;
+            s2v = q.w2 * e;
+            w1e = q.w1 * e;
+          }
+          a1[i] = w1e;
+          st0[i] = s0v;
+          st2[i] = s2v;
+          const float dphi = e + c0[j][i];
+          dl0 += c1[j][i];
+          dl1 += c2[j][i];
+          dl2 += c3[j][i];
+          if (last) {
+            Store<T>::put(a.dx, idx, ls[j][i] * dphi);
+            Store<T>::put(a.dlam, idx, xs[j][i] * dphi);
+            Store<T>::put(a.dl0, idx, dl0);
+            Store<T>::put(a.dl1, idx, dl1);
+            Store<T>::put(a.dl2, idx, dl2);
+            Store<T>::put(a.du, idx, gy[j][i] * hs[j][i]);
+          } else {
+            a.acc[idx] = dphi;
+            a.acc[ps + idx] = dl0;
+            a.acc[2 * ps + idx] = dl1;
+            a.acc[3 * ps + idx] = dl2;
+          }
+        }
+      }
+      if (!DB) __syncthreads();   // every thread has read the line after
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int o = threadIdx.x + i * blockDim.x;
+        if (o < n_o) { B0[o] = st0[i]; B2[o] = st2[i]; }
+      }
+      par ^= 1;
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -293,11 +373,27 @@ static int bw_block(int64_t n_o) {
   return static_cast<int>(r < kBwThreads ? r : kBwThreads);
 }
 
-template <typename T, int MAXP>
-static hipError_t launch_adj(const BwArgs<T>& a, int64_t planes, int64_t n_o, hipStream_t stream,
-                             Tracer* tr) {
-  auto kern = bwd_adj<T, MAXP>;
-  const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);
+template <typename T, int MAXP, int D, bool DB>
+static hipError_t launch_pair(const BwArgs<T>& a, int64_t planes, int64_t n_o, hipStream_t stream,
+                              Tracer* tr) {
+  const int nb = bw_block(n_o);
+  {
+    auto kern = bwd_fwd<T, MAXP, D>;
+    const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    tr->before(stream, "bwd_fwd", planes);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(nb), lds, stream, a);
+    tr->after(stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  auto kern = bwd_adj<T, MAXP, D, DB>;
+  const size_t lds = static_cast<size_t>((DB ? 4 : 2) * n_o) * sizeof(float);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -305,8 +401,7 @@ static hipError_t launch_adj(const BwArgs<T>& a, int64_t planes, int64_t n_o, hi
     if (e != hipSuccess) return e;
   }
   tr->before(stream, "bwd_adj", planes);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(bw_block(n_o)), lds, stream,
-                     a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(nb), lds, stream, a);
   tr->after(stream);
   return hipGetLastError();
 }
@@ -319,26 +414,12 @@ static hipError_t run_direction(BwArgs<T> a, int d, int mode, int64_t planes, hi
   a.dir = d;
   a.mode = mode;
   const int64_t n_o = d < 2 ? a.W : a.H;
-  {
-    auto kern = bwd_fwd<T>;
-    const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
-    tr->before(stream, "bwd_fwd", planes);
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(planes)), dim3(bw_block(n_o)), lds,
-                       stream, a);
-    tr->after(stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int nb = bw_block(n_o);
-  if (n_o <= nb) return launch_adj<T, 1>(a, planes, n_o, stream, tr);
-  if (n_o <= 4 * nb) return launch_adj<T, 4>(a, planes, n_o, stream, tr);
-  return launch_adj<T, 16>(a, planes, n_o, stream, tr);
+  if (n_o <= nb) return launch_pair<T, 1, 4, true>(a, planes, n_o, stream, tr);
+  if (n_o <= 2 * nb) return launch_pair<T, 2, 2, true>(a, planes, n_o, stream, tr);
+  if (n_o <= 4 * nb) return launch_pair<T, 4, 1, true>(a, planes, n_o, stream, tr);
+  if (n_o <= 8 * nb) return launch_pair<T, 8, 1, true>(a, planes, n_o, stream, tr);
+  return launch_pair<T, 16, 1, false>(a, planes, n_o, stream, tr);
 }
 
 template <typename E>

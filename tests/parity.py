@@ -4,7 +4,7 @@ Parity criterion (per element): |g - o| <= rtol * (|o| + rms(o)), where o is
 the oracle output, rms is taken over the whole compared tensor (outputs are
 roughly zero-mean, so a purely relative bound is meaningless near zero), and
 rtol = 1e-5 for float32 storage, 1e-2 for bfloat16 storage with fp32
-accumulation.
+accumulation (fp32 scans longer than 2048 steps: see rtol_for).
 
 Gradients (backward pass) use the same bound per tensor, with one more term
 in the scale: 1e-3 of the largest rms among the six gradient tensors of the
@@ -20,6 +20,21 @@ import torch
 import oracle
 
 RTOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
+
+
+def rtol_for(dtype, shape) -> float:
+    """The dtype's bound; for fp32 scans longer than 2048 steps, the bound the
+    arithmetic gives instead. The recurrence rounds each step (weights that
+    sum to 1 only to within an ulp, three FMAs), and over n steps those
+    errors add up to at most about n * 2^-24 relatively: 5.4e-4 at 9000
+    steps, where measured errors reach 4e-5 -- above a fixed 1e-5 although
+    nothing is wrong. Every workload scans at most 2048 steps and keeps the
+    plain bound."""
+    base = RTOL[dtype]
+    n = max(shape[-2], shape[-1])
+    if dtype == torch.float32 and n > 2048:
+        return max(base, n * 2.0 ** -24)
+    return base
 
 
 def to_oracle_array(t: torch.Tensor) -> np.ndarray:
@@ -45,7 +60,7 @@ def scaled_error(got: torch.Tensor, ref: np.ndarray) -> float:
 
 
 def assert_parity(got: torch.Tensor, ref: np.ndarray, what: str = "") -> float:
-    rtol = RTOL[got.dtype]
+    rtol = rtol_for(got.dtype, got.shape)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     g = got.detach().float().cpu().numpy()
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
@@ -70,7 +85,7 @@ def assert_grad_parity(got: dict, ref: dict, what: str = "", names=GRAD_NAMES) -
     worst = 0.0
     for k in names:
         g_t = got[k]
-        rtol = RTOL[g_t.dtype]
+        rtol = rtol_for(g_t.dtype, g_t.shape)
         assert tuple(g_t.shape) == ref[k].shape, (k, g_t.shape, ref[k].shape)
         g = g_t.detach().float().cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(g)), f"{what} d{k}: non-finite gradient"

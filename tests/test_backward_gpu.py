@@ -44,7 +44,7 @@ def test_workload_shapes(name, planes):
 
 SHAPES = [(1, 1, 1, 1), (1, 2, 1, 7), (1, 2, 7, 1), (1, 3, 16, 16), (2, 2, 13, 11),
           (1, 2, 17, 16), (1, 2, 64, 64), (1, 2, 65, 64), (1, 1, 100, 300), (1, 1, 300, 100),
-          (1, 1, 1, 1000), (1, 1, 777, 1), (1, 1, 1030, 40)]
+          (1, 1, 1, 1000), (1, 1, 777, 1), (1, 1, 1030, 40), (1, 1, 3, 9000), (1, 1, 5000, 2)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])

@@ -53,7 +53,8 @@ def test_t2i_full_size_sampled_planes():
 SHAPES = [
     (1, 1, 1, 1), (1, 3, 1, 7), (2, 2, 7, 1), (1, 5, 16, 16), (3, 3, 13, 11),
     (1, 2, 17, 16), (2, 3, 64, 64), (1, 3, 63, 61), (1, 2, 65, 64), (1, 2, 64, 65),
-    (1, 1, 100, 300), (1, 2, 300, 100), (1, 1, 1, 1000), (1, 1, 777, 1),
+    (1, 1, 100, 300), (1, 2, 300, 100), (1, 1, 1, 1000), (1, 1, 777, 1), (1, 1, 3, 9000),
+    (1, 1, 5000, 2),
 ]
 
 
