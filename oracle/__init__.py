@@ -56,6 +56,15 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     f.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
                   ctypes.c_uint32, i64, vp, ctypes.c_int]
     f.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_propagate_shared"):
+        f2 = lib.gspn_oracle_propagate_shared
+        f2.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                       ctypes.c_uint32, i64, vp, ctypes.c_int]
+        f2.restype = ctypes.c_int
+        b2 = lib.gspn_oracle_backward_shared
+        b2.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                       ctypes.c_uint32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        b2.restype = ctypes.c_int
     if hasattr(lib, "gspn_oracle_backward"):
         b = lib.gspn_oracle_backward
         b.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
@@ -77,35 +86,47 @@ def _as_input(a: np.ndarray, shape) -> tuple[np.ndarray, int]:
     raise TypeError(f"unsupported oracle input dtype {a.dtype}")
 
 
+def _gather(x, logits, others):
+    """Validate shapes and a common dtype; returns (arrays, dtype code, shape,
+    logit channel count). Logits may have fewer channels than x (shared)."""
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    shape = x.shape
+    lg0 = np.asarray(logits[0])
+    if lg0.ndim != 4:
+        raise ValueError("logits must be [B, Cl, H, W]")
+    cl = lg0.shape[1]
+    lshape = (shape[0], cl, shape[2], shape[3])
+    arrs, dts = [], set()
+    for a, shp in [(x, shape)] + [(lg, lshape) for lg in logits] + [(o, shape) for o in others]:
+        a2, dt = _as_input(np.asarray(a), shp)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    return arrs, dts.pop(), shape, cl
+
+
 def propagate(x, l0, l1, l2, lam, u, dirs: int = 15, group_rows: int = 0,
               nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
     """y = sum over directions in ``dirs`` of u * h_d, as float64 [B, C, H, W].
 
     Inputs are numpy arrays of one dtype: float64, float32, or uint16 holding
     bf16 bit patterns. ``l0, l1, l2`` are the logits of the neighbours at
-    orthogonal offsets -1, 0, +1.
+    orthogonal offsets -1, 0, +1: [B, C, H, W], or [B, Cl, H, W] with Cl
+    dividing C for logits shared by groups of C / Cl channels (channel c uses
+    logit channel c // (C // Cl)).
     """
-    x = np.asarray(x)
-    if x.ndim != 4:
-        raise ValueError("inputs must be [B, C, H, W]")
-    shape = x.shape
-    arrs = []
-    dts = set()
-    for a in (x, l0, l1, l2, lam, u):
-        a2, dt = _as_input(np.asarray(a), shape)
-        arrs.append(a2)
-        dts.add(dt)
-    if len(dts) != 1:
-        raise TypeError("all oracle inputs must share one dtype")
-    dt = dts.pop()
+    arrs, dt, shape, cl = _gather(x, (l0, l1, l2), (lam, u))
     out = np.empty(shape, dtype=np.float64)
     if nthreads is None:
         nthreads = len(os.sched_getaffinity(0))
     L = lib if lib is not None else load()
     B, C, H, W = shape
-    rc = L.gspn_oracle_propagate(*[a.ctypes.data for a in arrs], dt, B, C, H, W,
-                                 int(dirs), int(group_rows), out.ctypes.data,
-                                 int(nthreads))
+    rc = L.gspn_oracle_propagate_shared(*[a.ctypes.data for a in arrs], dt, B, C, H, W, cl,
+                                        int(dirs), int(group_rows), out.ctypes.data,
+                                        int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
@@ -117,31 +138,24 @@ GRAD_NAMES = ("x", "l0", "l1", "l2", "lam", "u")
 def backward(x, l0, l1, l2, lam, u, gy, dirs: int = 15, group_rows: int = 0,
              nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> dict:
     """Gradients of a loss L with respect to every input of ``propagate``,
-    given ``gy`` = dL/dy (same shape and dtype as the inputs). Returns a dict
-    ``{"x", "l0", "l1", "l2", "lam", "u"}`` of float64 [B, C, H, W] arrays
-    (CSDN page on GSPN, section 反向传播; the logit gradients are taken through
-    the sigmoid and the normalisation)."""
-    x = np.asarray(x)
-    if x.ndim != 4:
-        raise ValueError("inputs must be [B, C, H, W]")
-    shape = x.shape
-    arrs = []
-    dts = set()
-    for a in (x, l0, l1, l2, lam, u, gy):
-        a2, dt = _as_input(np.asarray(a), shape)
-        arrs.append(a2)
-        dts.add(dt)
-    if len(dts) != 1:
-        raise TypeError("all oracle inputs must share one dtype")
-    dt = dts.pop()
-    outs = {k: np.empty(shape, dtype=np.float64) for k in GRAD_NAMES}
+    given ``gy`` = dL/dy (same shape and dtype as x). Returns a dict
+    ``{"x", "l0", "l1", "l2", "lam", "u"}`` of float64 arrays shaped like the
+    corresponding inputs (CSDN page on GSPN, section 反向传播; the logit
+    gradients are taken through the sigmoid and the normalisation, and a
+    shared logit's gradient is the sum over the channels that use it)."""
+    arrs, dt, shape, cl = _gather(x, (l0, l1, l2), (lam, u, gy))
+    # argument order of the C function: x, l0, l1, l2, lam, u, gy
+    B, C, H, W = shape
+    lshape = (B, cl, H, W)
+    outs = {k: np.empty(lshape if k in ("l0", "l1", "l2") else shape, dtype=np.float64)
+            for k in GRAD_NAMES}
     if nthreads is None:
         nthreads = len(os.sched_getaffinity(0))
     L = lib if lib is not None else load()
-    B, C, H, W = shape
-    rc = L.gspn_oracle_backward(*[a.ctypes.data for a in arrs], dt, B, C, H, W,
-                                int(dirs), int(group_rows),
-                                *[outs[k].ctypes.data for k in GRAD_NAMES], int(nthreads))
+    rc = L.gspn_oracle_backward_shared(*[a.ctypes.data for a in arrs], dt, B, C, H, W, cl,
+                                       int(dirs), int(group_rows),
+                                       *[outs[k].ctypes.data for k in GRAD_NAMES],
+                                       int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return outs

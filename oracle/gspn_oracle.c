@@ -49,6 +49,11 @@
  *     G1..G3; here the chain rule continues through the normalisation and
  *     the sigmoid, since the gates are built from the logits inside the
  *     layer.
+ *  R9 Channel-shared logits (CSDN page, section 局限性: the speed test sets
+ *     the feature dimension of the weights to 1): the logits may have Cl
+ *     channels, Cl dividing C, and channel c then uses logit channel
+ *     c / (C / Cl) of the same batch entry. Cl = C is the unshared layer. A
+ *     shared logit's gradient is the sum over the channels that use it.
  */
 #include "gspn_oracle.h"
 
@@ -100,12 +105,18 @@ static int restarts(int d, int64_t n_s, int64_t s, int64_t G) {
 typedef struct {
   const void *x, *l[3], *lam, *u;
   int dt;
-  int64_t B, C, H, W, G;
+  int64_t B, C, H, W, G, Cl;
   uint32_t mask;
   double* out;
   int64_t next_plane;   /* shared work counter */
   pthread_mutex_t lock;
 } job_t;
+
+/* R9: the logit plane that plane (b, c) = plane uses */
+static int64_t logit_plane(int64_t plane, int64_t C, int64_t Cl) {
+  const int64_t b = plane / C, c = plane % C;
+  return b * Cl + c / (C / Cl);
+}
 
 /* one direction over one plane; adds u * h into y (this plane's slice) */
 static void scan_plane(const job_t* j, int d, int64_t plane, double* y,
@@ -113,6 +124,7 @@ static void scan_plane(const job_t* j, int d, int64_t plane, double* y,
   const int64_t H = j->H, W = j->W;
   const int64_t n_s = scan_len(d, H, W), n_o = orth_len(d, H, W);
   const int64_t base = plane * H * W;
+  const int64_t lbase = logit_plane(plane, j->C, j->Cl) * H * W;
   for (int64_t o = 0; o < n_o; ++o) h_prev[o] = 0.0;
 
   for (int64_t s = 0; s < n_s; ++s) {
@@ -129,7 +141,7 @@ static void scan_plane(const job_t* j, int d, int64_t plane, double* y,
         for (int k = 0; k < 3; ++k) {
           const int64_t q = o + k - 1;
           if (q < 0 || q >= n_o) continue;
-          sig[k] = sigmoid(load_value(j->l[k], j->dt, idx));
+          sig[k] = sigmoid(load_value(j->l[k], j->dt, lbase + r * W + c));
           S += sig[k];
         }
         for (int k = 0; k < 3; ++k) {
@@ -168,22 +180,24 @@ static void* worker(void* arg) {
   return NULL;
 }
 
-int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
-                          const void* l2, const void* lam, const void* u,
-                          int in_dtype, int64_t B, int64_t C, int64_t H,
-                          int64_t W, uint32_t dir_mask, int64_t group_rows,
-                          double* out, int nthreads) {
+int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
+                                 const void* l2, const void* lam, const void* u,
+                                 int in_dtype, int64_t B, int64_t C, int64_t H,
+                                 int64_t W, int64_t logit_channels, uint32_t dir_mask,
+                                 int64_t group_rows, double* out, int nthreads) {
   if (!x || !l0 || !l1 || !l2 || !lam || !u || !out) return -1;
   if (B < 0 || C < 0 || H <= 0 || W <= 0) return -1;
   if (dir_mask == 0 || dir_mask > 15) return -1;
   if (group_rows < 0) return -1;
   if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16)
     return -1;
+  if (logit_channels < 1 || (C > 0 && C % logit_channels != 0)) return -1;
   if (B * C == 0) return 0;
 
   job_t j;
   j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u;
   j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
+  j.Cl = logit_channels;
   j.mask = dir_mask; j.out = out; j.next_plane = 0;
   pthread_mutex_init(&j.lock, NULL);
 
@@ -205,6 +219,15 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
   }
   pthread_mutex_destroy(&j.lock);
   return rc;
+}
+
+int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
+                          const void* l2, const void* lam, const void* u,
+                          int in_dtype, int64_t B, int64_t C, int64_t H,
+                          int64_t W, uint32_t dir_mask, int64_t group_rows,
+                          double* out, int nthreads) {
+  return gspn_oracle_propagate_shared(x, l0, l1, l2, lam, u, in_dtype, B, C, H, W,
+                                      C > 0 ? C : 1, dir_mask, group_rows, out, nthreads);
 }
 
 /* ========================================================================
@@ -232,10 +255,10 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
 typedef struct {
   const void *x, *l[3], *lam, *u, *gy;
   int dt;
-  int64_t B, C, H, W, G;
+  int64_t B, C, H, W, G, Cl;
   uint32_t mask;
   double *dx, *dl[3], *dlam, *du;
-  int64_t next_plane;
+  int64_t next_group;   /* shared work counter over logit planes */
   pthread_mutex_t lock;
 } bjob_t;
 
@@ -263,12 +286,13 @@ static int64_t pixel_offset(const bjob_t* j, int d, int64_t s, int64_t o) {
 
 /* one direction over one plane: adds this direction's share of
  * d(lambda x) into dphi, of du / gy into hsum and of the logit gradients
- * into the output arrays */
+ * into the output arrays (at the plane's logit plane, R9) */
 static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
                            double* e_cur, double* e_next, double* dphi, double* hsum) {
   const int64_t H = j->H, W = j->W;
   const int64_t n_s = scan_len(d, H, W), n_o = orth_len(d, H, W);
   const int64_t base = plane * H * W;
+  const int64_t lbase = logit_plane(plane, j->C, j->Cl) * H * W;
 
   /* forward: every hidden state of the scan, h[s * n_o + o] */
   for (int64_t s = 0; s < n_s; ++s) {
@@ -280,7 +304,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
       if (!first) {
         double sig[3];
         int in_range[3];
-        const double S = link_sigmoids(j, idx, o, n_o, sig, in_range);
+        const double S = link_sigmoids(j, lbase + pix, o, n_o, sig, in_range);
         for (int k = 0; k < 3; ++k)
           if (in_range[k]) acc += (sig[k] / S) * h[(s - 1) * n_o + o + k - 1];
       }
@@ -303,7 +327,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
           if (op < 0 || op >= n_o) continue;
           double sig[3];
           int in_range[3];
-          const double S = link_sigmoids(j, base + pixel_offset(j, d, s + 1, op), op, n_o,
+          const double S = link_sigmoids(j, lbase + pixel_offset(j, d, s + 1, op), op, n_o,
                                          sig, in_range);
           e += (sig[k] / S) * e_next[op];
         }
@@ -313,7 +337,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
       if (!restarts(d, n_s, s, j->G)) {
         double sig[3], dw[3] = {0.0, 0.0, 0.0};
         int in_range[3];
-        const double S = link_sigmoids(j, idx, o, n_o, sig, in_range);
+        const double S = link_sigmoids(j, lbase + pix, o, n_o, sig, in_range);
         double t = 0.0;   /* sum_k dw_k sig_k */
         for (int k = 0; k < 3; ++k) {
           if (!in_range[k]) continue;
@@ -323,7 +347,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
         for (int k = 0; k < 3; ++k) {
           if (!in_range[k]) continue;
           const double dsig = dw[k] / S - t / (S * S);
-          j->dl[k][idx] += dsig * sig[k] * (1.0 - sig[k]);
+          j->dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);
         }
       }
     }
@@ -342,23 +366,31 @@ static void* bworker(void* arg) {
   double* e_next = (double*)malloc(sizeof(double) * (size_t)n_max);
   void* ret = NULL;
   if (!h || !dphi || !hsum || !e_cur || !e_next) { ret = (void*)1; goto done; }
+  /* one unit of work = one logit plane and, in channel order, the planes
+   * that share it, so every shared gradient is summed in a fixed order */
+  const int64_t per = j->C / j->Cl;
   for (;;) {
     pthread_mutex_lock(&j->lock);
-    const int64_t plane = j->next_plane++;
+    const int64_t grp = j->next_group++;
     pthread_mutex_unlock(&j->lock);
-    if (plane >= j->B * j->C) break;
-    const int64_t base = plane * H * W;
-    for (int64_t i = 0; i < H * W; ++i) {
-      dphi[i] = 0.0;
-      hsum[i] = 0.0;
-      for (int k = 0; k < 3; ++k) j->dl[k][base + i] = 0.0;
-    }
-    for (int d = 0; d < 4; ++d)
-      if (j->mask & (1u << d)) backward_plane(j, d, plane, h, e_cur, e_next, dphi, hsum);
-    for (int64_t i = 0; i < H * W; ++i) {
-      j->dx[base + i] = load_value(j->lam, j->dt, base + i) * dphi[i];
-      j->dlam[base + i] = load_value(j->x, j->dt, base + i) * dphi[i];
-      j->du[base + i] = load_value(j->gy, j->dt, base + i) * hsum[i];
+    if (grp >= j->B * j->Cl) break;
+    for (int k = 0; k < 3; ++k)
+      for (int64_t i = 0; i < H * W; ++i) j->dl[k][grp * H * W + i] = 0.0;
+    const int64_t b = grp / j->Cl, cl = grp % j->Cl;
+    for (int64_t c = cl * per; c < (cl + 1) * per; ++c) {
+      const int64_t plane = b * j->C + c;
+      const int64_t base = plane * H * W;
+      for (int64_t i = 0; i < H * W; ++i) {
+        dphi[i] = 0.0;
+        hsum[i] = 0.0;
+      }
+      for (int d = 0; d < 4; ++d)
+        if (j->mask & (1u << d)) backward_plane(j, d, plane, h, e_cur, e_next, dphi, hsum);
+      for (int64_t i = 0; i < H * W; ++i) {
+        j->dx[base + i] = load_value(j->lam, j->dt, base + i) * dphi[i];
+        j->dlam[base + i] = load_value(j->x, j->dt, base + i) * dphi[i];
+        j->du[base + i] = load_value(j->gy, j->dt, base + i) * hsum[i];
+      }
     }
   }
 done:
@@ -366,11 +398,13 @@ done:
   return ret;
 }
 
-int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const void* l2,
-                         const void* lam, const void* u, const void* gy, int in_dtype,
-                         int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
-                         int64_t group_rows, double* dx, double* dl0, double* dl1,
-                         double* dl2, double* dlam, double* du, int nthreads) {
+int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
+                                const void* l2, const void* lam, const void* u,
+                                const void* gy, int in_dtype, int64_t B, int64_t C,
+                                int64_t H, int64_t W, int64_t logit_channels,
+                                uint32_t dir_mask, int64_t group_rows, double* dx,
+                                double* dl0, double* dl1, double* dl2, double* dlam,
+                                double* du, int nthreads) {
   if (!x || !l0 || !l1 || !l2 || !lam || !u || !gy) return -1;
   if (!dx || !dl0 || !dl1 || !dl2 || !dlam || !du) return -1;
   if (B < 0 || C < 0 || H <= 0 || W <= 0) return -1;
@@ -378,18 +412,20 @@ int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const vo
   if (group_rows < 0) return -1;
   if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16)
     return -1;
+  if (logit_channels < 1 || (C > 0 && C % logit_channels != 0)) return -1;
   if (B * C == 0) return 0;
 
   bjob_t j;
   j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u; j.gy = gy;
   j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
+  j.Cl = logit_channels;
   j.mask = dir_mask;
   j.dx = dx; j.dl[0] = dl0; j.dl[1] = dl1; j.dl[2] = dl2; j.dlam = dlam; j.du = du;
-  j.next_plane = 0;
+  j.next_group = 0;
   pthread_mutex_init(&j.lock, NULL);
 
   int nt = nthreads <= 0 ? 1 : nthreads;
-  if ((int64_t)nt > B * C) nt = (int)(B * C);
+  if ((int64_t)nt > B * logit_channels) nt = (int)(B * logit_channels);
   int rc = 0;
   if (nt == 1) {
     if (bworker(&j) != NULL) rc = -1;
@@ -406,4 +442,14 @@ int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const vo
   }
   pthread_mutex_destroy(&j.lock);
   return rc;
+}
+
+int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const void* l2,
+                         const void* lam, const void* u, const void* gy, int in_dtype,
+                         int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                         int64_t group_rows, double* dx, double* dl0, double* dl1,
+                         double* dl2, double* dlam, double* du, int nthreads) {
+  return gspn_oracle_backward_shared(x, l0, l1, l2, lam, u, gy, in_dtype, B, C, H, W,
+                                     C > 0 ? C : 1, dir_mask, group_rows, dx, dl0, dl1,
+                                     dl2, dlam, du, nthreads);
 }

@@ -65,6 +65,27 @@ int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const vo
                          int64_t group_rows, double* dx, double* dl0, double* dl1,
                          double* dl2, double* dlam, double* du, int nthreads);
 
+/*
+ * Channel-shared logits (CSDN page, section 局限性: the speed test sets the
+ * weights' feature dimension to 1): l0, l1, l2 are [B, logit_channels, H, W]
+ * with logit_channels dividing C; channel c uses logit channel
+ * c / (C / logit_channels). The backward's dl0..dl2 then have that shape too,
+ * each the sum over the channels that share it. logit_channels = C is the
+ * plain call. Returns -1 when logit_channels is < 1 or does not divide C.
+ */
+int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
+                                 const void* l2, const void* lam, const void* u,
+                                 int in_dtype, int64_t B, int64_t C, int64_t H,
+                                 int64_t W, int64_t logit_channels, uint32_t dir_mask,
+                                 int64_t group_rows, double* out, int nthreads);
+int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
+                                const void* l2, const void* lam, const void* u,
+                                const void* gy, int in_dtype, int64_t B, int64_t C,
+                                int64_t H, int64_t W, int64_t logit_channels,
+                                uint32_t dir_mask, int64_t group_rows, double* dx,
+                                double* dl0, double* dl1, double* dl2, double* dlam,
+                                double* du, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,8 +38,8 @@ MUTANTS = [
     ("error_term_without_gate",
      "double e = load_value(j->u, j->dt, idx) * load_value(j->gy, j->dt, idx);",
      "double e = load_value(j->gy, j->dt, idx);", 1),
-    ("sigmoid_slope_missing", "j->dl[k][idx] += dsig * sig[k] * (1.0 - sig[k]);",
-     "j->dl[k][idx] += dsig * sig[k];", 1),
+    ("sigmoid_slope_missing", "j->dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);",
+     "j->dl[k][lbase + pix] += dsig * sig[k];", 1),
     ("normalisation_term_dropped", "const double dsig = dw[k] / S - t / (S * S);",
      "const double dsig = dw[k] / S;", 1),
     ("gate_gradient_uses_current_line", "dw[k] = e * h[(s - 1) * n_o + o + k - 1];",
