@@ -208,6 +208,45 @@ gspn_status gspn_propagate_backward_ws(const void* x, const void* const w_logits
                                        void* workspace, size_t ws_bytes,
                                        hipStream_t stream);
 
+/*
+ * Channel-shared logits (CSDN page, section 局限性: the speed test sets the
+ * weights' feature dimension to 1). The three logit tensors are
+ * [B, logit_channels, H, W] with logit_channels dividing C; channel c uses
+ * logit channel c / (C / logit_channels) of its batch entry.
+ * logit_channels == C is the unshared layer. A logit_channels that is < 1 or
+ * does not divide C gives GSPN_E_SHAPE.
+ *
+ * gspn_propagate_shared_ws -- gspn_propagate_ws with shared logits (same
+ * workspace size: gspn_workspace_bytes).
+ */
+gspn_status gspn_propagate_shared_ws(const void* x, const void* const w_logits[3],
+                                     int64_t logit_channels, const void* lambda,
+                                     const void* u, int64_t B, int64_t C, int64_t H,
+                                     int64_t W, uint32_t dir_mask, int64_t group_rows,
+                                     gspn_dtype dtype, void* out, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gspn_propagate_backward_shared_ws -- gspn_propagate_backward_ws with
+ * shared logits. grad_logits[0..2] are [B, logit_channels, H, W]: each is the
+ * sum, in channel order, over the channels that read that logit. The
+ * workspace (gspn_backward_workspace_bytes_shared) then also holds the fp32
+ * per-channel logit gradients before that sum.
+ */
+gspn_status gspn_propagate_backward_shared_ws(const void* x, const void* const w_logits[3],
+                                              int64_t logit_channels, const void* lambda,
+                                              const void* u, const void* grad_out,
+                                              int64_t B, int64_t C, int64_t H, int64_t W,
+                                              uint32_t dir_mask, int64_t group_rows,
+                                              gspn_dtype dtype, void* grad_x,
+                                              void* const grad_logits[3],
+                                              void* grad_lambda, void* grad_u,
+                                              void* workspace, size_t ws_bytes,
+                                              hipStream_t stream);
+size_t gspn_backward_workspace_bytes_shared(int64_t B, int64_t C, int64_t H, int64_t W,
+                                            int64_t logit_channels, uint32_t dir_mask,
+                                            int64_t group_rows, gspn_dtype dtype);
+
 /* gspn_backward_plan_name -- kernel plan gspn_propagate_backward would use,
  * or "invalid". Host-only. */
 const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,

@@ -84,6 +84,16 @@ def lib() -> ctypes.CDLL:
         L.gspn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.gspn_backward_plan_name.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
         L.gspn_backward_plan_name.restype = ctypes.c_char_p
+        L.gspn_propagate_shared_ws.argtypes = [vp, logits_t, i64, vp, vp, i64, i64, i64, i64, u32,
+                                               i64, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_shared_ws.restype = ctypes.c_int
+        L.gspn_propagate_backward_shared_ws.argtypes = [
+            vp, logits_t, i64, vp, vp, vp, i64, i64, i64, i64, u32, i64, ctypes.c_int,
+            vp, logits_t, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_backward_shared_ws.restype = ctypes.c_int
+        L.gspn_backward_workspace_bytes_shared.argtypes = [i64, i64, i64, i64, i64, u32, i64,
+                                                           ctypes.c_int]
+        L.gspn_backward_workspace_bytes_shared.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -110,23 +120,38 @@ def plan_name(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> str:
     return lib().gspn_plan_name(B, C, H, W, dirs, group_rows, dtype).decode()
 
 
+def _check_tensors(x, logits, others):
+    """Contiguous GPU tensors of x's dtype; logits may have fewer channels
+    (shared by groups of channels). Returns B, C, H, W, logit channels."""
+    import torch
+    if x.dim() != 4:
+        raise ValueError("inputs must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    cl = logits[0].shape[1] if logits[0].dim() == 4 else -1
+    for t in (x,) + tuple(logits) + tuple(others):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("all inputs must be torch tensors on a GPU device")
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous tensors of one dtype")
+    for t in others:
+        if t.shape != x.shape:
+            raise ValueError("x, lambda, u (and grad_out) must have one shape")
+    for t in logits:
+        if tuple(t.shape) != (B, cl, H, W):
+            raise ValueError("logits must be [B, Cl, H, W] with Cl dividing C")
+    return B, C, H, W, cl
+
+
 def propagate(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
               workspace=None, stream=None):
     """out = sum_{d in dirs} u * h_d for contiguous [B, C, H, W] device tensors
     of one dtype (float32 or bfloat16). ``logits`` = (l0, l1, l2) for the
-    neighbours at orthogonal offsets -1, 0, +1. Work is enqueued on ``stream``
-    (default: torch's current stream of x's device)."""
+    neighbours at orthogonal offsets -1, 0, +1, each [B, C, H, W] or
+    [B, Cl, H, W] (shared by groups of C / Cl channels). Work is enqueued on
+    ``stream`` (default: torch's current stream of x's device)."""
     import torch
     l0, l1, l2 = logits
-    ts = (x, l0, l1, l2, lam, u)
-    for t in ts:
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError("all inputs must be torch tensors on a GPU device")
-        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous tensors of one shape and dtype")
-    if x.dim() != 4:
-        raise ValueError("inputs must be [B, C, H, W]")
-    B, C, H, W = x.shape
+    B, C, H, W, cl = _check_tensors(x, (l0, l1, l2), (lam, u))
     dt = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
@@ -140,8 +165,9 @@ def propagate(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
     lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(L.gspn_propagate_ws(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H, W,
-                               dirs, group_rows, dt, out.data_ptr(), ws_ptr, ws_len, sptr))
+    _check(L.gspn_propagate_shared_ws(x.data_ptr(), lg, cl, lam.data_ptr(), u.data_ptr(), B, C,
+                                      H, W, dirs, group_rows, dt, out.data_ptr(), ws_ptr, ws_len,
+                                      sptr))
     return out
 
 
@@ -164,8 +190,10 @@ def propagate_alloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out
     return out
 
 
-def backward_workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
-    return int(lib().gspn_backward_workspace_bytes(B, C, H, W, dirs, group_rows, dtype))
+def backward_workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32,
+                             logit_channels=None) -> int:
+    cl = C if logit_channels is None else logit_channels
+    return int(lib().gspn_backward_workspace_bytes_shared(B, C, H, W, cl, dirs, group_rows, dtype))
 
 
 def backward_plan_name(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> str:
@@ -184,21 +212,14 @@ def propagate_backward(x, logits, lam, u, grad_out, dirs: int = ALL, group_rows:
     gspn_propagate_backward entry point)."""
     import torch
     l0, l1, l2 = logits
-    ts = (x, l0, l1, l2, lam, u, grad_out)
-    for t in ts:
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError("all inputs must be torch tensors on a GPU device")
-        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous tensors of one shape and dtype")
-    if x.dim() != 4:
-        raise ValueError("inputs must be [B, C, H, W]")
-    B, C, H, W = x.shape
+    B, C, H, W, cl = _check_tensors(x, (l0, l1, l2), (lam, u, grad_out))
     dt = _dtype_code(x)
     if grads is None:
-        grads = {k: torch.empty_like(x) for k in GRAD_NAMES}
+        grads = {k: torch.empty_like(l0 if k in ("l0", "l1", "l2") else x) for k in GRAD_NAMES}
     for k in GRAD_NAMES:
         t = grads[k]
-        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+        like = l0 if k in ("l0", "l1", "l2") else x
+        if t.shape != like.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
             raise ValueError("gradient tensors must match the inputs")
     L = lib()
     if stream is None:
@@ -211,12 +232,15 @@ def propagate_backward(x, logits, lam, u, grad_out, dirs: int = ALL, group_rows:
             dirs, group_rows, dt, grads["x"].data_ptr(), dlg, grads["lam"].data_ptr(),
             grads["u"].data_ptr())
     if alloc:
+        if cl != C:
+            raise ValueError("the allocating backward entry point takes unshared logits")
         _check(L.gspn_propagate_backward(*args, sptr))
         return grads
-    need = int(L.gspn_backward_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
+    need = int(L.gspn_backward_workspace_bytes_shared(B, C, H, W, cl, dirs, group_rows, dt))
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(L.gspn_propagate_backward_ws(*args, ws_ptr, ws_len, sptr))
+    _check(L.gspn_propagate_backward_shared_ws(args[0], args[1], cl, *args[2:], ws_ptr, ws_len,
+                                               sptr))
     return grads

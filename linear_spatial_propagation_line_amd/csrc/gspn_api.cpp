@@ -102,10 +102,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
 }
 
+// logit_channels must divide C (channel c reads logit channel c / (C / Cl))
+gspn_status check_logit_channels(int64_t C, int64_t Cl) {
+  if (Cl < 1 || (C > 0 && C % Cl != 0))
+    return fail(GSPN_E_SHAPE, "logit_channels must be >= 1 and divide C");
+  return GSPN_OK;
+}
+
 gspn_status check_all(const void* x, const void* const w_logits[3], const void* lambda,
                       const void* u, int64_t B, int64_t C, int64_t H, int64_t W,
                       uint32_t mask, int64_t G, gspn_dtype dtype, void* out,
-                      Checked* chk, gspn::Problem* pr) {
+                      Checked* chk, gspn::Problem* pr, int64_t Cl) {
   g_last_error.clear();
   if (!x || !w_logits || !lambda || !u || !out)
     return fail(GSPN_E_NULL, "x, w_logits, lambda, u and out must be non-null");
@@ -113,6 +120,10 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
     return fail(GSPN_E_NULL, "w_logits[0..2] must be non-null");
   *chk = check_shape(B, C, H, W, mask, G, static_cast<int>(dtype));
   if (chk->status != GSPN_OK) return chk->status;
+  if (check_logit_channels(C, Cl) != GSPN_OK) {
+    chk->status = GSPN_E_SHAPE;
+    return GSPN_E_SHAPE;
+  }
   const size_t es = elem_size(dtype);
   const void* ins[6] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u};
   bool vec4 = true, pair = true;
@@ -127,8 +138,10 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   if (vo % (4 * es)) vec4 = false;
   if (vo % (2 * es)) pair = false;
   const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
-  for (const void* p : ins)
-    if (overlaps(out, bytes, p, bytes)) return fail(GSPN_E_ALIAS, "out overlaps an input");
+  const size_t lbytes = static_cast<size_t>(B * Cl * H * W) * es;
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(out, bytes, ins[i], i >= 1 && i <= 3 ? lbytes : bytes))
+      return fail(GSPN_E_ALIAS, "out overlaps an input");
   pr->x = x;
   pr->l[0] = w_logits[0];
   pr->l[1] = w_logits[1];
@@ -142,6 +155,7 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   pr->dtype = dtype;
   pr->aligned_vec4 = vec4;
   pr->aligned_pair = pair;
+  pr->Cl = Cl;
   return GSPN_OK;
 }
 
@@ -195,16 +209,35 @@ const char* plan_str(Plan p) {
 
 // ---- backward pass ---------------------------------------------------------
 enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kStream };
+struct BChecked;
+BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
+                        int dtype);
 
 struct BChecked {
   gspn_status status;
   BPlan plan;
-  size_t ws_bytes;
+  size_t ws_bytes;     // total workspace
+  size_t plan_bytes;   // the plan's part; shared logits add their fp32
+                       // per-plane gradients after it (256-byte aligned)
 };
 
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
 BChecked check_bwd_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
-                         int dtype) {
-  BChecked r{GSPN_OK, BPlan::kInvalid, 0};
+                         int dtype, int64_t Cl) {
+  BChecked r = check_bwd_plan(B, C, H, W, mask, G, dtype);
+  if (r.status != GSPN_OK) return r;
+  if (check_logit_channels(C, Cl) != GSPN_OK) {
+    r.status = GSPN_E_SHAPE;
+    return r;
+  }
+  r.plan_bytes = r.ws_bytes;
+  if (Cl < C) r.ws_bytes = al256(r.plan_bytes) + static_cast<size_t>(3 * B * C * H * W) * sizeof(float);
+  return r;
+}
+BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
+                        int dtype) {
+  BChecked r{GSPN_OK, BPlan::kInvalid, 0, 0};
   const Checked f = check_shape(B, C, H, W, mask, G, dtype);
   if (f.status != GSPN_OK) {
     r.status = f.status;
@@ -249,13 +282,17 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
                           const void* u, const void* gy, int64_t B, int64_t C, int64_t H,
                           int64_t W, uint32_t mask, int64_t G, gspn_dtype dtype, void* dx,
                           void* const dlogits[3], void* dlam, void* du, BChecked* chk,
-                          gspn::BwdProblem* pr) {
+                          gspn::BwdProblem* pr, int64_t Cl) {
   if (!x || !w_logits || !lambda || !u || !gy || !dx || !dlogits || !dlam || !du)
     return fail(GSPN_E_NULL, "inputs, grad_out and the gradient outputs must be non-null");
   if (!w_logits[0] || !w_logits[1] || !w_logits[2] || !dlogits[0] || !dlogits[1] || !dlogits[2])
     return fail(GSPN_E_NULL, "w_logits[0..2] and grad_logits[0..2] must be non-null");
-  *chk = check_bwd_shape(B, C, H, W, mask, G, static_cast<int>(dtype));
-  if (chk->status != GSPN_OK) return chk->status;
+  *chk = check_bwd_shape(B, C, H, W, mask, G, static_cast<int>(dtype), Cl);
+  if (chk->status != GSPN_OK) {
+    if (chk->status == GSPN_E_SHAPE && g_last_error.empty())
+      fail(GSPN_E_SHAPE, "logit_channels must be >= 1 and divide C");
+    return chk->status;
+  }
   const size_t es = elem_size(dtype);
   const void* ins[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, gy};
   const void* outs[6] = {dx, dlogits[0], dlogits[1], dlogits[2], dlam, du};
@@ -270,12 +307,17 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
       return fail(GSPN_E_ALIGN, "gradient pointer not aligned to its element size");
     if (reinterpret_cast<uintptr_t>(p) % (4 * es)) vec4 = false;
   }
+  // the three logits and their gradients have Cl channels, the rest C
   const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+  const size_t lbytes = static_cast<size_t>(B * Cl * H * W) * es;
+  auto in_bytes = [&](int i) { return i >= 1 && i <= 3 ? lbytes : bytes; };
   for (int i = 0; i < 6; ++i) {
-    for (const void* p : ins)
-      if (overlaps(outs[i], bytes, p, bytes)) return fail(GSPN_E_ALIAS, "a gradient overlaps an input");
+    const size_t ob = in_bytes(i);   // outs[] has the same order for indices 0..3
+    for (int k = 0; k < 7; ++k)
+      if (overlaps(outs[i], ob, ins[k], in_bytes(k)))
+        return fail(GSPN_E_ALIAS, "a gradient overlaps an input");
     for (int j = i + 1; j < 6; ++j)
-      if (overlaps(outs[i], bytes, outs[j], bytes))
+      if (overlaps(outs[i], ob, outs[j], in_bytes(j)))
         return fail(GSPN_E_ALIAS, "two gradient outputs overlap");
   }
   pr->x = x;
@@ -294,15 +336,18 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
   pr->G = G;
   pr->dtype = dtype;
   pr->aligned_vec4 = vec4;
+  pr->Cl = Cl;
+  pr->dlw = nullptr;
   return GSPN_OK;
 }
 
-gspn_status run_bwd(const gspn::BwdProblem& pr, BPlan plan, void* ws, hipStream_t stream) {
+gspn_status run_bwd(gspn::BwdProblem pr, const BChecked& chk, void* ws, hipStream_t stream) {
   hipError_t e = hipSuccess;
   gspn::Tracer tr;
   tr.events = g_trace_events;
   tr.pairs = g_trace_pairs;
-  switch (plan) {
+  if (pr.Cl < pr.C) pr.dlw = reinterpret_cast<float*>(static_cast<char*>(ws) + al256(chk.plan_bytes));
+  switch (chk.plan) {
     case BPlan::kPlane16:
     case BPlan::kPlane64:
       e = gspn::launch_bplane(pr, stream, &tr);
@@ -316,6 +361,7 @@ gspn_status run_bwd(const gspn::BwdProblem& pr, BPlan plan, void* ws, hipStream_
     default:
       return fail(GSPN_E_SHAPE, "no backward plan");
   }
+  if (e == hipSuccess && pr.dlw) e = gspn::launch_bwd_reduce_logits(pr, stream, &tr);
   if (g_trace_events) {
     g_trace_count = tr.count;
     for (int i = 0; i < gspn::kTraceMax; ++i) {
@@ -338,7 +384,7 @@ gspn_status gspn_propagate(const void* x, const void* const w_logits[3], const v
   Checked chk;
   gspn::Problem pr;
   gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
-                            dtype, out, &chk, &pr);
+                            dtype, out, &chk, &pr, C > 0 ? C : 1);
   if (s != GSPN_OK) return s;
   if (B * C == 0) return GSPN_OK;
   void* ws = nullptr;
@@ -370,24 +416,8 @@ gspn_status gspn_propagate_ws(const void* x, const void* const w_logits[3], cons
                               uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
                               void* out, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
-  Checked chk;
-  gspn::Problem pr;
-  gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
-                            dtype, out, &chk, &pr);
-  if (s != GSPN_OK) return s;
-  if (chk.ws_bytes > 0) {
-    if (!workspace || ws_bytes < chk.ws_bytes)
-      return fail(GSPN_E_WORKSPACE, "workspace missing or smaller than gspn_workspace_bytes()");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256)
-      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
-    const size_t bytes = static_cast<size_t>(B * C * H * W) * elem_size(dtype);
-    const void* all[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, out};
-    for (const void* p : all)
-      if (overlaps(workspace, chk.ws_bytes, p, bytes))
-        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
-  }
-  if (B * C == 0) return GSPN_OK;
-  return run(pr, chk.plan, workspace, stream);
+  return gspn_propagate_shared_ws(x, w_logits, C > 0 ? C : 1, lambda, u, B, C, H, W, dir_mask,
+                                  group_rows, dtype, out, workspace, ws_bytes, stream);
 }
 
 const char* gspn_plan_name(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
@@ -443,7 +473,7 @@ gspn_status gspn_propagate_backward(const void* x, const void* const w_logits[3]
   gspn::BwdProblem pr;
   gspn_status s = check_all_bwd(x, w_logits, lambda, u, grad_out, B, C, H, W, dir_mask,
                                 group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u,
-                                &chk, &pr);
+                                &chk, &pr, C > 0 ? C : 1);
   if (s != GSPN_OK) return s;
   if (B * C == 0) return GSPN_OK;
   void* ws = nullptr;
@@ -454,7 +484,7 @@ gspn_status gspn_propagate_backward(const void* x, const void* const w_logits[3]
       return fail(GSPN_E_NOMEM, hipGetErrorString(e));
     }
   }
-  s = run_bwd(pr, chk.plan, ws, stream);
+  s = run_bwd(pr, chk, ws, stream);
   if (ws) {
     hipError_t e = hipFreeAsync(ws, stream);
     if (e != hipSuccess && s == GSPN_OK) s = fail(GSPN_E_HIP, hipGetErrorString(e));
@@ -464,11 +494,53 @@ gspn_status gspn_propagate_backward(const void* x, const void* const w_logits[3]
 
 size_t gspn_backward_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
                                      uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype) {
+  return gspn_backward_workspace_bytes_shared(B, C, H, W, C > 0 ? C : 1, dir_mask, group_rows,
+                                              dtype);
+}
+
+size_t gspn_backward_workspace_bytes_shared(int64_t B, int64_t C, int64_t H, int64_t W,
+                                            int64_t logit_channels, uint32_t dir_mask,
+                                            int64_t group_rows, gspn_dtype dtype) {
   const std::string keep = g_last_error;
-  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype),
+                                 logit_channels);
   g_last_error = keep;
   return chk.status == GSPN_OK ? chk.ws_bytes : 0;
 }
+
+namespace {
+gspn_status backward_ws(const void* x, const void* const w_logits[3], int64_t Cl,
+                        const void* lambda, const void* u, const void* grad_out, int64_t B,
+                        int64_t C, int64_t H, int64_t W, uint32_t dir_mask, int64_t group_rows,
+                        gspn_dtype dtype, void* grad_x, void* const grad_logits[3],
+                        void* grad_lambda, void* grad_u, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  BChecked chk;
+  gspn::BwdProblem pr;
+  gspn_status s = check_all_bwd(x, w_logits, lambda, u, grad_out, B, C, H, W, dir_mask,
+                                group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u,
+                                &chk, &pr, Cl);
+  if (s != GSPN_OK) return s;
+  if (chk.ws_bytes > 0) {
+    if (!workspace || ws_bytes < chk.ws_bytes)
+      return fail(GSPN_E_WORKSPACE,
+                  "workspace missing or smaller than gspn_backward_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+    const size_t lbytes = static_cast<size_t>(B * Cl * H * W) * es;
+    const void* all[13] = {x, lambda, u, grad_out, grad_x, grad_lambda, grad_u,
+                           w_logits[0], w_logits[1], w_logits[2],
+                           grad_logits[0], grad_logits[1], grad_logits[2]};
+    for (int i = 0; i < 13; ++i)
+      if (overlaps(workspace, chk.ws_bytes, all[i], i < 7 ? bytes : lbytes))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  if (B * C == 0) return GSPN_OK;
+  return run_bwd(pr, chk, workspace, stream);
+}
+}  // namespace
 
 gspn_status gspn_propagate_backward_ws(const void* x, const void* const w_logits[3],
                                        const void* lambda, const void* u, const void* grad_out,
@@ -477,36 +549,57 @@ gspn_status gspn_propagate_backward_ws(const void* x, const void* const w_logits
                                        void* grad_x, void* const grad_logits[3],
                                        void* grad_lambda, void* grad_u, void* workspace,
                                        size_t ws_bytes, hipStream_t stream) {
-  BChecked chk;
-  gspn::BwdProblem pr;
-  gspn_status s = check_all_bwd(x, w_logits, lambda, u, grad_out, B, C, H, W, dir_mask,
-                                group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u,
-                                &chk, &pr);
-  if (s != GSPN_OK) return s;
-  if (chk.ws_bytes > 0) {
-    if (!workspace || ws_bytes < chk.ws_bytes)
-      return fail(GSPN_E_WORKSPACE,
-                  "workspace missing or smaller than gspn_backward_workspace_bytes()");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256)
-      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
-    const size_t bytes = static_cast<size_t>(B * C * H * W) * elem_size(dtype);
-    const void* all[13] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, grad_out,
-                           grad_x, grad_logits[0], grad_logits[1], grad_logits[2],
-                           grad_lambda, grad_u};
-    for (const void* p : all)
-      if (overlaps(workspace, chk.ws_bytes, p, bytes))
-        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
-  }
-  if (B * C == 0) return GSPN_OK;
-  return run_bwd(pr, chk.plan, workspace, stream);
+  return backward_ws(x, w_logits, C > 0 ? C : 1, lambda, u, grad_out, B, C, H, W, dir_mask, group_rows,
+                     dtype, grad_x, grad_logits, grad_lambda, grad_u, workspace, ws_bytes,
+                     stream);
+}
+
+gspn_status gspn_propagate_backward_shared_ws(
+    const void* x, const void* const w_logits[3], int64_t logit_channels, const void* lambda,
+    const void* u, const void* grad_out, int64_t B, int64_t C, int64_t H, int64_t W,
+    uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype, void* grad_x,
+    void* const grad_logits[3], void* grad_lambda, void* grad_u, void* workspace,
+    size_t ws_bytes, hipStream_t stream) {
+  return backward_ws(x, w_logits, logit_channels, lambda, u, grad_out, B, C, H, W, dir_mask,
+                     group_rows, dtype, grad_x, grad_logits, grad_lambda, grad_u, workspace,
+                     ws_bytes, stream);
 }
 
 const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,
                                     uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype) {
   const std::string keep = g_last_error;
-  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  BChecked chk = check_bwd_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype),
+                                 C > 0 ? C : 1);
   g_last_error = keep;
   return chk.status == GSPN_OK ? bplan_str(chk.plan) : "invalid";
+}
+
+gspn_status gspn_propagate_shared_ws(const void* x, const void* const w_logits[3],
+                                     int64_t logit_channels, const void* lambda, const void* u,
+                                     int64_t B, int64_t C, int64_t H, int64_t W,
+                                     uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype,
+                                     void* out, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream) {
+  Checked chk;
+  gspn::Problem pr;
+  gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
+                            dtype, out, &chk, &pr, logit_channels);
+  if (s != GSPN_OK) return s;
+  if (chk.ws_bytes > 0) {
+    if (!workspace || ws_bytes < chk.ws_bytes)
+      return fail(GSPN_E_WORKSPACE, "workspace missing or smaller than gspn_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+    const size_t lbytes = static_cast<size_t>(B * logit_channels * H * W) * es;
+    const void* all[7] = {x, lambda, u, out, w_logits[0], w_logits[1], w_logits[2]};
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(workspace, chk.ws_bytes, all[i], i < 4 ? bytes : lbytes))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  if (B * C == 0) return GSPN_OK;
+  return run(pr, chk.plan, workspace, stream);
 }
 
 }  // extern "C"

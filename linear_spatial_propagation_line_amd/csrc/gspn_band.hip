@@ -52,6 +52,7 @@ struct BandArgs {
   int64_t planes;
   int H, W, G;
   unsigned mask;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
 };
 
 // GM = compile-time bound on G (8 or 16); chains have min(G, rest) steps.
@@ -99,13 +100,14 @@ __global__ __launch_bounds__(kBandThreads, GM <= 8 ? 4 : 2) void band_kernel(Ban
   // loads of round rd of plane p at clamped, always in-bounds addresses
   auto issue = [&](int64_t p, int rd, Loads& L) {
     const int64_t base = p * H * W;
+    const int64_t ls = logit_shift(p, a.C, a.Cl, static_cast<int64_t>(H) * W);
     if (rd < nrv) {
       const int b = rd * pv + vbl;
       const int r0 = min(b, nbv - 1) * G;
 #pragma unroll
       for (int s = 0; s < GM; ++s) {
         const int64_t i = base + static_cast<int64_t>(min(r0 + s, H - 1)) * W + vc;
-        L.g0[s] = bld(a.l0, i); L.g1[s] = bld(a.l1, i); L.g2[s] = bld(a.l2, i);
+        L.g0[s] = bld(a.l0, i + ls); L.g1[s] = bld(a.l1, i + ls); L.g2[s] = bld(a.l2, i + ls);
         L.x[s] = bld(a.x, i); L.l[s] = bld(a.lam, i);
       }
     } else {
@@ -114,13 +116,13 @@ __global__ __launch_bounds__(kBandThreads, GM <= 8 ? 4 : 2) void band_kernel(Ban
       const int r = min(hr, H - 1);
       if constexpr (VH) {
         const int64_t i = base + static_cast<int64_t>(r) * W + c0;
-        run_ld<GM>(a.l0, i, L.g0); run_ld<GM>(a.l1, i, L.g1); run_ld<GM>(a.l2, i, L.g2);
+        run_ld<GM>(a.l0, i + ls, L.g0); run_ld<GM>(a.l1, i + ls, L.g1); run_ld<GM>(a.l2, i + ls, L.g2);
         run_ld<GM>(a.x, i, L.x); run_ld<GM>(a.lam, i, L.l);
       } else {
 #pragma unroll
         for (int s = 0; s < GM; ++s) {
           const int64_t i = base + static_cast<int64_t>(r) * W + min(c0 + s, W - 1);
-          L.g0[s] = bld(a.l0, i); L.g1[s] = bld(a.l1, i); L.g2[s] = bld(a.l2, i);
+          L.g0[s] = bld(a.l0, i + ls); L.g1[s] = bld(a.l1, i + ls); L.g2[s] = bld(a.l2, i + ls);
           L.x[s] = bld(a.x, i); L.l[s] = bld(a.lam, i);
         }
       }
@@ -281,6 +283,8 @@ static hipError_t launch_band_t(const Problem& pr, hipStream_t stream, Tracer* t
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G);
   a.mask = pr.mask;
+  a.C = pr.C;
+  a.Cl = pr.Cl;
   const size_t lds = band_lds_bytes(pr.H, pr.W, pr.G);
   auto kern = band_kernel<T, GM, VH>;
   if (lds > 65536) {

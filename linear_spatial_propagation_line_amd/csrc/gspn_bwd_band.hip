@@ -60,6 +60,8 @@ struct BBandArgs {
   int64_t planes;
   int H, W, G;
   unsigned mask;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
+  float* dlw;       // shared logits: per-plane fp32 logit gradients [3][planes*H*W]
 };
 
 // VH: G == 8, W a multiple of 8 and every tensor 16-byte aligned, so a
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
 
   for (int64_t p = blockIdx.x; p < a.planes; p += gridDim.x) {
     const int64_t base = p * H * W;
+    const int64_t lsh = logit_shift(p, a.C, a.Cl, static_cast<int64_t>(H) * W);
     for (int rd = 0; rd < nrv + nrh; ++rd) {
       const bool vround = rd < nrv;
       int len, ls, nb, li, o, n_o;
@@ -124,14 +127,15 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
       {
         float vl0[GM], vl1[GM], vl2[GM], vlam[GM], vx[GM], vu[GM], vgy[GM];
         if (VH && !vround) {
-          run_ld<GM>(a.l0, gi0, vl0); run_ld<GM>(a.l1, gi0, vl1); run_ld<GM>(a.l2, gi0, vl2);
+          run_ld<GM>(a.l0, gi0 + lsh, vl0); run_ld<GM>(a.l1, gi0 + lsh, vl1);
+          run_ld<GM>(a.l2, gi0 + lsh, vl2);
           run_ld<GM>(a.lam, gi0, vlam); run_ld<GM>(a.x, gi0, vx);
           run_ld<GM>(a.u, gi0, vu); run_ld<GM>(a.gy, gi0, vgy);
         } else {
 #pragma unroll
           for (int s = 0; s < GM; ++s) {
             const int64_t i = gi0 + min(s, max(len - 1, 0)) * gstride;
-            vl0[s] = bb_ld(a.l0, i); vl1[s] = bb_ld(a.l1, i); vl2[s] = bb_ld(a.l2, i);
+            vl0[s] = bb_ld(a.l0, i + lsh); vl1[s] = bb_ld(a.l1, i + lsh); vl2[s] = bb_ld(a.l2, i + lsh);
             vlam[s] = bb_ld(a.lam, i); vx[s] = bb_ld(a.x, i);
             vu[s] = bb_ld(a.u, i); vgy[s] = bb_ld(a.gy, i);
           }
@@ -279,8 +283,14 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
             o6[4][s] = xs[s] * te;
             o6[5][s] = gys[s] * th;
           }
-          run_st<GM>(a.dx, gi0, o6[0]); run_st<GM>(a.dl0, gi0, o6[1]);
-          run_st<GM>(a.dl1, gi0, o6[2]); run_st<GM>(a.dl2, gi0, o6[3]);
+          run_st<GM>(a.dx, gi0, o6[0]);
+          if (a.dlw) {
+            run_st<GM>(a.dlw, gi0, o6[1]); run_st<GM>(a.dlw + ps, gi0, o6[2]);
+            run_st<GM>(a.dlw + 2 * ps, gi0, o6[3]);
+          } else {
+            run_st<GM>(a.dl0, gi0, o6[1]); run_st<GM>(a.dl1, gi0, o6[2]);
+            run_st<GM>(a.dl2, gi0, o6[3]);
+          }
           run_st<GM>(a.dlam, gi0, o6[4]); run_st<GM>(a.du, gi0, o6[5]);
         }
         __syncthreads();   // the line is cleared by the next round
@@ -295,9 +305,15 @@ __global__ __launch_bounds__(kBbThreads) void bband_kernel(BBandArgs<T> a) {
           if (final_round) {
             Store<T>::put(a.dx, i, lams[s] * te);
             Store<T>::put(a.dlam, i, xs[s] * te);
-            Store<T>::put(a.dl0, i, t0);
-            Store<T>::put(a.dl1, i, t1);
-            Store<T>::put(a.dl2, i, t2);
+            if (a.dlw) {
+              a.dlw[i] = t0;
+              a.dlw[ps + i] = t1;
+              a.dlw[2 * ps + i] = t2;
+            } else {
+              Store<T>::put(a.dl0, i, t0);
+              Store<T>::put(a.dl1, i, t1);
+              Store<T>::put(a.dl2, i, t2);
+            }
             Store<T>::put(a.du, i, gys[s] * th);
           } else {
             a.part[i] = te;
@@ -345,6 +361,9 @@ static hipError_t launch_bband_t(const BwdProblem& pr, void* ws, hipStream_t str
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G);
   a.mask = pr.mask;
+  a.C = pr.C;
+  a.Cl = pr.Cl;
+  a.dlw = pr.dlw;
   // four line arrays per round: at most kBbThreads / n_o bands of n_o + 2
   const int64_t nbv = (pr.H + pr.G - 1) / pr.G, nbh = (pr.W + pr.G - 1) / pr.G;
   const int64_t pv = kBbThreads / pr.W < nbv ? kBbThreads / pr.W : nbv;
@@ -375,7 +394,7 @@ static hipError_t launch_bband_dt(const BwdProblem& pr, void* ws, hipStream_t st
   const bool vh = pr.G == kBbG && pr.W % kBbG == 0 && al16(pr.x) && al16(pr.lam) &&
                   al16(pr.l[0]) && al16(pr.l[1]) && al16(pr.l[2]) && al16(pr.u) &&
                   al16(pr.gy) && al16(pr.dx) && al16(pr.dl[0]) && al16(pr.dl[1]) &&
-                  al16(pr.dl[2]) && al16(pr.dlam) && al16(pr.du) && al16(ws);
+                  al16(pr.dl[2]) && al16(pr.dlam) && al16(pr.du) && al16(ws) && al16(pr.dlw);
   return vh ? launch_bband_t<T, true>(pr, ws, stream, tr) : launch_bband_t<T, false>(pr, ws, stream, tr);
 }
 

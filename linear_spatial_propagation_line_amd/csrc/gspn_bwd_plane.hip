@@ -86,6 +86,8 @@ struct BPlaneArgs {
   unsigned mask;
   int pitch;        // LDS row pitch in pixels (W rounded up to odd)
   float inv_W, inv_HW;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
+  float* dlw;       // shared logits: per-plane fp32 logit gradients [3][planes*H*W]
 };
 
 // Pixel i of a plane group is handled by thread i % NT in every per-pixel
@@ -120,21 +122,23 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     const int npix = np * HW;
 
     // ---- 1. records ---------------------------------------------------------
-    // LDS index of pixel i of the group
-    auto lds_index = [&](int i, int* r, int* c) {
+    // LDS index of pixel i of the group (and its plane within the group)
+    auto lds_index = [&](int i, int* r, int* c, int* pp_out = nullptr) {
       int rem;
       const int pp = div_small(i, HW, a.inv_HW, &rem);
       *r = div_small(rem, W, a.inv_W, c);
+      if (pp_out) *pp_out = pp;
       return (pp * H + *r) * pitch + *c;
     };
 #pragma unroll 4
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i < npix) {
-        int r, c;
-        const int li = lds_index(i, &r, &c);
+        int r, c, pp;
+        const int li = lds_index(i, &r, &c, &pp);
         const int64_t gi = gbase + i;
-        const Weights w = make_weights(pl1(a.l0, gi), pl1(a.l1, gi), pl1(a.l2, gi), 1.f, 1.f);
+        const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
+        const Weights w = make_weights(pl1(a.l0, lgi), pl1(a.l1, lgi), pl1(a.l2, lgi), 1.f, 1.f);
         smem[li] = make_float4(w.w0, w.w1, w.w2, pl1(a.lam, gi) * pl1(a.x, gi));
       }
     }
@@ -259,11 +263,12 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i >= npix) continue;
-      int r, c;
-      const int li = lds_index(i, &r, &c);
+      int r, c, pp;
+      const int li = lds_index(i, &r, &c, &pp);
       const int64_t gi = gbase + i;
+      const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
       const float xv = pl1(a.x, gi), lv = pl1(a.lam, gi), gyv = pl1(a.gy, gi);
-      const float g0 = pl1(a.l0, gi), g1 = pl1(a.l1, gi), g2 = pl1(a.l2, gi);
+      const float g0 = pl1(a.l0, lgi), g1 = pl1(a.l1, lgi), g2 = pl1(a.l2, lgi);
       float se = 0.f, sh = 0.f;
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
@@ -310,9 +315,16 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
         }
       }
       Store<T>::put(a.dx, gi, lv * se);
-      Store<T>::put(a.dl0, gi, gl[0]);
-      Store<T>::put(a.dl1, gi, gl[1]);
-      Store<T>::put(a.dl2, gi, gl[2]);
+      if (a.dlw) {
+        const int64_t P = a.nplanes * HW;
+        a.dlw[gi] = gl[0];
+        a.dlw[P + gi] = gl[1];
+        a.dlw[2 * P + gi] = gl[2];
+      } else {
+        Store<T>::put(a.dl0, gi, gl[0]);
+        Store<T>::put(a.dl1, gi, gl[1]);
+        Store<T>::put(a.dl2, gi, gl[2]);
+      }
       Store<T>::put(a.dlam, gi, xv * se);
       Store<T>::put(a.du, gi, gyv * sh);
     }
@@ -355,6 +367,9 @@ static hipError_t launch_bplane_t(const BwdProblem& pr, hipStream_t stream, Trac
   a.pitch = static_cast<int>(pr.W | 1);
   a.inv_W = 1.0f / static_cast<float>(pr.W);
   a.inv_HW = 1.0f / static_cast<float>(pr.H * pr.W);
+  a.C = pr.C;
+  a.Cl = pr.Cl;
+  a.dlw = pr.dlw;
   const size_t lds = bplane_lds_bytes(pr.H, pr.W);
   auto kern = bplane_kernel<T, SEG, NT>;
   hipError_t e;

@@ -71,7 +71,25 @@ struct BwArgs {
   float* acc;       // [5][planes][H][W]: d(lambda x), dl0, dl1, dl2, sum of h
   int64_t pstride;  // planes * H * W
   int H, W, G, dir, mode;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
+  float* dlw;       // shared logits: per-plane fp32 logit gradients [3][planes*H*W]
 };
+
+// logit gradients of pixel idx: to the storage type, or per plane in fp32
+// when logits are shared (summed over each group afterwards)
+template <typename T>
+__device__ __forceinline__ void put_dl(const BwArgs<T>& a, int64_t idx, float g0, float g1,
+                                       float g2) {
+  if (a.dlw) {
+    a.dlw[idx] = g0;
+    a.dlw[a.pstride + idx] = g1;
+    a.dlw[2 * a.pstride + idx] = g2;
+  } else {
+    Store<T>::put(a.dl0, idx, g0);
+    Store<T>::put(a.dl1, idx, g1);
+    Store<T>::put(a.dl2, idx, g2);
+  }
+}
 
 // Both scans keep every position's loads for D consecutive steps in flight
 // together: all loads of a batch are issued first, unconditionally, at
@@ -92,6 +110,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
   const bool first = a.mode & kBwFirst, last = a.mode & kBwLast;
   const bool keep_sum = !(first && last);   // a single direction needs no running sum
   float* hsum = a.acc + 4 * a.pstride;
+  const int64_t ls = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
   for (int s0 = 0; s0 < n_s; s0 += D) {
     float lx[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP], hs[D][MAXP];
 #pragma unroll
@@ -104,9 +123,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
         const int r = vert ? pos : o, c = vert ? o : pos;
         const int64_t idx = base + static_cast<int64_t>(r) * W + c;
         lx[j][i] = bl(a.lam, idx) * bl(a.x, idx);
-        g0[j][i] = bl(a.l0, idx);
-        g1[j][i] = bl(a.l1, idx);
-        g2[j][i] = bl(a.l2, idx);
+        g0[j][i] = bl(a.l0, idx + ls);
+        g1[j][i] = bl(a.l1, idx + ls);
+        g2[j][i] = bl(a.l2, idx + ls);
         hs[j][i] = (keep_sum && !first) ? hsum[idx] : 0.f;
       }
     }
@@ -160,6 +179,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   const int back = fwd ? -1 : 1;
   const int64_t back_off = vert ? static_cast<int64_t>(back) * W : back;
   const int64_t oo = vert ? 1 : W;   // orthogonal stride
+  const int64_t lsh = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
 
   float a1[MAXP];
 #pragma unroll
@@ -189,9 +209,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
         const int64_t pidx = restart ? idx : idx + back_off;
         gy[j][i] = bl(a.gy, idx);
         ug[j][i] = bl(a.u, idx) * gy[j][i];
-        g0[j][i] = bl(a.l0, idx);
-        g1[j][i] = bl(a.l1, idx);
-        g2[j][i] = bl(a.l2, idx);
+        g0[j][i] = bl(a.l0, idx + lsh);
+        g1[j][i] = bl(a.l1, idx + lsh);
+        g2[j][i] = bl(a.l2, idx + lsh);
         hc[j][i] = a.hbuf[pidx];
         hl[j][i] = a.hbuf[o > 0 ? pidx - oo : pidx];
         hr[j][i] = a.hbuf[o < n_o - 1 ? pidx + oo : pidx];
@@ -260,9 +280,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
           if (last) {
             Store<T>::put(a.dx, idx, ls[j][i] * dphi);
             Store<T>::put(a.dlam, idx, xs[j][i] * dphi);
-            Store<T>::put(a.dl0, idx, dl0);
-            Store<T>::put(a.dl1, idx, dl1);
-            Store<T>::put(a.dl2, idx, dl2);
+            put_dl(a, idx, dl0, dl1, dl2);
             Store<T>::put(a.du, idx, gy[j][i] * hs[j][i]);
           } else {
             a.acc[idx] = dphi;
@@ -332,9 +350,7 @@ __global__ __launch_bounds__(256) void bwd_finish(BwArgs<T> a) {
     const float dphi = a.acc[i];
     Store<T>::put(a.dx, i, bl(a.lam, i) * dphi);
     Store<T>::put(a.dlam, i, bl(a.x, i) * dphi);
-    Store<T>::put(a.dl0, i, a.acc[ps + i]);
-    Store<T>::put(a.dl1, i, a.acc[2 * ps + i]);
-    Store<T>::put(a.dl2, i, a.acc[3 * ps + i]);
+    put_dl(a, i, a.acc[ps + i], a.acc[2 * ps + i], a.acc[3 * ps + i]);
     Store<T>::put(a.du, i, bl(a.gy, i) * a.acc[4 * ps + i]);
   }
 }
@@ -466,6 +482,9 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
   a.H = static_cast<int>(pr.H);
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G);
+  a.C = pr.C;
+  a.Cl = pr.Cl;
+  a.dlw = pr.dlw;
   const bool t2b = pr.mask & 1u, b2t = pr.mask & 2u, l2r = pr.mask & 4u, r2l = pr.mask & 8u;
   hipError_t e;
   bool acc_written = false;
@@ -476,7 +495,16 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
     T* dst[7];
     T* in_t = reinterpret_cast<T*>(wsb + lay.in_t);
     for (int i = 0; i < 7; ++i) dst[i] = in_t + i * a.pstride;
-    if ((e = transpose<T>(src, dst, 7, planes, a.H, a.W, stream, tr)) != hipSuccess) return e;
+    if (pr.Cl == pr.C) {
+      if ((e = transpose<T>(src, dst, 7, planes, a.H, a.W, stream, tr)) != hipSuccess) return e;
+    } else {
+      // shared logits have B * Cl planes of their own
+      const T* s4[4] = {a.x, a.lam, a.u, a.gy};
+      T* d4[4] = {dst[0], dst[4], dst[5], dst[6]};
+      if ((e = transpose<T>(s4, d4, 4, planes, a.H, a.W, stream, tr)) != hipSuccess) return e;
+      if ((e = transpose<T>(src + 1, dst + 1, 3, pr.B * pr.Cl, a.H, a.W, stream, tr)) != hipSuccess)
+        return e;
+    }
     BwArgs<T> t = a;
     t.x = dst[0]; t.l0 = dst[1]; t.l1 = dst[2]; t.l2 = dst[3]; t.lam = dst[4]; t.u = dst[5];
     t.gy = dst[6];
@@ -510,6 +538,50 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
     if ((e = run_direction(a, 1, mode, planes, stream, tr)) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// shared logits: the gradient of logit plane (b, cl) at a pixel is the sum,
+// in channel order, of the per-plane gradients of the C / Cl channels that
+// read it
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_logits(const float* dlw, T* d0, T* d1, T* d2,
+                                                         int64_t B, int64_t C, int64_t Cl,
+                                                         int64_t HW) {
+  const int64_t n = B * Cl * HW, P = B * C * HW, g = C / Cl;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t lp = i / HW, pix = i - lp * HW;
+    const int64_t b = lp / Cl, cl = lp - b * Cl;
+    const int64_t first = (b * C + cl * g) * HW + pix;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+    for (int64_t c = 0; c < g; ++c) {
+      const int64_t q = first + c * HW;
+      s0 += dlw[q];
+      s1 += dlw[P + q];
+      s2 += dlw[2 * P + q];
+    }
+    Store<T>::put(d0, i, s0);
+    Store<T>::put(d1, i, s1);
+    Store<T>::put(d2, i, s2);
+  }
+}
+
+template <typename T>
+static hipError_t launch_reduce_dt(const BwdProblem& pr, hipStream_t stream, Tracer* tr) {
+  const int64_t n = pr.B * pr.Cl * pr.H * pr.W;
+  const int64_t blocks = (n + 255) / 256;
+  const int64_t grid = blocks < 65536 * 16 ? blocks : 65536 * 16;
+  tr->before(stream, "bwd_reduce_logits", pr.B * pr.Cl);
+  hipLaunchKernelGGL(bwd_reduce_logits<T>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     pr.dlw, static_cast<T*>(pr.dl[0]), static_cast<T*>(pr.dl[1]),
+                     static_cast<T*>(pr.dl[2]), pr.B, pr.C, pr.Cl, pr.H * pr.W);
+  tr->after(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce_logits(const BwdProblem& pr, hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_reduce_dt<float>(pr, stream, tr);
+  return launch_reduce_dt<bf16_t>(pr, stream, tr);
 }
 
 hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr) {

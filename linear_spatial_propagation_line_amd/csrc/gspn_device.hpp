@@ -207,6 +207,19 @@ template <> __device__ __forceinline__ float from_right<16>(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// channel-shared logits: plane p = (b, c) of a [B, C] batch reads logit
+// channel c / (C / Cl) of batch entry b. Returns how many elements the
+// plane's logits sit after (or before) its own offset: add it to a pixel
+// index of the plane to get the pixel's logit index. 0 when Cl == C.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int64_t logit_shift(int64_t p, int64_t C, int64_t Cl,
+                                                        int64_t HW) {
+  if (Cl == C) return 0;
+  const int64_t b = p / C, c = p - b * C;
+  return (b * Cl + c / (C / Cl) - p) * HW;
+}
+
+// ---------------------------------------------------------------------------
 // small exact integer division for n < 2^24 (plane-local pixel indices)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int div_small(int n, int d, float inv_d, int* rem) {

@@ -22,6 +22,7 @@ struct Problem {
   gspn_dtype dtype;
   bool aligned_vec4;   // every pointer aligned to 4 elements
   bool aligned_pair;   // every pointer aligned to 2 elements
+  int64_t Cl;          // logit channels (Cl divides C; Cl == C: unshared)
 };
 
 // A validated backward problem: the forward inputs, grad_out (gy) and the six
@@ -41,6 +42,10 @@ struct BwdProblem {
   int64_t G;
   gspn_dtype dtype;
   bool aligned_vec4;   // every pointer aligned to 4 elements
+  int64_t Cl;          // logit channels (Cl divides C; Cl == C: unshared)
+  // Cl < C: the kernels write each plane's logit gradients here in fp32
+  // ([3][B*C*H*W]) and bwd_reduce_logits sums each group into dl[]
+  float* dlw;
 };
 
 // Records caller-owned events around kernel launches (gspn_trace_events),
@@ -89,6 +94,9 @@ hipError_t launch_bplane(const BwdProblem& pr, hipStream_t stream, Tracer* tr);
 bool bband_fits(int64_t H, int64_t W, int64_t G);
 size_t bband_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask);
 hipError_t launch_bband(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
+
+// sum per-plane logit gradients over the channels sharing each logit plane
+hipError_t launch_bwd_reduce_logits(const BwdProblem& pr, hipStream_t stream, Tracer* tr);
 
 // backward pass, streaming path for any plane (gspn_bwd_stream.hip)
 size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,

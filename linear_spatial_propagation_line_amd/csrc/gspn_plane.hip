@@ -45,6 +45,7 @@ struct PlaneArgs {
   unsigned mask;
   int pitch;        // records per LDS row (W rounded up to odd)
   float inv_W, inv_HW;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
 };
 
 __device__ __forceinline__ float ld1(const float* p, int64_t i) { return p[i]; }
@@ -80,12 +81,19 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int i0 = tid * 4 + it * 1024;
-      const int64_t gi = gb + (i0 < npx ? i0 : 0);   // always in bounds
+      const int ic = i0 < npx ? i0 : 0;                // always in bounds
+      const int64_t gi = gb + ic;
+      int64_t lgi = gi;
+      if (a.Cl != a.C) {
+        int rem;
+        const int pin = PPB == 1 ? 0 : div_small(ic, HW, a.inv_HW, &rem);
+        lgi += logit_shift(grp * PPB + pin, a.C, a.Cl, HW);
+      }
       rx[it] = V::load(a.x, gi);
       rl[it] = V::load(a.lam, gi);
-      r0[it] = V::load(a.l0, gi);
-      r1[it] = V::load(a.l1, gi);
-      r2[it] = V::load(a.l2, gi);
+      r0[it] = V::load(a.l0, lgi);
+      r1[it] = V::load(a.l1, lgi);
+      r2[it] = V::load(a.l2, lgi);
       ru[it] = V::load(a.u, gi);
     }
   };
@@ -127,7 +135,8 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
         const int p = div_small(i0, HW, a.inv_HW, &rem);
         const int r = div_small(rem, W, a.inv_W, &c);
         const int64_t gi = gbase + i0;
-        const Weights w = make_weights(ld1(a.l0, gi), ld1(a.l1, gi), ld1(a.l2, gi), 1.0f, 1.0f);
+        const int64_t lgi = gi + logit_shift(plane0 + p, a.C, a.Cl, HW);
+        const Weights w = make_weights(ld1(a.l0, lgi), ld1(a.l1, lgi), ld1(a.l2, lgi), 1.0f, 1.0f);
         smem[(p * H + r) * pitch + c] = make_float4(w.w0, w.w1, w.w2, ld1(a.lam, gi) * ld1(a.x, gi));
       }
     }
@@ -281,6 +290,8 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   a.pitch = static_cast<int>(pr.W | 1);
   a.inv_W = 1.0f / static_cast<float>(pr.W);
   a.inv_HW = 1.0f / static_cast<float>(pr.H * pr.W);
+  a.C = pr.C;
+  a.Cl = pr.Cl;
   const size_t lds = plane_lds_bytes(pr.H, pr.W);
   auto kern = plane_kernel<T, SEG, VEC>;
   hipError_t e;

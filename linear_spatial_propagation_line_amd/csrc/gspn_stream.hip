@@ -34,6 +34,7 @@ struct StreamArgs {
   int H, W, G;
   int dir;
   int mode;
+  int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
 };
 
 __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
@@ -46,6 +47,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs<T> a) {
   const bool vert = d < 2, fwd = (d == 0 || d == 2);
   const int n_s = vert ? H : W, n_o = vert ? W : H;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * H * W;
+  const int64_t ls = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
   int next_restart = n_s;
   if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
 
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs<T> a) {
       const int64_t idx = base + static_cast<int64_t>(r) * W + c;
       float h = ld(a.lam, idx) * ld(a.x, idx);
       if (!restart) {
-        const Weights w = make_weights(ld(a.l0, idx), ld(a.l1, idx), ld(a.l2, idx),
+        const Weights w = make_weights(ld(a.l0, idx + ls), ld(a.l1, idx + ls), ld(a.l2, idx + ls),
                                        o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
         const float hl = prev[o > 0 ? o - 1 : 0];
         const float hr = prev[o < n_o - 1 ? o + 1 : o];
@@ -104,6 +106,8 @@ static hipError_t launch_stream_dt(const Problem& pr, float* acc, hipStream_t st
     a.W = static_cast<int>(pr.W);
     a.G = static_cast<int>(pr.G);
     a.dir = dirs[i];
+    a.C = pr.C;
+    a.Cl = pr.Cl;
     a.mode = nd == 1 ? kOnly : (i == 0 ? kFirst : (i == nd - 1 ? kLast : kMid));
     const int64_t n_o = dirs[i] < 2 ? pr.W : pr.H;
     const size_t lds = static_cast<size_t>(2 * n_o) * sizeof(float);

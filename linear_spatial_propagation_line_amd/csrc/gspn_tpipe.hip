@@ -105,15 +105,16 @@ struct Raw2 {
   typename Pair<T>::raw x, lam, l0, l1, l2;
 };
 
+// (the logits of pixel i sit at i + ls: ls = 0 unless logits are shared)
 template <typename T>
 __device__ __forceinline__ Raw2<T> load_raw2(const T* x, const T* lam, const T* l0, const T* l1,
-                                             const T* l2, int64_t i) {
+                                             const T* l2, int64_t i, int64_t ls) {
   Raw2<T> r;
   r.x = Pair<T>::load(x, i);
   r.lam = Pair<T>::load(lam, i);
-  r.l0 = Pair<T>::load(l0, i);
-  r.l1 = Pair<T>::load(l1, i);
-  r.l2 = Pair<T>::load(l2, i);
+  r.l0 = Pair<T>::load(l0, i + ls);
+  r.l1 = Pair<T>::load(l1, i + ls);
+  r.l2 = Pair<T>::load(l2, i + ls);
   return r;
 }
 
@@ -202,6 +203,7 @@ struct TpArgs {
   unsigned mask;
   int64_t lg_stride;   // elements between the three logit copies
   int64_t plane0;      // first plane of this launch (blockIdx.x is relative)
+  int64_t C, Cl;       // channels and logit channels (shared logits when Cl < C)
 };
 
 // ===========================================================================
@@ -232,8 +234,9 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
   LineX lx{lbuf, n4, 0};
   const float mA0 = c0 > 0 ? 1.f : 0.f;              // column c0 has a left neighbour
   const float mB2 = c0 + 1 < W - 1 ? 1.f : 0.f;      // column c0+1 has a right neighbour
+  const int64_t ls = logit_shift(plane, a.C, a.Cl, static_cast<int64_t>(H) * W);
   auto load_row = [&](int r) {
-    return load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, base + (int64_t)min(r, H - 1) * W + cl);
+    return load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, base + (int64_t)min(r, H - 1) * W + cl, ls);
   };
 
   Raw2<T> ring[PF];
@@ -511,6 +514,7 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
   const int cl = act ? c0 : 0;
   const int64_t plane = a.plane0 + blockIdx.x;
   const int64_t base = plane * H * W;
+  const int64_t ls = logit_shift(plane, a.C, a.Cl, static_cast<int64_t>(H) * W);
   const int n4 = W + 4;
   for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
   __syncthreads();
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < kCkV; ++i) {
       const int64_t idx = base + (int64_t)min(rs + i, H - 1) * W + cl;
-      ch.in[i] = load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, idx);
+      ch.in[i] = load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, idx, ls);
       ch.u[i] = P::load(a.u, idx);
     }
     if constexpr (HZ) {
@@ -728,6 +732,8 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   a.nckv = static_cast<int>(L.nckv);
   a.nckh = static_cast<int>(L.nckh);
   a.mask = pr.mask;
+  a.C = pr.C;
+  a.Cl = pr.Cl;
   a.lg_stride = planes * pr.W * L.Hp;
   a.plane0 = 0;
   const unsigned tv = static_cast<unsigned>((pr.W / 2 + 63) / 64 * 64);

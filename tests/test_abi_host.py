@@ -208,3 +208,37 @@ def test_backward_plans(LB, monkeypatch):
     monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
     assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"
     assert g.backward_workspace_bytes(1, 2, 8, 8, dirs=g.T2B | g.B2T) == 6 * 2 * 64 * 4
+
+
+@pytest.mark.parametrize("cl", [0, -1, 3])
+def test_shared_logit_channels_must_divide(LB, cl):
+    lg = (ctypes.c_void_p * 3)(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ)
+    st = LB.gspn_propagate_shared_ws(BASE, lg, cl, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 8, 8, 15,
+                                     0, 0, BASE + 6 * SZ, None, 0, None)
+    assert st == g.STATUS["GSPN_E_SHAPE"]
+    dlg = (ctypes.c_void_p * 3)(BASE + 8 * SZ, BASE + 9 * SZ, BASE + 10 * SZ)
+    st = LB.gspn_propagate_backward_shared_ws(BASE, lg, cl, BASE + 4 * SZ, BASE + 5 * SZ,
+                                              BASE + 6 * SZ, 1, 4, 8, 8, 15, 0, 0, BASE + 7 * SZ,
+                                              dlg, BASE + 11 * SZ, BASE + 12 * SZ, None, 0, None)
+    assert st == g.STATUS["GSPN_E_SHAPE"]
+    assert LB.gspn_backward_workspace_bytes_shared(1, 4, 8, 8, cl, 15, 0, 0) == 0
+
+
+def test_shared_workspace(LB):
+    px = 2 * 4 * 56 * 56
+    # plane-resident backward: no plan workspace, only the per-channel logit gradients
+    assert g.backward_workspace_bytes(2, 4, 56, 56, logit_channels=1) == 3 * px * 4
+    assert g.backward_workspace_bytes(2, 4, 56, 56, logit_channels=4) == 0
+    assert g.backward_workspace_bytes(2, 4, 56, 56, logit_channels=2) == 3 * px * 4
+
+
+def test_shared_aliasing_uses_logit_size(LB):
+    # out placed right after one shared logit plane: no overlap with Cl = 1
+    lg = (ctypes.c_void_p * 3)(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ)
+    out = BASE + SZ + 8 * 8 * 4          # one 8x8 fp32 logit plane after l0
+    st = LB.gspn_propagate_shared_ws(BASE, lg, 1, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 8, 8, 15,
+                                     0, 0, out, None, 0, None)
+    assert st != g.STATUS["GSPN_E_ALIAS"]
+    st = LB.gspn_propagate_shared_ws(BASE, lg, 4, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 8, 8, 15,
+                                     0, 0, out, None, 0, None)
+    assert st == g.STATUS["GSPN_E_ALIAS"]
