@@ -124,6 +124,8 @@ def design_bytes(kernel: str, planes: int, w) -> float:
       bwd_transpose  seven inputs read and written (2 * 7 s), or, over 5x the
           planes, the fp32 accumulators (2 * 4)
       bwd_finish  5 * 4 accumulators + 3 s (x, lambda, grad_out) + 6 s out
+      bwd_reduce_logits (shared logits): three fp32 per-channel gradients
+          read, three shared gradients written (Cl / C of a tensor each)
       bband_kernel (local groups): seven inputs read in the vertical and again
           in the horizontal rounds, five fp32 partial sums written and read
           back, six gradients written -> 20 s + 40
@@ -146,6 +148,7 @@ def design_bytes(kernel: str, planes: int, w) -> float:
         "bwd_transpose": 2 * 7 * s if planes == w.B * w.C else 2 * 4,
         "bwd_finish": 20 + 9 * s,
         "bband_kernel": 20 * s + 40,
+        "bwd_reduce_logits": 12 + 3 * s * w.cl / w.C,
     }[kernel]
     return per * px
 
@@ -189,7 +192,20 @@ def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
             return t.view(torch.int16).numpy().view(np.uint16).reshape(1, planes, w.H, w.W)
         return t.numpy().reshape(1, planes, w.H, w.W)
 
-    arrs = [host(inp_dev[k]) for k in ("x", "l0", "l1", "l2", "lam", "u")]
+    # shared logits: whole channel groups, and the logit planes they read
+    g = w.C // w.cl
+    if g > 1 and planes > g:
+        planes = planes // g * g
+
+    def host_logits(t):
+        nlp = (planes + g - 1) // g
+        t = t.reshape(-1, w.H, w.W)[:nlp].cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16).reshape(1, nlp, w.H, w.W)
+        return t.numpy().reshape(1, nlp, w.H, w.W)
+
+    arrs = [host(inp_dev["x"])] + [host_logits(inp_dev[k]) for k in ("l0", "l1", "l2")] + \
+        [host(inp_dev[k]) for k in ("lam", "u")]
     threads = min(cores, planes)
     t0 = time.perf_counter()
     if grad_out is None:
@@ -271,7 +287,11 @@ def main() -> int:
     # inputs resident in HBM; small problems rotate several input sets so the
     # timed loop does not run out of the 256 MB last-level cache
     s = 4 if w.dtype == "f32" else 2
-    per_px = 13 * s if bwd else 7 * s     # compulsory bytes per pixel
+    # compulsory bytes per pixel: x, lambda, u (and grad_out) read, out (or
+    # the gradients) written, plus the logits (and their gradients) at
+    # Cl / C of a tensor each when they are shared
+    share = w.cl / w.C
+    per_px = (7 + 6 * share) * s if bwd else (4 + 3 * share) * s
     set_bytes = per_px * w.pixels
     nsets = max(1, min(8, -(-1024 ** 3 // set_bytes)))
     sets = []
@@ -287,8 +307,10 @@ def main() -> int:
                 st["gy"] = make_grad_out(w, seed=seed + 1000).to(dev)
         sets.append(st)
     if bwd:
-        outs = [{k: torch.empty_like(st["x"]) for k in g.GRAD_NAMES} for st in sets]
-        ws_bytes = g.backward_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+        outs = [{k: torch.empty_like(st[k] if k in ("l0", "l1", "l2") else st["x"])
+                 for k in g.GRAD_NAMES} for st in sets]
+        ws_bytes = g.backward_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code,
+                                              logit_channels=w.cl)
     else:
         outs = [torch.empty_like(st["x"]) for st in sets]
         ws_bytes = g.workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
@@ -357,7 +379,7 @@ def main() -> int:
     # by the step time. Algorithmic bytes: the compulsory Q_min = 7 s per
     # pixel (five inputs and u read once, out written once), 13 s for the
     # backward pass (seven tensors read, six gradients written).
-    q_min = per_px * w.pixels
+    q_min = int(per_px * w.pixels)
     if nl == 1:
         unit_name, unit_ms = launches[0][0], per_launch[0]
     else:
@@ -382,6 +404,7 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
                    "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
+                   "logit_channels": w.cl,
                    "plan": plan, "launches_per_step": counts[0],
                    "launches": [f"{n}[{p}]" for n, p in launches],
                    "launch_ms": [round(t, 4) for t in per_launch],
@@ -398,8 +421,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
         # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core forward
-        # and about a tenth of that backward
-        rate = 2.5e6 if bwd else 2.5e7
+        # and 0.6e6 - 3e6 backward (large planes at the low end)
+        rate = 6e5 if bwd else 2.5e7
         planes = int(args.cpu_seconds * rate * cores / (w.H * w.W * w.ndirs)) + 1
         result["cpu_baseline"] = cpu_baseline(sets[0], w, planes,
                                               grad_out=sets[0]["gy"] if bwd else None)

@@ -16,6 +16,9 @@ weights):
   t2i_2048x1024      B=1,  C=320,  2048x1024, bf16, 4 directions, global
                      (16Kx8K text-to-image latent, /8 VAE; aitntnews page,
                      section 文本到图像生成)
+  t2i_2048x1024_cl1  the same with one logit channel shared by all 320
+                     channels (the speed-test setting of the CSDN page,
+                     section 局限性: the weights' feature dimension set to 1)
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
 generator seeded with 1000 + k (k = 1..5 in the order above) and then cast
@@ -48,6 +51,11 @@ class Workload:
     x: tuple
     lam: tuple
     u: tuple
+    logit_channels: int = 0   # 0: one logit channel per channel (unshared)
+
+    @property
+    def cl(self) -> int:
+        return self.logit_channels or self.C
 
     @property
     def pixels(self) -> int:
@@ -85,6 +93,8 @@ WORKLOADS = {
                  ("normal", 2.0), NORMAL1, ("uniform", 0.0, 1.0), ("uniform", 0.0, 1.0)),
         Workload("t2i_2048x1024", 5, 1, 320, 2048, 1024, BF16, 15, 0,
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
+        Workload("t2i_2048x1024_cl1", 6, 1, 320, 2048, 1024, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, logit_channels=1),
     ]
 }
 
@@ -105,11 +115,14 @@ def _draw(spec, shape, gen, device):
 def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
                 B: int | None = None, C: int | None = None, H: int | None = None,
                 W: int | None = None) -> dict:
-    """Tensors x, l0, l1, l2, lam, u of shape [B, C, H, W] in the workload's
-    storage dtype on ``device``. Shape overrides keep the distributions."""
+    """Tensors x, lam, u of shape [B, C, H, W] and l0, l1, l2 of shape
+    [B, Cl, H, W] (Cl = C unless the workload shares logits) in the
+    workload's storage dtype on ``device``. Shape overrides keep the
+    distributions."""
     if isinstance(w, str):
         w = WORKLOADS[w]
     shape = (B or w.B, C or w.C, H or w.H, W or w.W)
+    lshape = (shape[0], w.logit_channels or shape[1], shape[2], shape[3])
     if seed is None:
         seed = 1000 + w.index
     gen = torch.Generator(device=device)
@@ -117,7 +130,8 @@ def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
     out = {}
     for name, spec in (("x", w.x), ("lam", w.lam), ("u", w.u),
                        ("l0", w.logits), ("l1", w.logits), ("l2", w.logits)):
-        out[name] = _draw(spec, shape, gen, device).to(w.torch_dtype)
+        shp = lshape if name in ("l0", "l1", "l2") else shape
+        out[name] = _draw(spec, shp, gen, device).to(w.torch_dtype)
     return out
 
 

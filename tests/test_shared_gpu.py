@@ -67,3 +67,25 @@ def test_shared_equals_repeated_unshared():
     b = g.propagate(d["x"], tuple(rep), d["lam"], d["u"])
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_t2i_shared_full_size_sampled_planes():
+    """The 2048x1024x320 bf16 workload with one logit channel shared by all
+    320 channels, at full size as the benchmark runs it, forward and
+    backward; the oracle checks sampled planes (with their logit plane)."""
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS
+    w = WORKLOADS["t2i_2048x1024_cl1"]
+    d = make_inputs(w, device=DEV)
+    gy = make_grad_out(w, device=DEV)
+    assert d["l0"].shape == (1, 1, 2048, 1024)
+    lg = (d["l0"], d["l1"], d["l2"])
+    out = g.propagate(d["x"], lg, d["lam"], d["u"], dirs=w.dirs)
+    grads = g.propagate_backward(d["x"], lg, d["lam"], d["u"], gy, dirs=w.dirs)
+    torch.cuda.synchronize()
+    for c in (0, 255):
+        inp = {k: (v if k in ("l0", "l1", "l2") else v[:, c:c + 1]).cpu() for k, v in d.items()}
+        assert_parity(out[:, c:c + 1], oracle_y(inp, w.dirs, 0), f"t2i shared plane {c}")
+        got = {k: v[:, c:c + 1] for k, v in grads.items() if k not in ("l0", "l1", "l2")}
+        ref = oracle_grads(inp, gy[:, c:c + 1].cpu(), w.dirs, 0)
+        ref = {k: ref[k] for k in got}
+        assert_grad_parity(got, ref, f"t2i shared plane {c}", names=tuple(got))
