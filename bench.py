@@ -114,6 +114,8 @@ def design_bytes(kernel: str, planes: int, w) -> float:
           tp_vfwd  5 s inputs + (4 + 3 s) copy write + 4/8 checkpoints
           tp_hpair 2 (4 + 3 s) copy reads + 2 * 4/4 checkpoints + 4 sum write
           tp_vbwd  5 s inputs + 4/8 checkpoints + 4 sum read + s (u) + s (out)
+          (shared logits, Cl < C: the logit part of the copy is 3 s Cl/C, made
+          by tp_lgcopy over the B * Cl logit planes: 6 s per logit pixel)
     Backward pass:
       bplane_kernel16/64: x, lambda, l0, l1, l2, u, grad_out read once, six
           gradients written -> 13 s (the second read of five inputs in the
@@ -133,13 +135,15 @@ def design_bytes(kernel: str, planes: int, w) -> float:
     s = 4 if w.dtype == "f32" else 2
     px = planes * w.H * w.W
     hz = bool(w.dirs & 12)
+    sh = w.cl / w.C   # shared logits: the logit copy is made once per logit plane
     per = {
         "plane_kernel16": 7 * s,
         "plane_kernel64": 7 * s,
         "stream_kernel": 5 * s + 4,
         "band_kernel": 12 * s,
-        "tp_vfwd": 5 * s + (4 + 3 * s if hz else 0) + (0.5 if w.dirs & 1 else 0),
-        "tp_hpair": 2 * (4 + 3 * s) + 2.0 + 4,
+        "tp_vfwd": 5 * s + (4 + 3 * s * sh if hz else 0) + (0.5 if w.dirs & 1 else 0),
+        "tp_hpair": 2 * (4 + 3 * s * sh) + 2.0 + 4,
+        "tp_lgcopy": 6 * s * (w.B * w.C) / max(planes, 1) * sh,
         "tp_vbwd": 5 * s + (0.5 if w.dirs & 1 else 0) + (4 if hz else 0) + 2 * s,
         "bplane_kernel16": 13 * s,
         "bplane_kernel64": 13 * s,

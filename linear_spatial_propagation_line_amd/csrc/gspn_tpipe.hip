@@ -209,11 +209,14 @@ struct TpArgs {
 // ===========================================================================
 // K1: top->bottom forward sweep, checkpoints, column-major copy
 // ===========================================================================
-// SCAN: run top->bottom and save checkpoints; COPY: write the column-major copy.
+// SCAN: run top->bottom and save checkpoints; COPY: write lambda*x into the
+// column-major copy; COPYLG: write the logits into it. With shared logits
+// the logit copy is made once per logit plane by tp_lgcopy and this kernel
+// writes lambda*x only.
 // The main loop covers full 32-row blocks with straight-line code and
 // unconditional (row-clamped) loads so that the prefetch ring stays in flight;
 // a partial last block runs the same body with per-row guards.
-template <typename T, bool SCAN, bool COPY>
+template <typename T, bool SCAN, bool COPY, bool COPYLG = COPY>
 __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
   __shared__ float lbuf[2 * (1024 + 4)];
   constexpr int LGP = sizeof(T) == 2 ? 32 : 16;   // logit flush period (rows): 64 B
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
             store_pair(a.ckv, (plane * a.nckv + r / kCkV) * W + c0, hA, hB);
           __syncthreads();
         }
-        if constexpr (COPY) {
-          lxP[j % LXP] = make_float2(lxa, lxb);
+        if constexpr (COPY) lxP[j % LXP] = make_float2(lxa, lxb);
+        if constexpr (COPYLG) {
           lgP[0][j % LGP] = v.l0;
           lgP[1][j % LGP] = v.l1;
           lgP[2][j % LGP] = v.l2;
@@ -295,6 +298,8 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
           for (int q = 0; q < LXP / 2; ++q)
             d[q] = make_float4(lxP[2 * q].x, lxP[2 * q].y, lxP[2 * q + 1].x, lxP[2 * q + 1].y);
         }
+      }
+      if constexpr (COPYLG) {
         if ((j % LGP) == LGP - 1 && act && (!TAIL || r0 + j - (LGP - 1) < H)) {
           const int rs = r0 + j - (LGP - 1);
 #pragma unroll
@@ -319,6 +324,45 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
   int r0 = 0;
   for (; r0 + U <= H; r0 += U) block(r0, std::false_type{});
   if (r0 < H) block(r0, std::true_type{});
+}
+
+// Shared logits: the column-major logit copy of the B * Cl logit planes, one
+// thread per (logit plane, 32-row block, column pair), column pair fastest so
+// that the row loads coalesce; each thread writes whole 32-row runs.
+template <typename T>
+__global__ __launch_bounds__(256) void tp_lgcopy(TpArgs<T> a, int64_t nlp) {
+  using P = Pair<T>;
+  const int H = a.H, W = a.W, Hp = a.Hp;
+  const int npairs = W / 2, nblk = Hp / 32;
+  const int64_t total = nlp * npairs * nblk;
+  for (int64_t t = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int cp = static_cast<int>(t % npairs);
+    const int64_t rest = t / npairs;
+    const int blk = static_cast<int>(rest % nblk);
+    const int64_t lp = rest / nblk;
+    const int r0 = blk * 32;
+    const int64_t src = lp * H * W + 2 * cp;
+    const int64_t dst = ((lp * npairs + cp) * Hp + r0) * 2;
+    const T* ls[3] = {a.l0, a.l1, a.l2};
+#pragma unroll
+    for (int z = 0; z < 3; ++z) {
+      typename P::raw v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j)   // rows past H land in the copy's padding
+        v[j] = P::load(ls[z], src + static_cast<int64_t>(min(r0 + j, H - 1)) * W);
+      T* g = a.lgt + z * a.lg_stride + dst;
+      if constexpr (sizeof(T) == 2) {
+        uint4* d = reinterpret_cast<uint4*>(g);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      } else {
+        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
+#pragma unroll
+        for (int q = 0; q < 16; ++q) d[q] = make_float4(v[2 * q].x, v[2 * q].y, v[2 * q + 1].x, v[2 * q + 1].y);
+      }
+    }
+  }
 }
 
 // ===========================================================================
@@ -350,13 +394,17 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
     float4 lx;                          // (o0: even, odd), (o0+1: even, odd)
     typename Q::raw g0, g1, g2;
   };
+  // the logit copy of this plane (shared logits: of its logit plane)
+  const int64_t lgpl = plane + logit_shift(plane, a.C, a.Cl, 1);
   auto load_pair = [&](int cp) {
     In2 v;
-    const int64_t i = ((plane * (W / 2) + min(max(cp, 0), W / 2 - 1)) * Hp + ol) * 2;
+    const int64_t cc = min(max(cp, 0), W / 2 - 1);
+    const int64_t i = ((plane * (W / 2) + cc) * Hp + ol) * 2;
+    const int64_t il = ((lgpl * (W / 2) + cc) * Hp + ol) * 2;
     v.lx = *reinterpret_cast<const float4*>(a.lxt + i);
-    v.g0 = Q::load(a.lgt, i);
-    v.g1 = Q::load(a.lgt + a.lg_stride, i);
-    v.g2 = Q::load(a.lgt + 2 * a.lg_stride, i);
+    v.g0 = Q::load(a.lgt, il);
+    v.g1 = Q::load(a.lgt + a.lg_stride, il);
+    v.g2 = Q::load(a.lgt + 2 * a.lg_stride, il);
     return v;
   };
   // the column (odd = 0: even column of the pair, 1: odd) as a per-row view
@@ -741,7 +789,11 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   const unsigned m = pr.mask;
   const bool tb = m & 1u, bt = m & 2u, lr = m & 4u, rl = m & 8u, hz = lr || rl;
   using K = void (*)(TpArgs<T>);
-  const K k1 = tb ? (hz ? tp_vfwd<T, true, true> : tp_vfwd<T, true, false>) : tp_vfwd<T, false, true>;
+  const bool shared = pr.Cl < pr.C;
+  const K k1 = shared ? (tb ? (hz ? tp_vfwd<T, true, true, false> : tp_vfwd<T, true, false, false>)
+                            : tp_vfwd<T, false, true, false>)
+                      : (tb ? (hz ? tp_vfwd<T, true, true> : tp_vfwd<T, true, false>)
+                            : tp_vfwd<T, false, true>);
   const K k2 = lr ? (rl ? tp_hpair<T, true, true> : tp_hpair<T, true, false>) : tp_hpair<T, false, true>;
   static const K k3s[8] = {tp_vbwd<T, false, false, false>, tp_vbwd<T, true, false, false>,
                            tp_vbwd<T, false, true, false>, tp_vbwd<T, true, true, false>,
@@ -756,6 +808,17 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   hipStream_t streams[kMaxGroups] = {stream, stream, stream, stream};
   hipEvent_t fork = nullptr, join[kMaxGroups] = {};
   hipError_t e = hipSuccess;
+  if (shared && hz) {
+    // the logit copy of each of the B * Cl logit planes, before any K2
+    const int64_t nlp = pr.B * pr.Cl;
+    const int64_t work = nlp * (pr.W / 2) * (L.Hp / 32);
+    const int64_t blocks = (work + 255) / 256;
+    tr->before(stream, "tp_lgcopy", nlp);
+    hipLaunchKernelGGL(tp_lgcopy<T>, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                       dim3(256), 0, stream, a, nlp);
+    tr->after(stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   auto release = [&]() {
     if (fork) (void)hipEventDestroy(fork);
     for (int g = 1; g < ngroups; ++g)
