@@ -157,6 +157,22 @@ def design_bytes(kernel: str, planes: int, w) -> float:
     return per * px
 
 
+def qmin_per_pixel(w, bwd: bool) -> float:
+    """Compulsory HBM bytes per pixel: x, lambda, u (and grad_out) read once,
+    out (or the gradients) written once, plus the logits (and their
+    gradients) at Cl / C of a tensor each when they are shared."""
+    s = 4 if w.dtype == "f32" else 2
+    share = w.cl / w.C
+    return (7 + 6 * share) * s if bwd else (4 + 3 * share) * s
+
+
+def input_sets(w, bwd: bool) -> int:
+    """Input sets the timed loop rotates through: small problems use several
+    so that it does not run out of the 256 MB last-level cache."""
+    set_bytes = int(qmin_per_pixel(w, bwd) * w.pixels)
+    return int(max(1, min(8, -(-1024 ** 3 // set_bytes))))
+
+
 def counter_traffic(plan: str, workload: str, digest: str):
     """HBM bytes per step (the launches of one step) from
     profiles/<plan>__<workload>__pmc.txt, or None when absent or taken on
@@ -288,16 +304,8 @@ def main() -> int:
     else:
         plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
 
-    # inputs resident in HBM; small problems rotate several input sets so the
-    # timed loop does not run out of the 256 MB last-level cache
-    s = 4 if w.dtype == "f32" else 2
-    # compulsory bytes per pixel: x, lambda, u (and grad_out) read, out (or
-    # the gradients) written, plus the logits (and their gradients) at
-    # Cl / C of a tensor each when they are shared
-    share = w.cl / w.C
-    per_px = (7 + 6 * share) * s if bwd else (4 + 3 * share) * s
-    set_bytes = per_px * w.pixels
-    nsets = max(1, min(8, -(-1024 ** 3 // set_bytes)))
+    per_px = qmin_per_pixel(w, bwd)
+    nsets = input_sets(w, bwd)
     sets = []
     for i in range(nsets):
         seed = 1000 + w.index + 17 * i
