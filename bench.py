@@ -305,6 +305,7 @@ def main() -> int:
         plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
 
     per_px = qmin_per_pixel(w, bwd)
+    set_bytes = int(per_px * w.pixels)
     nsets = input_sets(w, bwd)
     sets = []
     for i in range(nsets):
