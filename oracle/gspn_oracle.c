@@ -20,7 +20,8 @@
  *       links, global and local variants, four-direction integration, sigmoid
  *       plus normalisation for every propagation direction.
  *
- * Readings where the pages are silent or ambiguous:
+ * Readings where the pages are silent or ambiguous (R11 concerns only how
+ * the test inputs are drawn and has no part here):
  *  R1 The first line of a scan (and of every local group) has no predecessor:
  *     h = lambda x there (the recurrence starts at i = 1 and G_ii = lambda_i).
  *  R2 The weights of line s, orthogonal index o, come from the logits stored
@@ -34,22 +35,30 @@
  *     horizontal ones), the same three logit tensors for all four directions.
  *     This follows the listed order up-left, up, up-right and the algorithm's
  *     diagonal-up, horizontal, diagonal-down order.
- *  R5 One set of (logits, lambda, u) is shared by all directions and the
- *     direction outputs are summed (u (.) sum_d h_d).
+ *  R5 Unrolling the recurrence multiplies the weight matrices in scan order,
+ *     G_ij = w_i w_{i-1} ... w_{j+1} lambda_j; the loops below apply them one
+ *     line at a time in that order.
  *  R6 Local groups are blocks of G consecutive positions along the scan axis,
  *     fixed in absolute image coordinates ([mG, (m+1)G), the last one may be
  *     partial); the hidden state restarts whenever the scan enters a new
  *     block, in either scan order, on both axes.
- *  R7 sigmoid(+inf) = 1, sigmoid(-inf) = 0. A pixel whose in-range logits
+ *  R7 The group size is an argument; the default of 2 that one passage
+ *     names is not used (it contradicts the g-fold cost stated beside it).
+ *  R8 One set of (logits, lambda, u) is shared by all directions and the
+ *     direction outputs are summed (u (.) sum_d h_d).
+ *  R9 sigmoid(+inf) = 1, sigmoid(-inf) = 0. A pixel whose in-range logits
  *     all give sigmoid 0 has no defined weights (0/0) and yields NaN.
- *  R8 Backward pass (CSDN page, section 反向传播): the gradients are taken
+ *  R10 Everything here is fp64 from exactly decoded fp32 or bf16 inputs.
+ *  R12 Backward pass (CSDN page, section 反向传播): the gradients are taken
  *     with respect to this layer's own inputs -- x, lambda, the three logits
  *     before the sigmoid and the normalisation, and u -- for a scalar loss
  *     whose gradient dL/dy is given. The page's version stops at the gates
  *     G1..G3; here the chain rule continues through the normalisation and
  *     the sigmoid, since the gates are built from the logits inside the
  *     layer.
- *  R9 Channel-shared logits (CSDN page, section 局限性: the speed test sets
+ *  R13 A line that restarts reads nothing from the line before it, so in the
+ *     backward pass it sends no error term back to that line (R1, R6).
+ *  R14 Channel-shared logits (CSDN page, section 局限性: the speed test sets
  *     the feature dimension of the weights to 1): the logits may have Cl
  *     channels, Cl dividing C, and channel c then uses logit channel
  *     c / (C / Cl) of the same batch entry. Cl = C is the unshared layer. A
@@ -112,7 +121,7 @@ typedef struct {
   pthread_mutex_t lock;
 } job_t;
 
-/* R9: the logit plane that plane (b, c) = plane uses */
+/* R14: the logit plane that plane (b, c) = plane uses */
 static int64_t logit_plane(int64_t plane, int64_t C, int64_t Cl) {
   const int64_t b = plane / C, c = plane % C;
   return b * Cl + c / (C / Cl);
@@ -171,7 +180,7 @@ static void* worker(void* arg) {
     if (plane >= j->B * j->C) break;
     double* y = j->out + plane * j->H * j->W;
     for (int64_t i = 0; i < j->H * j->W; ++i) y[i] = 0.0;
-    /* R5: directions in the fixed order T->B, B->T, L->R, R->L, summed */
+    /* R8: directions in the fixed order T->B, B->T, L->R, R->L, summed */
     for (int d = 0; d < 4; ++d)
       if (j->mask & (1u << d)) scan_plane(j, d, plane, y, h_prev, h_cur);
   }
@@ -235,7 +244,7 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
  * gets a gradient; the gradient of a hidden state collects what the later
  * steps of the scan send back; the input gradient goes through the lambda
  * (there: B) factor; the gate gradients combine the error term with the
- * previous hidden state). Reading R8 for the logits.
+ * previous hidden state). Reading R12 for the logits.
  *
  * For one direction, with e_s = dL/dh_s (the "error term"):
  *   e_s[o] = u gy at pixel (s, o)
@@ -286,7 +295,7 @@ static int64_t pixel_offset(const bjob_t* j, int d, int64_t s, int64_t o) {
 
 /* one direction over one plane: adds this direction's share of
  * d(lambda x) into dphi, of du / gy into hsum and of the logit gradients
- * into the output arrays (at the plane's logit plane, R9) */
+ * into the output arrays (at the plane's logit plane, R14) */
 static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
                            double* e_cur, double* e_next, double* dphi, double* hsum) {
   const int64_t H = j->H, W = j->W;
