@@ -21,7 +21,7 @@ weights):
                      section 局限性: the weights' feature dimension set to 1)
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
-generator seeded with 1000 + k (k = 1..5 in the order above) and then cast
+generator seeded with 1000 + k (k = 1..6 in the order above) and then cast
 (round-to-nearest-even) to the storage type. The output gradient of the
 backward pass (make_grad_out) is N(0, 1) from a generator seeded with
 2000 + k, cast the same way.

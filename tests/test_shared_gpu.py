@@ -89,3 +89,35 @@ def test_t2i_shared_full_size_sampled_planes():
         ref = oracle_grads(inp, gy[:, c:c + 1].cpu(), w.dirs, 0)
         ref = {k: ref[k] for k in got}
         assert_grad_parity(got, ref, f"t2i shared plane {c}", names=tuple(got))
+
+
+def test_t2i_shared_logit_grads_full_size_sum_property():
+    """Full-size shared logit gradients of the 2048x1024x320 one-logit-plane
+    workload, which the oracle cannot take at this size (each sums all 320
+    channels). A shared logit's gradient is the sum over the channels that
+    read it, so it must equal the channel sum of the unshared call's logit
+    gradients on logits repeated over the channels -- a call that the other
+    tests check against the oracle. That call runs on the same values widened
+    to fp32 storage (exact), so its per-channel gradients carry no bf16
+    rounding into the sum. The x, lambda and u gradients must equal the
+    unshared bf16 call's bit for bit: sharing changes only where the logits
+    are read from."""
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS
+    w = WORKLOADS["t2i_2048x1024_cl1"]
+    d = make_inputs(w, device=DEV)
+    gy = make_grad_out(w, device=DEV)
+    lg = (d["l0"], d["l1"], d["l2"])
+    shared = g.propagate_backward(d["x"], lg, d["lam"], d["u"], gy, dirs=w.dirs)
+    rep = tuple(t.expand(-1, w.C, -1, -1).contiguous() for t in lg)
+    full = g.propagate_backward(d["x"], rep, d["lam"], d["u"], gy, dirs=w.dirs)
+    torch.cuda.synchronize()
+    for k in ("x", "lam", "u"):
+        assert torch.equal(shared[k], full[k]), f"d{k} differs from the unshared call"
+    del full
+    f32 = {k: v.float() for k, v in d.items() if k not in ("l0", "l1", "l2")}
+    rep = tuple(t.float() for t in rep)
+    full = g.propagate_backward(f32["x"], rep, f32["lam"], f32["u"], gy.float(), dirs=w.dirs)
+    torch.cuda.synchronize()
+    for k in ("l0", "l1", "l2"):
+        ref = full[k].sum(dim=1, keepdim=True).double().cpu().numpy()
+        assert_parity(shared[k], ref, f"shared d{k} vs channel sum")
