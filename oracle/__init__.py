@@ -65,6 +65,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         b2.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
                        ctypes.c_uint32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         b2.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_propagate_dirs"):
+        f3 = lib.gspn_oracle_propagate_dirs
+        f3.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp,
+                       ctypes.c_uint32, i64, vp, ctypes.c_int]
+        f3.restype = ctypes.c_int
     if hasattr(lib, "gspn_oracle_backward"):
         b = lib.gspn_oracle_backward
         b.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
@@ -127,6 +132,49 @@ def propagate(x, l0, l1, l2, lam, u, dirs: int = 15, group_rows: int = 0,
     rc = L.gspn_oracle_propagate_shared(*[a.ctypes.data for a in arrs], dt, B, C, H, W, cl,
                                         int(dirs), int(group_rows), out.ctypes.data,
                                         int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def propagate_dirs(x, l0, l1, l2, lam, u, merge=None, dirs: int = 15, group_rows: int = 0,
+                   nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Per-direction parameters with a per-channel merger, as float64
+    [B, C, H, W]: y = sum over d in ``dirs`` of merge[d, c] * u[d] * h_d, where
+    h_d is direction d's scan of x with lam[d] and logits l0[d], l1[d], l2[d].
+
+    ``x`` is [B, C, H, W]; ``l0, l1, l2, lam, u`` are [4, B, C, H, W] (one slice
+    per direction: top->bottom, bottom->top, left->right, right->left), all of
+    one dtype as in ``propagate``. ``merge`` is [4, C] (converted to float64)
+    or None for all ones.
+    """
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    shape = x.shape
+    dshape = (4,) + tuple(shape)
+    arrs, dts = [], set()
+    for a, shp in [(x, shape)] + [(t, dshape) for t in (l0, l1, l2, lam, u)]:
+        a2, dt = _as_input(np.asarray(a), shp)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    dt = dts.pop()
+    B, C, H, W = shape
+    m = None
+    if merge is not None:
+        m = np.ascontiguousarray(merge, dtype=np.float64)
+        if m.shape != (4, C):
+            raise ValueError(f"merge must be [4, {C}]")
+    out = np.empty(shape, dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    L = lib if lib is not None else load()
+    rc = L.gspn_oracle_propagate_dirs(*[a.ctypes.data for a in arrs], dt, B, C, H, W,
+                                      B * C * H * W, None if m is None else m.ctypes.data,
+                                      int(dirs), int(group_rows), out.ctypes.data,
+                                      int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out

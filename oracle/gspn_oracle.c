@@ -63,6 +63,14 @@
  *     channels, Cl dividing C, and channel c then uses logit channel
  *     c / (C / Cl) of the same batch entry. Cl = C is the unshared layer. A
  *     shared logit's gradient is the sum over the channels that use it.
+ *  R15 Per-direction parameters and the learnable merger (aitntnews page,
+ *     sections 二维线性传播 and GSPN架构; CSDN page, section GSPN模块的设计:
+ *     every direction has its own normalised weight matrices, and a linear
+ *     layer merges the directions): direction d reads its own lambda, logits
+ *     and u, stored dir_stride elements after direction d-1's (x is shared),
+ *     and the directions are merged by per-channel weights m[d][c],
+ *     y = sum_d m[d][c] u_d (.) h_d. A merger that mixes channels as well
+ *     would be a dense matrix product and is not part of this layer.
  */
 #include "gspn_oracle.h"
 
@@ -115,6 +123,8 @@ typedef struct {
   const void *x, *l[3], *lam, *u;
   int dt;
   int64_t B, C, H, W, G, Cl;
+  int64_t dstride;      /* R15: elements between two directions' parameters */
+  const double* merge;  /* R15: [4][C] merge weights, or NULL for all ones */
   uint32_t mask;
   double* out;
   int64_t next_plane;   /* shared work counter */
@@ -132,8 +142,10 @@ static void scan_plane(const job_t* j, int d, int64_t plane, double* y,
                        double* h_prev, double* h_cur) {
   const int64_t H = j->H, W = j->W;
   const int64_t n_s = scan_len(d, H, W), n_o = orth_len(d, H, W);
+  const int64_t doff = d * j->dstride;   /* R15: this direction's parameters */
   const int64_t base = plane * H * W;
-  const int64_t lbase = logit_plane(plane, j->C, j->Cl) * H * W;
+  const int64_t lbase = logit_plane(plane, j->C, j->Cl) * H * W + doff;
+  const double m = j->merge ? j->merge[d * j->C + plane % j->C] : 1.0;
   for (int64_t o = 0; o < n_o; ++o) h_prev[o] = 0.0;
 
   for (int64_t s = 0; s < n_s; ++s) {
@@ -159,9 +171,9 @@ static void scan_plane(const job_t* j, int d, int64_t plane, double* y,
           acc += (sig[k] / S) * h_prev[q];
         }
       }
-      h_cur[o] = acc + load_value(j->lam, j->dt, idx) *
+      h_cur[o] = acc + load_value(j->lam, j->dt, idx + doff) *
                            load_value(j->x, j->dt, idx);
-      y[r * W + c] += load_value(j->u, j->dt, idx) * h_cur[o];
+      y[r * W + c] += m * load_value(j->u, j->dt, idx + doff) * h_cur[o];
     }
     double* t = h_prev; h_prev = h_cur; h_cur = t;
   }
@@ -189,6 +201,30 @@ static void* worker(void* arg) {
   return NULL;
 }
 
+/* the forward pass over all planes, on nthreads workers */
+static int run_forward(job_t* j, int nthreads) {
+  j->next_plane = 0;
+  pthread_mutex_init(&j->lock, NULL);
+  int nt = nthreads <= 0 ? 1 : nthreads;
+  if ((int64_t)nt > j->B * j->C) nt = (int)(j->B * j->C);
+  int rc = 0;
+  if (nt == 1) {
+    if (worker(j) != NULL) rc = -1;
+  } else {
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    if (!th) { pthread_mutex_destroy(&j->lock); return -1; }
+    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, worker, j);
+    for (int t = 0; t < nt; ++t) {
+      void* ret = NULL;
+      pthread_join(th[t], &ret);
+      if (ret != NULL) rc = -1;
+    }
+    free(th);
+  }
+  pthread_mutex_destroy(&j->lock);
+  return rc;
+}
+
 int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
                                  const void* l2, const void* lam, const void* u,
                                  int in_dtype, int64_t B, int64_t C, int64_t H,
@@ -206,28 +242,31 @@ int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
   job_t j;
   j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u;
   j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
-  j.Cl = logit_channels;
-  j.mask = dir_mask; j.out = out; j.next_plane = 0;
-  pthread_mutex_init(&j.lock, NULL);
+  j.Cl = logit_channels; j.dstride = 0; j.merge = NULL;
+  j.mask = dir_mask; j.out = out;
+  return run_forward(&j, nthreads);
+}
 
-  int nt = nthreads <= 0 ? 1 : nthreads;
-  if ((int64_t)nt > B * C) nt = (int)(B * C);
-  int rc = 0;
-  if (nt == 1) {
-    if (worker(&j) != NULL) rc = -1;
-  } else {
-    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
-    if (!th) { pthread_mutex_destroy(&j.lock); return -1; }
-    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, worker, &j);
-    for (int t = 0; t < nt; ++t) {
-      void* ret = NULL;
-      pthread_join(th[t], &ret);
-      if (ret != NULL) rc = -1;
-    }
-    free(th);
-  }
-  pthread_mutex_destroy(&j.lock);
-  return rc;
+int gspn_oracle_propagate_dirs(const void* x, const void* l0, const void* l1,
+                               const void* l2, const void* lam, const void* u,
+                               int in_dtype, int64_t B, int64_t C, int64_t H,
+                               int64_t W, int64_t dir_stride, const double* merge,
+                               uint32_t dir_mask, int64_t group_rows, double* out,
+                               int nthreads) {
+  if (!x || !l0 || !l1 || !l2 || !lam || !u || !out) return -1;
+  if (B < 0 || C < 0 || H <= 0 || W <= 0) return -1;
+  if (dir_mask == 0 || dir_mask > 15) return -1;
+  if (group_rows < 0 || dir_stride < 0) return -1;
+  if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16)
+    return -1;
+  if (B * C == 0) return 0;
+
+  job_t j;
+  j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u;
+  j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
+  j.Cl = C; j.dstride = dir_stride; j.merge = merge;
+  j.mask = dir_mask; j.out = out;
+  return run_forward(&j, nthreads);
 }
 
 int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,

@@ -78,6 +78,22 @@ int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
                                  int in_dtype, int64_t B, int64_t C, int64_t H,
                                  int64_t W, int64_t logit_channels, uint32_t dir_mask,
                                  int64_t group_rows, double* out, int nthreads);
+
+/*
+ * Per-direction parameters and a per-channel merger (aitntnews page, sections
+ * 二维线性传播 and GSPN架构; CSDN page, section GSPN模块的设计): direction d
+ * (0 top->bottom, 1 bottom->top, 2 left->right, 3 right->left) reads lam, l0,
+ * l1, l2 and u at element offset d * dir_stride (x is shared), and
+ *   y = sum over d in dir_mask of merge[d * C + c] * u_d (.) h_d.
+ * merge: host array of 4 * C doubles, or NULL for all ones. dir_stride = 0
+ * with merge = NULL is gspn_oracle_propagate. Returns -1 on a bad argument.
+ */
+int gspn_oracle_propagate_dirs(const void* x, const void* l0, const void* l1,
+                               const void* l2, const void* lam, const void* u,
+                               int in_dtype, int64_t B, int64_t C, int64_t H,
+                               int64_t W, int64_t dir_stride, const double* merge,
+                               uint32_t dir_mask, int64_t group_rows, double* out,
+                               int nthreads);
 int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
                                 const void* l2, const void* lam, const void* u,
                                 const void* gy, int in_dtype, int64_t B, int64_t C,

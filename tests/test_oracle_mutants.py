@@ -19,13 +19,13 @@ MUTANTS = [
     ("neighbour_index_reversed", "const int64_t q = o + k - 1;", "const int64_t q = o - k + 1;", 0),
     ("no_local_restart", "return (p / G) != (prev / G);", "return 0;", 1),
     ("groups_relative_to_scan_start", "return (p / G) != (prev / G);", "return (s % G) == 0;", 1),
-    ("lambda_dropped", "load_value(j->lam, j->dt, idx) *", "", 1),
+    ("lambda_dropped", "load_value(j->lam, j->dt, idx + doff) *", "", 1),
     ("reverse_directions_swapped", "(d == 0 || d == 2) ? s : n_s - 1 - s",
      "(d == 0 || d == 3) ? s : n_s - 1 - s", 1),
     ("directions_overwrite", "y[r * W + c] +=", "y[r * W + c] =", 1),
     ("unnormalised_sigmoid", "acc += (sig[k] / S) * h_prev[q];", "acc += sig[k] * h_prev[q];", 1),
-    ("gate_missing", "y[r * W + c] += load_value(j->u, j->dt, idx) * h_cur[o];",
-     "y[r * W + c] += h_cur[o];", 1),
+    ("gate_missing", "y[r * W + c] += m * load_value(j->u, j->dt, idx + doff) * h_cur[o];",
+     "y[r * W + c] += m * h_cur[o];", 1),
     ("sigmoid_sign_flipped", "return 1.0 / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(v));", 1),
 ]
 
