@@ -18,7 +18,9 @@ JSON line:
             workload on this host's cores (rank 0, N = 1 only)
 With --backward a step is one backward pass instead (gradients of x, lambda,
 the three logits and u for a seeded dL/dout), with Q_min = 13 s per pixel
-(seven tensors read, six written).
+(seven tensors read, six written). Per-direction workloads (own lambda,
+logits and u per direction, per-channel merge weights) have
+Q_min = (2 + 5 * dirs) s per pixel: x, each direction's five tensors, out.
 """
 from __future__ import annotations
 
@@ -53,6 +55,7 @@ PLAN_SOURCES = {
     "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
+    "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
 }
 
 
@@ -98,9 +101,11 @@ class Hip:
             self.L.hipEventDestroy(e)
 
 
-def design_bytes(kernel: str, planes: int, w) -> float:
+def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = True) -> float:
     """HBM bytes one launch of `kernel` over `planes` planes moves by design
-    (every tensor it touches read or written once).
+    (every tensor it touches read or written once). `first` / `last`: the
+    launch's place among the direction passes of one call (per-direction
+    kernels only).
 
     Per pixel, with s = bytes per stored element:
       plane_kernel16/64 (all directions on chip): x, lambda, l0, l1, l2, u
@@ -131,6 +136,15 @@ def design_bytes(kernel: str, planes: int, w) -> float:
       bband_kernel (local groups): seven inputs read in the vertical and again
           in the horizontal rounds, five fp32 partial sums written and read
           back, six gradients written -> 20 s + 40
+    Per-direction parameters (one pass per direction; horizontal directions
+    run over transposed copies):
+      dir_vert  x and the direction's lambda, l0, l1, l2, u read (6 s), the
+          fp32 accumulator read unless first (4), then the accumulator
+          written (4) or, by the last pass, out (s)
+      dir_tr_in  one tensor read and written transposed (2 s), counted per
+          plane and tensor
+      dir_tr_acc  the fp32 sum of the horizontal passes read (4) and written
+          back row-major (4), or as out (s) when no vertical direction follows
     """
     s = 4 if w.dtype == "f32" else 2
     px = planes * w.H * w.W
@@ -153,6 +167,9 @@ def design_bytes(kernel: str, planes: int, w) -> float:
         "bwd_finish": 20 + 9 * s,
         "bband_kernel": 20 * s + 40,
         "bwd_reduce_logits": 12 + 3 * s * w.cl / w.C,
+        "dir_vert": 6 * s + (0 if first else 4) + (s if last else 4),
+        "dir_tr_in": 2 * s,
+        "dir_tr_acc": 4 + (4 if w.dirs & 3 else s),
     }[kernel]
     return per * px
 
@@ -160,8 +177,14 @@ def design_bytes(kernel: str, planes: int, w) -> float:
 def qmin_per_pixel(w, bwd: bool) -> float:
     """Compulsory HBM bytes per pixel: x, lambda, u (and grad_out) read once,
     out (or the gradients) written once, plus the logits (and their
-    gradients) at Cl / C of a tensor each when they are shared."""
+    gradients) at Cl / C of a tensor each when they are shared. Per-direction
+    parameters (forward only): x, each selected direction's lambda, l0, l1,
+    l2 and u read once, out written once."""
     s = 4 if w.dtype == "f32" else 2
+    if w.per_direction:
+        if bwd:
+            raise ValueError("no backward pass for per-direction parameters")
+        return (2 + 5 * w.ndirs) * s
     share = w.cl / w.C
     return (7 + 6 * share) * s if bwd else (4 + 3 * share) * s
 
@@ -224,9 +247,31 @@ def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
             return t.view(torch.int16).numpy().view(np.uint16).reshape(1, nlp, w.H, w.W)
         return t.numpy().reshape(1, nlp, w.H, w.W)
 
+    def host_dirs(t):
+        # [4, B, C, H, W]: the first `planes` planes of every direction
+        t = t.reshape(4, -1, w.H, w.W)[:, :planes].cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16).numpy().view(np.uint16)
+        else:
+            t = t.numpy()
+        return t.reshape(4, 1, planes, w.H, w.W)
+
+    threads = min(cores, planes)
+    if w.per_direction:
+        # sample plane p is channel p % C of the merge weights
+        merge = inp_dev["merge"].cpu().numpy()[:, np.arange(planes) % w.C]
+        args = [host(inp_dev["x"])] + [host_dirs(inp_dev[k]) for k in ("l0", "l1", "l2",
+                                                                         "lam", "u")]
+        t0 = time.perf_counter()
+        oracle.propagate_dirs(*args, merge=merge, dirs=w.dirs, group_rows=w.group_rows,
+                              nthreads=threads)
+        dt = time.perf_counter() - t0
+        steps = planes * w.H * w.W * w.ndirs
+        return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
+                "sample": f"per-direction, first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, "
+                          f"{w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}
     arrs = [host(inp_dev["x"])] + [host_logits(inp_dev[k]) for k in ("l0", "l1", "l2")] + \
         [host(inp_dev[k]) for k in ("lam", "u")]
-    threads = min(cores, planes)
     t0 = time.perf_counter()
     if grad_out is None:
         oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
@@ -297,10 +342,15 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     bwd = args.backward
+    if bwd and w.per_direction:
+        print("no backward pass for per-direction parameters", file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     dt_code = g.GSPN_F32 if w.dtype == "f32" else g.GSPN_BF16
     if bwd:
         plan = g.backward_plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+    elif w.per_direction:
+        plan = "dirs"
     else:
         plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
 
@@ -326,7 +376,8 @@ def main() -> int:
                                               logit_channels=w.cl)
     else:
         outs = [torch.empty_like(st["x"]) for st in sets]
-        ws_bytes = g.workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
+        wsb = g.workspace_bytes_dirs if w.per_direction else g.workspace_bytes
+        ws_bytes = wsb(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -337,6 +388,11 @@ def main() -> int:
                                  st["gy"], dirs=w.dirs, group_rows=w.group_rows,
                                  grads=outs[i % nsets], workspace=ws if ws_bytes else None,
                                  stream=stream)
+        elif w.per_direction:
+            g.propagate_dirs(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
+                             merge=st["merge"], dirs=w.dirs, group_rows=w.group_rows,
+                             out=outs[i % nsets], workspace=ws if ws_bytes else None,
+                             stream=stream)
         else:
             g.propagate(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
                         dirs=w.dirs, group_rows=w.group_rows, out=outs[i % nsets],
@@ -383,15 +439,18 @@ def main() -> int:
     # per kernel: summed launch time and design bytes (launches of one kernel
     # may run on two streams; each is timed on its own stream)
     kt, kb = {}, {}
-    for (name, np_), t in zip(launches, per_launch):
+    passes = [i for i, (name, _) in enumerate(launches) if name == "dir_vert"]
+    for i, ((name, np_), t) in enumerate(zip(launches, per_launch)):
         kt[name] = kt.get(name, 0.0) + t
-        kb[name] = kb.get(name, 0.0) + design_bytes(name, np_, w)
+        first, last = (i == passes[0], i == passes[-1]) if i in passes else (True, True)
+        kb[name] = kb.get(name, 0.0) + design_bytes(name, np_, w, first=first, last=last)
     path_bytes = sum(kb.values())
     # Roofline unit: the launches of one step. A single launch is timed by its
     # own events; a pipeline of several launches (overlapping on two streams)
     # by the step time. Algorithmic bytes: the compulsory Q_min = 7 s per
     # pixel (five inputs and u read once, out written once), 13 s for the
-    # backward pass (seven tensors read, six gradients written).
+    # backward pass (seven tensors read, six gradients written), (2 + 5 dirs) s
+    # with per-direction parameters.
     q_min = int(per_px * w.pixels)
     if nl == 1:
         unit_name, unit_ms = launches[0][0], per_launch[0]
@@ -417,7 +476,7 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
                    "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
-                   "logit_channels": w.cl,
+                   "logit_channels": w.cl, "per_direction": w.per_direction,
                    "plan": plan, "launches_per_step": counts[0],
                    "launches": [f"{n}[{p}]" for n, p in launches],
                    "launch_ms": [round(t, 4) for t in per_launch],

@@ -247,6 +247,44 @@ size_t gspn_backward_workspace_bytes_shared(int64_t B, int64_t C, int64_t H, int
                                             int64_t logit_channels, uint32_t dir_mask,
                                             int64_t group_rows, gspn_dtype dtype);
 
+/*
+ * Per-direction parameters with a per-channel merger (aitntnews page, sections
+ * 二维线性传播 and GSPN架构: every scan direction has its own normalised
+ * weight matrices, and a learnable merger combines the directions; CSDN page,
+ * section GSPN模块的设计: the merger is a linear layer over the directions).
+ *
+ *   out[b,c] = sum over d in dir_mask of merge[d * C + c] * u_d (.) h_d,
+ *   h_d = direction d's line scan of x with lambda_d and logits l_{d,0..2}.
+ *
+ * Direction d (0 top->bottom, 1 bottom->top, 2 left->right, 3 right->left)
+ * reads lambda, w_logits[0..2] and u at element offset d * dir_stride from the
+ * given pointers, each a contiguous [B, C, H, W] tensor; x is shared by all
+ * directions. dir_stride = 0 gives every direction the same parameters, and
+ * with merge = NULL that is gspn_propagate_ws's result. A dir_stride between
+ * 1 and B*C*H*W - 1 (overlapping directions) gives GSPN_E_SHAPE.
+ *
+ * merge: device memory, 4 * C fp32 values, direction-major, caller-owned, or
+ * NULL for all ones; only the selected directions' rows are read.
+ * H and W must be <= 8192 (GSPN_E_SHAPE). out may overlap no byte that the
+ * call reads (GSPN_E_ALIAS). The sum over directions is taken in fp32 in the
+ * fixed order left->right, right->left, top->bottom, bottom->top and rounded
+ * once to the storage type.
+ *
+ * Workspace: gspn_workspace_bytes_dirs() bytes, 256-byte aligned, caller-owned:
+ * fp32 partial sums, and with a horizontal direction selected, transposed
+ * copies of x and of each selected horizontal direction's five tensors. It is
+ * 0 for a single vertical direction (workspace may then be NULL). Same status
+ * codes as gspn_propagate_ws.
+ */
+gspn_status gspn_propagate_dirs_ws(const void* x, const void* const w_logits[3],
+                                   const void* lambda, const void* u, int64_t dir_stride,
+                                   const float* merge, int64_t B, int64_t C, int64_t H,
+                                   int64_t W, uint32_t dir_mask, int64_t group_rows,
+                                   gspn_dtype dtype, void* out, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream);
+size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
+                                 uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype);
+
 /* gspn_backward_plan_name -- kernel plan gspn_propagate_backward would use,
  * or "invalid". Host-only. */
 const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,

@@ -94,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.gspn_backward_workspace_bytes_shared.argtypes = [i64, i64, i64, i64, i64, u32, i64,
                                                            ctypes.c_int]
         L.gspn_backward_workspace_bytes_shared.restype = ctypes.c_size_t
+        L.gspn_propagate_dirs_ws.argtypes = [vp, logits_t, vp, vp, i64, vp, i64, i64, i64, i64,
+                                             u32, i64, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_dirs_ws.restype = ctypes.c_int
+        L.gspn_workspace_bytes_dirs.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_workspace_bytes_dirs.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -168,6 +173,57 @@ def propagate(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
     _check(L.gspn_propagate_shared_ws(x.data_ptr(), lg, cl, lam.data_ptr(), u.data_ptr(), B, C,
                                       H, W, dirs, group_rows, dt, out.data_ptr(), ws_ptr, ws_len,
                                       sptr))
+    return out
+
+
+def workspace_bytes_dirs(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
+    return int(lib().gspn_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dtype))
+
+
+def propagate_dirs(x, logits, lam, u, merge=None, dirs: int = ALL, group_rows: int = 0,
+                   out=None, workspace=None, stream=None):
+    """Per-direction parameters with a per-channel merger:
+    out = sum_{d in dirs} merge[d, c] * u[d] * h_d, where h_d scans x with
+    lam[d] and the logits' slice d. ``x`` is a contiguous [B, C, H, W] device
+    tensor; ``logits`` = (l0, l1, l2), ``lam`` and ``u`` are contiguous
+    [4, B, C, H, W] tensors of x's dtype, slice d for direction d (top->bottom,
+    bottom->top, left->right, right->left); ``merge`` is a contiguous float32
+    [4, C] device tensor, or None for all ones."""
+    import torch
+    l0, l1, l2 = logits
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    for t in (x, l0, l1, l2, lam, u):
+        if not isinstance(t, torch.Tensor) or t.device != x.device or t.device.type != "cuda":
+            raise TypeError("all inputs must be torch tensors on x's GPU device")
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous tensors of one dtype")
+    for t in (l0, l1, l2, lam, u):
+        if tuple(t.shape) != (4, B, C, H, W):
+            raise ValueError("per-direction tensors must be [4, B, C, H, W]")
+    mptr = None
+    if merge is not None:
+        if (merge.dtype != torch.float32 or merge.device != x.device or not merge.is_contiguous()
+                or tuple(merge.shape) != (4, C)):
+            raise ValueError("merge must be a contiguous float32 [4, C] tensor on x's device")
+        mptr = merge.data_ptr()
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    L = lib()
+    need = int(L.gspn_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dt))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.gspn_propagate_dirs_ws(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(),
+                                    B * C * H * W, mptr, B, C, H, W, dirs, group_rows, dt,
+                                    out.data_ptr(), ws_ptr, ws_len, sptr))
     return out
 
 

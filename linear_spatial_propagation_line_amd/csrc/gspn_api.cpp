@@ -26,7 +26,7 @@ gspn_status fail(gspn_status s, const std::string& detail) {
 
 size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
 
-enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream };
+enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream, kDirs };
 
 struct Checked {
   gspn_status status;
@@ -182,6 +182,9 @@ gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream
     case Plan::kStream:
       e = gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
       break;
+    case Plan::kDirs:
+      e = gspn::launch_dirs(pr, ws, stream, &tr);
+      break;
     default:
       return fail(GSPN_E_SHAPE, "no plan");
   }
@@ -203,8 +206,35 @@ const char* plan_str(Plan p) {
     case Plan::kBand: return "band";
     case Plan::kTpipe: return "tpipe";
     case Plan::kStream: return "stream";
+    case Plan::kDirs: return "dirs";
     default: return "invalid";
   }
+}
+
+// ---- per-direction parameters -----------------------------------------------
+// Shape limits of the per-direction path and its workspace (an fp32
+// accumulator, and transposed copies for the horizontal directions).
+Checked check_dirs_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
+                         int dtype, int64_t dir_stride) {
+  Checked r = check_shape(B, C, H, W, mask, G, dtype);
+  if (r.status != GSPN_OK) return r;
+  r.plan = Plan::kDirs;
+  r.ws_bytes = 0;
+  if (H > gspn::dirs_max_orth() || W > gspn::dirs_max_orth()) {
+    r.status = fail(GSPN_E_SHAPE, "per-direction parameters: H and W must be <= 8192");
+    return r;
+  }
+  const int64_t P = B * C * H * W;
+  if (dir_stride < 0 || (dir_stride > 0 && dir_stride < P)) {
+    r.status = fail(GSPN_E_SHAPE, "dir_stride must be 0 or at least B * C * H * W");
+    return r;
+  }
+  if (dir_stride > (INT64_MAX / 8 - P) / 3) {
+    r.status = fail(GSPN_E_SHAPE, "dir_stride too large");
+    return r;
+  }
+  r.ws_bytes = gspn::dirs_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
+  return r;
 }
 
 // ---- backward pass ---------------------------------------------------------
@@ -599,6 +629,87 @@ gspn_status gspn_propagate_shared_ws(const void* x, const void* const w_logits[3
         return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
   }
   if (B * C == 0) return GSPN_OK;
+  return run(pr, chk.plan, workspace, stream);
+}
+
+size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                                 int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  Checked chk = check_dirs_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype), 0);
+  g_last_error = keep;
+  return chk.status == GSPN_OK ? chk.ws_bytes : 0;
+}
+
+gspn_status gspn_propagate_dirs_ws(const void* x, const void* const w_logits[3],
+                                   const void* lambda, const void* u, int64_t dir_stride,
+                                   const float* merge, int64_t B, int64_t C, int64_t H,
+                                   int64_t W, uint32_t dir_mask, int64_t group_rows,
+                                   gspn_dtype dtype, void* out, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!x || !w_logits || !lambda || !u || !out)
+    return fail(GSPN_E_NULL, "x, w_logits, lambda, u and out must be non-null");
+  if (!w_logits[0] || !w_logits[1] || !w_logits[2])
+    return fail(GSPN_E_NULL, "w_logits[0..2] must be non-null");
+  const Checked chk = check_dirs_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype),
+                                       dir_stride);
+  if (chk.status != GSPN_OK) return chk.status;
+  const size_t es = elem_size(dtype);
+  const void* ins[6] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u};
+  for (const void* p : ins)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
+  if (reinterpret_cast<uintptr_t>(out) % es)
+    return fail(GSPN_E_ALIGN, "out not aligned to its element size");
+  if (reinterpret_cast<uintptr_t>(merge) % sizeof(float))
+    return fail(GSPN_E_ALIGN, "merge not aligned to 4 bytes");
+  // every byte range the call reads: x, each selected direction's five
+  // tensors, the merge weights
+  const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+  const size_t mbytes = merge ? static_cast<size_t>(4 * C) * sizeof(float) : 0;
+  const void* rd[22];
+  size_t rn[22];
+  int nr = 0;
+  rd[nr] = x; rn[nr++] = bytes;
+  if (merge) { rd[nr] = merge; rn[nr++] = mbytes; }
+  for (int d = 0; d < 4; ++d) {
+    if (!((dir_mask >> d) & 1u)) continue;
+    const size_t off = static_cast<size_t>(d * dir_stride) * es;
+    for (int k = 1; k < 6; ++k) {
+      rd[nr] = static_cast<const char*>(ins[k]) + off;
+      rn[nr++] = bytes;
+    }
+  }
+  for (int i = 0; i < nr; ++i)
+    if (overlaps(out, bytes, rd[i], rn[i])) return fail(GSPN_E_ALIAS, "out overlaps an input");
+  if (chk.ws_bytes > 0) {
+    if (!workspace || ws_bytes < chk.ws_bytes)
+      return fail(GSPN_E_WORKSPACE,
+                  "workspace missing or smaller than gspn_workspace_bytes_dirs()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    if (overlaps(workspace, chk.ws_bytes, out, bytes))
+      return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+    for (int i = 0; i < nr; ++i)
+      if (overlaps(workspace, chk.ws_bytes, rd[i], rn[i]))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  if (B * C == 0) return GSPN_OK;
+  gspn::Problem pr;
+  pr.x = x;
+  for (int k = 0; k < 3; ++k) pr.l[k] = w_logits[k];
+  pr.lam = lambda;
+  pr.u = u;
+  pr.out = out;
+  pr.B = B; pr.C = C; pr.H = H; pr.W = W;
+  pr.mask = dir_mask;
+  pr.G = group_rows;
+  pr.dtype = dtype;
+  pr.aligned_vec4 = false;   // the per-direction kernels check alignment per pass
+  pr.aligned_pair = false;
+  pr.Cl = C;
+  pr.dir_stride = dir_stride;
+  pr.merge = merge;
   return run(pr, chk.plan, workspace, stream);
 }
 

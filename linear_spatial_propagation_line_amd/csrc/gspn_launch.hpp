@@ -23,6 +23,10 @@ struct Problem {
   bool aligned_vec4;   // every pointer aligned to 4 elements
   bool aligned_pair;   // every pointer aligned to 2 elements
   int64_t Cl;          // logit channels (Cl divides C; Cl == C: unshared)
+  // per-direction parameters: direction d reads lambda, logits and u at
+  // element offset d * dir_stride, merged with merge[d * C + c] (null: 1)
+  int64_t dir_stride = 0;
+  const float* merge = nullptr;
 };
 
 // A validated backward problem: the forward inputs, grad_out (gy) and the six
@@ -85,6 +89,11 @@ hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer*
 // streaming per-direction path (gspn_stream.hip)
 int64_t stream_max_orth();
 hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Tracer* tr);
+
+// per-direction parameters with a per-channel merger (gspn_dirs.hip)
+int64_t dirs_max_orth();
+size_t dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask, gspn_dtype dt);
+hipError_t launch_dirs(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
 // backward pass, plane-resident path for H, W <= 64 (gspn_bwd_plane.hip)
 size_t bplane_lds_bytes(int64_t H, int64_t W);

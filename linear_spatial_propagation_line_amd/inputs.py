@@ -19,10 +19,16 @@ weights):
   t2i_2048x1024_cl1  the same with one logit channel shared by all 320
                      channels (the speed-test setting of the CSDN page,
                      section 局限性: the weights' feature dimension set to 1)
+  cls_56x56_pd       cls_56x56 with one set of (lambda, logits, u) per scan
+  t2i_2048x1024_pd   direction and per-channel merge weights (aitntnews page,
+                     sections 二维线性传播 and GSPN架构; CSDN page, section
+                     GSPN模块的设计)
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
-generator seeded with 1000 + k (k = 1..6 in the order above) and then cast
-(round-to-nearest-even) to the storage type. The output gradient of the
+generator seeded with 1000 + k (k = 1..8 in the order above) and then cast
+(round-to-nearest-even) to the storage type. Per-direction workloads draw
+lambda, u and the logits as [4, B, C, H, W] (slice d for direction d) in the
+same order, then merge weights [4, C] from U(-1, 1), kept in float32. The output gradient of the
 backward pass (make_grad_out) is N(0, 1) from a generator seeded with
 2000 + k, cast the same way.
 """
@@ -52,6 +58,7 @@ class Workload:
     lam: tuple
     u: tuple
     logit_channels: int = 0   # 0: one logit channel per channel (unshared)
+    per_direction: bool = False   # own (lambda, logits, u) per direction + merge weights
 
     @property
     def cl(self) -> int:
@@ -95,6 +102,10 @@ WORKLOADS = {
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
         Workload("t2i_2048x1024_cl1", 6, 1, 320, 2048, 1024, BF16, 15, 0,
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, logit_channels=1),
+        Workload("cls_56x56_pd", 7, 64, 96, 56, 56, F32, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, per_direction=True),
+        Workload("t2i_2048x1024_pd", 8, 1, 320, 2048, 1024, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, per_direction=True),
     ]
 }
 
@@ -117,8 +128,9 @@ def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
                 W: int | None = None) -> dict:
     """Tensors x, lam, u of shape [B, C, H, W] and l0, l1, l2 of shape
     [B, Cl, H, W] (Cl = C unless the workload shares logits) in the
-    workload's storage dtype on ``device``. Shape overrides keep the
-    distributions."""
+    workload's storage dtype on ``device``. Per-direction workloads give
+    lam, u, l0, l1, l2 of shape [4, B, C, H, W] and merge weights "merge"
+    [4, C] in float32. Shape overrides keep the distributions."""
     if isinstance(w, str):
         w = WORKLOADS[w]
     shape = (B or w.B, C or w.C, H or w.H, W or w.W)
@@ -131,7 +143,11 @@ def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
     for name, spec in (("x", w.x), ("lam", w.lam), ("u", w.u),
                        ("l0", w.logits), ("l1", w.logits), ("l2", w.logits)):
         shp = lshape if name in ("l0", "l1", "l2") else shape
+        if w.per_direction and name != "x":
+            shp = (4,) + tuple(shp)
         out[name] = _draw(spec, shp, gen, device).to(w.torch_dtype)
+    if w.per_direction:
+        out["merge"] = _draw(("uniform", -1.0, 1.0), (4, shape[1]), gen, device)
     return out
 
 

@@ -233,12 +233,86 @@ def test_shared_workspace(LB):
 
 
 def test_shared_aliasing_uses_logit_size(LB):
-    # out placed right after one shared logit plane: no overlap with Cl = 1
+    # out placed right after one shared logit plane: no overlap with Cl = 1.
+    # The shape needs a workspace and none is given, so the call that passes
+    # the aliasing check stops at the workspace check and launches nothing.
     lg = (ctypes.c_void_p * 3)(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ)
-    out = BASE + SZ + 8 * 8 * 4          # one 8x8 fp32 logit plane after l0
-    st = LB.gspn_propagate_shared_ws(BASE, lg, 1, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 8, 8, 15,
-                                     0, 0, out, None, 0, None)
-    assert st != g.STATUS["GSPN_E_ALIAS"]
-    st = LB.gspn_propagate_shared_ws(BASE, lg, 4, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 8, 8, 15,
-                                     0, 0, out, None, 0, None)
+    out = BASE + SZ + 100 * 100 * 4      # one 100x100 fp32 logit plane after l0
+    st = LB.gspn_propagate_shared_ws(BASE, lg, 1, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 100, 100,
+                                     15, 0, 0, out, None, 0, None)
+    assert st == g.STATUS["GSPN_E_WORKSPACE"]
+    st = LB.gspn_propagate_shared_ws(BASE, lg, 4, BASE + 4 * SZ, BASE + 5 * SZ, 1, 4, 100, 100,
+                                     15, 0, 0, out, None, 0, None)
     assert st == g.STATUS["GSPN_E_ALIAS"]
+
+
+# ---- per-direction parameters (gspn_propagate_dirs_ws) ----------------------
+# Every call below either fails validation or needs a workspace that it does
+# not get, so none reaches a launch.
+DP = 2 * 3 * 20 * 16          # elements of one [2, 3, 20, 16] tensor
+
+
+def dcall(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
+          u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, B=2, C=3, H=20, W=16, mask=15, G=0,
+          dt=0, out=BASE + 6 * SZ, ws=None, ws_bytes=0):
+    arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
+    return L.gspn_propagate_dirs_ws(x, arr, lam, u, stride, merge, B, C, H, W, mask, G, dt, out,
+                                    ws, ws_bytes, None)
+
+
+def test_dirs_workspace_bytes(L):
+    # fp32 sums (transposed, row-major) and transposed x plus five tensors per
+    # horizontal direction; DP * 4 and DP * 2 are multiples of 256 here
+    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * (2 + 11)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.L2R | g.R2L, 0, 1) == DP * (4 + 2 * 11)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.R2L, 0, 0) == DP * 4 * (1 + 6)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 0) == DP * 4
+    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.B2T, 0, 1) == 0
+    assert L.gspn_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0     # above the limit
+    assert g.workspace_bytes_dirs(2, 3, 20, 16) == DP * 4 * 13
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "GSPN_E_NULL"),
+    (dict(lg=None), "GSPN_E_NULL"),
+    (dict(u=None), "GSPN_E_NULL"),
+    (dict(stride=-1), "GSPN_E_SHAPE"),
+    (dict(stride=DP - 1), "GSPN_E_SHAPE"),         # directions would overlap
+    (dict(stride=1 << 62), "GSPN_E_SHAPE"),
+    (dict(H=8200, W=4), "GSPN_E_SHAPE"),          # above the per-direction limit
+    (dict(mask=0), "GSPN_E_DIRMASK"),
+    (dict(G=-2), "GSPN_E_GROUP"),
+    (dict(dt=3), "GSPN_E_DTYPE"),
+    (dict(merge=BASE + 8 * SZ + 2), "GSPN_E_ALIGN"),
+    (dict(dt=1, lam=BASE + 4 * SZ + 1), "GSPN_E_ALIGN"),
+    # out inside direction 2's lambda (element offset 2 * stride)
+    (dict(out=BASE + 4 * SZ + 2 * DP * 4 + 64), "GSPN_E_ALIAS"),
+    (dict(out=BASE + 8 * SZ - 64), "GSPN_E_ALIAS"),   # out runs into the merge weights
+    (dict(out=BASE + 8), "GSPN_E_ALIAS"),            # overlaps x
+])
+def test_dirs_rejects_bad_arguments(L, kw, status):
+    assert dcall(L, **kw) == g.STATUS[status]
+    assert L.gspn_last_error().decode() != ""
+
+
+def test_dirs_aliasing_only_for_selected_directions(L):
+    # out exactly on direction 2's lambda, but direction 2 is not selected:
+    # the call passes the aliasing check and stops at the missing workspace
+    out = BASE + 4 * SZ + 2 * DP * 4
+    assert dcall(L, out=out, mask=g.T2B | g.R2L) == g.STATUS["GSPN_E_WORKSPACE"]
+    # stride 0: every direction reads the same tensors, no overlap among them
+    assert dcall(L, stride=0) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert dcall(L, merge=None) == g.STATUS["GSPN_E_WORKSPACE"]
+
+
+def test_dirs_workspace_checks(L):
+    need = L.gspn_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0)
+    assert dcall(L, ws=BASE + 7 * SZ, ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert dcall(L, ws=BASE + 7 * SZ + 16, ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]
+    # the workspace inside direction 3's u
+    assert dcall(L, ws=BASE + 5 * SZ + 3 * DP * 4, ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]
+    assert dcall(L, ws=BASE + 6 * SZ, ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]   # out
+
+
+def test_dirs_empty_batch_is_ok_without_gpu(L):
+    assert dcall(L, B=0) == 0

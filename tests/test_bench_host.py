@@ -10,17 +10,26 @@ from linear_spatial_propagation_line_amd.inputs import WORKLOADS
 
 KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "tp_vfwd",
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
-           "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits"]
+           "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
+           "dir_vert", "dir_tr_in", "dir_tr_acc"]
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("bwd", [False, True])
 def test_input_sets_and_qmin(name, bwd):
     w = WORKLOADS[name]
+    s = 4 if w.dtype == "f32" else 2
+    if w.per_direction:
+        if bwd:
+            with pytest.raises(ValueError):
+                bench.qmin_per_pixel(w, bwd)
+            return
+        assert bench.qmin_per_pixel(w, bwd) == (2 + 5 * w.ndirs) * s
     n = bench.input_sets(w, bwd)
     assert isinstance(n, int) and 1 <= n <= 8
-    s = 4 if w.dtype == "f32" else 2
     q = bench.qmin_per_pixel(w, bwd)
+    if w.per_direction:
+        return
     if w.cl == w.C:
         assert q == (13 if bwd else 7) * s
     else:
@@ -31,6 +40,23 @@ def test_input_sets_and_qmin(name, bwd):
 def test_design_bytes_known(kernel):
     for w in WORKLOADS.values():
         assert bench.design_bytes(kernel, w.B * w.C, w) > 0
+
+
+def test_direction_passes_sum_to_their_design():
+    """Per-direction layer, four directions: x and the horizontal directions'
+    ten tensors transposed (11 tensors read and written), four passes that
+    each read their six tensors, the accumulator written by the first, read
+    and written by the next two and read by the last, which writes out, and
+    the horizontal sum transposed back (fp32 read and write)."""
+    w = WORKLOADS["t2i_2048x1024_pd"]
+    s = 2
+    planes = w.B * w.C
+    tot = bench.design_bytes("dir_tr_in", planes * 11, w)
+    for i in range(4):
+        tot += bench.design_bytes("dir_vert", planes, w, first=i == 0, last=i == 3)
+    tot += bench.design_bytes("dir_tr_acc", planes, w)
+    assert tot == w.pixels * (22 * s + 4 * 6 * s + 4 + 8 + 8 + 4 + s + 8)
+    assert bench.qmin_per_pixel(w, False) == 22 * s
 
 
 def test_every_traced_kernel_name_has_design_bytes():
