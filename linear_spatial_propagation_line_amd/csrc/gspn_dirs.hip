@@ -293,6 +293,47 @@ __global__ __launch_bounds__(256) void dir_transpose(TrArgs<S, Dt> a) {
   }
 }
 
+// The same for bf16 planes with even sides and 4-byte aligned tensors, two
+// adjacent elements per lane on both sides (4-byte accesses, 256-byte rows)
+// over tiles of 64 rows x 128 columns: a lane loads a column pair of one
+// source row and stores a pair of adjacent source rows into one destination
+// row.
+__global__ __launch_bounds__(256) void dir_transpose_pairs(TrArgs<bf16_t, bf16_t> a) {
+  __shared__ uint16_t tile[64][130];
+  const int R = a.R, C = a.C;
+  const int tr = (R + 63) / 64, tc = (C + 127) / 128;
+  const int64_t tiles = a.planes * tr * tc;
+  const uint16_t* src0 = reinterpret_cast<const uint16_t*>(a.src[blockIdx.y]);
+  uint16_t* dst0 = reinterpret_cast<uint16_t*>(a.dst[blockIdx.y]);
+  const int cp = threadIdx.x & 63, ry = threadIdx.x >> 6;   // load: column pair, row
+  const int rp = threadIdx.x & 31, cy = threadIdx.x >> 5;   // store: row pair, column
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t p = t / (tr * tc);
+    const int rem = static_cast<int>(t - p * tr * tc);
+    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 128;
+    const uint16_t* src = src0 + p * R * C;
+    uint16_t* dst = dst0 + p * R * C;
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const int r = r0 + ry + i, c = c0 + 2 * cp;
+      if (r < R && c < C)
+        *reinterpret_cast<uint32_t*>(&tile[ry + i][2 * cp]) =
+            *reinterpret_cast<const uint32_t*>(src + static_cast<int64_t>(r) * C + c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 128; i += 8) {
+      const int c = c0 + cy + i, r = r0 + 2 * rp;
+      if (c < C && r < R) {
+        const uint32_t v = static_cast<uint32_t>(tile[2 * rp][cy + i]) |
+                           (static_cast<uint32_t>(tile[2 * rp + 1][cy + i]) << 16);
+        *reinterpret_cast<uint32_t*>(dst + static_cast<int64_t>(c) * R + r) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 int64_t dirs_max_orth() { return 8192; }
 
 size_t dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
@@ -372,10 +413,25 @@ hipError_t transpose(const S* const* src, Dt* const* dst, int n, int64_t planes,
   t.planes = planes;
   t.R = R;
   t.C = C;
-  const int64_t tiles = planes * ((R + 63) / 64) * ((C + 63) / 64);
+  bool pairs = false;
+  if constexpr (sizeof(S) == 2 && sizeof(Dt) == 2) {
+    pairs = R % 2 == 0 && C % 2 == 0;
+    for (int i = 0; i < n; ++i)
+      pairs = pairs && reinterpret_cast<uintptr_t>(src[i]) % 4 == 0 &&
+              reinterpret_cast<uintptr_t>(dst[i]) % 4 == 0;
+  }
+  const int64_t tiles = planes * ((R + 63) / 64) * ((C + (pairs ? 127 : 63)) / (pairs ? 128 : 64));
   const int64_t grid = tiles < 65536 ? tiles : 65536;
-  auto kern = dir_transpose<S, Dt>;
   tr->before(stream, name, planes * n);
+  if constexpr (sizeof(S) == 2 && sizeof(Dt) == 2) {
+    if (pairs) {
+      hipLaunchKernelGGL(dir_transpose_pairs, dim3(static_cast<unsigned>(grid), n), dim3(256), 0,
+                         stream, t);
+      tr->after(stream);
+      return hipGetLastError();
+    }
+  }
+  auto kern = dir_transpose<S, Dt>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid), n), dim3(256), 0, stream, t);
   tr->after(stream);
   return hipGetLastError();
