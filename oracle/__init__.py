@@ -70,6 +70,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         f3.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp,
                        ctypes.c_uint32, i64, vp, ctypes.c_int]
         f3.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_prologue"):
+        f4 = lib.gspn_oracle_prologue
+        f4.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
+                       ctypes.c_int]
+        f4.restype = ctypes.c_int
     if hasattr(lib, "gspn_oracle_backward"):
         b = lib.gspn_oracle_backward
         b.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
@@ -177,6 +182,52 @@ def propagate_dirs(x, l0, l1, l2, lam, u, merge=None, dirs: int = 15, group_rows
                                       int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    return out
+
+
+PARAM_NAMES = ("l0", "l1", "l2", "lam", "u")
+
+
+def prologue(x_in, w_r, b_r, w_p, b_p, nthreads: int | None = None,
+             lib: ctypes.CDLL | None = None) -> dict:
+    """The module prologue's 1x1 convolutions (reading R16 in gspn_oracle.c).
+
+    ``x_in`` [B, Cin, H, W]; ``w_r`` [C, Cin]; ``b_r`` [C] or None; ``w_p``
+    [5C, C] (output channel t * C + c for t = l0, l1, l2, lam, u); ``b_p``
+    [5C] or None; all of one dtype as in ``propagate``. Returns float64
+    arrays: "x" (exact), "xr" (x rounded to the storage type) and "l0", "l1",
+    "l2", "lam", "u", each [B, C, H, W], computed from "xr"."""
+    x_in = np.asarray(x_in)
+    if x_in.ndim != 4:
+        raise ValueError("x_in must be [B, Cin, H, W]")
+    B, Cin, H, W = x_in.shape
+    C = np.asarray(w_r).shape[0]
+    arrs, dts = [], set()
+    for a, shp in ((x_in, (B, Cin, H, W)), (w_r, (C, Cin)), (b_r, (C,)), (w_p, (5 * C, C)),
+                   (b_p, (5 * C,))):
+        if a is None:
+            arrs.append(None)
+            continue
+        a2, dt = _as_input(np.asarray(a), shp)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    dt = dts.pop()
+    x = np.empty((B, C, H, W))
+    xr = np.empty((B, C, H, W))
+    p = np.empty((5, B, C, H, W))
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    L = lib if lib is not None else load()
+    ptr = [None if a is None else a.ctypes.data for a in arrs]
+    rc = L.gspn_oracle_prologue(ptr[0], dt, B, Cin, C, H, W, ptr[1], ptr[2], ptr[3], ptr[4],
+                                x.ctypes.data, xr.ctypes.data, p.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    out = {"x": x, "xr": xr}
+    for t, name in enumerate(PARAM_NAMES):
+        out[name] = p[t]
     return out
 
 

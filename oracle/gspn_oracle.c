@@ -71,6 +71,16 @@
  *     and the directions are merged by per-channel weights m[d][c],
  *     y = sum_d m[d][c] u_d (.) h_d. A merger that mixes channels as well
  *     would be a dense matrix product and is not part of this layer.
+ *  R16 The module's prologue (aitntnews page, section GSPN架构: a shared 1x1
+ *     convolution reduces the channels, then three independent 1x1
+ *     convolutions produce the input-dependent propagation parameters): a 1x1
+ *     convolution is a per-pixel affine map over channels. x = W_r X_in + b_r
+ *     (Cin -> C channels); the logit convolution maps x to the three logit
+ *     tensors (3C channels), the other two map x to lambda and to u (C
+ *     channels each). Every convolution output is a tensor of the storage
+ *     type, so x is rounded to it (to nearest, ties to even) before the three
+ *     parameter convolutions read it. No activation is applied: the sigmoid
+ *     and normalisation of the logits belong to the propagation.
  */
 #include "gspn_oracle.h"
 
@@ -276,6 +286,93 @@ int gspn_oracle_propagate(const void* x, const void* l0, const void* l1,
                           double* out, int nthreads) {
   return gspn_oracle_propagate_shared(x, l0, l1, l2, lam, u, in_dtype, B, C, H, W,
                                       C > 0 ? C : 1, dir_mask, group_rows, out, nthreads);
+}
+
+/* ========================================================================
+ * Module prologue (R16)
+ * ======================================================================== */
+
+/* v rounded to the nearest value of the storage type, ties to even */
+static double round_to_type(double v, int dt) {
+  if (dt == ORC_F64) return v;
+  if (dt == ORC_F32) return (double)(float)v;
+  if (v == 0.0 || !isfinite(v)) return v;
+  /* bf16 keeps 8 significant bits: v = m 2^e with 0.5 <= |m| < 1 */
+  int e;
+  const double m = frexp(v, &e);
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+typedef struct {
+  const void *x_in, *w_r, *b_r, *w_p, *b_p;
+  int dt;
+  int64_t B, Cin, C, HW;
+  double *x_out, *xr_out, *p_out;
+  int64_t next;          /* shared work counter over (b, pixel) */
+  pthread_mutex_t lock;
+} pjob_t;
+
+static void* prologue_worker(void* arg) {
+  pjob_t* j = (pjob_t*)arg;
+  const int64_t B = j->B, Cin = j->Cin, C = j->C, HW = j->HW;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
+  if (!xr) return (void*)1;
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t item = j->next++;
+    pthread_mutex_unlock(&j->lock);
+    if (item >= B * HW) break;
+    const int64_t b = item / HW, px = item % HW;
+    /* x[c] = b_r[c] + sum_k w_r[c][k] x_in[k] at this pixel */
+    for (int64_t c = 0; c < C; ++c) {
+      double acc = j->b_r ? load_value(j->b_r, j->dt, c) : 0.0;
+      for (int64_t k = 0; k < Cin; ++k)
+        acc += load_value(j->w_r, j->dt, c * Cin + k) *
+               load_value(j->x_in, j->dt, (b * Cin + k) * HW + px);
+      j->x_out[(b * C + c) * HW + px] = acc;
+      xr[c] = round_to_type(acc, j->dt);
+      j->xr_out[(b * C + c) * HW + px] = xr[c];
+    }
+    /* parameter channels q = t * C + c (t: l0, l1, l2, lambda, u) read the
+     * rounded x */
+    for (int64_t q = 0; q < 5 * C; ++q) {
+      double acc = j->b_p ? load_value(j->b_p, j->dt, q) : 0.0;
+      for (int64_t c = 0; c < C; ++c) acc += load_value(j->w_p, j->dt, q * C + c) * xr[c];
+      const int64_t t = q / C, c = q % C;
+      j->p_out[((t * B + b) * C + c) * HW + px] = acc;
+    }
+  }
+  free(xr);
+  return NULL;
+}
+
+int gspn_oracle_prologue(const void* x_in, int in_dtype, int64_t B, int64_t Cin, int64_t C,
+                         int64_t H, int64_t W, const void* w_r, const void* b_r,
+                         const void* w_p, const void* b_p, double* x_out, double* xr_out,
+                         double* p_out, int nthreads) {
+  if (!x_in || !w_r || !w_p || !x_out || !xr_out || !p_out) return -1;
+  if (B < 0 || Cin < 1 || C < 1 || H <= 0 || W <= 0) return -1;
+  if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16) return -1;
+  if (B == 0) return 0;
+  pjob_t j;
+  j.x_in = x_in; j.w_r = w_r; j.b_r = b_r; j.w_p = w_p; j.b_p = b_p;
+  j.dt = in_dtype; j.B = B; j.Cin = Cin; j.C = C; j.HW = H * W;
+  j.x_out = x_out; j.xr_out = xr_out; j.p_out = p_out; j.next = 0;
+  pthread_mutex_init(&j.lock, NULL);
+  int nt = nthreads <= 0 ? 1 : nthreads;
+  if ((int64_t)nt > B * H * W) nt = (int)(B * H * W);
+  int rc = 0;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  if (!th) { pthread_mutex_destroy(&j.lock); return -1; }
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, prologue_worker, &j);
+  for (int t = 0; t < nt; ++t) {
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret != NULL) rc = -1;
+  }
+  free(th);
+  pthread_mutex_destroy(&j.lock);
+  return rc;
 }
 
 /* ========================================================================

@@ -78,6 +78,13 @@ int gspn_oracle_propagate_shared(const void* x, const void* l0, const void* l1,
                                  int in_dtype, int64_t B, int64_t C, int64_t H,
                                  int64_t W, int64_t logit_channels, uint32_t dir_mask,
                                  int64_t group_rows, double* out, int nthreads);
+int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
+                                const void* l2, const void* lam, const void* u,
+                                const void* gy, int in_dtype, int64_t B, int64_t C,
+                                int64_t H, int64_t W, int64_t logit_channels,
+                                uint32_t dir_mask, int64_t group_rows, double* dx,
+                                double* dl0, double* dl1, double* dl2, double* dlam,
+                                double* du, int nthreads);
 
 /*
  * Per-direction parameters and a per-channel merger (aitntnews page, sections
@@ -94,13 +101,21 @@ int gspn_oracle_propagate_dirs(const void* x, const void* l0, const void* l1,
                                int64_t W, int64_t dir_stride, const double* merge,
                                uint32_t dir_mask, int64_t group_rows, double* out,
                                int nthreads);
-int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
-                                const void* l2, const void* lam, const void* u,
-                                const void* gy, int in_dtype, int64_t B, int64_t C,
-                                int64_t H, int64_t W, int64_t logit_channels,
-                                uint32_t dir_mask, int64_t group_rows, double* dx,
-                                double* dl0, double* dl1, double* dl2, double* dlam,
-                                double* du, int nthreads);
+
+/*
+ * Module prologue (aitntnews page, section GSPN架构; reading R16 in the
+ * source): x_in [B, Cin, H, W]; w_r [C, Cin], b_r [C]; w_p [5C, C], b_p [5C]
+ * with output channel q = t * C + c for t = 0..4 (l0, l1, l2, lambda, u), all
+ * of element type in_dtype; b_r / b_p may be NULL (zero bias).
+ *   x_out  [B, C, H, W]     = b_r + w_r x_in per pixel, exact (fp64)
+ *   xr_out [B, C, H, W]     = x_out rounded to in_dtype (nearest, ties even)
+ *   p_out  [5, B, C, H, W]  = b_p + w_p xr_out per pixel, exact (fp64)
+ * Returns 0, or -1 on a bad argument.
+ */
+int gspn_oracle_prologue(const void* x_in, int in_dtype, int64_t B, int64_t Cin, int64_t C,
+                         int64_t H, int64_t W, const void* w_r, const void* b_r,
+                         const void* w_p, const void* b_p, double* x_out, double* xr_out,
+                         double* p_out, int nthreads);
 
 #ifdef __cplusplus
 }
