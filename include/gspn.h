@@ -285,6 +285,47 @@ gspn_status gspn_propagate_dirs_ws(const void* x, const void* const w_logits[3],
 size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
                                  uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype);
 
+/*
+ * The module prologue (aitntnews page, section GSPN架构: a shared 1x1
+ * convolution reduces the channels, then three independent 1x1 convolutions
+ * produce the input-dependent propagation parameters). Per pixel:
+ *
+ *   x      = w_reduce (C x Cin) x_in + b_reduce          -> x_out
+ *   params = w_params (5C x C)  x    + b_params          -> params_out[0..4]
+ *
+ * where params rows t*C .. t*C+C-1 are l0, l1, l2, lambda, u for t = 0..4
+ * (the logit convolution is rows 0 .. 3C-1). Every output is rounded once,
+ * to nearest even, to the storage dtype, and the parameter convolutions read
+ * x as stored. No activation is applied (the propagation takes logits).
+ *
+ * x_in [B, Cin, H, W]; w_reduce [C, Cin]; b_reduce [C] or NULL (zero);
+ * w_params [5C, C]; b_params [5C] or NULL; x_out and params_out[0..4]
+ * [B, C, H, W]. All device memory of one dtype, caller-owned. Outputs may
+ * overlap neither an input nor each other (GSPN_E_ALIAS). B <= 65535 and
+ * H * W < 2^31 (GSPN_E_SHAPE). Computed with MFMA in fp32 accumulation.
+ * Enqueued on `stream`; no workspace.
+ */
+gspn_status gspn_prologue(const void* x_in, int64_t Cin, const void* w_reduce,
+                          const void* b_reduce, const void* w_params, const void* b_params,
+                          int64_t B, int64_t C, int64_t H, int64_t W, gspn_dtype dtype,
+                          void* x_out, void* const params_out[5], hipStream_t stream);
+
+/*
+ * The whole GSPN unit: gspn_prologue into the workspace, then
+ * gspn_propagate_ws on its outputs, out = sum_d u (.) h_d over dir_mask.
+ * Workspace: gspn_module_workspace_bytes() bytes, 256-byte aligned,
+ * caller-owned (the prologue's six tensors and the propagation's
+ * workspace). out [B, C, H, W] may not overlap an input or the workspace.
+ * Same status codes as gspn_prologue and gspn_propagate_ws.
+ */
+gspn_status gspn_module_ws(const void* x_in, int64_t Cin, const void* w_reduce,
+                           const void* b_reduce, const void* w_params, const void* b_params,
+                           int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                           int64_t group_rows, gspn_dtype dtype, void* out, void* workspace,
+                           size_t ws_bytes, hipStream_t stream);
+size_t gspn_module_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W,
+                                   uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype);
+
 /* gspn_backward_plan_name -- kernel plan gspn_propagate_backward would use,
  * or "invalid". Host-only. */
 const char* gspn_backward_plan_name(int64_t B, int64_t C, int64_t H, int64_t W,

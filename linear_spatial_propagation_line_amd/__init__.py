@@ -99,6 +99,15 @@ def lib() -> ctypes.CDLL:
         L.gspn_propagate_dirs_ws.restype = ctypes.c_int
         L.gspn_workspace_bytes_dirs.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
         L.gspn_workspace_bytes_dirs.restype = ctypes.c_size_t
+        outs5_t = ctypes.POINTER(ctypes.c_void_p)
+        L.gspn_prologue.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                    vp, outs5_t, vp]
+        L.gspn_prologue.restype = ctypes.c_int
+        L.gspn_module_ws.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, u32, i64,
+                                     ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+        L.gspn_module_ws.restype = ctypes.c_int
+        L.gspn_module_workspace_bytes.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
+        L.gspn_module_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -224,6 +233,83 @@ def propagate_dirs(x, logits, lam, u, merge=None, dirs: int = ALL, group_rows: i
     _check(L.gspn_propagate_dirs_ws(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(),
                                     B * C * H * W, mptr, B, C, H, W, dirs, group_rows, dt,
                                     out.data_ptr(), ws_ptr, ws_len, sptr))
+    return out
+
+
+PARAM_NAMES = ("l0", "l1", "l2", "lam", "u")
+
+
+def _check_prologue(x_in, w_r, b_r, w_p, b_p):
+    import torch
+    if x_in.dim() != 4:
+        raise ValueError("x_in must be [B, Cin, H, W]")
+    B, Cin, H, W = x_in.shape
+    if w_r.dim() != 2 or w_r.shape[1] != Cin:
+        raise ValueError("w_reduce must be [C, Cin]")
+    C = w_r.shape[0]
+    shapes = [(w_r, (C, Cin)), (b_r, (C,)), (w_p, (5 * C, C)), (b_p, (5 * C,))]
+    for t in [x_in] + [t for t, _ in shapes]:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.device != x_in.device or t.device.type != "cuda":
+            raise TypeError("all prologue tensors must be on x_in's GPU device")
+        if t.dtype != x_in.dtype or not t.is_contiguous():
+            raise ValueError("prologue tensors must be contiguous and of x_in's dtype")
+    for t, shp in shapes:
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"prologue weight of shape {tuple(t.shape)}, expected {shp}")
+    return B, Cin, C, H, W
+
+
+def prologue(x_in, w_reduce, b_reduce, w_params, b_params, outs=None, stream=None) -> dict:
+    """The module prologue's 1x1 convolutions: x = w_reduce x_in + b_reduce,
+    then l0, l1, l2, lam, u = the five C-row blocks of w_params x + b_params.
+    ``x_in`` [B, Cin, H, W]; ``w_reduce`` [C, Cin]; ``w_params`` [5C, C];
+    biases [C] / [5C] or None; contiguous device tensors of one dtype. Returns
+    {"x", "l0", "l1", "l2", "lam", "u"}, each [B, C, H, W]."""
+    import torch
+    B, Cin, C, H, W = _check_prologue(x_in, w_reduce, b_reduce, w_params, b_params)
+    if outs is None:
+        outs = {k: torch.empty((B, C, H, W), dtype=x_in.dtype, device=x_in.device)
+                for k in ("x",) + PARAM_NAMES}
+    if stream is None:
+        stream = torch.cuda.current_stream(x_in.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    po = (ctypes.c_void_p * 5)(*[outs[k].data_ptr() for k in PARAM_NAMES])
+    L = lib()
+    _check(L.gspn_prologue(x_in.data_ptr(), Cin, w_reduce.data_ptr(),
+                           None if b_reduce is None else b_reduce.data_ptr(),
+                           w_params.data_ptr(), None if b_params is None else b_params.data_ptr(),
+                           B, C, H, W, _dtype_code(x_in), outs["x"].data_ptr(), po, sptr))
+    return outs
+
+
+def module_workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
+    return int(lib().gspn_module_workspace_bytes(B, C, H, W, dirs, group_rows, dtype))
+
+
+def module(x_in, w_reduce, b_reduce, w_params, b_params, dirs: int = ALL, group_rows: int = 0,
+           out=None, workspace=None, stream=None):
+    """The GSPN unit: the prologue's convolutions, then the propagation of
+    their outputs; returns out = sum_{d in dirs} u * h_d, [B, C, H, W]."""
+    import torch
+    B, Cin, C, H, W = _check_prologue(x_in, w_reduce, b_reduce, w_params, b_params)
+    dt = _dtype_code(x_in)
+    if out is None:
+        out = torch.empty((B, C, H, W), dtype=x_in.dtype, device=x_in.device)
+    L = lib()
+    need = int(L.gspn_module_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_in.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x_in.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(L.gspn_module_ws(x_in.data_ptr(), Cin, w_reduce.data_ptr(),
+                            None if b_reduce is None else b_reduce.data_ptr(),
+                            w_params.data_ptr(), None if b_params is None else b_params.data_ptr(),
+                            B, C, H, W, dirs, group_rows, dt, out.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            sptr))
     return out
 
 

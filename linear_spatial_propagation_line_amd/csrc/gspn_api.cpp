@@ -159,11 +159,16 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   return GSPN_OK;
 }
 
-gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream) {
+// `cont`: a tracer that already holds earlier launches of the same call
+gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream,
+                gspn::Tracer* cont = nullptr) {
   hipError_t e = hipSuccess;
-  gspn::Tracer tr;
-  tr.events = g_trace_events;
-  tr.pairs = g_trace_pairs;
+  gspn::Tracer local;
+  gspn::Tracer& tr = cont ? *cont : local;
+  if (!cont) {
+    tr.events = g_trace_events;
+    tr.pairs = g_trace_pairs;
+  }
   switch (plan) {
     case Plan::kPlane16:
     case Plan::kPlane64:
@@ -235,6 +240,73 @@ Checked check_dirs_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t ma
   }
   r.ws_bytes = gspn::dirs_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
   return r;
+}
+
+// ---- module prologue --------------------------------------------------------
+gspn_status check_prologue(const void* x_in, int64_t Cin, const void* w_r, const void* b_r,
+                           const void* w_p, const void* b_p, int64_t B, int64_t C, int64_t H,
+                           int64_t W, gspn_dtype dtype, void* x_out, void* const p_out[5],
+                           gspn::PrologueProblem* pr) {
+  if (!x_in || !w_r || !w_p || !x_out || !p_out)
+    return fail(GSPN_E_NULL, "x_in, w_reduce, w_params, x_out and params_out must be non-null");
+  for (int t = 0; t < 5; ++t)
+    if (!p_out[t]) return fail(GSPN_E_NULL, "params_out[0..4] must be non-null");
+  if (dtype != GSPN_F32 && dtype != GSPN_BF16)
+    return fail(GSPN_E_DTYPE, "dtype must be GSPN_F32 or GSPN_BF16");
+  if (B < 0 || Cin < 1 || C < 1 || H < 1 || W < 1)
+    return fail(GSPN_E_SHAPE, "need B >= 0, Cin >= 1, C >= 1, H >= 1, W >= 1");
+  const int64_t k31 = int64_t(1) << 31;
+  if (B > 65535 || H >= k31 || W >= k31 || H * W >= k31 || Cin >= k31 || C >= k31 / 5)
+    return fail(GSPN_E_SHAPE, "prologue limits: B <= 65535, H * W < 2^31, 5C < 2^31");
+  if (B > 0 && (C * H * W > INT64_MAX / 16 / B || Cin * H * W > INT64_MAX / 16 / B))
+    return fail(GSPN_E_SHAPE, "tensor size overflows");
+  const size_t es = elem_size(dtype);
+  const void* ins[5] = {x_in, w_r, b_r, w_p, b_p};
+  const size_t in_n[5] = {static_cast<size_t>(B * Cin * H * W), static_cast<size_t>(C * Cin),
+                          static_cast<size_t>(C), static_cast<size_t>(5 * C * C),
+                          static_cast<size_t>(5 * C)};
+  const void* outs[6] = {x_out, p_out[0], p_out[1], p_out[2], p_out[3], p_out[4]};
+  for (const void* p : ins)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
+  for (const void* p : outs)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "output pointer not aligned to its element size");
+  const size_t ob = static_cast<size_t>(B * C * H * W) * es;
+  for (int i = 0; i < 6; ++i) {
+    for (int k = 0; k < 5; ++k)
+      if (ins[k] && overlaps(outs[i], ob, ins[k], in_n[k] * es))
+        return fail(GSPN_E_ALIAS, "a prologue output overlaps an input");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], ob, outs[j], ob))
+        return fail(GSPN_E_ALIAS, "two prologue outputs overlap");
+  }
+  pr->x_in = x_in;
+  pr->w_r = w_r;
+  pr->b_r = b_r;
+  pr->w_p = w_p;
+  pr->b_p = b_p;
+  pr->x_out = x_out;
+  for (int t = 0; t < 5; ++t) pr->p_out[t] = p_out[t];
+  pr->B = B; pr->Cin = Cin; pr->C = C; pr->H = H; pr->W = W;
+  pr->dtype = dtype;
+  return GSPN_OK;
+}
+
+gspn_status run_prologue(const gspn::PrologueProblem& pr, hipStream_t stream,
+                         gspn::Tracer* tr) {
+  const hipError_t e = gspn::launch_prologue(pr, stream, tr);
+  if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
+  return GSPN_OK;
+}
+
+void keep_trace(const gspn::Tracer& tr) {
+  if (!g_trace_events) return;
+  g_trace_count = tr.count;
+  for (int i = 0; i < gspn::kTraceMax; ++i) {
+    g_trace_names[i] = tr.names[i];
+    g_trace_planes[i] = tr.planes[i];
+  }
 }
 
 // ---- backward pass ---------------------------------------------------------
@@ -630,6 +702,89 @@ gspn_status gspn_propagate_shared_ws(const void* x, const void* const w_logits[3
   }
   if (B * C == 0) return GSPN_OK;
   return run(pr, chk.plan, workspace, stream);
+}
+
+gspn_status gspn_prologue(const void* x_in, int64_t Cin, const void* w_reduce,
+                          const void* b_reduce, const void* w_params, const void* b_params,
+                          int64_t B, int64_t C, int64_t H, int64_t W, gspn_dtype dtype,
+                          void* x_out, void* const params_out[5], hipStream_t stream) {
+  g_last_error.clear();
+  gspn::PrologueProblem pr;
+  gspn_status s = check_prologue(x_in, Cin, w_reduce, b_reduce, w_params, b_params, B, C, H, W,
+                                 dtype, x_out, params_out, &pr);
+  if (s != GSPN_OK || B == 0) return s;
+  gspn::Tracer tr;
+  tr.events = g_trace_events;
+  tr.pairs = g_trace_pairs;
+  s = run_prologue(pr, stream, &tr);
+  keep_trace(tr);
+  return s;
+}
+
+size_t gspn_module_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                                   int64_t group_rows, gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  const Checked chk = check_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  g_last_error = keep;
+  if (chk.status != GSPN_OK || C < 1) return 0;
+  return 6 * al256(static_cast<size_t>(B * C * H * W) * elem_size(dtype)) + chk.ws_bytes;
+}
+
+gspn_status gspn_module_ws(const void* x_in, int64_t Cin, const void* w_reduce,
+                           const void* b_reduce, const void* w_params, const void* b_params,
+                           int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                           int64_t group_rows, gspn_dtype dtype, void* out, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!out) return fail(GSPN_E_NULL, "out must be non-null");
+  const Checked chk = check_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype));
+  if (chk.status != GSPN_OK) return chk.status;
+  if (C < 1) return fail(GSPN_E_SHAPE, "need C >= 1");
+  const size_t es = elem_size(dtype);
+  const size_t tb = al256(static_cast<size_t>(B * C * H * W) * es);
+  const size_t need = 6 * tb + chk.ws_bytes;
+  if (!workspace || ws_bytes < need)
+    return fail(GSPN_E_WORKSPACE, "workspace missing or smaller than gspn_module_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  void* params[5];
+  for (int t = 0; t < 5; ++t) params[t] = ws + (1 + t) * tb;
+  gspn::PrologueProblem pp;
+  gspn_status s = check_prologue(x_in, Cin, w_reduce, b_reduce, w_params, b_params, B, C, H, W,
+                                 dtype, ws, params, &pp);
+  if (s != GSPN_OK) return s;
+  // out against the inputs and the workspace
+  const void* ins[5] = {x_in, w_reduce, b_reduce, w_params, b_params};
+  const size_t in_n[5] = {static_cast<size_t>(B * Cin * H * W), static_cast<size_t>(C * Cin),
+                          static_cast<size_t>(C), static_cast<size_t>(5 * C * C),
+                          static_cast<size_t>(5 * C)};
+  const size_t ob = static_cast<size_t>(B * C * H * W) * es;
+  if (reinterpret_cast<uintptr_t>(out) % es)
+    return fail(GSPN_E_ALIGN, "out not aligned to its element size");
+  for (int k = 0; k < 5; ++k)
+    if (ins[k] && overlaps(out, ob, ins[k], in_n[k] * es))
+      return fail(GSPN_E_ALIAS, "out overlaps an input");
+  if (overlaps(out, ob, workspace, need)) return fail(GSPN_E_ALIAS, "out overlaps the workspace");
+  for (int k = 0; k < 5; ++k)
+    if (ins[k] && overlaps(workspace, need, ins[k], in_n[k] * es))
+      return fail(GSPN_E_ALIAS, "workspace overlaps an input");
+  if (B == 0) return GSPN_OK;
+  const void* logits[3] = {params[0], params[1], params[2]};
+  Checked pchk;
+  gspn::Problem pr;
+  s = check_all(ws, logits, params[3], params[4], B, C, H, W, dir_mask, group_rows, dtype, out,
+                &pchk, &pr, C);
+  if (s != GSPN_OK) return s;
+  gspn::Tracer tr;
+  tr.events = g_trace_events;
+  tr.pairs = g_trace_pairs;
+  s = run_prologue(pp, stream, &tr);
+  if (s != GSPN_OK) {
+    keep_trace(tr);
+    return s;
+  }
+  return run(pr, pchk.plan, ws + 6 * tb, stream, &tr);
 }
 
 size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,

@@ -95,6 +95,21 @@ int64_t dirs_max_orth();
 size_t dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask, gspn_dtype dt);
 hipError_t launch_dirs(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
+// module prologue: the 1x1 convolutions producing x, the logits, lambda and u
+// (gspn_prologue.hip); all tensors [B, *, H, W] of one dtype
+struct PrologueProblem {
+  const void* x_in;    // [B, Cin, H, W]
+  const void* w_r;     // [C, Cin]
+  const void* b_r;     // [C] or null
+  const void* w_p;     // [5C, C]: l0, l1, l2, lambda, u blocks of C rows
+  const void* b_p;     // [5C] or null
+  void* x_out;         // [B, C, H, W]
+  void* p_out[5];      // l0, l1, l2, lambda, u: [B, C, H, W] each
+  int64_t B, Cin, C, H, W;
+  gspn_dtype dtype;
+};
+hipError_t launch_prologue(const PrologueProblem& pr, hipStream_t stream, Tracer* tr);
+
 // backward pass, plane-resident path for H, W <= 64 (gspn_bwd_plane.hip)
 size_t bplane_lds_bytes(int64_t H, int64_t W);
 hipError_t launch_bplane(const BwdProblem& pr, hipStream_t stream, Tracer* tr);

@@ -23,12 +23,22 @@ weights):
   t2i_2048x1024_pd   direction and per-channel merge weights (aitntnews page,
                      sections 二维线性传播 and GSPN架构; CSDN page, section
                      GSPN模块的设计)
+  cls_56x56_mod      the whole unit: the prologue's 1x1 convolutions produce
+  dit_16x16_mod      x, the logits, lambda and u from an input of Cin = C
+  t2i_2048x1024_mod  channels (aitntnews page, section GSPN架构), then the
+                     propagation
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
 generator seeded with 1000 + k (k = 1..8 in the order above) and then cast
 (round-to-nearest-even) to the storage type. Per-direction workloads draw
 lambda, u and the logits as [4, B, C, H, W] (slice d for direction d) in the
-same order, then merge weights [4, C] from U(-1, 1), kept in float32. The output gradient of the
+same order, then merge weights [4, C] from U(-1, 1), kept in float32. Module
+workloads draw, from one generator seeded 3000 + k, x_in ~ N(0, 1)
+[B, Cin, H, W], w_reduce [C, Cin] normal with standard deviation Cin^-1/2,
+b_reduce [C] with standard deviation 0.1, w_params [5C, C] with standard
+deviation C^-1/2, b_params [5C] with 0.1, in that order, each
+cast to the storage type (weights scaled so that x and the parameters stay
+near unit variance). The output gradient of the
 backward pass (make_grad_out) is N(0, 1) from a generator seeded with
 2000 + k, cast the same way.
 """
@@ -59,6 +69,7 @@ class Workload:
     u: tuple
     logit_channels: int = 0   # 0: one logit channel per channel (unshared)
     per_direction: bool = False   # own (lambda, logits, u) per direction + merge weights
+    prologue_cin: int = 0         # > 0: the whole unit, prologue from Cin channels
 
     @property
     def cl(self) -> int:
@@ -106,6 +117,12 @@ WORKLOADS = {
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, per_direction=True),
         Workload("t2i_2048x1024_pd", 8, 1, 320, 2048, 1024, BF16, 15, 0,
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, per_direction=True),
+        Workload("cls_56x56_mod", 9, 64, 96, 56, 56, F32, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, prologue_cin=96),
+        Workload("dit_16x16_mod", 10, 32, 1152, 16, 16, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, prologue_cin=1152),
+        Workload("t2i_2048x1024_mod", 11, 1, 320, 2048, 1024, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, prologue_cin=320),
     ]
 }
 
@@ -149,6 +166,36 @@ def make_inputs(w: Workload | str, seed: int | None = None, device="cpu",
     if w.per_direction:
         out["merge"] = _draw(("uniform", -1.0, 1.0), (4, shape[1]), gen, device)
     return out
+
+
+def make_prologue_inputs(w: Workload | str | None = None, seed: int | None = None,
+                         device="cpu", B: int | None = None, Cin: int | None = None,
+                         C: int | None = None, H: int | None = None, W: int | None = None,
+                         dtype: str | None = None) -> dict:
+    """Input and weights of the module prologue: "x_in" [B, Cin, H, W],
+    "w_r" [C, Cin], "b_r" [C], "w_p" [5C, C], "b_p" [5C] in the storage dtype
+    (the workload's, or ``dtype``) on ``device``."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    B = B or w.B
+    Cin = Cin or w.prologue_cin
+    C = C or w.C
+    H = H or w.H
+    W = W or w.W
+    tdt = {F32: torch.float32, BF16: torch.bfloat16}[dtype or w.dtype]
+    if seed is None:
+        seed = 3000 + (w.index if w is not None else 0)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(shape, std):
+        return (torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std).to(tdt)
+
+    return {"x_in": normal((B, Cin, H, W), 1.0),
+            "w_r": normal((C, Cin), Cin ** -0.5),
+            "b_r": normal((C,), 0.1),
+            "w_p": normal((5 * C, C), C ** -0.5),
+            "b_p": normal((5 * C,), 0.1)}
 
 
 def make_grad_out(w: Workload | str, seed: int | None = None, device="cpu",

@@ -75,6 +75,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         f4.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                        ctypes.c_int]
         f4.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_round"):
+        f5 = lib.gspn_oracle_round
+        f5.argtypes = [vp, ctypes.c_int, i64, vp]
+        f5.restype = ctypes.c_int
     if hasattr(lib, "gspn_oracle_backward"):
         b = lib.gspn_oracle_backward
         b.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
@@ -228,6 +232,18 @@ def prologue(x_in, w_r, b_r, w_p, b_p, nthreads: int | None = None,
     out = {"x": x, "xr": xr}
     for t, name in enumerate(PARAM_NAMES):
         out[name] = p[t]
+    return out
+
+
+def round_to(a, dtype: str, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """float64 values rounded to "f32" or "bf16" (nearest, ties to even), as
+    float64; the rounding the prologue applies to x."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    dt = {"f64": ORC_F64, "f32": ORC_F32, "bf16": ORC_BF16}[dtype]
+    L = lib if lib is not None else load()
+    if L.gspn_oracle_round(a.ctypes.data, dt, a.size, out.ctypes.data) != 0:
+        raise ValueError("oracle rejected its arguments")
     return out
 
 

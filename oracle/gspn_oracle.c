@@ -303,6 +303,13 @@ static double round_to_type(double v, int dt) {
   return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
+int gspn_oracle_round(const double* in, int dt, int64_t n, double* out) {
+  if (!in || !out || n < 0) return -1;
+  if (dt != ORC_F64 && dt != ORC_F32 && dt != ORC_BF16) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = round_to_type(in[i], dt);
+  return 0;
+}
+
 typedef struct {
   const void *x_in, *w_r, *b_r, *w_p, *b_p;
   int dt;

@@ -117,6 +117,10 @@ int gspn_oracle_prologue(const void* x_in, int in_dtype, int64_t B, int64_t Cin,
                          const void* w_p, const void* b_p, double* x_out, double* xr_out,
                          double* p_out, int nthreads);
 
+/* out[i] = in[i] rounded to the element type dt (nearest, ties to even), the
+ * rounding gspn_oracle_prologue applies to x. Returns 0, or -1. */
+int gspn_oracle_round(const double* in, int dt, int64_t n, double* out);
+
 #ifdef __cplusplus
 }
 #endif

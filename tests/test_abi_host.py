@@ -316,3 +316,67 @@ def test_dirs_workspace_checks(L):
 
 def test_dirs_empty_batch_is_ok_without_gpu(L):
     assert dcall(L, B=0) == 0
+
+
+# ---- module prologue (gspn_prologue, gspn_module_ws) -------------------------
+# fake addresses again; every call fails validation or has B = 0
+PB, PCIN, PC, PH, PW = 2, 6, 4, 5, 7
+
+
+def pcall(L, x_in=BASE, cin=PCIN, w_r=BASE + SZ, b_r=BASE + 2 * SZ, w_p=BASE + 3 * SZ,
+          b_p=BASE + 4 * SZ, B=PB, C=PC, H=PH, W=PW, dt=0, x_out=BASE + 5 * SZ,
+          p_out=(BASE + 6 * SZ, BASE + 7 * SZ, BASE + 8 * SZ, BASE + 9 * SZ, BASE + 10 * SZ)):
+    arr = None if p_out is None else (ctypes.c_void_p * 5)(*p_out)
+    return L.gspn_prologue(x_in, cin, w_r, b_r, w_p, b_p, B, C, H, W, dt, x_out, arr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_in=None), "GSPN_E_NULL"),
+    (dict(w_p=None), "GSPN_E_NULL"),
+    (dict(p_out=None), "GSPN_E_NULL"),
+    (dict(p_out=(BASE + 6 * SZ, None, BASE + 8 * SZ, BASE + 9 * SZ, BASE + 10 * SZ)), "GSPN_E_NULL"),
+    (dict(dt=4), "GSPN_E_DTYPE"),
+    (dict(cin=0), "GSPN_E_SHAPE"),
+    (dict(C=0), "GSPN_E_SHAPE"),
+    (dict(B=70000), "GSPN_E_SHAPE"),
+    (dict(H=1 << 16, W=1 << 16), "GSPN_E_SHAPE"),
+    (dict(w_r=BASE + SZ + 2), "GSPN_E_ALIGN"),
+    (dict(dt=1, x_out=BASE + 5 * SZ + 1), "GSPN_E_ALIGN"),
+    (dict(x_out=BASE + 16), "GSPN_E_ALIAS"),                      # inside x_in
+    (dict(x_out=BASE + 3 * SZ + 8), "GSPN_E_ALIAS"),              # inside w_params
+    (dict(p_out=(BASE + 5 * SZ + 64, BASE + 7 * SZ, BASE + 8 * SZ, BASE + 9 * SZ,
+                 BASE + 10 * SZ)), "GSPN_E_ALIAS"),               # l0 inside x_out
+])
+def test_prologue_rejects_bad_arguments(L, kw, status):
+    assert pcall(L, **kw) == g.STATUS[status]
+    assert L.gspn_last_error().decode() != ""
+
+
+def test_prologue_empty_batch_and_null_biases(L):
+    assert pcall(L, B=0) == 0
+    assert pcall(L, B=0, b_r=None, b_p=None) == 0
+
+
+def test_module_workspace(L):
+    px = PB * PC * PH * PW
+    tb = (px * 4 + 255) // 256 * 256
+    assert L.gspn_module_workspace_bytes(PB, PC, PH, PW, 15, 0, 0) == 6 * tb   # plane plan
+    assert L.gspn_module_workspace_bytes(PB, PC, PH, PW, 0, 0, 0) == 0        # bad mask
+    need = L.gspn_module_workspace_bytes(PB, PC, 300, 200, 15, 0, 1)
+    assert need > 6 * PB * PC * 300 * 200 * 2
+    assert g.module_workspace_bytes(PB, PC, PH, PW) == 6 * tb
+    st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, PB, PC, PH, PW, 15,
+                          0, 0, BASE + 5 * SZ, BASE + 7 * SZ, 6 * tb - 1, None)
+    assert st == g.STATUS["GSPN_E_WORKSPACE"]
+    st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, PB, PC, PH, PW, 15,
+                          0, 0, BASE + 7 * SZ + 64, BASE + 7 * SZ, 6 * tb, None)
+    assert st == g.STATUS["GSPN_E_ALIAS"]      # out inside the workspace
+    st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, PB, PC, PH, PW, 15,
+                          0, 0, BASE + 5 * SZ, BASE + 16, 6 * tb, None)
+    assert st == g.STATUS["GSPN_E_ALIGN"]      # workspace not 256-byte aligned
+    st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, PB, PC, PH, PW, 15,
+                          0, 0, BASE + 5 * SZ, BASE + 256, 6 * tb, None)
+    assert st == g.STATUS["GSPN_E_ALIAS"]      # workspace inside x_in
+    st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, 0, PC, PH, PW, 15,
+                          0, 0, BASE + 5 * SZ, BASE + 7 * SZ, 6 * tb, None)
+    assert st == 0
