@@ -21,6 +21,11 @@ the three logits and u for a seeded dL/dout), with Q_min = 13 s per pixel
 (seven tensors read, six written). Per-direction workloads (own lambda,
 logits and u per direction, per-channel merge weights) have
 Q_min = (2 + 5 * dirs) s per pixel: x, each direction's five tensors, out.
+Module workloads (*_mod) time the whole unit, the prologue's 1x1
+convolutions and the propagation, with Q_min = (Cin / C + 1) s per pixel
+(x_in read, out written); with --prologue a step is the prologue alone and
+the metric is its TFLOP/s, the roofline bound being MFMA or HBM, whichever
+the kernel's flops and bytes make the longer.
 """
 from __future__ import annotations
 
@@ -38,6 +43,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GSPN propagated elem-steps/s (B·C·H·W·dirs) + achieved HBM GB/s vs peak"
 METRIC_BWD = "GSPN backward elem-steps/s (B·C·H·W·dirs) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+METRIC_PRO = "GSPN module prologue (1x1 convolutions on MFMA) TFLOP/s"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}    # dense, MI355X
 DEFAULT_WORKLOAD = "t2i_2048x1024"
 CSRC = os.path.join(ROOT, "linear_spatial_propagation_line_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -56,6 +63,9 @@ PLAN_SOURCES = {
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
+    "prologue": ("gspn_prologue.hip", "gspn_device.hpp"),
+    "module": ("gspn_prologue.hip", "gspn_plane.hip", "gspn_band.hip", "gspn_tpipe.hip",
+               "gspn_stream.hip", "gspn_device.hpp"),
 }
 
 
@@ -145,6 +155,10 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
           plane and tensor
       dir_tr_acc  the fp32 sum of the horizontal passes read (4) and written
           back row-major (4), or as out (s) when no vertical direction follows
+    Module prologue (counted per pixel of B images: `planes` is B here):
+      prologue_reduce  x_in read (Cin s), x written (C s)
+      prologue_params  x read (C s), five parameter tensors written (5 C s)
+      (the weights, read once from HBM, are left out)
     """
     s = 4 if w.dtype == "f32" else 2
     px = planes * w.H * w.W
@@ -170,6 +184,8 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "dir_vert": 6 * s + (0 if first else 4) + (s if last else 4),
         "dir_tr_in": 2 * s,
         "dir_tr_acc": 4 + (4 if w.dirs & 3 else s),
+        "prologue_reduce": (w.prologue_cin + w.C) * s,
+        "prologue_params": 6 * w.C * s,
     }[kernel]
     return per * px
 
@@ -185,6 +201,10 @@ def qmin_per_pixel(w, bwd: bool) -> float:
         if bwd:
             raise ValueError("no backward pass for per-direction parameters")
         return (2 + 5 * w.ndirs) * s
+    if w.prologue_cin:
+        if bwd:
+            raise ValueError("no backward pass for the module prologue")
+        return (w.prologue_cin / w.C + 1) * s
     share = w.cl / w.C
     return (7 + 6 * share) * s if bwd else (4 + 3 * share) * s
 
@@ -286,6 +306,59 @@ def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
                       f"{steps} elem-steps in {dt:.2f} s"}
 
 
+def prologue_work(w, B=None, H=None):
+    """(flops, algorithmic bytes) of the prologue: two products over B*H*W
+    pixels, C x Cin then 5C x C, and x_in read, x and five parameter
+    tensors written, the weights and biases read once."""
+    s = 4 if w.dtype == "f32" else 2
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    px = B * H * w.W
+    cin, c = w.prologue_cin, w.C
+    flops = 2.0 * px * c * (cin + 5 * c)
+    nbytes = (px * (cin + 6 * c) + c * cin + 5 * c * c + 6 * c) * s
+    return flops, nbytes
+
+
+def cpu_baseline_module(inp_dev, w, seconds: float, prologue_only: bool):
+    """The oracle's prologue (and, for the whole unit, its propagation) on the
+    first image's first rows, sized for about `seconds` on all host cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    macs_per_row = w.W * w.C * (w.prologue_cin + 5 * w.C)
+    rows = int(max(1, min(w.H, seconds * 1.5e8 * cores / macs_per_row)))
+
+    def host(t):
+        t = t.cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    x_in = host(inp_dev["x_in"][:1, :, :rows])
+    wts = [host(inp_dev[k]) for k in ("w_r", "b_r", "w_p", "b_p")]
+    t0 = time.perf_counter()
+    pro = oracle.prologue(x_in, *wts, nthreads=cores)
+    t_pro = time.perf_counter() - t0
+    flops, _ = prologue_work(w, B=1, H=rows)
+    sample = f"first image, rows 0..{rows - 1} of {w.H} ({rows}x{w.W} pixels, Cin {w.prologue_cin}, C {w.C})"
+    if prologue_only:
+        return {"value": flops / t_pro / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"prologue, {sample}, {t_pro:.2f} s"}
+    p = {k: oracle.round_to(pro[k], w.dtype) for k in ("l0", "l1", "l2", "lam", "u")}
+    t0 = time.perf_counter()
+    oracle.propagate(pro["xr"], p["l0"], p["l1"], p["l2"], p["lam"], p["u"], dirs=w.dirs,
+                     group_rows=w.group_rows, nthreads=cores)
+    t_prop = time.perf_counter() - t0
+    steps = w.C * rows * w.W * w.ndirs
+    return {"value": steps / (t_pro + t_prop), "unit": "elem-steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"prologue + propagation, {sample}, {steps} elem-steps in "
+                      f"{t_pro:.2f} + {t_prop:.2f} s"}
+
+
 def calibrate(torch, reps: int) -> int:
     """Plain copy of a 4 GiB buffer (4 GiB read + 4 GiB written per call) and
     a sum over it (4 GiB read), timed with events; one JSON line."""
@@ -321,6 +394,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (all six gradients) instead of the forward")
+    ap.add_argument("--prologue", action="store_true",
+                    help="module workloads: time the prologue's 1x1 convolutions alone")
     ap.add_argument("--calibrate", action="store_true",
                     help="time a plain device copy and a read-only reduction of known size "
                          "(the reference points for HBM bandwidth and for counter scaling)")
@@ -338,12 +413,19 @@ def main() -> int:
         return calibrate(torch, args.steps)
 
     import linear_spatial_propagation_line_amd as g
-    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_grad_out, make_inputs
+    from linear_spatial_propagation_line_amd.inputs import (WORKLOADS, make_grad_out, make_inputs,
+                                                            make_prologue_inputs)
 
     w = WORKLOADS[args.workload]
     bwd = args.backward
-    if bwd and w.per_direction:
-        print("no backward pass for per-direction parameters", file=sys.stderr)
+    mod = w.prologue_cin > 0
+    pro_only = args.prologue
+    if bwd and (w.per_direction or mod):
+        print("no backward pass for per-direction parameters or the module prologue",
+              file=sys.stderr)
+        return 2
+    if pro_only and not mod:
+        print("--prologue needs a module workload (*_mod)", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     dt_code = g.GSPN_F32 if w.dtype == "f32" else g.GSPN_BF16
@@ -351,6 +433,8 @@ def main() -> int:
         plan = g.backward_plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
     elif w.per_direction:
         plan = "dirs"
+    elif mod:
+        plan = "prologue" if pro_only else "module"
     else:
         plan = g.plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
 
@@ -360,6 +444,11 @@ def main() -> int:
     sets = []
     for i in range(nsets):
         seed = 1000 + w.index + 17 * i
+        if mod:
+            big = set_bytes > 1 << 30
+            st = make_prologue_inputs(w, seed=seed + 2000, device=dev if big else "cpu")
+            sets.append({k: v.to(dev) for k, v in st.items()})
+            continue
         if set_bytes > 1 << 30:
             st = make_inputs(w, seed=seed, device=dev)
             if bwd:
@@ -374,6 +463,15 @@ def main() -> int:
                  for k in g.GRAD_NAMES} for st in sets]
         ws_bytes = g.backward_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code,
                                               logit_channels=w.cl)
+    elif mod:
+        shape = (w.B, w.C, w.H, w.W)
+        if pro_only:
+            outs = [{k: torch.empty(shape, dtype=w.torch_dtype, device=dev)
+                     for k in ("x",) + g.PARAM_NAMES} for _ in sets]
+            ws_bytes = 0
+        else:
+            outs = [torch.empty(shape, dtype=w.torch_dtype, device=dev) for _ in sets]
+            ws_bytes = g.module_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
     else:
         outs = [torch.empty_like(st["x"]) for st in sets]
         wsb = g.workspace_bytes_dirs if w.per_direction else g.workspace_bytes
@@ -388,6 +486,12 @@ def main() -> int:
                                  st["gy"], dirs=w.dirs, group_rows=w.group_rows,
                                  grads=outs[i % nsets], workspace=ws if ws_bytes else None,
                                  stream=stream)
+        elif mod and pro_only:
+            g.prologue(st["x_in"], st["w_r"], st["b_r"], st["w_p"], st["b_p"],
+                       outs=outs[i % nsets], stream=stream)
+        elif mod:
+            g.module(st["x_in"], st["w_r"], st["b_r"], st["w_p"], st["b_p"], dirs=w.dirs,
+                     group_rows=w.group_rows, out=outs[i % nsets], workspace=ws, stream=stream)
         elif w.per_direction:
             g.propagate_dirs(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
                              merge=st["merge"], dirs=w.dirs, group_rows=w.group_rows,
@@ -461,10 +565,32 @@ def main() -> int:
     traffic = counter_traffic(plan, w.name, source_digest(plan))
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
+    roofline = {"bound": "hbm", "kernel": unit_name, "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic, "algorithmic_bytes_per_step": q_min, "unit_ms": unit_ms}
+    if pro_only:
+        # the prologue's two products: bound by MFMA or by HBM, whichever its
+        # flops and bytes make the longer at peak
+        flops, nbytes = prologue_work(w)
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        if flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9):
+            ach = flops / (unit_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": unit_name, "achieved": ach, "peak": peak,
+                        "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
+                        "algorithmic_flops_per_step": flops, "unit_ms": unit_ms}
+        else:
+            ach = nbytes / (unit_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "kernel": unit_name, "achieved": ach,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                        "traffic": traffic, "algorithmic_bytes_per_step": nbytes,
+                        "unit_ms": unit_ms}
+        roofline["flops_per_step"] = flops
+        roofline["mfma_tflops"] = flops / (unit_ms * 1e-3) / 1e12
     result = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": METRIC_PRO if pro_only else (METRIC_BWD if bwd else METRIC),
         "value": value,
-        "unit": "elem-steps/s",
+        "unit": "TFLOP/s" if pro_only else "elem-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -472,11 +598,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if (pro_only and w.dtype == "bf16") else "f32",
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
                    "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
                    "logit_channels": w.cl, "per_direction": w.per_direction,
+                   "prologue_cin": w.prologue_cin,
                    "plan": plan, "launches_per_step": counts[0],
                    "launches": [f"{n}[{p}]" for n, p in launches],
                    "launch_ms": [round(t, 4) for t in per_launch],
@@ -485,12 +612,11 @@ def main() -> int:
                    "path_design_gbs": path_bytes / (ms_per_step * 1e-3) / 1e9,
                    "path_qmin_bytes": q_min,
                    "host_wall_s": round(wall, 3), "input_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": unit_name, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_step": q_min,
-                     "unit_ms": unit_ms},
+        "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mod:
+        result["cpu_baseline"] = cpu_baseline_module(sets[0], w, args.cpu_seconds, pro_only)
+    elif not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
         # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core forward
         # and 0.6e6 - 3e6 backward (large planes at the low end)

@@ -20,9 +20,11 @@
 // Tiling (gfx950, 64-wide wavefronts): a workgroup of four wavefronts owns a
 // 128 x 128 output tile; each wavefront a 64 x 64 quarter, 4 x 4 MFMA tiles
 // of 16 x 16 with fp32 accumulators (v_mfma_f32_16x16x32_bf16 for bf16,
-// v_mfma_f32_16x16x4_f32 for fp32). K advances 32 at a time through LDS: the
-// weight tile as [m][k] and the pixel tile transposed to [n][k], so every
-// MFMA operand is a run of consecutive k. The finished tile is staged in LDS
+// v_mfma_f32_16x16x4_f32 for fp32). K advances one 128-byte row at a time
+// (64 bf16 or 32 fp32) through LDS, the next tile's loads in flight while the
+// current one is multiplied: the weight tile as [m][k]; the bf16 pixel tile
+// transposed to [n][k] (an MFMA operand is 8 consecutive k), written as
+// 8-byte runs of four k; the fp32 pixel tile as loaded. The finished tile is staged in LDS
 // (64 rows at a time) and written as 16-byte row runs. The linear block index
 // walks M fastest, so the M tiles that share a pixel tile run together and
 // find it in L2.
@@ -32,8 +34,8 @@
 namespace gspn {
 
 namespace {
-constexpr int kMT = 128, kNT = 128, kKT = 32;
-constexpr int kAP = kKT + 8;     // LDS pitch (elements) of the [m][k] and [n][k] tiles
+constexpr int kMT = 128, kNT = 128;
+constexpr size_t kXsMaxLds = 150 * 1024;   // pixel-stationary variant up to this LDS size
 constexpr int kOP = kNT + 8;     // LDS pitch of the staged output tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -41,6 +43,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float g_ld(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float g_ld(const bf16_t* p, int64_t i) { return to_f32(p[i]); }
+
+// Barriers that order LDS only. A plain __syncthreads() also fences global
+// memory, which on this GPU waits for every outstanding global load and
+// store: the prefetched weights and the output runs just written would be
+// drained at each barrier. These wait for LDS traffic alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// the same within one wavefront (its lanes read what its other lanes wrote)
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// output tensor t of the kernel arguments, picked without indexing them (an
+// indexed kernel argument is a memory load the store would have to wait for)
+template <typename T>
+__device__ __forceinline__ T* pick_out(T* const (&out)[5], int t) {
+  return t == 0 ? out[0] : t == 1 ? out[1] : t == 2 ? out[2] : t == 3 ? out[3] : out[4];
+}
 
 // one element kept in storage form in LDS
 __device__ __forceinline__ uint16_t raw(bf16_t v) { return v.bits; }
@@ -57,16 +82,49 @@ struct GemmArgs {
   int vec_a, vec_x, vec_o;   // 16-byte runs allowed for A rows, X rows, output rows
 };
 
+// 16 bytes of consecutive elements p[i .. ], the first `avail` of them real
+// and the rest zero (a whole vector load when allowed)
+template <typename T>
+__device__ __forceinline__ uint4 run16(const T* p, int64_t i, int avail, bool vec) {
+  constexpr int E = 16 / sizeof(T);
+  if (vec && avail >= E) return *reinterpret_cast<const uint4*>(p + i);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < avail) {
+      if constexpr (sizeof(T) == 2)
+        w[e >> 1] |= static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(p)[i + e])
+                     << (16 * (e & 1));
+      else
+        w[e] = __float_as_uint(reinterpret_cast<const float*>(p)[i + e]);
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
   using R = decltype(raw(T{}));   // uint16_t (bf16 bits) or float
-  constexpr int E = 16 / sizeof(T);   // elements in 16 bytes
-  constexpr int kTileBytes = 2 * kMT * kAP * sizeof(R);
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int E = 16 / sizeof(T);          // elements in 16 bytes
+  constexpr int KT = 128 / sizeof(T);        // K per tile: 128-byte rows
+  constexpr int AP = KT + 16 / sizeof(T);    // pitch of the weight tile [m][k]
+  // pixel tile: bf16 transposed [n][k] (an MFMA operand is 8 consecutive k),
+  // fp32 as loaded [k][n] (an operand is one value)
+  constexpr int BP = BF ? KT + 8 : kNT + 4;
+  constexpr int kABytes = kMT * AP * sizeof(R);
+  constexpr int kBBytes = (BF ? kNT : KT) * BP * sizeof(R);
   constexpr int kOutBytes = (kMT / 2) * kOP * sizeof(R);
-  __shared__ __align__(16) unsigned char smem[kTileBytes > kOutBytes ? kTileBytes : kOutBytes];
-  R* As = reinterpret_cast<R*>(smem);                 // [kMT][kAP]
-  R* Bs = As + kMT * kAP;                             // [kNT][kAP], transposed pixel tile
-  R* Os = reinterpret_cast<R*>(smem);                 // [kMT / 2][kOP], after the K loop
+  constexpr int kSmem = kABytes + kBBytes > kOutBytes ? kABytes + kBBytes : kOutBytes;
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  R* As = reinterpret_cast<R*>(smem);
+  R* Bs = reinterpret_cast<R*>(smem + kABytes);
+  R* Os = reinterpret_cast<R*>(smem);        // [kMT / 2][kOP], after the K loop
 
   const int M = a.M, K = a.K, N = a.N;
   const int nmt = (M + kMT - 1) / kMT;
@@ -83,67 +141,93 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += kKT) {
-    // weight tile [kMT][kKT]: kMT * kKT / E runs of E elements
+  // Each thread moves four 16-byte runs of the weight tile and four of the
+  // pixel tile per K tile; the next tile's runs are loaded into registers
+  // while the current one is multiplied.
+  //   weights: run c = tid + 256 q is row c / 8, k offset (c % 8) * E
+  //   pixels, bf16: rows 4 g .. 4 g + 3 (g = tid / 16), pixels 8 (tid % 16) ..
+  //   pixels, fp32: run c = tid + 256 q is k row c / 32, pixels (c % 32) * 4 ..
+  uint4 pa[4], px[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int c = tid; c < kMT * kKT / E; c += 256) {
-      const int r = c / (kKT / E), kk = (c % (kKT / E)) * E;
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
       const int m = m0 + r, k = k0 + kk;
-      R* dst = As + r * kAP + kk;
-      if (a.vec_a && m < M && k + E <= K) {
-        *reinterpret_cast<uint4*>(dst) =
-            *reinterpret_cast<const uint4*>(a.A + static_cast<int64_t>(m) * K + k);
-      } else {
+      pa[q] = run16(a.A, static_cast<int64_t>(m) * K + k, m < M ? K - k : 0, a.vec_a);
+    }
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          dst[e] = (m < M && k + e < K) ? raw(a.A[static_cast<int64_t>(m) * K + k + e]) : R(0);
+    for (int q = 0; q < 4; ++q) {
+      int k, n;
+      if constexpr (BF) {
+        k = k0 + 4 * (tid >> 4) + q;
+        n = n0 + 8 * (tid & 15);
+      } else {
+        const int c = tid + 256 * q;
+        k = k0 + c / (kNT / E);
+        n = n0 + (c % (kNT / E)) * E;
+      }
+      px[q] = run16(X, static_cast<int64_t>(k) * N + n, k < K ? N - n : 0, a.vec_x);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
+      *reinterpret_cast<uint4*>(As + r * AP + kk) = pa[q];
+    }
+    if constexpr (BF) {
+      // four k rows of eight pixels -> eight 8-byte runs of four k
+      const int kr = 4 * (tid >> 4), nl = 8 * (tid & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint2 v = make_uint2(half16(px[0], e) | (half16(px[1], e) << 16),
+                                   half16(px[2], e) | (half16(px[3], e) << 16));
+        *reinterpret_cast<uint2*>(Bs + (nl + e) * BP + kr) = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = tid + 256 * q, kr = c / (kNT / E), nn = (c % (kNT / E)) * E;
+        *reinterpret_cast<uint4*>(Bs + kr * BP + nn) = px[q];
       }
     }
-    // pixel tile [kKT][kNT] from X, stored transposed as [n][k]
-#pragma unroll
-    for (int c = tid; c < kKT * kNT / E; c += 256) {
-      const int kr = c / (kNT / E), nn = (c % (kNT / E)) * E;
-      const int k = k0 + kr, n = n0 + nn;
-      R v[E];
-      if (a.vec_x && k < K && n + E <= N) {
-        const uint4 q = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(k) * N + n);
-        *reinterpret_cast<uint4*>(v) = q;
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          v[e] = (k < K && n + e < N) ? raw(X[static_cast<int64_t>(k) * N + n + e]) : R(0);
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) Bs[(nn + e) * kAP + kr] = v[e];
-    }
-    __syncthreads();
-    if constexpr (sizeof(T) == 2) {
+  };
+
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    stash();
+    lds_barrier();
+    if (k0 + KT < K) fetch(k0 + KT);
+    if constexpr (BF) {
       // v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) .. +7]
-      // and B[8 (l / 16) .. +7][l % 16]
+      // and B[8 (l / 16) .. +7][l % 16]; two of them cover K = 64
       const int r = lane & 15, kq = (lane >> 4) * 8;
-      bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm + 16 * i + r) * kAP + kq);
+      for (int kh = 0; kh < KT; kh += 32) {
+        bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn + 16 * j + r) * kAP + kq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
+          fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm + 16 * i + r) * AP + kh + kq);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn + 16 * j + r) * BP + kh + kq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
     } else {
       // v_mfma_f32_16x16x4_f32: lane l holds A[l % 16][l / 16] and
       // B[l / 16][l % 16]; eight of them cover K = 32
       const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-      for (int ks = 0; ks < kKT; ks += 4) {
+      for (int ks = 0; ks < KT; ks += 4) {
         float fa[4], fb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = As[(wm + 16 * i + r) * kAP + ks + kq];
+        for (int i = 0; i < 4; ++i) fa[i] = As[(wm + 16 * i + r) * AP + ks + kq];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = Bs[(wn + 16 * j + r) * kAP + ks + kq];
+        for (int j = 0; j < 4; ++j) fb[j] = Bs[(ks + kq) * BP + wn + 16 * j + r];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -151,7 +235,7 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // bias, rounding to the storage type, staging half a tile (64 rows, the
@@ -177,14 +261,14 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
           }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // the half's rows to their output tensors, 16-byte runs
     for (int c = tid; c < 64 * kNT / E; c += 256) {
       const int r = c / (kNT / E), nn = (c % (kNT / E)) * E;
       const int m = m0 + h * 64 + r, n = n0 + nn;
       if (m >= M || n >= N) continue;
       const int t = m / a.Mt, mr = m - t * a.Mt;
-      T* dst = a.out[t] + (b * a.Mt + mr) * static_cast<int64_t>(N);
+      T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N);
       const R* src = Os + r * kOP + nn;
       if (a.vec_o && n + E <= N) {
         *reinterpret_cast<uint4*>(dst + n) = *reinterpret_cast<const uint4*>(src);
@@ -197,7 +281,235 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+  }
+}
+
+// Pixel-stationary variant for small K (all K rows of a 64-pixel tile fit
+// in LDS). A block owns one pixel tile, loads it once and loops over every M
+// tile; each wavefront owns 32 rows x 64 pixels of an M tile (2 x 4 MFMA
+// tiles). Weight fragments come straight from global memory (a few hundred
+// KB, resident in L2) into registers a whole M tile ahead; the pixel
+// operands come from the LDS tile. Each finished strip is staged in the
+// wavefront's own LDS slice and written as 16-byte row runs halfway through
+// the next tile.
+//
+// The memory counter the hardware waits on is in-order, and the compiler
+// can only count what is in flight on straight-line code: a conditional or
+// variable-length load or store anywhere makes it wait for everything,
+// prefetches included. So this kernel has none: K is a compile-time multiple
+// of the step, every load is an unconditional 16-byte run at a clamped
+// address, the prefetch of the next M tile always runs (the last tile
+// reloads itself), the bias is staged in LDS once, and each store is one
+// masked 16-byte run. The host takes this path only when K, M and every
+// tensor allow it.
+constexpr int kXsMaxSteps = 12;   // K steps of one M tile held in registers
+
+template <typename T>
+__host__ __device__ constexpr int xs_kstep() { return sizeof(T) == 2 ? 32 : 16; }
+
+// pixel tile width and output slice pitch of this variant: 64 pixels keep
+// its LDS near 67 KB, so two blocks share a CU and one block's loads and
+// waits overlap the other's products
+constexpr int kNX = 64;
+constexpr int kOX = kNX + 8;
+
+// LDS bytes: pixel tile (bf16 [n][k] with 8 spare k, fp32 [k][n]), four
+// 32-row output slices, the bias of all M rows in fp32
+template <typename T>
+__host__ __device__ constexpr size_t xs_lds_bytes(int K, int M) {
+  return (sizeof(T) == 2 ? static_cast<size_t>(kNX) * (K + 8) * 2
+                         : static_cast<size_t>(K) * (kNX + 4) * 4) +
+         static_cast<size_t>(4 * 32 * kOX) * sizeof(T) + static_cast<size_t>(M) * 4;
+}
+
+// two blocks per CU (LDS), two wavefronts per SIMD
+template <typename T, int NKS>
+__global__ __launch_bounds__(256, 2) void prologue_xs(GemmArgs<T> a) {
+  extern __shared__ __align__(16) unsigned char dsm[];
+  using R = decltype(raw(T{}));
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int E = 16 / sizeof(T);
+  constexpr int KS = xs_kstep<T>();
+  constexpr int K = NKS * KS;
+  constexpr int KP = BF ? K + 8 : kNX + 4;   // bf16 [kNX][KP]; fp32 [K][KP]
+  const int M = a.M, N = a.N;
+  R* Xs = reinterpret_cast<R*>(dsm);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  R* Os = Xs + (BF ? kNX * KP : K * KP) + wave * 32 * kOX;   // this wavefront's [32][kOX]
+  float* Bsh = reinterpret_cast<float*>(Xs + (BF ? kNX * KP : K * KP) + 4 * 32 * kOX);   // [M]
+  const int n0 = blockIdx.x * kNX;
+  const int64_t b = blockIdx.y;
+  const T* X = a.X + b * static_cast<int64_t>(K) * N;
+
+  // the pixel tile (pixels past N read a clamped, valid run; their outputs
+  // are not stored)
+  if constexpr (BF) {
+    const int nl = 8 * (tid & 7);
+    const int n = min(n0 + nl, N - E);
+#pragma unroll
+    for (int g0 = 0; g0 < K / 4; g0 += 32) {
+      const int g = g0 + (tid >> 3);
+      if (g < K / 4) {
+        uint4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(4 * g + q) * N + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint2*>(Xs + (nl + e) * KP + 4 * g) =
+              make_uint2(half16(v[0], e) | (half16(v[1], e) << 16),
+                         half16(v[2], e) | (half16(v[3], e) << 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c0 = 0; c0 < K * (kNX / E); c0 += 256) {
+      const int c = c0 + tid;
+      if (c < K * (kNX / E)) {
+        const int k = c / (kNX / E), nn = (c % (kNX / E)) * E;
+        const int n = min(n0 + nn, N - E);
+        *reinterpret_cast<uint4*>(Xs + k * KP + nn) =
+            *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(k) * N + n);
+      }
+    }
+  }
+  // the bias, once (the loop below then has no load it must wait for at once)
+  for (int i = tid; i < M; i += 256) Bsh[i] = a.bias ? g_ld(a.bias, i) : 0.f;
+  lds_barrier();
+
+  // the weight fragments of K step ks sit in slot ks; right after step ks of
+  // M tile mt is multiplied, slot ks is refilled with step ks of M tile
+  // mt + 1 (of mt itself on the last tile)
+  const int nmt = (M + kMT - 1) / kMT;
+  const int r16 = lane & 15, q = lane >> 4;
+  // bf16: lane holds k = 8q .. 8q+7 of the step; fp32: four consecutive k
+  // 4q .. 4q+3, used one per MFMA (any k order works if both operands agree)
+  auto wload = [&](int mt, int ks, int i) {
+    const int m = min(mt * kMT + 32 * wave + 16 * i + r16, M - 1);
+    return *reinterpret_cast<const uint4*>(a.A + static_cast<int64_t>(m) * K + ks * KS +
+                                           (BF ? 8 : 4) * q);
+  };
+  uint4 fa0[NKS], fa1[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    fa0[ks] = wload(0, ks, 0);
+    fa1[ks] = wload(0, ks, 1);
+  }
+  const int col = lane & 15, rq = (lane >> 4) * 4;
+  // the staged strip of M tile mt to its output rows (mt = -1: nothing);
+  // called halfway through the next tile's K loop, so that the stores are
+  // not still in flight at the next wait on the in-order memory counter
+  auto store_tile = [&](int mt) {
+#pragma unroll
+    for (int c0 = 0; c0 < 32 * kNX / E; c0 += 64) {
+      const int c = c0 + lane;
+      const int r = c / (kNX / E), nn = (c % (kNX / E)) * E;
+      const int m = mt * kMT + 32 * wave + r, n = n0 + nn;
+      const uint4 v = *reinterpret_cast<const uint4*>(Os + r * kOX + nn);
+      if (mt >= 0 && m < M && n < N) {
+        const int t = m / a.Mt, mr = m - t * a.Mt;
+        T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N) + n;
+        *reinterpret_cast<uint4*>(dst) = v;
+      }
+    }
+  };
+  for (int mt = 0; mt < nmt; ++mt) {
+    const int mn = min(mt + 1, nmt - 1);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kb = ks * KS;
+      if constexpr (BF) {
+        const bf16x8 A0 = __builtin_bit_cast(bf16x8, fa0[ks]);
+        const bf16x8 A1 = __builtin_bit_cast(bf16x8, fa1[ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 fb = *reinterpret_cast<const bf16x8*>(Xs + (16 * j + r16) * KP + kb + 8 * q);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, fb, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, fb, acc[1][j], 0, 0, 0);
+        }
+      } else {
+        const float a0[4] = {__uint_as_float(fa0[ks].x), __uint_as_float(fa0[ks].y),
+                             __uint_as_float(fa0[ks].z), __uint_as_float(fa0[ks].w)};
+        const float a1[4] = {__uint_as_float(fa1[ks].x), __uint_as_float(fa1[ks].y),
+                             __uint_as_float(fa1[ks].z), __uint_as_float(fa1[ks].w)};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float fb = Xs[(kb + 4 * q + s4) * KP + 16 * j + r16];
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[s4], fb, acc[0][j], 0, 0, 0);
+            acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[s4], fb, acc[1][j], 0, 0, 0);
+          }
+        }
+      }
+      fa0[ks] = wload(mn, ks, 0);
+      fa1[ks] = wload(mn, ks, 1);
+      if (ks == NKS / 2) store_tile(mt - 1);
+    }
+    lds_wave_sync();   // the slice's reads by store_tile precede the staging below
+    // bias, rounding, staging (lane holds rows 4 (l / 16) + e, column l % 16
+    // of each 16 x 16 tile) in this wavefront's own LDS slice
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * i + rq + e;
+        const float bv = Bsh[min(mt * kMT + 32 * wave + r, M - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[i][j][e] + bv;
+          if constexpr (BF)
+            Os[r * kOX + 16 * j + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+          else
+            Os[r * kOX + 16 * j + col] = v;
+        }
+      }
+    lds_wave_sync();
+  }
+  store_tile(nmt - 1);
+}
+
+template <typename T, int NKS>
+hipError_t launch_xs(const GemmArgs<T>& g, int64_t B, const char* name, hipStream_t stream,
+                     Tracer* tr) {
+  auto kern = prologue_xs<T, NKS>;
+  const size_t lds = xs_lds_bytes<T>(NKS * xs_kstep<T>(), g.M);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((g.N + kNX - 1) / kNX), static_cast<unsigned>(B));
+  tr->before(stream, name, B);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, g);
+  tr->after(stream);
+  return hipGetLastError();
+}
+
+// the pixel-stationary kernel for this K, or hipErrorInvalidValue when K is
+// not a multiple of the step up to kXsMaxSteps steps
+template <typename T>
+hipError_t launch_xs_k(const GemmArgs<T>& g, int64_t B, const char* name, hipStream_t stream,
+                       Tracer* tr) {
+  switch (g.K / xs_kstep<T>()) {
+    case 1: return launch_xs<T, 1>(g, B, name, stream, tr);
+    case 2: return launch_xs<T, 2>(g, B, name, stream, tr);
+    case 3: return launch_xs<T, 3>(g, B, name, stream, tr);
+    case 4: return launch_xs<T, 4>(g, B, name, stream, tr);
+    case 5: return launch_xs<T, 5>(g, B, name, stream, tr);
+    case 6: return launch_xs<T, 6>(g, B, name, stream, tr);
+    case 7: return launch_xs<T, 7>(g, B, name, stream, tr);
+    case 8: return launch_xs<T, 8>(g, B, name, stream, tr);
+    case 9: return launch_xs<T, 9>(g, B, name, stream, tr);
+    case 10: return launch_xs<T, 10>(g, B, name, stream, tr);
+    case 11: return launch_xs<T, 11>(g, B, name, stream, tr);
+    case 12: return launch_xs<T, 12>(g, B, name, stream, tr);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -222,6 +534,11 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
   bool vo = N % E == 0;
   for (int t = 0; t < nout; ++t) vo = vo && al16(outs[t]);
   g.vec_o = vo;
+  // the pixel-stationary kernel where its straight-line conditions hold
+  const int ks = xs_kstep<T>();
+  if (K % ks == 0 && K / ks <= kXsMaxSteps && xs_lds_bytes<T>(K, M) <= kXsMaxLds &&
+      M % 32 == 0 && g.vec_a && g.vec_x && g.vec_o)
+    return launch_xs_k<T>(g, B, name, stream, tr);
   const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT);
   const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(B));
   tr->before(stream, name, B);

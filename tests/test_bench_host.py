@@ -11,7 +11,7 @@ from linear_spatial_propagation_line_amd.inputs import WORKLOADS
 KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "tp_vfwd",
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
-           "dir_vert", "dir_tr_in", "dir_tr_acc"]
+           "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params"]
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -19,16 +19,17 @@ KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "
 def test_input_sets_and_qmin(name, bwd):
     w = WORKLOADS[name]
     s = 4 if w.dtype == "f32" else 2
-    if w.per_direction:
+    if w.per_direction or w.prologue_cin:
         if bwd:
             with pytest.raises(ValueError):
                 bench.qmin_per_pixel(w, bwd)
             return
-        assert bench.qmin_per_pixel(w, bwd) == (2 + 5 * w.ndirs) * s
+        want = (2 + 5 * w.ndirs) * s if w.per_direction else (w.prologue_cin / w.C + 1) * s
+        assert bench.qmin_per_pixel(w, bwd) == want
     n = bench.input_sets(w, bwd)
     assert isinstance(n, int) and 1 <= n <= 8
     q = bench.qmin_per_pixel(w, bwd)
-    if w.per_direction:
+    if w.per_direction or w.prologue_cin:
         return
     if w.cl == w.C:
         assert q == (13 if bwd else 7) * s
@@ -74,3 +75,18 @@ def test_every_traced_kernel_name_has_design_bytes():
     assert {"plane_kernel64", "tp_vfwd", "bwd_adj", "tp_lgcopy"} <= names, names
     for n in names:
         assert n in KERNELS, f"traced kernel {n} missing from the list"
+
+
+def test_prologue_work():
+    """Flops and bytes of the prologue on the 2048x1024 unit: two products of
+    2 * pixels * C * (Cin + 5C) flops; x_in read, six tensors written."""
+    w = WORKLOADS["t2i_2048x1024_mod"]
+    flops, nbytes = bench.prologue_work(w)
+    px = 2048 * 1024
+    assert flops == 2.0 * px * 320 * (320 + 1600)
+    assert nbytes == (px * (320 + 6 * 320) + 320 * 320 + 5 * 320 * 320 + 6 * 320) * 2
+    # at MI355X peaks the bf16 products take less time than the bytes
+    assert flops / 2500e12 < nbytes / 8000e9
+    wd = WORKLOADS["dit_16x16_mod"]
+    f2, b2 = bench.prologue_work(wd)
+    assert f2 / 2500e12 > b2 / 8000e9     # C = 1152: MFMA-bound
