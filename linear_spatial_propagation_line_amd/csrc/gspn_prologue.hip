@@ -107,8 +107,21 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
+// 16 bytes as a plain vector of four words (arrays of these stay in
+// registers; arrays of the uint4 struct copied whole may not)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 vec4(const uint4& v) { return u32x4{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ uint32_t half16(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// FULL: M and N multiples of 128, K a multiple of the K tile, every tensor in
+// 16-byte runs. Then no access needs a bounds check, and the code between
+// memory waits is straight-line, so the compiler can count what is in
+// flight instead of draining the in-order memory counter at every check.
+template <typename T, bool FULL>
+__global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   using R = decltype(raw(T{}));   // uint16_t (bf16 bits) or float
   constexpr bool BF = sizeof(T) == 2;
   constexpr int E = 16 / sizeof(T);          // elements in 16 bytes
@@ -128,8 +141,15 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
 
   const int M = a.M, K = a.K, N = a.N;
   const int nmt = (M + kMT - 1) / kMT;
-  const int m0 = static_cast<int>(blockIdx.x % nmt) * kMT;
-  const int n0 = static_cast<int>(blockIdx.x / nmt) * kNT;
+  // Workgroups are dealt to the 8 XCDs in turn, each with its own L2. Tile
+  // t runs on XCD t / per, so consecutive tiles -- the M tiles that share a
+  // pixel tile -- meet in one L2.
+  const int tiles = nmt * ((N + kNT - 1) / kNT);
+  const int per = (tiles + 7) / 8;
+  const int tile = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  if (tile >= tiles) return;
+  const int m0 = (tile % nmt) * kMT;
+  const int n0 = (tile / nmt) * kNT;
   const int64_t b = blockIdx.y;
   const T* X = a.X + b * static_cast<int64_t>(K) * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -147,13 +167,16 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
   //   weights: run c = tid + 256 q is row c / 8, k offset (c % 8) * E
   //   pixels, bf16: rows 4 g .. 4 g + 3 (g = tid / 16), pixels 8 (tid % 16) ..
   //   pixels, fp32: run c = tid + 256 q is k row c / 32, pixels (c % 32) * 4 ..
-  uint4 pa[4], px[4];
+  u32x4 pa[4], px[4];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
       const int m = m0 + r, k = k0 + kk;
-      pa[q] = run16(a.A, static_cast<int64_t>(m) * K + k, m < M ? K - k : 0, a.vec_a);
+      if constexpr (FULL)
+        pa[q] = *reinterpret_cast<const u32x4*>(a.A + static_cast<int64_t>(m) * K + k);
+      else
+        pa[q] = vec4(run16(a.A, static_cast<int64_t>(m) * K + k, m < M ? K - k : 0, a.vec_a));
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -166,14 +189,17 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
         k = k0 + c / (kNT / E);
         n = n0 + (c % (kNT / E)) * E;
       }
-      px[q] = run16(X, static_cast<int64_t>(k) * N + n, k < K ? N - n : 0, a.vec_x);
+      if constexpr (FULL)
+        px[q] = *reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(k) * N + n);
+      else
+        px[q] = vec4(run16(X, static_cast<int64_t>(k) * N + n, k < K ? N - n : 0, a.vec_x));
     }
   };
   auto stash = [&]() {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
-      *reinterpret_cast<uint4*>(As + r * AP + kk) = pa[q];
+      *reinterpret_cast<u32x4*>(As + r * AP + kk) = pa[q];
     }
     if constexpr (BF) {
       // four k rows of eight pixels -> eight 8-byte runs of four k
@@ -188,7 +214,7 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = tid + 256 * q, kr = c / (kNT / E), nn = (c % (kNT / E)) * E;
-        *reinterpret_cast<uint4*>(Bs + kr * BP + nn) = px[q];
+        *reinterpret_cast<u32x4*>(Bs + kr * BP + nn) = px[q];
       }
     }
   };
@@ -197,7 +223,10 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
   for (int k0 = 0; k0 < K; k0 += KT) {
     stash();
     lds_barrier();
-    if (k0 + KT < K) fetch(k0 + KT);
+    if constexpr (FULL)
+      fetch(min(k0 + KT, K - KT));   // the last tile fetches itself again
+    else if (k0 + KT < K)
+      fetch(k0 + KT);
     if constexpr (BF) {
       // v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) .. +7]
       // and B[8 (l / 16) .. +7][l % 16]; two of them cover K = 64
@@ -266,11 +295,11 @@ __global__ __launch_bounds__(256) void prologue_gemm(GemmArgs<T> a) {
     for (int c = tid; c < 64 * kNT / E; c += 256) {
       const int r = c / (kNT / E), nn = (c % (kNT / E)) * E;
       const int m = m0 + h * 64 + r, n = n0 + nn;
-      if (m >= M || n >= N) continue;
+      if (!FULL && (m >= M || n >= N)) continue;
       const int t = m / a.Mt, mr = m - t * a.Mt;
       T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N);
       const R* src = Os + r * kOP + nn;
-      if (a.vec_o && n + E <= N) {
+      if (FULL || (a.vec_o && n + E <= N)) {
         *reinterpret_cast<uint4*>(dst + n) = *reinterpret_cast<const uint4*>(src);
       } else {
 #pragma unroll
@@ -540,9 +569,12 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
       M % 32 == 0 && g.vec_a && g.vec_x && g.vec_o)
     return launch_xs_k<T>(g, B, name, stream, tr);
   const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT);
-  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(B));
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8), static_cast<unsigned>(B));
+  const bool full = M % kMT == 0 && N % kNT == 0 && K % (128 / static_cast<int>(sizeof(T))) == 0 &&
+                    g.vec_a && g.vec_x && g.vec_o;
+  auto kern = full ? prologue_gemm<T, true> : prologue_gemm<T, false>;
   tr->before(stream, name, B);
-  hipLaunchKernelGGL(prologue_gemm<T>, grid, dim3(256), 0, stream, g);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g);
   tr->after(stream);
   return hipGetLastError();
 }
