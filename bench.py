@@ -62,6 +62,7 @@ PLAN_SOURCES = {
     "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
+    "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
     "prologue": ("gspn_prologue.hip", "gspn_device.hpp"),
     "module": ("gspn_prologue.hip", "gspn_plane.hip", "gspn_band.hip", "gspn_tpipe.hip",
@@ -146,6 +147,14 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
       bband_kernel (local groups): seven inputs read in the vertical and again
           in the horizontal rounds, five fp32 partial sums written and read
           back, six gradients written -> 20 s + 40
+      backward pipeline for large planes (states and error terms of the first
+      sweep of an axis stored as fp32 pairs, 8 bytes per pixel; the
+      column-major copy = lambda x and u gy in fp32 + 3 logits):
+          bt_vA  7 s inputs + 8 states + (8 + 3 s) copy write
+          bt_hA  (8 + 3 s) copy read + 8 states
+          bt_hB  (8 + 3 s) copy read + 8 states read + 20 horizontal parts
+          bt_vB  7 s inputs + 8 states read + 20 horizontal parts + 6 s out
+          (no horizontal direction: no copy, no parts, no bt_hA / bt_hB)
     Per-direction parameters (one pass per direction; horizontal directions
     run over transposed copies):
       dir_vert  x and the direction's lambda, l0, l1, l2, u read (6 s), the
@@ -180,6 +189,10 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "bwd_transpose": 2 * 7 * s if planes == w.B * w.C else 2 * 4,
         "bwd_finish": 20 + 9 * s,
         "bband_kernel": 20 * s + 40,
+        "bt_vA": 7 * s + 8 + (8 + 3 * s if hz else 0),
+        "bt_hA": 8 + 3 * s + 8,
+        "bt_hB": 8 + 3 * s + 8 + 20,
+        "bt_vB": 7 * s + 8 + (20 if hz else 0) + 6 * s,
         "bwd_reduce_logits": 12 + 3 * s * w.cl / w.C,
         "dir_vert": 6 * s + (0 if first else 4) + (s if last else 4),
         "dir_tr_in": 2 * s,

@@ -310,7 +310,7 @@ void keep_trace(const gspn::Tracer& tr) {
 }
 
 // ---- backward pass ---------------------------------------------------------
-enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kStream };
+enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream };
 struct BChecked;
 BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
                         int dtype);
@@ -345,13 +345,14 @@ BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mas
     r.status = f.status;
     return r;
   }
-  // GSPN_FORCE_BWD_PLAN=plane|band|stream picks a path for testing when the
-  // shape allows it; otherwise the first path that fits, in that order
+  // GSPN_FORCE_BWD_PLAN=plane|band|tpipe|stream picks a path for testing when
+  // the shape allows it; otherwise the first path that fits, in that order
   const char* force = std::getenv("GSPN_FORCE_BWD_PLAN");
   const bool f_plane = force && !std::strcmp(force, "plane");
   const bool f_band = force && !std::strcmp(force, "band");
+  const bool f_tpipe = force && !std::strcmp(force, "tpipe");
   const bool f_stream = force && !std::strcmp(force, "stream");
-  const bool any = !f_plane && !f_band && !f_stream;
+  const bool any = !f_plane && !f_band && !f_tpipe && !f_stream;
   if ((any || f_plane) && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? BPlan::kPlane16 : BPlan::kPlane64;
     return r;
@@ -359,6 +360,11 @@ BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mas
   if ((any || f_band) && gspn::bband_fits(H, W, G)) {
     r.plan = BPlan::kBand;
     r.ws_bytes = gspn::bband_workspace_bytes(B * C, H, W, mask);
+    return r;
+  }
+  if ((any || f_tpipe) && gspn::btpipe_fits(H, W)) {
+    r.plan = BPlan::kTpipe;
+    r.ws_bytes = gspn::bwd_tpipe_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
     return r;
   }
   if (f_plane && gspn::plane_fits(H, W)) {
@@ -375,6 +381,7 @@ const char* bplan_str(BPlan p) {
     case BPlan::kPlane16: return "bwd_plane16";
     case BPlan::kPlane64: return "bwd_plane64";
     case BPlan::kBand: return "bwd_band";
+    case BPlan::kTpipe: return "bwd_tpipe";
     case BPlan::kStream: return "bwd_stream";
     default: return "invalid";
   }
@@ -398,16 +405,18 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
   const size_t es = elem_size(dtype);
   const void* ins[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, gy};
   const void* outs[6] = {dx, dlogits[0], dlogits[1], dlogits[2], dlam, du};
-  bool vec4 = true;
+  bool vec4 = true, pair = true;
   for (const void* p : ins) {
     if (reinterpret_cast<uintptr_t>(p) % es)
       return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
     if (reinterpret_cast<uintptr_t>(p) % (4 * es)) vec4 = false;
+    if (reinterpret_cast<uintptr_t>(p) % (2 * es)) pair = false;
   }
   for (const void* p : outs) {
     if (reinterpret_cast<uintptr_t>(p) % es)
       return fail(GSPN_E_ALIGN, "gradient pointer not aligned to its element size");
     if (reinterpret_cast<uintptr_t>(p) % (4 * es)) vec4 = false;
+    if (reinterpret_cast<uintptr_t>(p) % (2 * es)) pair = false;
   }
   // the three logits and their gradients have Cl channels, the rest C
   const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
@@ -438,6 +447,7 @@ gspn_status check_all_bwd(const void* x, const void* const w_logits[3], const vo
   pr->G = G;
   pr->dtype = dtype;
   pr->aligned_vec4 = vec4;
+  pr->aligned_pair = pair;
   pr->Cl = Cl;
   pr->dlw = nullptr;
   return GSPN_OK;
@@ -456,6 +466,12 @@ gspn_status run_bwd(gspn::BwdProblem pr, const BChecked& chk, void* ws, hipStrea
       break;
     case BPlan::kBand:
       e = gspn::launch_bband(pr, ws, stream, &tr);
+      break;
+    case BPlan::kTpipe:
+      // the pipeline moves element pairs; tensors at odd element offsets
+      // take the streaming path, whose workspace fits in the pipeline's
+      e = pr.aligned_pair ? gspn::launch_bwd_tpipe(pr, ws, stream, &tr)
+                          : gspn::launch_bwd_stream(pr, ws, stream, &tr);
       break;
     case BPlan::kStream:
       e = gspn::launch_bwd_stream(pr, ws, stream, &tr);

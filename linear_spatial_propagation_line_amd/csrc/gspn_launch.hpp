@@ -46,6 +46,7 @@ struct BwdProblem {
   int64_t G;
   gspn_dtype dtype;
   bool aligned_vec4;   // every pointer aligned to 4 elements
+  bool aligned_pair;   // every pointer aligned to 2 elements
   int64_t Cl;          // logit channels (Cl divides C; Cl == C: unshared)
   // Cl < C: the kernels write each plane's logit gradients here in fp32
   // ([3][B*C*H*W]) and bwd_reduce_logits sums each group into dl[]
@@ -83,6 +84,13 @@ hipError_t launch_band(const Problem& pr, hipStream_t stream, Tracer* tr);
 
 // large-plane transpose pipeline (gspn_tpipe.hip)
 bool tpipe_fits(int64_t H, int64_t W);
+// Plane groups of the large-plane pipelines: each group's chain of launches
+// runs on its own stream (the caller's, then helper streams), so that one
+// group's tail overlaps the next launch of another.
+constexpr int kMaxGroups = 4;
+int cu_count();                        // compute units of the current device
+hipStream_t aux_stream(int i);         // helper stream i < kMaxGroups - 1 of the device
+int tpipe_groups(int64_t planes);      // number of plane groups for a launch
 size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt);
 hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
@@ -126,5 +134,12 @@ hipError_t launch_bwd_reduce_logits(const BwdProblem& pr, hipStream_t stream, Tr
 size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
                                   gspn_dtype dt);
 hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
+
+// backward pass, large-plane pipeline (gspn_bwd_tpipe.hip): planes with both
+// sides even, W <= 1024, H <= 2048, every pointer aligned to 2 elements
+bool btpipe_fits(int64_t H, int64_t W);
+size_t bwd_tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                 gspn_dtype dt);
+hipError_t launch_bwd_tpipe(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
 }  // namespace gspn

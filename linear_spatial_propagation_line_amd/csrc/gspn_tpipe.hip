@@ -708,7 +708,6 @@ TpLayout tp_layout(int64_t planes, int64_t H, int64_t W, size_t es) {
 }
 }  // namespace
 
-namespace {
 // compute units of the current device (cached per device)
 int cu_count() {
   static std::mutex mu;
@@ -727,7 +726,6 @@ int cu_count() {
 
 // up to three non-blocking, default-priority helper streams per device,
 // created on first use and kept for the life of the process
-constexpr int kMaxGroups = 4;
 hipStream_t aux_stream(int i) {
   static std::mutex mu;
   static hipStream_t cache[64][kMaxGroups - 1] = {};
@@ -749,7 +747,6 @@ int tpipe_groups(int64_t planes) {
   const int cus = cu_count();
   return (planes > cus && planes < 2 * cus) ? 2 : 1;
 }
-}  // namespace
 
 size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt) {
   return tp_layout(planes, H, W, dt == GSPN_F32 ? 4 : 2).total;

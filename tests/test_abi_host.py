@@ -197,17 +197,64 @@ def test_backward_plans(LB, monkeypatch):
     assert g.backward_plan_name(64, 96, 56, 56) == "bwd_plane64"
     assert g.backward_plan_name(32, 1152, 16, 16, dtype=1) == "bwd_plane16"
     assert g.backward_plan_name(1, 1, 65, 8) == "bwd_stream"
-    assert g.backward_plan_name(1, 320, 2048, 1024, dtype=1) == "bwd_stream"
+    assert g.backward_plan_name(1, 320, 2048, 1024, dtype=1) == "bwd_tpipe"
     assert g.backward_plan_name(1, 1, 0, 4) == "invalid"
     assert g.backward_plan_name(16, 192, 128, 128, group_rows=8) == "bwd_band"
-    assert g.backward_plan_name(16, 192, 128, 128, group_rows=9) == "bwd_stream"
-    assert g.backward_plan_name(1, 1, 600, 100, group_rows=4) == "bwd_stream"   # H > 512
+    assert g.backward_plan_name(16, 192, 128, 128, group_rows=9) == "bwd_tpipe"
+    assert g.backward_plan_name(1, 1, 600, 100, group_rows=4) == "bwd_tpipe"   # H > 512
+    # the pipeline: both sides even, H <= 2048, W <= 1024
+    assert g.backward_plan_name(1, 1, 2050, 100) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 100, 1026) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 100, 1025) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 2048, 2) == "bwd_tpipe"
     assert g.backward_workspace_bytes(2, 3, 128, 128, group_rows=8) == 5 * 6 * 128 * 128 * 4
     assert g.backward_workspace_bytes(2, 3, 128, 128, dirs=g.T2B, group_rows=8) == 0
     assert g.backward_workspace_bytes(64, 96, 56, 56) == 0
     monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
     assert g.backward_plan_name(64, 96, 56, 56) == "bwd_stream"
     assert g.backward_workspace_bytes(1, 2, 8, 8, dirs=g.T2B | g.B2T) == 6 * 2 * 64 * 4
+    monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "tpipe")
+    assert g.backward_plan_name(64, 96, 56, 56) == "bwd_tpipe"
+    assert g.backward_plan_name(1, 1, 65, 8) == "bwd_stream"
+
+
+def _al(v):
+    return (v + 255) // 256 * 256
+
+
+def _stream_ws(planes, H, W, dirs, es):
+    px = planes * H * W
+    hz = bool(dirs & 12)
+    accs = hz or bin(dirs).count("1") > 1
+    return (_al(px * 4) + _al(5 * px * 4 if accs else 0) + _al(7 * px * es if hz else 0)
+            + _al(5 * px * 4 if hz else 0))
+
+
+def _pipe_ws(planes, H, W, dirs, es):
+    """The pipeline's regions: states of the two first sweeps (8 bytes a
+    pixel each), the column-major copy (rows padded to 16), the five fp32
+    horizontal parts by groups of 8 rows."""
+    px = planes * H * W
+    hz = bool(dirs & 12)
+    Hp, ng = (H + 15) // 16 * 16, (H + 7) // 8
+    cp = planes * W * Hp
+    if not hz:
+        return _al(px * 8)
+    return (_al(px * 8) + 2 * _al(cp * 4) + _al(3 * cp * es) + _al(px * 8)
+            + _al(5 * planes * ng * 8 * W * 4))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 130, 96), (3, 1, 66, 1024), (1, 1, 2048, 2)])
+@pytest.mark.parametrize("dirs", [15, 3, 12, 1])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_backward_pipeline_workspace(shape, dirs, dtype):
+    """The pipeline asks for the larger of its own regions and the streaming
+    path's, which serves calls whose tensors start at odd element offsets."""
+    B, C, H, W = shape
+    es = 4 if dtype == 0 else 2
+    assert g.backward_plan_name(B, C, H, W, dirs, 0, dtype) == "bwd_tpipe"
+    want = max(_pipe_ws(B * C, H, W, dirs, es), _stream_ws(B * C, H, W, dirs, es))
+    assert g.backward_workspace_bytes(B, C, H, W, dirs, 0, dtype) == want
 
 
 @pytest.mark.parametrize("cl", [0, -1, 3])

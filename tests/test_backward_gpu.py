@@ -231,3 +231,39 @@ def test_band_path(force_bwd_plan, shape, dtype):
             got = run_bwd(inp, gy, mask, G)
             assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
                                f"band {shape} mask={mask} G={G}")
+
+
+PIPE_SHAPES = [(1, 2, 66, 40), (2, 1, 130, 96), (1, 1, 96, 130), (1, 1, 2, 2), (1, 1, 2, 70),
+               (1, 1, 70, 2), (1, 2, 18, 22), (1, 1, 250, 34), (1, 1, 34, 250)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", PIPE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pipeline_path(force_bwd_plan, shape, dtype):
+    """Large-plane backward pipeline forced onto small even planes: one row
+    or column pair, rows not a multiple of the 4-row group of the horizontal
+    parts, prefetch rings longer than the plane; every direction-mask family,
+    global and local groups (a restart line on either side of a pair)."""
+    force_bwd_plan("tpipe")
+    B, C, H, W = shape
+    assert g.backward_plan_name(B, C, H, W) == "bwd_tpipe"
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, 90 + H + W, B=B, C=C, H=H, W=W)
+    for G in (0, 1, 3, 8):
+        masks = (15, 1, 2, 4, 8, 3, 12, 5, 10) if G in (0, 3) else (15,)
+        for mask in masks:
+            got = run_bwd(inp, gy, mask, G)
+            assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
+                               f"pipeline {shape} mask={mask} G={G}")
+
+
+def test_pipeline_matches_streaming_path(force_bwd_plan):
+    """Both large-plane backward paths on the same bf16 planes agree to the
+    bf16 bound (they round differently)."""
+    inp, gy = case("t2i_2048x1024", 93, B=1, C=3, H=256, W=192)
+    force_bwd_plan("tpipe")
+    a = run_bwd(inp, gy, 15, 0)
+    force_bwd_plan("stream")
+    b = run_bwd(inp, gy, 15, 0)
+    ref = {k: a[k].double().cpu().numpy() for k in GRAD_NAMES}
+    assert_grad_parity(b, ref, "pipeline vs stream")

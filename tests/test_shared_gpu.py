@@ -20,7 +20,8 @@ CASES = [
     ((1, 4, 56, 56), 0, "plane64", "bwd_plane64"),
     ((1, 4, 128, 128), 8, "band", "bwd_band"),
     ((1, 6, 100, 70), 5, "band", "bwd_band"),
-    ((1, 4, 130, 96), 0, "tpipe", "bwd_stream"),
+    ((1, 4, 130, 96), 0, "tpipe", "bwd_tpipe"),
+    ((1, 4, 66, 40), 20, "tpipe", "bwd_tpipe"),
     ((1, 4, 65, 80), 0, "stream", "bwd_stream"),
 ]
 
