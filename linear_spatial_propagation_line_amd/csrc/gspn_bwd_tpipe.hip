@@ -25,10 +25,9 @@
 //          stored per pixel.
 //   bt_hB  right->left over the copy: h of right->left and e of left->right;
 //          with bt_hA's values it forms the horizontal parts of d(lambda x),
-//          the three logit gradients and sum h, written in fp32 in groups of
-//          8 rows (a column pair of a group is 64 contiguous bytes: taller
-//          groups make bt_hB's stores whole, shorter ones keep bt_vB's reads
-//          in L2; 8 rows measured best).
+//          the three logit gradients and sum h, written in fp32 in tiles of
+//          4 rows x 4 columns; the right column pair of a tile waits in LDS
+//          for its left pair, so each thread writes 32 contiguous bytes.
 //   bt_vB  bottom->top over the row-major inputs: h of bottom->top and e of
 //          top->bottom; with bt_vA's values and the horizontal parts it
 //          writes the six gradients once.
@@ -48,7 +47,12 @@ namespace gspn {
 
 namespace {
 
-constexpr int kGrp = 8;          // rows per group of the horizontal parts
+// The horizontal parts are stored in tiles of 4 rows x 4 columns (64 bytes,
+// row-major inside): bt_hB writes a thread's two rows of a tile as 32
+// contiguous bytes, and bt_vB reads a tile's rows on consecutive steps, so
+// each tile is used while it is still in L2.
+constexpr int kGrp = 4;          // rows per tile
+constexpr int kTc = 4;           // columns per tile
 constexpr int kNone = 1 << 30;
 
 // two adjacent elements in their storage form
@@ -292,9 +296,8 @@ struct BtArgs {
   float* ugt;        // same layout, u gy
   T* lgt;            // [3][planes][W/2][Hp][2] logits
   float4* hh;        // [planes][W][H/2]: (h_L2R A, B, e_R2L A, B) per row pair
-  float* part;       // [5][planes][ng][W/2][kGrp][2]: horizontal d(lambda x),
-                     // dl0, dl1, dl2, sum h, by groups of kGrp rows and
-                     // column pairs
+  float* part;       // [5][planes][ng][ceil(W/4)][kGrp][kTc]: horizontal
+                     // d(lambda x), dl0, dl1, dl2, sum h in 4 x 4 tiles
   int H, W, G, Hp, ng;
   float fT, fB, fL, fR;   // 1 for the directions in the mask, else 0
   int64_t lg_stride;      // elements between the three logit copies
@@ -495,22 +498,31 @@ __global__ __launch_bounds__(1024) void bt_hA(BtArgs<T> a) {
 
 // bt_hB: right->left, h of right->left and e of left->right; writes the
 // horizontal parts of the gradients
+size_t bt_hb_lds_bytes(unsigned threads) {
+  const size_t slots = threads + 2;
+  return 2 * slots * sizeof(float4) + 2 * slots * sizeof(float2) + 20 * threads * sizeof(float);
+}
+
 template <typename T>
 __global__ __launch_bounds__(1024) void bt_hB(BtArgs<T> a) {
-  __shared__ float4 lbuf[2 * (1024 + 2)];
-  // left->right states of the previous column (in that direction's order)
-  // of the neighbouring rows
-  __shared__ float2 nbuf[2 * (1024 + 2)];
-  constexpr int PP = 1;   // column pairs in flight (registers)
+  // the line, the left->right states of the previous column (in that
+  // direction's order) of the neighbouring rows, and each thread's outputs
+  // of the right column pair of a tile until its left pair is done
+  extern __shared__ float4 dyn[];
+  const int nt = blockDim.x, slots = nt + 2;
+  float4* lbuf = dyn;
+  float2* nbuf = reinterpret_cast<float2*>(dyn + 2 * slots);
+  float* stash = reinterpret_cast<float*>(nbuf + 2 * slots);   // [20][nt]
   using Q = Four<T>;
-  const int H = a.H, W = a.W, H2 = H / 2, W2 = W / 2;
+  const int H = a.H, W = a.W, H2 = H / 2, W2 = W / 2, nq = (W2 + 1) / 2;
   const int t = threadIdx.x, o0 = 2 * t;
   const bool act = o0 < H;
   const int tl = act ? t : 0, ol = 2 * tl;
   const int64_t plane = a.plane0 + blockIdx.x;
-  Line ln{lbuf, static_cast<int>(blockDim.x) + 2, 0};
-  for (int i = t; i < 2 * ln.slots; i += blockDim.x) nbuf[i] = make_float2(0.f, 0.f);
-  line_clear(lbuf, 2 * ln.slots);
+  Line ln{lbuf, slots, 0};
+  for (int i = t; i < 2 * slots; i += nt) nbuf[i] = make_float2(0.f, 0.f);
+  for (int i = 0; i < 20; ++i) stash[i * nt + t] = 0.f;
+  line_clear(lbuf, 2 * slots);
   const float mA0 = o0 > 0 ? 1.f : 0.f;
   const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
   const float4* hh = a.hh + plane * W * H2 + tl;
@@ -534,52 +546,74 @@ __global__ __launch_bounds__(1024) void bt_hB(BtArgs<T> a) {
     v.sp = *reinterpret_cast<const float2*>(hh + static_cast<int64_t>(max(2 * cc - 1, 0)) * H2);
     return v;
   };
-  // rows o0, o0 + 1 of column c in the horizontal parts
-  float* part = a.part + (plane * a.ng + ol / kGrp) * W2 * (2 * kGrp) + (ol % kGrp) * 2;
+  // rows o0, o0 + 1 of this thread in tile 0 of its row group
+  float* part = a.part + (plane * a.ng + ol / kGrp) * nq * (kGrp * kTc) + (ol % kGrp) * kTc;
 
-  In ring[PP];
-#pragma unroll
-  for (int j = 0; j < PP; ++j) ring[j] = load_pair(W2 - 1 - j);
+  // one pair in flight: registers
+  In ring = load_pair(W2 - 1);
   Sweep s{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   EndsDown rb = ends_down(W, a.G);     // right->left restarts
   StartsDown ra = starts_down(W, a.G); // left->right restarts
-  auto block = [&](int cb, auto tail) {
-    constexpr bool TAIL = decltype(tail)::value;
+  // columns 2 cp + 1, 2 cp: the outputs of rows o0, o0 + 1 (index: even / odd column)
+  auto pair = [&](int cp, Grad (&gA)[2], Grad (&gB)[2]) {
+    const In v = ring;
+    ring = load_pair(cp - 1);
 #pragma unroll
-    for (int j = 0; j < PP; ++j) {
-      const int cp = cb - j;
-      if (!TAIL || cp >= 0) {
-        const In v = ring[j];
-        ring[j] = load_pair(cp - PP);
-        Grad gA[2], gB[2];   // rows o0, o0 + 1 of columns 2 cp, 2 cp + 1
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int odd = 1 - k;
-          const int c = 2 * cp + odd;
-          const WeightSlopes qa = make_weight_slopes(Q::get(v.c.g0, 0, odd), Q::get(v.c.g1, 0, odd),
-                                                     Q::get(v.c.g2, 0, odd), mA0, 1.f);
-          const WeightSlopes qb = make_weight_slopes(Q::get(v.c.g0, 1, odd), Q::get(v.c.g1, 1, odd),
-                                                     Q::get(v.c.g2, 1, odd), 1.f, mB2);
-          const bool rbc = rb.at(c), rac = ra.at(c);
-          const float2 up = k ? v.sp : make_float2(v.st[1].x, v.st[1].y);
-          sweep_b(s, ln, t, act, qa, qb, quad(v.c.lx, 0, odd), quad(v.c.lx, 1, odd),
-                  quad(v.c.ug, 0, odd), quad(v.c.ug, 1, odd), rbc, rac, v.st[k], 0.f, up.x,
-                  up.y, 0.f, a.fL, a.fR, gA[odd], gB[odd], nbuf);
-        }
-        if (act) {
-          float* d = part + static_cast<int64_t>(cp) * (2 * kGrp);
-          *reinterpret_cast<float4*>(d) = make_float4(gA[0].dphi, gA[1].dphi, gB[0].dphi, gB[1].dphi);
-          *reinterpret_cast<float4*>(d + a.part_stride) = make_float4(gA[0].d0, gA[1].d0, gB[0].d0, gB[1].d0);
-          *reinterpret_cast<float4*>(d + 2 * a.part_stride) = make_float4(gA[0].d1, gA[1].d1, gB[0].d1, gB[1].d1);
-          *reinterpret_cast<float4*>(d + 3 * a.part_stride) = make_float4(gA[0].d2, gA[1].d2, gB[0].d2, gB[1].d2);
-          *reinterpret_cast<float4*>(d + 4 * a.part_stride) = make_float4(gA[0].hs, gA[1].hs, gB[0].hs, gB[1].hs);
-        }
-      }
+    for (int k = 0; k < 2; ++k) {
+      const int odd = 1 - k;
+      const int c = 2 * cp + odd;
+      const WeightSlopes qa = make_weight_slopes(Q::get(v.c.g0, 0, odd), Q::get(v.c.g1, 0, odd),
+                                                 Q::get(v.c.g2, 0, odd), mA0, 1.f);
+      const WeightSlopes qb = make_weight_slopes(Q::get(v.c.g0, 1, odd), Q::get(v.c.g1, 1, odd),
+                                                 Q::get(v.c.g2, 1, odd), 1.f, mB2);
+      const bool rbc = rb.at(c), rac = ra.at(c);
+      const float2 up = k ? v.sp : make_float2(v.st[1].x, v.st[1].y);
+      sweep_b(s, ln, t, act, qa, qb, quad(v.c.lx, 0, odd), quad(v.c.lx, 1, odd),
+              quad(v.c.ug, 0, odd), quad(v.c.ug, 1, odd), rbc, rac, v.st[k], 0.f, up.x, up.y,
+              0.f, a.fL, a.fR, gA[odd], gB[odd], nbuf);
     }
   };
-  int cb = W2 - 1;
-  for (; cb - (PP - 1) >= 0; cb -= PP) block(cb, std::false_type{});
-  if (cb >= 0) block(cb, std::true_type{});
+  auto field = [](const Grad& g, int p) {
+    return p == 0 ? g.dphi : (p == 1 ? g.d0 : (p == 2 ? g.d1 : (p == 3 ? g.d2 : g.hs)));
+  };
+  // the right pair of a tile: parked in the thread's own LDS slots
+  auto park = [&](const Grad (&gA)[2], const Grad (&gB)[2]) {
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      stash[(4 * p) * nt + t] = field(gA[0], p);
+      stash[(4 * p + 1) * nt + t] = field(gA[1], p);
+      stash[(4 * p + 2) * nt + t] = field(gB[0], p);
+      stash[(4 * p + 3) * nt + t] = field(gB[1], p);
+    }
+  };
+  // the left pair: the whole tile row pair, 32 contiguous bytes per part
+  auto put_tile = [&](int q, const Grad (&gA)[2], const Grad (&gB)[2]) {
+    if (!act) return;
+    float* d = part + static_cast<int64_t>(q) * (kGrp * kTc);
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      float4* dp = reinterpret_cast<float4*>(d + p * a.part_stride);
+      dp[0] = make_float4(field(gA[0], p), field(gA[1], p), stash[(4 * p) * nt + t],
+                          stash[(4 * p + 1) * nt + t]);
+      dp[1] = make_float4(field(gB[0], p), field(gB[1], p), stash[(4 * p + 2) * nt + t],
+                          stash[(4 * p + 3) * nt + t]);
+    }
+  };
+  int cp = W2 - 1;
+  Grad gA[2], gB[2];
+  if (!(cp & 1)) {
+    // an odd number of pairs: the last tile has no right pair (its half is
+    // padding and takes the zeroed slots)
+    pair(cp, gA, gB);
+    put_tile(cp / 2, gA, gB);
+    --cp;
+  }
+  for (; cp >= 1; cp -= 2) {
+    pair(cp, gA, gB);
+    park(gA, gB);
+    pair(cp - 1, gA, gB);
+    put_tile(cp / 2, gA, gB);
+  }
 }
 
 // ===========================================================================
@@ -612,7 +646,7 @@ __global__ __launch_bounds__(512) void bt_vB(BtArgs<T> a) {
   struct RowPair {
     Row r[2];          // rows 2k, 2k + 1
     float2 up0;        // top->bottom states of row 2k - 1 (the row above 2k)
-    float4 hz[5];      // horizontal parts: (2k, c0), (2k, c0 + 1), (2k + 1, c0), (2k + 1, c0 + 1)
+    float2 hz[5][2];   // horizontal parts of rows 2k, 2k + 1 at columns c0, c0 + 1
   };
   auto load_pair = [&](int k) {
     RowPair v;
@@ -638,13 +672,17 @@ __global__ __launch_bounds__(512) void bt_vB(BtArgs<T> a) {
     }
     v.up0 = *reinterpret_cast<const float2*>(hv + static_cast<int64_t>(max(2 * k - 1, 0)) * W2 + tl);
     if constexpr (HZ) {
-      const float* pp = a.part + ((plane * a.ng + (2 * k) / kGrp) * W2 + tl) * (2 * kGrp) +
-                        ((2 * k) % kGrp) * 2;
+      const int nq = (W2 + 1) / 2;
+      const float* pp = a.part + ((plane * a.ng + (2 * k) / kGrp) * nq + tl / 2) * (kGrp * kTc) +
+                        ((2 * k) % kGrp) * kTc + (tl % 2) * 2;
 #pragma unroll
-      for (int q = 0; q < 5; ++q) v.hz[q] = *reinterpret_cast<const float4*>(pp + q * a.part_stride);
+      for (int q = 0; q < 5; ++q) {
+        v.hz[q][0] = *reinterpret_cast<const float2*>(pp + q * a.part_stride);
+        v.hz[q][1] = *reinterpret_cast<const float2*>(pp + q * a.part_stride + kTc);
+      }
     } else {
 #pragma unroll
-      for (int q = 0; q < 5; ++q) v.hz[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < 5; ++q) v.hz[q][0] = v.hz[q][1] = make_float2(0.f, 0.f);
     }
     return v;
   };
@@ -663,7 +701,7 @@ __global__ __launch_bounds__(512) void bt_vB(BtArgs<T> a) {
     Grad ga, gb;
     sweep_b(s, ln, t, act, qa, qb, lxa, lxb, uga, ugb, rbr, rar, q.st, q.nl, up.x, up.y, q.nr,
             a.fT, a.fB, ga, gb);
-    auto hzv = [&](int q, int col) { return quad(v.hz[q], i, col); };
+    auto hzv = [&](int q, int col) { return col ? v.hz[q][i].y : v.hz[q][i].x; };
     ga.dphi += hzv(0, 0);
     gb.dphi += hzv(0, 1);
     ga.d0 += hzv(1, 0);
@@ -732,7 +770,7 @@ BtLayout bt_layout(int64_t planes, int64_t H, int64_t W, size_t es, bool hz) {
   L.ng = (H + kGrp - 1) / kGrp;
   const size_t px = static_cast<size_t>(planes * H * W);
   const size_t cp = static_cast<size_t>(planes * W * L.Hp);
-  const size_t np = static_cast<size_t>(planes * L.ng * kGrp * W);
+  const size_t np = static_cast<size_t>(planes * L.ng * ((W / 2 + 1) / 2) * kGrp * kTc);
   size_t o = 0;
   L.hv = o; o = al256(o + px * 8);
   L.lxt = o; o = al256(o + (hz ? cp * 4 : 0));
@@ -792,7 +830,7 @@ static hipError_t launch_bt_dt(const BwdProblem& pr, void* ws, hipStream_t strea
   a.fL = (m & 4u) ? 1.f : 0.f;
   a.fR = (m & 8u) ? 1.f : 0.f;
   a.lg_stride = planes * pr.W * L.Hp;
-  a.part_stride = planes * L.ng * kGrp * pr.W;
+  a.part_stride = planes * L.ng * ((pr.W / 2 + 1) / 2) * kGrp * kTc;
   a.pstride = planes * pr.H * pr.W;
   a.plane0 = 0;
   a.C = pr.C;
@@ -834,12 +872,22 @@ static hipError_t launch_bt_dt(const BwdProblem& pr, void* ws, hipStream_t strea
     g0[g] = planes * g / ngroups;
     gn[g] = planes * (g + 1) / ngroups - g0[g];
   }
+  const size_t hb_lds = bt_hb_lds_bytes(th);
+  if (hz && hb_lds > 65536) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(khb),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(hb_lds))) != hipSuccess) {
+      release();
+      return e;
+    }
+  }
   auto launch = [&](K k, unsigned threads, const char* name, int g) -> hipError_t {
     if (gn[g] == 0) return hipSuccess;
     BtArgs<T> ag = a;
     ag.plane0 = g0[g];
     tr->before(streams[g], name, gn[g]);
-    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(gn[g])), dim3(threads), 0, streams[g], ag);
+    const size_t lds = k == khb ? hb_lds : 0;
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(gn[g])), dim3(threads), lds, streams[g], ag);
     tr->after(streams[g]);
     return hipGetLastError();
   };

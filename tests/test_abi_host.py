@@ -233,18 +233,18 @@ def _stream_ws(planes, H, W, dirs, es):
 def _pipe_ws(planes, H, W, dirs, es):
     """The pipeline's regions: states of the two first sweeps (8 bytes a
     pixel each), the column-major copy (rows padded to 16), the five fp32
-    horizontal parts by groups of 8 rows."""
+    horizontal parts in tiles of 4 rows x 4 columns."""
     px = planes * H * W
     hz = bool(dirs & 12)
-    Hp, ng = (H + 15) // 16 * 16, (H + 7) // 8
+    Hp, ng, nq = (H + 15) // 16 * 16, (H + 3) // 4, (W // 2 + 1) // 2
     cp = planes * W * Hp
     if not hz:
         return _al(px * 8)
     return (_al(px * 8) + 2 * _al(cp * 4) + _al(3 * cp * es) + _al(px * 8)
-            + _al(5 * planes * ng * 8 * W * 4))
+            + _al(5 * planes * ng * nq * 16 * 4))
 
 
-@pytest.mark.parametrize("shape", [(1, 2, 130, 96), (3, 1, 66, 1024), (1, 1, 2048, 2)])
+@pytest.mark.parametrize("shape", [(1, 2, 130, 96), (3, 1, 66, 1024), (1, 1, 2048, 2), (1, 1, 66, 6)])
 @pytest.mark.parametrize("dirs", [15, 3, 12, 1])
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_backward_pipeline_workspace(shape, dirs, dtype):
