@@ -110,6 +110,20 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
 // 16 bytes as a plain vector of four words (arrays of these stay in
 // registers; arrays of the uint4 struct copied whole may not)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read of 16-bit data: within each group of 16 lanes
+// the lanes' 8-byte chunks, taken in lane order, form a run of 64 elements,
+// and lane j receives elements j, j + 16, j + 32, j + 48 of it. When lane c
+// of a group points at row r0 + c / 4, columns n0 + 4 (c % 4) of a [k][n]
+// tile, lane j therefore gets rows r0 .. r0 + 3 of column n0 + j: four
+// consecutive k of one n, half of an MFMA B operand (checked on the GPU with
+// a one-wavefront probe).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+}
 __device__ __forceinline__ u32x4 vec4(const uint4& v) { return u32x4{v.x, v.y, v.z, v.w}; }
 __device__ __forceinline__ uint32_t half16(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
@@ -127,11 +141,13 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   constexpr int E = 16 / sizeof(T);          // elements in 16 bytes
   constexpr int KT = 128 / sizeof(T);        // K per tile: 128-byte rows
   constexpr int AP = KT + 16 / sizeof(T);    // pitch of the weight tile [m][k]
-  // pixel tile: bf16 transposed [n][k] (an MFMA operand is 8 consecutive k),
-  // fp32 as loaded [k][n] (an operand is one value)
-  constexpr int BP = BF ? KT + 8 : kNT + 4;
+  // pixel tile as loaded, [k][n]: an fp32 operand is one value, a bf16
+  // operand (8 consecutive k of one n) comes from two transposing reads. The
+  // bf16 pitch of 144 elements puts the four rows a 16-lane group reads 8
+  // banks apart.
+  constexpr int BP = BF ? kNT + 16 : kNT + 4;
   constexpr int kABytes = kMT * AP * sizeof(R);
-  constexpr int kBBytes = (BF ? kNT : KT) * BP * sizeof(R);
+  constexpr int kBBytes = KT * BP * sizeof(R);
   constexpr int kOutBytes = (kMT / 2) * kOP * sizeof(R);
   constexpr int kSmem = kABytes + kBBytes > kOutBytes ? kABytes + kBBytes : kOutBytes;
   __shared__ __align__(16) unsigned char smem[kSmem];
@@ -202,14 +218,10 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
       *reinterpret_cast<u32x4*>(As + r * AP + kk) = pa[q];
     }
     if constexpr (BF) {
-      // four k rows of eight pixels -> eight 8-byte runs of four k
+      // four k rows of eight pixels, as loaded
       const int kr = 4 * (tid >> 4), nl = 8 * (tid & 15);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint2 v = make_uint2(half16(px[0], e) | (half16(px[1], e) << 16),
-                                   half16(px[2], e) | (half16(px[3], e) << 16));
-        *reinterpret_cast<uint2*>(Bs + (nl + e) * BP + kr) = v;
-      }
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(Bs + (kr + q) * BP + nl) = px[q];
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -231,6 +243,9 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
       // v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) .. +7]
       // and B[8 (l / 16) .. +7][l % 16]; two of them cover K = 64
       const int r = lane & 15, kq = (lane >> 4) * 8;
+      // transposing reads: lane c of each 16-lane group points at row c / 4,
+      // columns 4 (c % 4) .. of its group's 4 x 16 block
+      const int tr_off = (kq + (r >> 2)) * BP + 4 * (r & 3);
 #pragma unroll
       for (int kh = 0; kh < KT; kh += 32) {
         bf16x8 fa[4], fb[4];
@@ -238,8 +253,11 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
         for (int i = 0; i < 4; ++i)
           fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm + 16 * i + r) * AP + kh + kq);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn + 16 * j + r) * BP + kh + kq);
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t* bp = reinterpret_cast<const uint16_t*>(Bs) + kh * BP + wn + 16 * j + tr_off;
+          const v4i16 lo = lds_read_tr(bp), hi = lds_read_tr(bp + 4 * BP);
+          fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
