@@ -183,8 +183,11 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   //   weights: run c = tid + 256 q is row c / 8, k offset (c % 8) * E
   //   pixels, bf16: rows 4 g .. 4 g + 3 (g = tid / 16), pixels 8 (tid % 16) ..
   //   pixels, fp32: run c = tid + 256 q is k row c / 32, pixels (c % 32) * 4 ..
-  u32x4 pa[4], px[4];
-  auto fetch = [&](int k0) {
+  // two register sets: the straight-line variant for whole tiles keeps the
+  // loads of two K tiles in flight (one K tile of products, about 0.2 us, is
+  // shorter than a memory latency); the general one uses the first only
+  u32x4 pa[4], px[4], pb[4], py[4];
+  auto fetch_to = [&](int k0, u32x4 (&pa)[4], u32x4 (&px)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
@@ -211,7 +214,8 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
         px[q] = vec4(run16(X, static_cast<int64_t>(k) * N + n, k < K ? N - n : 0, a.vec_x));
     }
   };
-  auto stash = [&]() {
+  auto fetch = [&](int k0) { fetch_to(k0, pa, px); };
+  auto stash_from = [&](const u32x4 (&pa)[4], const u32x4 (&px)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
@@ -231,14 +235,10 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
     }
   };
 
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += KT) {
-    stash();
-    lds_barrier();
-    if constexpr (FULL)
-      fetch(min(k0 + KT, K - KT));   // the last tile fetches itself again
-    else if (k0 + KT < K)
-      fetch(k0 + KT);
+  auto stash = [&]() { stash_from(pa, px); };
+
+  // the products of the K tile in LDS
+  auto multiply = [&]() {
     if constexpr (BF) {
       // v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) .. +7]
       // and B[8 (l / 16) .. +7][l % 16]; two of them cover K = 64
@@ -282,7 +282,46 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     }
+  };
+
+  if constexpr (FULL) {
+    // whole tiles and an even number of K tiles: set a holds the even K
+    // tiles, set b the odd ones, each refilled two K tiles ahead right after
+    // it is stored (the last refills fetch the last tile again). The first
+    // tile is peeled, so that the loop is entered with the loads in flight
+    // in the same order as at its back edge: set b's, then set a's.
+    fetch_to(0, pa, px);
+    fetch_to(KT, pb, py);
+    stash_from(pa, px);
+    fetch_to(min(2 * KT, K - KT), pa, px);
     lds_barrier();
+    multiply();
+    lds_barrier();
+    for (int k0 = KT; k0 < K - KT; k0 += 2 * KT) {
+      stash_from(pb, py);
+      fetch_to(min(k0 + 2 * KT, K - KT), pb, py);
+      lds_barrier();
+      multiply();
+      lds_barrier();
+      stash_from(pa, px);
+      fetch_to(min(k0 + 3 * KT, K - KT), pa, px);
+      lds_barrier();
+      multiply();
+      lds_barrier();
+    }
+    stash_from(pb, py);   // the last K tile
+    lds_barrier();
+    multiply();
+    lds_barrier();
+  } else {
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KT) {
+      stash();
+      lds_barrier();
+      if (k0 + KT < K) fetch(k0 + KT);
+      multiply();
+      lds_barrier();
+    }
   }
 
   // bias, rounding to the storage type, staging half a tile (64 rows, the
@@ -588,8 +627,10 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
     return launch_xs_k<T>(g, B, name, stream, tr);
   const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT);
   const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8), static_cast<unsigned>(B));
-  const bool full = M % kMT == 0 && N % kNT == 0 && K % (128 / static_cast<int>(sizeof(T))) == 0 &&
-                    g.vec_a && g.vec_x && g.vec_o;
+  // the straight-line variant: whole tiles, an even number of K tiles
+  const int kt = 128 / static_cast<int>(sizeof(T));
+  const bool full = M % kMT == 0 && N % kNT == 0 && K % (2 * kt) == 0 && g.vec_a && g.vec_x &&
+                    g.vec_o;
   auto kern = full ? prologue_gemm<T, true> : prologue_gemm<T, false>;
   tr->before(stream, name, B);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g);
