@@ -70,6 +70,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         f3.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp,
                        ctypes.c_uint32, i64, vp, ctypes.c_int]
         f3.restype = ctypes.c_int
+    if hasattr(lib, "gspn_oracle_backward_dirs"):
+        b3 = lib.gspn_oracle_backward_dirs
+        b3.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp,
+                       ctypes.c_uint32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+        b3.restype = ctypes.c_int
     if hasattr(lib, "gspn_oracle_prologue"):
         f4 = lib.gspn_oracle_prologue
         f4.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp,
@@ -187,6 +192,61 @@ def propagate_dirs(x, l0, l1, l2, lam, u, merge=None, dirs: int = 15, group_rows
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
+
+
+def _gather_dirs(x, params, merge):
+    x = np.asarray(x)
+    if x.ndim != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    shape = x.shape
+    dshape = (4,) + tuple(shape)
+    arrs, dts = [], set()
+    for a, shp in [(x, shape)] + [(t, dshape) for t in params]:
+        a2, dt = _as_input(np.asarray(a), shp)
+        arrs.append(a2)
+        dts.add(dt)
+    if len(dts) != 1:
+        raise TypeError("all oracle inputs must share one dtype")
+    m = None
+    if merge is not None:
+        m = np.ascontiguousarray(merge, dtype=np.float64)
+        if m.shape != (4, shape[1]):
+            raise ValueError(f"merge must be [4, {shape[1]}]")
+    return arrs, dts.pop(), shape, m
+
+
+def backward_dirs(x, l0, l1, l2, lam, u, gy, merge=None, dirs: int = 15, group_rows: int = 0,
+                  nthreads: int | None = None, lib: ctypes.CDLL | None = None) -> dict:
+    """Gradients of the per-direction layer of ``propagate_dirs`` (CSDN page
+    on GSPN, section 反向传播; reading R15 in gspn_oracle.c), given ``gy`` =
+    dL/dy [B, C, H, W] in the inputs' dtype. Returns float64 arrays: "x"
+    [B, C, H, W]; "l0", "l1", "l2", "lam", "u" [4, B, C, H, W] (slice d =
+    direction d, zero outside ``dirs``); "merge" [4, C], the gradient of the
+    merge weights (of an all-ones merger when ``merge`` is None)."""
+    x = np.asarray(x)
+    arrs, dt, shape, m = _gather_dirs(x, (l0, l1, l2, lam, u), merge)
+    g2, gdt = _as_input(np.asarray(gy), shape)
+    if gdt != dt:
+        raise TypeError("gy must have the inputs' dtype")
+    B, C, H, W = shape
+    dshape = (4,) + tuple(shape)
+    outs = {"x": np.empty(shape, dtype=np.float64)}
+    for k in ("l0", "l1", "l2", "lam", "u"):
+        outs[k] = np.empty(dshape, dtype=np.float64)
+    outs["merge"] = np.empty((4, C), dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    L = lib if lib is not None else load()
+    rc = L.gspn_oracle_backward_dirs(*[a.ctypes.data for a in arrs], g2.ctypes.data, dt,
+                                     B, C, H, W, B * C * H * W,
+                                     None if m is None else m.ctypes.data, int(dirs),
+                                     int(group_rows),
+                                     *[outs[k].ctypes.data for k in ("x", "l0", "l1", "l2",
+                                                                     "lam", "u", "merge")],
+                                     int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return outs
 
 
 PARAM_NAMES = ("l0", "l1", "l2", "lam", "u")

@@ -410,8 +410,14 @@ typedef struct {
   int64_t B, C, H, W, G, Cl;
   uint32_t mask;
   double *dx, *dl[3], *dlam, *du;
-  int64_t next_group;   /* shared work counter over logit planes */
+  int64_t next_group;   /* shared work counter over logit planes (or channels) */
   pthread_mutex_t lock;
+  /* per-direction parameters (R15): direction d reads lam, the logits and u
+   * at element offset d * dstride, its output is scaled by merge[d * C + c],
+   * and its gradients go to slice d of dl, dlam and du ([4][B*C*H*W]) */
+  int64_t dstride;
+  const double* merge;
+  double* dmerge;       /* [4][C]: gradient of the merge weights */
 } bjob_t;
 
 /* sigmoids of the in-range links of the pixel at plane offset idx, which sits
@@ -438,13 +444,17 @@ static int64_t pixel_offset(const bjob_t* j, int d, int64_t s, int64_t o) {
 
 /* one direction over one plane: adds this direction's share of
  * d(lambda x) into dphi, of du / gy into hsum and of the logit gradients
- * into the output arrays (at the plane's logit plane, R14) */
-static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
-                           double* e_cur, double* e_next, double* dphi, double* hsum) {
+ * into dl (at the plane's logit plane, R14). The direction's lambda, logits
+ * and u sit at element offset doff (R15); its output gate is scaled by m, so
+ * its error term starts from m u gy. */
+static void backward_plane(const bjob_t* j, int d, int64_t plane, int64_t doff, double m,
+                           double* const dl[3], double* h, double* e_cur, double* e_next,
+                           double* dphi, double* hsum) {
   const int64_t H = j->H, W = j->W;
   const int64_t n_s = scan_len(d, H, W), n_o = orth_len(d, H, W);
   const int64_t base = plane * H * W;
   const int64_t lbase = logit_plane(plane, j->C, j->Cl) * H * W;
+  const int64_t lin = lbase + doff;   /* where the direction's logits are read */
 
   /* forward: every hidden state of the scan, h[s * n_o + o] */
   for (int64_t s = 0; s < n_s; ++s) {
@@ -456,11 +466,12 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
       if (!first) {
         double sig[3];
         int in_range[3];
-        const double S = link_sigmoids(j, lbase + pix, o, n_o, sig, in_range);
+        const double S = link_sigmoids(j, lin + pix, o, n_o, sig, in_range);
         for (int k = 0; k < 3; ++k)
           if (in_range[k]) acc += (sig[k] / S) * h[(s - 1) * n_o + o + k - 1];
       }
-      h[s * n_o + o] = acc + load_value(j->lam, j->dt, idx) * load_value(j->x, j->dt, idx);
+      h[s * n_o + o] =
+          acc + load_value(j->lam, j->dt, doff + idx) * load_value(j->x, j->dt, idx);
       hsum[pix] += h[s * n_o + o];
     }
   }
@@ -472,14 +483,14 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
     for (int64_t o = 0; o < n_o; ++o) {
       const int64_t pix = pixel_offset(j, d, s, o);
       const int64_t idx = base + pix;
-      double e = load_value(j->u, j->dt, idx) * load_value(j->gy, j->dt, idx);
+      double e = m * load_value(j->u, j->dt, doff + idx) * load_value(j->gy, j->dt, idx);
       if (next_reads) {
         for (int k = 0; k < 3; ++k) {
           const int64_t op = o - k + 1;   /* o' with o' + k - 1 == o */
           if (op < 0 || op >= n_o) continue;
           double sig[3];
           int in_range[3];
-          const double S = link_sigmoids(j, lbase + pixel_offset(j, d, s + 1, op), op, n_o,
+          const double S = link_sigmoids(j, lin + pixel_offset(j, d, s + 1, op), op, n_o,
                                          sig, in_range);
           e += (sig[k] / S) * e_next[op];
         }
@@ -489,7 +500,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
       if (!restarts(d, n_s, s, j->G)) {
         double sig[3], dw[3] = {0.0, 0.0, 0.0};
         int in_range[3];
-        const double S = link_sigmoids(j, lbase + pix, o, n_o, sig, in_range);
+        const double S = link_sigmoids(j, lin + pix, o, n_o, sig, in_range);
         double t = 0.0;   /* sum_k dw_k sig_k */
         for (int k = 0; k < 3; ++k) {
           if (!in_range[k]) continue;
@@ -499,7 +510,7 @@ static void backward_plane(const bjob_t* j, int d, int64_t plane, double* h,
         for (int k = 0; k < 3; ++k) {
           if (!in_range[k]) continue;
           const double dsig = dw[k] / S - t / (S * S);
-          j->dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);
+          dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);
         }
       }
     }
@@ -537,7 +548,8 @@ static void* bworker(void* arg) {
         hsum[i] = 0.0;
       }
       for (int d = 0; d < 4; ++d)
-        if (j->mask & (1u << d)) backward_plane(j, d, plane, h, e_cur, e_next, dphi, hsum);
+        if (j->mask & (1u << d))
+          backward_plane(j, d, plane, 0, 1.0, j->dl, h, e_cur, e_next, dphi, hsum);
       for (int64_t i = 0; i < H * W; ++i) {
         j->dx[base + i] = load_value(j->lam, j->dt, base + i) * dphi[i];
         j->dlam[base + i] = load_value(j->x, j->dt, base + i) * dphi[i];
@@ -574,6 +586,7 @@ int gspn_oracle_backward_shared(const void* x, const void* l0, const void* l1,
   j.mask = dir_mask;
   j.dx = dx; j.dl[0] = dl0; j.dl[1] = dl1; j.dl[2] = dl2; j.dlam = dlam; j.du = du;
   j.next_group = 0;
+  j.dstride = 0; j.merge = NULL; j.dmerge = NULL;
   pthread_mutex_init(&j.lock, NULL);
 
   int nt = nthreads <= 0 ? 1 : nthreads;
@@ -604,4 +617,105 @@ int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const vo
   return gspn_oracle_backward_shared(x, l0, l1, l2, lam, u, gy, in_dtype, B, C, H, W,
                                      C > 0 ? C : 1, dir_mask, group_rows, dx, dl0, dl1,
                                      dl2, dlam, du, nthreads);
+}
+
+/* Per-direction parameters (R15), backward. With y = sum_d m_d u_d (.) h_d
+ * (m_d = merge[d * C + c]), direction d is one scan with its own lambda,
+ * logits and u whose error term starts from m_d u_d gy; then
+ *   dx       = sum_d lambda_d d(lambda x)_d,   dlambda_d = x d(lambda x)_d,
+ *   du_d     = m_d gy h_d,
+ *   dmerge_d = sum over the batch and the pixels of u_d gy h_d,
+ * and the logit gradients of direction d are the single-direction ones. One
+ * unit of work is one channel (all of its images, in batch order), so each
+ * merge gradient is summed by one thread in a fixed order. */
+static void* bworker_dirs(void* arg) {
+  bjob_t* j = (bjob_t*)arg;
+  const int64_t H = j->H, W = j->W, HW = H * W, P = j->B * j->C * HW;
+  const int64_t n_max = H > W ? H : W;
+  double* h = (double*)malloc(sizeof(double) * (size_t)HW);
+  double* dphi = (double*)malloc(sizeof(double) * (size_t)HW);
+  double* hsum = (double*)malloc(sizeof(double) * (size_t)HW);
+  double* e_cur = (double*)malloc(sizeof(double) * (size_t)n_max);
+  double* e_next = (double*)malloc(sizeof(double) * (size_t)n_max);
+  void* ret = NULL;
+  if (!h || !dphi || !hsum || !e_cur || !e_next) { ret = (void*)1; goto done; }
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t c = j->next_group++;
+    pthread_mutex_unlock(&j->lock);
+    if (c >= j->C) break;
+    for (int d = 0; d < 4; ++d) j->dmerge[d * j->C + c] = 0.0;
+    for (int64_t b = 0; b < j->B; ++b) {
+      const int64_t plane = b * j->C + c;
+      const int64_t base = plane * HW;
+      for (int64_t i = 0; i < HW; ++i) j->dx[base + i] = 0.0;
+      for (int d = 0; d < 4; ++d) {
+        const int64_t go = d * P;   /* this direction's gradient slice */
+        double* const dl[3] = {j->dl[0] + go, j->dl[1] + go, j->dl[2] + go};
+        for (int k = 0; k < 3; ++k)
+          for (int64_t i = 0; i < HW; ++i) dl[k][base + i] = 0.0;
+        for (int64_t i = 0; i < HW; ++i) j->dlam[go + base + i] = j->du[go + base + i] = 0.0;
+        if (!(j->mask & (1u << d))) continue;
+        const int64_t doff = d * j->dstride;
+        const double m = j->merge ? j->merge[d * j->C + c] : 1.0;
+        for (int64_t i = 0; i < HW; ++i) dphi[i] = hsum[i] = 0.0;
+        backward_plane(j, d, plane, doff, m, dl, h, e_cur, e_next, dphi, hsum);
+        for (int64_t i = 0; i < HW; ++i) {
+          const double g = load_value(j->gy, j->dt, base + i);
+          j->dx[base + i] += load_value(j->lam, j->dt, doff + base + i) * dphi[i];
+          j->dlam[go + base + i] = load_value(j->x, j->dt, base + i) * dphi[i];
+          j->du[go + base + i] = m * g * hsum[i];
+          j->dmerge[d * j->C + c] += load_value(j->u, j->dt, doff + base + i) * g * hsum[i];
+        }
+      }
+    }
+  }
+done:
+  free(h); free(dphi); free(hsum); free(e_cur); free(e_next);
+  return ret;
+}
+
+int gspn_oracle_backward_dirs(const void* x, const void* l0, const void* l1, const void* l2,
+                              const void* lam, const void* u, const void* gy, int in_dtype,
+                              int64_t B, int64_t C, int64_t H, int64_t W, int64_t dir_stride,
+                              const double* merge, uint32_t dir_mask, int64_t group_rows,
+                              double* dx, double* dl0, double* dl1, double* dl2,
+                              double* dlam, double* du, double* dmerge, int nthreads) {
+  if (!x || !l0 || !l1 || !l2 || !lam || !u || !gy) return -1;
+  if (!dx || !dl0 || !dl1 || !dl2 || !dlam || !du || !dmerge) return -1;
+  if (B < 0 || C < 0 || H <= 0 || W <= 0) return -1;
+  if (dir_mask == 0 || dir_mask > 15) return -1;
+  if (group_rows < 0 || dir_stride < 0) return -1;
+  if (in_dtype != ORC_F64 && in_dtype != ORC_F32 && in_dtype != ORC_BF16)
+    return -1;
+  if (C == 0) return 0;
+
+  bjob_t j;
+  j.x = x; j.l[0] = l0; j.l[1] = l1; j.l[2] = l2; j.lam = lam; j.u = u; j.gy = gy;
+  j.dt = in_dtype; j.B = B; j.C = C; j.H = H; j.W = W; j.G = group_rows;
+  j.Cl = C;
+  j.mask = dir_mask;
+  j.dx = dx; j.dl[0] = dl0; j.dl[1] = dl1; j.dl[2] = dl2; j.dlam = dlam; j.du = du;
+  j.next_group = 0;
+  j.dstride = dir_stride; j.merge = merge; j.dmerge = dmerge;
+  pthread_mutex_init(&j.lock, NULL);
+
+  int nt = nthreads <= 0 ? 1 : nthreads;
+  if ((int64_t)nt > C) nt = (int)C;
+  int rc = 0;
+  if (nt == 1) {
+    if (bworker_dirs(&j) != NULL) rc = -1;
+  } else {
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    if (!th) { pthread_mutex_destroy(&j.lock); return -1; }
+    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, bworker_dirs, &j);
+    for (int t = 0; t < nt; ++t) {
+      void* r = NULL;
+      pthread_join(th[t], &r);
+      if (r != NULL) rc = -1;
+    }
+    free(th);
+  }
+  pthread_mutex_destroy(&j.lock);
+  return rc;
 }

@@ -103,6 +103,21 @@ int gspn_oracle_propagate_dirs(const void* x, const void* l0, const void* l1,
                                int nthreads);
 
 /*
+ * Backward pass of the per-direction layer (R15; CSDN page, section 反向传播):
+ * inputs as gspn_oracle_propagate_dirs plus gy = dL/dy [B, C, H, W]. Outputs
+ * (host, float64): dx [B, C, H, W]; dl0, dl1, dl2, dlam, du [4, B, C, H, W]
+ * (slice d = direction d; zero for directions outside dir_mask); dmerge
+ * [4, C], the gradient of the merge weights (of an all-ones merger when
+ * merge is NULL). Returns 0, or -1 on a bad argument.
+ */
+int gspn_oracle_backward_dirs(const void* x, const void* l0, const void* l1, const void* l2,
+                              const void* lam, const void* u, const void* gy, int in_dtype,
+                              int64_t B, int64_t C, int64_t H, int64_t W, int64_t dir_stride,
+                              const double* merge, uint32_t dir_mask, int64_t group_rows,
+                              double* dx, double* dl0, double* dl1, double* dl2,
+                              double* dlam, double* du, double* dmerge, int nthreads);
+
+/*
  * Module prologue (aitntnews page, section GSPN架构; reading R16 in the
  * source): x_in [B, Cin, H, W]; w_r [C, Cin], b_r [C]; w_p [5C, C], b_p [5C]
  * with output channel q = t * C + c for t = 0..4 (l0, l1, l2, lambda, u), all

@@ -33,13 +33,13 @@ MUTANTS = [
     ("adjoint_ignores_restart",
      "const int next_reads = s + 1 < n_s && !restarts(d, n_s, s + 1, j->G);",
      "const int next_reads = s + 1 < n_s;", 1),
-    ("adjoint_weights_of_wrong_line", "base + pixel_offset(j, d, s + 1, op)",
-     "base + pixel_offset(j, d, s, op)", 1),
+    ("adjoint_weights_of_wrong_line", "lin + pixel_offset(j, d, s + 1, op)",
+     "lin + pixel_offset(j, d, s, op)", 1),
     ("error_term_without_gate",
-     "double e = load_value(j->u, j->dt, idx) * load_value(j->gy, j->dt, idx);",
-     "double e = load_value(j->gy, j->dt, idx);", 1),
-    ("sigmoid_slope_missing", "j->dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);",
-     "j->dl[k][lbase + pix] += dsig * sig[k];", 1),
+     "double e = m * load_value(j->u, j->dt, doff + idx) * load_value(j->gy, j->dt, idx);",
+     "double e = m * load_value(j->gy, j->dt, idx);", 1),
+    ("sigmoid_slope_missing", "dl[k][lbase + pix] += dsig * sig[k] * (1.0 - sig[k]);",
+     "dl[k][lbase + pix] += dsig * sig[k];", 1),
     ("normalisation_term_dropped", "const double dsig = dw[k] / S - t / (S * S);",
      "const double dsig = dw[k] / S;", 1),
     ("gate_gradient_uses_current_line", "dw[k] = e * h[(s - 1) * n_o + o + k - 1];",
