@@ -286,6 +286,39 @@ size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
                                  uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype);
 
 /*
+ * Backward pass of the per-direction layer (CSDN page, section 反向传播; the
+ * layer as gspn_propagate_dirs_ws). Direction d is one scan with its own
+ * lambda, logits and u whose error term starts from merge[d * C + c] * u_d *
+ * grad_out; the results are
+ *   grad_x                 = sum over d of lambda_d (.) e_d   (e_d summed along its scan),
+ *   grad_lambda slice d    = x (.) e_d,
+ *   grad_logits[k] slice d = the logit gradients of direction d's scan,
+ *   grad_u slice d         = merge[d * C + c] * grad_out (.) h_d,
+ *   grad_merge[d * C + c]  = sum over the batch and the pixels of u_d grad_out h_d.
+ * Inputs as gspn_propagate_dirs_ws (x, w_logits, lambda, u, dir_stride,
+ * merge), plus grad_out [B, C, H, W] in the storage type. Outputs, device
+ * memory in the storage type, caller-owned, fully overwritten: grad_x
+ * [B, C, H, W]; grad_logits[0..2], grad_lambda, grad_u [4, B, C, H, W] (slice
+ * d = direction d, dense, whatever dir_stride is; zero for directions outside
+ * dir_mask); grad_merge: 4 * C fp32 values, or NULL to skip them. No output
+ * may overlap an input or another output (GSPN_E_ALIAS); H and W <= 8192.
+ * Every direction runs as its own scan pair; the horizontal ones on
+ * transposed copies. Workspace: gspn_backward_workspace_bytes_dirs() bytes,
+ * 256-byte aligned, caller-owned (the stored states, an fp32 sum for grad_x,
+ * and with a horizontal direction selected the transposed copies). Same
+ * status codes as gspn_propagate_backward_ws.
+ */
+gspn_status gspn_propagate_backward_dirs_ws(
+    const void* x, const void* const w_logits[3], const void* lambda, const void* u,
+    int64_t dir_stride, const float* merge, const void* grad_out, int64_t B, int64_t C,
+    int64_t H, int64_t W, uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype, void* grad_x,
+    void* const grad_logits[3], void* grad_lambda, void* grad_u, float* grad_merge,
+    void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t gspn_backward_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
+                                          uint32_t dir_mask, int64_t group_rows,
+                                          gspn_dtype dtype);
+
+/*
  * The module prologue (aitntnews page, section GSPN架构: a shared 1x1
  * convolution reduces the channels, then three independent 1x1 convolutions
  * produce the input-dependent propagation parameters). Per pixel:

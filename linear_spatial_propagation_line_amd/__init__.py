@@ -99,6 +99,13 @@ def lib() -> ctypes.CDLL:
         L.gspn_propagate_dirs_ws.restype = ctypes.c_int
         L.gspn_workspace_bytes_dirs.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
         L.gspn_workspace_bytes_dirs.restype = ctypes.c_size_t
+        L.gspn_propagate_backward_dirs_ws.argtypes = [
+            vp, logits_t, vp, vp, i64, vp, vp, i64, i64, i64, i64, u32, i64, ctypes.c_int, vp,
+            logits_t, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gspn_propagate_backward_dirs_ws.restype = ctypes.c_int
+        L.gspn_backward_workspace_bytes_dirs.argtypes = [i64, i64, i64, i64, u32, i64,
+                                                         ctypes.c_int]
+        L.gspn_backward_workspace_bytes_dirs.restype = ctypes.c_size_t
         outs5_t = ctypes.POINTER(ctypes.c_void_p)
         L.gspn_prologue.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                     vp, outs5_t, vp]
@@ -343,6 +350,73 @@ def backward_plan_name(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> st
 
 
 GRAD_NAMES = ("x", "l0", "l1", "l2", "lam", "u")
+
+
+def backward_workspace_bytes_dirs(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
+    return int(lib().gspn_backward_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dtype))
+
+
+def propagate_backward_dirs(x, logits, lam, u, grad_out, merge=None, dirs: int = ALL,
+                            group_rows: int = 0, grads=None, workspace=None, stream=None) -> dict:
+    """Gradients of the per-direction layer of propagate_dirs(), given
+    ``grad_out`` = dL/dout [B, C, H, W]: a dict with "x" [B, C, H, W]; "l0",
+    "l1", "l2", "lam", "u" [4, B, C, H, W] (slice d = direction d, zero
+    outside ``dirs``); "merge" float32 [4, C] (the merge weights' gradient;
+    of an all-ones merger when ``merge`` is None). ``grads`` may supply the
+    tensors."""
+    import torch
+    l0, l1, l2 = logits
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    for t in (x, l0, l1, l2, lam, u, grad_out):
+        if not isinstance(t, torch.Tensor) or t.device != x.device or t.device.type != "cuda":
+            raise TypeError("all inputs must be torch tensors on x's GPU device")
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous tensors of one dtype")
+    for t in (l0, l1, l2, lam, u):
+        if tuple(t.shape) != (4, B, C, H, W):
+            raise ValueError("per-direction tensors must be [4, B, C, H, W]")
+    if tuple(grad_out.shape) != (B, C, H, W):
+        raise ValueError("grad_out must be [B, C, H, W]")
+    mptr = None
+    if merge is not None:
+        if (merge.dtype != torch.float32 or merge.device != x.device or not merge.is_contiguous()
+                or tuple(merge.shape) != (4, C)):
+            raise ValueError("merge must be a contiguous float32 [4, C] tensor on x's device")
+        mptr = merge.data_ptr()
+    dt = _dtype_code(x)
+    if grads is None:
+        grads = {"x": torch.empty_like(x)}
+        for k in ("l0", "l1", "l2", "lam", "u"):
+            grads[k] = torch.empty_like(lam)
+        grads["merge"] = torch.empty((4, C), dtype=torch.float32, device=x.device)
+    for k in ("x", "l0", "l1", "l2", "lam", "u"):
+        t = grads[k]
+        like = x if k == "x" else lam
+        if t.shape != like.shape or t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("gradient tensors must match the inputs")
+    gm = grads.get("merge")
+    if gm is not None and (gm.dtype != torch.float32 or tuple(gm.shape) != (4, C)
+                           or not gm.is_contiguous() or gm.device != x.device):
+        raise ValueError("the merge gradient must be a contiguous float32 [4, C] tensor")
+    L = lib()
+    need = int(L.gspn_backward_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dt))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    dlg = (ctypes.c_void_p * 3)(grads["l0"].data_ptr(), grads["l1"].data_ptr(),
+                                grads["l2"].data_ptr())
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.gspn_propagate_backward_dirs_ws(
+        x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B * C * H * W, mptr, grad_out.data_ptr(),
+        B, C, H, W, dirs, group_rows, dt, grads["x"].data_ptr(), dlg, grads["lam"].data_ptr(),
+        grads["u"].data_ptr(), gm.data_ptr() if gm is not None else None, ws_ptr, ws_len, sptr))
+    return grads
 
 
 def propagate_backward(x, logits, lam, u, grad_out, dirs: int = ALL, group_rows: int = 0,

@@ -811,6 +811,120 @@ size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W, uin
   return chk.status == GSPN_OK ? chk.ws_bytes : 0;
 }
 
+size_t gspn_backward_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
+                                          uint32_t dir_mask, int64_t group_rows,
+                                          gspn_dtype dtype) {
+  const std::string keep = g_last_error;
+  const Checked chk = check_dirs_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype), 0);
+  g_last_error = keep;
+  return chk.status == GSPN_OK
+             ? gspn::bwd_dirs_workspace_bytes(B * C, H, W, dir_mask, dtype)
+             : 0;
+}
+
+gspn_status gspn_propagate_backward_dirs_ws(
+    const void* x, const void* const w_logits[3], const void* lambda, const void* u,
+    int64_t dir_stride, const float* merge, const void* grad_out, int64_t B, int64_t C,
+    int64_t H, int64_t W, uint32_t dir_mask, int64_t group_rows, gspn_dtype dtype, void* grad_x,
+    void* const grad_logits[3], void* grad_lambda, void* grad_u, float* grad_merge,
+    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (!x || !w_logits || !lambda || !u || !grad_out || !grad_x || !grad_logits ||
+      !grad_lambda || !grad_u)
+    return fail(GSPN_E_NULL, "inputs, grad_out and the gradient outputs must be non-null");
+  if (!w_logits[0] || !w_logits[1] || !w_logits[2] || !grad_logits[0] || !grad_logits[1] ||
+      !grad_logits[2])
+    return fail(GSPN_E_NULL, "w_logits[0..2] and grad_logits[0..2] must be non-null");
+  const Checked chk = check_dirs_shape(B, C, H, W, dir_mask, group_rows, static_cast<int>(dtype),
+                                       dir_stride);
+  if (chk.status != GSPN_OK) return chk.status;
+  const size_t es = elem_size(dtype);
+  const void* ins[7] = {x, w_logits[0], w_logits[1], w_logits[2], lambda, u, grad_out};
+  const void* outs[6] = {grad_x, grad_logits[0], grad_logits[1], grad_logits[2], grad_lambda,
+                         grad_u};
+  for (const void* p : ins)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "input pointer not aligned to its element size");
+  for (const void* p : outs)
+    if (reinterpret_cast<uintptr_t>(p) % es)
+      return fail(GSPN_E_ALIGN, "gradient pointer not aligned to its element size");
+  if (reinterpret_cast<uintptr_t>(merge) % sizeof(float) ||
+      reinterpret_cast<uintptr_t>(grad_merge) % sizeof(float))
+    return fail(GSPN_E_ALIGN, "merge and grad_merge must be aligned to 4 bytes");
+  // byte ranges read: x, grad_out, each selected direction's five tensors,
+  // the merge weights; written: grad_x, the four-slice gradients, grad_merge
+  const size_t bytes = static_cast<size_t>(B * C * H * W) * es;
+  const size_t mbytes = static_cast<size_t>(4 * C) * sizeof(float);
+  const void* rd[23];
+  size_t rn[23];
+  int nr = 0;
+  rd[nr] = x; rn[nr++] = bytes;
+  rd[nr] = grad_out; rn[nr++] = bytes;
+  if (merge) { rd[nr] = merge; rn[nr++] = mbytes; }
+  for (int d = 0; d < 4; ++d) {
+    if (!((dir_mask >> d) & 1u)) continue;
+    const size_t off = static_cast<size_t>(d * dir_stride) * es;
+    for (int k = 1; k < 6; ++k) {
+      rd[nr] = static_cast<const char*>(ins[k]) + off;
+      rn[nr++] = bytes;
+    }
+  }
+  const void* wr[7] = {grad_x, grad_logits[0], grad_logits[1], grad_logits[2], grad_lambda,
+                       grad_u, grad_merge};
+  const size_t wn[7] = {bytes, 4 * bytes, 4 * bytes, 4 * bytes, 4 * bytes, 4 * bytes,
+                        grad_merge ? mbytes : 0};
+  for (int i = 0; i < 7; ++i) {
+    for (int k = 0; k < nr; ++k)
+      if (overlaps(wr[i], wn[i], rd[k], rn[k]))
+        return fail(GSPN_E_ALIAS, "a gradient overlaps an input");
+    for (int k = i + 1; k < 7; ++k)
+      if (overlaps(wr[i], wn[i], wr[k], wn[k]))
+        return fail(GSPN_E_ALIAS, "two gradient outputs overlap");
+  }
+  const size_t need = gspn::bwd_dirs_workspace_bytes(B * C, H, W, dir_mask, dtype);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(GSPN_E_WORKSPACE,
+                  "workspace missing or smaller than gspn_backward_workspace_bytes_dirs()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(GSPN_E_ALIGN, "workspace must be 256-byte aligned");
+    for (int k = 0; k < nr; ++k)
+      if (overlaps(workspace, need, rd[k], rn[k]))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(workspace, need, wr[i], wn[i]))
+        return fail(GSPN_E_ALIAS, "workspace overlaps a tensor");
+  }
+  gspn::BwdProblem pr;
+  pr.x = x;
+  for (int k = 0; k < 3; ++k) {
+    pr.l[k] = w_logits[k];
+    pr.dl[k] = grad_logits[k];
+  }
+  pr.lam = lambda;
+  pr.u = u;
+  pr.gy = grad_out;
+  pr.dx = grad_x;
+  pr.dlam = grad_lambda;
+  pr.du = grad_u;
+  pr.B = B; pr.C = C; pr.H = H; pr.W = W;
+  pr.mask = dir_mask;
+  pr.G = group_rows >= H && group_rows >= W ? 0 : group_rows;
+  pr.dtype = dtype;
+  pr.aligned_vec4 = false;
+  pr.aligned_pair = false;
+  pr.Cl = C;
+  pr.dlw = nullptr;
+  gspn::BwdDirsExtra ex{dir_stride, merge, grad_merge};
+  gspn::Tracer tr;
+  tr.events = g_trace_events;
+  tr.pairs = g_trace_pairs;
+  const hipError_t e = gspn::launch_bwd_dirs(pr, ex, workspace, stream, &tr);
+  keep_trace(tr);
+  if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
+  return GSPN_OK;
+}
+
 gspn_status gspn_propagate_dirs_ws(const void* x, const void* const w_logits[3],
                                    const void* lambda, const void* u, int64_t dir_stride,
                                    const float* merge, int64_t B, int64_t C, int64_t H,

@@ -31,6 +31,8 @@
 // top->bottom and bottom->top there into transposed accumulators, and those
 // are transposed back before the vertical directions add to them (or, with
 // no vertical direction, a pointwise pass writes the gradients).
+#include <cstring>
+
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 
@@ -73,6 +75,13 @@ struct BwArgs {
   int H, W, G, dir, mode;
   int64_t C, Cl;    // channels and logit channels (shared logits when Cl < C)
   float* dlw;       // shared logits: per-plane fp32 logit gradients [3][planes*H*W]
+  // per-direction parameters: the output gate of this direction is scaled
+  // per channel (merge weights; null: 1), and dx sums lambda d(lambda x)
+  // over the directions in dxacc (fp32): the first direction writes it, the
+  // last writes dx, the others add (dxacc null: dx = lambda d(lambda x))
+  const float* gscale;
+  float* dxacc;
+  bool dxfirst, dxlast;
 };
 
 // logit gradients of pixel idx: to the storage type, or per plane in fp32
@@ -180,6 +189,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   const int64_t back_off = vert ? static_cast<int64_t>(back) * W : back;
   const int64_t oo = vert ? 1 : W;   // orthogonal stride
   const int64_t lsh = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
+  const float gsc = a.gscale ? a.gscale[blockIdx.x % a.C] : 1.f;
 
   float a1[MAXP];
 #pragma unroll
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
     float gy[D][MAXP], ug[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP];
     float hc[D][MAXP], hl[D][MAXP], hr[D][MAXP];
     float c0[D][MAXP], c1[D][MAXP], c2[D][MAXP], c3[D][MAXP];
-    float xs[D][MAXP], ls[D][MAXP], hs[D][MAXP];
+    float xs[D][MAXP], ls[D][MAXP], hs[D][MAXP], dxa[D][MAXP];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int s = max(s0 - j, 0);
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
         // a restart line has no previous line: its own position stands in
         const int64_t pidx = restart ? idx : idx + back_off;
         gy[j][i] = bl(a.gy, idx);
-        ug[j][i] = bl(a.u, idx) * gy[j][i];
+        ug[j][i] = gsc * bl(a.u, idx) * gy[j][i];
         g0[j][i] = bl(a.l0, idx + lsh);
         g1[j][i] = bl(a.l1, idx + lsh);
         g2[j][i] = bl(a.l2, idx + lsh);
@@ -227,8 +237,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
           xs[j][i] = bl(a.x, idx);
           ls[j][i] = bl(a.lam, idx);
           hs[j][i] = first ? a.hbuf[idx] : a.acc[4 * ps + idx];
+          dxa[j][i] = (a.dxacc && !a.dxfirst) ? a.dxacc[idx] : 0.f;
         } else {
-          xs[j][i] = 0.f; ls[j][i] = 0.f; hs[j][i] = 0.f;
+          xs[j][i] = 0.f; ls[j][i] = 0.f; hs[j][i] = 0.f; dxa[j][i] = 0.f;
         }
       }
     }
@@ -278,10 +289,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
           dl1 += c2[j][i];
           dl2 += c3[j][i];
           if (last) {
-            Store<T>::put(a.dx, idx, ls[j][i] * dphi);
+            const float dxv = dxa[j][i] + ls[j][i] * dphi;
+            if (!a.dxacc || a.dxlast)
+              Store<T>::put(a.dx, idx, dxv);
+            else
+              a.dxacc[idx] = dxv;
             Store<T>::put(a.dlam, idx, xs[j][i] * dphi);
             put_dl(a, idx, dl0, dl1, dl2);
-            Store<T>::put(a.du, idx, gy[j][i] * hs[j][i]);
+            Store<T>::put(a.du, idx, gsc * gy[j][i] * hs[j][i]);
           } else {
             a.acc[idx] = dphi;
             a.acc[ps + idx] = dl0;
@@ -485,6 +500,9 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
   a.C = pr.C;
   a.Cl = pr.Cl;
   a.dlw = pr.dlw;
+  a.gscale = nullptr;
+  a.dxacc = nullptr;
+  a.dxfirst = a.dxlast = false;
   const bool t2b = pr.mask & 1u, b2t = pr.mask & 2u, l2r = pr.mask & 4u, r2l = pr.mask & 8u;
   hipError_t e;
   bool acc_written = false;
@@ -587,6 +605,258 @@ hipError_t launch_bwd_reduce_logits(const BwdProblem& pr, hipStream_t stream, Tr
 hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr) {
   if (pr.dtype == GSPN_F32) return launch_bwd_stream_dt<float>(pr, ws, stream, tr);
   return launch_bwd_stream_dt<bf16_t>(pr, ws, stream, tr);
+}
+
+// ===========================================================================
+// Per-direction parameters with a per-channel merger, backward. Direction d
+// is one scan with its own lambda, logits and u (at element offset d *
+// dir_stride), whose error term starts from merge[d][c] u gy; each direction
+// runs the two launches above as a single direction (first and last), with
+// its gradients written straight to its slice of the outputs, and
+//   dx        = sum_d lambda_d d(lambda x)_d   (fp32 accumulator),
+//   du_d      = merge[d][c] gy h_d,
+//   dmerge[d][c] = sum over images and pixels of u_d gy h_d.
+// Horizontal directions run on transposed copies (x, gy and the direction's
+// five tensors), their five gradients are transposed back, and their share
+// of dx travels in a transposed accumulator.
+// ===========================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dirs_zero(T* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    Store<T>::put(p, i, 0.f);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dirs_store_dx(const float* acc, T* dx, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    Store<T>::put(dx, i, acc[i]);
+}
+
+// one block per channel: images in order, a fixed tree over the threads, in
+// fp64, so the sum does not depend on timing
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dirs_merge(const T* u, const T* gy, const float* h,
+                                                      int64_t B, int64_t C, int64_t HW,
+                                                      float* dmerge) {
+  __shared__ double red[256];
+  const int64_t c = blockIdx.x;
+  double sum = 0.0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t base = (b * C + c) * HW;
+    for (int64_t i = threadIdx.x; i < HW; i += 256)
+      sum += static_cast<double>(bl(u, base + i)) * static_cast<double>(bl(gy, base + i)) *
+             static_cast<double>(h[base + i]);
+  }
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dmerge[c] = static_cast<float>(red[0]);
+}
+
+namespace {
+struct DirsLayout {
+  size_t hbuf, dxacc, x_t, gy_t, par_t, out_t, dxacc_t, total;
+};
+
+DirsLayout dirs_layout(int64_t planes, int64_t H, int64_t W, uint32_t mask, size_t es) {
+  const size_t px = static_cast<size_t>(planes * H * W);
+  const bool hz = mask & 12u;
+  DirsLayout L;
+  size_t o = 0;
+  L.hbuf = o; o = al256(o + px * 4);
+  L.dxacc = o; o = al256(o + px * 4);
+  L.x_t = o; o = al256(o + (hz ? px * es : 0));
+  L.gy_t = o; o = al256(o + (hz ? px * es : 0));
+  L.par_t = o; o = al256(o + (hz ? 5 * px * es : 0));
+  L.out_t = o; o = al256(o + (hz ? 5 * px * es : 0));
+  L.dxacc_t = o; o = al256(o + (hz ? px * 4 : 0));
+  L.total = o;
+  return L;
+}
+
+int64_t fill_grid(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return b < 65536 * 16 ? (b > 0 ? b : 1) : 65536 * 16;
+}
+}  // namespace
+
+size_t bwd_dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                gspn_dtype dt) {
+  return dirs_layout(planes, H, W, mask, dt == GSPN_F32 ? 4 : 2).total;
+}
+
+template <typename T>
+static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& ex, void* ws,
+                                     hipStream_t stream, Tracer* tr) {
+  const int64_t planes = pr.B * pr.C;
+  const int64_t P = planes * pr.H * pr.W;
+  const DirsLayout lay = dirs_layout(planes, pr.H, pr.W, pr.mask, sizeof(T));
+  char* wsb = static_cast<char*>(ws);
+  const int64_t ds = ex.dir_stride;
+  const T* x = static_cast<const T*>(pr.x);
+  const T* gy = static_cast<const T*>(pr.gy);
+  const T* lam = static_cast<const T*>(pr.lam);
+  const T* u = static_cast<const T*>(pr.u);
+  const T* lg[3] = {static_cast<const T*>(pr.l[0]), static_cast<const T*>(pr.l[1]),
+                    static_cast<const T*>(pr.l[2])};
+  T* dx = static_cast<T*>(pr.dx);
+  T* dlam = static_cast<T*>(pr.dlam);
+  T* du = static_cast<T*>(pr.du);
+  T* dl[3] = {static_cast<T*>(pr.dl[0]), static_cast<T*>(pr.dl[1]), static_cast<T*>(pr.dl[2])};
+  float* hbuf = reinterpret_cast<float*>(wsb + lay.hbuf);
+  float* dxacc = reinterpret_cast<float*>(wsb + lay.dxacc);
+  hipError_t e;
+
+  if (planes == 0) {
+    // no image: the merge gradients are empty sums
+    if (ex.dmerge && pr.C > 0) {
+      tr->before(stream, "bwd_dirs_zero", pr.C);
+      hipLaunchKernelGGL(bwd_dirs_zero<float>, dim3(static_cast<unsigned>(fill_grid(4 * pr.C))),
+                         dim3(256), 0, stream, ex.dmerge, 4 * pr.C);
+      tr->after(stream);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+
+  // the order of the passes: horizontal first (their share of dx is
+  // transposed back), then vertical
+  const int order[4] = {2, 3, 0, 1};
+  int first = -1, last = -1;
+  for (int i = 0; i < 4; ++i)
+    if (pr.mask & (1u << order[i])) {
+      if (first < 0) first = order[i];
+      last = order[i];
+    }
+  const bool vert_last = last == 0 || last == 1;
+
+  // directions outside the mask: zero gradients
+  for (int d = 0; d < 4; ++d) {
+    if (pr.mask & (1u << d)) continue;
+    T* outs[5] = {dlam + d * P, dl[0] + d * P, dl[1] + d * P, dl[2] + d * P, du + d * P};
+    for (T* o : outs) {
+      tr->before(stream, "bwd_dirs_zero", planes);
+      hipLaunchKernelGGL(bwd_dirs_zero<T>, dim3(static_cast<unsigned>(fill_grid(P))), dim3(256), 0,
+                         stream, o, P);
+      tr->after(stream);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (ex.dmerge) {
+      tr->before(stream, "bwd_dirs_zero", pr.C);
+      hipLaunchKernelGGL(bwd_dirs_zero<float>, dim3(1), dim3(256), 0, stream,
+                         ex.dmerge + d * pr.C, pr.C);
+      tr->after(stream);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+
+  BwArgs<T> base;
+  std::memset(&base, 0, sizeof(base));
+  base.pstride = P;
+  base.hbuf = hbuf;
+  base.acc = nullptr;
+  base.G = static_cast<int>(pr.G);
+  base.C = pr.C;
+  base.Cl = pr.C;
+  base.dlw = nullptr;
+
+  auto merge_grad = [&](int d, const T* ud, const T* gyd) -> hipError_t {
+    if (!ex.dmerge) return hipSuccess;
+    tr->before(stream, "bwd_dirs_merge", pr.C);
+    hipLaunchKernelGGL(bwd_dirs_merge<T>, dim3(static_cast<unsigned>(pr.C)), dim3(256), 0, stream,
+                       ud, gyd, hbuf, pr.B, pr.C, pr.H * pr.W, ex.dmerge + d * pr.C);
+    tr->after(stream);
+    return hipGetLastError();
+  };
+
+  if (pr.mask & 12u) {
+    T* x_t = reinterpret_cast<T*>(wsb + lay.x_t);
+    T* gy_t = reinterpret_cast<T*>(wsb + lay.gy_t);
+    T* par_t = reinterpret_cast<T*>(wsb + lay.par_t);
+    T* out_t = reinterpret_cast<T*>(wsb + lay.out_t);
+    float* dxacc_t = reinterpret_cast<float*>(wsb + lay.dxacc_t);
+    {
+      const T* src[2] = {x, gy};
+      T* dst[2] = {x_t, gy_t};
+      if ((e = transpose<T>(src, dst, 2, planes, static_cast<int>(pr.H), static_cast<int>(pr.W),
+                            stream, tr)) != hipSuccess)
+        return e;
+    }
+    for (int d = 2; d < 4; ++d) {
+      if (!(pr.mask & (1u << d))) continue;
+      const T* src[5] = {lam + d * ds, lg[0] + d * ds, lg[1] + d * ds, lg[2] + d * ds, u + d * ds};
+      T* dst[5];
+      for (int i = 0; i < 5; ++i) dst[i] = par_t + i * P;
+      if ((e = transpose<T>(src, dst, 5, planes, static_cast<int>(pr.H), static_cast<int>(pr.W),
+                            stream, tr)) != hipSuccess)
+        return e;
+      BwArgs<T> t = base;
+      t.x = x_t;
+      t.gy = gy_t;
+      t.lam = dst[0]; t.l0 = dst[1]; t.l1 = dst[2]; t.l2 = dst[3]; t.u = dst[4];
+      t.dlam = out_t; t.dl0 = out_t + P; t.dl1 = out_t + 2 * P; t.dl2 = out_t + 3 * P;
+      t.du = out_t + 4 * P;
+      t.dx = nullptr;
+      t.dxacc = dxacc_t;
+      t.dxfirst = d == first;
+      t.dxlast = false;
+      t.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+      t.H = static_cast<int>(pr.W);
+      t.W = static_cast<int>(pr.H);
+      if ((e = run_direction(t, d == 2 ? 0 : 1, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess)
+        return e;
+      if ((e = merge_grad(d, dst[4], gy_t)) != hipSuccess) return e;
+      // the five gradients back to row-major, into direction d's slices
+      const T* bs[5] = {out_t, out_t + P, out_t + 2 * P, out_t + 3 * P, out_t + 4 * P};
+      T* bd[5] = {dlam + d * P, dl[0] + d * P, dl[1] + d * P, dl[2] + d * P, du + d * P};
+      if ((e = transpose<T>(bs, bd, 5, planes, static_cast<int>(pr.W), static_cast<int>(pr.H),
+                            stream, tr)) != hipSuccess)
+        return e;
+    }
+    const float* fs[1] = {dxacc_t};
+    float* fd[1] = {dxacc};
+    if ((e = transpose<float>(fs, fd, 1, planes, static_cast<int>(pr.W), static_cast<int>(pr.H),
+                              stream, tr)) != hipSuccess)
+      return e;
+  }
+  for (int d = 0; d < 2; ++d) {
+    if (!(pr.mask & (1u << d))) continue;
+    BwArgs<T> a = base;
+    a.x = x;
+    a.gy = gy;
+    a.lam = lam + d * ds; a.l0 = lg[0] + d * ds; a.l1 = lg[1] + d * ds; a.l2 = lg[2] + d * ds;
+    a.u = u + d * ds;
+    a.dlam = dlam + d * P; a.dl0 = dl[0] + d * P; a.dl1 = dl[1] + d * P; a.dl2 = dl[2] + d * P;
+    a.du = du + d * P;
+    a.dx = dx;
+    a.dxacc = dxacc;
+    a.dxfirst = d == first;
+    a.dxlast = d == last;
+    a.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+    a.H = static_cast<int>(pr.H);
+    a.W = static_cast<int>(pr.W);
+    if ((e = run_direction(a, d, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess) return e;
+    if ((e = merge_grad(d, a.u, gy)) != hipSuccess) return e;
+  }
+  if (!vert_last) {
+    tr->before(stream, "bwd_dirs_store_dx", planes);
+    hipLaunchKernelGGL(bwd_dirs_store_dx<T>, dim3(static_cast<unsigned>(fill_grid(P))), dim3(256), 0,
+                       stream, dxacc, dx, P);
+    tr->after(stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_dirs(const BwdProblem& pr, const BwdDirsExtra& ex, void* ws,
+                           hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_bwd_dirs_dt<float>(pr, ex, ws, stream, tr);
+  return launch_bwd_dirs_dt<bf16_t>(pr, ex, ws, stream, tr);
 }
 
 }  // namespace gspn

@@ -135,6 +135,20 @@ size_t bwd_stream_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t
                                   gspn_dtype dt);
 hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream, Tracer* tr);
 
+// backward pass of the per-direction layer (gspn_bwd_stream.hip): pr's
+// lambda, logits and u are direction 0's, direction d's sit at element
+// offset d * dir_stride; the gradients dl / dlam / du are [4][B*C*H*W]
+// (slice d = direction d), dx [B*C*H*W]; dmerge [4][C] fp32, or null
+struct BwdDirsExtra {
+  int64_t dir_stride;
+  const float* merge;   // [4][C] device, or null (all ones)
+  float* dmerge;
+};
+size_t bwd_dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                gspn_dtype dt);
+hipError_t launch_bwd_dirs(const BwdProblem& pr, const BwdDirsExtra& ex, void* ws,
+                           hipStream_t stream, Tracer* tr);
+
 // backward pass, large-plane pipeline (gspn_bwd_tpipe.hip): planes with both
 // sides even, W <= 1024, H <= 2048, every pointer aligned to 2 elements
 bool btpipe_fits(int64_t H, int64_t W);

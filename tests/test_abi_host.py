@@ -365,6 +365,68 @@ def test_dirs_empty_batch_is_ok_without_gpu(L):
     assert dcall(L, B=0) == 0
 
 
+# ---- per-direction backward (gspn_propagate_backward_dirs_ws) ------------------
+def bdcall(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
+           u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, gy=BASE + 9 * SZ, B=2, C=3, H=20,
+           W=16, mask=15, G=0, dt=0, gx=BASE + 10 * SZ,
+           glg=(BASE + 11 * SZ, BASE + 12 * SZ, BASE + 13 * SZ), glam=BASE + 14 * SZ,
+           gu=BASE + 15 * SZ, gm=BASE + 16 * SZ, ws=None, ws_bytes=0):
+    arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
+    garr = None if glg is None else (ctypes.c_void_p * 3)(*glg)
+    return L.gspn_propagate_backward_dirs_ws(x, arr, lam, u, stride, merge, gy, B, C, H, W, mask,
+                                             G, dt, gx, garr, glam, gu, gm, ws, ws_bytes, None)
+
+
+def test_backward_dirs_workspace_bytes(L):
+    # stored states and the fp32 sum for grad_x; with a horizontal direction
+    # also transposed x and grad_out, five inputs and five gradients of one
+    # direction, and a transposed fp32 sum (DP * 4 and DP * 2 are multiples
+    # of 256 here)
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * 15
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 1) == DP * (4 * 3 + 2 * 12)
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 1) == DP * 4 * 2
+    assert L.gspn_backward_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0   # above the limit
+    assert g.backward_workspace_bytes_dirs(2, 3, 20, 16, g.L2R) == DP * 4 * 15
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "GSPN_E_NULL"),
+    (dict(lg=None), "GSPN_E_NULL"),
+    (dict(gy=None), "GSPN_E_NULL"),
+    (dict(gx=None), "GSPN_E_NULL"),
+    (dict(glg=(BASE + 11 * SZ, None, BASE + 13 * SZ)), "GSPN_E_NULL"),
+    (dict(stride=DP - 1), "GSPN_E_SHAPE"),
+    (dict(H=8200, W=4), "GSPN_E_SHAPE"),
+    (dict(mask=0), "GSPN_E_DIRMASK"),
+    (dict(G=-1), "GSPN_E_GROUP"),
+    (dict(dt=3), "GSPN_E_DTYPE"),
+    (dict(gm=BASE + 16 * SZ + 2), "GSPN_E_ALIGN"),
+    (dict(dt=1, glam=BASE + 14 * SZ + 1), "GSPN_E_ALIGN"),
+    (dict(gx=BASE), "GSPN_E_ALIAS"),                                  # grad_x on x
+    (dict(glam=BASE + 5 * SZ + DP * 4), "GSPN_E_ALIAS"),              # on direction 1's u
+    (dict(gm=BASE + 8 * SZ + 4), "GSPN_E_ALIAS"),                     # on the merge weights
+    (dict(gu=BASE + 14 * SZ + 3 * DP * 4), "GSPN_E_ALIAS"),           # inside grad_lambda's slices
+])
+def test_backward_dirs_rejects_bad_arguments(L, kw, status):
+    assert bdcall(L, **kw) == g.STATUS[status]
+    assert L.gspn_last_error().decode() != ""
+
+
+def test_backward_dirs_workspace_checks(L):
+    need = L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0)
+    assert bdcall(L) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert bdcall(L, ws=BASE + 17 * SZ, ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert bdcall(L, ws=BASE + 17 * SZ + 16, ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]
+    assert bdcall(L, ws=BASE + 9 * SZ, ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]    # grad_out
+    assert bdcall(L, ws=BASE + 15 * SZ, ws_bytes=need) == g.STATUS["GSPN_E_ALIAS"]   # grad_u
+    # without a merger and without the merge gradient the pointers may be NULL
+    assert bdcall(L, merge=None, gm=None) == g.STATUS["GSPN_E_WORKSPACE"]
+
+
+def test_backward_dirs_empty_batch_is_ok_without_gpu(L):
+    assert bdcall(L, B=0, gm=None) == 0
+
+
 # ---- module prologue (gspn_prologue, gspn_module_ws) -------------------------
 # fake addresses again; every call fails validation or has B = 0
 PB, PCIN, PC, PH, PW = 2, 6, 4, 5, 7
