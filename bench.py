@@ -63,6 +63,7 @@ PLAN_SOURCES = {
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
     "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_device.hpp"),
+    "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
     "prologue": ("gspn_prologue.hip", "gspn_device.hpp"),
     "module": ("gspn_prologue.hip", "gspn_plane.hip", "gspn_band.hip", "gspn_tpipe.hip",
@@ -155,6 +156,12 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
           bt_hB  (8 + 3 s) copy read + 8 states read + 20 horizontal parts
           bt_vB  7 s inputs + 8 states read + 20 horizontal parts + 6 s out
           (no horizontal direction: no copy, no parts, no bt_hA / bt_hB)
+      backward of the per-direction layer (each direction a single-direction
+      bwd_fwd / bwd_adj pair on its own tensors, see bwd_dirs_path_bytes for
+      the whole path):
+          bwd_dirs_zero  one gradient slice of an unselected direction (s)
+          bwd_dirs_store_dx  the fp32 sum read, dx written (4 + s)
+          bwd_dirs_merge  u and grad_out read (2 s) with the stored states (4)
     Per-direction parameters (one pass per direction; horizontal directions
     run over transposed copies):
       dir_vert  x and the direction's lambda, l0, l1, l2, u read (6 s), the
@@ -189,6 +196,9 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "bwd_transpose": 2 * 7 * s if planes == w.B * w.C else 2 * 4,
         "bwd_finish": 20 + 9 * s,
         "bband_kernel": 20 * s + 40,
+        "bwd_dirs_zero": s,
+        "bwd_dirs_store_dx": 4 + s,
+        "bwd_dirs_merge": 2 * s + 4,
         "bt_vA": 7 * s + 8 + (8 + 3 * s if hz else 0),
         "bt_hA": 8 + 3 * s + 8,
         "bt_hB": 8 + 3 * s + 8 + 20,
@@ -203,16 +213,31 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     return per * px
 
 
+def bwd_dirs_path_bytes(w) -> float:
+    """Design bytes per pixel of the per-direction backward: x and grad_out
+    transposed (2 * 2 s) and, per horizontal direction, its five tensors in
+    and its five gradients back (2 * 10 s), the fp32 sum of dx back (8); per
+    direction the forward scan (5 s in, 4 states out), the reverse scan (u,
+    grad_out, three logits, x and lambda read: 7 s; states 4; the dx sum read
+    and written: 8; five gradients written: 5 s) and the merge reduction
+    (2 s + 4)."""
+    s = 4 if w.dtype == "f32" else 2
+    nh = bin(w.dirs & 12).count("1")
+    per_dir = (5 * s + 4) + (12 * s + 12) + (2 * s + 4)
+    return (4 * s if nh else 0) + nh * (20 * s) + (8 if nh else 0) + w.ndirs * per_dir
+
+
 def qmin_per_pixel(w, bwd: bool) -> float:
     """Compulsory HBM bytes per pixel: x, lambda, u (and grad_out) read once,
     out (or the gradients) written once, plus the logits (and their
     gradients) at Cl / C of a tensor each when they are shared. Per-direction
-    parameters (forward only): x, each selected direction's lambda, l0, l1,
-    l2 and u read once, out written once."""
+    parameters: x, each selected direction's lambda, l0, l1, l2 and u read
+    once, out written once; backward: x, grad_out and the directions' five
+    tensors read, dx and the directions' five gradients written."""
     s = 4 if w.dtype == "f32" else 2
     if w.per_direction:
         if bwd:
-            raise ValueError("no backward pass for per-direction parameters")
+            return (3 + 10 * w.ndirs) * s
         return (2 + 5 * w.ndirs) * s
     if w.prologue_cin:
         if bwd:
@@ -290,6 +315,18 @@ def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
         return t.reshape(4, 1, planes, w.H, w.W)
 
     threads = min(cores, planes)
+    if w.per_direction and grad_out is not None:
+        merge = inp_dev["merge"].cpu().numpy()[:, np.arange(planes) % w.C]
+        args = [host(inp_dev["x"])] + [host_dirs(inp_dev[k]) for k in ("l0", "l1", "l2",
+                                                                         "lam", "u")]
+        t0 = time.perf_counter()
+        oracle.backward_dirs(*args, host(grad_out), merge=merge, dirs=w.dirs,
+                             group_rows=w.group_rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        steps = planes * w.H * w.W * w.ndirs
+        return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
+                "sample": f"per-direction backward, first {planes} of {w.B * w.C} planes "
+                          f"({w.H}x{w.W}, {w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}
     if w.per_direction:
         # sample plane p is channel p % C of the merge weights
         merge = inp_dev["merge"].cpu().numpy()[:, np.arange(planes) % w.C]
@@ -433,16 +470,17 @@ def main() -> int:
     bwd = args.backward
     mod = w.prologue_cin > 0
     pro_only = args.prologue
-    if bwd and (w.per_direction or mod):
-        print("no backward pass for per-direction parameters or the module prologue",
-              file=sys.stderr)
+    if bwd and mod:
+        print("no backward pass for the module prologue", file=sys.stderr)
         return 2
     if pro_only and not mod:
         print("--prologue needs a module workload (*_mod)", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     dt_code = g.GSPN_F32 if w.dtype == "f32" else g.GSPN_BF16
-    if bwd:
+    if bwd and w.per_direction:
+        plan = "bwd_dirs"
+    elif bwd:
         plan = g.backward_plan_name(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code)
     elif w.per_direction:
         plan = "dirs"
@@ -471,7 +509,16 @@ def main() -> int:
             if bwd:
                 st["gy"] = make_grad_out(w, seed=seed + 1000).to(dev)
         sets.append(st)
-    if bwd:
+    if bwd and w.per_direction:
+        outs = []
+        for st in sets:
+            o = {k: torch.empty_like(st["lam"]) for k in g.PARAM_NAMES}
+            o["x"] = torch.empty_like(st["x"])
+            o["merge"] = torch.empty((4, w.C), dtype=torch.float32, device=dev)
+            outs.append(o)
+        ws_bytes = g.backward_workspace_bytes_dirs(w.B, w.C, w.H, w.W, w.dirs, w.group_rows,
+                                                   dt_code)
+    elif bwd:
         outs = [{k: torch.empty_like(st[k] if k in ("l0", "l1", "l2") else st["x"])
                  for k in g.GRAD_NAMES} for st in sets]
         ws_bytes = g.backward_workspace_bytes(w.B, w.C, w.H, w.W, w.dirs, w.group_rows, dt_code,
@@ -494,7 +541,12 @@ def main() -> int:
 
     def step(i):
         st = sets[i % nsets]
-        if bwd:
+        if bwd and w.per_direction:
+            g.propagate_backward_dirs(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
+                                      st["gy"], merge=st["merge"], dirs=w.dirs,
+                                      group_rows=w.group_rows, grads=outs[i % nsets],
+                                      workspace=ws if ws_bytes else None, stream=stream)
+        elif bwd:
             g.propagate_backward(st["x"], (st["l0"], st["l1"], st["l2"]), st["lam"], st["u"],
                                  st["gy"], dirs=w.dirs, group_rows=w.group_rows,
                                  grads=outs[i % nsets], workspace=ws if ws_bytes else None,
@@ -562,6 +614,10 @@ def main() -> int:
         first, last = (i == passes[0], i == passes[-1]) if i in passes else (True, True)
         kb[name] = kb.get(name, 0.0) + design_bytes(name, np_, w, first=first, last=last)
     path_bytes = sum(kb.values())
+    if bwd and w.per_direction:
+        # the transposes of this path move tensors the trace does not tell
+        # apart: the path's design bytes are counted as a whole
+        path_bytes = bwd_dirs_path_bytes(w) * w.pixels
     # Roofline unit: the launches of one step. A single launch is timed by its
     # own events; a pipeline of several launches (overlapping on two streams)
     # by the step time. Algorithmic bytes: the compulsory Q_min = 7 s per

@@ -12,7 +12,8 @@ KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
            "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",
-           "bt_vA", "bt_hA", "bt_hB", "bt_vB"]
+           "bt_vA", "bt_hA", "bt_hB", "bt_vB", "bwd_dirs_zero", "bwd_dirs_store_dx",
+           "bwd_dirs_merge"]
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -20,13 +21,17 @@ KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "
 def test_input_sets_and_qmin(name, bwd):
     w = WORKLOADS[name]
     s = 4 if w.dtype == "f32" else 2
-    if w.per_direction or w.prologue_cin:
-        if bwd:
-            with pytest.raises(ValueError):
-                bench.qmin_per_pixel(w, bwd)
-            return
-        want = (2 + 5 * w.ndirs) * s if w.per_direction else (w.prologue_cin / w.C + 1) * s
+    if w.prologue_cin and bwd:
+        with pytest.raises(ValueError):
+            bench.qmin_per_pixel(w, bwd)
+        return
+    if w.per_direction:
+        # forward: x and the directions' five tensors in, out; backward: x,
+        # grad_out and the five tensors in, dx and the five gradients out
+        want = ((3 + 10 * w.ndirs) if bwd else (2 + 5 * w.ndirs)) * s
         assert bench.qmin_per_pixel(w, bwd) == want
+    elif w.prologue_cin:
+        assert bench.qmin_per_pixel(w, bwd) == (w.prologue_cin / w.C + 1) * s
     n = bench.input_sets(w, bwd)
     assert isinstance(n, int) and 1 <= n <= 8
     q = bench.qmin_per_pixel(w, bwd)
@@ -91,3 +96,13 @@ def test_prologue_work():
     wd = WORKLOADS["dit_16x16_mod"]
     f2, b2 = bench.prologue_work(wd)
     assert f2 / 2500e12 > b2 / 8000e9     # C = 1152: MFMA-bound
+
+
+def test_per_direction_backward_path_bytes():
+    """Four directions, bf16: x and grad_out transposed, ten tensors through
+    each horizontal direction's transposes, the dx sum back; per direction
+    the scan pair and the merge reduction."""
+    w = WORKLOADS["t2i_2048x1024_pd"]
+    s = 2
+    per_dir = (5 * s + 4) + (12 * s + 12) + (2 * s + 4)
+    assert bench.bwd_dirs_path_bytes(w) == 4 * s + 2 * 20 * s + 8 + 4 * per_dir
