@@ -63,7 +63,7 @@ PLAN_SOURCES = {
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
     "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_device.hpp"),
-    "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
+    "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_dirs.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
     "prologue": ("gspn_prologue.hip", "gspn_device.hpp"),
     "module": ("gspn_prologue.hip", "gspn_plane.hip", "gspn_band.hip", "gspn_tpipe.hip",
@@ -161,7 +161,13 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
       the whole path):
           bwd_dirs_zero  one gradient slice of an unselected direction (s)
           bwd_dirs_store_dx  the fp32 sum read, dx written (4 + s)
-          bwd_dirs_merge  u and grad_out read (2 s) with the stored states (4)
+          bwd_dirs_tr  one tensor read and written transposed (2 s), counted
+          per plane and tensor
+          bwd_dirs_tr_acc  the transposed fp32 sum of dx read and written
+          row-major (8)
+          bwd_dirs_merge  the fp64 partials that bwd_adj leaves, 4 per plane
+          (8 bytes each; the products u gy h are summed inside bwd_adj,
+          which reads all three anyway)
     Per-direction parameters (one pass per direction; horizontal directions
     run over transposed copies):
       dir_vert  x and the direction's lambda, l0, l1, l2, u read (6 s), the
@@ -198,7 +204,9 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "bband_kernel": 20 * s + 40,
         "bwd_dirs_zero": s,
         "bwd_dirs_store_dx": 4 + s,
-        "bwd_dirs_merge": 2 * s + 4,
+        "bwd_dirs_tr": 2 * s,
+        "bwd_dirs_tr_acc": 8,
+        "bwd_dirs_merge": 4 * 8 / (w.H * w.W),
         "bt_vA": 7 * s + 8 + (8 + 3 * s if hz else 0),
         "bt_hA": 8 + 3 * s + 8,
         "bt_hB": 8 + 3 * s + 8 + 20,
@@ -219,11 +227,11 @@ def bwd_dirs_path_bytes(w) -> float:
     and its five gradients back (2 * 10 s), the fp32 sum of dx back (8); per
     direction the forward scan (5 s in, 4 states out), the reverse scan (u,
     grad_out, three logits, x and lambda read: 7 s; states 4; the dx sum read
-    and written: 8; five gradients written: 5 s) and the merge reduction
-    (2 s + 4)."""
+    and written: 8; five gradients written: 5 s); the merge gradients come
+    out of the reverse scan, whose per-plane partials are too few to count."""
     s = 4 if w.dtype == "f32" else 2
     nh = bin(w.dirs & 12).count("1")
-    per_dir = (5 * s + 4) + (12 * s + 12) + (2 * s + 4)
+    per_dir = (5 * s + 4) + (12 * s + 12)
     return (4 * s if nh else 0) + nh * (20 * s) + (8 if nh else 0) + w.ndirs * per_dir
 
 

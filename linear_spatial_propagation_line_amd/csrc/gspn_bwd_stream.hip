@@ -82,6 +82,9 @@ struct BwArgs {
   const float* gscale;
   float* dxacc;
   bool dxfirst, dxlast;
+  // per-plane merge-gradient partials, sum over the plane of u gy h in fp64
+  // (null: not wanted); only with first and last set
+  double* dmpart;
 };
 
 // logit gradients of pixel idx: to the storage type, or per plane in fp32
@@ -194,13 +197,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   float a1[MAXP];
 #pragma unroll
   for (int i = 0; i < MAXP; ++i) a1[i] = 0.f;
+  double dm = 0.0;   // this thread's share of the merge-gradient partial
   for (int o = threadIdx.x; o < (DB ? 4 : 2) * n_o; o += blockDim.x) sm[o] = 0.f;
   __syncthreads();
 
   int par = 0;
   for (int s0 = n_s - 1; s0 >= 0; s0 -= D) {
     // ---- loads of D steps
-    float gy[D][MAXP], ug[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP];
+    float gy[D][MAXP], ugp[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP];
     float hc[D][MAXP], hl[D][MAXP], hr[D][MAXP];
     float c0[D][MAXP], c1[D][MAXP], c2[D][MAXP], c3[D][MAXP];
     float xs[D][MAXP], ls[D][MAXP], hs[D][MAXP], dxa[D][MAXP];
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
         // a restart line has no previous line: its own position stands in
         const int64_t pidx = restart ? idx : idx + back_off;
         gy[j][i] = bl(a.gy, idx);
-        ug[j][i] = gsc * bl(a.u, idx) * gy[j][i];
+        ugp[j][i] = bl(a.u, idx) * gy[j][i];   // u gy
         g0[j][i] = bl(a.l0, idx + lsh);
         g1[j][i] = bl(a.l1, idx + lsh);
         g2[j][i] = bl(a.l2, idx + lsh);
@@ -244,6 +248,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
       }
     }
     // ---- D steps
+    // merge-gradient products of this batch: at most D terms per position
+    // summed in fp32, then added once to the fp64 total (fp64 arithmetic in
+    // every step would lengthen each step, which the block waits for)
+    float pm[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) pm[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int s = s0 - j;
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
         if (o < n_o) {
           const int r = vert ? pos : o, c = vert ? o : pos;
           const int64_t idx = base + static_cast<int64_t>(r) * W + c;
-          float e = ug[j][i] + a1[i];
+          float e = gsc * ugp[j][i] + a1[i];
           if (o + 1 < n_o) e += A0[o + 1];
           if (o > 0) e += A2[o - 1];
           float dl0 = 0.f, dl1 = 0.f, dl2 = 0.f, s0v = 0.f, s2v = 0.f, w1e = 0.f;
@@ -297,6 +307,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
             Store<T>::put(a.dlam, idx, xs[j][i] * dphi);
             put_dl(a, idx, dl0, dl1, dl2);
             Store<T>::put(a.du, idx, gsc * gy[j][i] * hs[j][i]);
+            pm[i] = __builtin_fmaf(ugp[j][i], hs[j][i], pm[i]);
           } else {
             a.acc[idx] = dphi;
             a.acc[ps + idx] = dl0;
@@ -313,6 +324,24 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
       }
       par ^= 1;
       __syncthreads();
+    }
+    if (a.dmpart) {
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) dm += static_cast<double>(pm[i]);
+    }
+  }
+  if (a.dmpart) {
+    // a fixed tree: butterfly inside each wavefront, then the wavefronts in
+    // order, so the partial does not depend on timing
+    __shared__ double red[kBwThreads / 64];
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) dm += __shfl_xor(dm, m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dm;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) t += red[k];
+      a.dmpart[blockIdx.x] = t;
     }
   }
 }
@@ -503,6 +532,7 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
   a.gscale = nullptr;
   a.dxacc = nullptr;
   a.dxfirst = a.dxlast = false;
+  a.dmpart = nullptr;
   const bool t2b = pr.mask & 1u, b2t = pr.mask & 2u, l2r = pr.mask & 4u, r2l = pr.mask & 8u;
   hipError_t e;
   bool acc_written = false;
@@ -615,10 +645,13 @@ hipError_t launch_bwd_stream(const BwdProblem& pr, void* ws, hipStream_t stream,
 // its gradients written straight to its slice of the outputs, and
 //   dx        = sum_d lambda_d d(lambda x)_d   (fp32 accumulator),
 //   du_d      = merge[d][c] gy h_d,
-//   dmerge[d][c] = sum over images and pixels of u_d gy h_d.
+//   dmerge[d][c] = sum over images and pixels of u_d gy h_d
+// (the reverse scan, which holds u_d, gy and h_d at every pixel, leaves one
+// fp64 partial per plane; a last launch sums the images in order).
 // Horizontal directions run on transposed copies (x, gy and the direction's
 // five tensors), their five gradients are transposed back, and their share
-// of dx travels in a transposed accumulator.
+// of dx travels in a transposed accumulator; the transposes are the
+// per-direction forward's (bf16 element pairs where the shapes allow).
 // ===========================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dirs_zero(T* p, int64_t n) {
@@ -634,33 +667,24 @@ __global__ __launch_bounds__(256) void bwd_dirs_store_dx(const float* acc, T* dx
     Store<T>::put(dx, i, acc[i]);
 }
 
-// one block per channel: images in order, a fixed tree over the threads, in
-// fp64, so the sum does not depend on timing
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_dirs_merge(const T* u, const T* gy, const float* h,
-                                                      int64_t B, int64_t C, int64_t HW,
-                                                      float* dmerge) {
-  __shared__ double red[256];
-  const int64_t c = blockIdx.x;
+// merge gradients from the per-plane partials of each direction
+// ([4][planes], fp64): one thread per (direction, channel) sums the images in
+// order; directions outside the mask (and an empty batch) get zeros
+__global__ __launch_bounds__(256) void bwd_dirs_merge(const double* part, int64_t B, int64_t C,
+                                                      uint32_t mask, float* dmerge) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= 4 * C) return;
+  const int d = static_cast<int>(i / C);
+  const int64_t c = i - d * C;
   double sum = 0.0;
-  for (int64_t b = 0; b < B; ++b) {
-    const int64_t base = (b * C + c) * HW;
-    for (int64_t i = threadIdx.x; i < HW; i += 256)
-      sum += static_cast<double>(bl(u, base + i)) * static_cast<double>(bl(gy, base + i)) *
-             static_cast<double>(h[base + i]);
-  }
-  red[threadIdx.x] = sum;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) dmerge[c] = static_cast<float>(red[0]);
+  if (mask & (1u << d))
+    for (int64_t b = 0; b < B; ++b) sum += part[d * B * C + b * C + c];
+  dmerge[i] = static_cast<float>(sum);
 }
 
 namespace {
 struct DirsLayout {
-  size_t hbuf, dxacc, x_t, gy_t, par_t, out_t, dxacc_t, total;
+  size_t hbuf, dxacc, x_t, gy_t, par_t, out_t, dxacc_t, dmpart, total;
 };
 
 DirsLayout dirs_layout(int64_t planes, int64_t H, int64_t W, uint32_t mask, size_t es) {
@@ -675,6 +699,7 @@ DirsLayout dirs_layout(int64_t planes, int64_t H, int64_t W, uint32_t mask, size
   L.par_t = o; o = al256(o + (hz ? 5 * px * es : 0));
   L.out_t = o; o = al256(o + (hz ? 5 * px * es : 0));
   L.dxacc_t = o; o = al256(o + (hz ? px * 4 : 0));
+  L.dmpart = o; o = al256(o + static_cast<size_t>(4 * planes) * sizeof(double));
   L.total = o;
   return L;
 }
@@ -712,17 +737,18 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
   float* dxacc = reinterpret_cast<float*>(wsb + lay.dxacc);
   hipError_t e;
 
-  if (planes == 0) {
-    // no image: the merge gradients are empty sums
-    if (ex.dmerge && pr.C > 0) {
-      tr->before(stream, "bwd_dirs_zero", pr.C);
-      hipLaunchKernelGGL(bwd_dirs_zero<float>, dim3(static_cast<unsigned>(fill_grid(4 * pr.C))),
-                         dim3(256), 0, stream, ex.dmerge, 4 * pr.C);
-      tr->after(stream);
-      return hipGetLastError();
-    }
-    return hipSuccess;
-  }
+  double* dmpart = reinterpret_cast<double*>(wsb + lay.dmpart);
+  // the merge gradients from the partials of the selected directions (zeros
+  // for the others and for an empty batch)
+  auto merge_grad = [&]() -> hipError_t {
+    if (!ex.dmerge || pr.C == 0) return hipSuccess;
+    tr->before(stream, "bwd_dirs_merge", planes);
+    hipLaunchKernelGGL(bwd_dirs_merge, dim3(static_cast<unsigned>((4 * pr.C + 255) / 256)),
+                       dim3(256), 0, stream, dmpart, pr.B, pr.C, pr.mask, ex.dmerge);
+    tr->after(stream);
+    return hipGetLastError();
+  };
+  if (planes == 0) return merge_grad();
 
   // the order of the passes: horizontal first (their share of dx is
   // transposed back), then vertical
@@ -746,13 +772,6 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
       tr->after(stream);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (ex.dmerge) {
-      tr->before(stream, "bwd_dirs_zero", pr.C);
-      hipLaunchKernelGGL(bwd_dirs_zero<float>, dim3(1), dim3(256), 0, stream,
-                         ex.dmerge + d * pr.C, pr.C);
-      tr->after(stream);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
   }
 
   BwArgs<T> base;
@@ -765,15 +784,6 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
   base.Cl = pr.C;
   base.dlw = nullptr;
 
-  auto merge_grad = [&](int d, const T* ud, const T* gyd) -> hipError_t {
-    if (!ex.dmerge) return hipSuccess;
-    tr->before(stream, "bwd_dirs_merge", pr.C);
-    hipLaunchKernelGGL(bwd_dirs_merge<T>, dim3(static_cast<unsigned>(pr.C)), dim3(256), 0, stream,
-                       ud, gyd, hbuf, pr.B, pr.C, pr.H * pr.W, ex.dmerge + d * pr.C);
-    tr->after(stream);
-    return hipGetLastError();
-  };
-
   if (pr.mask & 12u) {
     T* x_t = reinterpret_cast<T*>(wsb + lay.x_t);
     T* gy_t = reinterpret_cast<T*>(wsb + lay.gy_t);
@@ -783,8 +793,8 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
     {
       const T* src[2] = {x, gy};
       T* dst[2] = {x_t, gy_t};
-      if ((e = transpose<T>(src, dst, 2, planes, static_cast<int>(pr.H), static_cast<int>(pr.W),
-                            stream, tr)) != hipSuccess)
+      if ((e = transpose_planes<T>(src, dst, 2, planes, static_cast<int>(pr.H),
+                                   static_cast<int>(pr.W), "bwd_dirs_tr", stream, tr)) != hipSuccess)
         return e;
     }
     for (int d = 2; d < 4; ++d) {
@@ -792,8 +802,8 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
       const T* src[5] = {lam + d * ds, lg[0] + d * ds, lg[1] + d * ds, lg[2] + d * ds, u + d * ds};
       T* dst[5];
       for (int i = 0; i < 5; ++i) dst[i] = par_t + i * P;
-      if ((e = transpose<T>(src, dst, 5, planes, static_cast<int>(pr.H), static_cast<int>(pr.W),
-                            stream, tr)) != hipSuccess)
+      if ((e = transpose_planes<T>(src, dst, 5, planes, static_cast<int>(pr.H),
+                                   static_cast<int>(pr.W), "bwd_dirs_tr", stream, tr)) != hipSuccess)
         return e;
       BwArgs<T> t = base;
       t.x = x_t;
@@ -806,22 +816,23 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
       t.dxfirst = d == first;
       t.dxlast = false;
       t.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+      t.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
       t.H = static_cast<int>(pr.W);
       t.W = static_cast<int>(pr.H);
       if ((e = run_direction(t, d == 2 ? 0 : 1, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess)
         return e;
-      if ((e = merge_grad(d, dst[4], gy_t)) != hipSuccess) return e;
       // the five gradients back to row-major, into direction d's slices
       const T* bs[5] = {out_t, out_t + P, out_t + 2 * P, out_t + 3 * P, out_t + 4 * P};
       T* bd[5] = {dlam + d * P, dl[0] + d * P, dl[1] + d * P, dl[2] + d * P, du + d * P};
-      if ((e = transpose<T>(bs, bd, 5, planes, static_cast<int>(pr.W), static_cast<int>(pr.H),
-                            stream, tr)) != hipSuccess)
+      if ((e = transpose_planes<T>(bs, bd, 5, planes, static_cast<int>(pr.W),
+                                   static_cast<int>(pr.H), "bwd_dirs_tr", stream, tr)) != hipSuccess)
         return e;
     }
     const float* fs[1] = {dxacc_t};
     float* fd[1] = {dxacc};
-    if ((e = transpose<float>(fs, fd, 1, planes, static_cast<int>(pr.W), static_cast<int>(pr.H),
-                              stream, tr)) != hipSuccess)
+    if ((e = transpose_planes<float>(fs, fd, 1, planes, static_cast<int>(pr.W),
+                                     static_cast<int>(pr.H), "bwd_dirs_tr_acc", stream, tr)) !=
+        hipSuccess)
       return e;
   }
   for (int d = 0; d < 2; ++d) {
@@ -838,10 +849,10 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
     a.dxfirst = d == first;
     a.dxlast = d == last;
     a.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+    a.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
     a.H = static_cast<int>(pr.H);
     a.W = static_cast<int>(pr.W);
     if ((e = run_direction(a, d, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess) return e;
-    if ((e = merge_grad(d, a.u, gy)) != hipSuccess) return e;
   }
   if (!vert_last) {
     tr->before(stream, "bwd_dirs_store_dx", planes);
@@ -850,7 +861,7 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
     tr->after(stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  return merge_grad();
 }
 
 hipError_t launch_bwd_dirs(const BwdProblem& pr, const BwdDirsExtra& ex, void* ws,

@@ -540,6 +540,16 @@ hipError_t launch_dirs_dt(const Problem& pr, void* ws, hipStream_t stream, Trace
 }
 }  // namespace
 
+template <typename E>
+hipError_t transpose_planes(const E* const* src, E* const* dst, int n, int64_t planes, int R, int C,
+                            const char* name, hipStream_t stream, Tracer* tr) {
+  return transpose<E, E>(src, dst, n, planes, R, C, name, stream, tr);
+}
+template hipError_t transpose_planes<float>(const float* const*, float* const*, int, int64_t, int,
+                                            int, const char*, hipStream_t, Tracer*);
+template hipError_t transpose_planes<bf16_t>(const bf16_t* const*, bf16_t* const*, int, int64_t,
+                                             int, int, const char*, hipStream_t, Tracer*);
+
 hipError_t launch_dirs(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
   if (pr.dtype == GSPN_F32) return launch_dirs_dt<float>(pr, ws, stream, tr);
   return launch_dirs_dt<bf16_t>(pr, ws, stream, tr);

@@ -102,6 +102,12 @@ hipError_t launch_stream(const Problem& pr, float* acc, hipStream_t stream, Trac
 int64_t dirs_max_orth();
 size_t dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask, gspn_dtype dt);
 hipError_t launch_dirs(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
+// dst[k] = src[k] transposed plane by plane ([planes][R][C] -> [planes][C][R]),
+// k < n <= 11, one launch traced as `name` over planes * n units; bf16 with
+// even sides and 4-byte aligned tensors moves element pairs
+template <typename E>
+hipError_t transpose_planes(const E* const* src, E* const* dst, int n, int64_t planes, int R, int C,
+                            const char* name, hipStream_t stream, Tracer* tr);
 
 // module prologue: the 1x1 convolutions producing x, the logits, lambda and u
 // (gspn_prologue.hip); all tensors [B, *, H, W] of one dtype

@@ -381,12 +381,18 @@ def test_backward_dirs_workspace_bytes(L):
     # stored states and the fp32 sum for grad_x; with a horizontal direction
     # also transposed x and grad_out, five inputs and five gradients of one
     # direction, and a transposed fp32 sum (DP * 4 and DP * 2 are multiples
-    # of 256 here)
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * 15
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 1) == DP * (4 * 3 + 2 * 12)
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 1) == DP * 4 * 2
+    # of 256 here); last the fp64 merge partials, 4 per plane (6 planes:
+    # 192 bytes, one 256-byte block)
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * 15 + 256
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 1) == \
+        DP * (4 * 3 + 2 * 12) + 256
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 1) == \
+        DP * 4 * 2 + 256
     assert L.gspn_backward_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0   # above the limit
-    assert g.backward_workspace_bytes_dirs(2, 3, 20, 16, g.L2R) == DP * 4 * 15
+    assert g.backward_workspace_bytes_dirs(2, 3, 20, 16, g.L2R) == DP * 4 * 15 + 256
+    # 40 planes: 1280 bytes of partials
+    DP40 = 8 * 5 * 20 * 16
+    assert L.gspn_backward_workspace_bytes_dirs(8, 5, 20, 16, g.T2B, 0, 0) == DP40 * 4 * 2 + 1280
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -12,8 +12,8 @@ KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
            "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",
-           "bt_vA", "bt_hA", "bt_hB", "bt_vB", "bwd_dirs_zero", "bwd_dirs_store_dx",
-           "bwd_dirs_merge"]
+           "bt_vA", "bt_hA", "bt_hB", "bt_vB", "bwd_dirs_zero", "bwd_dirs_store_dx", "bwd_dirs_tr",
+           "bwd_dirs_tr_acc", "bwd_dirs_merge"]
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -101,8 +101,8 @@ def test_prologue_work():
 def test_per_direction_backward_path_bytes():
     """Four directions, bf16: x and grad_out transposed, ten tensors through
     each horizontal direction's transposes, the dx sum back; per direction
-    the scan pair and the merge reduction."""
+    the scan pair (the merge partials ride along in the reverse scan)."""
     w = WORKLOADS["t2i_2048x1024_pd"]
     s = 2
-    per_dir = (5 * s + 4) + (12 * s + 12) + (2 * s + 4)
+    per_dir = (5 * s + 4) + (12 * s + 12)
     assert bench.bwd_dirs_path_bytes(w) == 4 * s + 2 * 20 * s + 8 + 4 * per_dir
