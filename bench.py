@@ -581,7 +581,7 @@ def main() -> int:
 
     hip = Hip()
     L = g.lib()
-    max_launch = 16
+    max_launch = 64   # launches traced per step (two plane groups double a chain)
     evs = [hip.events(2 * max_launch) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)

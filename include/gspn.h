@@ -140,7 +140,8 @@ int gspn_trace_count(void);
 /*
  * gspn_trace_kernel -- name of the kernel of launch i of the last traced call
  * (static string), storing the number of planes it processed in *planes;
- * NULL when i is out of range. Launches may run on a library-owned helper
+ * NULL when i is out of range (the first 64 launches of a call are named).
+ * Launches may run on a library-owned helper
  * stream that is forked from and joined back to the caller's stream; each
  * launch's events are recorded on the stream that launch runs on.
  */

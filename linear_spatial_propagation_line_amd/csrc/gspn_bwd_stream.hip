@@ -85,6 +85,7 @@ struct BwArgs {
   // per-plane merge-gradient partials, sum over the plane of u gy h in fp64
   // (null: not wanted); only with first and last set
   double* dmpart;
+  int64_t plane0;   // first plane of this launch (blockIdx.x counts from it)
 };
 
 // logit gradients of pixel idx: to the storage type, or per plane in fp32
@@ -118,11 +119,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_fwd(BwArgs<T> a) {
   const int H = a.H, W = a.W, G = a.G, d = a.dir;
   const bool vert = d < 2, fwd = (d == 0 || d == 2);
   const int n_s = vert ? H : W, n_o = vert ? W : H;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * H * W;
+  const int64_t plane = a.plane0 + blockIdx.x;
+  const int64_t base = plane * H * W;
   const bool first = a.mode & kBwFirst, last = a.mode & kBwLast;
   const bool keep_sum = !(first && last);   // a single direction needs no running sum
   float* hsum = a.acc + 4 * a.pstride;
-  const int64_t ls = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
+  const int64_t ls = logit_shift(plane, a.C, a.Cl, static_cast<int64_t>(H) * W);
   for (int s0 = 0; s0 < n_s; s0 += D) {
     float lx[D][MAXP], g0[D][MAXP], g1[D][MAXP], g2[D][MAXP], hs[D][MAXP];
 #pragma unroll
@@ -184,15 +186,16 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
   const int H = a.H, W = a.W, G = a.G, d = a.dir;
   const bool vert = d < 2, fwd = (d == 0 || d == 2);
   const int n_s = vert ? H : W, n_o = vert ? W : H;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * H * W;
+  const int64_t plane = a.plane0 + blockIdx.x;
+  const int64_t base = plane * H * W;
   const int64_t ps = a.pstride;
   const bool first = a.mode & kBwFirst, last = a.mode & kBwLast;
   // previous line in scan order sits one position back along the scan axis
   const int back = fwd ? -1 : 1;
   const int64_t back_off = vert ? static_cast<int64_t>(back) * W : back;
   const int64_t oo = vert ? 1 : W;   // orthogonal stride
-  const int64_t lsh = logit_shift(blockIdx.x, a.C, a.Cl, static_cast<int64_t>(H) * W);
-  const float gsc = a.gscale ? a.gscale[blockIdx.x % a.C] : 1.f;
+  const int64_t lsh = logit_shift(plane, a.C, a.Cl, static_cast<int64_t>(H) * W);
+  const float gsc = a.gscale ? a.gscale[plane % a.C] : 1.f;
 
   float a1[MAXP];
 #pragma unroll
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_adj(BwArgs<T> a) {
     if (threadIdx.x == 0) {
       double t = 0.0;
       for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) t += red[k];
-      a.dmpart[blockIdx.x] = t;
+      a.dmpart[plane] = t;
     }
   }
 }
@@ -533,6 +536,7 @@ static hipError_t launch_bwd_stream_dt(const BwdProblem& pr, void* ws, hipStream
   a.dxacc = nullptr;
   a.dxfirst = a.dxlast = false;
   a.dmpart = nullptr;
+  a.plane0 = 0;
   const bool t2b = pr.mask & 1u, b2t = pr.mask & 2u, l2r = pr.mask & 4u, r2l = pr.mask & 8u;
   hipError_t e;
   bool acc_written = false;
@@ -784,83 +788,99 @@ static hipError_t launch_bwd_dirs_dt(const BwdProblem& pr, const BwdDirsExtra& e
   base.Cl = pr.C;
   base.dlw = nullptr;
 
-  if (pr.mask & 12u) {
-    T* x_t = reinterpret_cast<T*>(wsb + lay.x_t);
-    T* gy_t = reinterpret_cast<T*>(wsb + lay.gy_t);
-    T* par_t = reinterpret_cast<T*>(wsb + lay.par_t);
-    T* out_t = reinterpret_cast<T*>(wsb + lay.out_t);
-    float* dxacc_t = reinterpret_cast<float*>(wsb + lay.dxacc_t);
-    {
-      const T* src[2] = {x, gy};
-      T* dst[2] = {x_t, gy_t};
-      if ((e = transpose_planes<T>(src, dst, 2, planes, static_cast<int>(pr.H),
-                                   static_cast<int>(pr.W), "bwd_dirs_tr", stream, tr)) != hipSuccess)
+  const int64_t HW = pr.H * pr.W;
+  const int H = static_cast<int>(pr.H), W = static_cast<int>(pr.W);
+  T* x_t = reinterpret_cast<T*>(wsb + lay.x_t);
+  T* gy_t = reinterpret_cast<T*>(wsb + lay.gy_t);
+  T* par_t = reinterpret_cast<T*>(wsb + lay.par_t);
+  T* out_t = reinterpret_cast<T*>(wsb + lay.out_t);
+  float* dxacc_t = reinterpret_cast<float*>(wsb + lay.dxacc_t);
+
+  // every launch of the chain for planes [p0, p0 + np) on stream st; planes
+  // are independent throughout (their own slices of every buffer)
+  auto run_group = [&](int64_t p0, int64_t np, hipStream_t st) -> hipError_t {
+    hipError_t e;
+    const int64_t o = p0 * HW;   // element offset of the group in a [planes][H][W] tensor
+    if (pr.mask & 12u) {
+      {
+        const T* src[2] = {x + o, gy + o};
+        T* dst[2] = {x_t + o, gy_t + o};
+        if ((e = transpose_planes<T>(src, dst, 2, np, H, W, "bwd_dirs_tr", st, tr)) != hipSuccess)
+          return e;
+      }
+      for (int d = 2; d < 4; ++d) {
+        if (!(pr.mask & (1u << d))) continue;
+        const T* src[5] = {lam + d * ds + o, lg[0] + d * ds + o, lg[1] + d * ds + o,
+                           lg[2] + d * ds + o, u + d * ds + o};
+        T* dst[5];
+        for (int i = 0; i < 5; ++i) dst[i] = par_t + i * P + o;
+        if ((e = transpose_planes<T>(src, dst, 5, np, H, W, "bwd_dirs_tr", st, tr)) != hipSuccess)
+          return e;
+        BwArgs<T> t = base;
+        t.x = x_t;
+        t.gy = gy_t;
+        t.lam = par_t; t.l0 = par_t + P; t.l1 = par_t + 2 * P; t.l2 = par_t + 3 * P;
+        t.u = par_t + 4 * P;
+        t.dlam = out_t; t.dl0 = out_t + P; t.dl1 = out_t + 2 * P; t.dl2 = out_t + 3 * P;
+        t.du = out_t + 4 * P;
+        t.dx = nullptr;
+        t.dxacc = dxacc_t;
+        t.dxfirst = d == first;
+        t.dxlast = false;
+        t.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+        t.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
+        t.plane0 = p0;
+        t.H = W;
+        t.W = H;
+        if ((e = run_direction(t, d == 2 ? 0 : 1, kBwFirst | kBwLast, np, st, tr)) != hipSuccess)
+          return e;
+        // the five gradients back to row-major, into direction d's slices
+        const T* bs[5] = {out_t + o, out_t + P + o, out_t + 2 * P + o, out_t + 3 * P + o,
+                          out_t + 4 * P + o};
+        T* bd[5] = {dlam + d * P + o, dl[0] + d * P + o, dl[1] + d * P + o, dl[2] + d * P + o,
+                    du + d * P + o};
+        if ((e = transpose_planes<T>(bs, bd, 5, np, W, H, "bwd_dirs_tr", st, tr)) != hipSuccess)
+          return e;
+      }
+      const float* fs[1] = {dxacc_t + o};
+      float* fd[1] = {dxacc + o};
+      if ((e = transpose_planes<float>(fs, fd, 1, np, W, H, "bwd_dirs_tr_acc", st, tr)) !=
+          hipSuccess)
         return e;
     }
-    for (int d = 2; d < 4; ++d) {
+    for (int d = 0; d < 2; ++d) {
       if (!(pr.mask & (1u << d))) continue;
-      const T* src[5] = {lam + d * ds, lg[0] + d * ds, lg[1] + d * ds, lg[2] + d * ds, u + d * ds};
-      T* dst[5];
-      for (int i = 0; i < 5; ++i) dst[i] = par_t + i * P;
-      if ((e = transpose_planes<T>(src, dst, 5, planes, static_cast<int>(pr.H),
-                                   static_cast<int>(pr.W), "bwd_dirs_tr", stream, tr)) != hipSuccess)
-        return e;
-      BwArgs<T> t = base;
-      t.x = x_t;
-      t.gy = gy_t;
-      t.lam = dst[0]; t.l0 = dst[1]; t.l1 = dst[2]; t.l2 = dst[3]; t.u = dst[4];
-      t.dlam = out_t; t.dl0 = out_t + P; t.dl1 = out_t + 2 * P; t.dl2 = out_t + 3 * P;
-      t.du = out_t + 4 * P;
-      t.dx = nullptr;
-      t.dxacc = dxacc_t;
-      t.dxfirst = d == first;
-      t.dxlast = false;
-      t.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
-      t.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
-      t.H = static_cast<int>(pr.W);
-      t.W = static_cast<int>(pr.H);
-      if ((e = run_direction(t, d == 2 ? 0 : 1, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess)
-        return e;
-      // the five gradients back to row-major, into direction d's slices
-      const T* bs[5] = {out_t, out_t + P, out_t + 2 * P, out_t + 3 * P, out_t + 4 * P};
-      T* bd[5] = {dlam + d * P, dl[0] + d * P, dl[1] + d * P, dl[2] + d * P, du + d * P};
-      if ((e = transpose_planes<T>(bs, bd, 5, planes, static_cast<int>(pr.W),
-                                   static_cast<int>(pr.H), "bwd_dirs_tr", stream, tr)) != hipSuccess)
-        return e;
+      BwArgs<T> a = base;
+      a.x = x;
+      a.gy = gy;
+      a.lam = lam + d * ds; a.l0 = lg[0] + d * ds; a.l1 = lg[1] + d * ds; a.l2 = lg[2] + d * ds;
+      a.u = u + d * ds;
+      a.dlam = dlam + d * P; a.dl0 = dl[0] + d * P; a.dl1 = dl[1] + d * P; a.dl2 = dl[2] + d * P;
+      a.du = du + d * P;
+      a.dx = dx;
+      a.dxacc = dxacc;
+      a.dxfirst = d == first;
+      a.dxlast = d == last;
+      a.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
+      a.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
+      a.plane0 = p0;
+      a.H = H;
+      a.W = W;
+      if ((e = run_direction(a, d, kBwFirst | kBwLast, np, st, tr)) != hipSuccess) return e;
     }
-    const float* fs[1] = {dxacc_t};
-    float* fd[1] = {dxacc};
-    if ((e = transpose_planes<float>(fs, fd, 1, planes, static_cast<int>(pr.W),
-                                     static_cast<int>(pr.H), "bwd_dirs_tr_acc", stream, tr)) !=
-        hipSuccess)
-      return e;
-  }
-  for (int d = 0; d < 2; ++d) {
-    if (!(pr.mask & (1u << d))) continue;
-    BwArgs<T> a = base;
-    a.x = x;
-    a.gy = gy;
-    a.lam = lam + d * ds; a.l0 = lg[0] + d * ds; a.l1 = lg[1] + d * ds; a.l2 = lg[2] + d * ds;
-    a.u = u + d * ds;
-    a.dlam = dlam + d * P; a.dl0 = dl[0] + d * P; a.dl1 = dl[1] + d * P; a.dl2 = dl[2] + d * P;
-    a.du = du + d * P;
-    a.dx = dx;
-    a.dxacc = dxacc;
-    a.dxfirst = d == first;
-    a.dxlast = d == last;
-    a.gscale = ex.merge ? ex.merge + d * pr.C : nullptr;
-    a.dmpart = ex.dmerge ? dmpart + d * planes : nullptr;
-    a.H = static_cast<int>(pr.H);
-    a.W = static_cast<int>(pr.W);
-    if ((e = run_direction(a, d, kBwFirst | kBwLast, planes, stream, tr)) != hipSuccess) return e;
-  }
-  if (!vert_last) {
-    tr->before(stream, "bwd_dirs_store_dx", planes);
-    hipLaunchKernelGGL(bwd_dirs_store_dx<T>, dim3(static_cast<unsigned>(fill_grid(P))), dim3(256), 0,
-                       stream, dxacc, dx, P);
-    tr->after(stream);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+    if (!vert_last) {
+      tr->before(st, "bwd_dirs_store_dx", np);
+      hipLaunchKernelGGL(bwd_dirs_store_dx<T>, dim3(static_cast<unsigned>(fill_grid(np * HW))),
+                         dim3(256), 0, st, dxacc + o, dx + o, np * HW);
+      tr->after(st);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+
+  // A scan launch gives each plane one compute unit: plane groups on their
+  // own streams let one group's tail overlap another group's next launch.
+  if ((e = run_plane_groups(planes, stream, run_group)) != hipSuccess) return e;
   return merge_grad();
 }
 

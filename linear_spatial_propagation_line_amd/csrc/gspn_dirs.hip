@@ -455,88 +455,107 @@ hipError_t launch_dirs_dt(const Problem& pr, void* ws, hipStream_t stream, Trace
   a.plane0 = 0;
   a.G = static_cast<int>(pr.G);
   char* wsb = static_cast<char*>(ws);
-  float* acc = static_cast<float*>(ws);   // row-major sum (vertical passes)
-  int pass = 0;                           // passes run so far
-  hipError_t e;
+  const int64_t HW = pr.H * pr.W;
 
-  if (nh > 0) {
-    // workspace: [transposed sum][row-major sum][x^T][5 tensors^T per direction]
-    float* acc_t = reinterpret_cast<float*>(wsb);
-    size_t off = al(P * sizeof(float));
-    if (nv > 0) {
-      acc = reinterpret_cast<float*>(wsb + off);
-      off += al(P * sizeof(float));
-    }
-    const T* src[11];
-    T* dst[11];
-    int n = 0;
-    src[n] = xs;
-    dst[n++] = reinterpret_cast<T*>(wsb + off);
-    off += al(P * sizeof(T));
-    for (int d = 2; d < 4; ++d) {
-      if (!((pr.mask >> d) & 1u)) continue;
-      const void* bases[5] = {pr.lam, pr.l[0], pr.l[1], pr.l[2], pr.u};
-      for (int k = 0; k < 5; ++k) {
-        src[n] = param(bases[k], d);
-        dst[n++] = reinterpret_cast<T*>(wsb + off);
-        off += al(P * sizeof(T));
+  // every launch for planes [p0, p0 + np) on stream st; planes are
+  // independent throughout (their own slices of every buffer)
+  auto run_group = [&](int64_t p0, int64_t np, hipStream_t st) -> hipError_t {
+    const int64_t o = p0 * HW;   // element offset of the group in a [planes][H][W] tensor
+    DirArgs<T> ag = a;
+    ag.plane0 = p0;
+    float* acc = static_cast<float*>(ws);   // row-major sum (vertical passes)
+    int pass = 0;                           // passes run so far
+    hipError_t e;
+    if (nh > 0) {
+      // workspace: [transposed sum][row-major sum][x^T][5 tensors^T per direction]
+      float* acc_t = reinterpret_cast<float*>(wsb);
+      size_t off = al(P * sizeof(float));
+      if (nv > 0) {
+        acc = reinterpret_cast<float*>(wsb + off);
+        off += al(P * sizeof(float));
       }
+      // whole tensors (the kernels address planes from plane0), and the
+      // group's slices for the transposes
+      const T* src[11];
+      T* dst[11];
+      const T* gsrc[11];
+      T* gdst[11];
+      int n = 0;
+      src[n] = xs;
+      dst[n++] = reinterpret_cast<T*>(wsb + off);
+      off += al(P * sizeof(T));
+      for (int d = 2; d < 4; ++d) {
+        if (!((pr.mask >> d) & 1u)) continue;
+        const void* bases[5] = {pr.lam, pr.l[0], pr.l[1], pr.l[2], pr.u};
+        for (int k = 0; k < 5; ++k) {
+          src[n] = param(bases[k], d);
+          dst[n++] = reinterpret_cast<T*>(wsb + off);
+          off += al(P * sizeof(T));
+        }
+      }
+      for (int k = 0; k < n; ++k) {
+        gsrc[k] = src[k] + o;
+        gdst[k] = dst[k] + o;
+      }
+      e = transpose<T, T>(gsrc, gdst, n, np, H, W, "dir_tr_in", st, tr);
+      if (e != hipSuccess) return e;
+      // left->right and right->left as top->bottom and bottom->top passes over
+      // the transposed planes (W rows of H), into the transposed sum
+      int t = 1;
+      for (int d = 2; d < 4; ++d) {
+        if (!((pr.mask >> d) & 1u)) continue;
+        ag.x = dst[0];
+        ag.lam = dst[t];
+        ag.l0 = dst[t + 1];
+        ag.l1 = dst[t + 2];
+        ag.l2 = dst[t + 3];
+        ag.u = dst[t + 4];
+        t += 5;
+        ag.merge = pr.merge ? pr.merge + d * pr.C : nullptr;
+        ag.acc = acc_t;
+        ag.H = W;
+        ag.W = H;
+        ag.mode = (pass == 0 ? kDirFirst : 0);
+        e = vert_dispatch<T>(ag, d == 2, np, st, tr);
+        if (e != hipSuccess) return e;
+        ++pass;
+      }
+      // back to row-major: into the sum the vertical passes continue, or, with
+      // no vertical direction, straight into out
+      const float* s1[1] = {acc_t + o};
+      if (nv > 0) {
+        float* d1[1] = {acc + o};
+        e = transpose<float, float>(s1, d1, 1, np, W, H, "dir_tr_acc", st, tr);
+      } else {
+        T* d1[1] = {static_cast<T*>(pr.out) + o};
+        e = transpose<float, T>(s1, d1, 1, np, W, H, "dir_tr_acc", st, tr);
+      }
+      if (e != hipSuccess) return e;
     }
-    e = transpose<T, T>(src, dst, n, planes, H, W, "dir_tr_in", stream, tr);
-    if (e != hipSuccess) return e;
-    // left->right and right->left as top->bottom and bottom->top passes over
-    // the transposed planes (W rows of H), into the transposed sum
-    int t = 1;
-    for (int d = 2; d < 4; ++d) {
+    int done_v = 0;
+    for (int d = 0; d < 2; ++d) {
       if (!((pr.mask >> d) & 1u)) continue;
-      a.x = dst[0];
-      a.lam = dst[t];
-      a.l0 = dst[t + 1];
-      a.l1 = dst[t + 2];
-      a.l2 = dst[t + 3];
-      a.u = dst[t + 4];
-      t += 5;
-      a.merge = pr.merge ? pr.merge + d * pr.C : nullptr;
-      a.acc = acc_t;
-      a.H = W;
-      a.W = H;
-      a.mode = (pass == 0 ? kDirFirst : 0);
-      e = vert_dispatch<T>(a, d == 2, planes, stream, tr);
+      ag.x = xs;
+      ag.lam = param(pr.lam, d);
+      ag.l0 = param(pr.l[0], d);
+      ag.l1 = param(pr.l[1], d);
+      ag.l2 = param(pr.l[2], d);
+      ag.u = param(pr.u, d);
+      ag.merge = pr.merge ? pr.merge + d * pr.C : nullptr;
+      ag.acc = acc;
+      ag.H = H;
+      ag.W = W;
+      ++done_v;
+      ag.mode = (pass == 0 ? kDirFirst : 0) | (done_v == nv ? kDirLast : 0);
+      e = vert_dispatch<T>(ag, d == 0, np, st, tr);
       if (e != hipSuccess) return e;
       ++pass;
     }
-    // back to row-major: into the sum the vertical passes continue, or, with
-    // no vertical direction, straight into out
-    const float* s1[1] = {acc_t};
-    if (nv > 0) {
-      float* d1[1] = {acc};
-      e = transpose<float, float>(s1, d1, 1, planes, W, H, "dir_tr_acc", stream, tr);
-    } else {
-      T* d1[1] = {static_cast<T*>(pr.out)};
-      e = transpose<float, T>(s1, d1, 1, planes, W, H, "dir_tr_acc", stream, tr);
-    }
-    if (e != hipSuccess) return e;
-  }
-  int done_v = 0;
-  for (int d = 0; d < 2; ++d) {
-    if (!((pr.mask >> d) & 1u)) continue;
-    a.x = xs;
-    a.lam = param(pr.lam, d);
-    a.l0 = param(pr.l[0], d);
-    a.l1 = param(pr.l[1], d);
-    a.l2 = param(pr.l[2], d);
-    a.u = param(pr.u, d);
-    a.merge = pr.merge ? pr.merge + d * pr.C : nullptr;
-    a.acc = acc;
-    a.H = H;
-    a.W = W;
-    ++done_v;
-    a.mode = (pass == 0 ? kDirFirst : 0) | (done_v == nv ? kDirLast : 0);
-    e = vert_dispatch<T>(a, d == 0, planes, stream, tr);
-    if (e != hipSuccess) return e;
-    ++pass;
-  }
-  return hipSuccess;
+    return hipSuccess;
+  };
+  // A pass gives each plane one compute unit: plane groups on their own
+  // streams let one group's tail overlap another group's next launch.
+  return run_plane_groups(planes, stream, run_group);
 }
 }  // namespace
 

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <functional>
 #include <stdint.h>
 
 #include "gspn.h"
@@ -55,7 +56,7 @@ struct BwdProblem {
 
 // Records caller-owned events around kernel launches (gspn_trace_events),
 // and the kernel name and plane count of each launch.
-constexpr int kTraceMax = 16;
+constexpr int kTraceMax = 64;   // launches named per traced call
 struct Tracer {
   hipEvent_t* events = nullptr;
   int pairs = 0;
@@ -91,6 +92,12 @@ constexpr int kMaxGroups = 4;
 int cu_count();                        // compute units of the current device
 hipStream_t aux_stream(int i);         // helper stream i < kMaxGroups - 1 of the device
 int tpipe_groups(int64_t planes);      // number of plane groups for a launch
+// Calls fn(p0, np, s) for each of tpipe_groups(planes) contiguous plane
+// groups [p0, p0 + np): group 0 on `stream`, group g > 0 on helper stream
+// g - 1, forked from `stream` before and joined back into it after; the
+// first error stops the calls (the forked streams are still joined).
+hipError_t run_plane_groups(int64_t planes, hipStream_t stream,
+                            const std::function<hipError_t(int64_t, int64_t, hipStream_t)>& fn);
 size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt);
 hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr);
 

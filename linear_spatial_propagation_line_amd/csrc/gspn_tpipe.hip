@@ -748,6 +748,37 @@ int tpipe_groups(int64_t planes) {
   return (planes > cus && planes < 2 * cus) ? 2 : 1;
 }
 
+hipError_t run_plane_groups(int64_t planes, hipStream_t stream,
+                            const std::function<hipError_t(int64_t, int64_t, hipStream_t)>& fn) {
+  const int ngroups = tpipe_groups(planes);
+  if (ngroups <= 1) return fn(0, planes, stream);
+  hipStream_t streams[kMaxGroups] = {stream, stream, stream, stream};
+  hipEvent_t fork = nullptr, join[kMaxGroups] = {};
+  hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+  for (int g = 1; g < ngroups && e == hipSuccess; ++g) {
+    streams[g] = aux_stream(g - 1);
+    if (!streams[g]) e = hipErrorOutOfMemory;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join[g], hipEventDisableTiming);
+  }
+  if (e == hipSuccess) e = hipEventRecord(fork, stream);
+  for (int g = 1; g < ngroups && e == hipSuccess; ++g) e = hipStreamWaitEvent(streams[g], fork, 0);
+  for (int g = 0; g < ngroups && e == hipSuccess; ++g) {
+    const int64_t p0 = planes * g / ngroups, p1 = planes * (g + 1) / ngroups;
+    if (p1 > p0) e = fn(p0, p1 - p0, streams[g]);
+  }
+  // join whatever was forked, also after an error
+  for (int g = 1; g < ngroups; ++g) {
+    if (!join[g]) continue;
+    hipError_t e2 = hipEventRecord(join[g], streams[g]);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, join[g], 0);
+    if (e == hipSuccess) e = e2;
+  }
+  if (fork) (void)hipEventDestroy(fork);
+  for (int g = 1; g < ngroups; ++g)
+    if (join[g]) (void)hipEventDestroy(join[g]);
+  return e;
+}
+
 size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt) {
   return tp_layout(planes, H, W, dt == GSPN_F32 ? 4 : 2).total;
 }

@@ -67,6 +67,23 @@ def test_every_mask_family(dtype):
                                f"dirs backward mask={mask} merge={merge}", names=NAMES)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_plane_groups(dtype, monkeypatch):
+    """More planes than compute units (and fewer than twice as many) split
+    into plane groups on their own streams; 300 planes of 100 channels put
+    the group boundary inside an image. Three groups are forced on 10
+    planes as well (boundaries at planes 3 and 6)."""
+    inp, gy = case((3, 100, 12, 10), dtype, 91)
+    for G in (0, 4):
+        assert_grad_parity(run_bwd(inp, gy, 15, G), oracle_bwd(inp, gy, 15, G),
+                           f"dirs backward, 300 planes, G={G}", names=NAMES)
+    monkeypatch.setenv("GSPN_TPIPE_GROUPS", "3")
+    inp, gy = case((2, 5, 9, 7), dtype, 92)
+    for mask in (15, 12, 3):
+        assert_grad_parity(run_bwd(inp, gy, mask, 0), oracle_bwd(inp, gy, mask, 0),
+                           f"dirs backward, three groups, mask={mask}", names=NAMES)
+
+
 def test_classification_workload_shape():
     """The classification stage's plane shape and dtype (fewer planes than
     the benchmark: the fp64 oracle is slow)."""

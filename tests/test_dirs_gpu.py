@@ -78,6 +78,22 @@ def test_local_groups(G):
         assert_parity(run_dirs(inp, 15, G), oracle_dirs(inp, 15, G), f"dirs G={G}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_plane_groups(dtype, monkeypatch):
+    """More planes than compute units (and fewer than twice as many) split
+    into plane groups on their own streams; 300 planes of 100 channels put
+    the group boundary inside an image. Three groups are forced on 10
+    planes as well, over every mask family."""
+    inp = dirs_case((3, 100, 12, 10), dtype, 93)
+    for G in (0, 4):
+        assert_parity(run_dirs(inp, 15, G), oracle_dirs(inp, 15, G), f"dirs 300 planes G={G}")
+    monkeypatch.setenv("GSPN_TPIPE_GROUPS", "3")
+    inp = dirs_case((2, 5, 9, 7), dtype, 94)
+    for mask in (15, 12, 3, 4, 1):
+        assert_parity(run_dirs(inp, mask, 0), oracle_dirs(inp, mask, 0),
+                      f"dirs three groups mask={mask}")
+
+
 def test_stride_zero_is_the_shared_layer():
     """dir_stride = 0 and no merge weights through the C ABI: every direction
     reads the same [B, C, H, W] tensors, so the result is the shared layer's,
