@@ -81,6 +81,13 @@
  *     type, so x is rounded to it (to nearest, ties to even) before the three
  *     parameter convolutions read it. No activation is applied: the sigmoid
  *     and normalisation of the logits belong to the propagation.
+ *  R17 The backward pass of the per-direction layer (CSDN page, section
+ *     反向传播, with R15): the gradients of x, of every selected direction's
+ *     lambda, logits and u, and of the merge weights. Direction d's error
+ *     term starts from m[d][c] u_d gy; dx = sum_d lambda_d e_d,
+ *     dlambda_d = x e_d, du_d = m[d][c] gy h_d, and dm[d][c] is the sum over
+ *     the batch and the pixels of u_d gy h_d. Directions outside the mask get
+ *     zero gradients.
  */
 #include "gspn_oracle.h"
 
@@ -619,7 +626,7 @@ int gspn_oracle_backward(const void* x, const void* l0, const void* l1, const vo
                                      dl2, dlam, du, nthreads);
 }
 
-/* Per-direction parameters (R15), backward. With y = sum_d m_d u_d (.) h_d
+/* Per-direction parameters (R15), backward (R17). With y = sum_d m_d u_d (.) h_d
  * (m_d = merge[d * C + c]), direction d is one scan with its own lambda,
  * logits and u whose error term starts from m_d u_d gy; then
  *   dx       = sum_d lambda_d d(lambda x)_d,   dlambda_d = x d(lambda x)_d,
