@@ -117,6 +117,42 @@ def test_t2i_full_size_sampled_planes():
         print(f"[dirs bwd] t2i channel {c} worst scaled error {err:.3e}", flush=True)
 
 
+def _offset(v):
+    """A copy of v on the GPU that starts one element into its allocation."""
+    buf = torch.zeros(v.numel() + 1, dtype=v.dtype, device=DEV)
+    buf[1:].copy_(v.reshape(-1).to(DEV))
+    return buf[1:].view(v.shape)
+
+
+def test_offset_views_take_the_element_path():
+    """Inputs and gradients that start one element into their allocations
+    (no aligned vector runs, per-element transposes) give the oracle's
+    gradients too."""
+    shape = (1, 2, 40, 70)
+    for dtype in (torch.float32, torch.bfloat16):
+        inp, gy = case(shape, dtype, 23)
+        d = {k: (v.to(DEV) if k == "merge" else _offset(v)) for k, v in inp.items()}
+        grads = {"x": _offset(torch.zeros_like(inp["x"]))}
+        for k in KEYS:
+            grads[k] = _offset(torch.zeros_like(inp["lam"]))
+        grads["merge"] = _offset(torch.zeros((4, shape[1]), dtype=torch.float32))
+        got = g.propagate_backward_dirs(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"],
+                                        _offset(gy), merge=d["merge"], dirs=15, grads=grads)
+        torch.cuda.synchronize()
+        assert_grad_parity(got, oracle_bwd(inp, gy, 15, 0), f"dirs backward offset views {dtype}",
+                           names=NAMES)
+
+
+def test_deterministic():
+    """Two calls give bitwise equal gradients, the merge gradients included
+    (fixed reduction trees, no atomics), also across plane groups."""
+    inp, gy = case((3, 100, 12, 10), torch.bfloat16, 27)
+    a = run_bwd(inp, gy, 15, 0)
+    b = run_bwd(inp, gy, 15, 0)
+    for k in NAMES:
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_binding_rejects_aliased_gradients():
     inp, gy = case((1, 2, 8, 8), torch.float32, 5)
     d = {k: v.to(DEV) for k, v in inp.items()}
