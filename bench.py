@@ -168,8 +168,12 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
           bwd_dirs_merge  the fp64 partials that bwd_adj leaves, 4 per plane
           (8 bytes each; the products u gy h are summed inside bwd_adj,
           which reads all three anyway)
-    Per-direction parameters (one pass per direction; horizontal directions
-    run over transposed copies):
+    Per-direction parameters, planes up to 64 x 64 (one wavefront per plane,
+    the four directions in turn):
+      dir_plane  x read once, each selected direction's five tensors read once,
+          out written once: (2 + 5 dirs) s
+    Per-direction parameters, larger planes (one pass per direction;
+    horizontal directions run over transposed copies):
       dir_vert  x and the direction's lambda, l0, l1, l2, u read (6 s), the
           fp32 accumulator read unless first (4), then the accumulator
           written (4) or, by the last pass, out (s)
@@ -212,6 +216,7 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "bt_hB": 8 + 3 * s + 8 + 20,
         "bt_vB": 7 * s + 8 + (20 if hz else 0) + 6 * s,
         "bwd_reduce_logits": 12 + 3 * s * w.cl / w.C,
+        "dir_plane": (2 + 5 * w.ndirs) * s,
         "dir_vert": 6 * s + (0 if first else 4) + (s if last else 4),
         "dir_tr_in": 2 * s,
         "dir_tr_acc": 4 + (4 if w.dirs & 3 else s),

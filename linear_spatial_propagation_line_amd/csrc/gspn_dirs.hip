@@ -7,10 +7,14 @@
 //
 // With separate parameters the directions share only x, so nothing is gained
 // by running two directions from one read of the inputs: each direction is a
-// pass of its own over the plane, in its own scan order. One workgroup owns a
-// plane (the scan couples a whole line at every step); the line is exchanged
-// through a double-buffered LDS line with one barrier per step, and every
-// load is a coalesced run along a row.
+// pass of its own over the plane, in its own scan order.
+//
+// Planes up to 64 x 64 take dir_plane (below): one wavefront per plane, the
+// four directions in turn, their sum in LDS, no workspace.
+//
+// Larger planes: one workgroup owns a plane (the scan couples a whole line at
+// every step); the line is exchanged through a double-buffered LDS line with
+// one barrier per step, and every load is a coalesced run along a row.
 //
 //   dir_vert       one top->bottom or bottom->top pass: thread = CPT adjacent
 //                  columns, a row of every tensor is one coalesced run across
@@ -334,10 +338,152 @@ __global__ __launch_bounds__(256) void dir_transpose_pairs(TrArgs<bf16_t, bf16_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small planes (H, W <= 64): one wavefront per plane, no line in LDS and no
+// barrier. Lane o is orthogonal index o of every scan of the plane; it walks
+// the scan axis with its state in a register and takes its neighbours'
+// previous states by DPP (lane o - 1 holds offset -1 for all four directions).
+// Each direction streams its own five tensors: a vertical scan loads one row
+// per step, a coalesced run across the lanes; a horizontal scan loads four
+// consecutive columns of its row per lane at once (16 or 8 bytes) when the
+// row length and every pointer allow, else one element per step. The sum over
+// the directions, m[d][c] u_d h_d, stays in LDS ([H][W + 1] fp32 per plane:
+// rows and columns of it are both conflict-free) and is written once, in the
+// direction order T2B, B2T, L2R, R2L, with one rounding to the storage type.
+// Every input is read from HBM once, out written once.
+template <typename T>
+struct DpArgs {
+  const T* x;
+  const T* l0;
+  const T* l1;
+  const T* l2;
+  const T* lam;
+  const T* u;
+  int64_t dir_stride;   // elements between two directions' parameter sets
+  const float* merge;   // [4][C] merge weights, or null (all 1)
+  T* out;
+  int64_t nplanes, C;
+  int H, W, G;
+  unsigned mask;
+};
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void dir_plane(DpArgs<T> a) {
+  extern __shared__ float ysum[];   // [4 wavefronts][H][W + 1]
+  constexpr int D = 8;              // steps per batch of loads
+  const int wave = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t plane = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (plane >= a.nplanes) return;   // the whole wavefront
+  const int H = a.H, W = a.W, P = W + 1, G = a.G;
+  float* acc = ysum + wave * H * P;
+  const int64_t base = plane * H * W;
+  const int64_t ch = plane % a.C;
+  bool first = true;
+  for (int d = 0; d < 4; ++d) {
+    if (!((a.mask >> d) & 1u)) continue;
+    const int64_t off = d * a.dir_stride;
+    const T* lam = a.lam + off;
+    const T* l0 = a.l0 + off;
+    const T* l1 = a.l1 + off;
+    const T* l2 = a.l2 + off;
+    const T* u = a.u + off;
+    const float m = a.merge ? a.merge[d * a.C + ch] : 1.f;
+    const bool vert = d < 2, fwd = (d == 0 || d == 2);
+    const int n_s = vert ? H : W, n_o = vert ? W : H;
+    const bool act = o < n_o;
+    const int oc = act ? o : n_o - 1;   // clamped, for loads only
+    const float m0 = o > 0 ? 1.f : 0.f, m2 = o < n_o - 1 ? 1.f : 0.f;
+    // restarts after step 0: every G steps from the first block edge met
+    int next = n_s;
+    if (G > 0) next = fwd ? G : n_s - ((n_s - 1) / G) * G;
+    float h = 0.f;
+    // one step at scan position pos (row of a vertical scan, column of a
+    // horizontal one) from its lambda x, logits and u
+    auto step = [&](int s, int pos, float lx, float g0, float g1, float g2, float uv) {
+      const Weights w = make_weights(g0, g1, g2, m0, m2);
+      const float hl = from_left<64>(h), hr = from_right<64>(h);
+      const float hn = __builtin_fmaf(w.w0, hl, __builtin_fmaf(w.w1, h, __builtin_fmaf(w.w2, hr, lx)));
+      bool restart = s == 0;
+      if (s == next) { restart = true; next += G; }
+      h = act ? (restart ? lx : hn) : 0.f;
+      if (act) {
+        float* q = acc + (vert ? pos * P + o : o * P + pos);
+        const float v = m * uv * h;
+        *q = first ? v : *q + v;
+      }
+    };
+    if (vert || !VEC) {
+      for (int s0 = 0; s0 < n_s; s0 += D) {
+        float lx[D], g0[D], g1[D], g2[D], uv[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          const int s = min(s0 + j, n_s - 1);
+          const int pos = fwd ? s : n_s - 1 - s;
+          const int64_t i = base + (vert ? static_cast<int64_t>(pos) * W + oc
+                                         : static_cast<int64_t>(oc) * W + pos);
+          lx[j] = tr_ld(lam, i) * tr_ld(a.x, i);
+          g0[j] = tr_ld(l0, i);
+          g1[j] = tr_ld(l1, i);
+          g2[j] = tr_ld(l2, i);
+          uv[j] = tr_ld(u, i);
+        }
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          const int s = s0 + j;
+          if (s >= n_s) break;   // uniform
+          step(s, fwd ? s : n_s - 1 - s, lx[j], g0[j], g1[j], g2[j], uv[j]);
+        }
+      }
+    } else {
+      // horizontal, W % 4 == 0: each lane loads 64 bytes of its row per
+      // tensor at once (NQ runs of 4 columns), so that a 64-byte sector is
+      // fetched whole; partial sectors refetched run by run cost several
+      // times the bytes, since the rows of all the wavefronts in flight do
+      // not stay in L2 between runs. Left->right takes columns s0 .. in
+      // order; right->left the runs from the right end, used from the top.
+      using V = V4<T>;
+      constexpr int NQ = 64 / (4 * static_cast<int>(sizeof(T)));
+      const int64_t row = base + static_cast<int64_t>(oc) * W;
+      for (int s0 = 0; s0 < n_s; s0 += 4 * NQ) {
+        typename V::raw vx[NQ], vl[NQ], v0[NQ], v1[NQ], v2[NQ], vu[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          // runs past the end of the row repeat its last run (in bounds)
+          const int c4 = min(s0 + 4 * q, n_s - 4);
+          const int64_t i = row + (fwd ? c4 : n_s - 4 - c4);
+          vx[q] = V::load(a.x, i);
+          vl[q] = V::load(lam, i);
+          v0[q] = V::load(l0, i);
+          v1[q] = V::load(l1, i);
+          v2[q] = V::load(l2, i);
+          vu[q] = V::load(u, i);
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int s = s0 + 4 * q + j;
+            if (s < n_s) {   // uniform
+              const int e = fwd ? j : 3 - j;
+              step(s, fwd ? s : n_s - 1 - s, V::get(vl[q], e) * V::get(vx[q], e),
+                   V::get(v0[q], e), V::get(v1[q], e), V::get(v2[q], e), V::get(vu[q], e));
+            }
+          }
+        }
+      }
+    }
+    first = false;
+  }
+  // the plane's sum, row by row
+  if (o < W)
+    for (int r = 0; r < H; ++r) Store<T>::put(a.out, base + static_cast<int64_t>(r) * W + o, acc[r * P + o]);
+}
+
 int64_t dirs_max_orth() { return 8192; }
 
 size_t dirs_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
                             gspn_dtype dt) {
+  if (plane_fits(H, W)) return 0;   // one wavefront per plane, no workspace
   const size_t P = static_cast<size_t>(planes * H * W);
   const size_t es = dt == GSPN_F32 ? 4 : 2;
   auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
@@ -438,7 +584,50 @@ hipError_t transpose(const S* const* src, Dt* const* dst, int n, int64_t planes,
 }
 
 template <typename T>
+hipError_t launch_dir_plane(const Problem& pr, hipStream_t stream, Tracer* tr) {
+  DpArgs<T> a;
+  a.x = static_cast<const T*>(pr.x);
+  a.l0 = static_cast<const T*>(pr.l[0]);
+  a.l1 = static_cast<const T*>(pr.l[1]);
+  a.l2 = static_cast<const T*>(pr.l[2]);
+  a.lam = static_cast<const T*>(pr.lam);
+  a.u = static_cast<const T*>(pr.u);
+  a.dir_stride = pr.dir_stride;
+  a.merge = pr.merge;
+  a.out = static_cast<T*>(pr.out);
+  a.nplanes = pr.B * pr.C;
+  a.C = pr.C;
+  a.H = static_cast<int>(pr.H);
+  a.W = static_cast<int>(pr.W);
+  a.G = static_cast<int>(pr.G >= pr.H && pr.G >= pr.W ? 0 : pr.G);
+  a.mask = pr.mask;
+  // four-column loads for the horizontal scans: whole runs of 4 in a row and
+  // every tensor they read aligned to 4 elements
+  bool vec = pr.W % 4 == 0 && reinterpret_cast<uintptr_t>(a.x) % (4 * sizeof(T)) == 0;
+  for (int d = 2; d < 4; ++d) {
+    if (!((pr.mask >> d) & 1u)) continue;
+    const void* p[5] = {a.lam + d * a.dir_stride, a.l0 + d * a.dir_stride,
+                        a.l1 + d * a.dir_stride, a.l2 + d * a.dir_stride, a.u + d * a.dir_stride};
+    vec = vec && aligned_to(p, 5, 4 * sizeof(T));
+  }
+  const size_t lds = static_cast<size_t>(4 * pr.H * (pr.W + 1)) * sizeof(float);
+  auto kern = vec ? dir_plane<T, true> : dir_plane<T, false>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  tr->before(stream, "dir_plane", a.nplanes);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((a.nplanes + 3) / 4)), dim3(256), lds, stream,
+                     a);
+  tr->after(stream);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_dirs_dt(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+  if (plane_fits(pr.H, pr.W)) return launch_dir_plane<T>(pr, stream, tr);
   const int64_t planes = pr.B * pr.C;
   const int64_t P = planes * pr.H * pr.W;
   const int H = static_cast<int>(pr.H), W = static_cast<int>(pr.W);

@@ -296,11 +296,12 @@ def test_shared_aliasing_uses_logit_size(LB):
 # ---- per-direction parameters (gspn_propagate_dirs_ws) ----------------------
 # Every call below either fails validation or needs a workspace that it does
 # not get, so none reaches a launch.
-DP = 2 * 3 * 20 * 16          # elements of one [2, 3, 20, 16] tensor
+# (planes above 64 x 64: the calls need a workspace, and stop without one)
+DP = 2 * 3 * 100 * 80         # elements of one [2, 3, 100, 80] tensor
 
 
 def dcall(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
-          u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, B=2, C=3, H=20, W=16, mask=15, G=0,
+          u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, B=2, C=3, H=100, W=80, mask=15, G=0,
           dt=0, out=BASE + 6 * SZ, ws=None, ws_bytes=0):
     arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
     return L.gspn_propagate_dirs_ws(x, arr, lam, u, stride, merge, B, C, H, W, mask, G, dt, out,
@@ -310,13 +311,18 @@ def dcall(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 
 def test_dirs_workspace_bytes(L):
     # fp32 sums (transposed, row-major) and transposed x plus five tensors per
     # horizontal direction; DP * 4 and DP * 2 are multiples of 256 here
-    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * (2 + 11)
-    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.L2R | g.R2L, 0, 1) == DP * (4 + 2 * 11)
-    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.R2L, 0, 0) == DP * 4 * (1 + 6)
-    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 0) == DP * 4
-    assert L.gspn_workspace_bytes_dirs(2, 3, 20, 16, g.B2T, 0, 1) == 0
+    assert L.gspn_workspace_bytes_dirs(2, 3, 100, 80, 15, 0, 0) == DP * 4 * (2 + 11)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 100, 80, g.L2R | g.R2L, 0, 1) == DP * (4 + 2 * 11)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 100, 80, g.R2L, 0, 0) == DP * 4 * (1 + 6)
+    assert L.gspn_workspace_bytes_dirs(2, 3, 100, 80, g.T2B | g.B2T, 0, 0) == DP * 4
+    assert L.gspn_workspace_bytes_dirs(2, 3, 100, 80, g.B2T, 0, 1) == 0
     assert L.gspn_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0     # above the limit
-    assert g.workspace_bytes_dirs(2, 3, 20, 16) == DP * 4 * 13
+    assert g.workspace_bytes_dirs(2, 3, 100, 80) == DP * 4 * 13
+    # planes up to 64 x 64: one wavefront per plane, no workspace
+    for H, W in [(20, 16), (64, 64), (1, 64), (64, 1), (56, 56)]:
+        assert L.gspn_workspace_bytes_dirs(2, 3, H, W, 15, 0, 0) == 0
+    assert L.gspn_workspace_bytes_dirs(1, 1, 65, 64, 15, 0, 0) > 0
+    assert L.gspn_workspace_bytes_dirs(1, 1, 64, 65, 15, 0, 1) > 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -353,7 +359,7 @@ def test_dirs_aliasing_only_for_selected_directions(L):
 
 
 def test_dirs_workspace_checks(L):
-    need = L.gspn_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0)
+    need = L.gspn_workspace_bytes_dirs(2, 3, 100, 80, 15, 0, 0)
     assert dcall(L, ws=BASE + 7 * SZ, ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
     assert dcall(L, ws=BASE + 7 * SZ + 16, ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]
     # the workspace inside direction 3's u
@@ -367,8 +373,8 @@ def test_dirs_empty_batch_is_ok_without_gpu(L):
 
 # ---- per-direction backward (gspn_propagate_backward_dirs_ws) ------------------
 def bdcall(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
-           u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, gy=BASE + 9 * SZ, B=2, C=3, H=20,
-           W=16, mask=15, G=0, dt=0, gx=BASE + 10 * SZ,
+           u=BASE + 5 * SZ, stride=DP, merge=BASE + 8 * SZ, gy=BASE + 9 * SZ, B=2, C=3, H=100,
+           W=80, mask=15, G=0, dt=0, gx=BASE + 10 * SZ,
            glg=(BASE + 11 * SZ, BASE + 12 * SZ, BASE + 13 * SZ), glam=BASE + 14 * SZ,
            gu=BASE + 15 * SZ, gm=BASE + 16 * SZ, ws=None, ws_bytes=0):
     arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
@@ -383,13 +389,13 @@ def test_backward_dirs_workspace_bytes(L):
     # direction, and a transposed fp32 sum (DP * 4 and DP * 2 are multiples
     # of 256 here); last the fp64 merge partials, 4 per plane (6 planes:
     # 192 bytes, one 256-byte block)
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0) == DP * 4 * 15 + 256
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 1) == \
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 100, 80, 15, 0, 0) == DP * 4 * 15 + 256
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 100, 80, 15, 0, 1) == \
         DP * (4 * 3 + 2 * 12) + 256
-    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, g.T2B | g.B2T, 0, 1) == \
+    assert L.gspn_backward_workspace_bytes_dirs(2, 3, 100, 80, g.T2B | g.B2T, 0, 1) == \
         DP * 4 * 2 + 256
     assert L.gspn_backward_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0   # above the limit
-    assert g.backward_workspace_bytes_dirs(2, 3, 20, 16, g.L2R) == DP * 4 * 15 + 256
+    assert g.backward_workspace_bytes_dirs(2, 3, 100, 80, g.L2R) == DP * 4 * 15 + 256
     # 40 planes: 1280 bytes of partials
     DP40 = 8 * 5 * 20 * 16
     assert L.gspn_backward_workspace_bytes_dirs(8, 5, 20, 16, g.T2B, 0, 0) == DP40 * 4 * 2 + 1280
@@ -419,7 +425,7 @@ def test_backward_dirs_rejects_bad_arguments(L, kw, status):
 
 
 def test_backward_dirs_workspace_checks(L):
-    need = L.gspn_backward_workspace_bytes_dirs(2, 3, 20, 16, 15, 0, 0)
+    need = L.gspn_backward_workspace_bytes_dirs(2, 3, 100, 80, 15, 0, 0)
     assert bdcall(L) == g.STATUS["GSPN_E_WORKSPACE"]
     assert bdcall(L, ws=BASE + 17 * SZ, ws_bytes=need - 1) == g.STATUS["GSPN_E_WORKSPACE"]
     assert bdcall(L, ws=BASE + 17 * SZ + 16, ws_bytes=need) == g.STATUS["GSPN_E_ALIGN"]

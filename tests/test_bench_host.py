@@ -11,7 +11,7 @@ from linear_spatial_propagation_line_amd.inputs import WORKLOADS
 KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "tp_vfwd",
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
-           "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",
+           "dir_plane", "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",
            "bt_vA", "bt_hA", "bt_hB", "bt_vB", "bwd_dirs_zero", "bwd_dirs_store_dx", "bwd_dirs_tr",
            "bwd_dirs_tr_acc", "bwd_dirs_merge"]
 
