@@ -397,8 +397,8 @@ def test_backward_dirs_workspace_bytes(L):
     assert L.gspn_backward_workspace_bytes_dirs(1, 1, 9000, 16, 15, 0, 0) == 0   # above the limit
     assert g.backward_workspace_bytes_dirs(2, 3, 100, 80, g.L2R) == DP * 4 * 15 + 256
     # 40 planes: 1280 bytes of partials
-    DP40 = 8 * 5 * 20 * 16
-    assert L.gspn_backward_workspace_bytes_dirs(8, 5, 20, 16, g.T2B, 0, 0) == DP40 * 4 * 2 + 1280
+    DP40 = 8 * 5 * 20 * 80
+    assert L.gspn_backward_workspace_bytes_dirs(8, 5, 20, 80, g.T2B, 0, 0) == DP40 * 4 * 2 + 1280
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -69,16 +69,17 @@ def test_every_mask_family(dtype):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_plane_groups(dtype, monkeypatch):
-    """More planes than compute units (and fewer than twice as many) split
-    into plane groups on their own streams; 300 planes of 100 channels put
-    the group boundary inside an image. Three groups are forced on 10
-    planes as well (boundaries at planes 3 and 6)."""
-    inp, gy = case((3, 100, 12, 10), dtype, 91)
+    """Planes wider than 64 (the plane-group path): more planes than compute
+    units (and fewer than twice as many) split into plane groups on their own
+    streams; 300 planes of 100 channels put the group boundary inside an
+    image. Three groups are forced on 10 planes as well (boundaries at planes
+    3 and 6)."""
+    inp, gy = case((3, 100, 8, 66), dtype, 91)
     for G in (0, 4):
         assert_grad_parity(run_bwd(inp, gy, 15, G), oracle_bwd(inp, gy, 15, G),
                            f"dirs backward, 300 planes, G={G}", names=NAMES)
     monkeypatch.setenv("GSPN_TPIPE_GROUPS", "3")
-    inp, gy = case((2, 5, 9, 7), dtype, 92)
+    inp, gy = case((2, 5, 9, 70), dtype, 92)
     for mask in (15, 12, 3):
         assert_grad_parity(run_bwd(inp, gy, mask, 0), oracle_bwd(inp, gy, mask, 0),
                            f"dirs backward, three groups, mask={mask}", names=NAMES)
@@ -128,8 +129,8 @@ def test_offset_views_take_the_element_path():
     """Inputs and gradients that start one element into their allocations
     (no aligned vector runs, per-element transposes) give the oracle's
     gradients too."""
-    shape = (1, 2, 40, 70)
-    for dtype in (torch.float32, torch.bfloat16):
+    for shape, dtype in [((1, 2, 40, 70), torch.float32), ((1, 2, 40, 70), torch.bfloat16),
+                         ((1, 2, 20, 36), torch.float32), ((1, 2, 20, 36), torch.bfloat16)]:
         inp, gy = case(shape, dtype, 23)
         d = {k: (v.to(DEV) if k == "merge" else _offset(v)) for k, v in inp.items()}
         grads = {"x": _offset(torch.zeros_like(inp["x"]))}
@@ -145,12 +146,13 @@ def test_offset_views_take_the_element_path():
 
 def test_deterministic():
     """Two calls give bitwise equal gradients, the merge gradients included
-    (fixed reduction trees, no atomics), also across plane groups."""
-    inp, gy = case((3, 100, 12, 10), torch.bfloat16, 27)
-    a = run_bwd(inp, gy, 15, 0)
-    b = run_bwd(inp, gy, 15, 0)
-    for k in NAMES:
-        assert torch.equal(a[k], b[k]), k
+    (fixed reduction trees, no atomics), with and without plane groups."""
+    for shape in [(3, 100, 8, 66), (3, 100, 12, 12)]:
+        inp, gy = case(shape, torch.bfloat16, 27)
+        a = run_bwd(inp, gy, 15, 0)
+        b = run_bwd(inp, gy, 15, 0)
+        for k in NAMES:
+            assert torch.equal(a[k], b[k]), (shape, k)
 
 
 def test_binding_rejects_aliased_gradients():

@@ -80,15 +80,16 @@ def test_local_groups(G):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_plane_groups(dtype, monkeypatch):
-    """More planes than compute units (and fewer than twice as many) split
-    into plane groups on their own streams; 300 planes of 100 channels put
-    the group boundary inside an image. Three groups are forced on 10
-    planes as well, over every mask family."""
-    inp = dirs_case((3, 100, 12, 10), dtype, 93)
+    """Planes wider than 64 (the plane-group path): more planes than compute
+    units (and fewer than twice as many) split into plane groups on their own
+    streams; 300 planes of 100 channels put the group boundary inside an
+    image. Three groups are forced on 10 planes as well, over every mask
+    family."""
+    inp = dirs_case((3, 100, 8, 66), dtype, 93)
     for G in (0, 4):
         assert_parity(run_dirs(inp, 15, G), oracle_dirs(inp, 15, G), f"dirs 300 planes G={G}")
     monkeypatch.setenv("GSPN_TPIPE_GROUPS", "3")
-    inp = dirs_case((2, 5, 9, 7), dtype, 94)
+    inp = dirs_case((2, 5, 9, 70), dtype, 94)
     for mask in (15, 12, 3, 4, 1):
         assert_parity(run_dirs(inp, mask, 0), oracle_dirs(inp, mask, 0),
                       f"dirs three groups mask={mask}")
@@ -133,8 +134,8 @@ def test_merge_weights_are_per_channel_and_direction():
 def test_offset_views_take_the_element_path():
     """Tensors that start one element into their allocation (no aligned
     vector runs) give the oracle's result too."""
-    shape = (1, 2, 40, 1032)
-    for dtype in (torch.float32, torch.bfloat16):
+    for shape, dtype in [((1, 2, 40, 1032), torch.float32), ((1, 2, 40, 1032), torch.bfloat16),
+                         ((1, 2, 20, 36), torch.float32), ((1, 2, 20, 36), torch.bfloat16)]:
         inp = dirs_case(shape, dtype, 21)
         d = {}
         for k, v in inp.items():
