@@ -4,7 +4,8 @@
 // A workgroup of four wavefronts owns PPB = 64 / SEG planes at a time and
 // loops over plane groups (persistent grid). Per plane group:
 //   1. records (w0, w1, w2, lambda x) per pixel in LDS, and the edge-lane
-//      records whose missing neighbour changes the normalisation;
+//      records whose missing neighbour changes the normalisation (on 64-wide
+//      planes their inputs were loaded while the previous group ran);
 //   2. wavefront d runs the forward scan of direction d (lane = orthogonal
 //      index, neighbours by DPP) and keeps its states in registers;
 //   3. the record's fourth component becomes u * grad_out;
@@ -115,11 +116,47 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
   const int zero_off = eh_off + PPB * 2 * W;   // one zero record
   const int tid = threadIdx.x;
 
+  // 64-wide planes (one workgroup per CU, nothing else to hide latency): the
+  // inputs of the records (x, lambda, logits) are held raw in registers one
+  // plane group ahead; the next group's loads are issued right after this
+  // group's records are built, so they stay in flight through the scans.
+  // 16-wide planes run several workgroups per CU and load them in place.
+  constexpr bool kAhead = SEG == 64;
+  T px[KMAX], plm[KMAX], pq0[KMAX], pq1[KMAX], pq2[KMAX];
+  auto group_pixel = [&](int64_t grp, int k, int64_t* gi, int64_t* lgi) {
+    const int64_t pl0 = grp * PPB;
+    const int npx = static_cast<int>(min<int64_t>(PPB, a.nplanes - pl0)) * HW;
+    const int i = tid + NT * k;
+    const int ic = i < npx ? i : 0;   // always in bounds
+    *gi = pl0 * HW + ic;
+    *lgi = *gi;
+    if (a.Cl != a.C) {
+      int rem;
+      const int pin = PPB == 1 ? 0 : div_small(ic, HW, a.inv_HW, &rem);
+      *lgi += logit_shift(pl0 + pin, a.C, a.Cl, HW);
+    }
+  };
+  auto fetch_records = [&](int64_t grp) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      int64_t gi, lgi;
+      group_pixel(grp, k, &gi, &lgi);
+      px[k] = a.x[gi];
+      plm[k] = a.lam[gi];
+      pq0[k] = a.l0[lgi];
+      pq1[k] = a.l1[lgi];
+      pq2[k] = a.l2[lgi];
+    }
+  };
+  if constexpr (kAhead)
+    if (static_cast<int64_t>(blockIdx.x) < a.ngroups) fetch_records(blockIdx.x);
+
   for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
     const int64_t plane0 = grp * PPB;
     const int np = static_cast<int>(min<int64_t>(PPB, a.nplanes - plane0));
     const int64_t gbase = plane0 * HW;
     const int npix = np * HW;
+    const bool more = grp + gridDim.x < a.ngroups;
 
     // ---- 1. records ---------------------------------------------------------
     // LDS index of pixel i of the group (and its plane within the group)
@@ -130,18 +167,25 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
       if (pp_out) *pp_out = pp;
       return (pp * H + *r) * pitch + *c;
     };
-#pragma unroll 4
+#pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i < npix) {
         int r, c, pp;
         const int li = lds_index(i, &r, &c, &pp);
-        const int64_t gi = gbase + i;
-        const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
-        const Weights w = make_weights(pl1(a.l0, lgi), pl1(a.l1, lgi), pl1(a.l2, lgi), 1.f, 1.f);
-        smem[li] = make_float4(w.w0, w.w1, w.w2, pl1(a.lam, gi) * pl1(a.x, gi));
+        if constexpr (kAhead) {
+          const Weights w = make_weights(to_f32(pq0[k]), to_f32(pq1[k]), to_f32(pq2[k]), 1.f, 1.f);
+          smem[li] = make_float4(w.w0, w.w1, w.w2, to_f32(plm[k]) * to_f32(px[k]));
+        } else {
+          const int64_t gi = gbase + i;
+          const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
+          const Weights w = make_weights(pl1(a.l0, lgi), pl1(a.l1, lgi), pl1(a.l2, lgi), 1.f, 1.f);
+          smem[li] = make_float4(w.w0, w.w1, w.w2, pl1(a.lam, gi) * pl1(a.x, gi));
+        }
       }
     }
+    if constexpr (kAhead)
+      if (more) fetch_records(grp + gridDim.x);
     if (tid == 0) smem[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
@@ -208,7 +252,7 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     __syncthreads();
 
     // ---- 3. u * grad_out into the records ------------------------------------
-#pragma unroll 4
+#pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i < npix) {
