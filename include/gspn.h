@@ -274,8 +274,9 @@ size_t gspn_backward_workspace_bytes_shared(int64_t B, int64_t C, int64_t H, int
  * Workspace: gspn_workspace_bytes_dirs() bytes, 256-byte aligned, caller-owned:
  * fp32 partial sums, and with a horizontal direction selected, transposed
  * copies of x and of each selected horizontal direction's five tensors. It is
- * 0 for a single vertical direction (workspace may then be NULL). Same status
- * codes as gspn_propagate_ws.
+ * 0 for a single vertical direction and for planes up to 64 x 64 (one
+ * wavefront per plane, the sum over the directions kept on chip); workspace
+ * may then be NULL. Same status codes as gspn_propagate_ws.
  */
 gspn_status gspn_propagate_dirs_ws(const void* x, const void* const w_logits[3],
                                    const void* lambda, const void* u, int64_t dir_stride,
@@ -306,8 +307,9 @@ size_t gspn_workspace_bytes_dirs(int64_t B, int64_t C, int64_t H, int64_t W,
  * Every direction runs as its own scan pair; the horizontal ones on
  * transposed copies. Workspace: gspn_backward_workspace_bytes_dirs() bytes,
  * 256-byte aligned, caller-owned (the stored states, an fp32 sum for grad_x,
- * and with a horizontal direction selected the transposed copies). Same
- * status codes as gspn_propagate_backward_ws.
+ * with a horizontal direction selected the transposed copies, and four fp64
+ * merge-gradient partials per plane). Same status codes as
+ * gspn_propagate_backward_ws.
  */
 gspn_status gspn_propagate_backward_dirs_ws(
     const void* x, const void* const w_logits[3], const void* lambda, const void* u,
