@@ -71,8 +71,11 @@ def test_every_mask(dtype):
 
 
 @pytest.mark.parametrize("G", [1, 2, 5, 8, 16, 1000])
-def test_local_groups(G):
-    shape = (1, 2, 37, 45)
+@pytest.mark.parametrize("shape", [(1, 2, 37, 45), (1, 2, 36, 44), (1, 2, 70, 66)],
+                         ids=["small", "small-runs", "large"])
+def test_local_groups(G, shape):
+    """Local groups on the one-wavefront path (element loads, and 4-column
+    runs) and on the large-plane path."""
     for dtype in (torch.float32, torch.bfloat16):
         inp = dirs_case(shape, dtype, 11 + G)
         assert_parity(run_dirs(inp, 15, G), oracle_dirs(inp, 15, G), f"dirs G={G}")
