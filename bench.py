@@ -291,7 +291,8 @@ def counter_traffic(plan: str, workload: str, digest: str):
 def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
     """The oracle as it stands on the first `planes` planes of the same
     device-resident inputs, all host cores (its backward pass when grad_out
-    is given)."""
+    is given). Returns the timing record and (planes, the oracle's result),
+    which the caller holds the timed output to."""
     import numpy as np
     import torch
 
@@ -333,40 +334,72 @@ def cpu_baseline(inp_dev, w, planes: int, grad_out=None):
         args = [host(inp_dev["x"])] + [host_dirs(inp_dev[k]) for k in ("l0", "l1", "l2",
                                                                          "lam", "u")]
         t0 = time.perf_counter()
-        oracle.backward_dirs(*args, host(grad_out), merge=merge, dirs=w.dirs,
-                             group_rows=w.group_rows, nthreads=threads)
+        ref = oracle.backward_dirs(*args, host(grad_out), merge=merge, dirs=w.dirs,
+                                   group_rows=w.group_rows, nthreads=threads)
         dt = time.perf_counter() - t0
         steps = planes * w.H * w.W * w.ndirs
         return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
                 "sample": f"per-direction backward, first {planes} of {w.B * w.C} planes "
-                          f"({w.H}x{w.W}, {w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}
+                          f"({w.H}x{w.W}, {w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}, \
+            (planes, ref)
     if w.per_direction:
         # sample plane p is channel p % C of the merge weights
         merge = inp_dev["merge"].cpu().numpy()[:, np.arange(planes) % w.C]
         args = [host(inp_dev["x"])] + [host_dirs(inp_dev[k]) for k in ("l0", "l1", "l2",
                                                                          "lam", "u")]
         t0 = time.perf_counter()
-        oracle.propagate_dirs(*args, merge=merge, dirs=w.dirs, group_rows=w.group_rows,
-                              nthreads=threads)
+        ref = oracle.propagate_dirs(*args, merge=merge, dirs=w.dirs, group_rows=w.group_rows,
+                                    nthreads=threads)
         dt = time.perf_counter() - t0
         steps = planes * w.H * w.W * w.ndirs
         return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
                 "sample": f"per-direction, first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, "
-                          f"{w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}
+                          f"{w.ndirs} dirs), {steps} elem-steps in {dt:.2f} s"}, (planes, ref)
     arrs = [host(inp_dev["x"])] + [host_logits(inp_dev[k]) for k in ("l0", "l1", "l2")] + \
         [host(inp_dev[k]) for k in ("lam", "u")]
     t0 = time.perf_counter()
     if grad_out is None:
-        oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
+        ref = oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=threads)
     else:
-        oracle.backward(*arrs, host(grad_out), dirs=w.dirs, group_rows=w.group_rows,
-                        nthreads=threads)
+        ref = oracle.backward(*arrs, host(grad_out), dirs=w.dirs, group_rows=w.group_rows,
+                              nthreads=threads)
     dt = time.perf_counter() - t0
     steps = planes * w.H * w.W * w.ndirs
     what = "backward " if grad_out is not None else ""
     return {"value": steps / dt, "unit": "elem-steps/s", "cores": threads, "kind": "oracle",
             "sample": f"{what}first {planes} of {w.B * w.C} planes ({w.H}x{w.W}, {w.ndirs} dirs), "
-                      f"{steps} elem-steps in {dt:.2f} s"}
+                      f"{steps} elem-steps in {dt:.2f} s"}, (planes, ref)
+
+
+def timed_output_parity(out, ref, planes: int, w, bwd: bool) -> dict:
+    """The timed output's first `planes` planes against the oracle's result
+    on them (forward: out; backward: every gradient of the sampled planes,
+    the per-direction merge-weight gradient aside, which sums over every
+    plane)."""
+    import numpy as np
+
+    def host(t, lead=()):
+        return t.detach().float().reshape(*lead, -1, w.H, w.W).cpu().numpy()
+
+    if not bwd:
+        got = host(out)[:planes]
+        return parity_of_sample(got, ref.reshape(-1, w.H, w.W)[:planes], w.dtype)
+    worst = {"planes": planes, "scaled_error": 0.0, "ok": True}
+    for k in ("x", "l0", "l1", "l2", "lam", "u"):
+        o = np.asarray(ref[k])
+        if w.per_direction and k != "x":
+            gk = host(out[k], (4,))[:, :planes].reshape(-1, w.H, w.W)
+            o = o.reshape(4, -1, w.H, w.W)[:, :planes].reshape(-1, w.H, w.W)
+        else:
+            n = o.reshape(-1, w.H, w.W).shape[0]
+            gk = host(out[k])[:n]
+            o = o.reshape(-1, w.H, w.W)
+        p = parity_of_sample(gk, o, w.dtype)
+        worst["rtol"] = p["rtol"]
+        worst[k] = p["scaled_error"]
+        worst["scaled_error"] = max(worst["scaled_error"], p["scaled_error"])
+        worst["ok"] = worst["ok"] and p["ok"]
+    return worst
 
 
 def prologue_work(w, B=None, H=None):
@@ -422,15 +455,90 @@ def cpu_baseline_module(inp_dev, w, seconds: float, prologue_only: bool):
                       f"{t_pro:.2f} + {t_prop:.2f} s"}
 
 
+STREAM_KINDS = ("read", "write", "copy")
+
+
+def stream_ceiling(torch, L, reps: int = 5, nbytes: int = 4 << 30, variants=None) -> dict:
+    """The library's hand-written HBM stream kernels (gspn_bench_stream:
+    16-byte accesses, grid-stride, every CU filled) over `nbytes` buffers,
+    each variant timed with events over `reps` passes after one warm pass.
+    Returns the best rate of each kind in GB/s (copy counts its read and
+    its write) and every variant's rate."""
+    L.gspn_bench_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.gspn_bench_stream.restype = ctypes.c_int
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    variants = variants or [(k, nt, bpc) for k in range(3) for nt in (0, 1) for bpc in (1, 2, 4, 8)]
+    res = {"bytes": nbytes, "variants": {}}
+    for kind, nt, bpc in variants:
+        def run():
+            rc = L.gspn_bench_stream(kind, nt, src.data_ptr(), dst.data_ptr(), nbytes, bpc,
+                                     stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"gspn_bench_stream returned {rc}")
+        run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        moved = nbytes * (2 if kind == 2 else 1)
+        gbs = moved / (ms * 1e-3) / 1e9
+        name = STREAM_KINDS[kind]
+        res["variants"][f"{name}{'_nt' if nt else ''}_b{bpc}"] = round(gbs, 1)
+        res[f"{name}_gbs"] = round(max(res.get(f"{name}_gbs", 0.0), gbs), 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def handshake_latency(torch, L, rounds: int = 20000) -> dict:
+    """Round trips of a flag between two workgroups through device memory
+    (gspn_bench_handshake), for partner workgroups at several distances in
+    the dispatch order (workgroups are dealt to the XCDs in turn, so 8 apart
+    is the same XCD on an 8-XCD part). Microseconds per round trip."""
+    L.gspn_bench_handshake.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    L.gspn_bench_handshake.restype = ctypes.c_int
+    L.gspn_bench_wall_clock_khz.restype = ctypes.c_int
+    khz = L.gspn_bench_wall_clock_khz()
+    flags = torch.zeros(512, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    abort = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    res = {"wall_clock_khz": khz, "rounds": rounds}
+    for partner in (1, 8, 16, 64):
+        flags.zero_()
+        out.zero_()
+        rc = L.gspn_bench_handshake(flags.data_ptr(), abort.data_ptr(), rounds, 1 << 20, partner,
+                                    out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gspn_bench_handshake returned {rc}")
+        torch.cuda.synchronize()
+        ticks, missed, polls, missed_b = (int(v) for v in out.cpu())
+        res[f"partner_{partner}"] = {
+            "us_per_round_trip": ticks / max(khz, 1) * 1e3 / rounds if khz else None,
+            "polls_per_round_trip": polls / rounds, "gave_up": missed + missed_b}
+    return res
+
+
 def calibrate(torch, reps: int) -> int:
-    """Plain copy of a 4 GiB buffer (4 GiB read + 4 GiB written per call) and
-    a sum over it (4 GiB read), timed with events; one JSON line."""
+    """The hand-written read / write / copy stream kernels on 4 GiB buffers,
+    torch's own copy and sum for comparison, and the cross-workgroup
+    handshake latency; one JSON line."""
+    import linear_spatial_propagation_line_amd as g
+    res = {"stream_kernels": stream_ceiling(torch, g.lib(), reps=max(reps, 3)),
+           "handshake": handshake_latency(torch, g.lib())}
     n = 1 << 30                      # float32 elements = 4 GiB
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    res = {"copy_bytes_per_call": 2 * 4 * n, "read_bytes_per_call": 4 * n}
-    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 8 * n),
-                             ("read", lambda: src.sum(), 4 * n)):
+    for name, fn, nbytes in (("torch_copy", lambda: dst.copy_(src), 8 * n),
+                             ("torch_sum", lambda: src.sum(), 4 * n)):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -440,10 +548,54 @@ def calibrate(torch, reps: int) -> int:
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
-        res[f"{name}_ms"] = ms
         res[f"{name}_gbs"] = nbytes / (ms * 1e-3) / 1e9
     print(json.dumps(res), flush=True)
     return 0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_per_core_rate(seconds: float = 1.0) -> dict:
+    """The oracle on one thread over planes of the 56x56 classification
+    workload (4 directions, fp32): its per-core rate on this host."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["cls_56x56"]
+    planes = max(1, int(seconds * 2.0e7 / (w.H * w.W * w.ndirs)))
+    inp = make_inputs(w, seed=4242, B=1, C=planes)
+    arrs = [inp[k].numpy() for k in ("x", "l0", "l1", "l2", "lam", "u")]
+    t0 = time.perf_counter()
+    oracle.propagate(*arrs, dirs=w.dirs, group_rows=w.group_rows, nthreads=1)
+    dt = time.perf_counter() - t0
+    steps = planes * w.H * w.W * w.ndirs
+    del torch, np
+    return {"value": steps / dt, "unit": "elem-steps/s", "threads": 1,
+            "sample": f"{planes} planes of 56x56 fp32, 4 dirs, {steps} elem-steps in {dt:.2f} s"}
+
+
+def parity_of_sample(got, ref, dtype: str) -> dict:
+    """Scaled error max |g - o| / (|o| + rms(o)) of the timed output's sample
+    planes against the oracle's, per plane, with the rms over the sample."""
+    import numpy as np
+    rtol = 1e-5 if dtype == "f32" else 1e-2
+    rms = float(np.sqrt(np.mean([np.mean(r * r) for r in ref]))) if len(ref) else 0.0
+    worst = 0.0
+    for gp, rp in zip(got, ref):
+        err = np.max(np.abs(gp.astype(np.float64) - rp) / (np.abs(rp) + rms + 1e-300))
+        worst = max(worst, float(err))
+    return {"planes": len(ref), "scaled_error": worst, "rtol": rtol, "ok": bool(worst <= rtol)}
 
 
 def main() -> int:
@@ -455,6 +607,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough wall time of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the stream-kernel bandwidth ceiling measured after the timed steps")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (all six gradients) instead of the forward")
     ap.add_argument("--prologue", action="store_true",
@@ -588,22 +742,45 @@ def main() -> int:
     L = g.lib()
     max_launch = 64   # launches traced per step (two plane groups double a chain)
     evs = [hip.events(2 * max_launch) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # step boundaries: events on the caller's stream, into which every launch
+    # of a step (also those on helper streams) is joined
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t_start.record(stream)
+    sev[0].record(stream)
     wall0 = time.perf_counter()
     counts = []
     for k in range(args.steps):
         L.gspn_trace_events(evs[k], max_launch)
         step(k)
         counts.append(L.gspn_trace_count())
+        sev[k + 1].record(stream)
     L.gspn_trace_events(None, 0)
-    t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
+    ms_total = sev[0].elapsed_time(sev[-1])
     ms_per_step = ms_total / args.steps
+    step_ms = sorted(sev[k].elapsed_time(sev[k + 1]) for k in range(args.steps))
+
+    def med(v):
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+    step_stats = {"steps": args.steps, "median_ms": med(step_ms), "min_ms": step_ms[0],
+                  "mean_ms": ms_per_step, "max_ms": step_ms[-1]}
+    if args.steps < 50:
+        # a further sample of at least 50 steps and about a second, after the
+        # timed region, for the median and min of the step time
+        n_more = int(min(2000, max(50, 1000.0 / max(ms_per_step, 1e-3))))
+        mev = [torch.cuda.Event(enable_timing=True) for _ in range(n_more + 1)]
+        mev[0].record(stream)
+        for k in range(n_more):
+            step(args.steps + k)
+            mev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        more = sorted(mev[k].elapsed_time(mev[k + 1]) for k in range(n_more))
+        step_stats["extra_sample"] = {"steps": n_more, "median_ms": med(more),
+                                      "min_ms": more[0],
+                                      "mean_ms": mev[0].elapsed_time(mev[-1]) / n_more}
 
     nl = min(counts[0], max_launch)
     launches = []
@@ -647,9 +824,22 @@ def main() -> int:
     traffic = counter_traffic(plan, w.name, source_digest(plan))
 
     value = w.elem_steps * args.steps / (ms_total * 1e-3)
+    ceiling = None if args.no_ceiling else stream_ceiling(
+        torch, L, reps=5, variants=[(2, nt, bpc) for nt in (0, 1) for bpc in (1, 2, 4)] +
+        [(0, 1, 2), (1, 1, 2)])
     roofline = {"bound": "hbm", "kernel": unit_name, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": traffic, "algorithmic_bytes_per_step": q_min, "unit_ms": unit_ms}
+                "traffic": traffic,
+                "traffic_counter": "FETCH_SIZE * 2 + WRITE_SIZE per step (bytes between L2 and "
+                                   "the memory fabric; last-level-cache hits included, so an "
+                                   "upper bound on HBM bytes)",
+                "algorithmic_bytes_per_step": q_min, "unit_ms": unit_ms}
+    if ceiling:
+        roofline["ceiling_gbs"] = ceiling["copy_gbs"]
+        roofline["frac_of_ceiling"] = achieved / ceiling["copy_gbs"]
+        roofline["ceiling"] = "hand-written 16-byte copy kernel over 4 GiB (gspn_bench_stream), " \
+                              "read + write bytes; read-only %.0f, write-only %.0f GB/s" % (
+                                  ceiling["read_gbs"], ceiling["write_gbs"])
     if pro_only:
         # the prologue's two products: bound by MFMA or by HBM, whichever its
         # flops and bytes make the longer at peak
@@ -695,17 +885,26 @@ def main() -> int:
                    "path_qmin_bytes": q_min,
                    "host_wall_s": round(wall, 3), "input_sets": nsets},
         "roofline": roofline,
+        "step_stats": step_stats,
     }
     if not args.no_cpu_baseline and mod:
-        result["cpu_baseline"] = cpu_baseline_module(sets[0], w, args.cpu_seconds, pro_only)
+        cb = cpu_baseline_module(sets[0], w, args.cpu_seconds, pro_only)
+        cb["parity"] = {"checked": False,
+                        "why": "the CPU sample is a band of rows, not whole planes"}
+        result["cpu_baseline"] = cb
     elif not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
         # the oracle runs roughly 1.5e7 - 3.5e7 elem-steps/s per core forward
         # and 0.6e6 - 3e6 backward (large planes at the low end)
         rate = 6e5 if bwd else 2.5e7
         planes = int(args.cpu_seconds * rate * cores / (w.H * w.W * w.ndirs)) + 1
-        result["cpu_baseline"] = cpu_baseline(sets[0], w, planes,
-                                              grad_out=sets[0]["gy"] if bwd else None)
+        cb, (np_s, ref) = cpu_baseline(sets[0], w, planes,
+                                       grad_out=sets[0]["gy"] if bwd else None)
+        # outs[0] holds set 0's result from the last timed step that used it
+        cb["parity"] = timed_output_parity(outs[0], ref, np_s, w, bwd)
+        cb["cpu_model"] = cpu_model()
+        cb["per_core"] = oracle_per_core_rate()
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     return 0
 

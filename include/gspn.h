@@ -48,7 +48,15 @@
 extern "C" {
 #endif
 
-typedef enum { GSPN_F32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+typedef enum {
+  GSPN_F32 = 0,
+  GSPN_BF16 = 1,
+  /* Not element types. They give gspn_dtype the range of a 32-bit int, so
+   * that any value a caller passes is a valid value of the type and can be
+   * checked (GSPN_E_DTYPE) without undefined behaviour in C++. */
+  GSPN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  GSPN_DTYPE_RANGE_MAX_ = 2147483647
+} gspn_dtype;
 
 /* scan directions: top->bottom, bottom->top, left->right, right->left */
 enum {

@@ -133,6 +133,36 @@ def _check(status: int) -> None:
         raise GspnError(status, lib().gspn_last_error().decode())
 
 
+def _check_out(out, shape, dtype, device, what="out"):
+    """A caller-supplied output must be a contiguous tensor of the given
+    shape and dtype on the inputs' device: the library writes exactly that
+    many bytes through its pointer."""
+    import torch
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if out.device != device:
+        raise TypeError(f"{what} must be on {device}, not {out.device}")
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{what} must be {dtype} {tuple(shape)}, "
+                         f"not {out.dtype} {tuple(out.shape)}")
+    if not out.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _check_workspace(ws, device):
+    """A caller-supplied workspace must be a contiguous uint8 tensor on the
+    inputs' device; the library checks its size and alignment."""
+    import torch
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if ws.device != device:
+        raise TypeError(f"workspace must be on {device}, not {ws.device}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+
+
 def workspace_bytes(B, C, H, W, dirs=ALL, group_rows=0, dtype=GSPN_F32) -> int:
     return int(lib().gspn_workspace_bytes(B, C, H, W, dirs, group_rows, dtype))
 
@@ -150,8 +180,8 @@ def _check_tensors(x, logits, others):
     B, C, H, W = x.shape
     cl = logits[0].shape[1] if logits[0].dim() == 4 else -1
     for t in (x,) + tuple(logits) + tuple(others):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError("all inputs must be torch tensors on a GPU device")
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device != x.device:
+            raise TypeError("all inputs must be torch tensors on x's GPU device")
         if t.dtype != x.dtype or not t.is_contiguous():
             raise ValueError("inputs must be contiguous tensors of one dtype")
     for t in others:
@@ -176,6 +206,8 @@ def propagate(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
     dt = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(out, x.shape, x.dtype, x.device)
+    _check_workspace(workspace, x.device)
     L = lib()
     need = int(L.gspn_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
     if need > 0 and workspace is None:
@@ -227,6 +259,8 @@ def propagate_dirs(x, logits, lam, u, merge=None, dirs: int = ALL, group_rows: i
     dt = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(out, x.shape, x.dtype, x.device)
+    _check_workspace(workspace, x.device)
     L = lib()
     need = int(L.gspn_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dt))
     if need > 0 and workspace is None:
@@ -279,6 +313,10 @@ def prologue(x_in, w_reduce, b_reduce, w_params, b_params, outs=None, stream=Non
     if outs is None:
         outs = {k: torch.empty((B, C, H, W), dtype=x_in.dtype, device=x_in.device)
                 for k in ("x",) + PARAM_NAMES}
+    for k in ("x",) + PARAM_NAMES:
+        if k not in outs:
+            raise ValueError(f"outs is missing {k!r}")
+        _check_out(outs[k], (B, C, H, W), x_in.dtype, x_in.device, f"outs[{k!r}]")
     if stream is None:
         stream = torch.cuda.current_stream(x_in.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -304,6 +342,8 @@ def module(x_in, w_reduce, b_reduce, w_params, b_params, dirs: int = ALL, group_
     dt = _dtype_code(x_in)
     if out is None:
         out = torch.empty((B, C, H, W), dtype=x_in.dtype, device=x_in.device)
+    _check_out(out, (B, C, H, W), x_in.dtype, x_in.device)
+    _check_workspace(workspace, x_in.device)
     L = lib()
     need = int(L.gspn_module_workspace_bytes(B, C, H, W, dirs, group_rows, dt))
     if workspace is None:
@@ -326,10 +366,13 @@ def propagate_alloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out
     hipMallocAsync on the stream (the plain gspn_propagate entry point)."""
     import torch
     l0, l1, l2 = logits
-    B, C, H, W = x.shape
+    B, C, H, W, cl = _check_tensors(x, (l0, l1, l2), (lam, u))
+    if cl != C:
+        raise ValueError("the allocating entry point takes unshared logits")
     dt = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(out, x.shape, x.dtype, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -400,6 +443,7 @@ def propagate_backward_dirs(x, logits, lam, u, grad_out, merge=None, dirs: int =
     if gm is not None and (gm.dtype != torch.float32 or tuple(gm.shape) != (4, C)
                            or not gm.is_contiguous() or gm.device != x.device):
         raise ValueError("the merge gradient must be a contiguous float32 [4, C] tensor")
+    _check_workspace(workspace, x.device)
     L = lib()
     need = int(L.gspn_backward_workspace_bytes_dirs(B, C, H, W, dirs, group_rows, dt))
     if need > 0 and workspace is None:
@@ -452,6 +496,7 @@ def propagate_backward(x, logits, lam, u, grad_out, dirs: int = ALL, group_rows:
             raise ValueError("the allocating backward entry point takes unshared logits")
         _check(L.gspn_propagate_backward(*args, sptr))
         return grads
+    _check_workspace(workspace, x.device)
     need = int(L.gspn_backward_workspace_bytes_shared(B, C, H, W, cl, dirs, group_rows, dt))
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libgspn.so")
 SOURCES = ["gspn_api.cpp", "gspn_plane.hip", "gspn_stream.hip", "gspn_tpipe.hip",
            "gspn_band.hip", "gspn_bwd_stream.hip", "gspn_bwd_plane.hip",
            "gspn_bwd_band.hip", "gspn_dirs.hip",
-           "gspn_prologue.hip", "gspn_bwd_tpipe.hip", "gspn_groups.cpp"]
+           "gspn_prologue.hip", "gspn_bwd_tpipe.hip", "gspn_groups.cpp",
+           "gspn_calib.hip"]
 ARCH = os.environ.get("GSPN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

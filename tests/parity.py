@@ -23,17 +23,18 @@ RTOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 
 
 def rtol_for(dtype, shape) -> float:
-    """The dtype's bound; for fp32 scans longer than 2048 steps, the bound the
-    arithmetic gives instead. The recurrence rounds each step (weights that
-    sum to 1 only to within an ulp, three FMAs), and over n steps those
-    errors add up to at most about n * 2^-24 relatively: 5.4e-4 at 9000
-    steps, where measured errors reach 4e-5 -- above a fixed 1e-5 although
-    nothing is wrong. Every workload scans at most 2048 steps and keeps the
-    plain bound."""
+    """The dtype's bound; for fp32 scans longer than 2048 steps, a bound that
+    grows with the scan length. The recurrence rounds each step (weights
+    that sum to 1 only to within an ulp, three FMAs), so the relative error
+    can grow linearly with the number of steps n, up to about n * 2^-24.
+    Measured errors grow at about a thirteenth of that (4e-5 at 9000 steps);
+    the bound n * 2^-26 (1.3e-4 at 9000 steps) keeps a margin of about 3 over
+    them, so a kernel that rounds markedly worse still fails. Every workload
+    scans at most 2048 steps and keeps the plain bound."""
     base = RTOL[dtype]
     n = max(shape[-2], shape[-1])
     if dtype == torch.float32 and n > 2048:
-        return max(base, n * 2.0 ** -24)
+        return max(base, n * 2.0 ** -26)
     return base
 
 

@@ -9,8 +9,8 @@ import pytest
 
 import linear_spatial_propagation_line_amd as g
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "gspn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,16 +22,20 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gspn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(gspn_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 7, names
+    assert "gspn_bench_stream" in names
     for n in names:
-        assert hasattr(L, n), f"{n} declared in gspn.h but not exported"
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
 
 
 def test_abi_version(L):
@@ -501,3 +505,4 @@ def test_module_workspace(L):
     st = L.gspn_module_ws(BASE, PCIN, BASE + SZ, None, BASE + 3 * SZ, None, 0, PC, PH, PW, 15,
                           0, 0, BASE + 5 * SZ, BASE + 7 * SZ, 6 * tb, None)
     assert st == 0
+

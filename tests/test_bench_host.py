@@ -106,3 +106,41 @@ def test_per_direction_backward_path_bytes():
     s = 2
     per_dir = (5 * s + 4) + (12 * s + 12)
     assert bench.bwd_dirs_path_bytes(w) == 4 * s + 2 * 20 * s + 8 + 4 * per_dir
+
+
+def test_parity_of_sample_catches_a_planted_error():
+    """The bench's in-run check of the timed output: equal planes pass, one
+    element off by more than the dtype's bound fails."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((3, 8, 8))
+    got = ref.astype(np.float32)
+    p = bench.parity_of_sample(got, ref, "f32")
+    assert p["ok"] and p["planes"] == 3 and p["scaled_error"] < 1e-6
+    bad = got.copy()
+    bad[1, 2, 3] += 1e-2
+    assert not bench.parity_of_sample(bad, ref, "f32")["ok"]
+    assert bench.parity_of_sample(bad, ref, "bf16")["ok"]
+
+
+def test_timed_output_parity_forward_and_backward():
+    import numpy as np
+    import torch
+    w = WORKLOADS["cls_56x56"]
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal((1, 4, w.H, w.W))
+    out = torch.zeros((w.B, w.C, w.H, w.W))
+    out.reshape(-1, w.H, w.W)[:4] = torch.from_numpy(ref[0]).float()
+    assert bench.timed_output_parity(out, ref, 4, w, False)["ok"]
+    out.reshape(-1, w.H, w.W)[3, 0, 0] += 1.0
+    assert not bench.timed_output_parity(out, ref, 4, w, False)["ok"]
+    grads = {k: torch.zeros((w.B, w.C, w.H, w.W)) for k in ("x", "l0", "l1", "l2", "lam", "u")}
+    refs = {k: rng.standard_normal((1, 2, w.H, w.W)) for k in grads}
+    for k in grads:
+        grads[k].reshape(-1, w.H, w.W)[:2] = torch.from_numpy(refs[k][0]).float()
+    p = bench.timed_output_parity(grads, refs, 2, w, True)
+    assert p["ok"] and p["planes"] == 2
+
+
+def test_cpu_model_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
