@@ -103,6 +103,34 @@ gspn_status gspn_propagate(const void* x, const void* const w_logits[3],
                            hipStream_t stream);
 
 /*
+ * gspn_propagate_noalloc -- gspn_propagate for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, layout and result as gspn_propagate; it
+ * calls no hipMalloc, hipFree or other allocating routine, creates no stream
+ * or event, and enqueues every launch on `stream`.
+ *
+ * Scratch memory comes from one array of gspn_noalloc_scratch_bytes()
+ * (64 MiB) per device, a static device variable of the library: each device
+ * the library runs on holds it from the library's load until the process
+ * ends. A problem whose gspn_workspace_bytes() exceeds that size returns
+ * GSPN_E_WORKSPACE before anything is enqueued. Every call on one device uses
+ * the same array and leaves its contents behind (nothing in it needs to start
+ * at zero): calls whose work overlaps in time on one device, on different
+ * streams or from different threads, race on it and give wrong results, so
+ * the caller serialises them. The array's address is looked up once per
+ * device (on that device's first call whose plan needs scratch).
+ */
+gspn_status gspn_propagate_noalloc(const void* x, const void* const w_logits[3],
+                                   const void* lambda, const void* u, int64_t B,
+                                   int64_t C, int64_t H, int64_t W, uint32_t dir_mask,
+                                   int64_t group_rows, gspn_dtype dtype, void* out,
+                                   hipStream_t stream);
+
+/* gspn_noalloc_scratch_bytes -- size of gspn_propagate_noalloc's per-device
+ * scratch array in bytes. */
+size_t gspn_noalloc_scratch_bytes(void);
+
+/*
  * gspn_workspace_bytes -- scratch bytes gspn_propagate_ws needs for this
  * problem (0 when the plan keeps everything on chip). Returns 0 for invalid
  * arguments as well; gspn_propagate_ws reports those.

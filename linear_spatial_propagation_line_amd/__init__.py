@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.gspn_propagate.restype = ctypes.c_int
         L.gspn_propagate_ws.argtypes = common + [vp, ctypes.c_size_t, vp]
         L.gspn_propagate_ws.restype = ctypes.c_int
+        L.gspn_propagate_noalloc.argtypes = common + [vp]
+        L.gspn_propagate_noalloc.restype = ctypes.c_int
+        L.gspn_noalloc_scratch_bytes.argtypes = []
+        L.gspn_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.gspn_workspace_bytes.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
         L.gspn_workspace_bytes.restype = ctypes.c_size_t
         L.gspn_plan_name.argtypes = [i64, i64, i64, i64, u32, i64, ctypes.c_int]
@@ -379,6 +383,37 @@ def propagate_alloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out
     lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
     _check(lib().gspn_propagate(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H, W,
                                 dirs, group_rows, dt, out.data_ptr(), sptr))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of gspn_propagate_noalloc's per-device scratch array."""
+    return int(lib().gspn_noalloc_scratch_bytes())
+
+
+def propagate_noalloc(x, logits, lam, u, dirs: int = ALL, group_rows: int = 0, out=None,
+                      stream=None):
+    """Same as propagate() through the entry point that allocates nothing
+    (gspn_propagate_noalloc): scratch comes from the library's static
+    per-device array, so problems whose workspace exceeds
+    noalloc_scratch_bytes() raise GSPN_E_WORKSPACE, and calls that overlap in
+    time on one device race. ``out`` must be supplied by callers that cannot
+    allocate."""
+    import torch
+    l0, l1, l2 = logits
+    B, C, H, W, cl = _check_tensors(x, (l0, l1, l2), (lam, u))
+    if cl != C:
+        raise ValueError("the no-allocation entry point takes unshared logits")
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_out(out, x.shape, x.dtype, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lg = (ctypes.c_void_p * 3)(l0.data_ptr(), l1.data_ptr(), l2.data_ptr())
+    _check(lib().gspn_propagate_noalloc(x.data_ptr(), lg, lam.data_ptr(), u.data_ptr(), B, C, H,
+                                        W, dirs, group_rows, dt, out.data_ptr(), sptr))
     return out
 
 

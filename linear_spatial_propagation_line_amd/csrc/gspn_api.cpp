@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gspn.h"
@@ -25,6 +26,18 @@ gspn_status fail(gspn_status s, const std::string& detail) {
 }
 
 size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
+
+// Scratch memory of gspn_propagate_noalloc: one statically sized array per
+// device, held from the library's load until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream, kDirs };
 
@@ -519,6 +532,53 @@ gspn_status gspn_propagate(const void* x, const void* const w_logits[3], const v
     if (e != hipSuccess && s == GSPN_OK) s = fail(GSPN_E_HIP, hipGetErrorString(e));
   }
   return s;
+}
+
+size_t gspn_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+gspn_status gspn_propagate_noalloc(const void* x, const void* const w_logits[3],
+                                   const void* lambda, const void* u, int64_t B, int64_t C,
+                                   int64_t H, int64_t W, uint32_t dir_mask, int64_t group_rows,
+                                   gspn_dtype dtype, void* out, hipStream_t stream) {
+  Checked chk;
+  gspn::Problem pr;
+  gspn_status s = check_all(x, w_logits, lambda, u, B, C, H, W, dir_mask, group_rows,
+                            dtype, out, &chk, &pr, C > 0 ? C : 1);
+  if (s != GSPN_OK) return s;
+  if (chk.ws_bytes > kNoallocScratchBytes)
+    return fail(GSPN_E_WORKSPACE,
+                "this problem needs " + std::to_string(chk.ws_bytes) +
+                    " bytes of scratch; gspn_propagate_noalloc holds " +
+                    std::to_string(kNoallocScratchBytes) + " (use gspn_propagate_ws)");
+  if (B * C == 0) return GSPN_OK;
+  void* ws = nullptr;
+  if (chk.ws_bytes > 0) {
+    // the device the work runs on is the stream's; look its scratch up with
+    // that device current
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) {
+      dev = cur;
+      if (stream) e = hipStreamGetDevice(stream, &dev);
+    }
+    if (e != hipSuccess) return fail(GSPN_E_HIP, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GSPN_E_HIP, "device index out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+        return fail(GSPN_E_HIP, hipGetErrorString(e));
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur) (void)hipSetDevice(cur);
+      if (e != hipSuccess || !p)
+        return fail(GSPN_E_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                    hipGetErrorString(e));
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  pr.one_stream = true;
+  return run(pr, chk.plan, ws, stream);
 }
 
 size_t gspn_workspace_bytes(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dir_mask,

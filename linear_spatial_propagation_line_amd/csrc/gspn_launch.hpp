@@ -28,6 +28,8 @@ struct Problem {
   // element offset d * dir_stride, merged with merge[d * C + c] (null: 1)
   int64_t dir_stride = 0;
   const float* merge = nullptr;
+  // run every launch on the caller's stream (no helper streams or events)
+  bool one_stream = false;
 };
 
 // A validated backward problem: the forward inputs, grad_out (gy) and the six

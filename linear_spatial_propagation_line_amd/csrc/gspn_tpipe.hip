@@ -759,7 +759,7 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   // Every kernel needs one whole compute unit per plane, so a plane count a
   // little above the CU count leaves a latency-bound second round. Two plane
   // groups on two streams let one group's K2/K3 overlap the other's tail.
-  const int ngroups = tpipe_groups(planes);
+  const int ngroups = pr.one_stream ? 1 : tpipe_groups(planes);
   hipStream_t streams[kMaxGroups] = {stream, stream, stream, stream};
   hipEvent_t fork = nullptr, join[kMaxGroups] = {};
   hipError_t e = hipSuccess;

@@ -35,6 +35,8 @@ int main(void) {
   EXPECT(gspn_propagate(P(0), lg, P(4), P(5), 1, 1, 8, 8, 15, 0, GSPN_F32, (char*)P(0) + 8, NULL) == GSPN_E_ALIAS);
   EXPECT(gspn_propagate(P(0), lg, P(4), P(5), 0, 3, 8, 8, 15, 0, GSPN_F32, P(6), NULL) == GSPN_OK);
   EXPECT(gspn_propagate_ws(P(0), lg, P(4), P(5), 2, 3, 300, 200, 15, 0, GSPN_F32, P(6), NULL, 0, NULL) == GSPN_E_WORKSPACE);
+  EXPECT(gspn_propagate_noalloc(P(0), lg, P(4), P(5), 1, 320, 2048, 1024, 15, 0, GSPN_BF16, P(6), NULL) == GSPN_E_WORKSPACE);
+  EXPECT(gspn_propagate_noalloc(P(0), lg, P(4), P(5), 0, 3, 8, 8, 15, 0, GSPN_F32, P(6), NULL) == GSPN_OK);
   EXPECT(gspn_propagate_shared_ws(P(0), lg, 4, P(4), P(5), 1, 6, 8, 8, 15, 0, GSPN_F32, P(6), NULL, 0, NULL) == GSPN_E_SHAPE);
   EXPECT(gspn_workspace_bytes(1, 320, 2048, 1024, 15, 0, GSPN_BF16) > 0);
   EXPECT(gspn_workspace_bytes(1, 1, 0, 5, 15, 0, GSPN_F32) == 0);
@@ -67,6 +69,7 @@ int main(void) {
   EXPECT(gspn_trace_kernel(-1, NULL) == NULL);
   gspn_trace_events(NULL, 0);
   EXPECT(gspn_abi_version() == 1);
+  EXPECT(gspn_noalloc_scratch_bytes() == (size_t)64 << 20);
   EXPECT(gspn_bench_stream(3, 0, P(0), P(1), 4096, 4, NULL) == 1);
   EXPECT(gspn_bench_stream(2, 0, P(0), P(1), 4095, 4, NULL) == 1);
   if (fails) fprintf(stderr, "%d checks failed\n", fails);

@@ -33,7 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) >= 7, names
-    assert "gspn_bench_stream" in names
+    assert "gspn_bench_stream" in names and "gspn_propagate_noalloc" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
 
@@ -506,3 +506,23 @@ def test_module_workspace(L):
                           0, 0, BASE + 5 * SZ, BASE + 7 * SZ, 6 * tb, None)
     assert st == 0
 
+
+def call_noalloc(L, x=BASE, lg=(BASE + SZ, BASE + 2 * SZ, BASE + 3 * SZ), lam=BASE + 4 * SZ,
+                 u=BASE + 5 * SZ, B=1, C=1, H=8, W=8, mask=15, G=0, dt=0, out=BASE + 6 * SZ):
+    arr = None if lg is None else (ctypes.c_void_p * 3)(*lg)
+    return L.gspn_propagate_noalloc(x, arr, lam, u, B, C, H, W, mask, G, dt, out, None)
+
+
+def test_noalloc_validation_before_any_hip_call(L):
+    """The allocation-free entry point validates like gspn_propagate and
+    rejects, before touching HIP, a problem whose scratch exceeds its static
+    per-device array."""
+    assert L.gspn_noalloc_scratch_bytes() == 64 << 20
+    assert call_noalloc(L, x=None) == g.STATUS["GSPN_E_NULL"]
+    assert call_noalloc(L, mask=0) == g.STATUS["GSPN_E_DIRMASK"]
+    assert call_noalloc(L, out=BASE + 8) == g.STATUS["GSPN_E_ALIAS"]
+    assert call_noalloc(L, B=0) == 0
+    # 320 planes of 2048 x 1024: the pipeline's workspace is gigabytes
+    assert L.gspn_workspace_bytes(1, 320, 2048, 1024, 15, 0, 1) > 64 << 20
+    assert call_noalloc(L, B=1, C=320, H=2048, W=1024, dt=1) == g.STATUS["GSPN_E_WORKSPACE"]
+    assert "64" in L.gspn_last_error().decode() or "67108864" in L.gspn_last_error().decode()

@@ -44,6 +44,8 @@ def test_propagate_checks_out_and_workspace(inp):
             g.propagate(inp["x"], lg, inp["lam"], inp["u"], out=out)
         with pytest.raises(exc):
             g.propagate_alloc(inp["x"], lg, inp["lam"], inp["u"], out=out)
+        with pytest.raises(exc):
+            g.propagate_noalloc(inp["x"], lg, inp["lam"], inp["u"], out=out)
     for ws, exc in bad_workspaces():
         with pytest.raises(exc):
             g.propagate(inp["x"], lg, inp["lam"], inp["u"], workspace=ws)
