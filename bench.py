@@ -65,9 +65,9 @@ PLAN_SOURCES = {
     "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_device.hpp"),
     "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_dirs.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
-    "prologue": ("gspn_prologue.hip", "gspn_device.hpp"),
-    "module": ("gspn_prologue.hip", "gspn_plane.hip", "gspn_band.hip", "gspn_tpipe.hip",
-               "gspn_stream.hip", "gspn_device.hpp"),
+    "prologue": ("gspn_prologue.hip", "gspn_mfma.hpp", "gspn_device.hpp"),
+    "module": ("gspn_prologue.hip", "gspn_fused.hip", "gspn_mfma.hpp", "gspn_plane.hip",
+               "gspn_band.hip", "gspn_tpipe.hip", "gspn_stream.hip", "gspn_device.hpp"),
 }
 
 
@@ -184,6 +184,9 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     Module prologue (counted per pixel of B images: `planes` is B here):
       prologue_reduce  x_in read (Cin s), x written (C s)
       prologue_params  x read (C s), five parameter tensors written (5 C s)
+      fused_unit (small planes: the parameter product fused with the scan,
+          counted per pixel of the B * C planes): x read (s), out written (s);
+          the parameters never leave the chip
       (the weights, read once from HBM, are left out)
     """
     s = 4 if w.dtype == "f32" else 2
@@ -222,6 +225,7 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "dir_tr_acc": 4 + (4 if w.dirs & 3 else s),
         "prologue_reduce": (w.prologue_cin + w.C) * s,
         "prologue_params": 6 * w.C * s,
+        "fused_unit": 2 * s,
     }[kernel]
     return per * px
 
@@ -442,17 +446,20 @@ def cpu_baseline_module(inp_dev, w, seconds: float, prologue_only: bool):
     sample = f"first image, rows 0..{rows - 1} of {w.H} ({rows}x{w.W} pixels, Cin {w.prologue_cin}, C {w.C})"
     if prologue_only:
         return {"value": flops / t_pro / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": f"prologue, {sample}, {t_pro:.2f} s"}
+                "sample": f"prologue, {sample}, {t_pro:.2f} s"}, None
     p = {k: oracle.round_to(pro[k], w.dtype) for k in ("l0", "l1", "l2", "lam", "u")}
     t0 = time.perf_counter()
-    oracle.propagate(pro["xr"], p["l0"], p["l1"], p["l2"], p["lam"], p["u"], dirs=w.dirs,
-                     group_rows=w.group_rows, nthreads=cores)
+    ref = oracle.propagate(pro["xr"], p["l0"], p["l1"], p["l2"], p["lam"], p["u"], dirs=w.dirs,
+                           group_rows=w.group_rows, nthreads=cores)
     t_prop = time.perf_counter() - t0
     steps = w.C * rows * w.W * w.ndirs
-    return {"value": steps / (t_pro + t_prop), "unit": "elem-steps/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"prologue + propagation, {sample}, {steps} elem-steps in "
-                      f"{t_pro:.2f} + {t_prop:.2f} s"}
+    res = {"value": steps / (t_pro + t_prop), "unit": "elem-steps/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"prologue + propagation, {sample}, {steps} elem-steps in "
+                     f"{t_pro:.2f} + {t_prop:.2f} s"}
+    # the unit's output of the first image is comparable when the sample
+    # holds its whole planes
+    return res, (ref if rows == w.H else None)
 
 
 STREAM_KINDS = ("read", "write", "copy")
@@ -609,6 +616,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the stream-kernel bandwidth ceiling measured after the timed steps")
+    ap.add_argument("--no-step-sample", action="store_true",
+                    help="skip the extra sample of >= 50 steps taken for the median and min "
+                         "when fewer steps are timed (profiling runs)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (all six gradients) instead of the forward")
     ap.add_argument("--prologue", action="store_true",
@@ -767,7 +777,7 @@ def main() -> int:
 
     step_stats = {"steps": args.steps, "median_ms": med(step_ms), "min_ms": step_ms[0],
                   "mean_ms": ms_per_step, "max_ms": step_ms[-1]}
-    if args.steps < 50:
+    if args.steps < 50 and not args.no_step_sample:
         # a further sample of at least 50 steps and about a second, after the
         # timed region, for the median and min of the step time
         n_more = int(min(2000, max(50, 1000.0 / max(ms_per_step, 1e-3))))
@@ -840,6 +850,19 @@ def main() -> int:
         roofline["ceiling"] = "hand-written 16-byte copy kernel over 4 GiB (gspn_bench_stream), " \
                               "read + write bytes; read-only %.0f, write-only %.0f GB/s" % (
                                   ceiling["read_gbs"], ceiling["write_gbs"])
+    if mod and not pro_only:
+        # the whole unit: its products' flops against the MFMA peak, its
+        # compulsory bytes (x_in read, out written) against HBM; the bound is
+        # whichever takes the longer at peak
+        flops, _ = prologue_work(w)
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        if flops / (peak * 1e12) >= q_min / (HBM_PEAK_GBS * 1e9):
+            ach = flops / (unit_ms * 1e-3) / 1e12
+            roofline.update({"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                             "frac": ach / peak, "algorithmic_flops_per_step": flops,
+                             "hbm_qmin_gbs": achieved})
+            for k in ("ceiling_gbs", "frac_of_ceiling", "ceiling"):
+                roofline.pop(k, None)
     if pro_only:
         # the prologue's two products: bound by MFMA or by HBM, whichever its
         # flops and bytes make the longer at peak
@@ -870,7 +893,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if (pro_only and w.dtype == "bf16") else "f32",
+        "dtype": "bf16" if (mod and w.dtype == "bf16") else "f32",
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "B": w.B, "C": w.C, "H": w.H, "W": w.W,
                    "dirs": w.dirs, "group_rows": w.group_rows, "storage": w.dtype,
@@ -888,9 +911,15 @@ def main() -> int:
         "step_stats": step_stats,
     }
     if not args.no_cpu_baseline and mod:
-        cb = cpu_baseline_module(sets[0], w, args.cpu_seconds, pro_only)
-        cb["parity"] = {"checked": False,
-                        "why": "the CPU sample is a band of rows, not whole planes"}
+        cb, ref = cpu_baseline_module(sets[0], w, args.cpu_seconds, pro_only)
+        if ref is not None:
+            # outs[0]: set 0's unit output from the last timed step that used it
+            cb["parity"] = parity_of_sample(outs[0][:1].float().reshape(-1, w.H, w.W).cpu().numpy(),
+                                            ref.reshape(-1, w.H, w.W), w.dtype)
+        else:
+            cb["parity"] = {"checked": False,
+                            "why": "the CPU sample is a band of rows, not whole planes"}
+        cb["cpu_model"] = cpu_model()
         result["cpu_baseline"] = cb
     elif not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))

@@ -855,6 +855,17 @@ gspn_status gspn_module_ws(const void* x_in, int64_t Cin, const void* w_reduce,
   gspn::Tracer tr;
   tr.events = g_trace_events;
   tr.pairs = g_trace_pairs;
+  // small bf16 planes: the parameter product runs fused with the scan and
+  // the parameter tensors are never stored (GSPN_FORCE_MODULE=unfused keeps
+  // the two-step path, for comparisons)
+  const char* force = std::getenv("GSPN_FORCE_MODULE");
+  const bool unfused = force && !std::strcmp(force, "unfused");
+  if (!unfused && gspn::fused_unit_fits(pp) && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+    hipError_t e = gspn::launch_prologue_reduce(pp, stream, &tr);
+    if (e == hipSuccess) e = gspn::launch_fused_unit(pp, ws, out, dir_mask, group_rows, stream, &tr);
+    keep_trace(tr);
+    return e == hipSuccess ? GSPN_OK : fail(GSPN_E_HIP, hipGetErrorString(e));
+  }
   s = run_prologue(pp, stream, &tr);
   if (s != GSPN_OK) {
     keep_trace(tr);

@@ -1,0 +1,367 @@
+// The GSPN unit's parameter product fused with the propagation, for small
+// planes (H, W <= 16, bf16): the logits, lambda and u of a group of 16
+// channels go from MFMA accumulators into LDS records and are scanned there,
+// so the five parameter tensors never reach HBM.
+//
+// The unit (aitntnews page, section GSPN架构; CSDN page, section
+// GSPN模块的设计, Fig. 3c) is a shared 1x1 convolution x = W_r X_in + b_r,
+// three 1x1 convolutions producing the logits, lambda and u from x, and the
+// four-direction propagation of x with them. In [B, C, H, W] layout a 1x1
+// convolution of image b is a matrix product over channels with N = H W
+// pixels as columns. The first product runs as before (x is needed in full by
+// every channel group, so it is stored once); this kernel does the second
+// and the propagation. One workgroup owns channels c0 .. c0 + 15 of image b:
+//
+//   1. product: the 80 rows of W_p that produce the group's l0, l1, l2,
+//      lambda and u (rows t C + c0 + i, t = 0..4) times x[b] (C x N). Wave w
+//      owns pixel tiles w, w + 4, w + 8, w + 12 (16 pixels each) for all 80
+//      rows: 5 x 4 MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16), K in
+//      steps of 64 through LDS (the pixel operand by transposing reads of the
+//      tile as loaded), the next step's operands in registers while the
+//      current one is multiplied. Lane l then holds, for channels
+//      4 (l / 16) + e of the group and pixel 16 tile + l % 16, all five
+//      parameters, so a pixel's record needs no exchange between lanes;
+//   2. records: bias added, each parameter rounded to bf16 (the unit's
+//      parameters are tensors of the storage type, exactly as the unfused
+//      path stores and rereads them), then (w0, w1, w2, lambda x) with the
+//      sigmoid + row normalisation of the three logits; x of the group's
+//      channels is taken from the product's own LDS tile;
+//   3. scans: wave w scans planes 4w .. 4w + 3 (one per 16-lane row,
+//      neighbours by DPP row shifts) in each selected direction, edge lanes
+//      renormalising over their in-range neighbours;
+//   4. merge: out = u (h_T2B + h_B2T + h_L2R + h_R2L) in that order, one
+//      rounding, the group's 16 output planes written as one contiguous run.
+//
+// Line recurrence and output gate: CSDN page, section 方法; tridiagonal
+// row-normalised sigmoid weights, four directions: section
+// 如何设计一个高效的传播层; local groups: section GSPN模块的设计.
+#include "gspn_device.hpp"
+#include "gspn_launch.hpp"
+#include "gspn_mfma.hpp"
+
+namespace gspn {
+
+namespace {
+
+constexpr int kCg = 16;            // channels per workgroup
+constexpr int kIB = 4;             // images per block of the tile order
+constexpr int kMR = 5 * kCg;       // rows of W_p per workgroup
+constexpr int kKT = 64;            // K per step: 128-byte rows
+constexpr int kAP = kKT + 8;       // LDS pitch of the weight tile [m][k] (elements)
+constexpr int kNmax = 256;         // pixels of one image
+constexpr int kRP = 17;            // records per plane row (odd: no bank conflicts
+                                   // on horizontal scans)
+constexpr int kArun = kMR * kKT / 8;   // 16-byte runs of the weight tile
+constexpr int kStageBytes = kMR * kAP * 2 + kKT * kNmax * 2;
+constexpr int kRecBytes = kCg * (16 * kRP + 1) * 16;
+constexpr int kOutOff = kRecBytes;                  // output staging [16][N] bf16
+constexpr int kZeroOff = kRecBytes + kCg * kNmax * 2;
+constexpr int kLdsBytes = kZeroOff + 16;
+static_assert(kStageBytes <= kRecBytes, "the product's tiles live in the record area");
+
+struct FusedArgs {
+  const bf16_t* wp;    // [5C][C]
+  const bf16_t* bp;    // [5C] or null
+  const bf16_t* x;     // [B][C][N], as the first product stored it
+  bf16_t* out;         // [B][C][N]
+  int B, C, H, W, N, G;
+  unsigned mask;
+  int tiles, per;      // (image, channel group) tiles; tiles per XCD
+};
+
+// The pixel tile sits in LDS as [k][256] with its 32-byte blocks (16
+// pixels) swizzled per row: block b of row k is stored at block b ^ bswz(k).
+// The transposing reads of an MFMA operand take 4 consecutive rows from each
+// 16-lane group (rows k0 + 8 g + i, i < 4, for the four groups g), and the
+// swizzle puts rows i and 8 + i in different banks, where an unswizzled
+// 512-byte row would put all of them in the same ones.
+__device__ __forceinline__ int bswz(int k) { return (k & 3) | ((k >> 1) & 4); }
+__device__ __forceinline__ int bpos(int k, int n) {
+  return k * kNmax + ((((n >> 4) ^ bswz(k)) << 4) | (n & 15));
+}
+
+__device__ __forceinline__ float round_bf16(float v) {
+  return __uint_as_float(f32_to_bf16_bits(v) << 16);
+}
+
+__global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(smem + kMR * kAP * 2);
+  float4* recs = reinterpret_cast<float4*>(smem);
+  float* recf = reinterpret_cast<float*>(smem);
+  uint16_t* ost = reinterpret_cast<uint16_t*>(smem + kOutOff);
+
+  // Workgroups are dealt to the 8 XCDs in turn; tile t runs on XCD t / per.
+  // Tiles are ordered by blocks of kIB images, channel group, then image, so
+  // the workgroups one XCD runs at once (about 64) are some 16 channel
+  // groups of 4 images: each weight slice is shared by 4 of them and each
+  // image's x by 16, and the K step they all read meets in that L2.
+  const int tile = static_cast<int>(blockIdx.x % 8) * a.per + static_cast<int>(blockIdx.x / 8);
+  if (tile >= a.tiles) return;
+  const int C = a.C, N = a.N, H = a.H, W = a.W;
+  const int ps = H * kRP + 1;
+  const int ng = C / kCg;
+  const int blk = tile / (kIB * ng);
+  const int ibe = min(kIB, a.B - blk * kIB);
+  const int rem = tile - blk * kIB * ng;
+  const int64_t b = blk * kIB + rem % ibe;
+  const int c0 = (rem / ibe) * kCg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, rq = (lane >> 4) * 4;
+  const bf16_t* X = a.x + b * static_cast<int64_t>(C) * N;
+
+  // ---- 1. the product -------------------------------------------------------
+  f32x4 acc[5][4];
+#pragma unroll
+  for (int t = 0; t < 5; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // 16-byte runs this thread moves per K step, the same for every step:
+  // weight run c = tid + 256 q is row c / 8 of the 80, k offset 8 (c % 8);
+  // pixel run c is k row c / (N / 8), pixels 8 (c % (N / 8)) .. Runs past the
+  // end load a valid run and are not stored.
+  const int rpr = N / 8;
+  int a_off[3], b_goff[8], b_lds[8];
+  bool a_ok[3], b_ok[8];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int c = tid + 256 * q;
+    a_ok[q] = c < kArun;
+    const int m = (a_ok[q] ? c : kArun - 1) >> 3;
+    a_off[q] = ((m >> 4) * C + c0 + (m & 15)) * C + (c & 7) * 8;
+  }
+  const int a_lds = (tid >> 3) * kAP + (tid & 7) * 8;   // + 32 q rows
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int c = tid + 256 * q;
+    b_ok[q] = c < kKT * rpr;
+    const int cc = b_ok[q] ? c : kKT * rpr - 1;
+    const int row = cc / rpr, nn = (cc - row * rpr) * 8;
+    b_goff[q] = row * N + nn;
+    b_lds[q] = bpos(row, nn);
+  }
+  u32x4 pa[3], pb[8];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) pa[q] = *reinterpret_cast<const u32x4*>(a.wp + a_off[q] + k0);
+    const bf16_t* xk = X + static_cast<int64_t>(k0) * N;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pb[q] = *reinterpret_cast<const u32x4*>(xk + b_goff[q]);
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (a_ok[q]) *reinterpret_cast<u32x4*>(As + a_lds + 32 * q * kAP) = pa[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (b_ok[q]) *reinterpret_cast<u32x4*>(Bs + b_lds[q]) = pb[q];
+  };
+  auto multiply = [&]() {
+    // lane l: A[l % 16][8 (l / 16) .. +7] of each M tile; B by transposing reads
+    // (rows k + 4 share k's swizzle: bit 3 of the row is unchanged)
+    const int kq = (lane >> 4) * 8;
+#pragma unroll
+    for (int kh = 0; kh < kKT; kh += 32) {
+      bf16x8 fa[5], fb[4];
+#pragma unroll
+      for (int t = 0; t < 5; ++t)
+        fa[t] = *reinterpret_cast<const bf16x8*>(As + (16 * t + r16) * kAP + kh + kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // lane l: rows kh + kq + (l % 16) / 4 (+ 4), pixels 16 (4 j + w) + 4 (l % 4) ..
+        const int row = kh + kq + (r16 >> 2);
+        const uint16_t* q = Bs + bpos(row, 16 * (4 * j + wave) + 4 * (r16 & 3));
+        const v4i16 lo = lds_read_tr(q), hi = lds_read_tr(q + 4 * kNmax);
+        fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+      }
+#pragma unroll
+      for (int t = 0; t < 5; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb[j], acc[t][j], 0, 0, 0);
+    }
+  };
+
+  // x of the group's channels, for lambda x: rows c0 - kx0 .. of the pixel
+  // tile of K step kx0, taken while it is in LDS
+  const int kx0 = c0 & ~(kKT - 1);
+  uint16_t xv[4][4];
+  // The next step's runs are loaded while the current one is multiplied.
+  // Loads are never conditional and the loop body is straight-line, so the
+  // compiler can count the loads in flight instead of waiting for all of
+  // them at every step (the last step reloads itself). A second register
+  // set, two steps ahead, measured slower.
+  fetch(0);
+  for (int k0 = 0; k0 < C; k0 += kKT) {
+    stash();
+    lds_barrier();
+    fetch(min(k0 + kKT, C - kKT));
+    multiply();
+    if (k0 == kx0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xv[e][j] = Bs[bpos(c0 - kx0 + rq + e, 16 * (4 * j + wave) + r16)];
+    }
+    lds_barrier();
+  }
+
+  // ---- 2. records -------------------------------------------------------------
+  // plane p's records start at p ps: one spare record per plane moves each
+  // plane's LDS banks by four, so the lanes of different planes that read
+  // or write the same pixel together do not collide
+  float bias[5][4];
+#pragma unroll
+  for (int t = 0; t < 5; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      bias[t][e] = a.bp ? to_f32(a.bp[t * C + c0 + rq + e]) : 0.0f;
+  float uu[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 16 * (4 * j + wave) + r16;
+    const int row = n / W, col = n - row * W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float l0 = round_bf16(acc[0][j][e] + bias[0][e]);
+      const float l1 = round_bf16(acc[1][j][e] + bias[1][e]);
+      const float l2 = round_bf16(acc[2][j][e] + bias[2][e]);
+      const float lam = round_bf16(acc[3][j][e] + bias[3][e]);
+      uu[e][j] = round_bf16(acc[4][j][e] + bias[4][e]);
+      if (n < N) {
+        const Weights w = make_weights(l0, l1, l2, 1.0f, 1.0f);
+        const float xx = __uint_as_float(static_cast<uint32_t>(xv[e][j]) << 16);
+        recs[(rq + e) * ps + row * kRP + col] = make_float4(w.w0, w.w1, w.w2, lam * xx);
+      }
+    }
+  }
+  if (tid == 0) recs[kZeroOff / 16] = make_float4(0.f, 0.f, 0.f, 0.f);
+  lds_barrier();
+
+  // ---- 3. scans: wave w owns planes 4w .. 4w + 3 ------------------------------
+  const int pl = 4 * wave + (lane >> 4), o = r16;
+  const int G = a.G;
+  float hist[4][16];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if (!((a.mask >> d) & 1u)) continue;
+    const bool vert = d < 2, fwd = (d == 0 || d == 2);
+    const int n_s = vert ? H : W, n_o = vert ? W : H;
+    const bool active = o < n_o;
+    const float m0 = o > 0 ? 1.f : 0.f, m2 = o < n_o - 1 ? 1.f : 0.f;
+    const bool edge = active && (o == 0 || o == n_o - 1);
+    const int p0 = fwd ? 0 : n_s - 1;
+    int addr = vert ? pl * ps + p0 * kRP + o : pl * ps + o * kRP + p0;
+    int stride = (vert ? kRP : 1) * (fwd ? 1 : -1);
+    if (!active) { addr = kZeroOff / 16; stride = 0; }
+    int next_restart = n_s;
+    if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
+    float h = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < n_s) {
+        float4 rc = recs[addr];
+        addr += stride;
+        if (edge) {
+          const Weights we = edge_weights(rc.x, rc.y, rc.z, m0, m2);
+          rc.x = we.w0; rc.y = we.w1; rc.z = we.w2;
+        }
+        const float hl = from_left<16>(h), hr = from_right<16>(h);
+        const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+        bool restart = (s == 0);
+        if (s == next_restart) { restart = true; next_restart += G; }
+        h = restart ? rc.w : hn;
+        hist[d][s] = h;
+      }
+    }
+  }
+  // park each direction's states in its slot of the records of this wave's
+  // own planes (no other wave reads them)
+  lds_wave_sync();
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if (!((a.mask >> d) & 1u)) continue;
+    const bool vert = d < 2, fwd = (d == 0 || d == 2);
+    const int n_s = vert ? H : W, n_o = vert ? W : H;
+    if (o >= n_o) continue;
+    const int p0 = fwd ? 0 : n_s - 1;
+    int addr = vert ? pl * ps + p0 * kRP + o : pl * ps + o * kRP + p0;
+    const int stride = (vert ? kRP : 1) * (fwd ? 1 : -1);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < n_s) {
+        recf[4 * addr + d] = hist[d][s];
+        addr += stride;
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- 4. merge and store -------------------------------------------------------
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 16 * (4 * j + wave) + r16;
+    if (n >= N) continue;
+    const int row = n / W, col = n - row * W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 st = recs[(rq + e) * ps + row * kRP + col];
+      float sum = 0.0f;
+      if (a.mask & 1u) sum += st.x;
+      if (a.mask & 2u) sum += st.y;
+      if (a.mask & 4u) sum += st.z;
+      if (a.mask & 8u) sum += st.w;
+      ost[(rq + e) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(uu[e][j] * sum));
+    }
+  }
+  lds_barrier();
+  // the group's planes are one contiguous run of 16 N elements
+  uint4* dst = reinterpret_cast<uint4*>(a.out + (b * C + c0) * static_cast<int64_t>(N));
+  const uint4* src = reinterpret_cast<const uint4*>(ost);
+  for (int c = tid; c < 2 * N; c += 256) dst[c] = src[c];
+}
+
+bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+
+bool fused_unit_fits(const PrologueProblem& pr) {
+  // (weight offsets are 32-bit: 5 C^2 < 2^31)
+  return pr.dtype == GSPN_BF16 && pr.H >= 1 && pr.W >= 1 && pr.H <= 16 && pr.W <= 16 &&
+         (pr.H * pr.W) % 8 == 0 && pr.C % kKT == 0 && pr.C >= kKT && pr.C <= 20000 &&
+         al16(pr.w_p);
+}
+
+hipError_t launch_fused_unit(const PrologueProblem& pr, const void* x, void* out, uint32_t mask,
+                             int64_t G, hipStream_t stream, Tracer* tr) {
+  FusedArgs a;
+  a.wp = static_cast<const bf16_t*>(pr.w_p);
+  a.bp = static_cast<const bf16_t*>(pr.b_p);
+  a.x = static_cast<const bf16_t*>(x);
+  a.out = static_cast<bf16_t*>(out);
+  a.B = static_cast<int>(pr.B);
+  a.C = static_cast<int>(pr.C);
+  a.H = static_cast<int>(pr.H);
+  a.W = static_cast<int>(pr.W);
+  a.N = static_cast<int>(pr.H * pr.W);
+  a.G = static_cast<int>(G >= pr.H && G >= pr.W ? 0 : G);
+  a.mask = mask;
+  const int64_t tiles = pr.B * (pr.C / kCg);
+  a.tiles = static_cast<int>(tiles);
+  a.per = static_cast<int>((tiles + 7) / 8);
+  // two K steps in flight when the steps pair up
+  auto kern = fused_unit;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  tr->before(stream, "fused_unit", pr.B * pr.C);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.per * 8)), dim3(256), kLdsBytes, stream,
+                     a);
+  tr->after(stream);
+  return hipGetLastError();
+}
+
+}  // namespace gspn

@@ -132,6 +132,15 @@ struct PrologueProblem {
   gspn_dtype dtype;
 };
 hipError_t launch_prologue(const PrologueProblem& pr, hipStream_t stream, Tracer* tr);
+// the first product alone (x = W_r X_in + b_r into pr.x_out)
+hipError_t launch_prologue_reduce(const PrologueProblem& pr, hipStream_t stream, Tracer* tr);
+
+// the parameter product fused with the propagation for small bf16 planes
+// (gspn_fused.hip): reads x (as launch_prologue_reduce stored it), W_p and
+// b_p of pr, writes out; the parameter tensors are never stored
+bool fused_unit_fits(const PrologueProblem& pr);
+hipError_t launch_fused_unit(const PrologueProblem& pr, const void* x, void* out, uint32_t mask,
+                             int64_t G, hipStream_t stream, Tracer* tr);
 
 // backward pass, plane-resident path for H, W <= 64 (gspn_bwd_plane.hip)
 size_t bplane_lds_bytes(int64_t H, int64_t W);

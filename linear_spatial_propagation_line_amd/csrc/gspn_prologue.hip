@@ -30,6 +30,7 @@
 // find it in L2.
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
+#include "gspn_mfma.hpp"
 
 namespace gspn {
 
@@ -38,27 +39,8 @@ constexpr int kMT = 128, kNT = 128;
 constexpr size_t kXsMaxLds = 150 * 1024;   // pixel-stationary variant up to this LDS size
 constexpr int kOP = kNT + 8;     // LDS pitch of the staged output tile
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ float g_ld(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float g_ld(const bf16_t* p, int64_t i) { return to_f32(p[i]); }
-
-// Barriers that order LDS only. A plain __syncthreads() also fences global
-// memory, which on this GPU waits for every outstanding global load and
-// store: the prefetched weights and the output runs just written would be
-// drained at each barrier. These wait for LDS traffic alone.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-// the same within one wavefront (its lanes read what its other lanes wrote)
-__device__ __forceinline__ void lds_wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
 
 // output tensor t of the kernel arguments, picked without indexing them (an
 // indexed kernel argument is a memory load the store would have to wait for)
@@ -107,23 +89,6 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// 16 bytes as a plain vector of four words (arrays of these stay in
-// registers; arrays of the uint4 struct copied whole may not)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// gfx950 transposing LDS read of 16-bit data: within each group of 16 lanes
-// the lanes' 8-byte chunks, taken in lane order, form a run of 64 elements,
-// and lane j receives elements j, j + 16, j + 32, j + 48 of it. When lane c
-// of a group points at row r0 + c / 4, columns n0 + 4 (c % 4) of a [k][n]
-// tile, lane j therefore gets rows r0 .. r0 + 3 of column n0 + j: four
-// consecutive k of one n, half of an MFMA B operand (checked on the GPU with
-// a one-wavefront probe).
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-}
 __device__ __forceinline__ u32x4 vec4(const uint4& v) { return u32x4{v.x, v.y, v.z, v.w}; }
 __device__ __forceinline__ uint32_t half16(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
@@ -657,6 +622,22 @@ hipError_t launch_prologue_dt(const PrologueProblem& pr, hipStream_t stream, Tra
 hipError_t launch_prologue(const PrologueProblem& pr, hipStream_t stream, Tracer* tr) {
   if (pr.dtype == GSPN_F32) return launch_prologue_dt<float>(pr, stream, tr);
   return launch_prologue_dt<bf16_t>(pr, stream, tr);
+}
+
+namespace {
+template <typename T>
+hipError_t launch_reduce_dt(const PrologueProblem& pr, hipStream_t stream, Tracer* tr) {
+  T* x = static_cast<T*>(pr.x_out);
+  return gemm<T>(static_cast<const T*>(pr.w_r), static_cast<const T*>(pr.b_r),
+                 static_cast<const T*>(pr.x_in), &x, 1, pr.B, static_cast<int>(pr.C),
+                 static_cast<int>(pr.Cin), static_cast<int>(pr.H * pr.W), "prologue_reduce",
+                 stream, tr);
+}
+}  // namespace
+
+hipError_t launch_prologue_reduce(const PrologueProblem& pr, hipStream_t stream, Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return launch_reduce_dt<float>(pr, stream, tr);
+  return launch_reduce_dt<bf16_t>(pr, stream, tr);
 }
 
 }  // namespace gspn

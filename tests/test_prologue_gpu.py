@@ -139,3 +139,79 @@ def test_t2i_module_full_size_sampled():
     for c in (0, 211):
         arrs = [to_oracle_array(pro[k][:, c:c + 1]) for k in ("x", "l0", "l1", "l2", "lam", "u")]
         assert_parity(out[:, c:c + 1], oracle.propagate(*arrs, dirs=w.dirs), f"t2i module plane {c}")
+
+
+# (B, Cin, C, H, W, G) that take the fused path (bf16, H, W <= 16, H W a
+# multiple of 8, C a multiple of 64): full and partial planes, one-pixel-wide
+# lines, local groups, several channel groups and K steps
+FUSED_CASES = [(2, 24, 64, 16, 16, 0), (1, 40, 128, 8, 8, 0), (3, 64, 64, 16, 12, 3),
+               (1, 20, 64, 4, 2, 0), (1, 64, 192, 16, 1, 0), (2, 96, 64, 12, 16, 5),
+               (1, 7, 256, 2, 4, 0)]
+
+
+def _module(d, dirs, G, bias=True, force=None, monkeypatch=None):
+    if force:
+        monkeypatch.setenv("GSPN_FORCE_MODULE", force)
+    else:
+        monkeypatch.delenv("GSPN_FORCE_MODULE", raising=False)
+    out = g.module(d["x_in"], d["w_r"], d["b_r"] if bias else None, d["w_p"],
+                   d["b_p"] if bias else None, dirs=dirs, group_rows=G)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_unit(case, monkeypatch):
+    """The fused parameter product + scan against the oracle's prologue,
+    rounding and propagation, and against the unfused two-step path: the
+    same products in the same order, so the same bits."""
+    B, Cin, C, H, W, G = case
+    print(f"[fused] case={case}", flush=True)
+    inp = make_prologue_inputs(None, seed=31 + C + H, B=B, Cin=Cin, C=C, H=H, W=W, dtype="bf16")
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    for dirs in (15, g.T2B | g.R2L, g.L2R):
+        for bias in (True, False):
+            fused = _module(d, dirs, G, bias, monkeypatch=monkeypatch)
+            plain = _module(d, dirs, G, bias, force="unfused", monkeypatch=monkeypatch)
+            sub = dict(inp)
+            if not bias:
+                sub = {k: v for k, v in inp.items()}
+                sub["b_r"] = torch.zeros_like(inp["b_r"])
+                sub["b_p"] = torch.zeros_like(inp["b_p"])
+            assert_parity(fused, oracle_module(sub, dirs, G, torch.bfloat16),
+                          f"fused {case} dirs={dirs} bias={bias}")
+            assert torch.equal(fused, plain), f"fused and unfused paths differ: {case} {dirs}"
+
+
+def test_fused_unit_takes_the_fused_path(monkeypatch):
+    """The launches of a fused call: the first product, then the fused kernel
+    (no parameter product, no separate propagation)."""
+    import bench
+    monkeypatch.delenv("GSPN_FORCE_MODULE", raising=False)
+    inp = make_prologue_inputs(None, seed=3, B=1, Cin=16, C=64, H=16, W=16, dtype="bf16")
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    L = g.lib()
+    hip = bench.Hip()
+    evs = hip.events(16)
+    L.gspn_trace_events(evs, 8)
+    g.module(d["x_in"], d["w_r"], d["b_r"], d["w_p"], d["b_p"])
+    torch.cuda.synchronize()
+    L.gspn_trace_events(None, 0)
+    names = [L.gspn_trace_kernel(i, None).decode() for i in range(L.gspn_trace_count())]
+    hip.destroy(evs)
+    assert names == ["prologue_reduce", "fused_unit"], names
+
+
+def test_dit_unit_full_size_fused(monkeypatch):
+    """The DiT-XL/2 unit (32 x 1152 x 16 x 16, bf16) at full size through the
+    fused path, as the benchmark runs it: image 0 against the oracle, the
+    whole output against the unfused path bit for bit."""
+    monkeypatch.delenv("GSPN_FORCE_MODULE", raising=False)
+    w = WORKLOADS["dit_16x16_mod"]
+    d = make_prologue_inputs(w, device=DEV)
+    fused = _module(d, w.dirs, 0, monkeypatch=monkeypatch)
+    plain = _module(d, w.dirs, 0, force="unfused", monkeypatch=monkeypatch)
+    assert torch.equal(fused, plain)
+    sub = {k: v.cpu() for k, v in d.items()}
+    sub["x_in"] = sub["x_in"][:1]
+    assert_parity(fused[:1], oracle_module(sub, w.dirs, 0, torch.bfloat16), "DiT unit image 0")
