@@ -58,6 +58,8 @@ PLAN_SOURCES = {
     "band": ("gspn_band.hip", "gspn_device.hpp"),
     "tpipe": ("gspn_tpipe.hip", "gspn_device.hpp"),
     "stream": ("gspn_stream.hip", "gspn_device.hpp"),
+    "tpipe_t": ("gspn_tpipe.hip", "gspn_dirs.hip", "gspn_device.hpp"),
+    "large": ("gspn_dirs.hip", "gspn_stream.hip", "gspn_device.hpp"),
     "bwd_plane16": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
@@ -184,6 +186,8 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     Module prologue (counted per pixel of B images: `planes` is B here):
       prologue_reduce  x_in read (Cin s), x written (C s)
       prologue_params  x read (C s), five parameter tensors written (5 C s)
+      tp_t_in / tp_t_out  the pipeline on transposed copies: one tensor read
+          and written transposed (2 s), counted per plane and tensor
       fused_unit (small planes: the parameter product fused with the scan,
           counted per pixel of the B * C planes): x read (s), out written (s);
           the parameters never leave the chip
@@ -226,6 +230,8 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "prologue_reduce": (w.prologue_cin + w.C) * s,
         "prologue_params": 6 * w.C * s,
         "fused_unit": 2 * s,
+        "tp_t_in": 2 * s,
+        "tp_t_out": 2 * s,
     }[kernel]
     return per * px
 

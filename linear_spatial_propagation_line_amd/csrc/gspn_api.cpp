@@ -2,6 +2,7 @@
 // argument is known to be good), plan choice, workspace handling and launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -9,6 +10,7 @@
 #include <string>
 
 #include "gspn.h"
+#include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 
 namespace {
@@ -26,6 +28,7 @@ gspn_status fail(gspn_status s, const std::string& detail) {
 }
 
 size_t elem_size(gspn_dtype dt) { return dt == GSPN_F32 ? 4 : 2; }
+size_t al256_(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Scratch memory of gspn_propagate_noalloc: one statically sized array per
 // device, held from the library's load until the process ends. Host code never
@@ -39,7 +42,19 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream, kDirs };
+enum class Plan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kTpipeT, kLarge, kStream, kDirs };
+
+// Planes at least this large that no pipeline takes go through transposed
+// copies (kLarge) rather than the streaming path, whose horizontal passes
+// read with a stride.
+constexpr int64_t kLargePlane = 256 * 256;
+
+// workspace of the transposed pipeline: the six inputs and out transposed,
+// then the pipeline's own workspace for the transposed shape
+size_t tpipe_t_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt) {
+  const size_t t = al256_(static_cast<size_t>(planes * H * W) * (dt == GSPN_F32 ? 4 : 2));
+  return 7 * t + gspn::tpipe_workspace_bytes(planes, W, H, dt);
+}
 
 struct Checked {
   gspn_status status;
@@ -88,15 +103,31 @@ Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
   const bool f_band = force && !std::strcmp(force, "band");
   const bool f_tpipe = force && !std::strcmp(force, "tpipe");
   const bool f_stream = force && !std::strcmp(force, "stream");
-  const bool any = !f_plane && !f_band && !f_tpipe && !f_stream;
+  const bool f_tpipe_t = force && !std::strcmp(force, "tpipe_t");
+  const bool f_large = force && !std::strcmp(force, "large");
+  const bool any = !f_plane && !f_band && !f_tpipe && !f_stream && !f_tpipe_t && !f_large;
   const bool stream_ok = H <= gspn::stream_max_orth() && W <= gspn::stream_max_orth();
+  const gspn_dtype dt = static_cast<gspn_dtype>(dtype);
   if ((any || f_plane) && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? Plan::kPlane16 : Plan::kPlane64;
   } else if ((any || f_band) && gspn::band_fits(H, W, G)) {
     r.plan = Plan::kBand;
   } else if ((any || f_tpipe) && gspn::tpipe_fits(H, W)) {
     r.plan = Plan::kTpipe;
-    r.ws_bytes = gspn::tpipe_workspace_bytes(planes, H, W, static_cast<gspn_dtype>(dtype));
+    r.ws_bytes = gspn::tpipe_workspace_bytes(planes, H, W, dt);
+  } else if ((any || f_tpipe_t) && gspn::tpipe_fits(W, H)) {
+    // the transposed plane fits the pipeline: it runs on transposed copies
+    r.plan = Plan::kTpipeT;
+    r.ws_bytes = tpipe_t_workspace_bytes(planes, H, W, dt);
+  } else if ((any || f_large) && !gspn::plane_fits(H, W) && H <= gspn::dirs_max_orth() &&
+             W <= gspn::dirs_max_orth() && (f_large || H * W >= kLargePlane)) {
+    // horizontal directions over transposed copies; the streaming path's
+    // fp32 accumulator (taken instead for channel-shared logits) fits in
+    // the same workspace
+    r.plan = Plan::kLarge;
+    r.ws_bytes = gspn::dirs_workspace_bytes(planes, H, W, mask, dt);
+    const int nd = __builtin_popcount(mask);
+    if (nd > 1) r.ws_bytes = std::max(r.ws_bytes, static_cast<size_t>(planes * H * W) * sizeof(float));
   } else if (stream_ok && (any || f_stream || !gspn::plane_fits(H, W))) {
     r.plan = Plan::kStream;
     const int nd = __builtin_popcount(mask);
@@ -172,6 +203,58 @@ gspn_status check_all(const void* x, const void* const w_logits[3], const void* 
   return GSPN_OK;
 }
 
+// The pipeline on the transposed planes. Transposing a plane swaps the
+// axes: top->bottom on the transpose is left->right on the plane (the
+// neighbour at orthogonal offset k - 1 keeps its logit), bottom->top is
+// right->left, and the reverse; local groups are the same blocks on both
+// axes. So the six inputs are transposed, the pipeline runs with the
+// direction mask swapped between the axes, and its output is transposed
+// back.
+template <typename T>
+hipError_t run_tpipe_t_dt(const gspn::Problem& pr, void* ws, hipStream_t stream,
+                          gspn::Tracer* tr) {
+  const int64_t planes = pr.B * pr.C, lplanes = pr.B * pr.Cl;
+  const int H = static_cast<int>(pr.H), W = static_cast<int>(pr.W);
+  const size_t t = al256_(static_cast<size_t>(planes * H * W) * sizeof(T));
+  char* w = static_cast<char*>(ws);
+  T* xt = reinterpret_cast<T*>(w);
+  T* lamt = reinterpret_cast<T*>(w + t);
+  T* ut = reinterpret_cast<T*>(w + 2 * t);
+  T* lt[3] = {reinterpret_cast<T*>(w + 3 * t), reinterpret_cast<T*>(w + 4 * t),
+              reinterpret_cast<T*>(w + 5 * t)};
+  T* outt = reinterpret_cast<T*>(w + 6 * t);
+  const T* s1[3] = {static_cast<const T*>(pr.x), static_cast<const T*>(pr.lam),
+                    static_cast<const T*>(pr.u)};
+  T* d1[3] = {xt, lamt, ut};
+  hipError_t e = gspn::transpose_planes<T>(s1, d1, 3, planes, H, W, "tp_t_in", stream, tr);
+  if (e != hipSuccess) return e;
+  const T* s2[3] = {static_cast<const T*>(pr.l[0]), static_cast<const T*>(pr.l[1]),
+                    static_cast<const T*>(pr.l[2])};
+  if ((e = gspn::transpose_planes<T>(s2, lt, 3, lplanes, H, W, "tp_t_in", stream, tr)) !=
+      hipSuccess)
+    return e;
+  gspn::Problem pt = pr;
+  pt.x = xt;
+  pt.lam = lamt;
+  pt.u = ut;
+  for (int k = 0; k < 3; ++k) pt.l[k] = lt[k];
+  pt.out = outt;
+  pt.H = pr.W;
+  pt.W = pr.H;
+  pt.mask = ((pr.mask & 3u) << 2) | ((pr.mask >> 2) & 3u);
+  pt.aligned_vec4 = false;
+  pt.aligned_pair = true;
+  if ((e = gspn::launch_tpipe(pt, w + 7 * t, stream, tr)) != hipSuccess) return e;
+  const T* s3[1] = {outt};
+  T* d3[1] = {static_cast<T*>(pr.out)};
+  return gspn::transpose_planes<T>(s3, d3, 1, planes, W, H, "tp_t_out", stream, tr);
+}
+
+hipError_t run_tpipe_t(const gspn::Problem& pr, void* ws, hipStream_t stream, gspn::Tracer* tr) {
+  if (pr.dtype == GSPN_F32) return run_tpipe_t_dt<float>(pr, ws, stream, tr);
+  return run_tpipe_t_dt<gspn::bf16_t>(pr, ws, stream, tr);
+}
+
 // `cont`: a tracer that already holds earlier launches of the same call
 gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream,
                 gspn::Tracer* cont = nullptr) {
@@ -196,6 +279,15 @@ gspn_status run(const gspn::Problem& pr, Plan plan, void* ws, hipStream_t stream
       // accumulator fits in the front of the pipeline's larger workspace
       e = pr.aligned_pair ? gspn::launch_tpipe(pr, ws, stream, &tr)
                           : gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
+      break;
+    case Plan::kTpipeT:
+      e = pr.aligned_pair ? run_tpipe_t(pr, ws, stream, &tr)
+                          : gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
+      break;
+    case Plan::kLarge:
+      // the transposed-copy passes take one set of logits per plane
+      e = pr.Cl == pr.C ? gspn::launch_dirs(pr, ws, stream, &tr)
+                        : gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
       break;
     case Plan::kStream:
       e = gspn::launch_stream(pr, static_cast<float*>(ws), stream, &tr);
@@ -223,6 +315,8 @@ const char* plan_str(Plan p) {
     case Plan::kPlane64: return "plane64";
     case Plan::kBand: return "band";
     case Plan::kTpipe: return "tpipe";
+    case Plan::kTpipeT: return "tpipe_t";
+    case Plan::kLarge: return "large";
     case Plan::kStream: return "stream";
     case Plan::kDirs: return "dirs";
     default: return "invalid";

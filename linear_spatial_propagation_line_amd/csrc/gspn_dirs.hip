@@ -673,8 +673,12 @@ hipError_t launch_dirs_dt(const Problem& pr, void* ws, hipStream_t stream, Trace
       src[n] = xs;
       dst[n++] = reinterpret_cast<T*>(wsb + off);
       off += al(P * sizeof(T));
+      // with dir_stride 0 both horizontal directions read the same five
+      // tensors: they are transposed once
+      const bool shared_h = pr.dir_stride == 0;
       for (int d = 2; d < 4; ++d) {
         if (!((pr.mask >> d) & 1u)) continue;
+        if (shared_h && n > 1) break;
         const void* bases[5] = {pr.lam, pr.l[0], pr.l[1], pr.l[2], pr.u};
         for (int k = 0; k < 5; ++k) {
           src[n] = param(bases[k], d);
@@ -699,7 +703,7 @@ hipError_t launch_dirs_dt(const Problem& pr, void* ws, hipStream_t stream, Trace
         ag.l1 = dst[t + 2];
         ag.l2 = dst[t + 3];
         ag.u = dst[t + 4];
-        t += 5;
+        if (!shared_h) t += 5;
         ag.merge = pr.merge ? pr.merge + d * pr.C : nullptr;
         ag.acc = acc_t;
         ag.H = W;

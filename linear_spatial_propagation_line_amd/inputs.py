@@ -27,6 +27,9 @@ weights):
   dit_16x16_mod      x, the logits, lambda and u from an input of Cin = C
   t2i_2048x1024_mod  channels (aitntnews page, section GSPN架构), then the
                      propagation
+  t2i_1024x2048      the text-to-image latent in portrait orientation and
+  t2i_2047x1023      with odd sides (the pages' model runs at arbitrary
+                     resolution: aitntnews page, section 文本到图像生成)
 
 Draw order is x, lambda, u, l0, l1, l2, each drawn in float32 from one
 generator seeded with 1000 + k (k = 1..8 in the order above) and then cast
@@ -123,6 +126,10 @@ WORKLOADS = {
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, prologue_cin=1152),
         Workload("t2i_2048x1024_mod", 11, 1, 320, 2048, 1024, BF16, 15, 0,
                  NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL, prologue_cin=320),
+        Workload("t2i_1024x2048", 12, 1, 320, 1024, 2048, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
+        Workload("t2i_2047x1023", 13, 1, 320, 2047, 1023, BF16, 15, 0,
+                 NORMAL1, NORMAL1, SIG_NORMAL, SIG_NORMAL),
     ]
 }
 

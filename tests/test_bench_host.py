@@ -13,7 +13,7 @@ KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
            "dir_plane", "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",
            "bt_vA", "bt_hA", "bt_hB", "bt_vB", "bwd_dirs_zero", "bwd_dirs_store_dx", "bwd_dirs_tr",
-           "bwd_dirs_tr_acc", "bwd_dirs_merge", "fused_unit"]
+           "bwd_dirs_tr_acc", "bwd_dirs_merge", "fused_unit", "tp_t_in", "tp_t_out"]
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))

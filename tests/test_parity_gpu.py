@@ -44,10 +44,32 @@ def test_t2i_full_size_sampled_planes():
                       dirs=w.dirs, group_rows=w.group_rows)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    for c in (0, 137, 319):
+    # the two plane groups of the pipeline (two streams) meet at 159 / 160
+    for c in (0, 137, 159, 160, 319):
         inp = {k: v[:, c:c + 1].cpu() for k, v in d.items()}
         err = assert_parity(out[:, c:c + 1], oracle_y(inp, w.dirs, 0), f"t2i plane {c}")
         print(f"[parity] t2i plane {c} scaled error {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("shape,plan", [((1, 320, 1024, 2048), "tpipe_t"),
+                                        ((1, 320, 2047, 1023), "large")],
+                         ids=["portrait_1024x2048", "odd_2047x1023"])
+def test_large_planes_off_the_pipeline_full_size(shape, plan):
+    """Latents of the text-to-image size in other orientations and sizes
+    (the pages' model runs at arbitrary resolution): portrait planes take the
+    pipeline on transposed copies, odd sides the transposed-copy passes.
+    Sampled planes at full size, both plane groups."""
+    B, C, H, W = shape
+    assert g.plan_name(B, C, H, W, 15, 0, 1) == plan
+    print(f"[parity] {shape} plan={plan}, generating on device", flush=True)
+    d = make_inputs(WORKLOADS["t2i_2048x1024"], device=DEV, B=B, C=C, H=H, W=W)
+    out = g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], dirs=15)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for c in (0, 159, 160, 319):
+        inp = {k: v[:, c:c + 1].cpu() for k, v in d.items()}
+        err = assert_parity(out[:, c:c + 1], oracle_y(inp, 15, 0), f"{shape} plane {c}")
+        print(f"[parity] {shape} plane {c} scaled error {err:.3e}", flush=True)
 
 
 SHAPES = [
@@ -186,6 +208,46 @@ def test_forced_plan(force_plan, plan, shape, dtype):
         for G in ((0, 3, 8) if mask == 15 else (0,)):
             out = run(inp, mask, G)
             assert_parity(out, oracle_y(inp, mask, G), f"{plan} {shape} mask={mask} G={G}")
+
+
+# the pipeline on transposed copies: every shape whose transpose the pipeline
+# takes (W <= 2048, H <= 1024, both even)
+TPIPE_T_SHAPES = [(1, 2, 2, 2), (1, 2, 8, 8), (2, 3, 16, 32), (1, 2, 66, 40), (1, 1, 130, 96),
+                  (1, 2, 40, 130), (2, 1, 48, 1024), (1, 1, 64, 2048)]
+# the transposed-copy passes: planes above 64 x 64, odd sides included
+LARGE_SHAPES = [(1, 2, 66, 40), (1, 1, 130, 96), (1, 2, 40, 130), (1, 3, 65, 67),
+                (1, 1, 129, 33), (2, 1, 97, 255), (1, 1, 3, 300)]
+
+
+@pytest.mark.parametrize("plan,shape", [("tpipe_t", s) for s in TPIPE_T_SHAPES] +
+                         [("large", s) for s in LARGE_SHAPES],
+                         ids=lambda v: v if isinstance(v, str) else "x".join(map(str, v)))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_forced_large_plane_plans(force_plan, plan, shape, dtype):
+    """The plans for large planes the pipeline does not take, forced on small
+    and odd planes: every direction-subset family, global and local."""
+    force_plan(plan)
+    B, C, H, W = shape
+    assert g.plan_name(B, C, H, W, 15, 0, 0 if dtype == torch.float32 else 1) == plan
+    w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=(H * 37 + W) % 997, B=B, C=C, H=H, W=W)
+    for mask in (15, 1, 2, 3, 4, 8, 12, 5, 10):
+        for G in ((0, 3, 8) if mask == 15 else (0,)):
+            out = run(inp, mask, G)
+            assert_parity(out, oracle_y(inp, mask, G), f"{plan} {shape} mask={mask} G={G}")
+
+
+@pytest.mark.parametrize("plan", ["tpipe_t", "large"])
+def test_large_plane_plans_shared_logits(force_plan, plan):
+    """Logits shared by groups of channels on the large-plane plans (the
+    transposed-copy passes hand them to the streaming path)."""
+    force_plan(plan)
+    B, C, H, W = 2, 4, 66, 130
+    inp = make_inputs("dit_16x16", seed=77, B=B, C=C, H=H, W=W)
+    for k in ("l0", "l1", "l2"):
+        inp[k] = inp[k][:, :2].contiguous()    # two logit channels shared by pairs
+    out = run(inp, 15, 0)
+    assert_parity(out, oracle_y(inp, 15, 0), f"{plan} shared logits")
 
 
 BAND_SHAPES = [(1, 2, 72, 40), (2, 1, 128, 128), (1, 1, 100, 70), (1, 2, 66, 130),
