@@ -96,7 +96,7 @@ Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
     r.status = fail(GSPN_E_GROUP, "group_rows must be >= 0");
     return r;
   }
-  // GSPN_FORCE_PLAN=plane|band|tpipe|stream picks a path for testing when
+  // GSPN_FORCE_PLAN=plane|band|tpipe|tpipe_t|large|stream picks a path for testing when
   // the shape allows it; otherwise the first path that fits, in that order.
   const char* force = std::getenv("GSPN_FORCE_PLAN");
   const bool f_plane = force && !std::strcmp(force, "plane");
