@@ -55,8 +55,12 @@ __device__ __forceinline__ void st1(bf16_t* p, int64_t i, float v) {
   p[i].bits = static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
 
-template <typename T, int SEG, int VEC>
-__global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
+// HS, WS > 0: the plane's height and width fixed at compile time (common
+// shapes), so index arithmetic folds to constants and the scans unroll to
+// exactly their length; 0: taken from the arguments. LOCAL: local groups
+// (G > 0); without them a scan restarts only at its first step.
+template <typename T, int SEG, int VEC, int HS = 0, int WS = 0, bool LOCAL = true>
+__global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs<T> a) {
   constexpr int PPB = 64 / SEG;
   // pixels per thread handled in 4-wide vectors: up to 4096 (SEG 64) or 1024
   // (SEG 16) pixels per plane group over 256 threads
@@ -65,7 +69,21 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
   extern __shared__ float4 smem[];
   float* smem_f = reinterpret_cast<float*>(smem);
 
-  const int H = a.H, W = a.W, pitch = a.pitch;
+  constexpr bool FIX = HS > 0;
+  const int H = FIX ? HS : a.H, W = FIX ? WS : a.W, pitch = FIX ? (WS | 1) : a.pitch;
+  // pixel index -> (plane, row, column) within a plane group
+  auto split = [&](int i, int* pp, int* rr, int* cc) {
+    if constexpr (FIX) {
+      *pp = i / (HS * WS);
+      const int rem = i - *pp * (HS * WS);
+      *rr = rem / WS;
+      *cc = rem - *rr * WS;
+    } else {
+      int rem;
+      *pp = div_small(i, H * W, a.inv_HW, &rem);
+      *rr = div_small(rem, W, a.inv_W, cc);
+    }
+  };
   const int HW = H * W;
   const int rec_sz = PPB * H * pitch;          // records (float4 units)
   const int ev_off = rec_sz;                   // [PPB][2][H]
@@ -114,9 +132,8 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
         uu[it] = ru[it];
         const int i0 = tid * 4 + it * 1024;
         if (i0 < npix) {
-          int rem, c;
-          const int p = div_small(i0, HW, a.inv_HW, &rem);
-          const int r = div_small(rem, W, a.inv_W, &c);
+          int p, r, c;
+          split(i0, &p, &r, &c);
           // W % 4 == 0 on this path, so the four pixels share row r
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -131,9 +148,8 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
       if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x);
     } else {
       for (int i0 = tid; i0 < npix; i0 += 256) {
-        int rem, c;
-        const int p = div_small(i0, HW, a.inv_HW, &rem);
-        const int r = div_small(rem, W, a.inv_W, &c);
+        int p, r, c;
+        split(i0, &p, &r, &c);
         const int64_t gi = gbase + i0;
         const int64_t lgi = gi + logit_shift(plane0 + p, a.C, a.Cl, HW);
         const Weights w = make_weights(ld1(a.l0, lgi), ld1(a.l1, lgi), ld1(a.l2, lgi), 1.0f, 1.0f);
@@ -146,20 +162,24 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
     // ---- 2. edge-lane records ----------------------------------------------
     // vertical scans: lanes c = 0 (e = 0) and c = W-1 (e = 1), masks on c;
     // horizontal scans: lanes r = 0 and r = H-1, masks on r.
-    const int n_ev = np * 2 * H, n_eh = np * 2 * W;
-    for (int k = tid; k < n_ev + n_eh; k += 256) {
-      int p, e, pos, r, c, idx, n_o, o;
-      if (k < n_ev) {
-        p = k / (2 * H); e = (k / H) & 1; pos = k % H;
+    // Slot k of [horizontal][plane][side][SEG positions] (2 * PPB * 2 * SEG =
+    // 256 slots: one per thread, index arithmetic by shifts); positions past
+    // the line's end have nothing to do.
+    {
+      const int k = tid;
+      const int hz = k / (PPB * 2 * SEG), p = (k / (2 * SEG)) % PPB, e = (k / SEG) & 1;
+      const int pos = k % SEG;
+      int r, c, idx, n_o, o;
+      if (!hz) {
         r = pos; c = e ? W - 1 : 0; o = c; n_o = W; idx = ev_off + (p * 2 + e) * H + pos;
       } else {
-        const int k2 = k - n_ev;
-        p = k2 / (2 * W); e = (k2 / W) & 1; pos = k2 % W;
         c = pos; r = e ? H - 1 : 0; o = r; n_o = H; idx = eh_off + (p * 2 + e) * W + pos;
       }
-      const float4 m = smem[(p * H + r) * pitch + c];
-      const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
-      smem[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
+      if (p < np && pos < (hz ? W : H)) {
+        const float4 m = smem[(p * H + r) * pitch + c];
+        const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
+        smem[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
+      }
     }
     __syncthreads();
 
@@ -185,15 +205,17 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
     }
     // steps at which the state restarts: 0, then every G from the first
     // block edge met
-    const int G = a.G;
+    const int G = LOCAL ? a.G : 0;
     int next_restart = n_s;
     if (G > 0) next_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
 
-    float hist[SEG];
+    // longest scan: SEG, or the plane's longer side when it is fixed
+    constexpr int NS = FIX ? (HS > WS ? HS : WS) : SEG;
+    float hist[NS];
     if (on) {
       float h = 0.0f;
 #pragma unroll
-      for (int s = 0; s < SEG; ++s) {
+      for (int s = 0; s < NS; ++s) {
         if (s < n_s) {
           const float4 rc = smem[addr];
           addr += stride;
@@ -213,7 +235,7 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
     if (active) {
       int ya = d * rec_sz + mbase;
 #pragma unroll
-      for (int s = 0; s < SEG; ++s) {
+      for (int s = 0; s < NS; ++s) {
         if (s < n_s) { smem_f[ya] = hist[s]; ya += mstride; }
       }
     }
@@ -224,9 +246,8 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
       for (int it = 0; it < NIT; ++it) {
         const int i0 = tid * 4 + it * 1024;
         if (i0 < npix) {
-          int rem, c;
-          const int pp = div_small(i0, HW, a.inv_HW, &rem);
-          const int r = div_small(rem, W, a.inv_W, &c);
+          int pp, r, c;
+          split(i0, &pp, &r, &c);
           const int li = (pp * H + r) * pitch + c;
           float y[4];
 #pragma unroll
@@ -242,9 +263,8 @@ __global__ __launch_bounds__(256) void plane_kernel(PlaneArgs<T> a) {
       }
     } else {
       for (int i0 = tid; i0 < npix; i0 += 256) {
-        int rem, c;
-        const int pp = div_small(i0, HW, a.inv_HW, &rem);
-        const int r = div_small(rem, W, a.inv_W, &c);
+        int pp, r, c;
+        split(i0, &pp, &r, &c);
         const int li = (pp * H + r) * pitch + c;
         float sum = 0.0f;
 #pragma unroll
@@ -270,6 +290,34 @@ size_t plane_lds_bytes(int64_t H, int64_t W) {
   return recs * sizeof(float4);
 }
 
+// the kernel for a plane shape: compile-time shapes for common sizes (the
+// 16 x 16 DiT latents, the 56 x 56 first classification stage, and the
+// square planes of later stages), the general kernel otherwise
+template <typename T, int SEG, int VEC>
+static void (*pick_plane_kernel(int H, int W, bool local))(PlaneArgs<T>) {
+  if constexpr (VEC == 4) {
+    if (H == W) {
+      if constexpr (SEG == 16) {
+        if (H == 16) return local ? plane_kernel<T, 16, 4, 16, 16, true>
+                                  : plane_kernel<T, 16, 4, 16, 16, false>;
+      } else {
+        switch (H) {
+          case 28: return local ? plane_kernel<T, 64, 4, 28, 28, true>
+                                : plane_kernel<T, 64, 4, 28, 28, false>;
+          case 32: return local ? plane_kernel<T, 64, 4, 32, 32, true>
+                                : plane_kernel<T, 64, 4, 32, 32, false>;
+          case 56: return local ? plane_kernel<T, 64, 4, 56, 56, true>
+                                : plane_kernel<T, 64, 4, 56, 56, false>;
+          case 64: return local ? plane_kernel<T, 64, 4, 64, 64, true>
+                                : plane_kernel<T, 64, 4, 64, 64, false>;
+          default: break;
+        }
+      }
+    }
+  }
+  return local ? plane_kernel<T, SEG, VEC, 0, 0, true> : plane_kernel<T, SEG, VEC, 0, 0, false>;
+}
+
 template <typename T, int SEG, int VEC>
 static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* tr) {
   PlaneArgs<T> a;
@@ -293,7 +341,8 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   a.C = pr.C;
   a.Cl = pr.Cl;
   const size_t lds = plane_lds_bytes(pr.H, pr.W);
-  auto kern = plane_kernel<T, SEG, VEC>;
+  const bool local = a.G > 0;
+  auto kern = pick_plane_kernel<T, SEG, VEC>(a.H, a.W, local);
   hipError_t e;
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -303,14 +352,12 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   // SEG 64 (one large plane per workgroup): persistent grid of as many
   // workgroups as are resident at once, each prefetching its next plane.
   // SEG 16 (four tiny planes per workgroup): one plane group per workgroup.
-  int per_cu = 0, dev = 0, cus = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+  int per_cu = 0;
+  if (SEG == 64 &&
+      (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
                                                         256, lds)) != hipSuccess)
     return e;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-    return e;
-  const int64_t resident = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  const int64_t resident = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * cu_count();
   const int64_t grid = (SEG == 16 || a.ngroups < resident) ? a.ngroups : resident;
   tr->before(stream, SEG == 16 ? "plane_kernel16" : "plane_kernel64", a.nplanes);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), lds, stream, a);
