@@ -215,3 +215,68 @@ def test_dit_unit_full_size_fused(monkeypatch):
     sub = {k: v.cpu() for k, v in d.items()}
     sub["x_in"] = sub["x_in"][:1]
     assert_parity(fused[:1], oracle_module(sub, w.dirs, 0, torch.bfloat16), "DiT unit image 0")
+
+
+def _extreme_unit(B, Cin, C, H, W, seed, base, outside):
+    """A unit whose logits all lie near ``base`` (spread of a few units), and
+    with ``outside``, base + 40 for each neighbour outside the plane (l0 on
+    row 0 and column 0, l2 on row H - 1 and column W - 1): x channels 0 and
+    1 carry those border indicators, the logit rows of W_p weight them by 40."""
+    gen = torch.Generator().manual_seed(seed)
+    uni = lambda *s: 2.0 * torch.rand(*s, generator=gen, dtype=torch.float64) - 1.0
+    x_in = uni(B, Cin, H, W)
+    r = torch.arange(H).view(H, 1)
+    c = torch.arange(W).view(1, W)
+    x_in[:, 0] = ((r == 0) | (c == 0)).double()
+    x_in[:, 1] = ((r == H - 1) | (c == W - 1)).double()
+    w_r = torch.zeros(C, Cin, dtype=torch.float64)
+    for i in range(C):
+        w_r[i, i if i < Cin else 2 + i % (Cin - 2)] = 1.0
+    w_p = torch.zeros(5 * C, C, dtype=torch.float64)
+    b_p = torch.zeros(5 * C, dtype=torch.float64)
+    for t in range(5):
+        w_p[t * C:(t + 1) * C, 2:] = uni(C, C - 2) * (4.0 if t < 3 else 0.5) / (C - 2) ** 0.5
+    b_p[:3 * C] = base
+    b_p[3 * C:4 * C] = 0.5
+    b_p[4 * C:] = 1.0
+    if outside:
+        w_p[0:C, 0] = 40.0
+        w_p[2 * C:3 * C, 1] = 40.0
+    bf = torch.bfloat16
+    return {"x_in": x_in.to(bf), "w_r": w_r.to(bf), "b_r": torch.zeros(C, dtype=bf),
+            "w_p": w_p.to(bf), "b_p": b_p.to(bf)}
+
+
+def oracle_module_clamped(inp, dirs, G):
+    """The unit as the kernels form it: the bf16 logits clamped below at -40."""
+    pro = oracle_prologue(inp)
+    p = {k: oracle.round_to(pro[k], "bf16") for k in g.PARAM_NAMES}
+    for k in ("l0", "l1", "l2"):
+        p[k] = np.maximum(p[k], -40.0)
+    return oracle.propagate(pro["xr"], p["l0"], p["l1"], p["l2"], p["lam"], p["u"], dirs=dirs,
+                            group_rows=G)
+
+
+@pytest.mark.parametrize("recipe", [(-30.0, False), (-30.0, True), (-60.0, False)],
+                         ids=["shallow", "outside", "deep"])
+@pytest.mark.parametrize("case", [(2, 16, 64, 16, 16), (1, 16, 64, 16, 12), (1, 8, 64, 8, 8)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_fused_unit_extreme_logits(case, recipe, monkeypatch):
+    """Logits near -30 give weights far from uniform (they follow the logits'
+    differences); with +10 on the neighbours outside the plane, border pixels
+    hold nearly all their interior weight on a neighbour that edge lanes
+    drop. Near -60 the weights are those of the logits clamped at -40. Against
+    the oracle, and bit for bit against the unfused path."""
+    B, Cin, C, H, W = case
+    base, outside = recipe
+    inp = _extreme_unit(B, Cin, C, H, W, 40 + H + W, base, outside)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    for dirs in (15, g.T2B | g.R2L, g.L2R):
+        fused = _module(d, dirs, 0, monkeypatch=monkeypatch)
+        plain = _module(d, dirs, 0, force="unfused", monkeypatch=monkeypatch)
+        ref = oracle_module_clamped(inp, dirs, 0)
+        if base > -35.0:   # nothing clamped: the exact unit
+            ref_exact = oracle_module(inp, dirs, 0, torch.bfloat16)
+            assert np.array_equal(ref, ref_exact)
+        assert_parity(fused, ref, f"fused extreme {case} dirs={dirs}")
+        assert torch.equal(fused, plain), f"fused and unfused paths differ: {case} {dirs}"
