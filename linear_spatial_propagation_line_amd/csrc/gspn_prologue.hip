@@ -61,6 +61,7 @@ struct GemmArgs {
   const T* X;       // [B][K][N]
   T* out[5];        // output tensor t holds rows t*Mt .. t*Mt+Mt-1: [B][Mt][N]
   int M, K, N, Mt;
+  int64_t B;        // images
   int vec_a, vec_x, vec_o;   // 16-byte runs allowed for A rows, X rows, output rows
 };
 
@@ -122,16 +123,19 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
 
   const int M = a.M, K = a.K, N = a.N;
   const int nmt = (M + kMT - 1) / kMT;
-  // Workgroups are dealt to the 8 XCDs in turn, each with its own L2. Tile
-  // t runs on XCD t / per, so consecutive tiles -- the M tiles that share a
-  // pixel tile -- meet in one L2.
+  // Workgroups are dealt to the 8 XCDs in turn, each with its own L2. Over
+  // all images' tiles, tile t runs on XCD t / per, so consecutive tiles --
+  // the M tiles that share a pixel tile, then the next pixel tiles and
+  // images -- meet in one L2, and every XCD gets a share.
   const int tiles = nmt * ((N + kNT - 1) / kNT);
-  const int per = (tiles + 7) / 8;
-  const int tile = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
-  if (tile >= tiles) return;
+  const int64_t all = static_cast<int64_t>(tiles) * a.B;
+  const int64_t per = (all + 7) / 8;
+  const int64_t t = static_cast<int64_t>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= all) return;
+  const int64_t b = t / tiles;
+  const int tile = static_cast<int>(t - b * tiles);
   const int m0 = (tile % nmt) * kMT;
   const int n0 = (tile / nmt) * kNT;
-  const int64_t b = blockIdx.y;
   const T* X = a.X + b * static_cast<int64_t>(K) * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;   // this wavefront's quarter
@@ -579,6 +583,7 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
   g.K = K;
   g.N = N;
   g.Mt = M / nout;
+  g.B = B;
   constexpr int E = 16 / sizeof(T);
   g.vec_a = K % E == 0 && al16(A);
   g.vec_x = N % E == 0 && al16(X);
@@ -590,8 +595,8 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
   if (K % ks == 0 && K / ks <= kXsMaxSteps && xs_lds_bytes<T>(K, M) <= kXsMaxLds &&
       M % 32 == 0 && g.vec_a && g.vec_x && g.vec_o)
     return launch_xs_k<T>(g, B, name, stream, tr);
-  const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT);
-  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8), static_cast<unsigned>(B));
+  const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT) * B;
+  const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
   // the straight-line variant: whole tiles, an even number of K tiles
   const int kt = 128 / static_cast<int>(sizeof(T));
   const bool full = M % kMT == 0 && N % kNT == 0 && K % (2 * kt) == 0 && g.vec_a && g.vec_x &&
