@@ -241,9 +241,7 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
       for (int s = 0; s < SEG; ++s) {
         if (s < n_s) {
           const float4 rc = smem[addr0 + s * stride];
-          const float hl = from_left<SEG>(h);
-          const float hr = from_right<SEG>(h);
-          const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+          const float hn = line_step<SEG>(h, rc.x, rc.y, rc.z, rc.w);
           h = restarts(s) ? rc.w : hn;
           hist[s] = h;
         }

@@ -206,6 +206,17 @@ template <> __device__ __forceinline__ float from_right<16>(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xf, 0xf, true));
 }
 
+// One step of the line recurrence, lx + w1 h[o] + w2 h[o+1] + w0 h[o-1] (in
+// that order), the neighbours' states taken from the adjacent lanes. The
+// lane's own term comes first: it needs no cross-lane move, so it overlaps
+// the two DPP moves instead of waiting behind them.
+template <int SEG>
+__device__ __forceinline__ float line_step(float h, float w0, float w1, float w2, float lx) {
+  float acc = __builtin_fmaf(w1, h, lx);
+  acc = __builtin_fmaf(from_right<SEG>(h), w2, acc);
+  return __builtin_fmaf(from_left<SEG>(h), w0, acc);
+}
+
 // ---------------------------------------------------------------------------
 // channel-shared logits: plane p = (b, c) of a [B, C] batch reads logit
 // channel c / (C / Cl) of batch entry b. Returns how many elements the

@@ -401,8 +401,7 @@ __global__ __launch_bounds__(256) void dir_plane(DpArgs<T> a) {
     // horizontal one) from its lambda x, logits and u
     auto step = [&](int s, int pos, float lx, float g0, float g1, float g2, float uv) {
       const Weights w = make_weights(g0, g1, g2, m0, m2);
-      const float hl = from_left<64>(h), hr = from_right<64>(h);
-      const float hn = __builtin_fmaf(w.w0, hl, __builtin_fmaf(w.w1, h, __builtin_fmaf(w.w2, hr, lx)));
+      const float hn = line_step<64>(h, w.w0, w.w1, w.w2, lx);
       bool restart = s == 0;
       if (s == next) { restart = true; next += G; }
       h = act ? (restart ? lx : hn) : 0.f;

@@ -269,8 +269,7 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
           const Weights we = edge_weights(rc.x, rc.y, rc.z, m0, m2);
           rc.x = we.w0; rc.y = we.w1; rc.z = we.w2;
         }
-        const float hl = from_left<16>(h), hr = from_right<16>(h);
-        const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+        const float hn = line_step<16>(h, rc.x, rc.y, rc.z, rc.w);
         bool restart = (s == 0);
         if (s == next_restart) { restart = true; next_restart += G; }
         h = restart ? rc.w : hn;

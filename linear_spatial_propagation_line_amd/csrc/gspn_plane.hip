@@ -219,9 +219,7 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
         if (s < n_s) {
           const float4 rc = smem[addr];
           addr += stride;
-          const float hl = from_left<SEG>(h);
-          const float hr = from_right<SEG>(h);
-          const float hn = __builtin_fmaf(rc.x, hl, __builtin_fmaf(rc.y, h, __builtin_fmaf(rc.z, hr, rc.w)));
+          const float hn = line_step<SEG>(h, rc.x, rc.y, rc.z, rc.w);
           bool restart = (s == 0);
           if (s == next_restart) { restart = true; next_restart += G; }
           h = restart ? rc.w : hn;
