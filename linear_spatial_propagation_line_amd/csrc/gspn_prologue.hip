@@ -100,8 +100,11 @@ __device__ __forceinline__ uint32_t half16(const u32x4& v, int e) {
 // 16-byte runs. Then no access needs a bounds check, and the code between
 // memory waits is straight-line, so the compiler can count what is in
 // flight instead of draining the in-order memory counter at every check.
-template <typename T, bool FULL>
+template <typename T, bool FULL, int MT>
 __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
+  static_assert(MT == 128 || MT == 96, "M tile: 4 or 3 MFMA tiles per wavefront");
+  constexpr int MI = MT / 32;                // 16-row MFMA tiles per wavefront
+  constexpr int QA = MT * 8 / 256;           // 16-byte weight runs per thread per K tile
   using R = decltype(raw(T{}));   // uint16_t (bf16 bits) or float
   constexpr bool BF = sizeof(T) == 2;
   constexpr int E = 16 / sizeof(T);          // elements in 16 bytes
@@ -112,17 +115,17 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   // bf16 pitch of 144 elements puts the four rows a 16-lane group reads 8
   // banks apart.
   constexpr int BP = BF ? kNT + 16 : kNT + 4;
-  constexpr int kABytes = kMT * AP * sizeof(R);
+  constexpr int kABytes = MT * AP * sizeof(R);
   constexpr int kBBytes = KT * BP * sizeof(R);
-  constexpr int kOutBytes = (kMT / 2) * kOP * sizeof(R);
+  constexpr int kOutBytes = (MT / 2) * kOP * sizeof(R);
   constexpr int kSmem = kABytes + kBBytes > kOutBytes ? kABytes + kBBytes : kOutBytes;
   __shared__ __align__(16) unsigned char smem[kSmem];
   R* As = reinterpret_cast<R*>(smem);
   R* Bs = reinterpret_cast<R*>(smem + kABytes);
-  R* Os = reinterpret_cast<R*>(smem);        // [kMT / 2][kOP], after the K loop
+  R* Os = reinterpret_cast<R*>(smem);        // [MT / 2][kOP], after the K loop
 
   const int M = a.M, K = a.K, N = a.N;
-  const int nmt = (M + kMT - 1) / kMT;
+  const int nmt = (M + MT - 1) / MT;
   // Workgroups are dealt to the 8 XCDs in turn, each with its own L2. Over
   // all images' tiles, tile t runs on XCD t / per, so consecutive tiles --
   // the M tiles that share a pixel tile, then the next pixel tiles and
@@ -134,15 +137,15 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   if (t >= all) return;
   const int64_t b = t / tiles;
   const int tile = static_cast<int>(t - b * tiles);
-  const int m0 = (tile % nmt) * kMT;
+  const int m0 = (tile % nmt) * MT;
   const int n0 = (tile / nmt) * kNT;
   const T* X = a.X + b * static_cast<int64_t>(K) * N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;   // this wavefront's quarter
+  const int wm = (wave >> 1) * (MT / 2), wn = (wave & 1) * 64;   // this wavefront's quarter
 
-  f32x4 acc[4][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -155,10 +158,10 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
   // two register sets: the straight-line variant for whole tiles keeps the
   // loads of two K tiles in flight (one K tile of products, about 0.2 us, is
   // shorter than a memory latency); the general one uses the first only
-  u32x4 pa[4], px[4], pb[4], py[4];
-  auto fetch_to = [&](int k0, u32x4 (&pa)[4], u32x4 (&px)[4]) {
+  u32x4 pa[QA], px[4], pb[QA], py[4];
+  auto fetch_to = [&](int k0, u32x4 (&pa)[QA], u32x4 (&px)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QA; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
       const int m = m0 + r, k = k0 + kk;
       if constexpr (FULL)
@@ -184,9 +187,9 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
     }
   };
   auto fetch = [&](int k0) { fetch_to(k0, pa, px); };
-  auto stash_from = [&](const u32x4 (&pa)[4], const u32x4 (&px)[4]) {
+  auto stash_from = [&](const u32x4 (&pa)[QA], const u32x4 (&px)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QA; ++q) {
       const int c = tid + 256 * q, r = c / (KT / E), kk = (c % (KT / E)) * E;
       *reinterpret_cast<u32x4*>(As + r * AP + kk) = pa[q];
     }
@@ -217,9 +220,9 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
       const int tr_off = (kq + (r >> 2)) * BP + 4 * (r & 3);
 #pragma unroll
       for (int kh = 0; kh < KT; kh += 32) {
-        bf16x8 fa[4], fb[4];
+        bf16x8 fa[MI], fb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
           fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm + 16 * i + r) * AP + kh + kq);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
           fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -239,13 +242,13 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
       const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
       for (int ks = 0; ks < KT; ks += 4) {
-        float fa[4], fb[4];
+        float fa[MI], fb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = As[(wm + 16 * i + r) * AP + ks + kq];
+        for (int i = 0; i < MI; ++i) fa[i] = As[(wm + 16 * i + r) * AP + ks + kq];
 #pragma unroll
         for (int j = 0; j < 4; ++j) fb[j] = Bs[(ks + kq) * BP + wn + 16 * j + r];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -293,18 +296,18 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
     }
   }
 
-  // bias, rounding to the storage type, staging half a tile (64 rows, the
+  // bias, rounding to the storage type, staging half a tile (MT / 2 rows, the
   // two wavefronts of one row half) at a time: lane l holds rows
   // 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
   const int col = lane & 15, rq = (lane >> 4) * 4;
   for (int h = 0; h < 2; ++h) {
     if ((wave >> 1) == h) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * i + rq + e;          // row within the half
-          const int m = m0 + h * 64 + r;
+          const int m = m0 + h * (MT / 2) + r;
           const float bv = (a.bias && m < M) ? g_ld(a.bias, m) : 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -318,9 +321,9 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
     }
     lds_barrier();
     // the half's rows to their output tensors, 16-byte runs
-    for (int c = tid; c < 64 * kNT / E; c += 256) {
+    for (int c = tid; c < (MT / 2) * kNT / E; c += 256) {
       const int r = c / (kNT / E), nn = (c % (kNT / E)) * E;
-      const int m = m0 + h * 64 + r, n = n0 + nn;
+      const int m = m0 + h * (MT / 2) + r, n = n0 + nn;
       if (!FULL && (m >= M || n >= N)) continue;
       const int t = m / a.Mt, mr = m - t * a.Mt;
       T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N);
@@ -595,13 +598,23 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
   if (K % ks == 0 && K / ks <= kXsMaxSteps && xs_lds_bytes<T>(K, M) <= kXsMaxLds &&
       M % 32 == 0 && g.vec_a && g.vec_x && g.vec_o)
     return launch_xs_k<T>(g, B, name, stream, tr);
-  const int64_t tiles = static_cast<int64_t>((M + kMT - 1) / kMT) * ((N + kNT - 1) / kNT) * B;
+  // M tile height: the one that leaves the least work on the busiest compute
+  // unit (tiles spread evenly, each unit's time proportional to its tiles'
+  // rows), the taller one on a tie
+  const int64_t ntn = (N + kNT - 1) / kNT;
+  auto load = [&](int mt) {
+    const int64_t t = (M + mt - 1) / mt * ntn * B;
+    return (t + cu_count() - 1) / cu_count() * mt;
+  };
+  const int mt = load(96) < load(128) ? 96 : 128;
+  const int64_t tiles = (M + mt - 1) / mt * ntn * B;
   const dim3 grid(static_cast<unsigned>((tiles + 7) / 8 * 8));
   // the straight-line variant: whole tiles, an even number of K tiles
   const int kt = 128 / static_cast<int>(sizeof(T));
-  const bool full = M % kMT == 0 && N % kNT == 0 && K % (2 * kt) == 0 && g.vec_a && g.vec_x &&
+  const bool full = M % mt == 0 && N % kNT == 0 && K % (2 * kt) == 0 && g.vec_a && g.vec_x &&
                     g.vec_o;
-  auto kern = full ? prologue_gemm<T, true> : prologue_gemm<T, false>;
+  auto kern = mt == 96 ? (full ? prologue_gemm<T, true, 96> : prologue_gemm<T, false, 96>)
+                       : (full ? prologue_gemm<T, true, 128> : prologue_gemm<T, false, 128>);
   tr->before(stream, name, B);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g);
   tr->after(stream);
