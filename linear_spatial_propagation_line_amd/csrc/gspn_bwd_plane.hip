@@ -97,15 +97,34 @@ struct BPlaneArgs {
 // logits and grad_out again; they were read moments before, so from L2.
 // The first four wavefronts run the scans (one direction each); all NT
 // threads share the per-pixel phases.
-template <typename T, int SEG, int NT>
-__global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
+// HS, WS > 0: the plane's height and width fixed at compile time (common
+// shapes), so index arithmetic folds to constants and the scans unroll to
+// exactly their length; 0: taken from the arguments. LOCAL: local groups
+// (G > 0); without them a scan restarts only at its first step.
+template <typename T, int SEG, int NT, int HS = 0, int WS = 0, bool LOCAL = true>
+__global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArgs<T> a) {
   constexpr int PPB = 64 / SEG;
-  constexpr int KMAX = (PPB * SEG * SEG + NT - 1) / NT;   // pixels per thread at most
+  constexpr bool FIX = HS > 0;
+  // pixels per thread at most
+  constexpr int KMAX = ((FIX ? PPB * HS * WS : PPB * SEG * SEG) + NT - 1) / NT;
+  // longest scan: SEG, or the plane's longer side when it is fixed
+  constexpr int NS = FIX ? (HS > WS ? HS : WS) : SEG;
   extern __shared__ float4 smem[];
   float* smf = reinterpret_cast<float*>(smem);
 
-  const int H = a.H, W = a.W, pitch = a.pitch, G = a.G;
+  const int H = FIX ? HS : a.H, W = FIX ? WS : a.W, pitch = FIX ? (WS | 1) : a.pitch;
+  const int G = LOCAL ? a.G : 0;
   const int HW = H * W;
+  // pixel index -> (plane, remainder) within a plane group
+  auto split_plane = [&](int i, int* rem) {
+    if constexpr (FIX) {
+      const int pp = i / (HS * WS);
+      *rem = i - pp * (HS * WS);
+      return pp;
+    } else {
+      return div_small(i, HW, a.inv_HW, rem);
+    }
+  };
   const int rec_sz = PPB * H * pitch;          // pixels (with pitch padding)
   // float4 records [0, rec_sz) -> later parked states, floats [0, 4 rec_sz)
   float* hpark = smf;
@@ -132,7 +151,7 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     *lgi = *gi;
     if (a.Cl != a.C) {
       int rem;
-      const int pin = PPB == 1 ? 0 : div_small(ic, HW, a.inv_HW, &rem);
+      const int pin = PPB == 1 ? 0 : split_plane(ic, &rem);
       *lgi += logit_shift(pl0 + pin, a.C, a.Cl, HW);
     }
   };
@@ -162,8 +181,13 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     // LDS index of pixel i of the group (and its plane within the group)
     auto lds_index = [&](int i, int* r, int* c, int* pp_out = nullptr) {
       int rem;
-      const int pp = div_small(i, HW, a.inv_HW, &rem);
-      *r = div_small(rem, W, a.inv_W, c);
+      const int pp = split_plane(i, &rem);
+      if constexpr (FIX) {
+        *r = rem / WS;
+        *c = rem - *r * WS;
+      } else {
+        *r = div_small(rem, W, a.inv_W, c);
+      }
       if (pp_out) *pp_out = pp;
       return (pp * H + *r) * pitch + *c;
     };
@@ -234,11 +258,11 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
       return fwd ? (s % G) == 0 : ((n_s - 1 - s) % G) == G - 1;
     };
 
-    float hist[SEG];
+    float hist[NS];
     if (on) {
       float h = 0.0f;
 #pragma unroll
-      for (int s = 0; s < SEG; ++s) {
+      for (int s = 0; s < NS; ++s) {
         if (s < n_s) {
           const float4 rc = smem[addr0 + s * stride];
           const float hn = line_step<SEG>(h, rc.x, rc.y, rc.z, rc.w);
@@ -277,7 +301,7 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     if (on) {
       float p0 = 0.f, p1 = 0.f, p2 = 0.f;   // w_k e of the line after this one
 #pragma unroll
-      for (int s = SEG - 1; s >= 0; --s) {
+      for (int s = NS - 1; s >= 0; --s) {
         if (s < n_s) {
           const float4 rc = smem[addr0 + s * stride];
           const float e = rc.w + from_right<SEG>(p0) + p1 + from_left<SEG>(p2);
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(NT) void bplane_kernel(BPlaneArgs<T> a) {
     // ---- 5. park the forward states over the records --------------------------
     if (active) {
 #pragma unroll
-      for (int s = 0; s < SEG; ++s)
+      for (int s = 0; s < NS; ++s)
         if (s < n_s) hpark[d * rec_sz + mbase + s * mstride] = hist[s];
     }
     __syncthreads();
@@ -383,6 +407,32 @@ size_t bplane_lds_bytes(int64_t H, int64_t W) {
          static_cast<size_t>(ppb * (2 * H + 2 * W) + 1) * sizeof(float4);
 }
 
+// the kernel for a plane shape: compile-time shapes for common sizes (the
+// 16 x 16 DiT latents, the 56 x 56 first classification stage, and the
+// square planes of later stages), the general kernel otherwise
+template <typename T, int SEG, int NT>
+static void (*pick_bplane_kernel(int H, int W, bool local))(BPlaneArgs<T>) {
+  if (H == W) {
+    if constexpr (SEG == 16) {
+      if (H == 16) return local ? bplane_kernel<T, 16, NT, 16, 16, true>
+                                : bplane_kernel<T, 16, NT, 16, 16, false>;
+    } else {
+      switch (H) {
+        case 28: return local ? bplane_kernel<T, 64, NT, 28, 28, true>
+                              : bplane_kernel<T, 64, NT, 28, 28, false>;
+        case 32: return local ? bplane_kernel<T, 64, NT, 32, 32, true>
+                              : bplane_kernel<T, 64, NT, 32, 32, false>;
+        case 56: return local ? bplane_kernel<T, 64, NT, 56, 56, true>
+                              : bplane_kernel<T, 64, NT, 56, 56, false>;
+        case 64: return local ? bplane_kernel<T, 64, NT, 64, 64, true>
+                              : bplane_kernel<T, 64, NT, 64, 64, false>;
+        default: break;
+      }
+    }
+  }
+  return local ? bplane_kernel<T, SEG, NT, 0, 0, true> : bplane_kernel<T, SEG, NT, 0, 0, false>;
+}
+
 template <typename T, int SEG, int NT>
 static hipError_t launch_bplane_t(const BwdProblem& pr, hipStream_t stream, Tracer* tr) {
   BPlaneArgs<T> a;
@@ -413,7 +463,7 @@ static hipError_t launch_bplane_t(const BwdProblem& pr, hipStream_t stream, Trac
   a.Cl = pr.Cl;
   a.dlw = pr.dlw;
   const size_t lds = bplane_lds_bytes(pr.H, pr.W);
-  auto kern = bplane_kernel<T, SEG, NT>;
+  auto kern = pick_bplane_kernel<T, SEG, NT>(a.H, a.W, a.G > 0);
   hipError_t e;
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
