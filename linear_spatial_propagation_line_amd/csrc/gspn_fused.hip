@@ -84,6 +84,10 @@ __device__ __forceinline__ float round_bf16(float v) {
   return __uint_as_float(f32_to_bf16_bits(v) << 16);
 }
 
+// HS, WS > 0: the plane's sides fixed at compile time (the 16 x 16 latents),
+// so pixel indices split by constants and the scans unroll to their length.
+// (A variant without local groups runs out of registers.)
+template <int HS, int WS>
 __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   // image's x by 16, and the K step they all read meets in that L2.
   const int tile = static_cast<int>(blockIdx.x % 8) * a.per + static_cast<int>(blockIdx.x / 8);
   if (tile >= a.tiles) return;
-  const int C = a.C, N = a.N, H = a.H, W = a.W;
+  const int C = a.C, H = HS > 0 ? HS : a.H, W = WS > 0 ? WS : a.W, N = HS > 0 ? HS * WS : a.N;
   const int ps = H * kRP + 1;
   const int ng = C / kCg;
   const int blk = tile / (kIB * ng);
@@ -351,8 +355,7 @@ hipError_t launch_fused_unit(const PrologueProblem& pr, const void* x, void* out
   const int64_t tiles = pr.B * (pr.C / kCg);
   a.tiles = static_cast<int>(tiles);
   a.per = static_cast<int>((tiles + 7) / 8);
-  // two K steps in flight when the steps pair up
-  auto kern = fused_unit;
+  auto kern = (a.H == 16 && a.W == 16) ? fused_unit<16, 16> : fused_unit<0, 0>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
