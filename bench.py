@@ -122,7 +122,7 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     kernels only).
 
     Per pixel, with s = bytes per stored element:
-      plane_kernel16/64 (all directions on chip): x, lambda, l0, l1, l2, u
+      plane_kernel16/64, plane_pc_kernel (all directions on chip): x, lambda, l0, l1, l2, u
           read once, out written once -> 7 s
       stream_kernel (one launch per direction, fp32 accumulator between
           them): 5 s inputs + 4 (accumulator read or write, counted once);
@@ -200,6 +200,7 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     per = {
         "plane_kernel16": 7 * s,
         "plane_kernel64": 7 * s,
+        "plane_pc_kernel": 7 * s,
         "stream_kernel": 5 * s + 4,
         "band_kernel": 12 * s,
         "tp_vfwd": 5 * s + (4 + 3 * s * sh if hz else 0) + (0.5 if w.dirs & 1 else 0),

@@ -25,6 +25,8 @@
 // 方法; three-neighbour tridiagonal weights with sigmoid + row normalisation
 // and four scan directions: same page, section 如何设计一个高效的传播层;
 // local groups: section GSPN模块的设计.
+#include <cstdlib>
+
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 
@@ -276,6 +278,196 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
 }
 
 // ---------------------------------------------------------------------------
+// Producer / consumer variant for one plane of fixed shape H x W (both at
+// most 64, W % 4 == 0) per group. Eight wavefronts: wavefronts 0-3 produce
+// (records and edge records of group k, from inputs loaded one group ahead,
+// two in bf16), 4-7 consume (the four scans, the park and the merge of group
+// k - 1), on two record buffers, so that the serial scans of one group
+// overlap the weights of the next. Three workgroup barriers per group
+// separate the phases that share a buffer. The producers' raw inputs and the
+// consumers' scan states live in different wavefronts, which is what keeps
+// 64 x 64 fp32 planes out of scratch. Same arithmetic as plane_kernel, in
+// the same order: the two give the same bits.
+template <typename T, int HS, int WS, bool LOCAL>
+__global__ __launch_bounds__(512, 1) void plane_pc_kernel(PlaneArgs<T> a) {
+  constexpr int H = HS, W = WS, HW = HS * WS, pitch = WS | 1;
+  constexpr int NIT = (HW + 1023) / 1024;      // 4-pixel vectors per producer thread
+  constexpr int NS = HS > WS ? HS : WS;
+  constexpr int rec_sz = H * pitch;
+  constexpr int ev_off = rec_sz, eh_off = ev_off + 2 * H, zero_off = eh_off + 2 * W;
+  constexpr int buf_sz = zero_off + 1;          // float4 units per buffer
+  using V = V4<T>;
+  extern __shared__ float4 smem[];
+  const int tid = threadIdx.x;
+  const bool prod = tid < 256;
+  const int rt = tid & 255;
+  const int64_t ngroups = a.nplanes;            // one plane per group
+  // groups of this workgroup: blockIdx.x + k gridDim.x, k < n
+  const int64_t n = blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  auto group_of = [&](int64_t k) { return blockIdx.x + k * static_cast<int64_t>(gridDim.x); };
+
+  // producers: the raw inputs of the next groups in registers, two groups
+  // ahead in two register sets where they fit (bf16), else one group ahead
+  constexpr bool TWO = sizeof(T) == 2;
+  typename V::raw xA[NIT], lA[NIT], gA0[NIT], gA1[NIT], gA2[NIT];
+  typename V::raw xB[TWO ? NIT : 1], lB[TWO ? NIT : 1], gB0[TWO ? NIT : 1], gB1[TWO ? NIT : 1],
+      gB2[TWO ? NIT : 1];
+  auto issue = [&](int64_t k, auto& rx, auto& rl, auto& r0, auto& r1, auto& r2) {
+    const int64_t g = group_of(min(k, n - 1));  // past the last group: reload it
+    const int64_t gb = g * HW;
+    const int64_t ls = logit_shift(g, a.C, a.Cl, HW);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i0 = rt * 4 + it * 1024;
+      const int64_t gi = gb + (i0 < HW ? i0 : 0);
+      rx[it] = V::load(a.x, gi);
+      rl[it] = V::load(a.lam, gi);
+      r0[it] = V::load(a.l0, gi + ls);
+      r1[it] = V::load(a.l1, gi + ls);
+      r2[it] = V::load(a.l2, gi + ls);
+    }
+  };
+  auto records = [&](float4* buf, const auto& rx, const auto& rl, const auto& r0, const auto& r1,
+                     const auto& r2) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i0 = rt * 4 + it * 1024;
+      if (i0 < HW) {
+        const int r = i0 / WS, c = i0 - r * WS;   // W % 4 == 0: four pixels of row r
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const Weights w = make_weights(V::get(r0[it], e), V::get(r1[it], e), V::get(r2[it], e),
+                                         1.0f, 1.0f);
+          buf[r * pitch + c + e] = make_float4(w.w0, w.w1, w.w2, V::get(rl[it], e) * V::get(rx[it], e));
+        }
+      }
+    }
+  };
+  // edge-lane records: one slot per producer thread, [horizontal][side][64 positions]
+  auto edges = [&](float4* buf) {
+    const int k = rt;
+    const int hz = k >> 7, e = (k >> 6) & 1, pos = k & 63;
+    int r, c, idx, n_o, o;
+    if (!hz) { r = pos; c = e ? W - 1 : 0; o = c; n_o = W; idx = ev_off + e * H + pos; }
+    else     { c = pos; r = e ? H - 1 : 0; o = r; n_o = H; idx = eh_off + e * W + pos; }
+    if (pos < (hz ? W : H)) {
+      const float4 m = buf[r * pitch + c];
+      const Weights w = edge_weights(m.x, m.y, m.z, o > 0 ? 1.f : 0.f, o < n_o - 1 ? 1.f : 0.f);
+      buf[idx] = make_float4(w.w0, w.w1, w.w2, m.w);
+    }
+    if (k == 0) buf[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+
+  // consumers: wavefront d of 4..7 scans direction d - 4, lane o
+  const int d = (tid >> 6) & 3, o = tid & 63;
+  const bool on = (a.mask >> d) & 1u;
+  const bool vert = d < 2, fwd = (d == 0 || d == 2);
+  const int n_s = vert ? H : W, n_o = vert ? W : H;
+  const bool active = on && o < n_o;
+  int mbase, mstride;
+  if (vert) { mbase = (fwd ? 0 : H - 1) * pitch + o; mstride = fwd ? pitch : -pitch; }
+  else      { mbase = o * pitch + (fwd ? 0 : W - 1); mstride = fwd ? 1 : -1; }
+  int addr0 = mbase, stride = mstride;
+  if (!active) { addr0 = zero_off; stride = 0; }
+  else if (o == 0 || o == n_o - 1) {
+    const int e = (o == 0) ? 0 : 1;
+    if (vert) addr0 = ev_off + e * H + (fwd ? 0 : H - 1);
+    else      addr0 = eh_off + e * W + (fwd ? 0 : W - 1);
+    stride = fwd ? 1 : -1;
+  }
+  const int G = LOCAL ? a.G : 0;
+  int first_restart = n_s;
+  if (G > 0) first_restart = fwd ? G : n_s - ((n_s - 1) / G) * G;
+  float hist[NS];
+  typename V::raw uu[NIT];
+  auto load_u = [&](int64_t k, typename V::raw (&ru)[NIT]) {
+    const int64_t gb = group_of(k) * HW;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i0 = rt * 4 + it * 1024;
+      ru[it] = V::load(a.u, gb + (i0 < HW ? i0 : 0));
+    }
+  };
+
+  auto merge = [&](const float4* buf, int64_t cg, const typename V::raw (&ru)[NIT]) {
+    const float* pf = reinterpret_cast<const float*>(buf);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i0 = rt * 4 + it * 1024;
+      if (i0 < HW) {
+        const int r = i0 / WS, c = i0 - r * WS;
+        const int li = r * pitch + c;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd)
+            if ((a.mask >> dd) & 1u) sum += pf[dd * rec_sz + li + e];
+          y[e] = V::get(ru[it], e) * sum;
+        }
+        V::store(a.out, cg * HW + i0, y);
+      }
+    }
+  };
+
+  if (prod && n > 0) {
+    issue(0, xA, lA, gA0, gA1, gA2);
+    if constexpr (TWO) issue(1, xB, lB, gB0, gB1, gB2);
+  }
+  for (int64_t k = 0; k <= n; ++k) {
+    float4* pbuf = smem + (k & 1) * buf_sz;          // producers: group k
+    float4* cbuf = smem + ((k + 1) & 1) * buf_sz;    // consumers: group k - 1
+    // ---- A: records of group k | scans of group k - 1 ----------------------
+    if (prod) {
+      if (k < n) {
+        if constexpr (TWO) {
+          if (k & 1) { records(pbuf, xB, lB, gB0, gB1, gB2); issue(k + 2, xB, lB, gB0, gB1, gB2); }
+          else       { records(pbuf, xA, lA, gA0, gA1, gA2); issue(k + 2, xA, lA, gA0, gA1, gA2); }
+        } else {
+          records(pbuf, xA, lA, gA0, gA1, gA2);
+          issue(k + 1, xA, lA, gA0, gA1, gA2);
+        }
+      }
+    } else if (k > 0) {
+      load_u(k - 1, uu);                 // u of the group, for the merge
+      if (on) {
+        int addr = addr0, next_restart = first_restart;
+        float h = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          if (s < n_s) {
+            const float4 rc = cbuf[addr];
+            addr += stride;
+            const float hn = line_step<64>(h, rc.x, rc.y, rc.z, rc.w);
+            bool restart = (s == 0);
+            if (s == next_restart) { restart = true; next_restart += G; }
+            h = restart ? rc.w : hn;
+            hist[s] = h;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- B: edge records of group k | park the states of group k - 1 -------
+    if (prod) {
+      if (k < n) edges(pbuf);
+    } else if (k > 0 && active) {
+      float* pf = reinterpret_cast<float*>(cbuf);
+      int ya = d * rec_sz + mbase;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s < n_s) { pf[ya] = hist[s]; ya += mstride; }
+      }
+    }
+    __syncthreads();
+    // ---- C: merge of group k - 1 -------------------------------------------
+    if (!prod && k > 0) merge(cbuf, group_of(k - 1), uu);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 bool plane_fits(int64_t H, int64_t W) { return H >= 1 && W >= 1 && H <= 64 && W <= 64; }
 
 int plane_seg(int64_t H, int64_t W) { return (H <= 16 && W <= 16) ? 16 : 64; }
@@ -316,6 +508,22 @@ static void (*pick_plane_kernel(int H, int W, bool local))(PlaneArgs<T>) {
   return local ? plane_kernel<T, SEG, VEC, 0, 0, true> : plane_kernel<T, SEG, VEC, 0, 0, false>;
 }
 
+// the producer / consumer kernel where it is the faster one, else null:
+// fp32 planes of 64 x 64, where the one-role kernel runs out of registers
+// (about 0.15 against 0.21 ms for 64 x 96 such planes; at 56 x 56 and below,
+// and in bf16, the one-role kernel with two workgroups per CU is as fast or
+// faster). GSPN_PLANE_PC=0 turns it off, for comparisons.
+template <typename T>
+static void (*pick_plane_pc_kernel(int H, int W, bool local))(PlaneArgs<T>) {
+  const char* env = std::getenv("GSPN_PLANE_PC");
+  if (env && env[0] == '0') return nullptr;
+  if constexpr (sizeof(T) == 4) {
+    if (H == 64 && W == 64)
+      return local ? plane_pc_kernel<T, 64, 64, true> : plane_pc_kernel<T, 64, 64, false>;
+  }
+  return nullptr;
+}
+
 template <typename T, int SEG, int VEC>
 static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* tr) {
   PlaneArgs<T> a;
@@ -342,6 +550,21 @@ static hipError_t launch_plane_t(const Problem& pr, hipStream_t stream, Tracer* 
   const bool local = a.G > 0;
   auto kern = pick_plane_kernel<T, SEG, VEC>(a.H, a.W, local);
   hipError_t e;
+  if constexpr (SEG == 64 && VEC == 4) {
+    if (auto pk = pick_plane_pc_kernel<T>(a.H, a.W, local)) {
+      // two buffers of records, edge records and the zero record
+      const size_t pl = 2 * (static_cast<size_t>(pr.H) * (pr.W | 1) + 2 * pr.H + 2 * pr.W + 1) *
+                        sizeof(float4);
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(pk),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(pl));
+      if (e != hipSuccess) return e;
+      const int64_t grid = a.nplanes < cu_count() ? a.nplanes : cu_count();
+      tr->before(stream, "plane_pc_kernel", a.nplanes);
+      hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(grid)), dim3(512), pl, stream, a);
+      tr->after(stream);
+      return hipGetLastError();
+    }
+  }
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

@@ -8,7 +8,7 @@ import pytest
 import bench
 from linear_spatial_propagation_line_amd.inputs import WORKLOADS
 
-KERNELS = ["plane_kernel16", "plane_kernel64", "stream_kernel", "band_kernel", "tp_vfwd",
+KERNELS = ["plane_kernel16", "plane_kernel64", "plane_pc_kernel", "stream_kernel", "band_kernel", "tp_vfwd",
            "tp_hpair", "tp_vbwd", "tp_lgcopy", "bplane_kernel16", "bplane_kernel64", "bwd_fwd",
            "bwd_adj", "bwd_transpose", "bwd_finish", "bband_kernel", "bwd_reduce_logits",
            "dir_plane", "dir_vert", "dir_tr_in", "dir_tr_acc", "prologue_reduce", "prologue_params",

@@ -111,6 +111,29 @@ def test_local_groups(shape, G):
     assert_parity(out, oracle_y(inp, 15, G), f"{shape} G={G}")
 
 
+@pytest.mark.parametrize("C,cl", [(5, 5), (4, 1), (300, 300)], ids=["C5", "C4_Cl1", "C300"])
+@pytest.mark.parametrize("G", [0, 5])
+def test_plane64_fp32_producer_consumer(monkeypatch, C, cl, G):
+    """fp32 planes of 64 x 64 take the producer / consumer kernel: every
+    direction subset against the oracle (sampled planes when there are more
+    planes than CUs, so that each workgroup runs several groups), and the
+    same bits as the one-role kernel."""
+    inp = make_inputs("cls_56x56", seed=C + G, B=2, C=C, H=64, W=64)
+    if cl != C:
+        inp = {k: (v[:, :cl].contiguous() if k in ("l0", "l1", "l2") else v)
+               for k, v in inp.items()}
+    for mask in (15, 1, 8, 6):
+        monkeypatch.delenv("GSPN_PLANE_PC", raising=False)
+        out = run(inp, mask, G)
+        monkeypatch.setenv("GSPN_PLANE_PC", "0")
+        one = run(inp, mask, G)
+        assert torch.equal(out, one), f"C={C} Cl={cl} G={G} mask={mask}"
+        planes = [0, 1, C - 1] if C > 8 else list(range(C))
+        for c in planes:
+            sub = {k: v[:, c:c + 1] if v.shape[1] == C else v for k, v in inp.items()}
+            assert_parity(out[:, c:c + 1], oracle_y(sub, mask, G), f"C={C} plane {c} mask={mask}")
+
+
 @pytest.mark.parametrize("shape", [(2, 3, 16, 16), (1, 2, 56, 56), (1, 2, 200, 150)])
 def test_row_stochastic_invariant(shape):
     """lambda = x = u = 1: y = H + W + 2 everywhere (Theorem 1)."""
