@@ -76,7 +76,7 @@ template <> struct Two<bf16_t> {
   __device__ static float lo(raw v) { return bf16_lo(v); }
   __device__ static float hi(raw v) { return bf16_hi(v); }
   __device__ static void store(bf16_t* p, int64_t i, float a, float b) {
-    *reinterpret_cast<uint32_t*>(p + i) = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    *reinterpret_cast<uint32_t*>(p + i) = pack_bf16x2(a, b);
   }
 };
 

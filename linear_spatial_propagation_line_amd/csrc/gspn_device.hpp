@@ -23,12 +23,22 @@ __device__ __forceinline__ float to_f32(bf16_t v) {
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 
-// binary32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
+// binary32 -> bf16, round to nearest, ties to even (NaN stays a NaN), by
+// gfx950's packed conversion, one instruction per pair: `a` in the low half
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return pack_bf16x2(f, 0.0f) & 0xffffu;
+}
+// two values replaced by their nearest bf16 values, kept as binary32
+__device__ __forceinline__ void round_bf16x2(float& a, float& b) {
+  const uint32_t p = pack_bf16x2(a, b);
+  a = __uint_as_float(p << 16);
+  b = __uint_as_float(p & 0xffff0000u);
 }
 
 template <typename T> struct Store;
@@ -66,8 +76,8 @@ template <> struct V4<bf16_t> {
   }
   __device__ static void store(bf16_t* p, int64_t i, const float v[4]) {
     uint2 q;
-    q.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    q.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p + i) = q;
   }
 };
@@ -104,7 +114,7 @@ template <int N> __device__ __forceinline__ void run_st(bf16_t* p, int64_t i, co
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      w[j] = f32_to_bf16_bits(d[8 * k + 2 * j]) | (f32_to_bf16_bits(d[8 * k + 2 * j + 1]) << 16);
+      w[j] = pack_bf16x2(d[8 * k + 2 * j], d[8 * k + 2 * j + 1]);
     q[k] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }

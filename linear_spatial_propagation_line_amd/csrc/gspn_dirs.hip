@@ -130,7 +130,7 @@ template <int N> __device__ __forceinline__ void put_run(bf16_t* p, int64_t i, c
   uint32_t w[(N + 1) / 2];
 #pragma unroll
   for (int k = 0; k < N / 2; ++k)
-    w[k] = f32_to_bf16_bits(d[2 * k]) | (f32_to_bf16_bits(d[2 * k + 1]) << 16);
+    w[k] = pack_bf16x2(d[2 * k], d[2 * k + 1]);
   if constexpr (N % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 8; ++k)

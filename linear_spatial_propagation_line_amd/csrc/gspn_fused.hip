@@ -80,10 +80,6 @@ __device__ __forceinline__ int bpos(int k, int n) {
   return k * kNmax + ((((n >> 4) ^ bswz(k)) << 4) | (n & 15));
 }
 
-__device__ __forceinline__ float round_bf16(float v) {
-  return __uint_as_float(f32_to_bf16_bits(v) << 16);
-}
-
 // HS, WS > 0: the plane's sides fixed at compile time (the 16 x 16 latents),
 // so pixel indices split by constants and the scans unroll to their length.
 // (A variant without local groups runs out of registers.)
@@ -228,13 +224,20 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int n = 16 * (4 * j + wave) + r16;
     const int row = n / W, col = n - row * W;
+    // the parameters as the unfused path stores them: rounded to bf16
+    float pr[5][4];
+#pragma unroll
+    for (int t = 0; t < 5; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        pr[t][e] = acc[t][j][e] + bias[t][e];
+        pr[t][e + 1] = acc[t][j][e + 1] + bias[t][e + 1];
+        round_bf16x2(pr[t][e], pr[t][e + 1]);
+      }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float l0 = round_bf16(acc[0][j][e] + bias[0][e]);
-      const float l1 = round_bf16(acc[1][j][e] + bias[1][e]);
-      const float l2 = round_bf16(acc[2][j][e] + bias[2][e]);
-      const float lam = round_bf16(acc[3][j][e] + bias[3][e]);
-      uu[e][j] = round_bf16(acc[4][j][e] + bias[4][e]);
+      const float l0 = pr[0][e], l1 = pr[1][e], l2 = pr[2][e], lam = pr[3][e];
+      uu[e][j] = pr[4][e];
       if (n < N) {
         const Weights w = make_weights(l0, l1, l2, 1.0f, 1.0f);
         const float xx = __uint_as_float(static_cast<uint32_t>(xv[e][j]) << 16);

@@ -94,7 +94,7 @@ __device__ __forceinline__ void store_pair(float* p, int64_t i, float a, float b
   *reinterpret_cast<float2*>(p + i) = make_float2(a, b);
 }
 __device__ __forceinline__ void store_pair(bf16_t* p, int64_t i, float a, float b) {
-  *reinterpret_cast<uint32_t*>(p + i) = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  *reinterpret_cast<uint32_t*>(p + i) = pack_bf16x2(a, b);
 }
 
 // raw inputs of two adjacent pixels

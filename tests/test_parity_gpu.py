@@ -134,6 +134,39 @@ def test_plane64_fp32_producer_consumer(monkeypatch, C, cl, G):
             assert_parity(out[:, c:c + 1], oracle_y(sub, mask, G), f"C={C} plane {c} mask={mask}")
 
 
+@pytest.mark.parametrize("plan,shape", [("plane", (1, 3, 16, 16)), ("plane", (1, 2, 56, 56)),
+                                        ("band", (1, 2, 66, 40)), ("tpipe", (1, 2, 66, 40)),
+                                        ("tpipe_t", (1, 2, 40, 130)), ("large", (1, 3, 65, 67)),
+                                        ("stream", (1, 2, 66, 40))],
+                         ids=lambda v: v if isinstance(v, str) else "x".join(map(str, v)))
+def test_bf16_store_rounds_to_nearest_even(force_plan, plan, shape):
+    """With a restart at every step (G = 1) the state is lambda * x, exact in
+    fp32 for bf16 inputs (16 significant bits at most), and with u = 1 and one
+    direction the stored output is that product rounded once to bf16: it must
+    be the nearest bf16 value, ties to even, bit for bit. Random mantissas
+    give about one tie in 256 products."""
+    force_plan(plan)
+    B, C, H, W = shape
+    gen = torch.Generator().manual_seed(H * W + C)
+    def rnd():
+        m = 1.0 + torch.rand(shape, generator=gen, dtype=torch.float64)
+        e = torch.randint(-20, 20, shape, generator=gen).to(torch.float64)
+        sgn = torch.where(torch.rand(shape, generator=gen) < 0.5, -1.0, 1.0).to(torch.float64)
+        return (sgn * m * torch.exp2(e)).to(torch.bfloat16)
+    x, lam = rnd(), rnd()
+    lg = [torch.randn(shape, generator=gen).to(torch.bfloat16) for _ in range(3)]
+    u = torch.ones(shape, dtype=torch.bfloat16)
+    want = (lam.float() * x.float()).to(torch.bfloat16)
+    d = [t.to(DEV) for t in (x, *lg, lam, u)]
+    for mask in (1, 4):
+        assert g.plan_name(B, C, H, W, mask, 1, 1).startswith(plan)
+        out = g.propagate(d[0], (d[1], d[2], d[3]), d[4], d[5], dirs=mask, group_rows=1)
+        torch.cuda.synchronize()
+        got = out.cpu()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), \
+            f"{plan} {shape} mask={mask}: {(got != want).sum().item()} elements differ"
+
+
 @pytest.mark.parametrize("shape", [(2, 3, 16, 16), (1, 2, 56, 56), (1, 2, 200, 150)])
 def test_row_stochastic_invariant(shape):
     """lambda = x = u = 1: y = H + W + 2 everywhere (Theorem 1)."""
