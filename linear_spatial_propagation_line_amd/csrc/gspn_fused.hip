@@ -46,18 +46,18 @@ namespace {
 constexpr int kCg = 16;            // channels per workgroup
 constexpr int kIB = 4;             // images per block of the tile order
 constexpr int kMR = 5 * kCg;       // rows of W_p per workgroup
-constexpr int kKT = 64;            // K per step: 128-byte rows
-constexpr int kAP = kKT + 8;       // LDS pitch of the weight tile [m][k] (elements)
+constexpr int kKT = 32;            // K per stage: 64-byte rows of the weight tile
+constexpr int kStages = 3;         // stages in flight: loads run two stages ahead
 constexpr int kNmax = 256;         // pixels of one image
 constexpr int kRP = 17;            // records per plane row (odd: no bank conflicts
                                    // on horizontal scans)
-constexpr int kArun = kMR * kKT / 8;   // 16-byte runs of the weight tile
-constexpr int kStageBytes = kMR * kAP * 2 + kKT * kNmax * 2;
+constexpr int kABytes = kMR * kKT * 2;              // weight tile [80][32], 5 blocks of 1 KB
+constexpr int kStageBytes = kABytes + kKT * kNmax * 2;   // + pixel tile [32][256], 16 blocks
 constexpr int kRecBytes = kCg * (16 * kRP + 1) * 16;
 constexpr int kOutOff = kRecBytes;                  // output staging [16][N] bf16
 constexpr int kZeroOff = kRecBytes + kCg * kNmax * 2;
 constexpr int kLdsBytes = kZeroOff + 16;
-static_assert(kStageBytes <= kRecBytes, "the product's tiles live in the record area");
+static_assert(kStages * kStageBytes <= kRecBytes, "the product's stages live in the record area");
 
 struct FusedArgs {
   const bf16_t* wp;    // [5C][C]
@@ -86,8 +86,6 @@ __device__ __forceinline__ int bpos(int k, int n) {
 template <int HS, int WS>
 __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Bs = reinterpret_cast<uint16_t*>(smem + kMR * kAP * 2);
   float4* recs = reinterpret_cast<float4*>(smem);
   float* recf = reinterpret_cast<float*>(smem);
   uint16_t* ost = reinterpret_cast<uint16_t*>(smem + kOutOff);
@@ -107,7 +105,8 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   const int rem = tile - blk * kIB * ng;
   const int64_t b = blk * kIB + rem % ibe;
   const int c0 = (rem / ibe) * kCg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
   const int r16 = lane & 15, rq = (lane >> 4) * 4;
   const bf16_t* X = a.x + b * static_cast<int64_t>(C) * N;
 
@@ -118,96 +117,135 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // 16-byte runs this thread moves per K step, the same for every step:
-  // weight run c = tid + 256 q is row c / 8 of the 80, k offset 8 (c % 8);
-  // pixel run c is k row c / (N / 8), pixels 8 (c % (N / 8)) .. Runs past the
-  // end load a valid run and are not stored.
-  const int rpr = N / 8;
-  int a_off[3], b_goff[8], b_lds[8];
-  bool a_ok[3], b_ok[8];
+  // Stages of K = 32 go from global memory straight into LDS
+  // (global_load_lds_dwordx4: each instruction writes 64 lanes x 16 bytes
+  // as one contiguous 1 KB block, lane i at 16 i), three stages in a ring,
+  // loads two stages ahead of the multiply. The block layouts are fixed by
+  // choosing each lane's source:
+  //   weight block t (rows 16 t .. 16 t + 15 of the 80, 64 bytes each): lane
+  //     i fills row r = i / 4, slot i % 4 with the row's 16-byte unit
+  //     (i % 4) ^ sw(r), sw(r) = ((r >> 1) ^ (r >> 2)) & 3, so that the
+  //     fragment reads (16 rows, one unit each) hit distinct banks;
+  //   pixel block j (k rows 2 j, 2 j + 1, 256 pixels each): lane i fills
+  //     row 2 j + i / 32 at pixels 8 (i % 32) .. + 7 of the stored order,
+  //     which holds the swizzled 16-pixel blocks of bpos.
+  // Wave w loads pixel blocks 4 w .. 4 w + 3 and weight block w, wave 0
+  // weight block 4 as well: 5 or 6 loads per stage.
+  auto sw = [](int r) { return ((r >> 1) ^ (r >> 2)) & 3; };
+  const int64_t a_row = (static_cast<int64_t>(wave) * C + c0 + (lane >> 2)) * C;
+  const int64_t a_row4 = (static_cast<int64_t>(4) * C + c0 + (lane >> 2)) * C;
+  const int a_unit = 8 * ((lane & 3) ^ sw(lane >> 2));
+  const bf16_t* a_src = a.wp + a_row + a_unit;     // weight block `wave`
+  const bf16_t* a_src4 = a.wp + a_row4 + a_unit;   // weight block 4 (wave 0)
+  // (pixels past N, when N < 256, load pixel 0 again: every lane loads, so
+  // every wave issues the same number of loads per stage)
+  const bf16_t* b_src[4];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    const int c = tid + 256 * q;
-    a_ok[q] = c < kArun;
-    const int m = (a_ok[q] ? c : kArun - 1) >> 3;
-    a_off[q] = ((m >> 4) * C + c0 + (m & 15)) * C + (c & 7) * 8;
+  for (int q = 0; q < 4; ++q) {
+    const int blk = 4 * wave + q;
+    const int row = 2 * blk + (lane >> 5), pos = 8 * (lane & 31);
+    const int n = (((pos >> 4) ^ bswz(row)) << 4) | (pos & 15);
+    b_src[q] = X + static_cast<int64_t>(row) * N + (n < N ? n : 0);
   }
-  const int a_lds = (tid >> 3) * kAP + (tid & 7) * 8;   // + 32 q rows
+  auto issue = [&](int st) {
+    unsigned char* base = smem + (st % kStages) * kStageBytes;
+    const int k0 = st * kKT;
+    __builtin_amdgcn_global_load_lds(a_src + k0, base + wave * 1024, 16, 0, 0);
+    if (wave == 0) __builtin_amdgcn_global_load_lds(a_src4 + k0, base + 4 * 1024, 16, 0, 0);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int c = tid + 256 * q;
-    b_ok[q] = c < kKT * rpr;
-    const int cc = b_ok[q] ? c : kKT * rpr - 1;
-    const int row = cc / rpr, nn = (cc - row * rpr) * 8;
-    b_goff[q] = row * N + nn;
-    b_lds[q] = bpos(row, nn);
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(b_src[q] + static_cast<int64_t>(k0) * N,
+                                       base + kABytes + (4 * wave + q) * 1024, 16, 0, 0);
+  };
+  // LDS byte addresses of this lane's transposing reads in stage 0 (row
+  // 8 (l / 16) + (l % 16) / 4, pixels 16 (4 j + w) + 4 (l % 4) ..; the
+  // second half, rows + 4, is 2 KB further: rows k + 4 share k's swizzle)
+  const uint32_t lds_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
+  uint32_t tr_addr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (lane >> 4) + (r16 >> 2);
+    tr_addr[j] = lds_base + kABytes + 2 * bpos(row, 16 * (4 * j + wave) + 4 * (r16 & 3));
   }
-  u32x4 pa[3], pb[8];
-  auto fetch = [&](int k0) {
+  auto multiply = [&](int st) {
+    const unsigned char* base = smem + (st % kStages) * kStageBytes;
+    // lane l: A[l % 16][8 (l / 16) .. +7] of each M tile, unit l / 16 stored
+    // at slot (l / 16) ^ sw(l % 16) of its row
+    const int g = lane >> 4;
+    bf16x8 fa[5], fb[4];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) pa[q] = *reinterpret_cast<const u32x4*>(a.wp + a_off[q] + k0);
-    const bf16_t* xk = X + static_cast<int64_t>(k0) * N;
+    for (int t = 0; t < 5; ++t)
+      fa[t] = *reinterpret_cast<const bf16x8*>(base + t * 1024 + r16 * 64 + 16 * (g ^ sw(r16)));
+    // B by transposing reads, written out with their wait: the compiler
+    // would otherwise wait for every load in flight into LDS before them,
+    // the stages ahead included
+    const uint32_t so = static_cast<uint32_t>((st % kStages) * kStageBytes);
+    v4i16 tr[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]),
+          "=&v"(tr[6]), "=&v"(tr[7])
+        : "v"(tr_addr[0] + so), "v"(tr_addr[1] + so), "v"(tr_addr[2] + so), "v"(tr_addr[3] + so)
+        : "memory");
 #pragma unroll
-    for (int q = 0; q < 8; ++q) pb[q] = *reinterpret_cast<const u32x4*>(xk + b_goff[q]);
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-      if (a_ok[q]) *reinterpret_cast<u32x4*>(As + a_lds + 32 * q * kAP) = pa[q];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (b_ok[q]) *reinterpret_cast<u32x4*>(Bs + b_lds[q]) = pb[q];
-  };
-  auto multiply = [&]() {
-    // lane l: A[l % 16][8 (l / 16) .. +7] of each M tile; B by transposing reads
-    // (rows k + 4 share k's swizzle: bit 3 of the row is unchanged)
-    const int kq = (lane >> 4) * 8;
-#pragma unroll
-    for (int kh = 0; kh < kKT; kh += 32) {
-      bf16x8 fa[5], fb[4];
-#pragma unroll
-      for (int t = 0; t < 5; ++t)
-        fa[t] = *reinterpret_cast<const bf16x8*>(As + (16 * t + r16) * kAP + kh + kq);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // lane l: rows kh + kq + (l % 16) / 4 (+ 4), pixels 16 (4 j + w) + 4 (l % 4) ..
-        const int row = kh + kq + (r16 >> 2);
-        const uint16_t* q = Bs + bpos(row, 16 * (4 * j + wave) + 4 * (r16 & 3));
-        const v4i16 lo = lds_read_tr(q), hi = lds_read_tr(q + 4 * kNmax);
-        fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
-      }
-#pragma unroll
-      for (int t = 0; t < 5; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb[j], acc[t][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const v4i16 lo = tr[2 * j], hi = tr[2 * j + 1];
+      fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
     }
+#pragma unroll
+    for (int t = 0; t < 5; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb[j], acc[t][j], 0, 0, 0);
+  };
+  // a workgroup barrier that orders no memory by itself: the waits for the
+  // stage's loads are explicit, and the empty asm keeps the compiler from
+  // moving LDS accesses across it
+  auto stage_barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // x of the group's channels, for lambda x: rows c0 - kx0 .. of the pixel
-  // tile of K step kx0, taken while it is in LDS
+  // tile of the stage at kx0, taken while it is in LDS
   const int kx0 = c0 & ~(kKT - 1);
   uint16_t xv[4][4];
-  // The next step's runs are loaded while the current one is multiplied.
-  // Loads are never conditional and the loop body is straight-line, so the
-  // compiler can count the loads in flight instead of waiting for all of
-  // them at every step (the last step reloads itself). A second register
-  // set, two steps ahead, measured slower.
-  fetch(0);
-  for (int k0 = 0; k0 < C; k0 += kKT) {
-    stash();
-    lds_barrier();
-    fetch(min(k0 + kKT, C - kKT));
-    multiply();
-    if (k0 == kx0) {
+  const int S = C / kKT;
+  issue(0);
+  if (S > 1) issue(1);
+  for (int st = 0; st < S; ++st) {
+    // this wave's loads of stage st are done when at most the next stage's
+    // are in flight (vector memory loads complete in order)
+    if (st + 1 < S) {
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
+      else           __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    stage_barrier();   // ... and every wave's; stage st - 1 is no longer read
+    if (st + 2 < S) issue(st + 2);
+    multiply(st);
+    if (st * kKT == kx0) {
+      const uint16_t* Bst = reinterpret_cast<const uint16_t*>(smem + (st % kStages) * kStageBytes +
+                                                              kABytes);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          xv[e][j] = Bs[bpos(c0 - kx0 + rq + e, 16 * (4 * j + wave) + r16)];
+          xv[e][j] = Bst[bpos(c0 - kx0 + rq + e, 16 * (4 * j + wave) + r16)];
     }
-    lds_barrier();
   }
+  lds_barrier();   // the records overwrite the stages
 
   // ---- 2. records -------------------------------------------------------------
   // plane p's records start at p ps: one spare record per plane moves each
@@ -335,9 +373,8 @@ bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 }  // namespace
 
 bool fused_unit_fits(const PrologueProblem& pr) {
-  // (weight offsets are 32-bit: 5 C^2 < 2^31)
   return pr.dtype == GSPN_BF16 && pr.H >= 1 && pr.W >= 1 && pr.H <= 16 && pr.W <= 16 &&
-         (pr.H * pr.W) % 8 == 0 && pr.C % kKT == 0 && pr.C >= kKT && pr.C <= 20000 &&
+         (pr.H * pr.W) % 8 == 0 && pr.C % 64 == 0 && pr.C >= 64 && pr.C <= 20000 &&
          al16(pr.w_p);
 }
 
