@@ -28,6 +28,8 @@
 // (64 rows at a time) and written as 16-byte row runs. The linear block index
 // walks M fastest, so the M tiles that share a pixel tile run together and
 // find it in L2.
+#include <cstdlib>
+
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 #include "gspn_mfma.hpp"
@@ -94,6 +96,63 @@ __device__ __forceinline__ u32x4 vec4(const uint4& v) { return u32x4{v.x, v.y, v
 __device__ __forceinline__ uint32_t half16(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// The finished M x 128 tile: bias, rounding to the storage type, staging
+// half a tile (MT / 2 rows, the two wavefronts of one row half) at a time in
+// LDS, then 16-byte row runs to the output tensors.
+template <typename T, bool FULL, int MT>
+__device__ __forceinline__ void store_tile(const GemmArgs<T>& a, const f32x4 (&acc)[MT / 32][4],
+                                           decltype(raw(T{}))* Os, int m0, int n0, int64_t b,
+                                           int tid, int wave) {
+  using R = decltype(raw(T{}));
+  constexpr int MI = MT / 32;
+  constexpr int E = 16 / sizeof(T);
+  const int M = a.M, N = a.N;
+  const int lane = tid & 63, wn = (wave & 1) * 64;
+  // lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
+  const int col = lane & 15, rq = (lane >> 4) * 4;
+  for (int h = 0; h < 2; ++h) {
+    if ((wave >> 1) == h) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + rq + e;          // row within the half
+          const int m = m0 + h * (MT / 2) + r;
+          const float bv = (a.bias && m < M) ? g_ld(a.bias, m) : 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = acc[i][j][e] + bv;
+            if constexpr (sizeof(T) == 2)
+              Os[r * kOP + wn + 16 * j + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+            else
+              Os[r * kOP + wn + 16 * j + col] = v;
+          }
+        }
+    }
+    lds_barrier();
+    // the half's rows to their output tensors, 16-byte runs
+    for (int c = tid; c < (MT / 2) * kNT / E; c += 256) {
+      const int r = c / (kNT / E), nn = (c % (kNT / E)) * E;
+      const int m = m0 + h * (MT / 2) + r, n = n0 + nn;
+      if (!FULL && (m >= M || n >= N)) continue;
+      const int t = m / a.Mt, mr = m - t * a.Mt;
+      T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N);
+      const R* src = Os + r * kOP + nn;
+      if (FULL || (a.vec_o && n + E <= N)) {
+        *reinterpret_cast<uint4*>(dst + n) = *reinterpret_cast<const uint4*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (n + e >= N) break;
+          if constexpr (sizeof(T) == 2) dst[n + e].bits = src[e];
+          else dst[n + e] = src[e];
+        }
+      }
+    }
+    lds_barrier();
+  }
 }
 
 // FULL: M and N multiples of 128, K a multiple of the K tile, every tensor in
@@ -296,51 +355,160 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
     }
   }
 
-  // bias, rounding to the storage type, staging half a tile (MT / 2 rows, the
-  // two wavefronts of one row half) at a time: lane l holds rows
-  // 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
-  const int col = lane & 15, rq = (lane >> 4) * 4;
-  for (int h = 0; h < 2; ++h) {
-    if ((wave >> 1) == h) {
+  store_tile<T, FULL, MT>(a, acc, Os, m0, n0, b, tid, wave);
+}
+
+// bf16, whole tiles (the FULL conditions): the same tiling, with the K loop's
+// stages (K = 32) moved from global memory straight into LDS by
+// global_load_lds_dwordx4, three stages in a ring, loads two stages ahead of
+// the multiply. Each instruction writes 64 lanes x 16 bytes as one
+// contiguous 1 KB block (lane i at 16 i), so each lane's source is chosen to
+// give the block the layout the fragment reads want:
+//   weight block t (rows 16 t .. 16 t + 15 of the M tile, 64 bytes each):
+//     lane i fills row i / 4, slot i % 4 with the row's 16-byte unit
+//     (i % 4) ^ sw(i / 4), sw(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 16 rows
+//     a fragment read takes hit distinct banks;
+//   pixel block j (k rows 4 j .. 4 j + 3, 128 pixels each): lane i fills row
+//     4 j + i / 16 at stored pixels 8 (i % 16) .. + 7, the row's 16-pixel
+//     blocks stored at block ^ tsw(row), so the four rows a transposing read
+//     takes are in different banks.
+// Same products in the same order as prologue_gemm: the same bits.
+template <int MT>
+__global__ __launch_bounds__(256, 2) void prologue_gemm_lds(GemmArgs<bf16_t> a) {
+  constexpr int MI = MT / 32;                // 16-row MFMA tiles per wavefront
+  constexpr int KS = 32;                     // K per stage
+  constexpr int NS = 3;                      // stages in the ring
+  constexpr int ABLK = MT / 16, BBLK = KS * kNT * 2 / 1024, NBLK = ABLK + BBLK;
+  constexpr int STAGE = NBLK * 1024;
+  constexpr int kOutBytes = (MT / 2) * kOP * 2;
+  constexpr int kSmem = NS * STAGE > kOutBytes ? NS * STAGE : kOutBytes;
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  uint16_t* Os = reinterpret_cast<uint16_t*>(smem);   // [MT / 2][kOP], after the K loop
+
+  const int M = a.M, K = a.K, N = a.N;
+  const int nmt = M / MT;
+  // the tile order of prologue_gemm: XCD t / per runs tile t
+  const int tiles = nmt * (N / kNT);
+  const int64_t all = static_cast<int64_t>(tiles) * a.B;
+  const int64_t per = (all + 7) / 8;
+  const int64_t t = static_cast<int64_t>(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= all) return;
+  const int64_t b = t / tiles;
+  const int tile = static_cast<int>(t - b * tiles);
+  const int m0 = (tile % nmt) * MT;
+  const int n0 = (tile / nmt) * kNT;
+  const bf16_t* X = a.X + b * static_cast<int64_t>(K) * N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
+  const int wm = (wave >> 1) * (MT / 2), wn = (wave & 1) * 64;   // this wavefront's quarter
+  const int r16 = lane & 15, g = lane >> 4;
+
+  f32x4 acc[MI][4];
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + rq + e;          // row within the half
-          const int m = m0 + h * (MT / 2) + r;
-          const float bv = (a.bias && m < M) ? g_ld(a.bias, m) : 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto sw = [](int r) { return ((r >> 1) ^ (r >> 2)) & 3; };
+  auto tsw = [](int k) { return (k & 3) | ((k >> 1) & 4); };
+  // wave w loads blocks w, w + 4, w + 8, w + 12 of each stage (those below
+  // NBLK): its source pointers at stage 0 and their step per stage
+  const int nld = (NBLK - wave + 3) / 4;
+  const bf16_t* src[4];
+  int64_t step[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float v = acc[i][j][e] + bv;
-            if constexpr (sizeof(T) == 2)
-              Os[r * kOP + wn + 16 * j + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-            else
-              Os[r * kOP + wn + 16 * j + col] = v;
-          }
-        }
+  for (int q = 0; q < 4; ++q) {
+    const int blk = wave + 4 * q < NBLK ? wave + 4 * q : wave;
+    if (blk < ABLK) {
+      const int r = lane >> 2;
+      src[q] = a.A + static_cast<int64_t>(m0 + 16 * blk + r) * K + 8 * ((lane & 3) ^ sw(r));
+      step[q] = KS;
+    } else {
+      const int row = 4 * (blk - ABLK) + (lane >> 4), pos = 8 * (lane & 15);
+      const int n = n0 + ((((pos >> 4) ^ tsw(row)) << 4) | (pos & 15));
+      src[q] = X + static_cast<int64_t>(row) * N + n;
+      step[q] = static_cast<int64_t>(KS) * N;
     }
-    lds_barrier();
-    // the half's rows to their output tensors, 16-byte runs
-    for (int c = tid; c < (MT / 2) * kNT / E; c += 256) {
-      const int r = c / (kNT / E), nn = (c % (kNT / E)) * E;
-      const int m = m0 + h * (MT / 2) + r, n = n0 + nn;
-      if (!FULL && (m >= M || n >= N)) continue;
-      const int t = m / a.Mt, mr = m - t * a.Mt;
-      T* dst = pick_out(a.out, t) + (b * a.Mt + mr) * static_cast<int64_t>(N);
-      const R* src = Os + r * kOP + nn;
-      if (FULL || (a.vec_o && n + E <= N)) {
-        *reinterpret_cast<uint4*>(dst + n) = *reinterpret_cast<const uint4*>(src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (n + e >= N) break;
-          if constexpr (sizeof(T) == 2) dst[n + e].bits = src[e];
-          else dst[n + e] = src[e];
-        }
-      }
-    }
-    lds_barrier();
   }
+  auto issue = [&](int st) {
+    unsigned char* base = smem + (st % NS) * STAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < nld)
+        __builtin_amdgcn_global_load_lds(src[q] + st * step[q], base + (wave + 4 * q) * 1024,
+                                         16, 0, 0);
+  };
+  // LDS byte addresses of this lane's transposing reads in stage 0: rows
+  // 8 (l / 16) + (l % 16) / 4 (+ 4: 1 KB further, rows k + 4 share k's
+  // swizzle), pixels wn + 16 j + 4 (l % 4) ..
+  const uint32_t lds_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
+  uint32_t tr_addr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * g + (r16 >> 2), n = wn + 16 * j + 4 * (r16 & 3);
+    tr_addr[j] = lds_base + ABLK * 1024 +
+                 2 * (row * kNT + ((((n >> 4) ^ tsw(row)) << 4) | (n & 15)));
+  }
+  auto multiply = [&](int st) {
+    const unsigned char* base = smem + (st % NS) * STAGE;
+    bf16x8 fa[MI], fb[4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(base + (wm / 16 + i) * 1024 + r16 * 64 +
+                                               16 * (g ^ sw(r16)));
+    // the transposing reads with their own wait: the compiler would wait for
+    // every load in flight into LDS before the builtin form
+    const uint32_t so = static_cast<uint32_t>((st % NS) * STAGE);
+    v4i16 tr[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]),
+          "=&v"(tr[6]), "=&v"(tr[7])
+        : "v"(tr_addr[0] + so), "v"(tr_addr[1] + so), "v"(tr_addr[2] + so), "v"(tr_addr[3] + so)
+        : "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i16 lo = tr[2 * j], hi = tr[2 * j + 1];
+      fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  const int S = K / KS;
+  issue(0);
+  if (S > 1) issue(1);
+  for (int st = 0; st < S; ++st) {
+    // this wave's loads of stage st are done when at most the next stage's
+    // are in flight (vector memory loads complete in order)
+    if (st + 1 < S) {
+      if (nld == 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+      else          __builtin_amdgcn_s_waitcnt(0x0F70 | 3);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    // every wave's loads of stage st are in, and stage st - 1 is no longer
+    // read; the empty asm keeps the compiler from moving LDS accesses across
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 2 < S) issue(st + 2);
+    multiply(st);
+  }
+  lds_barrier();   // the output staging overwrites the stages
+  store_tile<bf16_t, true, MT>(a, acc, Os, m0, n0, b, tid, wave);
 }
 
 // Pixel-stationary variant for small K (all K rows of a 64-pixel tile fit
@@ -615,6 +783,12 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
                     g.vec_o;
   auto kern = mt == 96 ? (full ? prologue_gemm<T, true, 96> : prologue_gemm<T, false, 96>)
                        : (full ? prologue_gemm<T, true, 128> : prologue_gemm<T, false, 128>);
+  if constexpr (sizeof(T) == 2) {
+    // whole bf16 tiles, K a multiple of the stage: stages straight into LDS
+    const char* env = std::getenv("GSPN_GEMM_LDS");
+    if (full && K % 32 == 0 && !(env && env[0] == '0'))
+      kern = mt == 96 ? prologue_gemm_lds<96> : prologue_gemm_lds<128>;
+  }
   tr->before(stream, name, B);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g);
   tr->after(stream);

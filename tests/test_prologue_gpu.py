@@ -55,6 +55,31 @@ def test_prologue_shapes(shape, dtype):
             assert_parity(got[k], ref[k], f"prologue {k} {shape} bias={bias}")
 
 
+@pytest.mark.parametrize("shape", [(2, 512, 96, 16, 16), (75, 512, 384, 16, 16),
+                                   (1, 1152, 1152, 16, 16)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_prologue_whole_tiles_direct_to_lds(shape, monkeypatch):
+    """bf16 products of whole tiles with K above the pixel-stationary
+    kernel's reach load their K stages straight into LDS: the first shape's
+    first product takes M tiles of 96 rows, the second's of 128, the third
+    (DiT width) both products. Same sums
+    in the same order as the register-staged kernel: the same bits, and the
+    oracle's bound."""
+    B, Cin, C, H, W = shape
+    inp = make_prologue_inputs(None, seed=5 + C, B=B, Cin=Cin, C=C, H=H, W=W, dtype="bf16")
+    monkeypatch.delenv("GSPN_GEMM_LDS", raising=False)
+    got = gpu_prologue(inp)
+    monkeypatch.setenv("GSPN_GEMM_LDS", "0")
+    reg = gpu_prologue(inp)
+    for k in ("x",) + tuple(g.PARAM_NAMES):
+        assert torch.equal(got[k].view(torch.int16), reg[k].view(torch.int16)), f"{shape} {k}"
+    if B <= 2:
+        ref = oracle_prologue(inp)
+        assert_parity(got["x"], ref["x"], f"x {shape}")
+        for k in g.PARAM_NAMES:
+            assert_parity(got[k], ref[k], f"{k} {shape}")
+
+
 def test_prologue_wide_channels():
     """C = Cin = 1152 (the DiT-XL/2 width): K spans 36 tiles, 5C 45 M tiles."""
     inp = make_prologue_inputs("dit_16x16_mod", B=1)
