@@ -360,8 +360,10 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
 
 // bf16, whole tiles (the FULL conditions): the same tiling, with the K loop's
 // stages (K = 32) moved from global memory straight into LDS by
-// global_load_lds_dwordx4, three stages in a ring, loads two stages ahead of
-// the multiply. Each instruction writes 64 lanes x 16 bytes as one
+// global_load_lds_dwordx4, NS stages in a ring, loads NS - 1 stages ahead of
+// the multiply. Two stages (one ahead) measured best: 28-32 KB of LDS leave
+// room for four workgroups per CU, where three stages (three workgroups) and
+// four (two) were 10% and 20% slower on the DiT-width products. Each instruction writes 64 lanes x 16 bytes as one
 // contiguous 1 KB block (lane i at 16 i), so each lane's source is chosen to
 // give the block the layout the fragment reads want:
 //   weight block t (rows 16 t .. 16 t + 15 of the M tile, 64 bytes each):
@@ -373,11 +375,10 @@ __global__ __launch_bounds__(256, 1) void prologue_gemm(GemmArgs<T> a) {
 //     blocks stored at block ^ tsw(row), so the four rows a transposing read
 //     takes are in different banks.
 // Same products in the same order as prologue_gemm: the same bits.
-template <int MT>
+template <int MT, int NS>
 __global__ __launch_bounds__(256, 2) void prologue_gemm_lds(GemmArgs<bf16_t> a) {
   constexpr int MI = MT / 32;                // 16-row MFMA tiles per wavefront
   constexpr int KS = 32;                     // K per stage
-  constexpr int NS = 3;                      // stages in the ring
   constexpr int ABLK = MT / 16, BBLK = KS * kNT * 2 / 1024, NBLK = ABLK + BBLK;
   constexpr int STAGE = NBLK * 1024;
   constexpr int kOutBytes = (MT / 2) * kOP * 2;
@@ -488,23 +489,27 @@ __global__ __launch_bounds__(256, 2) void prologue_gemm_lds(GemmArgs<bf16_t> a) 
   };
 
   const int S = K / KS;
-  issue(0);
-  if (S > 1) issue(1);
+  constexpr int AH = NS - 1;                 // stages loaded ahead
+  for (int st = 0; st < AH && st < S; ++st) issue(st);
   for (int st = 0; st < S; ++st) {
-    // this wave's loads of stage st are done when at most the next stage's
+    // this wave's loads of stage st are done when at most the later stages'
     // are in flight (vector memory loads complete in order)
-    if (st + 1 < S) {
-      if (nld == 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-      else          __builtin_amdgcn_s_waitcnt(0x0F70 | 3);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+    const int later = (AH - 1 < S - 1 - st ? AH - 1 : S - 1 - st) * nld;
+    switch (later) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | 3); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F70 | 4); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F70 | 6); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
+      case 9: __builtin_amdgcn_s_waitcnt(0x0F70 | 9); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70 | 12); break;
     }
     // every wave's loads of stage st are in, and stage st - 1 is no longer
     // read; the empty asm keeps the compiler from moving LDS accesses across
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (st + 2 < S) issue(st + 2);
+    if (st + AH < S) issue(st + AH);
     multiply(st);
   }
   lds_barrier();   // the output staging overwrites the stages
@@ -787,7 +792,7 @@ hipError_t gemm(const T* A, const T* bias, const T* X, T* const* outs, int nout,
     // whole bf16 tiles, K a multiple of the stage: stages straight into LDS
     const char* env = std::getenv("GSPN_GEMM_LDS");
     if (full && K % 32 == 0 && !(env && env[0] == '0'))
-      kern = mt == 96 ? prologue_gemm_lds<96> : prologue_gemm_lds<128>;
+      kern = mt == 96 ? prologue_gemm_lds<96, 2> : prologue_gemm_lds<128, 2>;
   }
   tr->before(stream, name, B);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g);
