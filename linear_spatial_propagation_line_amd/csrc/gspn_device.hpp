@@ -135,9 +135,15 @@ struct Weights {
   float w0, w1, w2;
 };
 
+// exp(-max(l, -40)), as exp2 of -l log2(e) capped at the exponent of -40.
+// The cap is applied after the multiply: rounding is monotonic, so the cap
+// gives the same bits as clamping l first, NaN and -inf included (both go
+// to the cap), and a cap on a product needs no NaN quieting of its input,
+// where a clamp of the raw logit costs one more instruction.
 __device__ __forceinline__ float exp_neg(float l) {
-  constexpr float kLog2e = 1.4426950408889634f;
-  return __builtin_amdgcn_exp2f(-fmaxf(l, -40.0f) * kLog2e);
+  constexpr float kNegLog2e = -1.4426950408889634f;
+  constexpr float kCap = -40.0f * kNegLog2e;
+  return __builtin_amdgcn_exp2f(fminf(l * kNegLog2e, kCap));
 }
 
 // Reciprocal: hardware estimate refined by one Newton-Raphson step
