@@ -102,7 +102,7 @@ struct BPlaneArgs {
 // exactly their length; 0: taken from the arguments. LOCAL: local groups
 // (G > 0); without them a scan restarts only at its first step.
 template <typename T, int SEG, int NT, int HS = 0, int WS = 0, bool LOCAL = true>
-__global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArgs<T> a) {
+__global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArgs<T> a) {
   constexpr int PPB = 64 / SEG;
   constexpr bool FIX = HS > 0;
   // pixels per thread at most
@@ -135,13 +135,14 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
   const int zero_off = eh_off + PPB * 2 * W;   // one zero record
   const int tid = threadIdx.x;
 
-  // 64-wide planes (one workgroup per CU, nothing else to hide latency): the
-  // inputs of the records (x, lambda, logits) are held raw in registers one
-  // plane group ahead; the next group's loads are issued right after this
-  // group's records are built, so they stay in flight through the scans.
-  // 16-wide planes run several workgroups per CU and load them in place.
-  constexpr bool kAhead = SEG == 64;
+  // The inputs of the records (x, lambda, logits) are held raw in registers
+  // one plane group ahead; the next group's loads are issued right after
+  // this group's records are built, so they stay in flight through the
+  // scans. 16-wide planes hold u and grad_out ahead as well.
+  constexpr bool kAhead = true;
+  constexpr bool kAheadUg = SEG == 16;
   T px[KMAX], plm[KMAX], pq0[KMAX], pq1[KMAX], pq2[KMAX];
+  T pu[kAheadUg ? KMAX : 1], pg[kAheadUg ? KMAX : 1];
   auto group_pixel = [&](int64_t grp, int k, int64_t* gi, int64_t* lgi) {
     const int64_t pl0 = grp * PPB;
     const int npx = static_cast<int>(min<int64_t>(PPB, a.nplanes - pl0)) * HW;
@@ -165,6 +166,10 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
       pq0[k] = a.l0[lgi];
       pq1[k] = a.l1[lgi];
       pq2[k] = a.l2[lgi];
+      if constexpr (kAheadUg) {
+        pu[k] = a.u[gi];
+        pg[k] = a.gy[gi];
+      }
     }
   };
   if constexpr (kAhead)
@@ -205,6 +210,26 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
           const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
           const Weights w = make_weights(pl1(a.l0, lgi), pl1(a.l1, lgi), pl1(a.l2, lgi), 1.f, 1.f);
           smem[li] = make_float4(w.w0, w.w1, w.w2, pl1(a.lam, gi) * pl1(a.x, gi));
+        }
+      }
+    }
+    // this group's inputs, before the next group's loads replace them: u and
+    // grad_out for step 3, and (fixed 16 x 16 shapes) all seven for step 6
+    constexpr int KC = kAheadUg ? KMAX : 1;
+    constexpr bool kKeep = kAheadUg && FIX;
+    T ug_u[KC], ug_g[KC], cx[kKeep ? KMAX : 1], clm[kKeep ? KMAX : 1], cq0[kKeep ? KMAX : 1],
+        cq1[kKeep ? KMAX : 1], cq2[kKeep ? KMAX : 1];
+    if constexpr (kAheadUg) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        ug_u[k] = pu[k];
+        ug_g[k] = pg[k];
+        if constexpr (kKeep) {
+          cx[k] = px[k];
+          clm[k] = plm[k];
+          cq0[k] = pq0[k];
+          cq1[k] = pq1[k];
+          cq2[k] = pq2[k];
         }
       }
     }
@@ -279,7 +304,8 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
       const int i = tid + NT * k;
       if (i < npix) {
         int r, c;
-        smf[4 * lds_index(i, &r, &c) + 3] = pl1(a.u, gbase + i) * pl1(a.gy, gbase + i);
+        smf[4 * lds_index(i, &r, &c) + 3] =
+            kAheadUg ? to_f32(ug_u[k]) * to_f32(ug_g[k]) : pl1(a.u, gbase + i) * pl1(a.gy, gbase + i);
       }
     }
     __syncthreads();
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
 
     // ---- 6. gradients per pixel ----------------------------------------------
     const unsigned mask = a.mask;
-#pragma unroll 2
+#pragma unroll (SEG == 16 && FIX ? KMAX : 2)
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i >= npix) continue;
@@ -333,8 +359,13 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 4 : 1) void bplane_kernel(BPlaneArg
       const int li = lds_index(i, &r, &c, &pp);
       const int64_t gi = gbase + i;
       const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
-      const float xv = pl1(a.x, gi), lv = pl1(a.lam, gi), gyv = pl1(a.gy, gi);
-      const float g0 = pl1(a.l0, lgi), g1 = pl1(a.l1, lgi), g2 = pl1(a.l2, lgi);
+      // (the fixed-shape kernels unroll this loop, so k indexes registers)
+      const float xv = kKeep ? to_f32(cx[k]) : pl1(a.x, gi);
+      const float lv = kKeep ? to_f32(clm[k]) : pl1(a.lam, gi);
+      const float gyv = kKeep ? to_f32(ug_g[k]) : pl1(a.gy, gi);
+      const float g0 = kKeep ? to_f32(cq0[k]) : pl1(a.l0, lgi);
+      const float g1 = kKeep ? to_f32(cq1[k]) : pl1(a.l1, lgi);
+      const float g2 = kKeep ? to_f32(cq2[k]) : pl1(a.l2, lgi);
       float se = 0.f, sh = 0.f;
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
