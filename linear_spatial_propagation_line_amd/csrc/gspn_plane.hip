@@ -95,11 +95,13 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
 
   // registers filled one iteration ahead (VEC == 4 only)
   typename V::raw rx[NIT], rl[NIT], r0[NIT], r1[NIT], r2[NIT], ru[NIT];
-  auto issue = [&](int64_t grp) {
+  // loads of 4-pixel vectors lo .. hi - 1 of plane group grp
+  auto issue = [&](int64_t grp, int lo, int hi) {
     const int64_t gb = grp * PPB * HW;
     const int npx = static_cast<int>(min<int64_t>(PPB, a.nplanes - grp * PPB)) * HW;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
+      if (it < lo || it >= hi) continue;
       const int i0 = tid * 4 + it * 1024;
       const int ic = i0 < npx ? i0 : 0;                // always in bounds
       const int64_t gi = gb + ic;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
     }
   };
   if constexpr (VEC == 4)
-    if (static_cast<int64_t>(blockIdx.x) < a.ngroups) issue(blockIdx.x);
+    if (static_cast<int64_t>(blockIdx.x) < a.ngroups) issue(blockIdx.x, 0, NIT);
 
   for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
     const int64_t plane0 = grp * PPB;
@@ -146,8 +148,9 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
           }
         }
       }
-      // the next plane group's loads fly during steps 2-4
-      if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x);
+      // the next plane group's loads fly during steps 2-4; on 64-wide planes
+      // they are issued a part per phase, so the memory stays busy
+      if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x, 0, SEG == 64 ? 2 : NIT);
     } else {
       for (int i0 = tid; i0 < npix; i0 += 256) {
         int p, r, c;
@@ -184,6 +187,8 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
       }
     }
     __syncthreads();
+    if constexpr (VEC == 4 && SEG == 64)
+      if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x, 2, 3);
 
     // ---- 3. one scan direction per wavefront -------------------------------
     const int d = tid >> 6;
@@ -230,6 +235,8 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
       }
     }
     __syncthreads();   // every wavefront is done with the records
+    if constexpr (VEC == 4 && SEG == 64)
+      if (grp + gridDim.x < a.ngroups) issue(grp + gridDim.x, 3, NIT);
 
     // ---- 4. park states over the records, then merge ------------------------
     if (active) {
