@@ -4,8 +4,8 @@
 // A workgroup of four wavefronts owns PPB = 64 / SEG planes at a time and
 // loops over plane groups (persistent grid). Per plane group:
 //   1. records (w0, w1, w2, lambda x) per pixel in LDS, and the edge-lane
-//      records whose missing neighbour changes the normalisation (on 64-wide
-//      planes their inputs were loaded while the previous group ran);
+//      records whose missing neighbour changes the normalisation (their
+//      inputs were loaded while the previous group ran);
 //   2. wavefront d runs the forward scan of direction d (lane = orthogonal
 //      index, neighbours by DPP) and keeps its states in registers;
 //   3. the record's fourth component becomes u * grad_out;
@@ -25,8 +25,9 @@
 //      neighbouring states (sum_j w_j = 1) and the weights recomputed from
 //      the logits for the scan axis of d (edge masks differ between axes).
 // LDS holds 32 bytes per pixel (records, later the parked states, plus the
-// parked error terms). HBM traffic: seven inputs read (the logits, x and
-// lambda once more in step 6, from L2), six gradients written.
+// parked error terms). HBM traffic: seven inputs read, six gradients
+// written; step 6 reads the logits, x, lambda and grad_out once more (from
+// L2), except on fixed 16 x 16 planes, which keep them in registers.
 #include "gspn_device.hpp"
 #include "gspn_launch.hpp"
 
@@ -139,7 +140,6 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
   // one plane group ahead; the next group's loads are issued right after
   // this group's records are built, so they stay in flight through the
   // scans. 16-wide planes hold u and grad_out ahead as well.
-  constexpr bool kAhead = true;
   constexpr bool kAheadUg = SEG == 16;
   T px[KMAX], plm[KMAX], pq0[KMAX], pq1[KMAX], pq2[KMAX];
   T pu[kAheadUg ? KMAX : 1], pg[kAheadUg ? KMAX : 1];
@@ -172,8 +172,7 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
       }
     }
   };
-  if constexpr (kAhead)
-    if (static_cast<int64_t>(blockIdx.x) < a.ngroups) fetch_records(blockIdx.x);
+  if (static_cast<int64_t>(blockIdx.x) < a.ngroups) fetch_records(blockIdx.x);
 
   for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
     const int64_t plane0 = grp * PPB;
@@ -200,17 +199,10 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
     for (int k = 0; k < KMAX; ++k) {
       const int i = tid + NT * k;
       if (i < npix) {
-        int r, c, pp;
-        const int li = lds_index(i, &r, &c, &pp);
-        if constexpr (kAhead) {
-          const Weights w = make_weights(to_f32(pq0[k]), to_f32(pq1[k]), to_f32(pq2[k]), 1.f, 1.f);
-          smem[li] = make_float4(w.w0, w.w1, w.w2, to_f32(plm[k]) * to_f32(px[k]));
-        } else {
-          const int64_t gi = gbase + i;
-          const int64_t lgi = gi + logit_shift(plane0 + pp, a.C, a.Cl, HW);
-          const Weights w = make_weights(pl1(a.l0, lgi), pl1(a.l1, lgi), pl1(a.l2, lgi), 1.f, 1.f);
-          smem[li] = make_float4(w.w0, w.w1, w.w2, pl1(a.lam, gi) * pl1(a.x, gi));
-        }
+        int r, c;
+        const int li = lds_index(i, &r, &c);
+        const Weights w = make_weights(to_f32(pq0[k]), to_f32(pq1[k]), to_f32(pq2[k]), 1.f, 1.f);
+        smem[li] = make_float4(w.w0, w.w1, w.w2, to_f32(plm[k]) * to_f32(px[k]));
       }
     }
     // this group's inputs, before the next group's loads replace them: u and
@@ -233,8 +225,7 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
         }
       }
     }
-    if constexpr (kAhead)
-      if (more) fetch_records(grp + gridDim.x);
+    if (more) fetch_records(grp + gridDim.x);
     if (tid == 0) smem[zero_off] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 

@@ -287,8 +287,8 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
 // ---------------------------------------------------------------------------
 // Producer / consumer variant for one plane of fixed shape H x W (both at
 // most 64, W % 4 == 0) per group. Eight wavefronts: wavefronts 0-3 produce
-// (records and edge records of group k, from inputs loaded one group ahead,
-// two in bf16), 4-7 consume (the four scans, the park and the merge of group
+// (records and edge records of group k, from inputs loaded one group ahead),
+// 4-7 consume (the four scans, the park and the merge of group
 // k - 1), on two record buffers, so that the serial scans of one group
 // overlap the weights of the next. Three workgroup barriers per group
 // separate the phases that share a buffer. The producers' raw inputs and the
@@ -313,12 +313,8 @@ __global__ __launch_bounds__(512, 1) void plane_pc_kernel(PlaneArgs<T> a) {
   const int64_t n = blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   auto group_of = [&](int64_t k) { return blockIdx.x + k * static_cast<int64_t>(gridDim.x); };
 
-  // producers: the raw inputs of the next groups in registers, two groups
-  // ahead in two register sets where they fit (bf16), else one group ahead
-  constexpr bool TWO = sizeof(T) == 2;
+  // producers: the raw inputs of the next group in registers
   typename V::raw xA[NIT], lA[NIT], gA0[NIT], gA1[NIT], gA2[NIT];
-  typename V::raw xB[TWO ? NIT : 1], lB[TWO ? NIT : 1], gB0[TWO ? NIT : 1], gB1[TWO ? NIT : 1],
-      gB2[TWO ? NIT : 1];
   auto issue = [&](int64_t k, auto& rx, auto& rl, auto& r0, auto& r1, auto& r2) {
     const int64_t g = group_of(min(k, n - 1));  // past the last group: reload it
     const int64_t gb = g * HW;
@@ -418,23 +414,15 @@ __global__ __launch_bounds__(512, 1) void plane_pc_kernel(PlaneArgs<T> a) {
     }
   };
 
-  if (prod && n > 0) {
-    issue(0, xA, lA, gA0, gA1, gA2);
-    if constexpr (TWO) issue(1, xB, lB, gB0, gB1, gB2);
-  }
+  if (prod && n > 0) issue(0, xA, lA, gA0, gA1, gA2);
   for (int64_t k = 0; k <= n; ++k) {
     float4* pbuf = smem + (k & 1) * buf_sz;          // producers: group k
     float4* cbuf = smem + ((k + 1) & 1) * buf_sz;    // consumers: group k - 1
     // ---- A: records of group k | scans of group k - 1 ----------------------
     if (prod) {
       if (k < n) {
-        if constexpr (TWO) {
-          if (k & 1) { records(pbuf, xB, lB, gB0, gB1, gB2); issue(k + 2, xB, lB, gB0, gB1, gB2); }
-          else       { records(pbuf, xA, lA, gA0, gA1, gA2); issue(k + 2, xA, lA, gA0, gA1, gA2); }
-        } else {
-          records(pbuf, xA, lA, gA0, gA1, gA2);
-          issue(k + 1, xA, lA, gA0, gA1, gA2);
-        }
+        records(pbuf, xA, lA, gA0, gA1, gA2);
+        issue(k + 1, xA, lA, gA0, gA1, gA2);
       }
     } else if (k > 0) {
       load_u(k - 1, uu);                 // u of the group, for the merge
