@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
       r0[it] = V::load(a.l0, lgi);
       r1[it] = V::load(a.l1, lgi);
       r2[it] = V::load(a.l2, lgi);
-      ru[it] = V::load(a.u, gi);
+      if constexpr (SEG == 16) ru[it] = V::load(a.u, gi);
     }
   };
   if constexpr (VEC == 4)
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
     if constexpr (VEC == 4) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        uu[it] = ru[it];
+        if constexpr (SEG == 16) uu[it] = ru[it];
         const int i0 = tid * 4 + it * 1024;
         if (i0 < npix) {
           int p, r, c;
@@ -146,6 +146,15 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
             smem[(p * H + r) * pitch + c + e] =
                 make_float4(w.w0, w.w1, w.w2, V::get(rl[it], e) * V::get(rx[it], e));
           }
+        }
+      }
+      // 64-wide planes load this group's u now, for the merge: holding it a
+      // group ahead as well would not fit the registers
+      if constexpr (SEG == 64) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int i0 = tid * 4 + it * 1024;
+          uu[it] = V::load(a.u, gbase + (i0 < npix ? i0 : 0));
         }
       }
       // the next plane group's loads fly during steps 2-4; on 64-wide planes
