@@ -206,11 +206,24 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
       }
     }
     // this group's inputs, before the next group's loads replace them: u and
-    // grad_out for step 3, and (fixed 16 x 16 shapes) all seven for step 6
-    constexpr int KC = kAheadUg ? KMAX : 1;
+    // grad_out for step 3, and (fixed 16 x 16 shapes) all seven for step 6.
+    // Fixed 64-wide shapes load u and grad_out here, for step 3, so that the
+    // forward scans hide their latency (the general kernel has no registers
+    // left for them and loads them in step 3).
     constexpr bool kKeep = kAheadUg && FIX;
+    constexpr bool kEarlyUg = !kAheadUg && FIX;
+    constexpr int KC = kAheadUg || kEarlyUg ? KMAX : 1;
     T ug_u[KC], ug_g[KC], cx[kKeep ? KMAX : 1], clm[kKeep ? KMAX : 1], cq0[kKeep ? KMAX : 1],
         cq1[kKeep ? KMAX : 1], cq2[kKeep ? KMAX : 1];
+    if constexpr (kEarlyUg) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int i = tid + NT * k;
+        const int64_t gi = gbase + (i < npix ? i : 0);
+        ug_u[k] = a.u[gi];
+        ug_g[k] = a.gy[gi];
+      }
+    }
     if constexpr (kAheadUg) {
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(NT, SEG == 16 ? 3 : 1) void bplane_kernel(BPlaneArg
       if (i < npix) {
         int r, c;
         smf[4 * lds_index(i, &r, &c) + 3] =
-            kAheadUg ? to_f32(ug_u[k]) * to_f32(ug_g[k]) : pl1(a.u, gbase + i) * pl1(a.gy, gbase + i);
+            KC > 1 ? to_f32(ug_u[k]) * to_f32(ug_g[k]) : pl1(a.u, gbase + i) * pl1(a.gy, gbase + i);
       }
     }
     __syncthreads();
