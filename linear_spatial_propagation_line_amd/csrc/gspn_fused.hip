@@ -177,43 +177,15 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
 #pragma unroll
     for (int t = 0; t < 5; ++t)
       fa[t] = *reinterpret_cast<const bf16x8*>(base + t * 1024 + r16 * 64 + 16 * (g ^ sw(r16)));
-    // B by transposing reads, written out with their wait: the compiler
-    // would otherwise wait for every load in flight into LDS before them,
-    // the stages ahead included
+    // B by transposing reads (rows + 4 are 2 KB further)
     const uint32_t so = static_cast<uint32_t>((st % kStages) * kStageBytes);
-    v4i16 tr[8];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]),
-          "=&v"(tr[6]), "=&v"(tr[7])
-        : "v"(tr_addr[0] + so), "v"(tr_addr[1] + so), "v"(tr_addr[2] + so), "v"(tr_addr[3] + so)
-        : "memory");
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i16 lo = tr[2 * j], hi = tr[2 * j + 1];
-      fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
-    }
+    const uint32_t q[4] = {tr_addr[0] + so, tr_addr[1] + so, tr_addr[2] + so, tr_addr[3] + so};
+    lds_read_tr_b4<2048>(q, fb);
 #pragma unroll
     for (int t = 0; t < 5; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb[j], acc[t][j], 0, 0, 0);
-  };
-  // a workgroup barrier that orders no memory by itself: the waits for the
-  // stage's loads are explicit, and the empty asm keeps the compiler from
-  // moving LDS accesses across it
-  auto stage_barrier = [] {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
   };
 
   // x of the group's channels, for lambda x: rows c0 - kx0 .. of the pixel
@@ -227,12 +199,12 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
     // this wave's loads of stage st are done when at most the next stage's
     // are in flight (vector memory loads complete in order)
     if (st + 1 < S) {
-      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
-      else           __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+      if (wave == 0) wait_vmcnt<6>();
+      else           wait_vmcnt<5>();
     } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      wait_vmcnt<0>();
     }
-    stage_barrier();   // ... and every wave's; stage st - 1 is no longer read
+    bare_barrier();   // ... and every wave's; stage st - 1 is no longer read
     if (st + 2 < S) issue(st + 2);
     multiply(st);
     if (st * kKT == kx0) {

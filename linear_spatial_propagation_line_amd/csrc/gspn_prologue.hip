@@ -458,29 +458,10 @@ __global__ __launch_bounds__(256, 2) void prologue_gemm_lds(GemmArgs<bf16_t> a) 
     for (int i = 0; i < MI; ++i)
       fa[i] = *reinterpret_cast<const bf16x8*>(base + (wm / 16 + i) * 1024 + r16 * 64 +
                                                16 * (g ^ sw(r16)));
-    // the transposing reads with their own wait: the compiler would wait for
-    // every load in flight into LDS before the builtin form
+    // the transposing reads (rows + 4 are 1 KB further)
     const uint32_t so = static_cast<uint32_t>((st % NS) * STAGE);
-    v4i16 tr[8];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]),
-          "=&v"(tr[6]), "=&v"(tr[7])
-        : "v"(tr_addr[0] + so), "v"(tr_addr[1] + so), "v"(tr_addr[2] + so), "v"(tr_addr[3] + so)
-        : "memory");
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i16 lo = tr[2 * j], hi = tr[2 * j + 1];
-      fb[j] = __builtin_bit_cast(bf16x8, v8i16{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
-    }
+    const uint32_t q[4] = {tr_addr[0] + so, tr_addr[1] + so, tr_addr[2] + so, tr_addr[3] + so};
+    lds_read_tr_b4<1024>(q, fb);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -494,21 +475,9 @@ __global__ __launch_bounds__(256, 2) void prologue_gemm_lds(GemmArgs<bf16_t> a) 
   for (int st = 0; st < S; ++st) {
     // this wave's loads of stage st are done when at most the later stages'
     // are in flight (vector memory loads complete in order)
-    const int later = (AH - 1 < S - 1 - st ? AH - 1 : S - 1 - st) * nld;
-    switch (later) {
-      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-      case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | 3); break;
-      case 4: __builtin_amdgcn_s_waitcnt(0x0F70 | 4); break;
-      case 6: __builtin_amdgcn_s_waitcnt(0x0F70 | 6); break;
-      case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
-      case 9: __builtin_amdgcn_s_waitcnt(0x0F70 | 9); break;
-      default: __builtin_amdgcn_s_waitcnt(0x0F70 | 12); break;
-    }
-    // every wave's loads of stage st are in, and stage st - 1 is no longer
-    // read; the empty asm keeps the compiler from moving LDS accesses across
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    wait_vmcnt_of((AH - 1 < S - 1 - st ? AH - 1 : S - 1 - st) * nld);
+    // every wave's loads of stage st are in, and stage st - 1 is no longer read
+    bare_barrier();
     if (st + AH < S) issue(st + AH);
     multiply(st);
   }
