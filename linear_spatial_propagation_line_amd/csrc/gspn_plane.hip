@@ -93,8 +93,9 @@ __global__ __launch_bounds__(256, SEG == 64 ? 2 : 1) void plane_kernel(PlaneArgs
   const int zero_off = eh_off + PPB * 2 * W;   // one zero record
   const int tid = threadIdx.x;
 
-  // registers filled one iteration ahead (VEC == 4 only)
-  typename V::raw rx[NIT], rl[NIT], r0[NIT], r1[NIT], r2[NIT], ru[NIT];
+  // registers filled one plane group ahead (VEC == 4 only); u only on
+  // 16-wide planes, 64-wide ones load it for the group at hand
+  typename V::raw rx[NIT], rl[NIT], r0[NIT], r1[NIT], r2[NIT], ru[SEG == 16 ? NIT : 1];
   // loads of 4-pixel vectors lo .. hi - 1 of plane group grp
   auto issue = [&](int64_t grp, int lo, int hi) {
     const int64_t gb = grp * PPB * HW;
