@@ -110,6 +110,15 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   const int r16 = lane & 15, rq = (lane >> 4) * 4;
   const bf16_t* X = a.x + b * static_cast<int64_t>(C) * N;
 
+  // the bias of the group's rows, loaded now so that the product hides it
+  // (without a bias, the weights stand in as a valid address, unused)
+  const bf16_t* bsrc = a.bp ? a.bp : a.wp;
+  bf16_t braw[5][4];
+#pragma unroll
+  for (int t = 0; t < 5; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) braw[t][e] = bsrc[t * C + c0 + rq + e];
+
   // ---- 1. the product -------------------------------------------------------
   f32x4 acc[5][4];
 #pragma unroll
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void fused_unit(FusedArgs a) {
   for (int t = 0; t < 5; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      bias[t][e] = a.bp ? to_f32(a.bp[t * C + c0 + rq + e]) : 0.0f;
+      bias[t][e] = a.bp ? to_f32(braw[t][e]) : 0.0f;
   float uu[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
