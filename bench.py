@@ -133,6 +133,7 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
           tp_vfwd  5 s inputs + (4 + 3 s) copy write + 4/8 checkpoints
           tp_hpair 2 (4 + 3 s) copy reads + 2 * 4/4 checkpoints + 4 sum write
           tp_vbwd  5 s inputs + 4/8 checkpoints + 4 sum read + s (u) + s (out)
+          (planes wider than 1024 take a checkpoint every 4 rows: 4/4)
           (shared logits, Cl < C: the logit part of the copy is 3 s Cl/C, made
           by tp_lgcopy over the B * Cl logit planes: 6 s per logit pixel)
     Backward pass:
@@ -197,16 +198,17 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     px = planes * w.H * w.W
     hz = bool(w.dirs & 12)
     sh = w.cl / w.C   # shared logits: the logit copy is made once per logit plane
+    ckv = (4 / 4 if w.W > 1024 else 4 / 8) if w.dirs & 1 else 0   # vertical checkpoints
     per = {
         "plane_kernel16": 7 * s,
         "plane_kernel64": 7 * s,
         "plane_pc_kernel": 7 * s,
         "stream_kernel": 5 * s + 4,
         "band_kernel": 12 * s,
-        "tp_vfwd": 5 * s + (4 + 3 * s * sh if hz else 0) + (0.5 if w.dirs & 1 else 0),
+        "tp_vfwd": 5 * s + (4 + 3 * s * sh if hz else 0) + ckv,
         "tp_hpair": 2 * (4 + 3 * s * sh) + 2.0 + 4,
         "tp_lgcopy": 6 * s * (w.B * w.C) / max(planes, 1) * sh,
-        "tp_vbwd": 5 * s + (0.5 if w.dirs & 1 else 0) + (4 if hz else 0) + 2 * s,
+        "tp_vbwd": 5 * s + ckv + (4 if hz else 0) + 2 * s,
         "bplane_kernel16": 13 * s,
         "bplane_kernel64": 13 * s,
         "bwd_fwd": 5 * s + 8,

@@ -116,7 +116,8 @@ Checked check_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask,
     r.plan = Plan::kTpipe;
     r.ws_bytes = gspn::tpipe_workspace_bytes(planes, H, W, dt);
   } else if ((any || f_tpipe_t) && gspn::tpipe_fits(W, H)) {
-    // the transposed plane fits the pipeline: it runs on transposed copies
+    // the pipeline on transposed copies; the pipeline's limits are symmetric,
+    // so this is reached only when forced (kept for comparison)
     r.plan = Plan::kTpipeT;
     r.ws_bytes = tpipe_t_workspace_bytes(planes, H, W, dt);
   } else if ((any || f_large) && !gspn::plane_fits(H, W) && H <= gspn::dirs_max_orth() &&

@@ -754,7 +754,8 @@ __global__ __launch_bounds__(512) void bt_vB(BtArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-bool btpipe_fits(int64_t H, int64_t W) { return tpipe_fits(H, W); }
+// a column pair per thread of the 512-thread row sweeps: W <= 1024
+bool btpipe_fits(int64_t H, int64_t W) { return tpipe_fits(H, W) && W <= 1024; }
 
 namespace {
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }

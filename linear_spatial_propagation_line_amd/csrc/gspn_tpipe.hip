@@ -1,5 +1,8 @@
 // Large-plane GSPN propagation ("transpose pipeline"), for planes above 64x64
-// with W <= 1024 and H <= 2048, both even.
+// with W <= 2048 and H <= 2048, both even. Planes up to 1024 wide run the row
+// sweeps (K1, K3) with 512 threads; wider ones with 1024 threads, smaller
+// per-thread buffers and 4-row chunks, so that the same pipeline serves the
+// portrait form of a latent without transposing it.
 //
 // A plane is too large for on-chip memory, and every scan step couples a whole
 // line (each pixel mixes its three predecessors), so one workgroup must own a
@@ -41,11 +44,23 @@ namespace gspn {
 
 namespace {
 
-constexpr int kCkV = 8;    // rows per vertical chunk / checkpoint interval
 constexpr int kCkH = 4;    // columns per horizontal chunk / checkpoint interval
-constexpr int kPf = 8;     // prefetch distance (steps) of the forward sweeps
-// K1 holds copy buffers as well: fp32 elements get a shorter prefetch ring
-template <typename T> constexpr int pf_rows() { return sizeof(T) == 2 ? 8 : 4; }
+
+// Shapes of the row sweeps (K1, K3) by workgroup size NT: 512 threads own up
+// to 1024 columns, 1024 threads up to 2048. At 1024 threads a thread has 128
+// registers, so its buffers are halved: copy runs of 64 bytes instead of 128,
+// a 4-row prefetch ring, and 4-row vertical chunks (which is also the
+// checkpoint interval of K1 and the chunk height of the horizontal sum).
+template <typename T, int NT> struct RowShape {
+  static constexpr bool kWide = NT > 512;
+  static constexpr int CKV = kWide ? 4 : 8;                          // rows per vertical chunk
+  static constexpr int PF = kWide ? 4 : (sizeof(T) == 2 ? 8 : 4);    // K1 prefetch distance
+  static constexpr int LXP = kWide ? 8 : 16;                         // lambda*x flush period
+  static constexpr int LGP = (kWide ? 64 : 128) / (2 * static_cast<int>(sizeof(T)));  // logits
+  static constexpr int MAXW = 2 * NT;                                // widest plane
+};
+// vertical chunk height for a plane of width W (the launcher's choice of NT)
+inline int row_chunk(int64_t W) { return W > 1024 ? 4 : 8; }
 
 // ---- storage access: pairs of adjacent elements --------------------------
 template <typename T> struct Pair;
@@ -194,10 +209,11 @@ struct TpArgs {
   T* out;
   float* lxt;     // [planes][W/2][Hp][2] lambda*x, column-major by column pairs
   T* lgt;         // [3][planes][W/2][Hp][2] logits, same layout
-  float* yht;     // [planes][nckv][W][8] h_L2R + h_R2L, in 8-row chunks
-  float* ckv;     // [planes][nckv][W] top->bottom states after rows 8k+7
+  float* yht;     // [planes][nckv][W][ckr] h_L2R + h_R2L, in ckr-row chunks
+  float* ckv;     // [planes][nckv][W] top->bottom states after rows ckr k + ckr - 1
   float* ckh;     // [planes][nckh][H] left->right states after columns 4k+3
   int H, W, G, Hp, nckv, nckh;
+  int ckr;        // rows per vertical chunk (8, or 4 for planes wider than 1024)
   unsigned mask;
   int64_t lg_stride;   // elements between the three logit copies
   int64_t plane0;      // first plane of this launch (blockIdx.x is relative)
@@ -214,13 +230,15 @@ struct TpArgs {
 // The main loop covers full 32-row blocks with straight-line code and
 // unconditional (row-clamped) loads so that the prefetch ring stays in flight;
 // a partial last block runs the same body with per-row guards.
-template <typename T, bool SCAN, bool COPY, bool COPYLG = COPY>
-__global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
-  __shared__ float lbuf[2 * (1024 + 4)];
-  constexpr int LGP = sizeof(T) == 2 ? 32 : 16;   // logit flush period (rows): 64 B
-  constexpr int LXP = 16;                         // lambda*x flush period: 64 B
+template <typename T, int NT, bool SCAN, bool COPY, bool COPYLG = COPY>
+__global__ __launch_bounds__(NT) void tp_vfwd(TpArgs<T> a) {
+  using S = RowShape<T, NT>;
+  __shared__ float lbuf[2 * (S::MAXW + 4)];
+  constexpr int LGP = S::LGP;                     // logit flush period (rows)
+  constexpr int LXP = S::LXP;                     // lambda*x flush period (rows)
   constexpr int U = 32;                           // unroll (multiple of both periods)
-  constexpr int PF = sizeof(T) == 2 ? 8 : 4;      // prefetch distance (rows)
+  constexpr int PF = S::PF;                       // prefetch distance (rows)
+  constexpr int CKV = S::CKV;                     // checkpoint interval (rows)
   using P = Pair<T>;
   const int H = a.H, W = a.W, G = a.G;
   const int t = threadIdx.x;
@@ -274,8 +292,8 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
           hB = restart ? lxb : nb;
           if (act) *reinterpret_cast<float2*>(lx.nxt() + c0 + 2) = make_float2(hA, hB);
           lx.par ^= 1;
-          if ((j + 1) % kCkV == 0 && act)
-            store_pair(a.ckv, (plane * a.nckv + r / kCkV) * W + c0, hA, hB);
+          if ((j + 1) % CKV == 0 && act)
+            store_pair(a.ckv, (plane * a.nckv + r / CKV) * W + c0, hA, hB);
           __syncthreads();
         }
         if constexpr (COPY) lxP[j % LXP] = make_float2(lxa, lxb);
@@ -286,9 +304,10 @@ __global__ __launch_bounds__(512) void tp_vfwd(TpArgs<T> a) {
         }
       }
       if constexpr (COPY) {
-        // flush whole 128-byte runs (16 rows of lambda*x pairs, 32 rows of
-        // bf16 logit pairs or 16 of fp32); the row pitch Hp is a multiple of
-        // 32, so a run that passes H lands in padding
+        // flush whole runs (128 bytes at 512 threads: 16 rows of lambda*x
+        // pairs, 32 rows of bf16 logit pairs or 16 of fp32; 64 bytes at
+        // 1024); the row pitch Hp is a multiple of 32, so a run that passes H
+        // lands in padding
         if ((j % LXP) == LXP - 1 && act && (!TAIL || r0 + j - (LXP - 1) < H)) {
           const int rs = r0 + j - (LXP - 1);
           float4* d = reinterpret_cast<float4*>(a.lxt + pbase + 2 * rs);
@@ -377,7 +396,6 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
   const bool act = o0 < H;
   const int ol = act ? o0 : 0;
   const int64_t plane = a.plane0 + blockIdx.x;
-  const int64_t pb = plane * W * Hp;    // this plane in the copy
   const int n4 = H + 4;
   for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
   __syncthreads();
@@ -418,11 +436,12 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
     Q::split(v.g2, odd, c.g2);
     return c;
   };
-  // the horizontal sum is stored in 8-row chunks, [plane][row / 8][column][8],
-  // so that the bottom->top kernel reads whole chunks contiguously
-  auto yidx = [&](int c) {
-    return ((plane * a.nckv + o0 / 8) * W + c) * 8 + (o0 % 8);
-  };
+  // the horizontal sum is stored in chunks of ckr rows,
+  // [plane][row / ckr][column][ckr], so that the bottom->top kernel reads
+  // whole chunks contiguously
+  const int ckr = a.ckr;
+  const int64_t ychunk = plane * a.nckv + o0 / ckr, yoff = o0 % ckr;
+  auto yidx = [&](int c) { return (ychunk * W + c) * ckr + yoff; };
   auto recs = [&](const In& v, Rec& ra, Rec& rb) {
     ra = make_rec(v.g0[0], v.g1[0], v.g2[0], v.lx.x, mA0, 1.f);
     rb = make_rec(v.g0[1], v.g1[1], v.g2[1], v.lx.y, 1.f, mB2);
@@ -549,9 +568,11 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
 // ===========================================================================
 // K3: bottom->top with top->bottom recomputed per chunk, merge, output
 // ===========================================================================
-template <typename T, bool TB, bool BT, bool HZ>
-__global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
-  __shared__ float lbuf[2 * (1024 + 4)];
+template <typename T, int NT, bool TB, bool BT, bool HZ>
+__global__ __launch_bounds__(NT) void tp_vbwd(TpArgs<T> a) {
+  using S = RowShape<T, NT>;
+  constexpr int kCkV = S::CKV;
+  __shared__ float lbuf[2 * (S::MAXW + 4)];
   using P = Pair<T>;
   const int H = a.H, W = a.W, G = a.G, Hp = a.Hp;
   const int t = threadIdx.x;
@@ -571,7 +592,7 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
   struct Chunk {
     Raw2<T> in[kCkV];
     typename P::raw u[kCkV];
-    float4 yA[2], yB[2];
+    float4 yA[kCkV / 4], yB[kCkV / 4];
     float2 ck;
   };
   auto load_chunk = [&](int k) {
@@ -583,15 +604,17 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
       ch.in[i] = load_raw2(a.x, a.lam, a.l0, a.l1, a.l2, idx, ls);
       ch.u[i] = P::load(a.u, idx);
     }
-    if constexpr (HZ) {
-      // rows rs..rs+7 of columns c0, c0+1: 64 contiguous bytes
-      const float4* y = reinterpret_cast<const float4*>(a.yht + ((plane * a.nckv + k) * W + cl) * 8);
-      ch.yA[0] = y[0];
-      ch.yA[1] = y[1];
-      ch.yB[0] = y[2];
-      ch.yB[1] = y[3];
-    } else {
-      ch.yA[0] = ch.yA[1] = ch.yB[0] = ch.yB[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < kCkV / 4; ++q) {
+      if constexpr (HZ) {
+        // the chunk's rows of columns c0, c0+1: 8 kCkV contiguous bytes
+        const float4* y =
+            reinterpret_cast<const float4*>(a.yht + ((plane * a.nckv + k) * W + cl) * kCkV);
+        ch.yA[q] = y[q];
+        ch.yB[q] = y[kCkV / 4 + q];
+      } else {
+        ch.yA[q] = ch.yB[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     ch.ck = make_float2(0.f, 0.f);
     if constexpr (TB)
@@ -678,7 +701,7 @@ __global__ __launch_bounds__(512) void tp_vbwd(TpArgs<T> a) {
 
 // ---------------------------------------------------------------------------
 bool tpipe_fits(int64_t H, int64_t W) {
-  return H >= 2 && W >= 2 && H % 2 == 0 && W % 2 == 0 && W <= 1024 && H <= 2048;
+  return H >= 2 && W >= 2 && H % 2 == 0 && W % 2 == 0 && W <= 2048 && H <= 2048;
 }
 
 namespace {
@@ -691,14 +714,15 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 TpLayout tp_layout(int64_t planes, int64_t H, int64_t W, size_t es) {
   TpLayout L;
+  const int ckr = row_chunk(W);
   L.Hp = (H + 31) / 32 * 32;
-  L.nckv = (H + kCkV - 1) / kCkV;
+  L.nckv = (H + ckr - 1) / ckr;
   L.nckh = (W + kCkH - 1) / kCkH;
   const size_t cp = static_cast<size_t>(planes * W * L.Hp);
   size_t o = 0;
   L.off_lxt = o; o = align256(o + cp * 4);
   L.off_lgt = o; o = align256(o + 3 * cp * es);
-  L.off_yht = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * 8 * 4);
+  L.off_yht = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * ckr * 4);
   L.off_ckv = o; o = align256(o + static_cast<size_t>(planes * L.nckv * W) * 4);
   L.off_ckh = o; o = align256(o + static_cast<size_t>(planes * L.nckh * H) * 4);
   L.total = o;
@@ -710,8 +734,8 @@ size_t tpipe_workspace_bytes(int64_t planes, int64_t H, int64_t W, gspn_dtype dt
   return tp_layout(planes, H, W, dt == GSPN_F32 ? 4 : 2).total;
 }
 
-template <typename T>
-static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+template <typename T, int NT>
+static hipError_t launch_tpipe_nt(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
   const int64_t planes = pr.B * pr.C;
   const TpLayout L = tp_layout(planes, pr.H, pr.W, sizeof(T));
   char* w = static_cast<char*>(ws);
@@ -734,6 +758,7 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   a.Hp = static_cast<int>(L.Hp);
   a.nckv = static_cast<int>(L.nckv);
   a.nckh = static_cast<int>(L.nckh);
+  a.ckr = RowShape<T, NT>::CKV;
   a.mask = pr.mask;
   a.C = pr.C;
   a.Cl = pr.Cl;
@@ -745,15 +770,15 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   const bool tb = m & 1u, bt = m & 2u, lr = m & 4u, rl = m & 8u, hz = lr || rl;
   using K = void (*)(TpArgs<T>);
   const bool shared = pr.Cl < pr.C;
-  const K k1 = shared ? (tb ? (hz ? tp_vfwd<T, true, true, false> : tp_vfwd<T, true, false, false>)
-                            : tp_vfwd<T, false, true, false>)
-                      : (tb ? (hz ? tp_vfwd<T, true, true> : tp_vfwd<T, true, false>)
-                            : tp_vfwd<T, false, true>);
+  const K k1 = shared ? (tb ? (hz ? tp_vfwd<T, NT, true, true, false> : tp_vfwd<T, NT, true, false, false>)
+                            : tp_vfwd<T, NT, false, true, false>)
+                      : (tb ? (hz ? tp_vfwd<T, NT, true, true> : tp_vfwd<T, NT, true, false>)
+                            : tp_vfwd<T, NT, false, true>);
   const K k2 = lr ? (rl ? tp_hpair<T, true, true> : tp_hpair<T, true, false>) : tp_hpair<T, false, true>;
-  static const K k3s[8] = {tp_vbwd<T, false, false, false>, tp_vbwd<T, true, false, false>,
-                           tp_vbwd<T, false, true, false>, tp_vbwd<T, true, true, false>,
-                           tp_vbwd<T, false, false, true>, tp_vbwd<T, true, false, true>,
-                           tp_vbwd<T, false, true, true>, tp_vbwd<T, true, true, true>};
+  static const K k3s[8] = {tp_vbwd<T, NT, false, false, false>, tp_vbwd<T, NT, true, false, false>,
+                           tp_vbwd<T, NT, false, true, false>, tp_vbwd<T, NT, true, true, false>,
+                           tp_vbwd<T, NT, false, false, true>, tp_vbwd<T, NT, true, false, true>,
+                           tp_vbwd<T, NT, false, true, true>, tp_vbwd<T, NT, true, true, true>};
   const K k3 = k3s[(tb ? 1 : 0) | (bt ? 2 : 0) | (hz ? 4 : 0)];
 
   // Every kernel needs one whole compute unit per plane, so a plane count a
@@ -819,6 +844,14 @@ static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t strea
   }
   release();
   return e;
+}
+
+template <typename T>
+static hipError_t launch_tpipe_dt(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {
+  // the row sweeps take a column pair per thread: 512 threads up to 1024
+  // columns, 1024 threads beyond (row_chunk() gives the matching chunk height)
+  return pr.W > 1024 ? launch_tpipe_nt<T, 1024>(pr, ws, stream, tr)
+                     : launch_tpipe_nt<T, 512>(pr, ws, stream, tr);
 }
 
 hipError_t launch_tpipe(const Problem& pr, void* ws, hipStream_t stream, Tracer* tr) {

@@ -116,8 +116,11 @@ def test_workspace_and_plans(L, monkeypatch):
     assert g.plan_name(16, 192, 128, 128, group_rows=0) == "tpipe"
     assert g.plan_name(16, 192, 128, 128, group_rows=17) == "tpipe"   # groups above 16
     assert g.plan_name(1, 1, 512, 512, group_rows=8) == "tpipe"       # y_V too big for LDS
-    assert g.plan_name(1, 1, 100, 2048) == "tpipe_t"      # W above the pair-kernel limit:
-    assert g.plan_name(1, 320, 1024, 2048, dtype=1) == "tpipe_t"   # the transposed plane fits
+    assert g.plan_name(1, 1, 100, 2048) == "tpipe"        # W above 1024: 1024-thread row sweeps
+    assert g.plan_name(1, 320, 1024, 2048, dtype=1) == "tpipe"     # the portrait latent
+    assert g.plan_name(1, 1, 2048, 2048, dtype=1) == "tpipe"
+    assert g.plan_name(1, 1, 100, 2050) == "large"        # W above 2048: transposed copies
+    assert g.plan_name(1, 1, 2050, 100) == "large"        # H above 2048
     assert g.plan_name(1, 4, 2047, 1023, dtype=1) == "large"  # odd sides: transposed copies
     assert g.plan_name(1, 1, 3001, 9, dtype=1) == "stream"    # small plane, odd
     assert g.plan_name(1, 1, 20000, 4) == "invalid"
