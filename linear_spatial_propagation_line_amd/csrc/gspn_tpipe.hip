@@ -46,19 +46,47 @@ namespace {
 
 constexpr int kCkH = 4;    // columns per horizontal chunk / checkpoint interval
 
+// The column-major copy K1 writes and K2 reads holds the columns of a plane
+// in quads: [plane][ceil(W / 4)][Hp][4], so a 128-byte line is 8 rows of
+// four lambda*x values (16 rows of four bf16 logits). The two threads that
+// own a quad's column pairs swap half their buffered rows (a DPP move within
+// the lane pair) and then each writes 64 contiguous bytes: together one
+// whole line in the same four stores.
+//
 // Shapes of the row sweeps (K1, K3) by workgroup size NT: 512 threads own up
 // to 1024 columns, 1024 threads up to 2048. At 1024 threads a thread has 128
-// registers, so its buffers are halved: copy runs of 64 bytes instead of 128,
-// a 4-row prefetch ring, and 4-row vertical chunks (which is also the
-// checkpoint interval of K1 and the chunk height of the horizontal sum).
+// registers, so the prefetch ring is 4 rows deep and the vertical chunks 4
+// rows high (which is also the checkpoint interval of K1 and the chunk height
+// of the horizontal sum).
 template <typename T, int NT> struct RowShape {
   static constexpr bool kWide = NT > 512;
   static constexpr int CKV = kWide ? 4 : 8;                          // rows per vertical chunk
   static constexpr int PF = kWide ? 4 : (sizeof(T) == 2 ? 8 : 4);    // K1 prefetch distance
-  static constexpr int LXP = kWide ? 8 : 16;                         // lambda*x flush period
-  static constexpr int LGP = (kWide ? 64 : 128) / (2 * static_cast<int>(sizeof(T)));  // logits
+  static constexpr int LXP = 8;                                      // lambda*x rows per line
+  static constexpr int LGP = 128 / (4 * static_cast<int>(sizeof(T)));   // logit rows per line
   static constexpr int MAXW = 2 * NT;                                // widest plane
 };
+
+// the value held by the other lane of an adjacent lane pair (2i, 2i + 1)
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float pair_swap(float v) {
+  return __uint_as_float(pair_swap(__float_as_uint(v)));
+}
+__device__ __forceinline__ float2 pair_swap(float2 v) {
+  return make_float2(pair_swap(v.x), pair_swap(v.y));
+}
+// rows k of the even lane and k + n / 2 of the odd lane, both as the quad's
+// four values: the even lane's pair first
+template <typename R>
+__device__ __forceinline__ void quad_rows(const R* buf, int n, int k, bool odd, R* lo, R* hi) {
+  const R keep = odd ? buf[k + n / 2] : buf[k];
+  const R got = pair_swap(odd ? buf[k] : buf[k + n / 2]);
+  *lo = odd ? got : keep;
+  *hi = odd ? keep : got;
+}
 // vertical chunk height for a plane of width W (the launcher's choice of NT)
 inline int row_chunk(int64_t W) { return W > 1024 ? 4 : 8; }
 
@@ -81,27 +109,31 @@ template <> struct Pair<bf16_t> {
   __device__ static float hi(raw v) { return bf16_hi(v); }
 };
 
-// four elements (rows o, o+1 of a column pair) of the copy
+// rows o, o + 1 of a column quad of the copy: 4 values per row
 template <typename T> struct Quad;
 template <> struct Quad<float> {
-  using raw = float4;
+  struct raw {
+    float4 r0, r1;
+  };
   __device__ static raw load(const float* p, int64_t i) {
-    return *reinterpret_cast<const float4*>(p + i);
+    const float4* q = reinterpret_cast<const float4*>(p + i);
+    return raw{q[0], q[1]};
   }
-  // values of column `odd` of the pair for the two rows
-  __device__ static void split(raw v, int odd, float out[2]) {
-    out[0] = odd ? v.y : v.x;
-    out[1] = odd ? v.w : v.z;
+  // column c (0..3) of the quad for the two rows
+  __device__ static void col(const raw& v, int c, float out[2]) {
+    out[0] = c == 0 ? v.r0.x : (c == 1 ? v.r0.y : (c == 2 ? v.r0.z : v.r0.w));
+    out[1] = c == 0 ? v.r1.x : (c == 1 ? v.r1.y : (c == 2 ? v.r1.z : v.r1.w));
   }
 };
 template <> struct Quad<bf16_t> {
-  using raw = uint2;
+  using raw = uint4;   // row o: x (columns 0, 1), y (2, 3); row o + 1: z, w
   __device__ static raw load(const bf16_t* p, int64_t i) {
-    return *reinterpret_cast<const uint2*>(p + i);
+    return *reinterpret_cast<const uint4*>(p + i);
   }
-  __device__ static void split(raw v, int odd, float out[2]) {
-    out[0] = odd ? bf16_hi(v.x) : bf16_lo(v.x);
-    out[1] = odd ? bf16_hi(v.y) : bf16_lo(v.y);
+  __device__ static void col(const raw& v, int c, float out[2]) {
+    const uint32_t a = c < 2 ? v.x : v.y, b = c < 2 ? v.z : v.w;
+    out[0] = (c & 1) ? bf16_hi(a) : bf16_lo(a);
+    out[1] = (c & 1) ? bf16_hi(b) : bf16_lo(b);
   }
 };
 
@@ -207,12 +239,13 @@ struct TpArgs {
   const T* l2;
   const T* u;
   T* out;
-  float* lxt;     // [planes][W/2][Hp][2] lambda*x, column-major by column pairs
-  T* lgt;         // [3][planes][W/2][Hp][2] logits, same layout
+  float* lxt;     // [planes][Wq][Hp][4] lambda*x, column-major by column quads
+  T* lgt;         // [3][planes][Wq][Hp][4] logits, same layout
   float* yht;     // [planes][nckv][W][ckr] h_L2R + h_R2L, in ckr-row chunks
   float* ckv;     // [planes][nckv][W] top->bottom states after rows ckr k + ckr - 1
   float* ckh;     // [planes][nckh][H] left->right states after columns 4k+3
   int H, W, G, Hp, nckv, nckh;
+  int Wq;         // column quads of the copy, ceil(W / 4)
   int ckr;        // rows per vertical chunk (8, or 4 for planes wider than 1024)
   unsigned mask;
   int64_t lg_stride;   // elements between the three logit copies
@@ -264,12 +297,18 @@ __global__ __launch_bounds__(NT) void tp_vfwd(TpArgs<T> a) {
 
   float hA = 0.f, hB = 0.f;
   FwdRestart rst{0, G};
-  // copy buffers, kept in the copy's pair-interleaved layout: per row, the
-  // values of columns c0 and c0+1 side by side
+  // copy buffers: per row, the values of columns c0 and c0 + 1
   float2 lxP[LXP];
   typename P::raw lgP[3][LGP];
-  // this thread's column pair in the copy ([plane][W/2][Hp][2])
-  const int64_t pbase = ((plane * (W / 2) + t) * a.Hp) * 2;
+#pragma unroll
+  for (int k = 0; k < LXP; ++k) lxP[k] = make_float2(0.f, 0.f);   // rows past H: padding
+#pragma unroll
+  for (int k = 0; k < LGP; ++k) lgP[0][k] = lgP[1][k] = lgP[2][k] = typename P::raw{};
+  // this thread's quad in the copy; the odd lane of the pair writes the
+  // second half of each line
+  const bool odd = t & 1;
+  const bool qact = 2 * (t & ~1) < W;             // the quad holds a column of the plane
+  const int64_t qbase = ((plane * a.Wq + t / 2) * a.Hp) * 4;
 
   auto block = [&](int r0, auto tail) {
     constexpr bool TAIL = decltype(tail)::value;
@@ -304,34 +343,53 @@ __global__ __launch_bounds__(NT) void tp_vfwd(TpArgs<T> a) {
         }
       }
       if constexpr (COPY) {
-        // flush whole runs (128 bytes at 512 threads: 16 rows of lambda*x
-        // pairs, 32 rows of bf16 logit pairs or 16 of fp32; 64 bytes at
-        // 1024); the row pitch Hp is a multiple of 32, so a run that passes H
-        // lands in padding
-        if ((j % LXP) == LXP - 1 && act && (!TAIL || r0 + j - (LXP - 1) < H)) {
+        // a whole line of lambda*x quads (8 rows) per lane pair; every lane
+        // takes part in the swap, and a line that passes H lands in the
+        // padding (Hp is a multiple of 32)
+        if ((j % LXP) == LXP - 1 && (!TAIL || r0 + j - (LXP - 1) < H)) {
           const int rs = r0 + j - (LXP - 1);
-          float4* d = reinterpret_cast<float4*>(a.lxt + pbase + 2 * rs);
+          float4 o[LXP / 2];
 #pragma unroll
-          for (int q = 0; q < LXP / 2; ++q)
-            d[q] = make_float4(lxP[2 * q].x, lxP[2 * q].y, lxP[2 * q + 1].x, lxP[2 * q + 1].y);
+          for (int k = 0; k < LXP / 2; ++k) {
+            float2 lo, hi;
+            quad_rows(lxP, LXP, k, odd, &lo, &hi);
+            o[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+          }
+          if (qact) {
+            float4* d = reinterpret_cast<float4*>(a.lxt + qbase + 4 * (rs + (odd ? LXP / 2 : 0)));
+#pragma unroll
+            for (int k = 0; k < LXP / 2; ++k) d[k] = o[k];
+          }
         }
       }
       if constexpr (COPYLG) {
-        if ((j % LGP) == LGP - 1 && act && (!TAIL || r0 + j - (LGP - 1) < H)) {
+        if ((j % LGP) == LGP - 1 && (!TAIL || r0 + j - (LGP - 1) < H)) {
           const int rs = r0 + j - (LGP - 1);
 #pragma unroll
           for (int z = 0; z < 3; ++z) {
-            T* g = a.lgt + z * a.lg_stride + pbase + 2 * rs;
+            T* g = a.lgt + z * a.lg_stride + qbase + 4 * (rs + (odd ? LGP / 2 : 0));
             if constexpr (sizeof(T) == 2) {
-              uint4* d = reinterpret_cast<uint4*>(g);
+              uint32_t o[LGP];   // per row: columns 4q, 4q+1 then 4q+2, 4q+3
 #pragma unroll
-              for (int q = 0; q < LGP / 4; ++q)
-                d[q] = make_uint4(lgP[z][4 * q], lgP[z][4 * q + 1], lgP[z][4 * q + 2], lgP[z][4 * q + 3]);
+              for (int k = 0; k < LGP / 2; ++k) quad_rows(lgP[z], LGP, k, odd, &o[2 * k], &o[2 * k + 1]);
+              if (qact) {
+                uint4* d = reinterpret_cast<uint4*>(g);
+#pragma unroll
+                for (int k = 0; k < LGP / 4; ++k) d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+              }
             } else {
-              float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
+              float4 o[LGP / 2];
 #pragma unroll
-              for (int q = 0; q < LGP / 2; ++q)
-                d[q] = make_float4(lgP[z][2 * q].x, lgP[z][2 * q].y, lgP[z][2 * q + 1].x, lgP[z][2 * q + 1].y);
+              for (int k = 0; k < LGP / 2; ++k) {
+                float2 lo, hi;
+                quad_rows(lgP[z], LGP, k, odd, &lo, &hi);
+                o[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+              }
+              if (qact) {
+                float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
+#pragma unroll
+                for (int k = 0; k < LGP / 2; ++k) d[k] = o[k];
+              }
             }
           }
         }
@@ -344,39 +402,46 @@ __global__ __launch_bounds__(NT) void tp_vfwd(TpArgs<T> a) {
 }
 
 // Shared logits: the column-major logit copy of the B * Cl logit planes, one
-// thread per (logit plane, 32-row block, column pair), column pair fastest so
-// that the row loads coalesce; each thread writes whole 32-row runs.
+// thread per (logit plane, 16-row block, column quad), quad fastest so that
+// the row loads coalesce; each thread writes whole 16-row runs of its quad.
 template <typename T>
 __global__ __launch_bounds__(256) void tp_lgcopy(TpArgs<T> a, int64_t nlp) {
   using P = Pair<T>;
-  const int H = a.H, W = a.W, Hp = a.Hp;
-  const int npairs = W / 2, nblk = Hp / 32;
-  const int64_t total = nlp * npairs * nblk;
+  constexpr int RB = 16;                    // rows per thread
+  const int H = a.H, W = a.W, Hp = a.Hp, Wq = a.Wq;
+  const int nblk = Hp / RB;
+  const int64_t total = nlp * Wq * nblk;
   for (int64_t t = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; t < total;
        t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int cp = static_cast<int>(t % npairs);
-    const int64_t rest = t / npairs;
+    const int qd = static_cast<int>(t % Wq);
+    const int64_t rest = t / Wq;
     const int blk = static_cast<int>(rest % nblk);
     const int64_t lp = rest / nblk;
-    const int r0 = blk * 32;
-    const int64_t src = lp * H * W + 2 * cp;
-    const int64_t dst = ((lp * npairs + cp) * Hp + r0) * 2;
+    const int r0 = blk * RB;
+    // the quad's two column pairs (the second one clamped: with W % 4 == 2
+    // the last quad's second pair is padding)
+    const int64_t srcA = lp * H * W + 4 * qd;
+    const int64_t srcB = lp * H * W + min(4 * qd + 2, W - 2);
+    const int64_t dst = ((lp * Wq + qd) * Hp + r0) * 4;
     const T* ls[3] = {a.l0, a.l1, a.l2};
 #pragma unroll
     for (int z = 0; z < 3; ++z) {
-      typename P::raw v[32];
+      typename P::raw va[RB], vb[RB];
 #pragma unroll
-      for (int j = 0; j < 32; ++j)   // rows past H land in the copy's padding
-        v[j] = P::load(ls[z], src + static_cast<int64_t>(min(r0 + j, H - 1)) * W);
+      for (int j = 0; j < RB; ++j) {   // rows past H land in the copy's padding
+        const int64_t ro = static_cast<int64_t>(min(r0 + j, H - 1)) * W;
+        va[j] = P::load(ls[z], srcA + ro);
+        vb[j] = P::load(ls[z], srcB + ro);
+      }
       T* g = a.lgt + z * a.lg_stride + dst;
       if constexpr (sizeof(T) == 2) {
         uint4* d = reinterpret_cast<uint4*>(g);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) d[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int q = 0; q < RB / 2; ++q) d[q] = make_uint4(va[2 * q], vb[2 * q], va[2 * q + 1], vb[2 * q + 1]);
       } else {
         float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
 #pragma unroll
-        for (int q = 0; q < 16; ++q) d[q] = make_float4(v[2 * q].x, v[2 * q].y, v[2 * q + 1].x, v[2 * q + 1].y);
+        for (int q = 0; q < RB; ++q) d[q] = make_float4(va[q].x, va[q].y, vb[q].x, vb[q].y);
       }
     }
   }
@@ -403,38 +468,41 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
   const float mA0 = o0 > 0 ? 1.f : 0.f;
   const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
 
-  // One load covers rows o0, o0+1 of the column pair (2 cp, 2 cp + 1): the
-  // copy stores, per row, both columns of a pair side by side.
+  // One load covers rows o0, o0 + 1 of a column quad (columns 4 qd ..
+  // 4 qd + 3): 32 contiguous bytes of lambda*x, 16 (bf16) or 32 of each logit.
   using Q = Quad<T>;
-  struct In2 {
-    float4 lx;                          // (o0: even, odd), (o0+1: even, odd)
+  struct In4 {
+    Quad<float>::raw lx;
     typename Q::raw g0, g1, g2;
   };
+  const int Wq = a.Wq;
   // the logit copy of this plane (shared logits: of its logit plane)
   const int64_t lgpl = plane + logit_shift(plane, a.C, a.Cl, 1);
-  auto load_pair = [&](int cp) {
-    In2 v;
-    const int64_t cc = min(max(cp, 0), W / 2 - 1);
-    const int64_t i = ((plane * (W / 2) + cc) * Hp + ol) * 2;
-    const int64_t il = ((lgpl * (W / 2) + cc) * Hp + ol) * 2;
-    v.lx = *reinterpret_cast<const float4*>(a.lxt + i);
+  auto load_quad = [&](int qd) {
+    In4 v;
+    const int64_t qq = min(max(qd, 0), Wq - 1);
+    const int64_t i = ((plane * Wq + qq) * Hp + ol) * 4;
+    const int64_t il = ((lgpl * Wq + qq) * Hp + ol) * 4;
+    v.lx = Quad<float>::load(a.lxt, i);
     v.g0 = Q::load(a.lgt, il);
     v.g1 = Q::load(a.lgt + a.lg_stride, il);
     v.g2 = Q::load(a.lgt + 2 * a.lg_stride, il);
     return v;
   };
-  // the column (odd = 0: even column of the pair, 1: odd) as a per-row view
+  // column c (0..3) of the quad as a per-row view
   struct In {
     float2 lx;
     float g0[2], g1[2], g2[2];
   };
-  auto column = [&](const In2& v, int odd) {
-    In c;
-    c.lx = odd ? make_float2(v.lx.y, v.lx.w) : make_float2(v.lx.x, v.lx.z);
-    Q::split(v.g0, odd, c.g0);
-    Q::split(v.g1, odd, c.g1);
-    Q::split(v.g2, odd, c.g2);
-    return c;
+  auto column = [&](const In4& v, int c) {
+    In cc;
+    float l[2];
+    Quad<float>::col(v.lx, c, l);
+    cc.lx = make_float2(l[0], l[1]);
+    Q::col(v.g0, c, cc.g0);
+    Q::col(v.g1, c, cc.g1);
+    Q::col(v.g2, c, cc.g2);
+    return cc;
   };
   // the horizontal sum is stored in chunks of ckr rows,
   // [plane][row / ckr][column][ckr], so that the bottom->top kernel reads
@@ -466,31 +534,33 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
 
   // ---- left->right: checkpoints, or the final sum when there is no reverse
   if constexpr (LR) {
-    constexpr int PP = PF / 2;            // column pairs in flight
-    In2 ring[PP];
+    constexpr int PQ = PF / 4;            // column quads in flight
+    In4 ring[PQ];
 #pragma unroll
-    for (int j = 0; j < PP; ++j) ring[j] = load_pair(j);
+    for (int j = 0; j < PQ; ++j) ring[j] = load_quad(j);
     float hA = 0.f, hB = 0.f;
     FwdRestart rst{0, G};
     auto block = [&](int cb, auto tail) {
       constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
-      for (int j = 0; j < PP; ++j) {
-        const int cp = cb / 2 + j;
-        if (!TAIL || 2 * cp < W) {
-          const In2 v2 = ring[j];
-          ring[j] = load_pair(cp + PP);
+      for (int j = 0; j < PQ; ++j) {
+        const int qd = cb / 4 + j;
+        if (!TAIL || 4 * qd < W) {
+          const In4 v4 = ring[j];
+          ring[j] = load_quad(qd + PQ);
 #pragma unroll
-          for (int odd = 0; odd < 2; ++odd) {
-            const int c = 2 * cp + odd;
-            Rec ra, rb;
-            recs(column(v2, odd), ra, rb);
-            step(ra, rb, rst.at(c), hA, hB);
-            if (act) {
-              if constexpr (RL) {
-                if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
-              } else {
-                store_pair(a.yht, yidx(c), hA, hB);
+          for (int i = 0; i < 4; ++i) {
+            const int c = 4 * qd + i;
+            if (!TAIL || c < W) {   // the last quad of W % 4 == 2 holds two columns
+              Rec ra, rb;
+              recs(column(v4, i), ra, rb);
+              step(ra, rb, rst.at(c), hA, hB);
+              if (act) {
+                if constexpr (RL) {
+                  if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
+                } else {
+                  store_pair(a.yht, yidx(c), hA, hB);
+                }
               }
             }
           }
@@ -504,14 +574,14 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
 
   // ---- right->left in chunks of kCkH columns, recomputing left->right -----
   if constexpr (RL) {
+    static_assert(kCkH == 4, "a right->left chunk is one column quad of the copy");
     struct Chunk {
-      In2 in[kCkH / 2];
+      In4 in;
       float2 ck;
     };
     auto load_chunk = [&](int k) {
       Chunk ch;
-#pragma unroll
-      for (int i = 0; i < kCkH / 2; ++i) ch.in[i] = load_pair(k * (kCkH / 2) + i);
+      ch.in = load_quad(k);
       ch.ck = make_float2(0.f, 0.f);
       if constexpr (LR)
         ch.ck = *reinterpret_cast<const float2*>(a.ckh + (plane * a.nckh + max(k - 1, 0)) * H + ol);
@@ -523,7 +593,7 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
       const int cs = k * kCkH;
       Rec ra[kCkH], rb[kCkH];
 #pragma unroll
-      for (int i = 0; i < kCkH; ++i) recs(column(ch.in[i / 2], i % 2), ra[i], rb[i]);
+      for (int i = 0; i < kCkH; ++i) recs(column(ch.in, i), ra[i], rb[i]);
       float hlA[kCkH], hlB[kCkH];
 #pragma unroll
       for (int i = 0; i < kCkH; ++i) { hlA[i] = 0.f; hlB[i] = 0.f; }
@@ -706,7 +776,7 @@ bool tpipe_fits(int64_t H, int64_t W) {
 
 namespace {
 struct TpLayout {
-  int64_t Hp, nckv, nckh;
+  int64_t Hp, Wq, nckv, nckh;
   size_t off_lxt, off_lgt, off_yht, off_ckv, off_ckh, total;
 };
 
@@ -716,9 +786,10 @@ TpLayout tp_layout(int64_t planes, int64_t H, int64_t W, size_t es) {
   TpLayout L;
   const int ckr = row_chunk(W);
   L.Hp = (H + 31) / 32 * 32;
+  L.Wq = (W + 3) / 4;
   L.nckv = (H + ckr - 1) / ckr;
   L.nckh = (W + kCkH - 1) / kCkH;
-  const size_t cp = static_cast<size_t>(planes * W * L.Hp);
+  const size_t cp = static_cast<size_t>(planes * 4 * L.Wq * L.Hp);   // elements of one copy
   size_t o = 0;
   L.off_lxt = o; o = align256(o + cp * 4);
   L.off_lgt = o; o = align256(o + 3 * cp * es);
@@ -758,11 +829,12 @@ static hipError_t launch_tpipe_nt(const Problem& pr, void* ws, hipStream_t strea
   a.Hp = static_cast<int>(L.Hp);
   a.nckv = static_cast<int>(L.nckv);
   a.nckh = static_cast<int>(L.nckh);
+  a.Wq = static_cast<int>(L.Wq);
   a.ckr = RowShape<T, NT>::CKV;
   a.mask = pr.mask;
   a.C = pr.C;
   a.Cl = pr.Cl;
-  a.lg_stride = planes * pr.W * L.Hp;
+  a.lg_stride = planes * 4 * L.Wq * L.Hp;
   a.plane0 = 0;
   const unsigned tv = static_cast<unsigned>((pr.W / 2 + 63) / 64 * 64);
   const unsigned th = static_cast<unsigned>((pr.H / 2 + 63) / 64 * 64);
@@ -791,7 +863,7 @@ static hipError_t launch_tpipe_nt(const Problem& pr, void* ws, hipStream_t strea
   if (shared && hz) {
     // the logit copy of each of the B * Cl logit planes, before any K2
     const int64_t nlp = pr.B * pr.Cl;
-    const int64_t work = nlp * (pr.W / 2) * (L.Hp / 32);
+    const int64_t work = nlp * L.Wq * (L.Hp / 16);
     const int64_t blocks = (work + 255) / 256;
     tr->before(stream, "tp_lgcopy", nlp);
     hipLaunchKernelGGL(tp_lgcopy<T>, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
