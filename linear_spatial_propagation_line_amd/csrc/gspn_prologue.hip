@@ -523,6 +523,11 @@ __host__ __device__ constexpr size_t xs_lds_bytes(int K, int M) {
          static_cast<size_t>(4 * 32 * kOX) * sizeof(T) + static_cast<size_t>(M) * 4;
 }
 
+// The XCD-aware tile order pays on planes of many tiles (a 2048 x 1024
+// plane has 32768); on small planes (a 56 x 56 plane has 49) the padding
+// to a multiple of 8 costs more than the pages save.
+__host__ __device__ constexpr bool xs_xcd_order(int ntiles) { return ntiles >= 1024; }
+
 // two blocks per CU (LDS), two wavefronts per SIMD
 template <typename T, int NKS>
 __global__ __launch_bounds__(256, 2) void prologue_xs(GemmArgs<T> a) {
@@ -538,7 +543,19 @@ __global__ __launch_bounds__(256, 2) void prologue_xs(GemmArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   R* Os = Xs + (BF ? kNX * KP : K * KP) + wave * 32 * kOX;   // this wavefront's [32][kOX]
   float* Bsh = reinterpret_cast<float*>(Xs + (BF ? kNX * KP : K * KP) + 4 * 32 * kOX);   // [M]
-  const int n0 = blockIdx.x * kNX;
+  // XCD-aware tile order on large planes: workgroups are dealt to the 8
+  // XCDs in turn, so XCD x takes the contiguous pixel tiles [x per,
+  // (x + 1) per) and the tiles running at once on an XCD write neighbouring
+  // pieces of every output row (the same pages, one translation each in the
+  // XCD's caches)
+  const int ntiles = (N + kNX - 1) / kNX;
+  int tile = static_cast<int>(blockIdx.x);
+  if (xs_xcd_order(ntiles)) {
+    const int per = (ntiles + 7) / 8;
+    tile = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+    if (tile >= ntiles) return;
+  }
+  const int n0 = tile * kNX;
   const int64_t b = blockIdx.y;
   const T* X = a.X + b * static_cast<int64_t>(K) * N;
 
@@ -684,7 +701,11 @@ hipError_t launch_xs(const GemmArgs<T>& g, int64_t B, const char* name, hipStrea
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>((g.N + kNX - 1) / kNX), static_cast<unsigned>(B));
+  // with the XCD-aware order, 8 x ceil(tiles / 8) workgroups, so that every
+  // tile has one
+  const int ntiles = (g.N + kNX - 1) / kNX;
+  const int gx = xs_xcd_order(ntiles) ? (ntiles + 7) / 8 * 8 : ntiles;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(B));
   tr->before(stream, name, B);
   hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, g);
   tr->after(stream);
