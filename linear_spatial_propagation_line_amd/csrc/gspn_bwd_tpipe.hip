@@ -88,6 +88,12 @@ template <> struct Four<float> {
   __device__ static raw load(const float* p, int64_t i) {
     return *reinterpret_cast<const float4*>(p + i);
   }
+  // the pair's values in two rows of a quad copy (rows 4 elements apart)
+  __device__ static raw load_rows(const float* p, int64_t i) {
+    const float2 r0 = *reinterpret_cast<const float2*>(p + i);
+    const float2 r1 = *reinterpret_cast<const float2*>(p + i + 4);
+    return make_float4(r0.x, r0.y, r1.x, r1.y);
+  }
   __device__ static float get(const raw& v, int row, int odd) {
     return row ? (odd ? v.w : v.z) : (odd ? v.y : v.x);
   }
@@ -96,6 +102,10 @@ template <> struct Four<bf16_t> {
   using raw = uint2;
   __device__ static raw load(const bf16_t* p, int64_t i) {
     return *reinterpret_cast<const uint2*>(p + i);
+  }
+  __device__ static raw load_rows(const bf16_t* p, int64_t i) {
+    return make_uint2(*reinterpret_cast<const uint32_t*>(p + i),
+                      *reinterpret_cast<const uint32_t*>(p + i + 4));
   }
   __device__ static float get(const raw& v, int row, int odd) {
     const uint32_t w = row ? v.y : v.x;
@@ -292,13 +302,14 @@ struct BtArgs {
   T* du;
   float* dlw;        // shared logits: fp32 per-plane logit gradients [3][pstride]
   float4* hv;        // [planes][H][W/2]: (h_T2B A, B, e_B2T A, B) per column pair
-  float* lxt;        // [planes][W/2][Hp][2] lambda x, both columns of a pair per row
+  float* lxt;        // [planes][Wq][Hp][4] lambda x in column quads, four columns per row
   float* ugt;        // same layout, u gy
-  T* lgt;            // [3][planes][W/2][Hp][2] logits
+  T* lgt;            // [3][planes][Wq][Hp][4] logits
   float4* hh;        // [planes][W][H/2]: (h_L2R A, B, e_R2L A, B) per row pair
   float* part;       // [5][planes][ng][ceil(W/4)][kGrp][kTc]: horizontal
                      // d(lambda x), dl0, dl1, dl2, sum h in 4 x 4 tiles
   int H, W, G, Hp, ng;
+  int Wq;                 // column quads of the copy, ceil(W / 4)
   float fT, fB, fL, fR;   // 1 for the directions in the mask, else 0
   int64_t lg_stride;      // elements between the three logit copies
   int64_t part_stride;    // elements between the five horizontal parts
@@ -315,8 +326,8 @@ __global__ __launch_bounds__(512) void bt_vA(BtArgs<T> a) {
   __shared__ float4 lbuf[2 * (512 + 2)];
   constexpr bool BF = sizeof(T) == 2;
   constexpr int PF = BF ? 8 : 4;    // rows in flight
-  constexpr int XP = BF ? 16 : 8;   // rows per copy run of lambda x / u gy (128 / 64 bytes)
-  constexpr int GP = BF ? 16 : 8;   // rows per copy run of a logit (64 bytes)
+  constexpr int XP = 8;             // rows per 128-byte line of lambda x / u gy quads
+  constexpr int GP = BF ? 16 : 8;   // rows per 128-byte line of logit quads
   constexpr int U = 16;             // unroll: a multiple of both periods
   using P = Two<T>;
   const int H = a.H, W = a.W, W2 = W / 2;
@@ -354,7 +365,15 @@ __global__ __launch_bounds__(512) void bt_vA(BtArgs<T> a) {
   StartsUp rst{0, a.G};
   float2 lxP[XP], ugP[XP];
   typename P::raw lgP[3][GP];
-  const int64_t pbase = ((plane * W2 + t) * a.Hp) * 2;   // this column pair in the copy
+#pragma unroll
+  for (int k = 0; k < XP; ++k) lxP[k] = ugP[k] = make_float2(0.f, 0.f);   // rows past H: padding
+#pragma unroll
+  for (int k = 0; k < GP; ++k) lgP[0][k] = lgP[1][k] = lgP[2][k] = typename P::raw{};
+  // this thread's quad of the copy: the lane pair that owns it swaps half its
+  // buffered rows, and the odd lane writes the second half of each line
+  const bool odd = t & 1;
+  const bool qact = 2 * (t & ~1) < W;
+  const int64_t qbase = ((plane * a.Wq + t / 2) * a.Hp) * 4;
   float4* hv = a.hv + plane * H * W2 + t;
 
   auto block = [&](int r0, auto tail) {
@@ -382,34 +401,58 @@ __global__ __launch_bounds__(512) void bt_vA(BtArgs<T> a) {
         }
       }
       if constexpr (COPY) {
-        // whole runs; the copy's row pitch Hp is a multiple of U, so a run
-        // that passes H lands in the padding
-        if ((j % XP) == XP - 1 && act && (!TAIL || r0 + j - (XP - 1) < H)) {
+        // whole 128-byte lines per lane pair (every lane takes part in the
+        // swap); the copy's row pitch Hp is a multiple of U, so a line that
+        // passes H lands in the padding
+        if ((j % XP) == XP - 1 && (!TAIL || r0 + j - (XP - 1) < H)) {
           const int rs = r0 + j - (XP - 1);
-          float4* dl = reinterpret_cast<float4*>(a.lxt + pbase + 2 * rs);
-          float4* du = reinterpret_cast<float4*>(a.ugt + pbase + 2 * rs);
+          float4 ol[XP / 2], ou[XP / 2];
 #pragma unroll
-          for (int q = 0; q < XP / 2; ++q) {
-            dl[q] = make_float4(lxP[2 * q].x, lxP[2 * q].y, lxP[2 * q + 1].x, lxP[2 * q + 1].y);
-            du[q] = make_float4(ugP[2 * q].x, ugP[2 * q].y, ugP[2 * q + 1].x, ugP[2 * q + 1].y);
+          for (int k = 0; k < XP / 2; ++k) {
+            float2 lo, hi;
+            quad_rows(lxP, XP, k, odd, &lo, &hi);
+            ol[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+            quad_rows(ugP, XP, k, odd, &lo, &hi);
+            ou[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+          }
+          if (qact) {
+            const int64_t o = qbase + 4 * (rs + (odd ? XP / 2 : 0));
+            float4* dl = reinterpret_cast<float4*>(a.lxt + o);
+            float4* du = reinterpret_cast<float4*>(a.ugt + o);
+#pragma unroll
+            for (int k = 0; k < XP / 2; ++k) {
+              dl[k] = ol[k];
+              du[k] = ou[k];
+            }
           }
         }
-        if ((j % GP) == GP - 1 && act && (!TAIL || r0 + j - (GP - 1) < H)) {
+        if ((j % GP) == GP - 1 && (!TAIL || r0 + j - (GP - 1) < H)) {
           const int rs = r0 + j - (GP - 1);
 #pragma unroll
           for (int z = 0; z < 3; ++z) {
-            T* g = a.lgt + z * a.lg_stride + pbase + 2 * rs;
+            T* g = a.lgt + z * a.lg_stride + qbase + 4 * (rs + (odd ? GP / 2 : 0));
             if constexpr (BF) {
-              uint4* d = reinterpret_cast<uint4*>(g);
+              uint32_t o[GP];   // per row: columns 4q, 4q+1 then 4q+2, 4q+3
 #pragma unroll
-              for (int q = 0; q < GP / 4; ++q)
-                d[q] = make_uint4(lgP[z][4 * q], lgP[z][4 * q + 1], lgP[z][4 * q + 2], lgP[z][4 * q + 3]);
+              for (int k = 0; k < GP / 2; ++k) quad_rows(lgP[z], GP, k, odd, &o[2 * k], &o[2 * k + 1]);
+              if (qact) {
+                uint4* d = reinterpret_cast<uint4*>(g);
+#pragma unroll
+                for (int k = 0; k < GP / 4; ++k) d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+              }
             } else {
-              float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
+              float4 o[GP / 2];
 #pragma unroll
-              for (int q = 0; q < GP / 2; ++q)
-                d[q] = make_float4(lgP[z][2 * q].x, lgP[z][2 * q].y, lgP[z][2 * q + 1].x,
-                                   lgP[z][2 * q + 1].y);
+              for (int k = 0; k < GP / 2; ++k) {
+                float2 lo, hi;
+                quad_rows(lgP[z], GP, k, odd, &lo, &hi);
+                o[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+              }
+              if (qact) {
+                float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(g));
+#pragma unroll
+                for (int k = 0; k < GP / 2; ++k) d[k] = o[k];
+              }
             }
           }
         }
@@ -431,17 +474,45 @@ struct CopyIn {
   typename Four<T>::raw g0, g1, g2;
 };
 
+// one column pair: its half of the quad in rows o0 and o0 + 1 (two loads per
+// tensor, 8 bytes of lambda x apart by 16)
 template <typename T>
 __device__ __forceinline__ CopyIn<T> load_copy(const BtArgs<T>& a, int64_t plane, int cp, int ol) {
   using Q = Four<T>;
   const int64_t cc = min(max(cp, 0), a.W / 2 - 1);
-  const int64_t i = ((plane * (a.W / 2) + cc) * a.Hp + ol) * 2;
+  const int64_t i = ((plane * a.Wq + cc / 2) * a.Hp + ol) * 4 + 2 * (cc % 2);
+  auto f4 = [](const float* p) {
+    const float2 r0 = *reinterpret_cast<const float2*>(p);
+    const float2 r1 = *reinterpret_cast<const float2*>(p + 4);
+    return make_float4(r0.x, r0.y, r1.x, r1.y);
+  };
   CopyIn<T> v;
-  v.lx = *reinterpret_cast<const float4*>(a.lxt + i);
-  v.ug = *reinterpret_cast<const float4*>(a.ugt + i);
-  v.g0 = Q::load(a.lgt, i);
-  v.g1 = Q::load(a.lgt + a.lg_stride, i);
-  v.g2 = Q::load(a.lgt + 2 * a.lg_stride, i);
+  v.lx = f4(a.lxt + i);
+  v.ug = f4(a.ugt + i);
+  v.g0 = Q::load_rows(a.lgt, i);
+  v.g1 = Q::load_rows(a.lgt + a.lg_stride, i);
+  v.g2 = Q::load_rows(a.lgt + 2 * a.lg_stride, i);
+  return v;
+}
+
+// a whole column quad: rows o0, o0 + 1 of four columns, one contiguous run
+// per tensor (32 bytes of lambda x)
+template <typename T>
+struct CopyQ {
+  Quad<float>::raw lx, ug;
+  typename Quad<T>::raw g0, g1, g2;
+};
+
+template <typename T>
+__device__ __forceinline__ CopyQ<T> load_copy_quad(const BtArgs<T>& a, int64_t plane, int q, int ol) {
+  const int64_t qq = min(max(q, 0), a.Wq - 1);
+  const int64_t i = ((plane * a.Wq + qq) * a.Hp + ol) * 4;
+  CopyQ<T> v;
+  v.lx = Quad<float>::load(a.lxt, i);
+  v.ug = Quad<float>::load(a.ugt, i);
+  v.g0 = Quad<T>::load(a.lgt, i);
+  v.g1 = Quad<T>::load(a.lgt + a.lg_stride, i);
+  v.g2 = Quad<T>::load(a.lgt + 2 * a.lg_stride, i);
   return v;
 }
 
@@ -449,9 +520,8 @@ __device__ __forceinline__ CopyIn<T> load_copy(const BtArgs<T>& a, int64_t plane
 template <typename T>
 __global__ __launch_bounds__(1024) void bt_hA(BtArgs<T> a) {
   __shared__ float4 lbuf[2 * (1024 + 2)];
-  constexpr int PP = 4;   // column pairs in flight
-  using Q = Four<T>;
-  const int H = a.H, W = a.W, H2 = H / 2, W2 = W / 2;
+  constexpr int PQ = sizeof(T) == 2 ? 2 : 1;   // column quads in flight (fp32: registers)
+  const int H = a.H, W = a.W, H2 = H / 2;
   const int t = threadIdx.x, o0 = 2 * t;
   const bool act = o0 < H;
   const int ol = act ? o0 : 0;
@@ -462,38 +532,44 @@ __global__ __launch_bounds__(1024) void bt_hA(BtArgs<T> a) {
   const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
   float4* hh = a.hh + plane * W * H2 + t;
 
-  CopyIn<T> ring[PP];
+  CopyQ<T> ring[PQ];
 #pragma unroll
-  for (int j = 0; j < PP; ++j) ring[j] = load_copy(a, plane, j, ol);
+  for (int j = 0; j < PQ; ++j) ring[j] = load_copy_quad(a, plane, j, ol);
   Sweep s{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   StartsUp rst{0, a.G};
+  // columns cb .. cb + 4 PQ - 1 (a partial last block: only those below W)
   auto block = [&](int cb, auto tail) {
     constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
-    for (int j = 0; j < PP; ++j) {
-      const int cp = cb + j;
-      if (!TAIL || cp < W2) {
-        const CopyIn<T> v = ring[j];
-        ring[j] = load_copy(a, plane, cp + PP, ol);
+    for (int j = 0; j < PQ; ++j) {
+      const int q = cb / 4 + j;
+      if (!TAIL || 4 * q < W) {
+        const CopyQ<T> v = ring[j];
+        ring[j] = load_copy_quad(a, plane, q + PQ, ol);
 #pragma unroll
-        for (int odd = 0; odd < 2; ++odd) {
-          const int c = 2 * cp + odd;
-          const Weights wa = make_weights(Q::get(v.g0, 0, odd), Q::get(v.g1, 0, odd),
-                                          Q::get(v.g2, 0, odd), mA0, 1.f);
-          const Weights wb = make_weights(Q::get(v.g0, 1, odd), Q::get(v.g1, 1, odd),
-                                          Q::get(v.g2, 1, odd), 1.f, mB2);
-          const float4* cur = ln.buf + ln.par * ln.slots;
-          advance(s, cur[t], cur[t + 2], wa, wb, quad(v.lx, 0, odd), quad(v.lx, 1, odd),
-                  quad(v.ug, 0, odd), quad(v.ug, 1, odd), rst.at(c));
-          publish(s, ln, t, act, wa.w0, wb.w2);
-          if (act) hh[static_cast<int64_t>(c) * H2] = make_float4(s.hA, s.hB, s.eA, s.eB);
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * q + i;
+          if (!TAIL || c < W) {   // the last quad of W % 4 == 2 holds two columns
+            float g0[2], g1[2], g2[2], lx[2], ug[2];
+            Quad<T>::col(v.g0, i, g0);
+            Quad<T>::col(v.g1, i, g1);
+            Quad<T>::col(v.g2, i, g2);
+            Quad<float>::col(v.lx, i, lx);
+            Quad<float>::col(v.ug, i, ug);
+            const Weights wa = make_weights(g0[0], g1[0], g2[0], mA0, 1.f);
+            const Weights wb = make_weights(g0[1], g1[1], g2[1], 1.f, mB2);
+            const float4* cur = ln.buf + ln.par * ln.slots;
+            advance(s, cur[t], cur[t + 2], wa, wb, lx[0], lx[1], ug[0], ug[1], rst.at(c));
+            publish(s, ln, t, act, wa.w0, wb.w2);
+            if (act) hh[static_cast<int64_t>(c) * H2] = make_float4(s.hA, s.hB, s.eA, s.eB);
+          }
         }
       }
     }
   };
   int cb = 0;
-  for (; cb + PP <= W2; cb += PP) block(cb, std::false_type{});
-  if (cb < W2) block(cb, std::true_type{});
+  for (; cb + 4 * PQ <= W; cb += 4 * PQ) block(cb, std::false_type{});
+  if (cb < W) block(cb, std::true_type{});
 }
 
 // bt_hB: right->left, h of right->left and e of left->right; writes the
@@ -761,16 +837,17 @@ namespace {
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct BtLayout {
-  int64_t Hp, ng;
+  int64_t Hp, Wq, ng;
   size_t hv, lxt, ugt, lgt, hh, part, total;
 };
 
 BtLayout bt_layout(int64_t planes, int64_t H, int64_t W, size_t es, bool hz) {
   BtLayout L;
   L.Hp = (H + 15) / 16 * 16;
+  L.Wq = (W + 3) / 4;
   L.ng = (H + kGrp - 1) / kGrp;
   const size_t px = static_cast<size_t>(planes * H * W);
-  const size_t cp = static_cast<size_t>(planes * W * L.Hp);
+  const size_t cp = static_cast<size_t>(planes * 4 * L.Wq * L.Hp);   // elements of one copy
   const size_t np = static_cast<size_t>(planes * L.ng * ((W / 2 + 1) / 2) * kGrp * kTc);
   size_t o = 0;
   L.hv = o; o = al256(o + px * 8);
@@ -825,12 +902,13 @@ static hipError_t launch_bt_dt(const BwdProblem& pr, void* ws, hipStream_t strea
   a.W = static_cast<int>(pr.W);
   a.G = static_cast<int>(pr.G >= pr.H && pr.G >= pr.W ? 0 : pr.G);
   a.Hp = static_cast<int>(L.Hp);
+  a.Wq = static_cast<int>(L.Wq);
   a.ng = static_cast<int>(L.ng);
   a.fT = (m & 1u) ? 1.f : 0.f;
   a.fB = (m & 2u) ? 1.f : 0.f;
   a.fL = (m & 4u) ? 1.f : 0.f;
   a.fR = (m & 8u) ? 1.f : 0.f;
-  a.lg_stride = planes * pr.W * L.Hp;
+  a.lg_stride = planes * 4 * L.Wq * L.Hp;
   a.part_stride = planes * L.ng * ((pr.W / 2 + 1) / 2) * kGrp * kTc;
   a.pstride = planes * pr.H * pr.W;
   a.plane0 = 0;

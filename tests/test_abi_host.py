@@ -243,12 +243,13 @@ def _stream_ws(planes, H, W, dirs, es):
 
 def _pipe_ws(planes, H, W, dirs, es):
     """The pipeline's regions: states of the two first sweeps (8 bytes a
-    pixel each), the column-major copy (rows padded to 16), the five fp32
-    horizontal parts in tiles of 4 rows x 4 columns."""
+    pixel each), the column-major copy in column quads (rows padded to 16,
+    columns to a multiple of 4), the five fp32 horizontal parts in tiles of
+    4 rows x 4 columns."""
     px = planes * H * W
     hz = bool(dirs & 12)
     Hp, ng, nq = (H + 15) // 16 * 16, (H + 3) // 4, (W // 2 + 1) // 2
-    cp = planes * W * Hp
+    cp = planes * 4 * ((W + 3) // 4) * Hp
     if not hz:
         return _al(px * 8)
     return (_al(px * 8) + 2 * _al(cp * 4) + _al(3 * cp * es) + _al(px * 8)
