@@ -56,20 +56,21 @@ PLAN_SOURCES = {
     "plane16": ("gspn_plane.hip", "gspn_device.hpp"),
     "plane64": ("gspn_plane.hip", "gspn_device.hpp"),
     "band": ("gspn_band.hip", "gspn_device.hpp"),
-    "tpipe": ("gspn_tpipe.hip", "gspn_device.hpp"),
+    "tpipe": ("gspn_tpipe.hip", "gspn_quad.hpp", "gspn_device.hpp"),
     "stream": ("gspn_stream.hip", "gspn_device.hpp"),
-    "tpipe_t": ("gspn_tpipe.hip", "gspn_dirs.hip", "gspn_device.hpp"),
+    "tpipe_t": ("gspn_tpipe.hip", "gspn_quad.hpp", "gspn_dirs.hip", "gspn_device.hpp"),
     "large": ("gspn_dirs.hip", "gspn_stream.hip", "gspn_device.hpp"),
     "bwd_plane16": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_plane64": ("gspn_bwd_plane.hip", "gspn_device.hpp"),
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
-    "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_device.hpp"),
+    "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_quad.hpp", "gspn_device.hpp"),
     "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_dirs.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
     "prologue": ("gspn_prologue.hip", "gspn_mfma.hpp", "gspn_device.hpp"),
     "module": ("gspn_prologue.hip", "gspn_fused.hip", "gspn_mfma.hpp", "gspn_plane.hip",
-               "gspn_band.hip", "gspn_tpipe.hip", "gspn_stream.hip", "gspn_device.hpp"),
+               "gspn_band.hip", "gspn_tpipe.hip", "gspn_quad.hpp", "gspn_stream.hip",
+               "gspn_device.hpp"),
 }
 
 

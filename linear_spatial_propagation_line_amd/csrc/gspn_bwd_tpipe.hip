@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "gspn_device.hpp"
+#include "gspn_quad.hpp"
 #include "gspn_launch.hpp"
 
 namespace gspn {
