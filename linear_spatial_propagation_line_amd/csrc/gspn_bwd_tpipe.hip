@@ -19,8 +19,9 @@
 //
 //   bt_vA  top->bottom over the row-major inputs: h of top->bottom and e of
 //          bottom->top, stored per pixel; writes the column-major copy
-//          (lambda x and u gy in fp32, the logits in the storage type) that
-//          the horizontal sweeps read as contiguous lines.
+//          (lambda x and u gy in fp32, the logits in the storage type, in
+//          column quads written as whole lines by lane pairs) that the
+//          horizontal sweeps read as contiguous lines.
 //   bt_hA  left->right over the copy: h of left->right and e of right->left,
 //          stored per pixel.
 //   bt_hB  right->left over the copy: h of right->left and e of left->right;
@@ -81,14 +82,11 @@ template <> struct Two<bf16_t> {
   }
 };
 
-// Rows o, o+1 of a column pair in the copy, which keeps per row both columns
-// of the pair side by side: (o, even), (o, odd), (o+1, even), (o+1, odd).
+// Rows o, o+1 of a column pair, as (o, even), (o, odd), (o+1, even),
+// (o+1, odd): the pair's half of two rows of a quad of the copy.
 template <typename T> struct Four;
 template <> struct Four<float> {
   using raw = float4;
-  __device__ static raw load(const float* p, int64_t i) {
-    return *reinterpret_cast<const float4*>(p + i);
-  }
   // the pair's values in two rows of a quad copy (rows 4 elements apart)
   __device__ static raw load_rows(const float* p, int64_t i) {
     const float2 r0 = *reinterpret_cast<const float2*>(p + i);
@@ -101,9 +99,6 @@ template <> struct Four<float> {
 };
 template <> struct Four<bf16_t> {
   using raw = uint2;
-  __device__ static raw load(const bf16_t* p, int64_t i) {
-    return *reinterpret_cast<const uint2*>(p + i);
-  }
   __device__ static raw load_rows(const bf16_t* p, int64_t i) {
     return make_uint2(*reinterpret_cast<const uint32_t*>(p + i),
                       *reinterpret_cast<const uint32_t*>(p + i + 4));
@@ -466,8 +461,9 @@ __global__ __launch_bounds__(512) void bt_vA(BtArgs<T> a) {
 }
 
 // ===========================================================================
-// Horizontal sweeps over the copy: a thread owns image rows o0, o0 + 1, and
-// one load of a copy tensor covers both rows of a column pair.
+// Horizontal sweeps over the copy: a thread owns image rows o0, o0 + 1;
+// bt_hA loads both rows of a whole column quad at once, bt_hB (no registers
+// for a quad) its column pair's half of them.
 // ===========================================================================
 template <typename T>
 struct CopyIn {

@@ -8,14 +8,16 @@
 // line (each pixel mixes its three predecessors), so one workgroup must own a
 // whole line of a plane. Three launches, one workgroup per plane each:
 //
-//   K1 vfwd  -- top->bottom sweep over the row-major inputs (lane pair = two
-//               adjacent columns, coalesced 4-byte loads prefetched 8 rows
+//   K1 vfwd  -- top->bottom sweep over the row-major inputs (a thread owns
+//               two adjacent columns, coalesced 4-byte loads prefetched 8 rows
 //               ahead). Saves the state every 8 rows (checkpoints) and writes a
-//               column-major copy of lambda*x (fp32) and the three logits
-//               through per-thread register buffers, so every store is a
-//               contiguous >= 64-byte column segment.
+//               column-major copy of lambda*x (fp32) and the three logits in
+//               column quads: per-thread register buffers, then a swap within
+//               the lane pair that owns a quad, so that the pair's stores
+//               complete whole 128-byte lines.
 //   K2 hpair -- left->right and right->left on the column-major copy, where a
-//               horizontal scan reads whole contiguous lines. The right->left
+//               horizontal scan reads whole contiguous lines (a thread loads
+//               two rows of a column quad at once). The right->left
 //               pass walks 4-column chunks from the right; for each chunk it
 //               recomputes left->right from the checkpoint before it, so one
 //               pass over the copy serves both directions. Writes
