@@ -407,7 +407,9 @@ __global__ __launch_bounds__(256) void tp_lgcopy(TpArgs<T> a, int64_t nlp) {
 // ===========================================================================
 template <typename T, bool LR, bool RL>
 __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
-  __shared__ float lbuf[2 * (2048 + 4)];
+  // two double-buffered lines: left->right (the first pass and the
+  // recomputes) and right->left, whose states then stay in LDS across chunks
+  __shared__ float lbuf[4 * (2048 + 4)];
   constexpr int PF = 8;
   using P = Pair<T>;
   const int H = a.H, W = a.W, G = a.G, Hp = a.Hp;
@@ -417,9 +419,10 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
   const int ol = act ? o0 : 0;
   const int64_t plane = a.plane0 + blockIdx.x;
   const int n4 = H + 4;
-  for (int i = t; i < 2 * n4; i += blockDim.x) lbuf[i] = 0.0f;
+  for (int i = t; i < 4 * n4; i += blockDim.x) lbuf[i] = 0.0f;
   __syncthreads();
   LineX lx{lbuf, n4, 0};
+  LineX lr{lbuf + 2 * n4, n4, 0};
   const float mA0 = o0 > 0 ? 1.f : 0.f;
   const float mB2 = o0 + 1 < H - 1 ? 1.f : 0.f;
 
@@ -469,22 +472,23 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
     ra = make_rec(v.g0[0], v.g1[0], v.g2[0], v.lx.x, mA0, 1.f);
     rb = make_rec(v.g0[1], v.g1[1], v.g2[1], v.lx.y, 1.f, mB2);
   };
-  // one scan step on the line: the new pair is the mix of the previous line
-  // (or the restart value); publishes it and waits for the whole line
-  auto step = [&](const Rec& ra, const Rec& rb, bool restart, float& hA, float& hB) {
-    const float* pv = lx.cur();
-    const float na = mix(ra, pv[o0 + 1], hA, hB);
-    const float nb = mix(rb, hA, hB, pv[o0 + 4]);
+  // one scan step on line ln given the previous states of the neighbouring
+  // rows (o0 - 1, o0 + 2): the new pair is the mix of the previous line (or
+  // the restart value); publishes it and waits for the whole line
+  auto step_nb = [&](LineX& ln, const Rec& ra, const Rec& rb, bool restart, float& hA,
+                     float& hB, float nl, float nr) {
+    const float na = mix(ra, nl, hA, hB);
+    const float nb = mix(rb, hA, hB, nr);
     hA = restart ? ra.lx : na;
     hB = restart ? rb.lx : nb;
-    if (act) *reinterpret_cast<float2*>(lx.nxt() + o0 + 2) = make_float2(hA, hB);
-    lx.par ^= 1;
+    if (act) *reinterpret_cast<float2*>(ln.nxt() + o0 + 2) = make_float2(hA, hB);
+    ln.par ^= 1;
     __syncthreads();
   };
-  auto seed = [&](float hA, float hB) {
-    if (act) *reinterpret_cast<float2*>(lx.nxt() + o0 + 2) = make_float2(hA, hB);
-    lx.par ^= 1;
-    __syncthreads();
+  // ... with the neighbours' previous states taken from the line
+  auto step = [&](LineX& ln, const Rec& ra, const Rec& rb, bool restart, float& hA, float& hB) {
+    const float* pv = ln.cur();
+    step_nb(ln, ra, rb, restart, hA, hB, pv[o0 + 1], pv[o0 + 4]);
   };
 
   // ---- left->right: checkpoints, or the final sum when there is no reverse
@@ -509,7 +513,7 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
             if (!TAIL || c < W) {   // the last quad of W % 4 == 2 holds two columns
               Rec ra, rb;
               recs(column(v4, i), ra, rb);
-              step(ra, rb, rst.at(c), hA, hB);
+              step(lx, ra, rb, rst.at(c), hA, hB);
               if (act) {
                 if constexpr (RL) {
                   if ((c + 1) % kCkH == 0) store_pair(a.ckh, (plane * a.nckh + c / kCkH) * H + o0, hA, hB);
@@ -532,14 +536,19 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
     static_assert(kCkH == 4, "a right->left chunk is one column quad of the copy");
     struct Chunk {
       In4 in;
-      float2 ck;
+      float2 ck;      // left->right states of rows o0, o0 + 1 before the chunk
+      float2 nb;      // ... and of the neighbouring rows o0 - 1, o0 + 2 (0 past the edge)
     };
     auto load_chunk = [&](int k) {
       Chunk ch;
       ch.in = load_quad(k);
       ch.ck = make_float2(0.f, 0.f);
-      if constexpr (LR)
-        ch.ck = *reinterpret_cast<const float2*>(a.ckh + (plane * a.nckh + max(k - 1, 0)) * H + ol);
+      ch.nb = make_float2(0.f, 0.f);
+      if constexpr (LR) {
+        const float* ck = a.ckh + (plane * a.nckh + max(k - 1, 0)) * H;
+        ch.ck = *reinterpret_cast<const float2*>(ck + ol);
+        ch.nb = make_float2(ck[max(ol - 1, 0)], ck[min(ol + 2, H - 1)]);
+      }
       return ch;
     };
     float hrA = 0.f, hrB = 0.f;   // right->left state, carried across chunks
@@ -553,23 +562,29 @@ __global__ __launch_bounds__(1024) void tp_hpair(TpArgs<T> a) {
 #pragma unroll
       for (int i = 0; i < kCkH; ++i) { hlA[i] = 0.f; hlB[i] = 0.f; }
       if constexpr (LR) {
-        float hA = k > 0 ? ch.ck.x : 0.f, hB = k > 0 ? ch.ck.y : 0.f;
-        seed(hA, hB);
+        // the first step takes the neighbours' checkpoint states from memory,
+        // so the line needs no seeding barrier
+        const bool in = k > 0;
+        float hA = in ? ch.ck.x : 0.f, hB = in ? ch.ck.y : 0.f;
+        const float nl = in && o0 > 0 ? ch.nb.x : 0.f, nr = in && o0 + 2 < H ? ch.nb.y : 0.f;
         FwdRestart rst{fwd_restart_from(cs, G), G};
 #pragma unroll
         for (int i = 0; i < kCkH; ++i) {
-          if (!TAIL || cs + i < W) step(ra[i], rb[i], rst.at(cs + i), hA, hB);
+          if (!TAIL || cs + i < W) {
+            if (i == 0) step_nb(lx, ra[i], rb[i], rst.at(cs), hA, hB, nl, nr);
+            else step(lx, ra[i], rb[i], rst.at(cs + i), hA, hB);
+          }
           hlA[i] = hA;
           hlB[i] = hB;
         }
       }
-      seed(hrA, hrB);
+      // right->left continues on its own line from the previous chunk
       RevRestart rst = rev_counter(min(cs + kCkH - 1, W - 1), W, G);
 #pragma unroll
       for (int i = kCkH - 1; i >= 0; --i) {
         const int c = cs + i;
         if (!TAIL || c < W) {
-          step(ra[i], rb[i], rst.at(c), hrA, hrB);
+          step(lr, ra[i], rb[i], rst.at(c), hrA, hrB);
           if (act) store_pair(a.yht, yidx(c), hlA[i] + hrA, hlB[i] + hrB);
         }
       }
