@@ -570,6 +570,79 @@ def calibrate(torch, reps: int) -> int:
     return 0
 
 
+def strip_prototype(torch, steps: int) -> int:
+    """The other schedule for large planes, measured: the top->bottom scan
+    with each 2048 x 1024 plane split over 32 one-wavefront workgroups that
+    exchange halo states through device memory every K rows
+    (gspn_bench_strip_t2b), at several slab sizes (planes in flight), against
+    the library's own top->bottom propagation (one workgroup per plane) on the
+    same inputs. Every output is compared with the library's; one JSON line."""
+    import linear_spatial_propagation_line_amd as g
+    from linear_spatial_propagation_line_amd.inputs import WORKLOADS, make_inputs
+    L = g.lib()
+    L.gspn_bench_strip_work_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.gspn_bench_strip_work_bytes.restype = ctypes.c_size_t
+    L.gspn_bench_strip_fail_offset.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.gspn_bench_strip_fail_offset.restype = ctypes.c_size_t
+    L.gspn_bench_strip_t2b.argtypes = [ctypes.c_void_p] * 2 + [ctypes.POINTER(ctypes.c_void_p)] + \
+        [ctypes.c_void_p] * 2 + [ctypes.c_int64] + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.gspn_bench_strip_t2b.restype = ctypes.c_int
+    w = WORKLOADS["t2i_2048x1024"]
+    d = make_inputs(w, device="cuda")
+    B, C, H, W = d["x"].shape
+    planes = B * C
+    lg = (ctypes.c_void_p * 3)(*(d[k].data_ptr() for k in ("l0", "l1", "l2")))
+    stream = torch.cuda.current_stream()
+    abort = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    steps = max(steps, 2)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ref = g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], dirs=g.T2B)
+    lib_ms = timed(lambda: g.propagate(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"],
+                                       dirs=g.T2B, out=ref))
+    res = {"workload": w.name, "planes": planes, "H": H, "W": W, "direction": "top->bottom",
+           "library_ms": lib_ms, "library_plan": g.plan_name(B, C, H, W, g.T2B, 0, 1),
+           "prototype": []}
+    out = torch.empty_like(ref)
+    S = 32
+    for K in (16, 8):
+        for pf in (8, 32, 64, 128, 256):
+            nbytes = L.gspn_bench_strip_work_bytes(S, K, pf)
+            work = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda")
+            wp = (work.data_ptr() + 255) // 256 * 256
+            fail_at = L.gspn_bench_strip_fail_offset(S, pf)
+
+            def run():
+                work.zero_()
+                rc = L.gspn_bench_strip_t2b(d["x"].data_ptr(), d["lam"].data_ptr(), lg,
+                                            d["u"].data_ptr(), out.data_ptr(), planes, H, W, S, K,
+                                            pf, wp, nbytes, abort.data_ptr(), 1 << 20,
+                                            stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"gspn_bench_strip_t2b returned {rc}")
+            print(f"[strip] K={K} pf={pf}", flush=True)
+            ms = timed(run)
+            fail = int(work.view(torch.uint8)[wp - work.data_ptr() + fail_at:][:4].view(torch.int32)[0])
+            err = float(((out.float() - ref.float()).abs() /
+                         (ref.float().abs() + ref.float().pow(2).mean().sqrt())).max())
+            res["prototype"].append({"K": K, "planes_in_flight": pf, "workgroups": pf * S,
+                                     "ms": ms, "vs_library": ms / lib_ms, "gave_up": fail,
+                                     "scaled_diff_vs_library": err})
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as f:
@@ -636,6 +709,9 @@ def main() -> int:
     ap.add_argument("--calibrate", action="store_true",
                     help="time a plain device copy and a read-only reduction of known size "
                          "(the reference points for HBM bandwidth and for counter scaling)")
+    ap.add_argument("--strip-prototype", action="store_true",
+                    help="time the split-line prototype (top->bottom over strips of 32 "
+                         "workgroups per plane) against the library's top->bottom scan")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -646,6 +722,8 @@ def main() -> int:
 
     import torch
 
+    if args.strip_prototype:
+        return strip_prototype(torch, args.steps)
     if args.calibrate:
         return calibrate(torch, args.steps)
 

@@ -55,6 +55,35 @@ int gspn_bench_handshake(void* flags, const uint32_t* abort_flag, int rounds, in
  * (the one gspn_bench_handshake reads) in kHz, or 0 on a HIP error. */
 int gspn_bench_wall_clock_khz(void);
 
+/*
+ * gspn_bench_strip_t2b -- a measured prototype of the schedule that splits a
+ * scan line over several workgroups (not a plan of the library): the
+ * top->bottom scan of the propagation (CSDN page on GSPN, section 方法; the
+ * weights of section 如何设计一个高效的传播层), global, bf16 storage, fp32
+ * state, out = u * h_T2B, for `planes` contiguous row-major H x W planes.
+ * Each plane is split into S strips of W / S columns; one 64-lane workgroup
+ * owns a strip plus K halo columns on each side (W / S + 2K <= 64, W / S >= K,
+ * K 8 or 16) and hands its edge states to its neighbours through device
+ * memory every K rows. pf planes are in flight at once; the pf * S
+ * workgroups must all be resident (checked: returns 1 otherwise).
+ *   x, lam, logits[3], u, out  device bf16 tensors of planes * H * W elements;
+ *   work        device memory, 256-byte aligned, at least
+ *               gspn_bench_strip_work_bytes(S, K, pf) bytes, zeroed by the
+ *               caller before every launch (flags, give-up word, halo states);
+ *   abort_flag  host-visible memory; setting it non-zero ends every wait;
+ *   spin_max    polls after which a wait gives up; a give-up sets the word
+ *               at work + gspn_bench_strip_fail_offset(S, pf) (uint32), every
+ *               workgroup then exits, and out is not valid.
+ * Returns 0 when enqueued, 1 for a bad argument (nothing enqueued), 2 for a
+ * HIP error.
+ */
+size_t gspn_bench_strip_work_bytes(int S, int K, int pf);
+size_t gspn_bench_strip_fail_offset(int S, int pf);
+int gspn_bench_strip_t2b(const void* x, const void* lam, const void* const logits[3],
+                         const void* u, void* out, int64_t planes, int H, int W, int S, int K,
+                         int pf, void* work, size_t work_bytes, const uint32_t* abort_flag,
+                         int spin_max, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

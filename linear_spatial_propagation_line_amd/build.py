@@ -20,7 +20,7 @@ SOURCES = ["gspn_api.cpp", "gspn_plane.hip", "gspn_stream.hip", "gspn_tpipe.hip"
            "gspn_band.hip", "gspn_bwd_stream.hip", "gspn_bwd_plane.hip",
            "gspn_bwd_band.hip", "gspn_dirs.hip",
            "gspn_prologue.hip", "gspn_bwd_tpipe.hip", "gspn_groups.cpp",
-           "gspn_calib.hip", "gspn_fused.hip"]
+           "gspn_calib.hip", "gspn_fused.hip", "gspn_strip.hip"]
 ARCH = os.environ.get("GSPN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
