@@ -65,6 +65,7 @@ PLAN_SOURCES = {
     "bwd_stream": ("gspn_bwd_stream.hip", "gspn_device.hpp"),
     "bwd_band": ("gspn_bwd_band.hip", "gspn_device.hpp"),
     "bwd_tpipe": ("gspn_bwd_tpipe.hip", "gspn_quad.hpp", "gspn_device.hpp"),
+    "bwd_tpipe_t": ("gspn_bwd_tpipe.hip", "gspn_quad.hpp", "gspn_dirs.hip", "gspn_device.hpp"),
     "bwd_dirs": ("gspn_bwd_stream.hip", "gspn_dirs.hip", "gspn_device.hpp"),
     "dirs": ("gspn_dirs.hip", "gspn_device.hpp"),
     "prologue": ("gspn_prologue.hip", "gspn_mfma.hpp", "gspn_device.hpp"),
@@ -188,8 +189,9 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
     Module prologue (counted per pixel of B images: `planes` is B here):
       prologue_reduce  x_in read (Cin s), x written (C s)
       prologue_params  x read (C s), five parameter tensors written (5 C s)
-      tp_t_in / tp_t_out  the pipeline on transposed copies: one tensor read
-          and written transposed (2 s), counted per plane and tensor
+      tp_t_in / tp_t_out, btp_t_in / btp_t_out  the forward and backward
+          pipelines on transposed copies: one tensor read and written
+          transposed (2 s), counted per plane and tensor
       fused_unit (small planes: the parameter product fused with the scan,
           counted per pixel of the B * C planes): x read (s), out written (s);
           the parameters never leave the chip
@@ -236,6 +238,8 @@ def design_bytes(kernel: str, planes: int, w, first: bool = True, last: bool = T
         "fused_unit": 2 * s,
         "tp_t_in": 2 * s,
         "tp_t_out": 2 * s,
+        "btp_t_in": 2 * s,
+        "btp_t_out": 2 * s,
     }[kernel]
     return per * px
 

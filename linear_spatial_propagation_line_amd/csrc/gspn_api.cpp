@@ -418,7 +418,7 @@ void keep_trace(const gspn::Tracer& tr) {
 }
 
 // ---- backward pass ---------------------------------------------------------
-enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kStream };
+enum class BPlan { kInvalid, kPlane16, kPlane64, kBand, kTpipe, kTpipeT, kStream };
 struct BChecked;
 BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
                         int dtype);
@@ -433,10 +433,65 @@ struct BChecked {
 
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// the backward pipeline on transposed planes (as run_tpipe_t for the forward
+// pass): the seven inputs and six gradients transposed, then the pipeline's
+// own workspace for the transposed shape and mask
+uint32_t swap_axes(uint32_t mask) { return ((mask & 3u) << 2) | ((mask >> 2) & 3u); }
+size_t bwd_tpipe_t_workspace_bytes(int64_t planes, int64_t H, int64_t W, uint32_t mask,
+                                   gspn_dtype dt) {
+  const size_t t = al256(static_cast<size_t>(planes * H * W) * (dt == GSPN_F32 ? 4 : 2));
+  return 13 * t + gspn::bwd_tpipe_workspace_bytes(planes, W, H, swap_axes(mask), dt);
+}
+
+template <typename T>
+hipError_t run_bwd_tpipe_t_dt(const gspn::BwdProblem& pr, void* ws, hipStream_t stream,
+                              gspn::Tracer* tr) {
+  const int64_t planes = pr.B * pr.C;
+  const int H = static_cast<int>(pr.H), W = static_cast<int>(pr.W);
+  const size_t t = al256(static_cast<size_t>(planes * H * W) * sizeof(T));
+  char* w = static_cast<char*>(ws);
+  auto buf = [&](int i) { return reinterpret_cast<T*>(w + i * t); };
+  // inputs: x, lambda, u, grad_out, l0, l1, l2; gradients: x, l0, l1, l2, lambda, u
+  const T* si[7] = {static_cast<const T*>(pr.x), static_cast<const T*>(pr.lam),
+                    static_cast<const T*>(pr.u), static_cast<const T*>(pr.gy),
+                    static_cast<const T*>(pr.l[0]), static_cast<const T*>(pr.l[1]),
+                    static_cast<const T*>(pr.l[2])};
+  T* di[7] = {buf(0), buf(1), buf(2), buf(3), buf(4), buf(5), buf(6)};
+  hipError_t e = gspn::transpose_planes<T>(si, di, 7, planes, H, W, "btp_t_in", stream, tr);
+  if (e != hipSuccess) return e;
+  gspn::BwdProblem pt = pr;
+  pt.x = di[0];
+  pt.lam = di[1];
+  pt.u = di[2];
+  pt.gy = di[3];
+  for (int k = 0; k < 3; ++k) pt.l[k] = di[4 + k];
+  T* go[6] = {buf(7), buf(8), buf(9), buf(10), buf(11), buf(12)};
+  pt.dx = go[0];
+  for (int k = 0; k < 3; ++k) pt.dl[k] = go[1 + k];
+  pt.dlam = go[4];
+  pt.du = go[5];
+  pt.H = pr.W;
+  pt.W = pr.H;
+  pt.mask = swap_axes(pr.mask);
+  pt.aligned_vec4 = false;
+  pt.aligned_pair = true;
+  pt.dlw = nullptr;
+  if ((e = gspn::launch_bwd_tpipe(pt, w + 13 * t, stream, tr)) != hipSuccess) return e;
+  const T* so[6] = {go[0], go[1], go[2], go[3], go[4], go[5]};
+  T* dd[6] = {static_cast<T*>(pr.dx), static_cast<T*>(pr.dl[0]), static_cast<T*>(pr.dl[1]),
+              static_cast<T*>(pr.dl[2]), static_cast<T*>(pr.dlam), static_cast<T*>(pr.du)};
+  return gspn::transpose_planes<T>(so, dd, 6, planes, W, H, "btp_t_out", stream, tr);
+}
+
 BChecked check_bwd_shape(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mask, int64_t G,
                          int dtype, int64_t Cl) {
   BChecked r = check_bwd_plan(B, C, H, W, mask, G, dtype);
   if (r.status != GSPN_OK) return r;
+  if (r.plan == BPlan::kTpipeT && Cl < C) {
+    // the transposed pipeline takes unshared logits only
+    r.plan = BPlan::kStream;
+    r.ws_bytes = gspn::bwd_stream_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
+  }
   if (check_logit_channels(C, Cl) != GSPN_OK) {
     r.status = GSPN_E_SHAPE;
     return r;
@@ -453,14 +508,16 @@ BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mas
     r.status = f.status;
     return r;
   }
-  // GSPN_FORCE_BWD_PLAN=plane|band|tpipe|stream picks a path for testing when
-  // the shape allows it; otherwise the first path that fits, in that order
+  // GSPN_FORCE_BWD_PLAN=plane|band|tpipe|tpipe_t|stream picks a path for
+  // testing when the shape allows it; otherwise the first path that fits, in
+  // that order
   const char* force = std::getenv("GSPN_FORCE_BWD_PLAN");
   const bool f_plane = force && !std::strcmp(force, "plane");
   const bool f_band = force && !std::strcmp(force, "band");
   const bool f_tpipe = force && !std::strcmp(force, "tpipe");
+  const bool f_tpipe_t = force && !std::strcmp(force, "tpipe_t");
   const bool f_stream = force && !std::strcmp(force, "stream");
-  const bool any = !f_plane && !f_band && !f_tpipe && !f_stream;
+  const bool any = !f_plane && !f_band && !f_tpipe && !f_tpipe_t && !f_stream;
   if ((any || f_plane) && gspn::plane_fits(H, W)) {
     r.plan = gspn::plane_seg(H, W) == 16 ? BPlan::kPlane16 : BPlan::kPlane64;
     return r;
@@ -473,6 +530,13 @@ BChecked check_bwd_plan(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t mas
   if ((any || f_tpipe) && gspn::btpipe_fits(H, W)) {
     r.plan = BPlan::kTpipe;
     r.ws_bytes = gspn::bwd_tpipe_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
+    return r;
+  }
+  if ((any || f_tpipe_t) && gspn::btpipe_fits(W, H)) {
+    // planes wider than the pipeline's row sweeps take, whose transpose it
+    // takes: the pipeline on transposed copies
+    r.plan = BPlan::kTpipeT;
+    r.ws_bytes = bwd_tpipe_t_workspace_bytes(B * C, H, W, mask, static_cast<gspn_dtype>(dtype));
     return r;
   }
   if (f_plane && gspn::plane_fits(H, W)) {
@@ -490,6 +554,7 @@ const char* bplan_str(BPlan p) {
     case BPlan::kPlane64: return "bwd_plane64";
     case BPlan::kBand: return "bwd_band";
     case BPlan::kTpipe: return "bwd_tpipe";
+    case BPlan::kTpipeT: return "bwd_tpipe_t";
     case BPlan::kStream: return "bwd_stream";
     default: return "invalid";
   }
@@ -580,6 +645,12 @@ gspn_status run_bwd(gspn::BwdProblem pr, const BChecked& chk, void* ws, hipStrea
       // take the streaming path, whose workspace fits in the pipeline's
       e = pr.aligned_pair ? gspn::launch_bwd_tpipe(pr, ws, stream, &tr)
                           : gspn::launch_bwd_stream(pr, ws, stream, &tr);
+      break;
+    case BPlan::kTpipeT:
+      // the transposes take any alignment; the pipeline then works on
+      // aligned workspace copies
+      e = pr.dtype == GSPN_F32 ? run_bwd_tpipe_t_dt<float>(pr, ws, stream, &tr)
+                               : run_bwd_tpipe_t_dt<gspn::bf16_t>(pr, ws, stream, &tr);
       break;
     case BPlan::kStream:
       e = gspn::launch_bwd_stream(pr, ws, stream, &tr);

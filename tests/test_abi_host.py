@@ -213,9 +213,13 @@ def test_backward_plans(LB, monkeypatch):
     assert g.backward_plan_name(16, 192, 128, 128, group_rows=8) == "bwd_band"
     assert g.backward_plan_name(16, 192, 128, 128, group_rows=9) == "bwd_tpipe"
     assert g.backward_plan_name(1, 1, 600, 100, group_rows=4) == "bwd_tpipe"   # H > 512
-    # the pipeline: both sides even, H <= 2048, W <= 1024
+    # the pipeline: both sides even, H <= 2048, W <= 1024; wider planes whose
+    # transpose fits take it on transposed copies
     assert g.backward_plan_name(1, 1, 2050, 100) == "bwd_stream"
-    assert g.backward_plan_name(1, 1, 100, 1026) == "bwd_stream"
+    assert g.backward_plan_name(1, 1, 100, 1026) == "bwd_tpipe_t"
+    assert g.backward_plan_name(1, 320, 1024, 2048, dtype=1) == "bwd_tpipe_t"
+    assert g.backward_plan_name(1, 1, 1026, 1026) == "bwd_stream"    # transpose too wide too
+    assert g.backward_plan_name(1, 1, 100, 2050) == "bwd_stream"
     assert g.backward_plan_name(1, 1, 100, 1025) == "bwd_stream"
     assert g.backward_plan_name(1, 1, 2048, 2) == "bwd_tpipe"
     assert g.backward_workspace_bytes(2, 3, 128, 128, group_rows=8) == 5 * 6 * 128 * 128 * 4
@@ -227,6 +231,13 @@ def test_backward_plans(LB, monkeypatch):
     monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "tpipe")
     assert g.backward_plan_name(64, 96, 56, 56) == "bwd_tpipe"
     assert g.backward_plan_name(1, 1, 65, 8) == "bwd_stream"
+    monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "tpipe_t")
+    assert g.backward_plan_name(1, 2, 66, 40) == "bwd_tpipe_t"
+    # shared logits: the transposed pipeline is not taken, the streaming path is
+    monkeypatch.delenv("GSPN_FORCE_BWD_PLAN")
+    shared = g.backward_workspace_bytes(1, 4, 100, 1026, logit_channels=2)
+    monkeypatch.setenv("GSPN_FORCE_BWD_PLAN", "stream")
+    assert shared == g.backward_workspace_bytes(1, 4, 100, 1026, logit_channels=2) > 0
 
 
 def _al(v):

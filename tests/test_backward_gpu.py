@@ -203,6 +203,27 @@ def test_t2i_full_size_sampled_planes():
         print(f"[bwd] t2i plane {c} worst scaled error {err:.3e}", flush=True)
 
 
+def test_portrait_full_size_sampled_planes():
+    """The text-to-image latent in portrait orientation (1024 x 2048 x 320
+    bf16): wider than the backward pipeline's row sweeps, so it runs the
+    pipeline on transposed copies; sampled planes of both plane groups."""
+    w = WORKLOADS["t2i_2048x1024"]
+    B, C, H, W = 1, 320, 1024, 2048
+    assert g.backward_plan_name(B, C, H, W, w.dirs, 0, 1) == "bwd_tpipe_t"
+    print("[bwd] portrait full size, generating on device", flush=True)
+    d = make_inputs(w, device=DEV, B=B, C=C, H=H, W=W)
+    gy = make_grad_out(w, device=DEV, B=B, C=C, H=H, W=W)
+    grads = g.propagate_backward(d["x"], (d["l0"], d["l1"], d["l2"]), d["lam"], d["u"], gy,
+                                 dirs=w.dirs, group_rows=0)
+    torch.cuda.synchronize()
+    for c in (0, 159, 160, 319):
+        inp = {k: v[:, c:c + 1].cpu() for k, v in d.items()}
+        got = {k: v[:, c:c + 1] for k, v in grads.items()}
+        err = assert_grad_parity(got, oracle_grads(inp, gy[:, c:c + 1].cpu(), w.dirs, 0),
+                                 f"portrait plane {c}")
+        print(f"[bwd] portrait plane {c} worst scaled error {err:.3e}", flush=True)
+
+
 def test_local_full_size():
     w = WORKLOADS["local_128x128_g8"]
     inp, gy = make_inputs(w), make_grad_out(w)
@@ -255,6 +276,30 @@ def test_pipeline_path(force_bwd_plan, shape, dtype):
             got = run_bwd(inp, gy, mask, G)
             assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
                                f"pipeline {shape} mask={mask} G={G}")
+
+
+PIPE_T_SHAPES = [(1, 2, 40, 66), (2, 1, 96, 130), (1, 1, 2, 2), (1, 1, 70, 2), (1, 1, 2, 70),
+                 (1, 2, 22, 18), (1, 1, 34, 250), (1, 1, 30, 1100)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", PIPE_T_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_transposed_pipeline_path(force_bwd_plan, shape, dtype):
+    """The backward pipeline on transposed copies (the plan of planes wider
+    than its row sweeps take), forced onto small even planes: every
+    direction-mask family (the mask's axes swap for the transposed planes),
+    global and local groups."""
+    force_bwd_plan("tpipe_t")
+    B, C, H, W = shape
+    assert g.backward_plan_name(B, C, H, W) == "bwd_tpipe_t"
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, 70 + H + 3 * W, B=B, C=C, H=H, W=W)
+    for G in (0, 1, 3, 8):
+        masks = (15, 1, 2, 4, 8, 3, 12, 5, 10) if G in (0, 3) else (15,)
+        for mask in masks:
+            got = run_bwd(inp, gy, mask, G)
+            assert_grad_parity(got, oracle_grads(inp, gy, mask, G),
+                               f"transposed pipeline {shape} mask={mask} G={G}")
 
 
 def test_pipeline_matches_streaming_path(force_bwd_plan):
