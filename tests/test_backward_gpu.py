@@ -312,3 +312,30 @@ def test_pipeline_matches_streaming_path(force_bwd_plan):
     b = run_bwd(inp, gy, 15, 0)
     ref = {k: a[k].double().cpu().numpy() for k in GRAD_NAMES}
     assert_grad_parity(b, ref, "pipeline vs stream")
+
+
+@pytest.mark.parametrize("plan,shape", [("tpipe", (1, 11, 34, 66)), ("tpipe_t", (1, 11, 66, 34))],
+                         ids=lambda v: v if isinstance(v, str) else "x".join(map(str, v)))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_pipeline_plane_groups(force_bwd_plan, monkeypatch, plan, shape, dtype):
+    """The backward pipelines with one to four plane groups on their own
+    streams (GSPN_TPIPE_GROUPS): each group count matches the oracle, and all
+    of them give the same bits. 11 planes put group boundaries inside an
+    image."""
+    force_bwd_plan(plan)
+    B, C, H, W = shape
+    assert g.backward_plan_name(B, C, H, W) == "bwd_" + plan
+    name = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp, gy = case(name, 612, B=B, C=C, H=H, W=W)
+    for mask, G in ((15, 0), (15, 3), (5, 0)):
+        ref = oracle_grads(inp, gy, mask, G)
+        first = None
+        for n in (1, 2, 3, 4):
+            monkeypatch.setenv("GSPN_TPIPE_GROUPS", str(n))
+            print(f"[parity] bwd_{plan} groups={n} mask={mask} G={G}", flush=True)
+            got = run_bwd(inp, gy, mask, G)
+            assert_grad_parity(got, ref, f"bwd_{plan} groups={n} mask={mask} G={G}")
+            if first is None:
+                first = got
+            for k in GRAD_NAMES:
+                assert torch.equal(got[k], first[k]), (k, n)

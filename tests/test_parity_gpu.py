@@ -362,3 +362,26 @@ def test_element_offset_views(shape, G, plan, dtype, off):
                 out=out)
     torch.cuda.synchronize()
     assert_parity(out, oracle_y(inp, 15, G), f"{plan} offset {off}")
+
+
+@pytest.mark.parametrize("plan", ["tpipe", "tpipe_t"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_pipeline_plane_groups(force_plan, monkeypatch, plan, dtype):
+    """The pipelines with one to four plane groups on their own streams
+    (GSPN_TPIPE_GROUPS): each group count matches the oracle, and all of them
+    give the same bits, since every plane is computed the same way whichever
+    group and stream it runs in. 11 planes put group boundaries inside an
+    image."""
+    force_plan(plan)
+    w = "cls_56x56" if dtype == torch.float32 else "dit_16x16"
+    inp = make_inputs(w, seed=611, B=1, C=11, H=34, W=66)
+    for mask, G in ((15, 0), (15, 3), (3, 0), (12, 0)):
+        ref = oracle_y(inp, mask, G)
+        outs = []
+        for n in (1, 2, 3, 4):
+            monkeypatch.setenv("GSPN_TPIPE_GROUPS", str(n))
+            print(f"[parity] {plan} groups={n} mask={mask} G={G}", flush=True)
+            outs.append(run(inp, mask, G))
+            assert_parity(outs[-1], ref, f"{plan} groups={n} mask={mask} G={G}")
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
